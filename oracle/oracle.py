@@ -1,0 +1,300 @@
+"""ctypes + numpy marshalling for the C oracle (liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the bench's
+CPU-baseline leg; never by the product package. Every computation happens in
+moe_oracle.c; this file only allocates arrays and passes pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+TIE_EXPERT, TIE_GROUP, TIE_ORDER = 1, 2, 4
+
+
+class OrcCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("rsf", ctypes.c_float)]
+
+
+class OrcTaps(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("z", "ids", "w", "flags", "qx", "dx", "h", "qh", "dh", "e_out")]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        L = ctypes.CDLL(os.path.join(_HERE, "liboracle.so"))
+        P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        L.orc_quant_int4_rows.argtypes = [P, I64, I64, P, P]
+        L.orc_pack_int4.argtypes = [P, I64, P]
+        L.orc_unpack_int4.argtypes = [P, I64, P]
+        L.orc_unpack_int4_tiled64.argtypes = [P, I64, I64, P]
+        L.orc_q8_0.argtypes = [P, I64, P, P]
+        L.orc_router_logits.argtypes = [P, I32, I32, P, I32, P]
+        L.orc_route.argtypes = [P, P, P, I32, P, P, P, P, P]
+        L.orc_dispatch.argtypes = [I32, I32, I32, P, P, P, P, P, P, P]
+        L.orc_block_sums.argtypes = [P, P, I64, P]
+        L.orc_dot_q4q8.argtypes = [P, F, P, P, I64]
+        L.orc_dot_q4q8.restype = F
+        L.orc_swiglu.argtypes = [F, F]
+        L.orc_swiglu.restype = F
+        L.orc_expert_token.argtypes = [I32, I32] + [P] * 12
+        L.orc_combine.argtypes = [I32, I32, I32, I32, P, P, P, P]
+        L.orc_layer_forward.argtypes = [P, I32] + [P] * 12 + [P]
+        L.orc_lru_new.argtypes = [I32, I32]
+        L.orc_lru_new.restype = P
+        L.orc_lru_free.argtypes = [P]
+        L.orc_lru_step.argtypes = [P, I64, P, I32, P, P, P, P]
+        L.orc_lru_counters.argtypes = [P, P, P, P]
+        L.orc_lru_resident.argtypes = [P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+@dataclass
+class Cfg:
+    hidden: int
+    n_experts: int
+    n_group: int
+    topk_group: int
+    top_k: int
+    inter: int
+    n_shared: int
+    rsf: float
+
+    def c(self):
+        return OrcCfg(self.hidden, self.n_experts, self.n_group, self.topk_group, self.top_k, self.inter,
+                      self.n_shared, self.rsf)
+
+    @staticmethod
+    def of(shape):
+        return Cfg(shape.hidden, shape.n_experts, shape.n_group, shape.topk_group, shape.top_k, shape.inter,
+                   shape.n_shared, shape.rsf)
+
+
+def quant_int4_rows(w):
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), np.int8)
+    s = np.empty(rows, np.float32)
+    lib().orc_quant_int4_rows(_p(w), rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def pack_int4(q):
+    q = _c(q, np.int8).reshape(-1)
+    out = np.empty(q.size // 2, np.uint8)
+    lib().orc_pack_int4(_p(q), q.size, _p(out))
+    return out
+
+
+def unpack_int4(b, n):
+    b = _c(b, np.uint8).reshape(-1)
+    q = np.empty(n, np.int8)
+    lib().orc_unpack_int4(_p(b), n, _p(q))
+    return q
+
+
+def unpack_int4_tiled64(b, rows, cols):
+    b = _c(b, np.uint8).reshape(-1)
+    q = np.empty((rows, cols), np.int8)
+    lib().orc_unpack_int4_tiled64(_p(b), rows, cols, _p(q))
+    return q
+
+
+def q8_0(v):
+    v = _c(v, np.float32)
+    shp = v.shape
+    n = v.size
+    q = np.empty(n, np.int8)
+    d = np.empty(n // 32, np.float32)
+    lib().orc_q8_0(_p(v), n, _p(q), _p(d))
+    return q.reshape(shp), d.reshape(shp[:-1] + (shp[-1] // 32,))
+
+
+def router_logits(x, Wr):
+    x = _c(x, np.float32)
+    Wr = _c(Wr, np.float32)
+    T, H = x.shape
+    E = Wr.shape[0]
+    z = np.empty((T, E), np.float32)
+    lib().orc_router_logits(_p(x), T, H, _p(Wr), E, _p(z))
+    return z
+
+
+def route(cfg: Cfg, z, bias, want_scores=False):
+    z = _c(z, np.float32)
+    bias = _c(bias, np.float32)
+    T = z.shape[0]
+    K, E = cfg.top_k, cfg.n_experts
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float32)
+    fl = np.empty(T, np.uint8)
+    s = np.empty((T, E), np.float32) if want_scores else None
+    c = np.empty((T, E), np.float32) if want_scores else None
+    oc = cfg.c()
+    rc = lib().orc_route(ctypes.byref(oc), _p(z), _p(bias), T, _p(ids), _p(w), _p(fl), _p(s), _p(c))
+    if rc != 0:
+        raise ValueError(f"orc_route: invalid shape (rc={rc})")
+    if want_scores:
+        return ids, w, fl, s, c
+    return ids, w, fl
+
+
+def dispatch(ids, E):
+    ids = _c(ids, np.int32)
+    T, K = ids.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    ss = np.empty(T * K, np.int32)
+    sp = np.empty(T * K, np.int32)
+    uq = np.empty(E, np.int32)
+    nu = np.zeros(1, np.int32)
+    rc = lib().orc_dispatch(T, K, E, _p(ids), _p(counts), _p(offsets), _p(ss), _p(sp), _p(uq), _p(nu))
+    if rc != 0:
+        raise ValueError("orc_dispatch: expert id out of range")
+    return dict(counts=counts, offsets=offsets, sorted_slots=ss, slot_pos=sp, unique_ids=uq,
+                n_unique=int(nu[0]))
+
+
+def block_sums(a, b):
+    a = _c(a, np.int8).reshape(-1)
+    b = _c(b, np.int8).reshape(-1)
+    S = np.empty(a.size // 32, np.int32)
+    lib().orc_block_sums(_p(a), _p(b), a.size, _p(S))
+    return S
+
+
+def dot_q4q8(q4, srow, q8, d8):
+    q4 = _c(q4, np.int8)
+    q8 = _c(q8, np.int8)
+    d8 = _c(d8, np.float32)
+    return np.float32(lib().orc_dot_q4q8(_p(q4), float(srow), _p(q8), _p(d8), q4.size))
+
+
+def swiglu(g, u):
+    return np.float32(lib().orc_swiglu(float(g), float(u)))
+
+
+def expert_token(q13, s13, q2, s2, qx, dx, want_sums=False):
+    q13 = _c(q13, np.int8)
+    s13 = _c(s13, np.float32)
+    q2 = _c(q2, np.int8)
+    s2 = _c(s2, np.float32)
+    qx = _c(qx, np.int8)
+    dx = _c(dx, np.float32)
+    H = q2.shape[0]
+    I = q2.shape[1]
+    h = np.empty(I, np.float32)
+    qh = np.empty(I, np.int8)
+    dh = np.empty(I // 32, np.float32)
+    out = np.empty(H, np.float32)
+    S13 = np.empty((2 * I, H // 32), np.int32) if want_sums else None
+    S2 = np.empty((H, I // 32), np.int32) if want_sums else None
+    lib().orc_expert_token(H, I, _p(q13), _p(s13), _p(q2), _p(s2), _p(qx), _p(dx), _p(h), _p(qh), _p(dh),
+                           _p(out), _p(S13), _p(S2))
+    r = dict(h=h, qh=qh, dh=dh, out=out)
+    if want_sums:
+        r.update(S13=S13, S2=S2)
+    return r
+
+
+def combine(e_routed, e_shared, w):
+    e_routed = _c(e_routed, np.float32)
+    w = _c(w, np.float32)
+    T, K, H = e_routed.shape
+    NS = 0 if e_shared is None else e_shared.shape[0]
+    es = None if e_shared is None else _c(e_shared, np.float32)
+    y = np.empty((T, H), np.float32)
+    lib().orc_combine(T, K, H, NS, _p(e_routed), _p(es), _p(w), _p(y))
+    return y
+
+
+@dataclass
+class LayerQ:
+    """A layer's weights in the oracle's unpacked form: int8 codes + fp32 row scales."""
+    router_w: np.ndarray  # [E][H] fp32
+    bias: np.ndarray      # [E] fp32
+    q13: np.ndarray       # [E][2I][H] int8
+    s13: np.ndarray       # [E][2I]
+    q2: np.ndarray        # [E][H][I] int8
+    s2: np.ndarray        # [E][H]
+    sq13: np.ndarray      # [NS][2I][H]
+    ss13: np.ndarray
+    sq2: np.ndarray
+    ss2: np.ndarray
+
+
+def layer_forward(cfg: Cfg, x, L: LayerQ, taps=True):
+    x = _c(x, np.float32)
+    T, H = x.shape
+    E, K, I, NS = cfg.n_experts, cfg.top_k, cfg.inter, cfg.n_shared
+    R = T * K + NS * T
+    y = np.empty((T, H), np.float32)
+    t = dict(z=np.empty((T, E), np.float32), ids=np.empty((T, K), np.int32), w=np.empty((T, K), np.float32),
+             flags=np.empty(T, np.uint8), qx=np.empty((T, H), np.int8), dx=np.empty((T, H // 32), np.float32),
+             h=np.empty((R, I), np.float32), qh=np.empty((R, I), np.int8), dh=np.empty((R, I // 32), np.float32),
+             e_out=np.empty((R, H), np.float32))
+    ot = OrcTaps(*[_p(t[n]) for n in ("z", "ids", "w", "flags", "qx", "dx", "h", "qh", "dh", "e_out")])
+    oc = cfg.c()
+    arrs = [_c(a, dt) for a, dt in ((L.router_w, np.float32), (L.bias, np.float32), (L.q13, np.int8),
+                                     (L.s13, np.float32), (L.q2, np.int8), (L.s2, np.float32),
+                                     (L.sq13, np.int8), (L.ss13, np.float32), (L.sq2, np.int8),
+                                     (L.ss2, np.float32))]
+    rc = lib().orc_layer_forward(ctypes.byref(oc), T, _p(x), *[_p(a) for a in arrs], _p(y), ctypes.byref(ot))
+    if rc != 0:
+        raise ValueError(f"orc_layer_forward failed rc={rc}")
+    return (y, t) if taps else y
+
+
+class LRU:
+    """The oracle's per-layer LRU policy simulator."""
+
+    def __init__(self, n_experts, n_slots):
+        self.E = n_experts
+        self.h = lib().orc_lru_new(n_experts, n_slots)
+        if not self.h:
+            raise ValueError("bad LRU shape")
+
+    def step(self, step, needed):
+        nd = _c(np.sort(np.asarray(needed)), np.int32)
+        n = nd.size
+        hit = np.zeros(n, np.uint8)
+        slot = np.zeros(n, np.int32)
+        ev = np.zeros(n, np.int32)
+        wf = np.zeros(n, np.int32)
+        rc = lib().orc_lru_step(self.h, step, _p(nd), n, _p(hit), _p(slot), _p(ev), _p(wf))
+        if rc != 0:
+            raise ValueError("needed list must be unique expert ids")
+        return dict(needed=nd, hit=hit.astype(bool), slot=slot, evicted=ev, wait_for=wf)
+
+    def counters(self):
+        a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        lib().orc_lru_counters(self.h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+        return dict(hits=a.value, misses=b.value, evictions=c.value)
+
+    def resident(self):
+        out = np.empty(self.E, np.int32)
+        lib().orc_lru_resident(self.h, _p(out))
+        return out
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            lib().orc_lru_free(self.h)
+            self.h = None
