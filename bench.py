@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of one GLM-5.2-shaped MoE-layer forward on one MI355X.
+
+A step is one full layer forward (router, top-k, dispatch, Q8_0 of x, gate-up +
+SwiGLU, down, combine) over one batch of synthetic tokens, inputs already in HBM.
+Workloads (GLM shape: H=6144, 256 routed experts in 8 groups, top-4 groups,
+top-8, I=2048, one shared expert, rsf 2.5; int4 weights from N(0,0.02) with
+per-row scales; Zipf(1.1) correction bias; hidden states N(0,1)):
+  decode32  T=32 decode batch (default; the metric's headline workload)
+  decode1   T=1
+  mtp192    64 sequences x 3 positions, correlated (rho 0.8)
+  prefill   T=2048
+Weights rotate over --copies layer copies (different seeds) and every step
+uses fresh tokens, so the 256 MB last-level cache cannot serve weights from a
+previous step.
+
+Prints one JSON line (rank 0). Multi-GPU runs are not supported: this build
+measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / int8 MFMA % (prefill)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode32", choices=["decode32", "decode1", "mtp192", "prefill"])
+    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--gemm-min", type=int, default=0)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def tokens_of(workload):
+    return {"decode32": 32, "decode1": 1, "mtp192": 192, "prefill": 2048}[workload]
+
+
+def make_inputs(shape, workload, n, seed):
+    from synth import synth
+    T = tokens_of(workload)
+    xs = []
+    for s in range(n):
+        if workload == "mtp192":
+            xs.append(synth.mtp_hidden_states(shape, 64, 3, 0.8, seed=seed, step=s))
+        else:
+            xs.append(synth.hidden_states(shape, T, seed=seed, step=s))
+    return xs
+
+
+def routing_stats(moe, cfg, layer, x_dev, ws, gemm_min):
+    """Unique experts and bucket sizes of one batch (router + dispatch, outside the timed region)."""
+    import torch
+    T = x_dev.shape[0]
+    E, K = cfg.n_experts, cfg.top_k
+    dev = x_dev.device
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    moe.moe_router(cfg, x_dev, layer.router_w, layer.bias, ids, w, None, ws)
+    outs = [torch.empty(E, dtype=torch.int32, device=dev), torch.empty(E + 1, dtype=torch.int32, device=dev),
+            torch.empty(T * K, dtype=torch.int32, device=dev), torch.empty(T * K, dtype=torch.int32, device=dev),
+            torch.empty(E, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev)]
+    moe.moe_dispatch(cfg, ids, *outs, ws)
+    counts = outs[0].cpu().numpy()
+    gm = gemm_min if gemm_min > 0 else 8
+    nz = counts[counts > 0]
+    return dict(U=int(nz.size), gemv_experts=int((nz < gm).sum()) + (1 if T < gm else 0),
+                mfma_experts=int((nz >= gm).sum()) + (1 if T >= gm else 0),
+                gemv_tokens=int(nz[nz < gm].sum()) + (T if T < gm else 0),
+                mfma_tokens=int(nz[nz >= gm].sum()) + (T if T >= gm else 0), counts=counts)
+
+
+def cpu_baseline(shape, x, seconds, seed):
+    """The oracle as it stands, single-threaded, on the first tokens of the first batch."""
+    from oracle import oracle as O
+    from synth import synth
+    from tests.harness import oracle_expert
+    cfg = O.Cfg.of(shape)
+    Wr = synth.router_weights(shape, seed)
+    bias = synth.router_bias(shape, seed)
+    done, t_oracle = 0, 0.0
+    T = x.shape[0]
+    sample = 0
+    while t_oracle < seconds and sample < T:
+        xt = x[sample:sample + 1]
+        ids, _, _ = O.route(cfg, O.router_logits(xt, Wr), bias)
+        parts = [oracle_expert(shape, int(e), seed) for e in ids[0]] + [oracle_expert(shape, 0, seed, shared=True)]
+        t0 = time.perf_counter()
+        z = O.router_logits(xt, Wr)
+        ids, w, _ = O.route(cfg, z, bias)
+        qx, dx = O.q8_0(xt[0])
+        rows = [O.expert_token(*p, qx, dx)["out"] for p in parts]
+        O.combine(np.stack(rows[:-1])[None], np.stack(rows[-1:])[:, None], w)
+        t_oracle += time.perf_counter() - t0
+        done += 1
+        sample += 1
+    return dict(value=done / t_oracle, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done} tokens of the first batch, each: fp64 router over 256 experts, 8 routed + 1 shared "
+                       f"int4xint8 expert FFNs, combine; {t_oracle:.1f} s of single-threaded oracle time "
+                       f"(weight generation excluded)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import int4_quantized_expert_amd as moe
+    from synth import synth
+    from tests.harness import GpuLayer, config_of
+
+    shape = synth.GLM
+    T = tokens_of(args.workload)
+    dev = torch.device("cuda:0")
+    cfg = config_of(shape, args.gemm_min)
+    layers = [GpuLayer(shape, seed=args.seed + c) for c in range(args.copies)]
+    n_in = args.warmup + args.steps
+    xs_host = make_inputs(shape, args.workload, min(n_in, 64), args.seed)
+    xs = [torch.from_numpy(x).to(dev) for x in xs_host]
+    ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, shape.hidden), dtype=torch.float32, device=dev)
+    wts = [l.weights() for l in layers]
+
+    # routing statistics of every timed step (outside the timed region)
+    stats = []
+    for s in range(args.steps):
+        i = args.warmup + s
+        stats.append(routing_stats(moe, cfg, layers[i % args.copies], xs[i % len(xs)], ws, args.gemm_min))
+
+    stream = torch.cuda.current_stream()
+    for s in range(args.warmup):
+        moe.moe_layer_forward(cfg, wts[s % args.copies], xs[s % len(xs)], y, ws)
+    torch.cuda.synchronize()
+    moe.moe_prof_enable(args.steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for s in range(args.steps):
+        i = args.warmup + s
+        moe.moe_layer_forward(cfg, wts[i % args.copies], xs[i % len(xs)], y, ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    prof = moe.moe_prof_read(args.steps)
+    moe.moe_prof_disable()
+
+    H, I, E = shape.hidden, shape.inter, shape.n_experts
+    w13_bytes = I * H + 2 * I * 4  # int4 gate+up rows + fp32 row scales
+    w2_bytes = H * I // 2 + H * 4
+    U = np.array([s["U"] for s in stats], np.float64)
+    layer_bytes = (E * H * 4 + E * 4) + (U + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 4
+    stage_ms = prof.mean(0)
+    # dominant kernel: the gate-up launch of the path that moves most bytes
+    if args.workload == "prefill":
+        kidx, kname = 5, "k_gateup_mfma"
+        ops = np.array([2.0 * s["mfma_tokens"] * 2 * I * H for s in stats])
+        kt = prof[:, kidx] / 1e3
+        achieved = float(np.mean(ops / kt) / 1e12)
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
+                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=None, kernel=kname,
+                    kernel_ms=round(float(kt.mean() * 1e3), 4),
+                    per_unit="2*2I*H int8 ops per (token, expert) on the MFMA path")
+    else:
+        kidx, kname = 4, "k_gateup_gemv"
+        gb = np.array([s["gemv_experts"] * w13_bytes + s["gemv_tokens"] * (H + H // 32 * 4 + I + I // 32 * 4)
+                       for s in stats], np.float64)
+        kt = prof[:, kidx] / 1e3
+        achieved = float(np.mean(gb / kt) / 1e9)
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel=kname,
+                    kernel_ms=round(float(kt.mean() * 1e3), 4),
+                    per_unit=f"{w13_bytes} B of gate/up weights+scales per GEMV-path expert, plus Q8_0 activations "
+                             f"in and Q8_0 h out per token")
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": f"glm5.2-moe-layer {args.workload}", "tokens": T, "hidden": H, "experts": E,
+                   "groups": shape.n_group, "topk_group": shape.topk_group, "top_k": shape.top_k, "inter": I,
+                   "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or 8,
+                   "layer_copies": args.copies},
+        "layer_hbm_gbs": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9), 1),
+        "layer_hbm_frac": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9) / HBM_PEAK_GBS, 4),
+        "unique_experts_mean": round(float(U.mean()), 2),
+        "stage_ms": {n: round(float(v), 5) for n, v in zip(moe.STAGES, stage_ms)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

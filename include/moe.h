@@ -1,0 +1,243 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) MoE-layer library: one GLM-5.2-style
+ * Mixture-of-Experts layer forward with packed-int4 expert weights and
+ * Q8_0-style int8 activations, as the colibrì pages describe the method.
+ *
+ * Passages followed (page title, section):
+ *  [A] "Colibri: 25GB RAM을 탑재한 노트북에서 744B AI 모델 실행하기", how MoE
+ *      works: a router picks 8 routed experts per token per layer; 3-tier
+ *      memory: routed experts (about 19 MB each in int4) stream through a
+ *      per-layer LRU cache, and the router's decisions and outputs do not
+ *      depend on which tier holds an expert.
+ *  [B] "Show HN: 느린 컴퓨터에서 GLM 5.2 실행하기", implemented features:
+ *      DeepSeek-V3-style sigmoid router (noaux_tc, routed_scaling_factor) with
+ *      a shared expert; integer-dot kernels on Q8_0-style int8 activations;
+ *      int8 / packed int4 weights with per-row scales, dequantized on use;
+ *      batch-union MoE for prefill and MTP verification, which reads each
+ *      unique expert of the batch once and applies it to every position routed
+ *      to it; expert readahead overlapping the next expert's load with the
+ *      current multiply.
+ *  [C] same page, disk-streaming MoE: per-layer LRU expert cache.
+ *
+ * Conventions for every call:
+ *  - All array arguments are DEVICE pointers owned by the caller unless marked
+ *    "host". The library never frees or keeps them past the call.
+ *  - Calls are asynchronous on the given HIP stream; kernel faults surface at
+ *    the caller's next synchronization. Outputs are overwritten, never
+ *    accumulated into.
+ *  - Every argument is validated before anything is enqueued: a call that
+ *    returns an error has left the stream untouched.
+ *  - Return value: MOE_OK (0) or a negative MOE_E_* code. After MOE_E_HIP,
+ *    moe_last_hip_error() returns the hipError_t that caused it.
+ *  - The forward path allocates no memory: the caller passes a workspace of at
+ *    least moe_workspace_bytes() bytes (device, 256-byte aligned).
+ *  - Stateless calls are re-entrant on distinct streams; a cache object is not
+ *    thread-safe.
+ *
+ * Weight layout ("row-tiled int4", rows of K int4 values, K % 32 == 0,
+ * rows % 64 == 0): two's-complement nibbles, element 2j of a 32-element block
+ * in the low nibble of byte j. Rows are grouped in tiles of 64; inside a tile,
+ * for each 32-element block of the row, the 64 rows' 16-byte blocks are
+ * adjacent. Byte j of block b of row r is at
+ *     ((r / 64) * (K / 32) + b) * 1024 + (r % 64) * 16 + j.
+ * One fp32 scale per row. moe_quantize_int4() produces this layout.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_E_NULL (-1)        /* a required pointer is NULL */
+#define MOE_E_SHAPE (-2)       /* unsupported or inconsistent sizes */
+#define MOE_E_WORKSPACE (-3)   /* workspace missing, misaligned or too small */
+#define MOE_E_HIP (-4)         /* a HIP runtime call failed */
+#define MOE_E_NOMEM (-5)       /* allocation failed (expert cache only) */
+#define MOE_E_UNSUPPORTED (-6) /* valid request this build does not handle */
+#define MOE_E_ARG (-7)         /* invalid scalar argument */
+
+/* Router flag bits written per token (moe_router near_tie output). */
+#define MOE_TIE_EXPERT 1 /* K-th and (K+1)-th candidate biased scores within 1e-6 */
+#define MOE_TIE_GROUP 2  /* topk_group-th and next group score within 1e-6 */
+#define MOE_TIE_ORDER 4  /* two selected experts' biased scores within 1e-6 */
+
+typedef struct moe_config {
+  int32_t hidden;        /* H: multiple of 64 */
+  int32_t n_experts;     /* E: 2..1024 routed experts */
+  int32_t n_group;       /* G: E % G == 0, E / G >= 2, G <= 64 */
+  int32_t topk_group;    /* groups kept per token, 1..G */
+  int32_t top_k;         /* K: 1..32 and K <= topk_group * E / G */
+  int32_t inter;         /* I: expert intermediate size, multiple of 64 */
+  int32_t n_shared;      /* shared experts, 0..4 */
+  float routed_scaling_factor;
+  int32_t gemm_min_tokens; /* bucket size from which the int8-MFMA path is used;
+                              <= 0 selects the default. Never changes results. */
+} moe_config;
+
+/* A layer's weights. Routed arrays hold E experts back to back; shared arrays
+ * hold n_shared experts back to back (may be NULL when n_shared == 0).
+ *   router_w [E][H] fp32 row-major;  router_bias [E] fp32 (selection only)
+ *   w13      per expert: row-tiled int4 of [2I][H] (gate rows 0..I-1, up rows I..2I-1), I*H bytes
+ *   s13      per expert: [2I] fp32 row scales
+ *   w2       per expert: row-tiled int4 of [H][I] (down projection), H*I/2 bytes
+ *   s2       per expert: [H] fp32 row scales                                      */
+typedef struct moe_layer_weights {
+  const float* router_w;
+  const float* router_bias;
+  const uint8_t* w13;
+  const float* s13;
+  const uint8_t* w2;
+  const float* s2;
+  const uint8_t* sh_w13;
+  const float* sh_s13;
+  const uint8_t* sh_w2;
+  const float* sh_s2;
+} moe_layer_weights;
+
+/* Optional device buffers the forward also writes, for bit-exact checks.
+ * Rows of h/qh/dh/e_out are "slot rows": routed slot t*K+k, shared expert s of
+ * token t at row T*K + s*T + t. qx and qh are in natural element order. Any
+ * field may be NULL. Block sums are written for one slot row (sum_slot, or -1
+ * for none): gateup_sums [2I][H/32] and down_sums [H][I/32], int32. */
+typedef struct moe_taps {
+  int32_t* topk_ids; /* [T][K] */
+  float* topk_w;     /* [T][K] */
+  uint8_t* near_tie; /* [T] MOE_TIE_* bits */
+  int8_t* qx;        /* [T][H] */
+  float* dx;         /* [T][H/32] */
+  float* h;          /* [R][I] fp32 SwiGLU output, R = T*K + n_shared*T */
+  int8_t* qh;        /* [R][I] */
+  float* dh;         /* [R][I/32] */
+  float* e_out;      /* [R][H] per-slot expert outputs (before the router weight) */
+  int32_t sum_slot;
+  int32_t* gateup_sums;
+  int32_t* down_sums;
+  int32_t* counts;       /* [E]   as moe_dispatch */
+  int32_t* offsets;      /* [E+1] */
+  int32_t* sorted_slots; /* [T*K] */
+  int32_t* slot_pos;     /* [T*K] */
+  int32_t* unique_ids;   /* [E] */
+  int32_t* n_unique;     /* [1] */
+} moe_taps;
+
+int32_t moe_version(void);
+const char* moe_strerror(int32_t code);
+int32_t moe_last_hip_error(void);
+
+/* Bytes of device workspace moe_layer_forward / moe_router / moe_dispatch need
+ * for up to max_tokens tokens; 0 if the config is invalid. */
+size_t moe_workspace_bytes(const moe_config* cfg, int32_t max_tokens);
+
+/* Converter: fp32 rows w [rows][cols] -> row-tiled int4 (packed, rows*cols/2
+ * bytes) + per-row fp32 scales. Per-row symmetric quantization [B]:
+ * s = amax/7, q = round-half-away(w * (1/s)) clamped to [-7,7], s = 0 for an
+ * all-zero row. rows % 64 == 0, cols % 32 == 0. */
+int32_t moe_quantize_int4(const float* w, int32_t rows, int32_t cols, uint8_t* packed, float* scales,
+                          hipStream_t stream);
+
+/* Q8_0 of n fp32 values (n % 32 == 0) [B]: per 32-block d = amax/127,
+ * q = round-half-away(v * (1/d)) clamped to [-127,127]; natural order. */
+int32_t moe_quantize_q8_0(const float* x, int64_t n, int8_t* q, float* d, hipStream_t stream);
+
+/* Router [B]: logits z = x . router_w^T (fp32 inputs, fp64 accumulation in a
+ * fixed order independent of T and of the token's position), s = sigmoid(z),
+ * c = s + bias; group score = top-2 sum of c per group; keep topk_group
+ * groups; top-K experts by c among them (ties to the lower index; slot order
+ * c descending); weights = s / sum(s) * routed_scaling_factor.
+ * x [T][H] fp32; topk_ids [T][K] int32; topk_w [T][K] fp32; near_tie [T]
+ * (nullable). T >= 1. */
+int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float* router_w,
+                   const float* router_bias, int32_t* topk_ids, float* topk_w, uint8_t* near_tie, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* Batch-union bucketing [B]: slot j = t*K + k. counts[e]; offsets[E+1] the
+ * exclusive prefix sum; sorted_slots groups slots by expert, ascending slot
+ * inside each expert (stable, deterministic, no float atomics); slot_pos its
+ * inverse; unique_ids the experts with a non-zero count, ascending (rest -1);
+ * n_unique [1]. topk_ids values must lie in [0, E). */
+int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, int32_t* counts, int32_t* offsets,
+                     int32_t* sorted_slots, int32_t* slot_pos, int32_t* unique_ids, int32_t* n_unique, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Whole layer [A][B]: y [T][H] = sum over shared experts of FFN_s(x) (weight
+ * 1, added first) + sum_k topk_w[t][k] * FFN_{id(t,k)}(x[t]) in slot order,
+ * where FFN(x) = W2 . Q8_0(silu(W1 . Q8_0(x)) * (W3 . Q8_0(x))) with int4 rows
+ * dotted against int8 activations: exact int32 sums per 32-element block,
+ * then acc = fma(d_block, sum, acc) in ascending block order from 0 and one
+ * multiply by the row scale; silu(g)*u = g*u/(1+exp(-g)) in fp64, rounded
+ * once. Each unique expert's weights are read once for all its tokens.
+ * taps may be NULL. */
+int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
+                          void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-layer LRU expert cache [A][C]: routed experts live in pinned host
+ * memory; an HBM pool of n_slots expert slots holds the recently used ones.
+ * moe_expert_cache_forward routes on the GPU, reads the unique expert list
+ * back to the host (the one host synchronization of this path), updates the
+ * LRU, copies misses host->device on the `copy` stream (overlapping the
+ * compute of experts already resident), and runs the same kernels as
+ * moe_layer_forward, so outputs are bit-identical to the all-resident layer.
+ * Policy: hits are computed first; a miss takes a free slot, else the slot of
+ * a resident expert not needed this step (oldest last use first, lower id
+ * first); when misses outnumber such slots, a later miss reuses the slot of an
+ * expert already consumed this step, after that expert's compute.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_expert_cache moe_expert_cache;
+
+/* Host arrays of E pointers into pinned host memory (hipHostMalloc), one per
+ * routed expert, in the device layout above. */
+typedef struct moe_host_experts {
+  const uint8_t* const* w13;
+  const float* const* s13;
+  const uint8_t* const* w2;
+  const float* const* s2;
+} moe_host_experts;
+
+typedef struct moe_cache_stats {
+  int64_t hits;
+  int64_t misses;
+  int64_t evictions;
+  int64_t bytes_h2d;
+  int64_t steps;
+  double h2d_ms; /* summed host->device copy time of the last step (event-timed), 0 if unknown */
+} moe_cache_stats;
+
+/* Allocates the HBM slot pool (n_slots experts) and its bookkeeping; the only
+ * allocating call of the library. */
+int32_t moe_expert_cache_create(const moe_config* cfg, int32_t n_slots, int32_t max_tokens,
+                                moe_expert_cache** out);
+/* resident: router and shared-expert weights on the device (routed w13/s13/w2/s2
+ * ignored). Per-step trace (nullable host arrays of E entries): is_hit 0/1/-1
+ * (not needed), slot per needed expert. */
+int32_t moe_expert_cache_forward(moe_expert_cache* cache, const moe_layer_weights* resident,
+                                 const moe_host_experts* host, const float* x, int32_t T, float* y, void* ws,
+                                 size_t ws_bytes, hipStream_t compute, hipStream_t copy, int8_t* trace_is_hit,
+                                 int32_t* trace_slot);
+int32_t moe_expert_cache_stats(const moe_expert_cache* cache, moe_cache_stats* out /* host */);
+void moe_expert_cache_destroy(moe_expert_cache* cache);
+
+/* ------------------------------------------------------------------------
+ * Stage timing for measurement: when enabled, moe_layer_forward records a HIP
+ * event pair around each stage on its stream. moe_prof_read synchronizes on
+ * the recorded events and returns per-call milliseconds, [n_calls][MOE_N_STAGES]
+ * (host), in the order router-logits, top-k, dispatch, q8-x, gate-up GEMV,
+ * gate-up MFMA, down GEMV, down MFMA, combine (a stage with no launch reads
+ * near 0). Process-wide, not thread-safe; for benchmarks only.
+ * ---------------------------------------------------------------------- */
+#define MOE_N_STAGES 9
+int32_t moe_prof_enable(int32_t max_calls);
+int32_t moe_prof_read(float* ms /* host */, int32_t max_calls, int32_t* n_calls /* host */);
+void moe_prof_disable(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,192 @@
+// k_dispatch.hip — batch-union bucketing ("Show HN: 느린 컴퓨터에서 GLM 5.2
+// 실행하기", implemented features: batch-union MoE reads each unique expert of
+// the batch once and applies it to every position routed to it).
+//
+// One launch, ceil(E/4) workgroups of four wavefronts. Every workgroup builds
+// the full per-expert histogram of the T*K slots in LDS (integer atomics, so
+// the counts are exact and order-free) and its exclusive prefix sum; wavefront
+// w then owns expert e = 4*block + w and walks the slots in ascending order,
+// placing its matches with a ballot prefix count — a stable counting sort
+// with no cross-workgroup synchronization and no float atomics. Workgroup 0
+// additionally emits the bucket tables the expert kernels consume: the unique
+// expert list, the GEMV bucket list (buckets below the MFMA threshold) and the
+// MFMA tile list (bucket, first token) pairs.
+#include "moe_internal.h"
+
+namespace moe {
+
+struct DispatchArgs {
+  const int32_t* ids;
+  int32_t T, K, E, NS, gemm_min, tok_tile;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* slotpos;
+  int32_t* unique;
+  int32_t* nunique;
+  int32_t* bk_e;
+  int32_t* bk_p0;
+  int32_t* bk_n;
+  int32_t* gemv;
+  int32_t* tiles;
+  int32_t* pos_token;
+  Meta* meta;
+};
+
+__global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
+  __shared__ int hist[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int uq[kMaxExperts];
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, TK = a.T * a.K;
+  for (int e = tid; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  for (int j = tid; j < TK; j += 256) atomicAdd(&hist[a.ids[j]], 1);
+  __syncthreads();
+  // exclusive prefix sum over experts: 4 per thread, then a block scan
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = tid * 4 + i;
+    int c = (e < E) ? hist[e] : 0;
+    loc[i] = sum;
+    sum += c;
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int wpre = 0;
+  for (int w = 0; w < wave; ++w) wpre += wsum[w];
+  const int excl = wpre + incl - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int e = tid * 4 + i;
+    if (e < E) off[e] = excl + loc[i];
+  }
+  if (tid == 0) off[E] = TK;
+  __syncthreads();
+
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int e = blockIdx.x * 4 + wave;
+  if (e < E) {
+    const int cnt = hist[e];
+    int pos = off[e];
+    if (lane == 0) {
+      a.counts[e] = cnt;
+      a.offsets[e] = pos;
+      if (e == E - 1) a.offsets[E] = TK;
+    }
+    const int end = pos + cnt;
+    for (int jb = 0; jb < TK && pos < end; jb += 64) {
+      int j = jb + lane;
+      bool m = (j < TK) && (a.ids[j] == e);
+      uint64_t mask = __ballot(m);
+      if (m) {
+        int p = pos + __popcll(mask & lt);
+        a.sorted[p] = j;
+        a.slotpos[j] = p;
+        a.pos_token[p] = j / a.K;
+      }
+      pos += __popcll(mask);
+    }
+  }
+
+  if (blockIdx.x == 0) {
+    __shared__ int s_nu;
+    if (wave == 0) {
+      int nu = 0;
+      for (int eb = 0; eb < E; eb += 64) {
+        int e2 = eb + lane;
+        bool f = (e2 < E) && hist[e2] > 0;
+        uint64_t mask = __ballot(f);
+        if (f) {
+          int u = nu + __popcll(mask & lt);
+          uq[u] = e2;
+          a.unique[u] = e2;
+          a.bk_e[u] = e2;
+          a.bk_p0[u] = off[e2];
+          a.bk_n[u] = hist[e2];
+        }
+        nu += __popcll(mask);
+      }
+      for (int u = nu + lane; u < E; u += 64) a.unique[u] = -1;
+      for (int s = lane; s < a.NS; s += 64) {
+        a.bk_e[nu + s] = E + s;
+        a.bk_p0[nu + s] = TK + s * a.T;
+        a.bk_n[nu + s] = a.T;
+      }
+      if (lane == 0) s_nu = nu;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int nu = s_nu;
+      const int nbk = nu + a.NS;
+      int ng = 0, nt = 0;
+      for (int bb = 0; bb < nbk; bb += 64) {
+        int b = bb + lane;
+        bool valid = b < nbk;
+        int nb = valid ? (b < nu ? hist[uq[b]] : a.T) : 0;
+        bool g = valid && nb < a.gemm_min;
+        uint64_t mask = __ballot(g);
+        if (g) a.gemv[ng + __popcll(mask & lt)] = b;
+        ng += __popcll(mask);
+        int ntile = (valid && !g) ? (nb + a.tok_tile - 1) / a.tok_tile : 0;
+        int inc = ntile;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          int v = __shfl_up(inc, o);
+          if (lane >= o) inc += v;
+        }
+        int ex = nt + inc - ntile;
+        for (int q = 0; q < ntile; ++q) {
+          a.tiles[2 * (ex + q)] = b;
+          a.tiles[2 * (ex + q) + 1] = q * a.tok_tile;
+        }
+        nt += __shfl(inc, 63);
+      }
+      if (lane == 0) {
+        a.meta->n_unique = nu;
+        a.meta->n_buckets = nbk;
+        a.meta->n_gemv = ng;
+        a.meta->n_tiles = nt;
+        a.nunique[0] = nu;
+      }
+    }
+  }
+}
+
+hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, const Layout& L,
+                           char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
+                           int32_t* unique, int32_t* nunique, hipStream_t st) {
+  DispatchArgs a;
+  a.ids = ids;
+  a.T = T;
+  a.K = c.top_k;
+  a.E = c.n_experts;
+  a.NS = c.n_shared;
+  a.gemm_min = gemm_min;
+  a.tok_tile = kMfmaTokTile;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.sorted = sorted;
+  a.slotpos = slotpos;
+  a.unique = unique;
+  a.nunique = nunique;
+  a.bk_e = reinterpret_cast<int32_t*>(ws + L.bk_e);
+  a.bk_p0 = reinterpret_cast<int32_t*>(ws + L.bk_p0);
+  a.bk_n = reinterpret_cast<int32_t*>(ws + L.bk_n);
+  a.gemv = reinterpret_cast<int32_t*>(ws + L.gemv);
+  a.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+  a.pos_token = reinterpret_cast<int32_t*>(ws + L.pos_token);
+  a.meta = reinterpret_cast<Meta*>(ws + L.meta);
+  k_dispatch<<<(c.n_experts + 3) / 4, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

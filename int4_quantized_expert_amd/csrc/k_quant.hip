@@ -1,0 +1,137 @@
+// k_quant.hip — encoders of the two quantized formats the colibrì pages name
+// ("Show HN: 느린 컴퓨터에서 GLM 5.2 실행하기", implemented features): Q8_0-style
+// int8 activations (32-element blocks, one fp32 scale each) and packed int4
+// weights with one fp32 scale per row. Both are memory-bound streaming kernels:
+// one lane owns one 32-element block (128 B in, 32 B or 16 B out).
+#include "moe_internal.h"
+
+namespace moe {
+
+// q = round-half-away(v * (1/d)), d = amax/127, clamped; all single fp32 ops.
+__device__ __forceinline__ void q8_block(const float* __restrict__ src, int8_t q[32], float& d) {
+  float v[32];
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float4 t = s4[i];
+    v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  d = __fdiv_rn(amax, 127.0f);
+  float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float r = roundf(__fmul_rn(v[i], inv));
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    q[i] = (int8_t)(int)r;
+  }
+}
+
+__device__ __forceinline__ uint32_t pack4(int8_t a, int8_t b, int8_t c, int8_t d) {
+  return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
+         ((uint32_t)(uint8_t)d << 24);
+}
+
+// x [T][H] -> permuted codes (even elements of each group of 8 first), block
+// scales, and optionally the natural-order codes.
+__global__ void k_q8_0_x(const float* __restrict__ x, int64_t nblocks, int8_t* __restrict__ q_perm,
+                         float* __restrict__ d, int8_t* __restrict__ q_nat) {
+  int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  int8_t q[32];
+  float db;
+  q8_block(x + b * 32, q, db);
+  uint32_t wv[8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    wv[2 * g] = pack4(q[8 * g], q[8 * g + 2], q[8 * g + 4], q[8 * g + 6]);
+    wv[2 * g + 1] = pack4(q[8 * g + 1], q[8 * g + 3], q[8 * g + 5], q[8 * g + 7]);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(q_perm + b * 32);
+  dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+  d[b] = db;
+  if (q_nat) {
+    uint32_t nv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) nv[i] = pack4(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+    uint4* nd = reinterpret_cast<uint4*>(q_nat + b * 32);
+    nd[0] = make_uint4(nv[0], nv[1], nv[2], nv[3]);
+    nd[1] = make_uint4(nv[4], nv[5], nv[6], nv[7]);
+  }
+}
+
+// Per-row symmetric int4: one workgroup per row; amax over the row, then each
+// lane encodes its 32-element blocks into the row-tiled layout.
+__global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ w, int cols,
+                                                    uint8_t* __restrict__ packed, float* __restrict__ scales) {
+  const int r = blockIdx.x;
+  const int nb = cols / 32;
+  const float* row = w + (size_t)r * cols;
+  float amax = 0.0f;
+  for (int k = threadIdx.x; k < cols; k += blockDim.x) amax = fmaxf(amax, fabsf(row[k]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 7.0f);
+  const float inv = (s == 0.0f) ? 0.0f : __fdiv_rn(1.0f, s);
+  if (threadIdx.x == 0) scales[r] = s;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+    const float* src = row + b * 32;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float qf = roundf(__fmul_rn(src[i], inv));
+      qf = fminf(fmaxf(qf, -7.0f), 7.0f);
+      uint32_t nib = (uint32_t)((int)qf) & 0xFu;
+      wv[i >> 3] |= nib << (4 * (i & 7));
+    }
+    size_t off = ((size_t)(r / 64) * nb + b) * 1024 + (size_t)(r % 64) * 16;
+    *reinterpret_cast<uint4*>(packed + off) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+}
+
+__global__ void k_q8_0_plain(const float* __restrict__ x, int64_t nblocks, int8_t* __restrict__ q,
+                             float* __restrict__ d) {
+  int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  int8_t qq[32];
+  float db;
+  q8_block(x + b * 32, qq, db);
+  uint32_t nv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) nv[i] = pack4(qq[4 * i], qq[4 * i + 1], qq[4 * i + 2], qq[4 * i + 3]);
+  uint4* nd = reinterpret_cast<uint4*>(q + b * 32);
+  nd[0] = make_uint4(nv[0], nv[1], nv[2], nv[3]);
+  nd[1] = make_uint4(nv[4], nv[5], nv[6], nv[7]);
+  d[b] = db;
+}
+
+hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float* d, int8_t* q_nat,
+                         hipStream_t st) {
+  int64_t nb = T * (H / 32);
+  if (nb == 0) return hipSuccess;
+  k_q8_0_x<<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(x, nb, q_perm, d, q_nat);
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hipStream_t st) {
+  int64_t nb = n / 32;
+  if (nb == 0) return hipSuccess;
+  k_q8_0_plain<<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(x, nb, q, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed, float* scales,
+                             hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  k_quant_int4<<<rows, 256, 0, st>>>(w, cols, packed, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

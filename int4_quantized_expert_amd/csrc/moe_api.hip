@@ -1,0 +1,346 @@
+// moe_api.hip — the C ABI of include/moe.h: argument validation, workspace
+// layout and the launch sequence of one MoE-layer forward on a HIP stream.
+// Nothing here synchronizes with the device; the number of unique experts never
+// travels back to the host: grids are sized for the worst case and workgroups
+// beyond the device-side bucket counts exit at once.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid_gemv, hipStream_t st);
+hipError_t launch_gemv_down(const ExpertArgs& a, int grid_gemv, hipStream_t st);
+hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid_tiles, const int32_t* tiles, const int32_t* n_tiles,
+                              hipStream_t st);
+hipError_t launch_mfma_down(const ExpertArgs& a, int grid_tiles, const int32_t* tiles, const int32_t* n_tiles,
+                            hipStream_t st);
+
+static thread_local int32_t g_last_hip = 0;
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout make_layout(const moe_config& c, int64_t T) {
+  Layout L;
+  L.T = T;
+  L.E = c.n_experts;
+  L.K = c.top_k;
+  L.H = c.hidden;
+  L.I = c.inter;
+  L.NS = c.n_shared;
+  L.TK = T * L.K;
+  L.R = L.TK + L.NS * T;
+  L.NB = std::min<int64_t>(L.E, L.TK) + L.NS;
+  L.TILES = L.TK / kMfmaTokTile + std::min<int64_t>(L.E, L.TK) + L.NS * ((T + kMfmaTokTile - 1) / kMfmaTokTile);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  L.z = take((size_t)T * L.E * 4);
+  L.ids = take((size_t)L.TK * 4);
+  L.w = take((size_t)L.TK * 4);
+  L.flags = take((size_t)T);
+  L.counts = take((size_t)L.E * 4);
+  L.offsets = take((size_t)(L.E + 1) * 4);
+  L.sorted = take((size_t)L.TK * 4);
+  L.slotpos = take((size_t)L.TK * 4);
+  L.unique = take((size_t)L.E * 4);
+  L.nunique = take(4);
+  L.bk_e = take((size_t)(L.E + L.NS) * 4);
+  L.bk_p0 = take((size_t)(L.E + L.NS) * 4);
+  L.bk_n = take((size_t)(L.E + L.NS) * 4);
+  L.gemv = take((size_t)(L.E + L.NS) * 4);
+  L.tiles = take((size_t)L.TILES * 8);
+  L.meta = take(sizeof(Meta));
+  L.pos_token = take((size_t)L.TK * 4);
+  L.qx = take((size_t)T * L.H);
+  L.dx = take((size_t)T * (L.H / 32) * 4);
+  L.qh = take((size_t)L.R * L.I);
+  L.dh = take((size_t)L.R * (L.I / 32) * 4);
+  L.eout = take((size_t)L.R * L.H * 4);
+  L.total = off;
+  return L;
+}
+
+int validate_config(const moe_config* c) {
+  if (!c) return MOE_E_NULL;
+  if (c->hidden <= 0 || c->hidden % 64 != 0) return MOE_E_SHAPE;
+  if (c->inter <= 0 || c->inter % 64 != 0) return MOE_E_SHAPE;
+  if (c->n_experts < 2 || c->n_experts > kMaxExperts) return MOE_E_SHAPE;
+  if (c->n_group < 1 || c->n_group > kMaxGroups || c->n_experts % c->n_group != 0) return MOE_E_SHAPE;
+  if (c->n_experts / c->n_group < 2) return MOE_E_SHAPE;
+  if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_E_SHAPE;
+  if (c->top_k < 1 || c->top_k > kMaxTopK) return MOE_E_SHAPE;
+  if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return MOE_E_SHAPE;
+  if (c->n_shared < 0 || c->n_shared > kMaxShared) return MOE_E_SHAPE;
+  if (!std::isfinite(c->routed_scaling_factor) || c->routed_scaling_factor <= 0.0f) return MOE_E_ARG;
+  return MOE_OK;
+}
+
+constexpr int64_t kMaxTokens = 1 << 20;
+
+static int check_tokens(const moe_config* c, int32_t T) {
+  if (T < 1 || T > kMaxTokens) return MOE_E_SHAPE;
+  if ((int64_t)T * c->top_k > (int64_t)INT32_MAX / 4) return MOE_E_SHAPE;
+  return MOE_OK;
+}
+
+static int check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return MOE_E_WORKSPACE;
+  if (ws_bytes < L.total) return MOE_E_WORKSPACE;
+  return MOE_OK;
+}
+
+static int32_t hip_fail(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return MOE_E_HIP;
+}
+
+// ------------------------------------------------------------------ profiling
+struct Prof {
+  bool on = false;
+  int max_calls = 0;
+  int n = 0;
+  std::vector<hipEvent_t> ev;  // [max_calls][MOE_N_STAGES + 1]
+};
+static Prof g_prof;
+
+static void prof_mark(int call, int stage, hipStream_t st) {
+  if (call >= 0) hipEventRecord(g_prof.ev[(size_t)call * (MOE_N_STAGES + 1) + stage], st);
+}
+
+static int prof_begin() {
+  if (!g_prof.on || g_prof.n >= g_prof.max_calls) return -1;
+  return g_prof.n++;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_version(void) { return 10000; }
+
+const char* moe_strerror(int32_t code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULL: return "required pointer is NULL";
+    case MOE_E_SHAPE: return "unsupported or inconsistent sizes";
+    case MOE_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_E_HIP: return "HIP runtime call failed (see moe_last_hip_error)";
+    case MOE_E_NOMEM: return "allocation failed";
+    case MOE_E_UNSUPPORTED: return "unsupported request";
+    case MOE_E_ARG: return "invalid scalar argument";
+    default: return "unknown error";
+  }
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip; }
+
+size_t moe_workspace_bytes(const moe_config* cfg, int32_t max_tokens) {
+  if (validate_config(cfg) != MOE_OK || check_tokens(cfg, max_tokens) != MOE_OK) return 0;
+  return make_layout(*cfg, max_tokens).total;
+}
+
+int32_t moe_quantize_int4(const float* w, int32_t rows, int32_t cols, uint8_t* packed, float* scales,
+                          hipStream_t stream) {
+  if (!w || !packed || !scales) return MOE_E_NULL;
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 32 != 0) return MOE_E_SHAPE;
+  hipError_t e = launch_quant_int4(w, rows, cols, packed, scales, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_quantize_q8_0(const float* x, int64_t n, int8_t* q, float* d, hipStream_t stream) {
+  if (!x || !q || !d) return MOE_E_NULL;
+  if (n <= 0 || n % 32 != 0) return MOE_E_SHAPE;
+  hipError_t e = launch_q8_0_plain(x, n, q, d, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float* router_w,
+                   const float* router_bias, int32_t* topk_ids, float* topk_w, uint8_t* near_tie, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!x || !router_w || !router_bias || !topk_ids || !topk_w) return MOE_E_NULL;
+  if ((rc = check_tokens(cfg, T))) return rc;
+  Layout L = make_layout(*cfg, T);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  char* wsb = static_cast<char*>(ws);
+  float* z = reinterpret_cast<float*>(wsb + L.z);
+  hipError_t e = launch_router_logits(x, T, cfg->hidden, router_w, cfg->n_experts, z, stream);
+  if (e == hipSuccess) e = launch_topk(z, router_bias, T, *cfg, topk_ids, topk_w, near_tie, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, int32_t* counts, int32_t* offsets,
+                     int32_t* sorted_slots, int32_t* slot_pos, int32_t* unique_ids, int32_t* n_unique, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!topk_ids || !counts || !offsets || !sorted_slots || !slot_pos || !unique_ids || !n_unique) return MOE_E_NULL;
+  if ((rc = check_tokens(cfg, T))) return rc;
+  Layout L = make_layout(*cfg, T);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  int gemm_min = cfg->gemm_min_tokens > 0 ? cfg->gemm_min_tokens : kDefaultGemmMin;
+  hipError_t e = launch_dispatch(topk_ids, T, *cfg, gemm_min, L, static_cast<char*>(ws), counts, offsets,
+                                 sorted_slots, slot_pos, unique_ids, n_unique, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
+                          void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!wts || !x || !y) return MOE_E_NULL;
+  if (!wts->router_w || !wts->router_bias || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_E_NULL;
+  if (cfg->n_shared > 0 && (!wts->sh_w13 || !wts->sh_s13 || !wts->sh_w2 || !wts->sh_s2)) return MOE_E_NULL;
+  if ((rc = check_tokens(cfg, T))) return rc;
+  Layout L = make_layout(*cfg, T);
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if (taps && (taps->gateup_sums || taps->down_sums) && (taps->sum_slot < -1 || taps->sum_slot >= L.R))
+    return MOE_E_ARG;
+
+  char* wsb = static_cast<char*>(ws);
+  const moe_taps* tp = taps;
+  auto pick = [&](auto* tap_ptr, size_t off) -> decltype(tap_ptr) {
+    return tap_ptr ? tap_ptr : reinterpret_cast<decltype(tap_ptr)>(wsb + off);
+  };
+  int32_t* ids = pick(tp ? tp->topk_ids : (int32_t*)nullptr, L.ids);
+  float* w = pick(tp ? tp->topk_w : (float*)nullptr, L.w);
+  uint8_t* flags = pick(tp ? tp->near_tie : (uint8_t*)nullptr, L.flags);
+  int32_t* counts = pick(tp ? tp->counts : (int32_t*)nullptr, L.counts);
+  int32_t* offsets = pick(tp ? tp->offsets : (int32_t*)nullptr, L.offsets);
+  int32_t* sorted = pick(tp ? tp->sorted_slots : (int32_t*)nullptr, L.sorted);
+  int32_t* slotpos = pick(tp ? tp->slot_pos : (int32_t*)nullptr, L.slotpos);
+  int32_t* unique = pick(tp ? tp->unique_ids : (int32_t*)nullptr, L.unique);
+  int32_t* nunique = pick(tp ? tp->n_unique : (int32_t*)nullptr, L.nunique);
+  float* z = reinterpret_cast<float*>(wsb + L.z);
+  const int gemm_min = cfg->gemm_min_tokens > 0 ? cfg->gemm_min_tokens : kDefaultGemmMin;
+
+  ExpertArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.wv.w13 = wts->w13;
+  a.wv.s13 = wts->s13;
+  a.wv.w2 = wts->w2;
+  a.wv.s2 = wts->s2;
+  a.wv.sh_w13 = wts->sh_w13;
+  a.wv.sh_s13 = wts->sh_s13;
+  a.wv.sh_w2 = wts->sh_w2;
+  a.wv.sh_s2 = wts->sh_s2;
+  a.wv.slotmap = nullptr;
+  a.E = cfg->n_experts;
+  a.H = cfg->hidden;
+  a.I = cfg->inter;
+  a.K = cfg->top_k;
+  a.T = T;
+  a.TK = T * cfg->top_k;
+  Meta* meta = reinterpret_cast<Meta*>(wsb + L.meta);
+  a.list = reinterpret_cast<const int32_t*>(wsb + L.gemv);
+  a.list_count = &meta->n_gemv;
+  a.bk_e = reinterpret_cast<const int32_t*>(wsb + L.bk_e);
+  a.bk_p0 = reinterpret_cast<const int32_t*>(wsb + L.bk_p0);
+  a.bk_n = reinterpret_cast<const int32_t*>(wsb + L.bk_n);
+  a.pos_token = reinterpret_cast<const int32_t*>(wsb + L.pos_token);
+  a.sorted = sorted;
+  a.qx = reinterpret_cast<const int8_t*>(wsb + L.qx);
+  a.dx = reinterpret_cast<const float*>(wsb + L.dx);
+  a.qh = reinterpret_cast<int8_t*>(wsb + L.qh);
+  a.dh = reinterpret_cast<float*>(wsb + L.dh);
+  a.eout = reinterpret_cast<float*>(wsb + L.eout);
+  if (tp) {
+    a.t_h = tp->h;
+    a.t_qh = tp->qh;
+    a.t_dh = tp->dh;
+    a.t_eout = tp->e_out;
+    a.sum_slot = tp->sum_slot;
+    a.t_gu_sums = tp->gateup_sums;
+    a.t_dn_sums = tp->down_sums;
+  } else {
+    a.sum_slot = -1;
+  }
+  const int grid_gemv = (int)L.NB;
+  const int grid_tiles = (T >= gemm_min) ? (int)L.TILES : 0;
+  const int32_t* tiles = reinterpret_cast<const int32_t*>(wsb + L.tiles);
+  const int32_t* n_tiles = &meta->n_tiles;
+
+  const int call = prof_begin();
+  hipError_t e = hipSuccess;
+  prof_mark(call, 0, stream);
+  e = launch_router_logits(x, T, cfg->hidden, wts->router_w, cfg->n_experts, z, stream);
+  prof_mark(call, 1, stream);
+  if (e == hipSuccess) e = launch_topk(z, wts->router_bias, T, *cfg, ids, w, flags, stream);
+  prof_mark(call, 2, stream);
+  if (e == hipSuccess)
+    e = launch_dispatch(ids, T, *cfg, gemm_min, L, wsb, counts, offsets, sorted, slotpos, unique, nunique, stream);
+  prof_mark(call, 3, stream);
+  if (e == hipSuccess)
+    e = launch_q8_0_x(x, T, cfg->hidden, reinterpret_cast<int8_t*>(wsb + L.qx), reinterpret_cast<float*>(wsb + L.dx),
+                      tp ? tp->qx : nullptr, stream);
+  if (e == hipSuccess && tp && tp->dx)
+    e = hipMemcpyAsync(tp->dx, wsb + L.dx, (size_t)T * (cfg->hidden / 32) * 4, hipMemcpyDeviceToDevice, stream);
+  prof_mark(call, 4, stream);
+  if (e == hipSuccess) e = launch_gemv_gateup(a, grid_gemv, stream);
+  prof_mark(call, 5, stream);
+  if (e == hipSuccess) e = launch_mfma_gateup(a, grid_tiles, tiles, n_tiles, stream);
+  prof_mark(call, 6, stream);
+  if (e == hipSuccess) e = launch_gemv_down(a, grid_gemv, stream);
+  prof_mark(call, 7, stream);
+  if (e == hipSuccess) e = launch_mfma_down(a, grid_tiles, tiles, n_tiles, stream);
+  prof_mark(call, 8, stream);
+  if (e == hipSuccess) e = launch_combine(a.eout, w, slotpos, T, *cfg, y, stream);
+  prof_mark(call, 9, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_prof_enable(int32_t max_calls) {
+  if (max_calls <= 0 || max_calls > 100000) return MOE_E_ARG;
+  moe_prof_disable();
+  g_prof.ev.resize((size_t)max_calls * (MOE_N_STAGES + 1));
+  for (auto& ev : g_prof.ev) {
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      g_prof.ev.clear();
+      return hip_fail(e);
+    }
+  }
+  g_prof.max_calls = max_calls;
+  g_prof.n = 0;
+  g_prof.on = true;
+  return MOE_OK;
+}
+
+int32_t moe_prof_read(float* ms, int32_t max_calls, int32_t* n_calls) {
+  if (!ms || !n_calls) return MOE_E_NULL;
+  int n = std::min(g_prof.n, max_calls);
+  for (int c = 0; c < n; ++c) {
+    hipEvent_t* ev = &g_prof.ev[(size_t)c * (MOE_N_STAGES + 1)];
+    hipError_t e = hipEventSynchronize(ev[MOE_N_STAGES]);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int s = 0; s < MOE_N_STAGES; ++s) {
+      float t = 0.0f;
+      e = hipEventElapsedTime(&t, ev[s], ev[s + 1]);
+      if (e != hipSuccess) return hip_fail(e);
+      ms[(size_t)c * MOE_N_STAGES + s] = t;
+    }
+  }
+  *n_calls = n;
+  return MOE_OK;
+}
+
+void moe_prof_disable(void) {
+  for (auto& ev : g_prof.ev) hipEventDestroy(ev);
+  g_prof.ev.clear();
+  g_prof.on = false;
+  g_prof.n = 0;
+  g_prof.max_calls = 0;
+}
+
+}  // extern "C"

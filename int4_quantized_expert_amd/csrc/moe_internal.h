@@ -1,0 +1,146 @@
+// moe_internal.h — internal types shared by the gfx950 kernels and the host
+// sequencing of libmoe.so. Not part of the public ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxGroups = 64;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxShared = 4;
+constexpr int kMfmaTokTile = 32;     // tokens per int8-MFMA tile
+constexpr int kDefaultGemmMin = 8;   // bucket size from which the MFMA path runs
+constexpr int kGemvMaxN = 8;         // tokens a GEMV pass keeps in registers
+
+// Bucket b: routed unique experts b < n_unique (ascending expert id), then the
+// shared experts. bk_e = expert index (E + s for shared expert s), bk_p0 =
+// first position, bk_n = tokens. Positions p: routed ones in sorted-slot order
+// (0 .. T*K-1), shared expert s of token t at T*K + s*T + t.
+struct Meta {
+  int32_t n_unique;
+  int32_t n_buckets;
+  int32_t n_gemv;
+  int32_t n_tiles;
+};
+
+// Device workspace layout for T tokens (all offsets 256-byte aligned).
+struct Layout {
+  int64_t T = 0, E = 0, K = 0, H = 0, I = 0, NS = 0, TK = 0, R = 0, NB = 0, TILES = 0;
+  size_t z = 0, ids = 0, w = 0, flags = 0, counts = 0, offsets = 0, sorted = 0, slotpos = 0, unique = 0,
+         nunique = 0, bk_e = 0, bk_p0 = 0, bk_n = 0, gemv = 0, tiles = 0, meta = 0, pos_token = 0, qx = 0,
+         dx = 0, qh = 0, dh = 0, eout = 0, total = 0;
+};
+
+Layout make_layout(const moe_config& c, int64_t T);
+int validate_config(const moe_config* c);
+
+struct WeightView {
+  const uint8_t* w13;  // routed, E back to back (or slot pool)
+  const float* s13;
+  const uint8_t* w2;
+  const float* s2;
+  const uint8_t* sh_w13;
+  const float* sh_s13;
+  const uint8_t* sh_w2;
+  const float* sh_s2;
+  const int32_t* slotmap;  // nullable: routed expert -> index into w13/s13/w2/s2
+};
+
+struct ExpertArgs {
+  WeightView wv;
+  int32_t E, H, I, K, T, TK;
+  const int32_t* list;        // bucket list (GEMV) or tile list (MFMA: bucket, token start pairs)
+  const int32_t* list_count;  // device count of list entries
+  const int32_t* bk_e;
+  const int32_t* bk_p0;
+  const int32_t* bk_n;
+  const int32_t* pos_token;   // [T*K] token of each routed position
+  const int32_t* sorted;      // [T*K] slot of each routed position
+  const int8_t* qx;           // [T][H] permuted Q8_0 codes of x
+  const float* dx;            // [T][H/32]
+  int8_t* qh;                 // [R][I] permuted Q8_0 codes of h (written by gate-up, read by down)
+  float* dh;                  // [R][I/32]
+  float* eout;                // [R][H]
+  // taps (nullable), indexed by slot row
+  float* t_h;
+  int8_t* t_qh;
+  float* t_dh;
+  float* t_eout;
+  int32_t sum_slot;
+  int32_t* t_gu_sums;
+  int32_t* t_dn_sums;
+};
+
+// ------------------------------------------------------------ device helpers
+
+// Position of element m (0..31) of a 32-block in the permuted code order: in each
+// group of 8 the even elements come first, then the odd ones. This matches the
+// order in which one 32-bit word of 8 packed nibbles splits into its low and
+// high nibbles.
+__device__ __forceinline__ int perm32(int m) {
+  int g = m >> 3, k = m & 7;
+  return (g << 3) | ((k & 1) << 2) | (k >> 1);
+}
+
+// Q8_0 of one value per lane over aligned groups of 32 lanes.
+__device__ __forceinline__ void q8_0_lanes32(float v, int8_t& q, float& d) {
+  float a = fabsf(v);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+  d = __fdiv_rn(a, 127.0f);
+  float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
+  float r = roundf(__fmul_rn(v, inv));
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  q = (int8_t)(int)r;
+}
+
+__device__ __forceinline__ float swiglu_f(float g, float u) {
+  return (float)(((double)g * (double)u) / (1.0 + exp(-(double)g)));
+}
+
+__device__ __forceinline__ const uint8_t* expert_w13(const WeightView& v, int ex, int E, size_t bytes) {
+  if (ex >= E) return v.sh_w13 + (size_t)(ex - E) * bytes;
+  int s = v.slotmap ? v.slotmap[ex] : ex;
+  return v.w13 + (size_t)s * bytes;
+}
+__device__ __forceinline__ const float* expert_s13(const WeightView& v, int ex, int E, int n) {
+  if (ex >= E) return v.sh_s13 + (size_t)(ex - E) * n;
+  int s = v.slotmap ? v.slotmap[ex] : ex;
+  return v.s13 + (size_t)s * n;
+}
+__device__ __forceinline__ const uint8_t* expert_w2(const WeightView& v, int ex, int E, size_t bytes) {
+  if (ex >= E) return v.sh_w2 + (size_t)(ex - E) * bytes;
+  int s = v.slotmap ? v.slotmap[ex] : ex;
+  return v.w2 + (size_t)s * bytes;
+}
+__device__ __forceinline__ const float* expert_s2(const WeightView& v, int ex, int E, int n) {
+  if (ex >= E) return v.sh_s2 + (size_t)(ex - E) * n;
+  int s = v.slotmap ? v.slotmap[ex] : ex;
+  return v.s2 + (size_t)s * n;
+}
+
+// ------------------------------------------------------------ launchers
+hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float* d, int8_t* q_nat,
+                         hipStream_t st);
+hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hipStream_t st);
+hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed, float* scales,
+                             hipStream_t st);
+hipError_t launch_router_logits(const float* x, int T, int H, const float* Wr, int E, float* z,
+                                hipStream_t st);
+hipError_t launch_topk(const float* z, const float* bias, int T, const moe_config& c, int32_t* ids, float* w,
+                       uint8_t* flags, hipStream_t st);
+hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, const Layout& L,
+                           char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
+                           int32_t* unique, int32_t* nunique, hipStream_t st);
+hipError_t launch_combine(const float* eout, const float* w, const int32_t* slotpos, int T, const moe_config& c,
+                          float* y, hipStream_t st);
+
+}  // namespace moe

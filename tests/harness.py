@@ -1,0 +1,154 @@
+"""Test/bench harness: builds a layer on the GPU through the library's converter
+(moe_quantize_int4) from the seeded generator, and the oracle's counterpart
+(the same fp32 weights quantized by the C oracle) for parity checks.
+
+Only tests, the smoke check and bench.py import this module.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from synth import synth
+
+_ORACLE_CACHE: dict = {}
+
+
+def config_of(shape, gemm_min: int = 0):
+    import int4_quantized_expert_amd as moe
+    return moe.Config(shape.hidden, shape.n_experts, shape.n_group, shape.topk_group, shape.top_k, shape.inter,
+                      shape.n_shared, shape.rsf, gemm_min)
+
+
+class GpuLayer:
+    """Device-resident layer: router fp32, routed and shared experts in row-tiled int4 with fp32 row scales."""
+
+    def __init__(self, shape, seed: int = 0, layer: int = 0, device: str = "cuda", n_shared: int | None = None):
+        import torch
+
+        import int4_quantized_expert_amd as moe
+        self.shape = shape
+        H, I, E = shape.hidden, shape.inter, shape.n_experts
+        NS = shape.n_shared if n_shared is None else n_shared
+        self.NS = NS
+        dev = torch.device(device)
+        self.router_w = torch.from_numpy(synth.router_weights(shape, seed, layer)).to(dev)
+        self.bias = torch.from_numpy(synth.router_bias(shape, seed, layer)).to(dev)
+        self.w13 = torch.empty((E, I * H), dtype=torch.uint8, device=dev)
+        self.s13 = torch.empty((E, 2 * I), dtype=torch.float32, device=dev)
+        self.w2 = torch.empty((E, H * I // 2), dtype=torch.uint8, device=dev)
+        self.s2 = torch.empty((E, H), dtype=torch.float32, device=dev)
+        ns = max(NS, 1)
+        self.sh_w13 = torch.empty((ns, I * H), dtype=torch.uint8, device=dev)
+        self.sh_s13 = torch.empty((ns, 2 * I), dtype=torch.float32, device=dev)
+        self.sh_w2 = torch.empty((ns, H * I // 2), dtype=torch.uint8, device=dev)
+        self.sh_s2 = torch.empty((ns, H), dtype=torch.float32, device=dev)
+        scratch = torch.empty((2 * I, H), dtype=torch.float32, device=dev)
+        scratch2 = torch.empty((H, I), dtype=torch.float32, device=dev)
+        st = torch.cuda.current_stream().cuda_stream
+        for e in range(E + NS):
+            if e < E:
+                k13, k2, idx, dst = synth.W13, synth.W2, e, (self.w13[e], self.s13[e], self.w2[e], self.s2[e])
+            else:
+                s = e - E
+                k13, k2, idx = synth.SH_W13, synth.SH_W2, s
+                dst = (self.sh_w13[s], self.sh_s13[s], self.sh_w2[s], self.sh_s2[s])
+            synth.gpu_normal_(scratch, seed, synth.stream_id(k13, layer, idx), shape.w_sigma, cuda_stream=st)
+            moe.moe_quantize_int4(scratch, dst[0], dst[1])
+            synth.gpu_normal_(scratch2, seed, synth.stream_id(k2, layer, idx), shape.w_sigma, cuda_stream=st)
+            moe.moe_quantize_int4(scratch2, dst[2], dst[3])
+        del scratch, scratch2
+        torch.cuda.synchronize()
+
+    def weights(self):
+        import int4_quantized_expert_amd as moe
+        if self.NS > 0:
+            return moe.layer_weights(self.router_w, self.bias, self.w13, self.s13, self.w2, self.s2, self.sh_w13,
+                                     self.sh_s13, self.sh_w2, self.sh_s2)
+        return moe.layer_weights(self.router_w, self.bias, self.w13, self.s13, self.w2, self.s2)
+
+    def nbytes(self):
+        n = 0
+        for t in (self.router_w, self.bias, self.w13, self.s13, self.w2, self.s2):
+            n += t.numel() * t.element_size()
+        if self.NS:
+            for t in (self.sh_w13, self.sh_s13, self.sh_w2, self.sh_s2):
+                n += t.numel() * t.element_size()
+        return n
+
+
+def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = False):
+    """(q13, s13, q2, s2) of routed expert e (or shared expert e) from the host generator + oracle quantizer."""
+    from oracle import oracle as O
+    key = (shape, e, seed, layer, shared)
+    if key not in _ORACLE_CACHE:
+        if shared:
+            w13, w2 = synth.shared_w13(shape, e, seed, layer), synth.shared_w2(shape, e, seed, layer)
+        else:
+            w13, w2 = synth.expert_w13(shape, e, seed, layer), synth.expert_w2(shape, e, seed, layer)
+        q13, s13 = O.quant_int4_rows(w13)
+        q2, s2 = O.quant_int4_rows(w2)
+        if len(_ORACLE_CACHE) > 48:
+            _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[key] = (q13, s13, q2, s2)
+    return _ORACLE_CACHE[key]
+
+
+def oracle_layer(shape, seed: int = 0, layer: int = 0, n_shared: int | None = None):
+    """Whole layer in the oracle's unpacked form (small shapes only)."""
+    from oracle import oracle as O
+    NS = shape.n_shared if n_shared is None else n_shared
+    parts = [oracle_expert(shape, e, seed, layer) for e in range(shape.n_experts)]
+    sh = [oracle_expert(shape, s, seed, layer, shared=True) for s in range(NS)]
+    H, I = shape.hidden, shape.inter
+
+    def stack(lst, i, shp, dt):
+        return np.stack([p[i] for p in lst]) if lst else np.zeros((0,) + shp, dt)
+
+    return O.LayerQ(synth.router_weights(shape, seed, layer), synth.router_bias(shape, seed, layer),
+                    stack(parts, 0, (2 * I, H), np.int8), stack(parts, 1, (2 * I,), np.float32),
+                    stack(parts, 2, (H, I), np.int8), stack(parts, 3, (H,), np.float32),
+                    stack(sh, 0, (2 * I, H), np.int8), stack(sh, 1, (2 * I,), np.float32),
+                    stack(sh, 2, (H, I), np.int8), stack(sh, 3, (H,), np.float32))
+
+
+def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n_shared: int | None = None):
+    """Oracle outputs for selected tokens of a batch, one token at a time (any size).
+
+    Returns dict per token: ids, w, flags, rows {k: e_out row}, shared rows, y."""
+    from oracle import oracle as O
+    NS = shape.n_shared if n_shared is None else n_shared
+    cfg = O.Cfg.of(shape)
+    Wr = synth.router_weights(shape, seed, layer)
+    bias = synth.router_bias(shape, seed, layer)
+    out = {}
+    for t in tokens:
+        xt = x[t:t + 1]
+        z = O.router_logits(xt, Wr)
+        ids, w, fl = O.route(cfg, z, bias)
+        qx, dx = O.q8_0(xt[0])
+        rows, shrows = [], []
+        for k in range(shape.top_k):
+            q13, s13, q2, s2 = oracle_expert(shape, int(ids[0, k]), seed, layer)
+            rows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
+        for s in range(NS):
+            q13, s13, q2, s2 = oracle_expert(shape, s, seed, layer, shared=True)
+            shrows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
+        er = np.stack(rows)[None]
+        es = np.stack(shrows)[:, None] if NS else None
+        y = O.combine(er, es, w)[0]
+        out[t] = dict(ids=ids[0], w=w[0], flags=int(fl[0]), z=z[0], rows=np.stack(rows),
+                      shrows=np.stack(shrows) if NS else None, y=y)
+    return out
+
+
+def rel_err(a, b, floor=1e-6):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), floor))) if a.size else 0.0
+
+
+def within_tol(gpu, ref, rel=1e-5, floor=1e-6):
+    """|gpu - ref| <= max(rel*|ref|, floor) elementwise."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    return bool(np.all(np.abs(g - r) <= np.maximum(rel * np.abs(r), floor)))

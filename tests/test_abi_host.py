@@ -1,0 +1,85 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+entry point include/moe.h declares, sizes its workspace, and rejects bad
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_quantized_expert_amd as moe
+from int4_quantized_expert_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert "moe_layer_forward" in names and "moe_router" in names and "moe_dispatch" in names
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_version_and_errors():
+    assert moe.moe_version() >= 10000
+    for rc in range(0, -8, -1):
+        assert L._lib.moe_strerror(rc)
+
+
+def _glm(**kw):
+    c = moe.Config(6144, 256, 8, 4, 8, 2048, 1, 2.5)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_bytes():
+    c = _glm()
+    w1, w32, w2048 = (moe.moe_workspace_bytes(c, t) for t in (1, 32, 2048))
+    assert 0 < w1 < w32 < w2048
+    # dominated by the per-slot fp32 expert outputs: (T*K + T) * H * 4
+    assert w2048 >= (2048 * 9) * 6144 * 4
+    assert moe.moe_workspace_bytes(c, 0) == 0
+
+
+@pytest.mark.parametrize("bad", [dict(hidden=100), dict(inter=96), dict(n_group=5), dict(topk_group=9),
+                                 dict(top_k=40), dict(n_experts=1), dict(n_shared=9), dict(n_group=128, n_experts=128),
+                                 dict(routed_scaling_factor=float("nan")), dict(top_k=33)])
+def test_invalid_configs_rejected(bad):
+    assert moe.moe_workspace_bytes(_glm(**bad), 8) == 0
+
+
+def test_validation_before_any_device_work():
+    c = _glm().c()
+    w = L.moe_layer_weights()
+    # null weights / inputs are rejected on the host
+    rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(w), None, 4, None, None, 0, None, None)
+    assert rc == L.MOE_E_NULL
+    bad = _glm(hidden=100).c()
+    rc = L._lib.moe_layer_forward(ctypes.byref(bad), ctypes.byref(w), None, 4, None, None, 0, None, None)
+    assert rc == L.MOE_E_SHAPE
+    rc = L._lib.moe_quantize_int4(None, 64, 32, None, None, None)
+    assert rc == L.MOE_E_NULL
+    dummy = ctypes.c_void_p(256)
+    rc = L._lib.moe_quantize_int4(dummy, 63, 32, dummy, dummy, None)
+    assert rc == L.MOE_E_SHAPE
+    rc = L._lib.moe_quantize_q8_0(dummy, 33, dummy, dummy, None)
+    assert rc == L.MOE_E_SHAPE
+    # workspace too small / misaligned, checked before launch
+    x = ctypes.c_void_p(4096)
+    wts = L.moe_layer_weights(*([4096] * 10))
+    rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(wts), x, 4, x, x, 16, None, None)
+    assert rc == L.MOE_E_WORKSPACE
+    rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(wts), x, 4, x, ctypes.c_void_p(4100), 1 << 40,
+                                  None, None)
+    assert rc == L.MOE_E_WORKSPACE
+    rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(wts), x, 0, x, x, 1 << 40, None, None)
+    assert rc == L.MOE_E_SHAPE
