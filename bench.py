@@ -172,7 +172,7 @@ def main():
     stage_ms = prof.mean(0)
     # dominant kernel: the gate-up launch of the path that moves most bytes
     if args.workload == "prefill":
-        kidx, kname = 5, "k_gateup_mfma"
+        kidx, kname = 6, "k_gateup_mfma"
         ops = np.array([2.0 * s["mfma_tokens"] * 2 * I * H for s in stats])
         kt = prof[:, kidx] / 1e3
         achieved = float(np.mean(ops / kt) / 1e12)

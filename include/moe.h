@@ -29,8 +29,12 @@
  *    returns an error has left the stream untouched.
  *  - Return value: MOE_OK (0) or a negative MOE_E_* code. After MOE_E_HIP,
  *    moe_last_hip_error() returns the hipError_t that caused it.
- *  - The forward path allocates no memory: the caller passes a workspace of at
- *    least moe_workspace_bytes() bytes (device, 256-byte aligned).
+ *  - The forward path allocates no device memory: the caller passes a
+ *    workspace of at least moe_workspace_bytes() bytes (device, 256-byte
+ *    aligned). Buckets large enough for the int8-MFMA path run on a helper
+ *    stream that forks from and joins back into the caller's stream; the
+ *    helper stream and two events are created on first use per (device,
+ *    stream) and kept until the process ends.
  *  - Stateless calls are re-entrant on distinct streams; a cache object is not
  *    thread-safe.
  *
@@ -225,17 +229,30 @@ int32_t moe_expert_cache_stats(const moe_expert_cache* cache, moe_cache_stats* o
 void moe_expert_cache_destroy(moe_expert_cache* cache);
 
 /* ------------------------------------------------------------------------
- * Stage timing for measurement: when enabled, moe_layer_forward records a HIP
- * event pair around each stage on its stream. moe_prof_read synchronizes on
- * the recorded events and returns per-call milliseconds, [n_calls][MOE_N_STAGES]
- * (host), in the order router-logits, top-k, dispatch, q8-x, gate-up GEMV,
- * gate-up MFMA, down GEMV, down MFMA, combine (a stage with no launch reads
- * near 0). Process-wide, not thread-safe; for benchmarks only.
+ * Stage timing for measurement: when enabled, moe_layer_forward records HIP
+ * events around each stage on the stream that runs it. moe_prof_read
+ * synchronizes on them and returns per-call milliseconds,
+ * [n_calls][MOE_N_STAGES] (host), in the order router-logits, top-k, dispatch,
+ * q8-x, GEMV gate-up, GEMV down (caller's stream), MFMA gate-up, MFMA down
+ * (helper stream, overlapping the GEMV stages; 0 when no bucket reaches the
+ * MFMA threshold), combine. Process-wide, not thread-safe; for benchmarks only.
  * ---------------------------------------------------------------------- */
 #define MOE_N_STAGES 9
 int32_t moe_prof_enable(int32_t max_calls);
 int32_t moe_prof_read(float* ms /* host */, int32_t max_calls, int32_t* n_calls /* host */);
 void moe_prof_disable(void);
+
+/* ------------------------------------------------------------------------
+ * Memory microbenchmarks (measurement only): a streaming read of `bytes`
+ * (multiple of 16) from buf with `blocks` workgroups of 256 lanes, each lane
+ * keeping `unroll` (1, 2, 4 or 8) 16-byte loads in flight; sink is a device
+ * word that is written only in a case the data never produces. And a plain
+ * device-to-device copy. Used to measure achievable HBM bandwidth and to
+ * calibrate hardware byte counters on a known byte count.
+ * ---------------------------------------------------------------------- */
+int32_t moe_membench_read(const void* buf, size_t bytes, int32_t blocks, int32_t unroll, uint32_t* sink,
+                          hipStream_t stream);
+int32_t moe_membench_copy(const void* src, void* dst, size_t bytes, int32_t blocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

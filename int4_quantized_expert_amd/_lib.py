@@ -17,7 +17,7 @@ MOE_OK, MOE_E_NULL, MOE_E_SHAPE, MOE_E_WORKSPACE, MOE_E_HIP, MOE_E_NOMEM, MOE_E_
     0, -1, -2, -3, -4, -5, -6, -7)
 MOE_TIE_EXPERT, MOE_TIE_GROUP, MOE_TIE_ORDER = 1, 2, 4
 MOE_N_STAGES = 9
-STAGES = ("router", "topk", "dispatch", "q8_x", "gateup_gemv", "gateup_mfma", "down_gemv", "down_mfma",
+STAGES = ("router", "topk", "dispatch", "q8_x", "gateup_gemv", "down_gemv", "gateup_mfma", "down_mfma",
           "combine")
 
 if not os.path.exists(LIB_PATH):
@@ -75,11 +75,13 @@ _sig("moe_expert_cache_destroy", None, [P])
 _sig("moe_prof_enable", I32, [I32])
 _sig("moe_prof_read", I32, [P, I32, P])
 _sig("moe_prof_disable", None, [])
+_sig("moe_membench_read", I32, [P, SZ, I32, I32, P, P])
+_sig("moe_membench_copy", I32, [P, P, SZ, I32, P])
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_workspace_bytes", "moe_quantize_int4",
             "moe_quantize_q8_0", "moe_router", "moe_dispatch", "moe_layer_forward", "moe_expert_cache_create",
             "moe_expert_cache_forward", "moe_expert_cache_stats", "moe_expert_cache_destroy", "moe_prof_enable",
-            "moe_prof_read", "moe_prof_disable")
+            "moe_prof_read", "moe_prof_disable", "moe_membench_read", "moe_membench_copy")
 
 
 class MoeError(RuntimeError):
@@ -201,3 +203,13 @@ def moe_prof_read(max_calls: int):
 
 def moe_prof_disable():
     _lib.moe_prof_disable()
+
+
+def moe_membench_read(buf, blocks: int, unroll: int, sink, stream=None):
+    return _check("moe_membench_read", _lib.moe_membench_read(_ptr(buf), buf.numel() * buf.element_size(), blocks,
+                                                              unroll, _ptr(sink), _stream(stream)))
+
+
+def moe_membench_copy(src, dst, blocks: int, stream=None):
+    return _check("moe_membench_copy", _lib.moe_membench_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                                                              blocks, _stream(stream)))

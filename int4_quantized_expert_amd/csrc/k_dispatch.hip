@@ -9,8 +9,9 @@
 // placing its matches with a ballot prefix count — a stable counting sort
 // with no cross-workgroup synchronization and no float atomics. Workgroup 0
 // additionally emits the bucket tables the expert kernels consume: the unique
-// expert list, the GEMV bucket list (buckets below the MFMA threshold) and the
-// MFMA tile list (bucket, first token) pairs.
+// expert list, the GEMV work list ((bucket, first token) pairs in chunks of up
+// to 8 tokens, for buckets below the MFMA threshold) and the MFMA tile list
+// ((bucket, first token) pairs).
 #include "moe_internal.h"
 
 namespace moe {
@@ -133,9 +134,19 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
         bool valid = b < nbk;
         int nb = valid ? (b < nu ? hist[uq[b]] : a.T) : 0;
         bool g = valid && nb < a.gemm_min;
-        uint64_t mask = __ballot(g);
-        if (g) a.gemv[ng + __popcll(mask & lt)] = b;
-        ng += __popcll(mask);
+        int nch = g ? (nb + 7) / 8 : 0;
+        int incg = nch;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          int v = __shfl_up(incg, o);
+          if (lane >= o) incg += v;
+        }
+        const int exg = ng + incg - nch;
+        for (int q = 0; q < nch; ++q) {
+          a.gemv[2 * (exg + q)] = b;
+          a.gemv[2 * (exg + q) + 1] = q * 8;
+        }
+        ng += __shfl(incg, 63);
         int ntile = (valid && !g) ? (nb + a.tok_tile - 1) / a.tok_tile : 0;
         int inc = ntile;
 #pragma unroll
@@ -161,8 +172,8 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
   }
 }
 
-hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, const Layout& L,
-                           char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
+hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
+                           const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
                            int32_t* unique, int32_t* nunique, hipStream_t st) {
   DispatchArgs a;
   a.ids = ids;
@@ -171,7 +182,7 @@ hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int g
   a.E = c.n_experts;
   a.NS = c.n_shared;
   a.gemm_min = gemm_min;
-  a.tok_tile = kMfmaTokTile;
+  a.tok_tile = tok_tile;
   a.counts = counts;
   a.offsets = offsets;
   a.sorted = sorted;

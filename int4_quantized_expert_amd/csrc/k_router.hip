@@ -9,59 +9,161 @@
 // fixed and independent of the number of tokens or a token's place in the
 // batch, so a token routes identically alone or inside any batch: H is split
 // into 64 contiguous chunks; each chunk is summed in ascending h; the 64 chunk
-// sums are added in ascending chunk order. Two kernels evaluate exactly this
-// order — one lane per chunk for small batches (W read once, bandwidth-bound)
-// and an LDS-tiled token x expert kernel for large ones (fp64-FMA-bound).
+// sums are added in ascending chunk order, starting from 0. Two kernel paths
+// evaluate exactly this order — chunk-parallel partial sums plus an ordered
+// reduction for small batches (the router weights are read once,
+// bandwidth-bound) and an LDS-tiled token x expert kernel for large ones
+// (fp64-FMA-bound).
 #include <limits.h>
 
 #include "moe_internal.h"
 
 namespace moe {
 
-constexpr int kRouterTG = 8;  // tokens per wave in the small-batch kernel
+#define CAS __attribute__((address_space(4)))
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Small batches (T < 64): lane = expert, workgroup (y) = one of the 64 chunks,
+// z = a group of kRouterTT tokens. The chunk of the group's activations is
+// staged in LDS (fp64) and read by every lane at the same address; the router
+// row chunk streams through the lane once. Each (token, chunk, expert) partial
+// sum is written in fp64; the top-k kernel adds the 64 partials in ascending
+// chunk order. Workgroups of the first expert group also encode Q8_0 of the
+// activations (blocks j, j+64, ... of each of their tokens), which saves a
+// launch on the latency-bound decode path.
+constexpr int kRouterTT = 16;
+constexpr int kRouterMaxC = 128;  // chunk length staged at once (H <= 8192 in one pass)
+
+__device__ __forceinline__ uint32_t pack4q(int8_t a, int8_t b, int8_t c, int8_t d) {
+  return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
+         ((uint32_t)(uint8_t)d << 24);
+}
 
 template <bool VEC4>
-__global__ __launch_bounds__(64) void k_router_small(const float* __restrict__ x, int T, int H,
-                                                     const float* __restrict__ Wr, int E, float* __restrict__ z) {
-  const int e = blockIdx.x, t0 = blockIdx.y * kRouterTG, lane = threadIdx.x;
+__global__ __launch_bounds__(64) void k_router_part(const float* __restrict__ x, int T, int H,
+                                                    const float* __restrict__ Wr, int E, double* __restrict__ part,
+                                                    int8_t* __restrict__ qx_perm, float* __restrict__ dx,
+                                                    int8_t* __restrict__ qx_nat) {
+  __shared__ double xs[kRouterTT][kRouterMaxC];
+  const int lane = threadIdx.x, e = blockIdx.x * 64 + lane, j = blockIdx.y, t0 = blockIdx.z * kRouterTT;
   const int C = H / 64;
-  const int nt = min(kRouterTG, T - t0);
-  const float* wrow = Wr + (size_t)e * H + (size_t)lane * C;
-  const float* xb = x + (size_t)t0 * H + (size_t)lane * C;
-  double p[kRouterTG];
+  const int ec = min(e, E - 1);
+  const float* wrow = Wr + (size_t)ec * H + (size_t)j * C;
+  double p[kRouterTT];
 #pragma unroll
-  for (int tt = 0; tt < kRouterTG; ++tt) p[tt] = 0.0;
-  if (VEC4) {
-    for (int i = 0; i < C; i += 4) {
-      float4 w4 = *reinterpret_cast<const float4*>(wrow + i);
+  for (int tt = 0; tt < kRouterTT; ++tt) p[tt] = 0.0;
+  for (int c0 = 0; c0 < C; c0 += kRouterMaxC) {
+    const int cw = min(kRouterMaxC, C - c0);
+    // issue every load of the chunk before the first wait: the lane's router
+    // weights (registers) and the group's activations (staged through LDS)
+    float4 wreg[kRouterMaxC / 4];
+    if (VEC4) {
 #pragma unroll
-      for (int tt = 0; tt < kRouterTG; ++tt) {
-        if (tt < nt) {
-          float4 x4 = *reinterpret_cast<const float4*>(xb + (size_t)tt * H + i);
-          p[tt] = fma((double)x4.x, (double)w4.x, p[tt]);
-          p[tt] = fma((double)x4.y, (double)w4.y, p[tt]);
-          p[tt] = fma((double)x4.z, (double)w4.z, p[tt]);
-          p[tt] = fma((double)x4.w, (double)w4.w, p[tt]);
-        }
+      for (int u = 0; u < kRouterMaxC / 4; ++u)
+        if (4 * u < cw) wreg[u] = *reinterpret_cast<const float4*>(wrow + c0 + 4 * u);
+    }
+    float xr[kRouterTT * kRouterMaxC / 64];
+#pragma unroll
+    for (int m = 0; m < kRouterTT * kRouterMaxC / 64; ++m) {
+      const int idx = lane + 64 * m;
+      if (idx < kRouterTT * cw) {
+        const int tt = idx / cw, i = idx - tt * cw;
+        xr[m] = x[(size_t)min(t0 + tt, T - 1) * H + (size_t)j * C + c0 + i];
       }
     }
-  } else {
-    for (int i = 0; i < C; ++i) {
-      double wv = (double)wrow[i];
+    __syncthreads();
 #pragma unroll
-      for (int tt = 0; tt < kRouterTG; ++tt)
-        if (tt < nt) p[tt] = fma((double)xb[(size_t)tt * H + i], wv, p[tt]);
+    for (int m = 0; m < kRouterTT * kRouterMaxC / 64; ++m) {
+      const int idx = lane + 64 * m;
+      if (idx < kRouterTT * cw) {
+        const int tt = idx / cw, i = idx - tt * cw;
+        xs[tt][i] = (double)xr[m];
+      }
+    }
+    __syncthreads();
+    if (VEC4) {
+#pragma unroll
+      for (int u = 0; u < kRouterMaxC / 4; ++u) {
+        if (4 * u < cw) {
+          const int i = 4 * u;
+          const double w0 = wreg[u].x, w1 = wreg[u].y, w2 = wreg[u].z, w3 = wreg[u].w;
+#pragma unroll
+          for (int tt = 0; tt < kRouterTT; ++tt) {
+            p[tt] = fma(xs[tt][i], w0, p[tt]);
+            p[tt] = fma(xs[tt][i + 1], w1, p[tt]);
+            p[tt] = fma(xs[tt][i + 2], w2, p[tt]);
+            p[tt] = fma(xs[tt][i + 3], w3, p[tt]);
+          }
+        }
+      }
+    } else {
+      for (int i = 0; i < cw; ++i) {
+        const double wv = (double)wrow[c0 + i];
+#pragma unroll
+        for (int tt = 0; tt < kRouterTT; ++tt) p[tt] = fma(xs[tt][i], wv, p[tt]);
+      }
     }
   }
-  __shared__ double part[kRouterTG][64];
+  if (e < E) {
 #pragma unroll
-  for (int tt = 0; tt < kRouterTG; ++tt) part[tt][lane] = p[tt];
-  __syncthreads();
-  if (lane < nt) {
-    double tot = 0.0;
-    for (int j = 0; j < 64; ++j) tot += part[lane][j];
-    z[(size_t)(t0 + lane) * E + e] = (float)tot;
+    for (int tt = 0; tt < kRouterTT; ++tt)
+      if (t0 + tt < T) part[((size_t)(t0 + tt) * 64 + j) * E + e] = p[tt];
   }
+  if (blockIdx.x == 0 && qx_perm) {
+    // Q8_0 of x: lane -> (token, block) pairs of this chunk's block set
+    const int nb = H / 32, nbj = (nb - j + 63) / 64;  // blocks j, j+64, ... of one token
+    for (int idx = lane; idx < kRouterTT * nbj; idx += 64) {
+      const int tt = idx / nbj, bq = j + 64 * (idx - tt * nbj), t = t0 + tt;
+      if (t >= T) continue;
+      const float* src = x + (size_t)t * H + (size_t)bq * 32;
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float4 q4 = reinterpret_cast<const float4*>(src)[i];
+        v[4 * i] = q4.x; v[4 * i + 1] = q4.y; v[4 * i + 2] = q4.z; v[4 * i + 3] = q4.w;
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      const float d = __fdiv_rn(amax, 127.0f);
+      const float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
+      int8_t q[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        float r = roundf(__fmul_rn(v[i], inv));
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q[i] = (int8_t)(int)r;
+      }
+      uint32_t wv[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        wv[2 * g] = pack4q(q[8 * g], q[8 * g + 2], q[8 * g + 4], q[8 * g + 6]);
+        wv[2 * g + 1] = pack4q(q[8 * g + 1], q[8 * g + 3], q[8 * g + 5], q[8 * g + 7]);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(qx_perm + (size_t)t * H + (size_t)bq * 32);
+      dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+      dx[(size_t)t * nb + bq] = d;
+      if (qx_nat) {
+        uint32_t nv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) nv[i] = pack4q(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+        uint4* nd = reinterpret_cast<uint4*>(qx_nat + (size_t)t * H + (size_t)bq * 32);
+        nd[0] = make_uint4(nv[0], nv[1], nv[2], nv[3]);
+        nd[1] = make_uint4(nv[4], nv[5], nv[6], nv[7]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_reduce(const double* __restrict__ part, int T, int E,
+                                                       float* __restrict__ z) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * E) return;
+  const int t = idx / E, e = idx - t * E;
+  double tot = 0.0;
+  for (int j = 0; j < 64; ++j) tot += part[((size_t)t * 64 + j) * E + e];
+  z[idx] = (float)tot;
 }
 
 // Large batches: 64 tokens x 32 experts per workgroup; each thread owns
@@ -123,22 +225,6 @@ __global__ __launch_bounds__(256) void k_router_large(const float* __restrict__ 
       if (e < E) z[(size_t)t * E + e] = (float)tot[a][b];
     }
   }
-}
-
-hipError_t launch_router_logits(const float* x, int T, int H, const float* Wr, int E, float* z,
-                                hipStream_t st) {
-  if (T <= 0) return hipSuccess;
-  if (T < kRT_M) {
-    dim3 grid(E, (T + kRouterTG - 1) / kRouterTG);
-    if ((H / 64) % 4 == 0)
-      k_router_small<true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, z);
-    else
-      k_router_small<false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, z);
-  } else {
-    dim3 grid((T + kRT_M - 1) / kRT_M, (E + kRT_N - 1) / kRT_N);
-    k_router_large<<<grid, 256, 0, st>>>(x, T, H, Wr, E, z);
-  }
-  return hipGetLastError();
 }
 
 // (value descending, index ascending) maximum over the wave; every lane ends
@@ -261,11 +347,198 @@ __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ z, const 
   if (lane == 0 && flags) flags[t] = fl;
 }
 
-hipError_t launch_topk(const float* z, const float* bias, int T, const moe_config& c, int32_t* ids, float* w,
-                       uint8_t* flags, hipStream_t st) {
+// Register-resident top-k for the common shapes: lane l owns the EPL
+// consecutive experts l*EPL .. l*EPL+EPL-1, a group of E/G experts spans an
+// aligned power-of-two set of LG lanes. With PARTS the kernel first adds the
+// router's 64 chunk partials in ascending chunk order (the logit order every
+// router path uses) and rounds once to fp32.
+template <int EPL, bool PARTS>
+__global__ __launch_bounds__(64) void k_topk_fast(const float* __restrict__ z, const double* __restrict__ part,
+                                                  const float* __restrict__ bias, int E, int G, int KG, int K,
+                                                  float rsf, int32_t* __restrict__ ids, float* __restrict__ w,
+                                                  uint8_t* __restrict__ flags) {
+  __shared__ int sel_e[kMaxTopK];
+  __shared__ float sel_c[kMaxTopK];
+  __shared__ float sel_s[kMaxTopK];
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int LG = (E / G) / EPL;
+  const bool has = lane * EPL < E;
+  float s[EPL], c[EPL];
+  if (!PARTS) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = min(lane * EPL + i, E - 1);
+      s[i] = (float)(1.0 / (1.0 + exp(-(double)z[(size_t)t * E + e])));
+      c[i] = has ? __fadd_rn(s[i], bias[e]) : -INFINITY;
+    }
+  } else {
+    // add the 64 chunk partials of each owned expert in ascending chunk order;
+    // loads are issued in batches of 64 doubles per lane before the adds
+    constexpr int JB = EPL >= 64 ? 1 : 64 / EPL;
+    double tot[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) tot[i] = 0.0;
+    for (int jb = 0; jb < 64; jb += JB) {
+      double v[JB][EPL];
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          v[jj][i] = part[((size_t)t * 64 + jb + jj) * E + min(lane * EPL + i, E - 1)];
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) tot[i] += v[jj][i];
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = min(lane * EPL + i, E - 1);
+      s[i] = (float)(1.0 / (1.0 + exp(-(double)(float)tot[i])));
+      c[i] = has ? __fadd_rn(s[i], bias[e]) : -INFINITY;
+    }
+  }
+  // group score: the two largest c of the group (insertion order within the lane,
+  // then pairwise merges across the group's lanes; max/min are exact)
+  float t1 = -INFINITY, t2 = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const float v = c[i];
+    if (v > t1) {
+      t2 = t1;
+      t1 = v;
+    } else if (v > t2) {
+      t2 = v;
+    }
+  }
+  for (int off = 1; off < LG; off <<= 1) {
+    const float o1 = __shfl_xor(t1, off), o2 = __shfl_xor(t2, off);
+    const float n1 = fmaxf(t1, o1), n2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
+    t1 = n1;
+    t2 = n2;
+  }
+  const float gs = __fadd_rn(t1, t2);
+  const int g = lane / LG;
+  const bool rep = has && (lane % LG == 0);
+  bool kept_rep = false;
+  float min_kept = 0.0f;
+  for (int r = 0; r < KG; ++r) {
+    const bool cand = rep && !kept_rep;
+    float v = cand ? gs : -INFINITY;
+    int idx = cand ? g : INT_MAX;
+    wave_argmax(v, idx);
+    if (rep && g == idx) kept_rep = true;
+    min_kept = v;
+  }
+  uint8_t fl = 0;
+  if (KG < G) {
+    const bool cand = rep && !kept_rep;
+    float v = cand ? gs : -INFINITY;
+    int idx = cand ? g : INT_MAX;
+    wave_argmax(v, idx);
+    if ((double)min_kept - (double)v < 1e-6) fl |= MOE_TIE_GROUP;
+  }
+  const bool kept = __shfl((int)kept_rep, g * LG) != 0;
+  uint32_t taken = 0;
+  for (int k = 0; k <= K; ++k) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    if (has && kept) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!((taken >> i) & 1u) && c[i] > bv) {
+          bv = c[i];
+          bi = lane * EPL + i;
+        }
+    }
+    wave_argmax(bv, bi);
+    if (k == K) {  // the best candidate left out: expert-boundary near-tie check
+      if (K < KG * (E / G) && (double)sel_c[K - 1] - (double)bv < 1e-6) fl |= MOE_TIE_EXPERT;
+      break;
+    }
+    const int owner = bi / EPL, slot = bi - owner * EPL;
+    float sv = s[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i)
+      if (i == slot) sv = s[i];
+    sv = __shfl(sv, owner);
+    if (lane == owner) taken |= 1u << slot;
+    if (lane == 0) {
+      sel_e[k] = bi;
+      sel_c[k] = bv;
+      sel_s[k] = sv;
+    }
+    __syncthreads();
+  }
+  for (int k = 0; k + 1 < K; ++k)
+    if ((double)sel_c[k] - (double)sel_c[k + 1] < 1e-6) fl |= MOE_TIE_ORDER;
+  if (lane < K) {
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) sum += (double)sel_s[k];
+    ids[(size_t)t * K + lane] = sel_e[lane];
+    w[(size_t)t * K + lane] = (float)(((double)sel_s[lane] / sum) * (double)rsf);
+  }
+  if (lane == 0 && flags) flags[t] = fl;
+}
+
+static int fast_epl(const moe_config& c) {
+  const int E = c.n_experts, n = E / c.n_group;
+  const int epl = E <= 64 ? 1 : (E + 63) / 64;
+  if (epl != 1 && epl != 2 && epl != 4 && epl != 8 && epl != 16) return 0;
+  if (E % epl != 0 || n % epl != 0) return 0;
+  const int lg = n / epl;
+  if (lg <= 0 || lg > 64 || (lg & (lg - 1)) != 0) return 0;
+  return epl;
+}
+
+template <bool PARTS>
+static void topk_fast_launch(int epl, int T, const float* z, const double* part, const float* bias,
+                             const moe_config& c, int32_t* ids, float* w, uint8_t* flags, hipStream_t st) {
+  const int E = c.n_experts, G = c.n_group, KG = c.topk_group, K = c.top_k;
+  const float r = c.routed_scaling_factor;
+  switch (epl) {
+    case 1: k_topk_fast<1, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
+    case 2: k_topk_fast<2, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
+    case 4: k_topk_fast<4, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
+    case 8: k_topk_fast<8, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
+    default: k_topk_fast<16, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
+  }
+}
+
+// Router + top-k. For T < 64 the logits come as chunk partials and, when
+// qx_perm is given, Q8_0 of x is encoded in the same launch (*q8_done = true).
+hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias, float* z,
+                        double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
+                        int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
+                        hipStream_t st) {
+  if (q8_done) *q8_done = false;
   if (T <= 0) return hipSuccess;
-  k_topk<<<T, 64, 0, st>>>(z, bias, c.n_experts, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, ids,
-                           w, flags);
+  const int H = c.hidden, E = c.n_experts;
+  const int epl = fast_epl(c);
+  if (T < kRT_M) {
+    dim3 grid((E + 63) / 64, 64, (T + kRouterTT - 1) / kRouterTT);
+    if ((H / 64) % 4 == 0)
+      k_router_part<true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    else
+      k_router_part<false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    if (q8_done && qx_perm) *q8_done = true;
+    if (mark) mark(mark_call, 1, st);
+    if (epl) {
+      topk_fast_launch<true>(epl, T, nullptr, part, bias, c, ids, w, flags, st);
+    } else {
+      k_router_reduce<<<(T * E + 255) / 256, 256, 0, st>>>(part, T, E, z);
+      k_topk<<<T, 64, 0, st>>>(z, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, ids, w,
+                               flags);
+    }
+  } else {
+    dim3 grid((T + kRT_M - 1) / kRT_M, (E + kRT_N - 1) / kRT_N);
+    k_router_large<<<grid, 256, 0, st>>>(x, T, H, Wr, E, z);
+    if (mark) mark(mark_call, 1, st);
+    if (epl)
+      topk_fast_launch<false>(epl, T, z, nullptr, bias, c, ids, w, flags, st);
+    else
+      k_topk<<<T, 64, 0, st>>>(z, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, ids, w,
+                               flags);
+  }
   return hipGetLastError();
 }
 

@@ -6,18 +6,15 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "moe_internal.h"
 
 namespace moe {
 
-hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid_gemv, hipStream_t st);
-hipError_t launch_gemv_down(const ExpertArgs& a, int grid_gemv, hipStream_t st);
-hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid_tiles, const int32_t* tiles, const int32_t* n_tiles,
-                              hipStream_t st);
-hipError_t launch_mfma_down(const ExpertArgs& a, int grid_tiles, const int32_t* tiles, const int32_t* n_tiles,
-                            hipStream_t st);
 
 static thread_local int32_t g_last_hip = 0;
 
@@ -54,7 +51,7 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.bk_e = take((size_t)(L.E + L.NS) * 4);
   L.bk_p0 = take((size_t)(L.E + L.NS) * 4);
   L.bk_n = take((size_t)(L.E + L.NS) * 4);
-  L.gemv = take((size_t)(L.E + L.NS) * 4);
+  L.gemv = take((size_t)((L.TK + L.NS * T) / 8 + L.E + 2 * L.NS) * 8);
   L.tiles = take((size_t)L.TILES * 8);
   L.meta = take(sizeof(Meta));
   L.pos_token = take((size_t)L.TK * 4);
@@ -63,6 +60,7 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.qh = take((size_t)L.R * L.I);
   L.dh = take((size_t)L.R * (L.I / 32) * 4);
   L.eout = take((size_t)L.R * L.H * 4);
+  L.part = take(T < 64 ? (size_t)T * 64 * L.E * 8 : 0);
   L.total = off;
   return L;
 }
@@ -97,22 +95,59 @@ static int check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
   return MOE_OK;
 }
 
+// MFMA token tile: 64 tokens per wavefront for large batches, else 32.
+static int token_tile(int64_t T) { return T >= 256 ? 64 : 32; }
+
 static int32_t hip_fail(hipError_t e) {
   g_last_hip = (int32_t)e;
   return MOE_E_HIP;
 }
 
+// ------------------------------------------------------- helper stream (fork/join)
+// The MFMA chain (buckets with many tokens) runs on a helper stream while the
+// GEMV chain runs on the caller's stream; two events fork and join them. One
+// helper stream and its events are created the first time a (device, caller
+// stream) pair needs them and are kept until the process ends.
+struct Helper {
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+static std::mutex g_helper_mu;
+static std::map<std::pair<int, hipStream_t>, Helper> g_helpers;
+
+static hipError_t get_helper(hipStream_t st, Helper* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_helper_mu);
+  auto key = std::make_pair(dev, st);
+  auto it = g_helpers.find(key);
+  if (it == g_helpers.end()) {
+    Helper h;
+    if ((e = hipStreamCreateWithFlags(&h.side, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&h.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&h.join, hipEventDisableTiming)) != hipSuccess) return e;
+    it = g_helpers.emplace(key, h).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
 // ------------------------------------------------------------------ profiling
+// Per call: 9 events on the caller's stream (start, after router, top-k,
+// dispatch, q8-x, GEMV gate-up, GEMV down, after the join, end) and 3 on the
+// helper stream (MFMA chain start, after gate-up, after down).
+constexpr int kProfEv = 12;
 struct Prof {
   bool on = false;
   int max_calls = 0;
   int n = 0;
-  std::vector<hipEvent_t> ev;  // [max_calls][MOE_N_STAGES + 1]
+  std::vector<hipEvent_t> ev;  // [max_calls][kProfEv]
 };
 static Prof g_prof;
 
-static void prof_mark(int call, int stage, hipStream_t st) {
-  if (call >= 0) hipEventRecord(g_prof.ev[(size_t)call * (MOE_N_STAGES + 1) + stage], st);
+static void prof_mark(int call, int idx, hipStream_t st) {
+  if (call >= 0) hipEventRecord(g_prof.ev[(size_t)call * kProfEv + idx], st);
 }
 
 static int prof_begin() {
@@ -175,8 +210,8 @@ int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float
   if ((rc = check_ws(L, ws, ws_bytes))) return rc;
   char* wsb = static_cast<char*>(ws);
   float* z = reinterpret_cast<float*>(wsb + L.z);
-  hipError_t e = launch_router_logits(x, T, cfg->hidden, router_w, cfg->n_experts, z, stream);
-  if (e == hipSuccess) e = launch_topk(z, router_bias, T, *cfg, topk_ids, topk_w, near_tie, stream);
+  hipError_t e = launch_route(x, T, *cfg, router_w, router_bias, z, reinterpret_cast<double*>(wsb + L.part), topk_ids,
+                              topk_w, near_tie, nullptr, nullptr, nullptr, nullptr, -1, nullptr, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
@@ -190,7 +225,7 @@ int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, 
   Layout L = make_layout(*cfg, T);
   if ((rc = check_ws(L, ws, ws_bytes))) return rc;
   int gemm_min = cfg->gemm_min_tokens > 0 ? cfg->gemm_min_tokens : kDefaultGemmMin;
-  hipError_t e = launch_dispatch(topk_ids, T, *cfg, gemm_min, L, static_cast<char*>(ws), counts, offsets,
+  hipError_t e = launch_dispatch(topk_ids, T, *cfg, gemm_min, token_tile(T), L, static_cast<char*>(ws), counts, offsets,
                                  sorted_slots, slot_pos, unique_ids, n_unique, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
@@ -266,44 +301,78 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   } else {
     a.sum_slot = -1;
   }
-  const int grid_gemv = (int)L.NB;
-  const int grid_tiles = (T >= gemm_min) ? (int)L.TILES : 0;
+  const int tok_tile = token_tile(T);
+  const int64_t mfma_buckets = std::min<int64_t>(L.E, L.TK / gemm_min) + (T >= gemm_min ? L.NS : 0);
+  const int grid_tiles =
+      (T >= gemm_min) ? (int)(L.TK / tok_tile + mfma_buckets + L.NS * ((T + tok_tile - 1) / tok_tile)) : 0;
+  // GEMV work items: one per bucket when buckets below the threshold hold at most 8 tokens
+  const int64_t gemv_buckets = std::min<int64_t>(L.E, L.TK) + (T < gemm_min ? L.NS : 0);
+  const int grid_gemv =
+      (int)(gemm_min <= 9 ? gemv_buckets : (L.TK + (T < gemm_min ? L.NS * T : 0)) / 8 + gemv_buckets);
   const int32_t* tiles = reinterpret_cast<const int32_t*>(wsb + L.tiles);
   const int32_t* n_tiles = &meta->n_tiles;
+
+  // few buckets: 4 lanes per row so the GEMV kernels still fill the GPU
+  // (each projection needs an even number of 4-block rounds)
+  const bool few = L.TK + L.NS <= 40;
+  const bool quad_gu = few && (cfg->hidden / 32) % 8 == 0;
+  const bool quad_dn = few && (cfg->inter / 32) % 8 == 0;
+  Helper hp;
+  const bool fork = grid_tiles > 0;
+  if (fork) {
+    hipError_t he = get_helper(stream, &hp);
+    if (he != hipSuccess) return hip_fail(he);
+  }
 
   const int call = prof_begin();
   hipError_t e = hipSuccess;
   prof_mark(call, 0, stream);
-  e = launch_router_logits(x, T, cfg->hidden, wts->router_w, cfg->n_experts, z, stream);
-  prof_mark(call, 1, stream);
-  if (e == hipSuccess) e = launch_topk(z, wts->router_bias, T, *cfg, ids, w, flags, stream);
+  bool q8_done = false;
+  int8_t* qx_ws = reinterpret_cast<int8_t*>(wsb + L.qx);
+  float* dx_ws = reinterpret_cast<float*>(wsb + L.dx);
+  e = launch_route(x, T, *cfg, wts->router_w, wts->router_bias, z, reinterpret_cast<double*>(wsb + L.part), ids, w,
+                   flags, qx_ws, dx_ws, tp ? tp->qx : nullptr, &q8_done, call, prof_mark, stream);
   prof_mark(call, 2, stream);
   if (e == hipSuccess)
-    e = launch_dispatch(ids, T, *cfg, gemm_min, L, wsb, counts, offsets, sorted, slotpos, unique, nunique, stream);
+    e = launch_dispatch(ids, T, *cfg, gemm_min, tok_tile, L, wsb, counts, offsets, sorted, slotpos, unique, nunique,
+                        stream);
   prof_mark(call, 3, stream);
-  if (e == hipSuccess)
-    e = launch_q8_0_x(x, T, cfg->hidden, reinterpret_cast<int8_t*>(wsb + L.qx), reinterpret_cast<float*>(wsb + L.dx),
-                      tp ? tp->qx : nullptr, stream);
+  if (e == hipSuccess && !q8_done) e = launch_q8_0_x(x, T, cfg->hidden, qx_ws, dx_ws, tp ? tp->qx : nullptr, stream);
   if (e == hipSuccess && tp && tp->dx)
-    e = hipMemcpyAsync(tp->dx, wsb + L.dx, (size_t)T * (cfg->hidden / 32) * 4, hipMemcpyDeviceToDevice, stream);
+    e = hipMemcpyAsync(tp->dx, dx_ws, (size_t)T * (cfg->hidden / 32) * 4, hipMemcpyDeviceToDevice, stream);
   prof_mark(call, 4, stream);
-  if (e == hipSuccess) e = launch_gemv_gateup(a, grid_gemv, stream);
+  if (e == hipSuccess && fork) {
+    e = hipEventRecord(hp.fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.fork, 0);
+    prof_mark(call, 9, hp.side);
+    if (e == hipSuccess) e = launch_mfma_gateup(a, grid_tiles, tok_tile / 32, tiles, n_tiles, hp.side);
+    prof_mark(call, 10, hp.side);
+    if (e == hipSuccess) e = launch_mfma_down(a, grid_tiles, tok_tile / 32, tiles, n_tiles, hp.side);
+    prof_mark(call, 11, hp.side);
+  }
+  if (e == hipSuccess) e = launch_gemv_gateup(a, grid_gemv, quad_gu, stream);
   prof_mark(call, 5, stream);
-  if (e == hipSuccess) e = launch_mfma_gateup(a, grid_tiles, tiles, n_tiles, stream);
+  if (e == hipSuccess) e = launch_gemv_down(a, grid_gemv, quad_dn, stream);
   prof_mark(call, 6, stream);
-  if (e == hipSuccess) e = launch_gemv_down(a, grid_gemv, stream);
+  if (e == hipSuccess && fork) {
+    e = hipEventRecord(hp.join, hp.side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, hp.join, 0);
+  }
+  if (!fork) {
+    prof_mark(call, 9, stream);
+    prof_mark(call, 10, stream);
+    prof_mark(call, 11, stream);
+  }
   prof_mark(call, 7, stream);
-  if (e == hipSuccess) e = launch_mfma_down(a, grid_tiles, tiles, n_tiles, stream);
-  prof_mark(call, 8, stream);
   if (e == hipSuccess) e = launch_combine(a.eout, w, slotpos, T, *cfg, y, stream);
-  prof_mark(call, 9, stream);
+  prof_mark(call, 8, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
 int32_t moe_prof_enable(int32_t max_calls) {
   if (max_calls <= 0 || max_calls > 100000) return MOE_E_ARG;
   moe_prof_disable();
-  g_prof.ev.resize((size_t)max_calls * (MOE_N_STAGES + 1));
+  g_prof.ev.resize((size_t)max_calls * kProfEv);
   for (auto& ev : g_prof.ev) {
     hipError_t e = hipEventCreate(&ev);
     if (e != hipSuccess) {
@@ -319,14 +388,16 @@ int32_t moe_prof_enable(int32_t max_calls) {
 
 int32_t moe_prof_read(float* ms, int32_t max_calls, int32_t* n_calls) {
   if (!ms || !n_calls) return MOE_E_NULL;
+  // stage -> (first event, second event): main-stream stages, then the MFMA chain, then combine
+  static const int pairs[MOE_N_STAGES][2] = {{0, 1}, {1, 2}, {2, 3}, {3, 4}, {4, 5}, {5, 6}, {9, 10}, {10, 11}, {7, 8}};
   int n = std::min(g_prof.n, max_calls);
   for (int c = 0; c < n; ++c) {
-    hipEvent_t* ev = &g_prof.ev[(size_t)c * (MOE_N_STAGES + 1)];
-    hipError_t e = hipEventSynchronize(ev[MOE_N_STAGES]);
+    hipEvent_t* ev = &g_prof.ev[(size_t)c * kProfEv];
+    hipError_t e = hipEventSynchronize(ev[8]);
     if (e != hipSuccess) return hip_fail(e);
     for (int s = 0; s < MOE_N_STAGES; ++s) {
       float t = 0.0f;
-      e = hipEventElapsedTime(&t, ev[s], ev[s + 1]);
+      e = hipEventElapsedTime(&t, ev[pairs[s][0]], ev[pairs[s][1]]);
       if (e != hipSuccess) return hip_fail(e);
       ms[(size_t)c * MOE_N_STAGES + s] = t;
     }

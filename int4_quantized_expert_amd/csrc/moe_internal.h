@@ -16,7 +16,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxGroups = 64;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 4;
-constexpr int kMfmaTokTile = 32;     // tokens per int8-MFMA tile
+constexpr int kMfmaTokTile = 32;     // smallest token tile of the int8-MFMA path
 constexpr int kDefaultGemmMin = 8;   // bucket size from which the MFMA path runs
 constexpr int kGemvMaxN = 8;         // tokens a GEMV pass keeps in registers
 
@@ -36,7 +36,7 @@ struct Layout {
   int64_t T = 0, E = 0, K = 0, H = 0, I = 0, NS = 0, TK = 0, R = 0, NB = 0, TILES = 0;
   size_t z = 0, ids = 0, w = 0, flags = 0, counts = 0, offsets = 0, sorted = 0, slotpos = 0, unique = 0,
          nunique = 0, bk_e = 0, bk_p0 = 0, bk_n = 0, gemv = 0, tiles = 0, meta = 0, pos_token = 0, qx = 0,
-         dx = 0, qh = 0, dh = 0, eout = 0, total = 0;
+         dx = 0, qh = 0, dh = 0, eout = 0, part = 0, total = 0;
 };
 
 Layout make_layout(const moe_config& c, int64_t T);
@@ -57,7 +57,7 @@ struct WeightView {
 struct ExpertArgs {
   WeightView wv;
   int32_t E, H, I, K, T, TK;
-  const int32_t* list;        // bucket list (GEMV) or tile list (MFMA: bucket, token start pairs)
+  const int32_t* list;        // GEMV work list: (bucket, first token) pairs, chunks of up to 8 tokens
   const int32_t* list_count;  // device count of list entries
   const int32_t* bk_e;
   const int32_t* bk_p0;
@@ -133,13 +133,19 @@ hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float
 hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hipStream_t st);
 hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed, float* scales,
                              hipStream_t st);
-hipError_t launch_router_logits(const float* x, int T, int H, const float* Wr, int E, float* z,
-                                hipStream_t st);
-hipError_t launch_topk(const float* z, const float* bias, int T, const moe_config& c, int32_t* ids, float* w,
-                       uint8_t* flags, hipStream_t st);
-hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, const Layout& L,
-                           char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
+hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias, float* z,
+                        double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
+                        int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
+                        hipStream_t st);
+hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
+                           const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
                            int32_t* unique, int32_t* nunique, hipStream_t st);
+hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool quad, hipStream_t st);
+hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool quad, hipStream_t st);
+hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
+                              hipStream_t st);
+hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
+                            hipStream_t st);
 hipError_t launch_combine(const float* eout, const float* w, const int32_t* slotpos, int T, const moe_config& c,
                           float* y, hipStream_t st);
 

@@ -113,6 +113,18 @@ def test_router_glm(T):
     assert within_tol(w[clean], rw[clean])
 
 
+def test_router_generic_topk_path():
+    """E=48 in 4 groups of 12 does not fit the register-resident top-k; the LDS fallback must agree too."""
+    sh = synth.Shape(256, 48, 4, 2, 6, 64, 0, 1.5, bias_kind="uniform")
+    for T in (5, 70):
+        x = synth.hidden_states(sh, T, seed=T)
+        ids, w, fl, rids, rw, rfl = _router_case(sh, x)
+        clean = (rfl & (O.TIE_EXPERT | O.TIE_GROUP)) == 0
+        assert np.array_equal(ids[clean], rids[clean])
+        assert within_tol(w[clean], rw[clean])
+        assert np.array_equal(fl, rfl)
+
+
 def test_router_batch_invariance_small_vs_large_kernel():
     """T < 64 and T >= 64 use different kernels; a token's result must not depend on the batch."""
     x = synth.hidden_states(synth.GLM, 80, seed=5)
@@ -191,12 +203,13 @@ def _run_layer(layer, shape, x, gemm_min=0, sum_slot=-1, want_taps=True):
     return _np(y), {k: _np(v) for k, v in bufs.items()}
 
 
+@pytest.mark.parametrize("T", [8, 16])
 @pytest.mark.parametrize("gemm_min", [1000, 1, 4])
-def test_layer_tiny_all_stages(tiny_gpu, tiny_ref, gemm_min):
+def test_layer_tiny_all_stages(tiny_gpu, tiny_ref, gemm_min, T):
     """Every tap bit-exact against the oracle; the GEMV path (gemm_min=1000), the MFMA path (gemm_min=1) and a
-    mix give the same bits."""
+    mix give the same bits. T=8 takes the 4-lanes-per-row GEMV, T=16 the one-lane-per-row GEMV."""
     sh = synth.TINY
-    T, K = 8, sh.top_k
+    K = sh.top_k
     x = synth.hidden_states(sh, T)
     slot = 5
     y, tp = _run_layer(tiny_gpu, sh, x, gemm_min, sum_slot=slot)
