@@ -235,10 +235,14 @@ void moe_expert_cache_destroy(moe_expert_cache* cache);
  * [n_calls][MOE_N_STAGES] (host), in the order router-logits, top-k, dispatch,
  * q8-x, GEMV gate-up, GEMV down (caller's stream), MFMA gate-up, MFMA down
  * (helper stream, overlapping the GEMV stages; 0 when no bucket reaches the
- * MFMA threshold), combine. Process-wide, not thread-safe; for benchmarks only.
+ * MFMA threshold), combine. stage_mask selects the stages to time (bit s =
+ * stage s; 0 selects all): only the events those stages need are recorded, so
+ * a narrow mask keeps the timed stream close to an unprofiled one. Stages left
+ * out read as NaN. Process-wide, not thread-safe; for benchmarks only.
+ * Errors: MOE_E_ARG for max_calls outside 1..100000.
  * ---------------------------------------------------------------------- */
 #define MOE_N_STAGES 9
-int32_t moe_prof_enable(int32_t max_calls);
+int32_t moe_prof_enable(int32_t max_calls, uint32_t stage_mask);
 int32_t moe_prof_read(float* ms /* host */, int32_t max_calls, int32_t* n_calls /* host */);
 void moe_prof_disable(void);
 

@@ -72,7 +72,7 @@ _sig("moe_expert_cache_create", I32, [P, I32, I32, ctypes.POINTER(P)])
 _sig("moe_expert_cache_forward", I32, [P, P, P, P, I32, P, P, SZ, P, P, P, P])
 _sig("moe_expert_cache_stats", I32, [P, P])
 _sig("moe_expert_cache_destroy", None, [P])
-_sig("moe_prof_enable", I32, [I32])
+_sig("moe_prof_enable", I32, [I32, ctypes.c_uint32])
 _sig("moe_prof_read", I32, [P, I32, P])
 _sig("moe_prof_disable", None, [])
 _sig("moe_membench_read", I32, [P, SZ, I32, I32, P, P])
@@ -189,8 +189,10 @@ def moe_layer_forward(cfg: Config, weights: moe_layer_weights, x, y, ws, tap: mo
                                          _stream(stream)))
 
 
-def moe_prof_enable(max_calls: int):
-    return _check("moe_prof_enable", _lib.moe_prof_enable(int(max_calls)))
+def moe_prof_enable(max_calls: int, stages=None):
+    """Time the named stages (names from STAGES; None = all) of the next max_calls forwards."""
+    mask = 0 if stages is None else sum(1 << STAGES.index(n) for n in stages)
+    return _check("moe_prof_enable", _lib.moe_prof_enable(int(max_calls), mask))
 
 
 def moe_prof_read(max_calls: int):

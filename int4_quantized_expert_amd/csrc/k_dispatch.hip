@@ -10,7 +10,7 @@
 // with no cross-workgroup synchronization and no float atomics. Workgroup 0
 // additionally emits the bucket tables the expert kernels consume: the unique
 // expert list, the GEMV work list ((bucket, first token) pairs in chunks of up
-// to 8 tokens, for buckets below the MFMA threshold) and the MFMA tile list
+// to kGemvMaxN tokens, for buckets below the MFMA threshold) and the MFMA tile list
 // ((bucket, first token) pairs).
 #include "moe_internal.h"
 
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
         bool valid = b < nbk;
         int nb = valid ? (b < nu ? hist[uq[b]] : a.T) : 0;
         bool g = valid && nb < a.gemm_min;
-        int nch = g ? (nb + 7) / 8 : 0;
+        int nch = g ? (nb + kGemvMaxN - 1) / kGemvMaxN : 0;
         int incg = nch;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
         const int exg = ng + incg - nch;
         for (int q = 0; q < nch; ++q) {
           a.gemv[2 * (exg + q)] = b;
-          a.gemv[2 * (exg + q) + 1] = q * 8;
+          a.gemv[2 * (exg + q) + 1] = q * kGemvMaxN;
         }
         ng += __shfl(incg, 63);
         int ntile = (valid && !g) ? (nb + a.tok_tile - 1) / a.tok_tile : 0;

@@ -11,13 +11,9 @@
 // Grids are sized for the worst case and workgroups beyond the device-side
 // counts exit at once, so the bucket structure never travels back to the host.
 //
-// GEMV (few tokens, HBM-bound): one lane owns one weight row; the row-tiled
-// layout makes each 16-byte block load of a wavefront one contiguous 1 KB
-// segment; a ring of PF blocks is kept in flight per lane. A word of 8
-// nibbles splits with a shift and two masks into two words of int8 lanes
-// holding 16*q; v_dot4 multiplies them against the activation codes, which are
-// stored permuted to match and are read with scalar loads (the same for every
-// lane); the block sum is shifted right by 4 (exact).
+// GEMV (few tokens, HBM-bound): one lane owns one weight row of a 64-row
+// tile; the tile's eight wavefronts take its K blocks round-robin and merge
+// their exact block sums through LDS (details at the GEMV section).
 //
 // MFMA (many tokens): v_mfma_i32_32x32x32_i8 contracts exactly one 32-element
 // Q8_0 block, giving the exact int32 block sums of a 32-row x 32-token tile.
@@ -27,9 +23,11 @@
 // codes already have, so A and B pair the same elements register by register.
 // The result is 16 values per lane: column l%32, rows 8*(i/4) + 4*(l/32) + i%4.
 //
-// Both paths run the same fp32 epilogue: acc = fma(d_block, S_block, acc) over
-// ascending blocks from +0, then one multiply by the row scale, so a bucket's
-// result does not depend on the path it takes.
+// Both paths run the same fp32 arithmetic: block b belongs to class b % 8;
+// each class accumulates fma(d_block, S_block, acc) over its blocks in
+// ascending order from +0; the class totals are added in class order from +0;
+// one multiply by the row scale. So a bucket's result does not depend on the
+// path it takes.
 #include "moe_internal.h"
 
 namespace moe {
@@ -137,356 +135,250 @@ __device__ __forceinline__ void store_h_lanes(const ExpertArgs& a, const Bucket&
 }
 
 // ------------------------------------------------------------------ GEMV paths
+// Few tokens per expert: HBM-bound. A 512-lane workgroup owns one 64-row tile
+// (one lane per row); its eight wavefronts are the eight accumulation classes
+// of the dot: wavefront w walks blocks w, w+8, w+16, ... with its own fp32
+// chain, so per step the workgroup reads one contiguous 8 KB run of each
+// weight stream and no wavefront waits for another until the end, where the
+// class totals meet in LDS and are added in class order. Keeping few requests
+// in flight (PF blocks per wavefront) and adjacent is what lets many buckets
+// stream near the HBM ceiling; deep per-lane queues measurably lose.
+//
+// The chunk's activation codes and scales are staged in LDS once; the block a
+// wavefront needs is the same for all its lanes, so those reads broadcast.
+//
+// Unpacking: a word of 8 nibbles splits with a shift and two masks into two
+// words of int8 lanes holding 16*q; v_dot4 multiplies them against the
+// activation codes, which are stored permuted to match; the block sum is
+// shifted right by 4 (exact).
+constexpr int kGW = kDotClasses;  // wavefronts per tile
+constexpr int kGemvThreads = 64 * kGW;
 
-// N tokens per pass (nn <= N are real; the rest repeat the last real token and
-// are not stored).
-template <int N, int PF, bool TAP>
-__device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
-                                                const uint8_t* w13, const float* s13, int tile, int lane) {
-  const int H = a.H, I = a.I, nb = H / 32;
-  const int r = tile * 64 + lane;
-  const uint8_t* gbase = w13 + (size_t)tile * nb * 1024;
-  const uint8_t* ubase = w13 + (size_t)(I / 64 + tile) * nb * 1024;
-  const uint32_t loff = (uint32_t)lane * 16;
-  const CAS v4i* xq[N];
-  const CAS float* xd[N];
-  int tap_i = -1;
+// Bytes of dynamic LDS for a GEMV launch whose chunks hold at most n tokens
+// (rounded up to the instantiated 1, 2 or 4) over K inputs; pairs = outputs per
+// token (2 for gate/up, 1 for down).
+static inline size_t gemv_lds_bytes(int n, int K, int pairs) {
+  const int nc = n <= 1 ? 1 : (n <= 2 ? 2 : kGemvMaxN);
+  const size_t stage = (size_t)nc * ((size_t)K + (size_t)(K / 32) * 4);
+  const size_t part = (size_t)kGW * pairs * nc * 64 * 4;
+  return stage > part ? stage : part;
+}
+
+// Stage codes [N][K] and scales [N][K/32] of the chunk's N (padded) tokens.
+template <int N>
+__device__ __forceinline__ void stage_codes(const int8_t* const (&src)[N], const float* const (&dsrc)[N], int K,
+                                            int8_t* xs, float* xd) {
+  const int nb = K / 32;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const int p = k.p0 + c0 + min(i, nn - 1);
-    const int tok = token_of(a, k, p);
-    xq[i] = cptr(reinterpret_cast<const v4i*>(a.qx + (size_t)tok * H));
-    xd[i] = cptr(a.dx + (size_t)tok * nb);
-    if (TAP && i < nn && slot_of(a, k, p) == a.sum_slot) tap_i = i;
+    const v4i* s4 = reinterpret_cast<const v4i*>(src[i]);
+    v4i* d4 = reinterpret_cast<v4i*>(xs + (size_t)i * K);
+    for (int v = threadIdx.x; v < K / 16; v += kGemvThreads) d4[v] = s4[v];
+    for (int v = threadIdx.x; v < nb; v += kGemvThreads) xd[i * nb + v] = dsrc[i][v];
+  }
+  __syncthreads();
+}
+
+template <int N, int PF, bool TAP>
+__device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
+                                                const uint8_t* w13, const float* s13, int tile, char* lds) {
+  const int H = a.H, I = a.I, nb = H / 32;
+  // the wavefront index is uniform: say so, so that its branches stay scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = tile * 64 + lane;
+  int8_t* xs = reinterpret_cast<int8_t*>(lds);
+  float* xd = reinterpret_cast<float*>(lds + (size_t)N * H);
+  {
+    const int8_t* src[N];
+    const float* dsrc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int tok = token_of(a, k, k.p0 + c0 + min(i, nn - 1));
+      src[i] = a.qx + (size_t)tok * H;
+      dsrc[i] = a.dx + (size_t)tok * nb;
+    }
+    stage_codes<N>(src, dsrc, H, xs, xd);
+  }
+  int tap_i = -1;
+  if (TAP) {
+    for (int i = 0; i < nn; ++i)
+      if (slot_of(a, k, k.p0 + c0 + i) == a.sum_slot) tap_i = i;
   }
   float ag[N], au[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) ag[i] = au[i] = 0.0f;
-  uint4 bg[PF], bu[PF];
-#pragma unroll
-  for (int kk = 0; kk < PF; ++kk) {
-    const int bb = min(kk, nb - 1);
-    bg[kk] = *reinterpret_cast<const uint4*>(gbase + (size_t)bb * 1024 + loff);
-    bu[kk] = *reinterpret_cast<const uint4*>(ubase + (size_t)bb * 1024 + loff);
-  }
-  for (int b0 = 0; b0 < nb; b0 += PF) {
+  const int ncls = w < nb ? (nb - w + kGW - 1) / kGW : 0;  // blocks of class w
+  if (ncls > 0) {
+    const uint8_t* gcls = w13 + tb_off(tile, w, nb) + (size_t)lane * 16;
+    const uint8_t* ucls = w13 + tb_off(I / 64 + tile, w, nb) + (size_t)lane * 16;
+    constexpr size_t step = kGW * kBlkStride;  // class stride
+    uint4 bg[PF], bu[PF];
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const int blk = b0 + kk;
-      const uint4 g4 = bg[kk], u4 = bu[kk];
-      // prefetch PF blocks ahead; past the end, re-read the last block (a cache hit)
-      const int nxt = min(blk + PF, nb - 1);
-      bg[kk] = *reinterpret_cast<const uint4*>(gbase + (size_t)nxt * 1024 + loff);
-      bu[kk] = *reinterpret_cast<const uint4*>(ubase + (size_t)nxt * 1024 + loff);
-      int gl[4], gh[4], ul[4], uh[4];
-      split16(g4.x, gl[0], gh[0]);
-      split16(g4.y, gl[1], gh[1]);
-      split16(g4.z, gl[2], gh[2]);
-      split16(g4.w, gl[3], gh[3]);
-      split16(u4.x, ul[0], uh[0]);
-      split16(u4.y, ul[1], uh[1]);
-      split16(u4.z, ul[2], uh[2]);
-      split16(u4.w, ul[3], uh[3]);
+      const size_t off = (size_t)min(kk, ncls - 1) * step;
+      bg[kk] = *reinterpret_cast<const uint4*>(gcls + off);
+      bu[kk] = *reinterpret_cast<const uint4*>(ucls + off);
+    }
+    for (int j0 = 0; j0 < ncls; j0 += PF) {
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const v4i xa = xq[i][2 * blk], xb = xq[i][2 * blk + 1];
-        const float d = xd[i][blk];
-        const int Sg = dot_block16(gl, gh, xa, xb) >> 4;
-        const int Su = dot_block16(ul, uh, xa, xb) >> 4;
-        ag[i] = fmaf(d, (float)Sg, ag[i]);
-        au[i] = fmaf(d, (float)Su, au[i]);
-        if (TAP && i == tap_i) {
-          a.t_gu_sums[(size_t)r * nb + blk] = Sg;
-          a.t_gu_sums[(size_t)(I + r) * nb + blk] = Su;
+      for (int kk = 0; kk < PF; ++kk) {
+        const int j = j0 + kk;
+        const bool live = j < ncls;
+        const int blk = w + kGW * min(j, ncls - 1);
+        const uint4 g4 = bg[kk], u4 = bu[kk];
+        const size_t noff = (size_t)min(j + PF, ncls - 1) * step;  // past the end: a repeat (cache hit)
+        bg[kk] = *reinterpret_cast<const uint4*>(gcls + noff);
+        bu[kk] = *reinterpret_cast<const uint4*>(ucls + noff);
+        int gl[4], gh[4], ul[4], uh[4];
+        split16(g4.x, gl[0], gh[0]);
+        split16(g4.y, gl[1], gh[1]);
+        split16(g4.z, gl[2], gh[2]);
+        split16(g4.w, gl[3], gh[3]);
+        split16(u4.x, ul[0], uh[0]);
+        split16(u4.y, ul[1], uh[1]);
+        split16(u4.z, ul[2], uh[2]);
+        split16(u4.w, ul[3], uh[3]);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)blk * 32);
+          const v4i xa = xb4[0], xb = xb4[1];
+          const float d = xd[i * nb + blk];
+          const int Sg = dot_block16(gl, gh, xa, xb) >> 4;
+          const int Su = dot_block16(ul, uh, xa, xb) >> 4;
+          if (live) {
+            ag[i] = fmaf(d, (float)Sg, ag[i]);
+            au[i] = fmaf(d, (float)Su, au[i]);
+            if (TAP && i == tap_i) {
+              a.t_gu_sums[(size_t)r * nb + blk] = Sg;
+              a.t_gu_sums[(size_t)(I + r) * nb + blk] = Su;
+            }
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  const float sg = s13[r], su = s13[I + r];
+  // class totals meet in LDS: part[class][2*token + projection][row]
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(lds);
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    if (i < nn) store_h_lanes(a, k, k.p0 + c0 + i, r, lane, __fmul_rn(sg, ag[i]), __fmul_rn(su, au[i]));
-}
-
-// Prefetch depths: DEEP blocks for 1-2 tokens, DEEP/2 (at least 2) for more;
-// the host picks DEEP so that it divides the number of blocks.
-template <int DEEP, bool TAP>
-__device__ __forceinline__ void gemv_gateup_chunk(const ExpertArgs& a, const Bucket& k, int c0, const uint8_t* w13,
-                                                  const float* s13, int tile, int lane) {
-  constexpr int HALF = DEEP >= 4 ? DEEP / 2 : DEEP;
-  const int nn = min(8, k.n - c0);
-  if (nn == 1)
-    gemv_gateup_run<1, DEEP, TAP>(a, k, c0, nn, w13, s13, tile, lane);
-  else if (nn == 2)
-    gemv_gateup_run<2, DEEP, TAP>(a, k, c0, nn, w13, s13, tile, lane);
-  else if (nn <= 4)
-    gemv_gateup_run<4, HALF, TAP>(a, k, c0, nn, w13, s13, tile, lane);
-  else
-    gemv_gateup_run<8, HALF, TAP>(a, k, c0, nn, w13, s13, tile, lane);
+  for (int i = 0; i < N; ++i) {
+    part[(w * 2 * N + 2 * i) * 64 + lane] = ag[i];
+    part[(w * 2 * N + 2 * i + 1) * 64 + lane] = au[i];
+  }
+  __syncthreads();
+  if (w < nn) {
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kGW; ++c) {
+      g = __fadd_rn(g, part[(c * 2 * N + 2 * w) * 64 + lane]);
+      u = __fadd_rn(u, part[(c * 2 * N + 2 * w + 1) * 64 + lane]);
+    }
+    store_h_lanes(a, k, k.p0 + c0 + w, r, lane, __fmul_rn(s13[r], g), __fmul_rn(s13[I + r], u));
+  }
 }
 
 template <int N, int PF, bool TAP>
 __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
-                                              const uint8_t* w2, const float* s2, int tile, int lane) {
+                                              const uint8_t* w2, const float* s2, int tile, char* lds) {
   const int H = a.H, I = a.I, nbi = I / 32;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int o = tile * 64 + lane;
-  const uint8_t* wbase = w2 + (size_t)tile * nbi * 1024;
-  const uint32_t loff = (uint32_t)lane * 16;
-  const CAS v4i* hq[N];
-  const CAS float* hd[N];
-  int tap_i = -1;
+  int8_t* hs = reinterpret_cast<int8_t*>(lds);
+  float* hd = reinterpret_cast<float*>(lds + (size_t)N * I);
+  {
+    const int8_t* src[N];
+    const float* dsrc[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int p = k.p0 + c0 + min(i, nn - 1);
-    hq[i] = cptr(reinterpret_cast<const v4i*>(a.qh + (size_t)p * I));
-    hd[i] = cptr(a.dh + (size_t)p * nbi);
-    if (TAP && i < nn && slot_of(a, k, p) == a.sum_slot) tap_i = i;
+    for (int i = 0; i < N; ++i) {
+      const int p = k.p0 + c0 + min(i, nn - 1);
+      src[i] = a.qh + (size_t)p * I;
+      dsrc[i] = a.dh + (size_t)p * nbi;
+    }
+    stage_codes<N>(src, dsrc, I, hs, hd);
+  }
+  int tap_i = -1;
+  if (TAP) {
+    for (int i = 0; i < nn; ++i)
+      if (slot_of(a, k, k.p0 + c0 + i) == a.sum_slot) tap_i = i;
   }
   float acc[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-  uint4 bw[PF];
+  const int ncls = w < nbi ? (nbi - w + kGW - 1) / kGW : 0;
+  if (ncls > 0) {
+    const uint8_t* wcls = w2 + tb_off(tile, w, nbi) + (size_t)lane * 16;
+    constexpr size_t step = kGW * kBlkStride;
+    uint4 bw[PF];
 #pragma unroll
-  for (int kk = 0; kk < PF; ++kk) bw[kk] = *reinterpret_cast<const uint4*>(wbase + (size_t)min(kk, nbi - 1) * 1024 + loff);
-  for (int b0 = 0; b0 < nbi; b0 += PF) {
+    for (int kk = 0; kk < PF; ++kk) bw[kk] = *reinterpret_cast<const uint4*>(wcls + (size_t)min(kk, ncls - 1) * step);
+    for (int j0 = 0; j0 < ncls; j0 += PF) {
 #pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const int blk = b0 + kk;
-      const uint4 w4 = bw[kk];
-      const int nxt = min(blk + PF, nbi - 1);
-      bw[kk] = *reinterpret_cast<const uint4*>(wbase + (size_t)nxt * 1024 + loff);
-      int lo[4], hi[4];
-      split16(w4.x, lo[0], hi[0]);
-      split16(w4.y, lo[1], hi[1]);
-      split16(w4.z, lo[2], hi[2]);
-      split16(w4.w, lo[3], hi[3]);
+      for (int kk = 0; kk < PF; ++kk) {
+        const int j = j0 + kk;
+        const bool live = j < ncls;
+        const int blk = w + kGW * min(j, ncls - 1);
+        const uint4 w4 = bw[kk];
+        bw[kk] = *reinterpret_cast<const uint4*>(wcls + (size_t)min(j + PF, ncls - 1) * step);
+        int lo[4], hi[4];
+        split16(w4.x, lo[0], hi[0]);
+        split16(w4.y, lo[1], hi[1]);
+        split16(w4.z, lo[2], hi[2]);
+        split16(w4.w, lo[3], hi[3]);
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const v4i xa = hq[i][2 * blk], xb = hq[i][2 * blk + 1];
-        const int S = dot_block16(lo, hi, xa, xb) >> 4;
-        acc[i] = fmaf(hd[i][blk], (float)S, acc[i]);
-        if (TAP && i == tap_i) a.t_dn_sums[(size_t)o * nbi + blk] = S;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  const float so = s2[o];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i >= nn) break;
-    const int p = k.p0 + c0 + i;
-    const float e = __fmul_rn(so, acc[i]);
-    a.eout[(size_t)p * H + o] = e;
-    if (a.t_eout) a.t_eout[(size_t)slot_of(a, k, p) * H + o] = e;
-  }
-}
-
-template <int DEEP, bool TAP>
-__device__ __forceinline__ void gemv_down_chunk(const ExpertArgs& a, const Bucket& k, int c0, const uint8_t* w2,
-                                                const float* s2, int tile, int lane) {
-  constexpr int HALF = DEEP >= 4 ? DEEP / 2 : DEEP;
-  const int nn = min(8, k.n - c0);
-  if (nn == 1)
-    gemv_down_run<1, DEEP, TAP>(a, k, c0, nn, w2, s2, tile, lane);
-  else if (nn == 2)
-    gemv_down_run<2, DEEP, TAP>(a, k, c0, nn, w2, s2, tile, lane);
-  else if (nn <= 4)
-    gemv_down_run<4, HALF, TAP>(a, k, c0, nn, w2, s2, tile, lane);
-  else
-    gemv_down_run<8, HALF, TAP>(a, k, c0, nn, w2, s2, tile, lane);
-}
-
-// ------------------------------------------------- GEMV, 4 lanes per row
-// For tiny batches (a few buckets) one lane per row leaves most of the GPU
-// idle. Here a 256-lane workgroup covers 64 rows: the 4 lanes of a quad share
-// a row and take blocks 4r+0..3 of round r. After each round the quad's four
-// exact block sums are broadcast inside the quad (DPP quad permute) and every
-// lane of the quad applies them in ascending block order — the same fp32 chain
-// as the one-lane-per-row path, so results are bit-identical.
-
-__device__ __forceinline__ int quad_bcast(int v, int q) {
-  switch (q) {
-    case 0: return __builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false);
-    case 1: return __builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false);
-    case 2: return __builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false);
-    default: return __builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false);
-  }
-}
-
-template <int N, int PF, bool TAP>
-__device__ __forceinline__ void gemv4_gateup_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
-                                                 const uint8_t* w13, const float* s13, int tile, int8_t* xs) {
-  __shared__ float amax_part[N][4];
-  const int H = a.H, I = a.I, nb = H / 32, rounds = nb / 4;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane & 3;
-  const int rloc = wave * 16 + (lane >> 2);  // row within the 64-row tile
-  const int r = tile * 64 + rloc;
-  const uint8_t* gbase = w13 + (size_t)tile * nb * 1024 + (size_t)rloc * 16 + (size_t)q * 1024;
-  const uint8_t* ubase = w13 + (size_t)(I / 64 + tile) * nb * 1024 + (size_t)rloc * 16 + (size_t)q * 1024;
-  // the tokens' activation codes are staged in LDS once: the four lanes of a
-  // quad read four different blocks, so these reads cannot use scalar loads
-  const CAS float* xd[N];
-  int tap_i = -1;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int p = k.p0 + c0 + min(i, nn - 1);
-    const int tok = token_of(a, k, p);
-    const v4i* src = reinterpret_cast<const v4i*>(a.qx + (size_t)tok * H);
-    v4i* dst = reinterpret_cast<v4i*>(xs + (size_t)i * H);
-    for (int v = tid; v < H / 16; v += 256) dst[v] = src[v];
-    xd[i] = cptr(a.dx + (size_t)tok * nb);
-    if (TAP && i < nn && slot_of(a, k, p) == a.sum_slot) tap_i = i;
-  }
-  __syncthreads();
-  const v4i* xq = reinterpret_cast<const v4i*>(xs);
-  float ag[N], au[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) ag[i] = au[i] = 0.0f;
-  uint4 bg[PF], bu[PF];
-#pragma unroll
-  for (int kk = 0; kk < PF; ++kk) {
-    const int rr = min(kk, rounds - 1);
-    bg[kk] = *reinterpret_cast<const uint4*>(gbase + (size_t)rr * 4096);
-    bu[kk] = *reinterpret_cast<const uint4*>(ubase + (size_t)rr * 4096);
-  }
-  for (int r0 = 0; r0 < rounds; r0 += PF) {
-#pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const int rr = r0 + kk;
-      const uint4 g4 = bg[kk], u4 = bu[kk];
-      const int nxt = min(rr + PF, rounds - 1);
-      bg[kk] = *reinterpret_cast<const uint4*>(gbase + (size_t)nxt * 4096);
-      bu[kk] = *reinterpret_cast<const uint4*>(ubase + (size_t)nxt * 4096);
-      int gl[4], gh[4], ul[4], uh[4];
-      split16(g4.x, gl[0], gh[0]);
-      split16(g4.y, gl[1], gh[1]);
-      split16(g4.z, gl[2], gh[2]);
-      split16(g4.w, gl[3], gh[3]);
-      split16(u4.x, ul[0], uh[0]);
-      split16(u4.y, ul[1], uh[1]);
-      split16(u4.z, ul[2], uh[2]);
-      split16(u4.w, ul[3], uh[3]);
-      const int myblk = 4 * rr + q;
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const v4i xa = xq[i * (H / 16) + 2 * myblk], xb = xq[i * (H / 16) + 2 * myblk + 1];
-        const int Sg = dot_block16(gl, gh, xa, xb) >> 4;
-        const int Su = dot_block16(ul, uh, xa, xb) >> 4;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          const float d = xd[i][4 * rr + qq];
-          const int sg = quad_bcast(Sg, qq), su = quad_bcast(Su, qq);
-          ag[i] = fmaf(d, (float)sg, ag[i]);
-          au[i] = fmaf(d, (float)su, au[i]);
+        for (int i = 0; i < N; ++i) {
+          const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)blk * 32);
+          const int S = dot_block16(lo, hi, hb4[0], hb4[1]) >> 4;
+          if (live) {
+            acc[i] = fmaf(hd[i * nbi + blk], (float)S, acc[i]);
+            if (TAP && i == tap_i) a.t_dn_sums[(size_t)o * nbi + blk] = S;
+          }
         }
-        if (TAP && i == tap_i) {
-          a.t_gu_sums[(size_t)r * nb + myblk] = Sg;
-          a.t_gu_sums[(size_t)(I + r) * nb + myblk] = Su;
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-  // SwiGLU and Q8_0 of h: a 32-row block spans two wavefronts (16 rows each)
-  const float sg = s13[r], su = s13[I + r];
-  float h[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    h[i] = swiglu_f(__fmul_rn(sg, ag[i]), __fmul_rn(su, au[i]));
-    float m = fabsf(h[i]);
-#pragma unroll
-    for (int off = 4; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) amax_part[i][wave] = m;
   }
   __syncthreads();
-  const int hb = r >> 5, mrow = r & 31;
+  float* part = reinterpret_cast<float*>(lds);  // part[class][token][row]
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i >= nn) break;
-    const float amax = fmaxf(amax_part[i][wave & ~1], amax_part[i][wave | 1]);
-    const float d = __fdiv_rn(amax, 127.0f);
-    const float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
-    float rq = roundf(__fmul_rn(h[i], inv));
-    rq = fminf(fmaxf(rq, -127.0f), 127.0f);
-    const int8_t qv = (int8_t)(int)rq;
-    const int p = k.p0 + c0 + i;
-    if (q == 0) {
-      a.qh[(size_t)p * I + hb * 32 + perm32(mrow)] = qv;
-      if (mrow == 0) a.dh[(size_t)p * (I / 32) + hb] = d;
-      if (a.t_h || a.t_qh || a.t_dh) {
-        const int slot = slot_of(a, k, p);
-        if (a.t_h) a.t_h[(size_t)slot * I + r] = h[i];
-        if (a.t_qh) a.t_qh[(size_t)slot * I + r] = qv;
-        if (a.t_dh && mrow == 0) a.t_dh[(size_t)slot * (I / 32) + hb] = d;
-      }
-    }
-  }
-}
-
-template <int N, int PF, bool TAP>
-__device__ __forceinline__ void gemv4_down_run(const ExpertArgs& a, const Bucket& k, int c0, int nn, const uint8_t* w2,
-                                               const float* s2, int tile, int8_t* hs) {
-  const int H = a.H, I = a.I, nbi = I / 32, rounds = nbi / 4;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane & 3;
-  const int rloc = wave * 16 + (lane >> 2);
-  const int o = tile * 64 + rloc;
-  const uint8_t* wbase = w2 + (size_t)tile * nbi * 1024 + (size_t)rloc * 16 + (size_t)q * 1024;
-  const CAS float* hd[N];
-  int tap_i = -1;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int p = k.p0 + c0 + min(i, nn - 1);
-    const v4i* src = reinterpret_cast<const v4i*>(a.qh + (size_t)p * I);
-    v4i* dst = reinterpret_cast<v4i*>(hs + (size_t)i * I);
-    for (int v = tid; v < I / 16; v += 256) dst[v] = src[v];
-    hd[i] = cptr(a.dh + (size_t)p * nbi);
-    if (TAP && i < nn && slot_of(a, k, p) == a.sum_slot) tap_i = i;
-  }
+  for (int i = 0; i < N; ++i) part[(w * N + i) * 64 + lane] = acc[i];
   __syncthreads();
-  const v4i* hq = reinterpret_cast<const v4i*>(hs);
-  float acc[N];
+  if (w < nn) {
+    float e = 0.0f;
 #pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-  uint4 bw[PF];
-#pragma unroll
-  for (int kk = 0; kk < PF; ++kk) bw[kk] = *reinterpret_cast<const uint4*>(wbase + (size_t)min(kk, rounds - 1) * 4096);
-  for (int r0 = 0; r0 < rounds; r0 += PF) {
-#pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const int rr = r0 + kk;
-      const uint4 w4 = bw[kk];
-      const int nxt = min(rr + PF, rounds - 1);
-      bw[kk] = *reinterpret_cast<const uint4*>(wbase + (size_t)nxt * 4096);
-      int lo[4], hi[4];
-      split16(w4.x, lo[0], hi[0]);
-      split16(w4.y, lo[1], hi[1]);
-      split16(w4.z, lo[2], hi[2]);
-      split16(w4.w, lo[3], hi[3]);
-      const int myblk = 4 * rr + q;
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int S = dot_block16(lo, hi, hq[i * (I / 16) + 2 * myblk], hq[i * (I / 16) + 2 * myblk + 1]) >> 4;
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) acc[i] = fmaf(hd[i][4 * rr + qq], (float)quad_bcast(S, qq), acc[i]);
-        if (TAP && i == tap_i) a.t_dn_sums[(size_t)o * nbi + myblk] = S;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  if (q != 0) return;
-  const float so = s2[o];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i >= nn) break;
-    const int p = k.p0 + c0 + i;
-    const float e = __fmul_rn(so, acc[i]);
+    for (int c = 0; c < kGW; ++c) e = __fadd_rn(e, part[(c * N + w) * 64 + lane]);
+    e = __fmul_rn(s2[o], e);
+    const int p = k.p0 + c0 + w;
     a.eout[(size_t)p * H + o] = e;
     if (a.t_eout) a.t_eout[(size_t)slot_of(a, k, p) * H + o] = e;
   }
 }
 
 // ------------------------------------------------------------------ MFMA paths
+// One wavefront walks all K blocks of its tile in class-major order (class 0's
+// blocks ascending, then class 1's, ...), keeps one fp32 chain for the current
+// class and folds it into the running total when the class ends: the same
+// arithmetic as the GEMV path, class by class instead of class per wavefront.
+
+// Block at position i of the class-major order; last = it ends its class.
+__device__ __forceinline__ int class_major_block(int i, int nb, bool& last) {
+  if (nb % kDotClasses == 0) {
+    const int per = nb / kDotClasses;
+    last = (i % per) == per - 1;
+    return (i % per) * kDotClasses + i / per;
+  }
+  for (int c = 0; c < kDotClasses; ++c) {
+    const int n = (nb - c + kDotClasses - 1) / kDotClasses;  // blocks of class c (0 when c >= nb)
+    if (i < n) {
+      last = i == n - 1;
+      return c + kDotClasses * i;
+    }
+    i -= n;
+  }
+  last = true;
+  return nb - 1;
+}
+
 
 // 32 gate rows and the matching 32 up rows per wavefront (one 32x32 MFMA tile
 // each), NTT x 32 tokens. t32 = index of the 32-row block.
@@ -514,21 +406,23 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   const v16i zero = {0};
   {
     const int r0 = tile * 64 + s * 32;
-    const uint8_t* gbase = w13 + (size_t)tile * nb * 1024 + s * 512;
-    const uint8_t* ubase = w13 + (size_t)(I / 64 + tile) * nb * 1024 + s * 512;
-    float ag[NTT][16], au[NTT][16];
+    constexpr size_t bs = kBlkStride;
+    const uint8_t* gbase = w13 + tb_off(tile, 0, nb) + s * 512;
+    const uint8_t* ubase = w13 + tb_off(I / 64 + tile, 0, nb) + s * 512;
+    float ag[NTT][16], au[NTT][16], tg[NTT][16], tu[NTT][16];  // class chains, totals
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ag[tt][i] = au[tt][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) ag[tt][i] = au[tt][i] = tg[tt][i] = tu[tt][i] = 0.0f;
     v2i rg[PF], ru[PF];
     v4i rb[PF][NTT];
     float rd[PF][NTT];
+    bool unused;
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const int bb = min(kk, nb - 1);
-      rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)bb * 1024 + loff);
-      ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)bb * 1024 + loff);
+      const int bb = class_major_block(min(kk, nb - 1), nb, unused);
+      rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)bb * bs + loff);
+      ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)bb * bs + loff);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)bb * 32);
@@ -538,7 +432,8 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
     for (int b0 = 0; b0 < nb; b0 += PF) {
 #pragma unroll
       for (int kk = 0; kk < PF; ++kk) {
-        const int blk = b0 + kk;
+        bool fold;
+        const int blk = class_major_block(b0 + kk, nb, fold);
         const v4i Ag = unpack_a(rg[kk]), Au = unpack_a(ru[kk]);
         v4i bv[NTT];
         float dv[NTT];
@@ -547,9 +442,9 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
           bv[tt] = valid[tt] ? rb[kk][tt] : v4i{0, 0, 0, 0};
           dv[tt] = valid[tt] ? rd[kk][tt] : 0.0f;
         }
-        const int nxt = min(blk + PF, nb - 1);
-        rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)nxt * 1024 + loff);
-        ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)nxt * 1024 + loff);
+        const int nxt = class_major_block(min(b0 + kk + PF, nb - 1), nb, unused);
+        rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)nxt * bs + loff);
+        ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)nxt * bs + loff);
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
           rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)nxt * 32);
@@ -574,6 +469,16 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        if (fold) {
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              tg[tt][i] = __fadd_rn(tg[tt][i], ag[tt][i]);
+              tu[tt][i] = __fadd_rn(tu[tt][i], au[tt][i]);
+              ag[tt][i] = au[tt][i] = 0.0f;
+            }
+        }
       }
     }
     float sg[16], su[16];
@@ -588,7 +493,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
       float amax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        h[i] = swiglu_f(__fmul_rn(sg[i], ag[tt][i]), __fmul_rn(su[i], au[tt][i]));
+        h[i] = swiglu_f(__fmul_rn(sg[i], tg[tt][i]), __fmul_rn(su[i], tu[tt][i]));
         amax = fmaxf(amax, fabsf(h[i]));
         __builtin_amdgcn_sched_barrier(0);  // one fp64 exp at a time keeps the epilogue's registers low
       }
@@ -643,19 +548,21 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   const v16i zero = {0};
   {
     const int r0 = tile * 64 + s * 32;
-    const uint8_t* wbase = w2 + (size_t)tile * nbi * 1024 + s * 512;
-    float acc[NTT][16];
+    constexpr size_t bs = kBlkStride;
+    const uint8_t* wbase = w2 + tb_off(tile, 0, nbi) + s * 512;
+    float acc[NTT][16], tot[NTT][16];  // class chain, total
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[tt][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) acc[tt][i] = tot[tt][i] = 0.0f;
     v2i ra[PF];
     v4i rb[PF][NTT];
     float rd[PF][NTT];
+    bool unused;
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const int bb = min(kk, nbi - 1);
-      ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)bb * 1024 + loff);
+      const int bb = class_major_block(min(kk, nbi - 1), nbi, unused);
+      ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)bb * bs + loff);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)bb * 32);
@@ -665,7 +572,8 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
     for (int b0 = 0; b0 < nbi; b0 += PF) {
 #pragma unroll
       for (int kk = 0; kk < PF; ++kk) {
-        const int blk = b0 + kk;
+        bool fold;
+        const int blk = class_major_block(b0 + kk, nbi, fold);
         const v4i A = unpack_a(ra[kk]);
         v4i bv[NTT];
         float dv[NTT];
@@ -674,8 +582,8 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
           bv[tt] = valid[tt] ? rb[kk][tt] : v4i{0, 0, 0, 0};
           dv[tt] = valid[tt] ? rd[kk][tt] : 0.0f;
         }
-        const int nxt = min(blk + PF, nbi - 1);
-        ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)nxt * 1024 + loff);
+        const int nxt = class_major_block(min(b0 + kk + PF, nbi - 1), nbi, unused);
+        ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)nxt * bs + loff);
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
           rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)nxt * 32);
@@ -692,6 +600,15 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        if (fold) {
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              tot[tt][i] = __fadd_rn(tot[tt][i], acc[tt][i]);
+              acc[tt][i] = 0.0f;
+            }
+        }
       }
     }
     float so[16];
@@ -706,10 +623,10 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float4 v;
-        v.x = __fmul_rn(so[4 * g + 0], acc[tt][4 * g + 0]);
-        v.y = __fmul_rn(so[4 * g + 1], acc[tt][4 * g + 1]);
-        v.z = __fmul_rn(so[4 * g + 2], acc[tt][4 * g + 2]);
-        v.w = __fmul_rn(so[4 * g + 3], acc[tt][4 * g + 3]);
+        v.x = __fmul_rn(so[4 * g + 0], tot[tt][4 * g + 0]);
+        v.y = __fmul_rn(so[4 * g + 1], tot[tt][4 * g + 1]);
+        v.z = __fmul_rn(so[4 * g + 2], tot[tt][4 * g + 2]);
+        v.w = __fmul_rn(so[4 * g + 3], tot[tt][4 * g + 3]);
         const int mm = 8 * g + 4 * half;
         *reinterpret_cast<float4*>(orow + mm) = v;
         if (trow) *reinterpret_cast<float4*>(trow + mm) = v;
@@ -722,29 +639,38 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
 // Separate GEMV and MFMA kernels keep each path's register budget (and so its
 // occupancy) independent; the host runs the two chains on two streams so they
 // overlap. TAP instantiations write block-sum taps and are launched only when
-// those taps are requested. DEEP: GEMV prefetch depth (divides the block
-// count); the MFMA path prefetches 8 blocks for 32-token tiles, 4 for 64.
+// those taps are requested. The MFMA path prefetches 8 blocks for 32-token
+// tiles, 4 for 64.
 
-template <int DEEP, bool TAP>
-__global__ __launch_bounds__(64) void k_gateup_gemv(ExpertArgs a) {
-  const int li = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
+// PF: blocks in flight per wavefront (chosen by the host).
+template <int PF, bool TAP>
+__global__ __launch_bounds__(kGemvThreads) void k_gateup_gemv(ExpertArgs a) {
+  extern __shared__ char gemv_lds[];
+  const int li = blockIdx.y, tile = blockIdx.x;
   if (li >= *cptr(a.list_count)) return;
   const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
   const int c0 = cptr(a.list)[2 * li + 1];
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, (size_t)a.I * a.H);
   const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
-  gemv_gateup_chunk<DEEP, TAP>(a, k, c0, w13, s13, tile, lane);
+  const int nn = min(kGemvMaxN, k.n - c0);
+  if (nn == 1) gemv_gateup_run<1, PF, TAP>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  else if (nn == 2) gemv_gateup_run<2, PF, TAP>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  else gemv_gateup_run<kGemvMaxN, PF, TAP>(a, k, c0, nn, w13, s13, tile, gemv_lds);
 }
 
-template <int DEEP, bool TAP>
-__global__ __launch_bounds__(64) void k_down_gemv(ExpertArgs a) {
-  const int li = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
+template <int PF, bool TAP>
+__global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
+  extern __shared__ char gemv_lds[];
+  const int li = blockIdx.y, tile = blockIdx.x;
   if (li >= *cptr(a.list_count)) return;
   const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
   const int c0 = cptr(a.list)[2 * li + 1];
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, (size_t)a.H * a.I / 2);
   const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
-  gemv_down_chunk<DEEP, TAP>(a, k, c0, w2, s2, tile, lane);
+  const int nn = min(kGemvMaxN, k.n - c0);
+  if (nn == 1) gemv_down_run<1, PF, TAP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else if (nn == 2) gemv_down_run<2, PF, TAP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else gemv_down_run<kGemvMaxN, PF, TAP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
 }
 
 template <int NTT, int MPF, bool TAP>
@@ -771,86 +697,52 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
   mfma_down_tile<NTT, MPF, TAP>(a, k, t0, w2, s2, tile, lane);
 }
 
-// DEEP: prefetch depth in rounds of 4 blocks; the host picks it to divide the
-// round count (8, else 2); more than two tokens use half of it (at least 2).
-template <int DEEP, bool TAP>
-__global__ __launch_bounds__(256) void k_gateup_gemv4(ExpertArgs a) {
-  constexpr int HALF = DEEP >= 4 ? DEEP / 2 : DEEP;
-  const int li = blockIdx.y, tile = blockIdx.x;
-  if (li >= *cptr(a.list_count)) return;
-  const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
-  const int c0 = cptr(a.list)[2 * li + 1];
-  const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, (size_t)a.I * a.H);
-  const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
-  extern __shared__ int8_t xs_dyn[];  // up to 8 tokens x H activation codes
-  const int nn = min(8, k.n - c0);
-  if (nn == 1) gemv4_gateup_run<1, DEEP, TAP>(a, k, c0, nn, w13, s13, tile, xs_dyn);
-  else if (nn == 2) gemv4_gateup_run<2, DEEP, TAP>(a, k, c0, nn, w13, s13, tile, xs_dyn);
-  else if (nn <= 4) gemv4_gateup_run<4, HALF, TAP>(a, k, c0, nn, w13, s13, tile, xs_dyn);
-  else gemv4_gateup_run<8, HALF, TAP>(a, k, c0, nn, w13, s13, tile, xs_dyn);
-}
-
-template <int DEEP, bool TAP>
-__global__ __launch_bounds__(256) void k_down_gemv4(ExpertArgs a) {
-  constexpr int HALF = DEEP >= 4 ? DEEP / 2 : DEEP;
-  const int li = blockIdx.y, tile = blockIdx.x;
-  if (li >= *cptr(a.list_count)) return;
-  const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
-  const int c0 = cptr(a.list)[2 * li + 1];
-  const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, (size_t)a.H * a.I / 2);
-  const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
-  extern __shared__ int8_t hs_dyn[];  // up to 8 positions x I activation codes
-  const int nn = min(8, k.n - c0);
-  if (nn == 1) gemv4_down_run<1, DEEP, TAP>(a, k, c0, nn, w2, s2, tile, hs_dyn);
-  else if (nn == 2) gemv4_down_run<2, DEEP, TAP>(a, k, c0, nn, w2, s2, tile, hs_dyn);
-  else if (nn <= 4) gemv4_down_run<4, HALF, TAP>(a, k, c0, nn, w2, s2, tile, hs_dyn);
-  else gemv4_down_run<8, HALF, TAP>(a, k, c0, nn, w2, s2, tile, hs_dyn);
-}
-
 static bool deep8(int nblocks) { return nblocks % 8 == 0; }
 
-hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool quad, hipStream_t st) {
+// Blocks in flight per wavefront: about 4 KB of weights per wavefront when
+// many buckets stream at once (2 blocks of the two gate/up streams, 4 of the
+// single down stream), half that with a few buckets, where fewer queued
+// requests finish sooner. A depth is used only if it divides the class length.
+constexpr int kPfGateupMany = 2, kPfGateupFew = 1, kPfDownMany = 4, kPfDownFew = 2;
+
+static int gemv_pf(int nblocks, int want) {
+  const int per_class = (nblocks + kGW - 1) / kGW;
+  while (want > 1 && per_class % want != 0) want >>= 1;
+  return want;
+}
+
+template <int PF>
+static void gateup_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_t st) {
+  if (a.t_gu_sums) k_gateup_gemv<PF, true><<<g, kGemvThreads, lds, st>>>(a);
+  else k_gateup_gemv<PF, false><<<g, kGemvThreads, lds, st>>>(a);
+}
+
+template <int PF>
+static void down_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_t st) {
+  if (a.t_dn_sums) k_down_gemv<PF, true><<<g, kGemvThreads, lds, st>>>(a);
+  else k_down_gemv<PF, false><<<g, kGemvThreads, lds, st>>>(a);
+}
+
+hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(a.I / 64, grid);
-  const bool tap = a.t_gu_sums != nullptr;
-  if (quad) {  // requires (H/32/4) even
-    const size_t lds = (size_t)8 * a.H;
-    if (deep8(a.H / 128)) {
-      if (tap) k_gateup_gemv4<8, true><<<g, 256, lds, st>>>(a);
-      else k_gateup_gemv4<8, false><<<g, 256, lds, st>>>(a);
-    } else {
-      if (tap) k_gateup_gemv4<2, true><<<g, 256, lds, st>>>(a);
-      else k_gateup_gemv4<2, false><<<g, 256, lds, st>>>(a);
-    }
-  } else if (deep8(a.H / 32)) {
-    if (tap) k_gateup_gemv<8, true><<<g, 64, 0, st>>>(a);
-    else k_gateup_gemv<8, false><<<g, 64, 0, st>>>(a);
-  } else {
-    if (tap) k_gateup_gemv<2, true><<<g, 64, 0, st>>>(a);
-    else k_gateup_gemv<2, false><<<g, 64, 0, st>>>(a);
+  const size_t lds = gemv_lds_bytes(max_chunk, a.H, 2);
+  switch (gemv_pf(a.H / 32, many ? kPfGateupMany : kPfGateupFew)) {
+    case 4: gateup_gemv_launch<4>(a, g, lds, st); break;
+    case 2: gateup_gemv_launch<2>(a, g, lds, st); break;
+    default: gateup_gemv_launch<1>(a, g, lds, st); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool quad, hipStream_t st) {
+hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(a.H / 64, grid);
-  const bool tap = a.t_dn_sums != nullptr;
-  if (quad) {  // requires (I/32/4) even
-    const size_t lds = (size_t)8 * a.I;
-    if (deep8(a.I / 128)) {
-      if (tap) k_down_gemv4<8, true><<<g, 256, lds, st>>>(a);
-      else k_down_gemv4<8, false><<<g, 256, lds, st>>>(a);
-    } else {
-      if (tap) k_down_gemv4<2, true><<<g, 256, lds, st>>>(a);
-      else k_down_gemv4<2, false><<<g, 256, lds, st>>>(a);
-    }
-  } else if (deep8(a.I / 32)) {
-    if (tap) k_down_gemv<8, true><<<g, 64, 0, st>>>(a);
-    else k_down_gemv<8, false><<<g, 64, 0, st>>>(a);
-  } else {
-    if (tap) k_down_gemv<2, true><<<g, 64, 0, st>>>(a);
-    else k_down_gemv<2, false><<<g, 64, 0, st>>>(a);
+  const size_t lds = gemv_lds_bytes(max_chunk, a.I, 1);
+  switch (gemv_pf(a.I / 32, many ? kPfDownMany : kPfDownFew)) {
+    case 4: down_gemv_launch<4>(a, g, lds, st); break;
+    case 2: down_gemv_launch<2>(a, g, lds, st); break;
+    default: down_gemv_launch<1>(a, g, lds, st); break;
   }
   return hipGetLastError();
 }

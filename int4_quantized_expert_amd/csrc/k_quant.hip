@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ w,
       uint32_t nib = (uint32_t)((int)qf) & 0xFu;
       wv[i >> 3] |= nib << (4 * (i & 7));
     }
-    size_t off = ((size_t)(r / 64) * nb + b) * 1024 + (size_t)(r % 64) * 16;
+    size_t off = tb_off(r / 64, b, nb) + (size_t)(r % 64) * 16;
     *reinterpret_cast<uint4*>(packed + off) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
 }

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -138,16 +139,21 @@ static hipError_t get_helper(hipStream_t st, Helper* out) {
 // dispatch, q8-x, GEMV gate-up, GEMV down, after the join, end) and 3 on the
 // helper stream (MFMA chain start, after gate-up, after down).
 constexpr int kProfEv = 12;
+// stage -> (first event, second event): main-stream stages, then the MFMA chain, then combine
+static const int kStageEv[MOE_N_STAGES][2] = {{0, 1}, {1, 2}, {2, 3}, {3, 4}, {4, 5},
+                                              {5, 6}, {9, 10}, {10, 11}, {7, 8}};
 struct Prof {
   bool on = false;
   int max_calls = 0;
   int n = 0;
+  uint32_t stages = 0;  // timed stages
+  uint32_t events = 0;  // events they need
   std::vector<hipEvent_t> ev;  // [max_calls][kProfEv]
 };
 static Prof g_prof;
 
 static void prof_mark(int call, int idx, hipStream_t st) {
-  if (call >= 0) hipEventRecord(g_prof.ev[(size_t)call * kProfEv + idx], st);
+  if (call >= 0 && (g_prof.events >> idx & 1u)) hipEventRecord(g_prof.ev[(size_t)call * kProfEv + idx], st);
 }
 
 static int prof_begin() {
@@ -305,18 +311,18 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   const int64_t mfma_buckets = std::min<int64_t>(L.E, L.TK / gemm_min) + (T >= gemm_min ? L.NS : 0);
   const int grid_tiles =
       (T >= gemm_min) ? (int)(L.TK / tok_tile + mfma_buckets + L.NS * ((T + tok_tile - 1) / tok_tile)) : 0;
-  // GEMV work items: one per bucket when buckets below the threshold hold at most 8 tokens
+  // GEMV work items: chunks of up to kGemvMaxN tokens of the buckets below the
+  // threshold (one per bucket when no such bucket can hold more)
   const int64_t gemv_buckets = std::min<int64_t>(L.E, L.TK) + (T < gemm_min ? L.NS : 0);
   const int grid_gemv =
-      (int)(gemm_min <= 9 ? gemv_buckets : (L.TK + (T < gemm_min ? L.NS * T : 0)) / 8 + gemv_buckets);
+      (int)(gemm_min <= kGemvMaxN + 1 ? gemv_buckets
+                                      : (L.TK + (T < gemm_min ? L.NS * T : 0)) / kGemvMaxN + gemv_buckets);
+  const int gemv_chunk = std::max(1, std::min({kGemvMaxN, gemm_min - 1, T}));
   const int32_t* tiles = reinterpret_cast<const int32_t*>(wsb + L.tiles);
   const int32_t* n_tiles = &meta->n_tiles;
 
-  // few buckets: 4 lanes per row so the GEMV kernels still fill the GPU
-  // (each projection needs an even number of 4-block rounds)
-  const bool few = L.TK + L.NS <= 40;
-  const bool quad_gu = few && (cfg->hidden / 32) % 8 == 0;
-  const bool quad_dn = few && (cfg->inter / 32) % 8 == 0;
+  // many buckets stream at once: the GEMV keeps more blocks in flight
+  const bool many = L.TK + L.NS > 40;
   Helper hp;
   const bool fork = grid_tiles > 0;
   if (fork) {
@@ -350,9 +356,9 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
     if (e == hipSuccess) e = launch_mfma_down(a, grid_tiles, tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 11, hp.side);
   }
-  if (e == hipSuccess) e = launch_gemv_gateup(a, grid_gemv, quad_gu, stream);
+  if (e == hipSuccess) e = launch_gemv_gateup(a, grid_gemv, many, gemv_chunk, stream);
   prof_mark(call, 5, stream);
-  if (e == hipSuccess) e = launch_gemv_down(a, grid_gemv, quad_dn, stream);
+  if (e == hipSuccess) e = launch_gemv_down(a, grid_gemv, many, gemv_chunk, stream);
   prof_mark(call, 6, stream);
   if (e == hipSuccess && fork) {
     e = hipEventRecord(hp.join, hp.side);
@@ -369,9 +375,14 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
-int32_t moe_prof_enable(int32_t max_calls) {
+int32_t moe_prof_enable(int32_t max_calls, uint32_t stage_mask) {
   if (max_calls <= 0 || max_calls > 100000) return MOE_E_ARG;
   moe_prof_disable();
+  const uint32_t all = (1u << MOE_N_STAGES) - 1u;
+  g_prof.stages = (stage_mask & all) ? (stage_mask & all) : all;
+  g_prof.events = 0;
+  for (int s = 0; s < MOE_N_STAGES; ++s)
+    if (g_prof.stages >> s & 1u) g_prof.events |= (1u << kStageEv[s][0]) | (1u << kStageEv[s][1]);
   g_prof.ev.resize((size_t)max_calls * kProfEv);
   for (auto& ev : g_prof.ev) {
     hipError_t e = hipEventCreate(&ev);
@@ -388,16 +399,18 @@ int32_t moe_prof_enable(int32_t max_calls) {
 
 int32_t moe_prof_read(float* ms, int32_t max_calls, int32_t* n_calls) {
   if (!ms || !n_calls) return MOE_E_NULL;
-  // stage -> (first event, second event): main-stream stages, then the MFMA chain, then combine
-  static const int pairs[MOE_N_STAGES][2] = {{0, 1}, {1, 2}, {2, 3}, {3, 4}, {4, 5}, {5, 6}, {9, 10}, {10, 11}, {7, 8}};
   int n = std::min(g_prof.n, max_calls);
   for (int c = 0; c < n; ++c) {
     hipEvent_t* ev = &g_prof.ev[(size_t)c * kProfEv];
-    hipError_t e = hipEventSynchronize(ev[8]);
-    if (e != hipSuccess) return hip_fail(e);
     for (int s = 0; s < MOE_N_STAGES; ++s) {
-      float t = 0.0f;
-      e = hipEventElapsedTime(&t, ev[pairs[s][0]], ev[pairs[s][1]]);
+      float t = std::numeric_limits<float>::quiet_NaN();
+      if (!(g_prof.stages >> s & 1u)) {
+        ms[(size_t)c * MOE_N_STAGES + s] = t;
+        continue;
+      }
+      hipError_t e = hipEventSynchronize(ev[kStageEv[s][1]]);
+      if (e != hipSuccess) return hip_fail(e);
+      e = hipEventElapsedTime(&t, ev[kStageEv[s][0]], ev[kStageEv[s][1]]);
       if (e != hipSuccess) return hip_fail(e);
       ms[(size_t)c * MOE_N_STAGES + s] = t;
     }
@@ -412,6 +425,7 @@ void moe_prof_disable(void) {
   g_prof.on = false;
   g_prof.n = 0;
   g_prof.max_calls = 0;
+  g_prof.stages = g_prof.events = 0;
 }
 
 }  // extern "C"

@@ -18,7 +18,8 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 4;
 constexpr int kMfmaTokTile = 32;     // smallest token tile of the int8-MFMA path
 constexpr int kDefaultGemmMin = 8;   // bucket size from which the MFMA path runs
-constexpr int kGemvMaxN = 8;         // tokens a GEMV pass keeps in registers
+constexpr int kGemvMaxN = 4;         // tokens per GEMV work item (chunk)
+constexpr int kDotClasses = 8;       // fp32 accumulation classes of a dot: block b is in class b % 8
 
 // Bucket b: routed unique experts b < n_unique (ascending expert id), then the
 // shared experts. bk_e = expert index (E + s for shared expert s), bk_p0 =
@@ -57,7 +58,7 @@ struct WeightView {
 struct ExpertArgs {
   WeightView wv;
   int32_t E, H, I, K, T, TK;
-  const int32_t* list;        // GEMV work list: (bucket, first token) pairs, chunks of up to 8 tokens
+  const int32_t* list;        // GEMV work list: (bucket, first token) pairs, chunks of up to kGemvMaxN tokens
   const int32_t* list_count;  // device count of list entries
   const int32_t* bk_e;
   const int32_t* bk_p0;
@@ -78,6 +79,15 @@ struct ExpertArgs {
   int32_t* t_gu_sums;
   int32_t* t_dn_sums;
 };
+
+// ------------------------------------------------------------ weight layout
+// Int4 matrices are stored in tile-blocks of 64 rows x one 32-element block:
+// 1 KB contiguous, 16 bytes per row in row order. The blocks of one 64-row
+// tile follow each other, so one tile of a matrix is a single contiguous run.
+__host__ __device__ __forceinline__ size_t tb_off(int tile, int blk, int nblocks) {
+  return ((size_t)tile * nblocks + blk) * 1024;
+}
+constexpr size_t kBlkStride = 1024;  // bytes from block b to block b+1 of a tile
 
 // ------------------------------------------------------------ device helpers
 
@@ -140,8 +150,8 @@ hipError_t launch_route(const float* x, int T, const moe_config& c, const float*
 hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
                            const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
                            int32_t* unique, int32_t* nunique, hipStream_t st);
-hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool quad, hipStream_t st);
-hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool quad, hipStream_t st);
+hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
+hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
 hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
                               hipStream_t st);
 hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,

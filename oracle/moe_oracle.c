@@ -230,18 +230,26 @@ void orc_block_sums(const int8_t* a, const int8_t* b, int64_t n, int32_t* S) {
 }
 
 /* Dequant-on-use integer dot ("Show HN", implemented features: int8 x int4
- * integer dots with per-row scales, dequantized on use). Reading of the fp32
- * order: block sums are exact int32; they are scaled by the activation block
- * scale and accumulated in ascending block order with one fused multiply-add
- * each, starting from +0; the row scale multiplies the total once. */
+ * integer dots with per-row scales, dequantized on use). The pages fix no fp32
+ * order; the reading used here: block sums are exact int32; block b belongs to
+ * class b mod ORC_DOT_CLASSES; each class scales its blocks' sums by the
+ * activation block scale and accumulates them in ascending block order with one
+ * fused multiply-add each, starting from +0; the class totals are added in
+ * ascending class order, starting from +0; the row scale multiplies the sum
+ * once. */
 float orc_dot_q4q8(const int8_t* q4, float srow, const int8_t* q8, const float* d8, int64_t n) {
-  float acc = 0.0f;
-  for (int64_t blk = 0; blk < n / 32; ++blk) {
-    int32_t S = 0;
-    for (int i = 0; i < 32; ++i) S += (int32_t)q4[blk * 32 + i] * (int32_t)q8[blk * 32 + i];
-    acc = fmaf(d8[blk], (float)S, acc);
+  const int64_t nb = n / 32;
+  float total = 0.0f;
+  for (int c = 0; c < ORC_DOT_CLASSES; ++c) {
+    float acc = 0.0f;
+    for (int64_t blk = c; blk < nb; blk += ORC_DOT_CLASSES) {
+      int32_t S = 0;
+      for (int i = 0; i < 32; ++i) S += (int32_t)q4[blk * 32 + i] * (int32_t)q8[blk * 32 + i];
+      acc = fmaf(d8[blk], (float)S, acc);
+    }
+    total = total + acc;
   }
-  return srow * acc;
+  return srow * total;
 }
 
 /* SwiGLU gate: silu(g) * u = g * u / (1 + exp(-g)), in fp64, rounded once. */

@@ -68,6 +68,8 @@ int orc_dispatch(int32_t T, int32_t K, int32_t E, const int32_t* ids, int32_t* c
                  int32_t* sorted_slots, int32_t* slot_pos, int32_t* unique_ids, int32_t* n_unique);
 
 void orc_block_sums(const int8_t* a, const int8_t* b, int64_t n, int32_t* S);
+/* fp32 accumulation classes of a dot: block b is in class b mod 8 */
+#define ORC_DOT_CLASSES 8
 float orc_dot_q4q8(const int8_t* q4, float srow, const int8_t* q8, const float* d8, int64_t n);
 float orc_swiglu(float g, float u);
 void orc_expert_token(int32_t H, int32_t I, const int8_t* q13, const float* s13, const int8_t* q2,

@@ -286,6 +286,19 @@ def test_dot_golden_order():
     assert v == np.float32(g["expected"])
 
 
+@pytest.mark.parametrize("case", ["dot_classes", "dot_class_chain_order"])
+def test_dot_golden_classes(case):
+    g = HW[case]
+    nb = g["n_blocks"]
+    q4 = np.zeros(32 * nb, np.int8)
+    q8 = np.zeros(32 * nb, np.int8)
+    for b in range(nb):
+        q4[32 * b] = 1
+        q8[32 * b] = g["block_sums"][b]
+    v = O.dot_q4q8(q4, g["srow"], q8, np.array(g["d8"], np.float32))
+    assert v == np.float32(g["expected"])
+
+
 def test_dot_vs_dequantized_fp64_bound():
     rng = np.random.default_rng(5)
     for n in (64, 2048, 6144):
