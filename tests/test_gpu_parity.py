@@ -206,8 +206,10 @@ def _run_layer(layer, shape, x, gemm_min=0, sum_slot=-1, want_taps=True):
 @pytest.mark.parametrize("T", [8, 16])
 @pytest.mark.parametrize("gemm_min", [1000, 1, 4])
 def test_layer_tiny_all_stages(tiny_gpu, tiny_ref, gemm_min, T):
-    """Every tap bit-exact against the oracle; the GEMV path (gemm_min=1000), the MFMA path (gemm_min=1) and a
-    mix give the same bits. T=8 takes the 4-lanes-per-row GEMV, T=16 the one-lane-per-row GEMV."""
+    """Every tap bit-exact against the oracle; the GEMV path (gemm_min=1000, buckets split into chunks of up to 4
+    tokens), the MFMA path (gemm_min=1) and a mix give the same bits. The tiny shape has one block per
+    accumulation class in gate/up and four empty classes in down; T=8 runs the few-bucket GEMV depth, T=16 the
+    many-bucket one."""
     sh = synth.TINY
     K = sh.top_k
     x = synth.hidden_states(sh, T)
