@@ -46,6 +46,11 @@ def parse():
     ap.add_argument("--gemm-min", type=int, default=0)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run the plain read and copy kernels over 1 GiB (for hardware byte-counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a benchmark run and of "
+                         "a --calibrate run into per-launch HBM bytes of the dominant kernel")
     return ap.parse_args()
 
 
@@ -117,11 +122,107 @@ def cpu_baseline(shape, x, seconds, seed):
                        f"(weight generation excluded)")
 
 
+KERNEL_SRC = os.path.join(ROOT, "int4_quantized_expert_amd", "csrc", "k_expert.hip")
+CAL_BYTES = 1 << 30
+
+
+def source_sha256():
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def calibrate():
+    """Plain streaming kernels of known size: 1 GiB read, 1 GiB copied (read + written)."""
+    import torch
+
+    import int4_quantized_expert_amd as moe
+    src = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(CAL_BYTES, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        moe.moe_membench_read(src, 2048, 1, sink)
+        moe.moe_membench_copy(src, dst, 4096)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate": "k_read 1 GiB x3, k_copy 1 GiB x3"}), flush=True)
+
+
+def _pmc_rows(path):
+    """(kernel name, counter value) per dispatch from a rocprofv3 counter_collection CSV."""
+    import csv
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            name = row["Kernel_Name"]
+            out.setdefault(key, [name, 0.0])
+            out[key][1] += float(row["Counter_Value"])
+    return list(out.values())
+
+
+def _mean_kib(rows, needle):
+    v = [val for name, val in rows if needle in name]
+    return (sum(v) / len(v), len(v)) if v else (float("nan"), 0)
+
+
+def pmc_summary(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """Per-launch HBM bytes of the dominant kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
+    by what the same counter reads for plain kernels of known traffic."""
+    cal_read_kib, _ = _mean_kib(_pmc_rows(cal_fetch_csv), "k_read")
+    cal_copy_kib, _ = _mean_kib(_pmc_rows(cal_write_csv), "k_copy")
+    f_fetch = CAL_BYTES / (cal_read_kib * 1024.0)
+    f_write = CAL_BYTES / (cal_copy_kib * 1024.0)
+    lines = [f"calibration: k_read of {CAL_BYTES} B reads FETCH_SIZE {cal_read_kib:.1f} KiB -> factor {f_fetch:.4f}; "
+             f"k_copy of {CAL_BYTES} B reads WRITE_SIZE {cal_copy_kib:.1f} KiB -> factor {f_write:.4f}", ""]
+    lines.append("| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read B | HBM write B |")
+    lines.append("|---|---|---|---|---|---|")
+    fr, wr = _pmc_rows(fetch_csv), _pmc_rows(write_csv)
+    names = sorted({n for n, _ in fr})
+    res = {}
+    for n in names:
+        fk, cnt = _mean_kib(fr, n)
+        wk, _ = _mean_kib(wr, n)
+        rb, wb = fk * 1024.0 * f_fetch, wk * 1024.0 * f_write
+        short = n.split("(")[0][:60]
+        lines.append(f"| `{short}` | {cnt} | {fk:.1f} | {wk:.1f} | {rb:.4g} | {wb:.4g} |")
+        res[n] = rb + wb
+    print("\n".join(lines))
+    for n, t in res.items():
+        for k in ("k_gateup_gemv", "k_gateup_mfma"):
+            if k in n:
+                print(f"\ntraffic {k} bytes_per_launch {t:.6g}")
+    print(f"source_sha256 {source_sha256()}")
+
+
+def traffic_of(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None once the kernel source has changed."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    val, sha = None, None
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel:
+                val = float(parts[3])
+            if len(parts) == 2 and parts[0] == "source_sha256":
+                sha = parts[1]
+    return val if (val is not None and sha == source_sha256()) else None
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate:
+        calibrate()
+        return
     import torch
 
     import int4_quantized_expert_amd as moe
@@ -187,7 +288,8 @@ def main():
         kt = prof[:, kidx] / 1e3
         achieved = float(np.mean(ops / kt) / 1e12)
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
-                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=None, kernel="k_" + kname,
+                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic_of("k_" + kname, args.workload),
+                    kernel="k_" + kname,
                     kernel_ms=round(float(kt.mean() * 1e3), 4),
                     per_unit="2*2I*H int8 ops per (token, expert) on the MFMA path")
     else:
@@ -196,7 +298,8 @@ def main():
         kt = prof[:, kidx] / 1e3
         achieved = float(np.mean(gb / kt) / 1e9)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, kernel="k_" + kname,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_of("k_" + kname, args.workload),
+                    kernel="k_" + kname, algorithmic_bytes=round(float(gb.mean()), 1),
                     kernel_ms=round(float(kt.mean() * 1e3), 4),
                     per_unit=f"{w13_bytes} B of gate/up weights+scales per GEMV-path expert, plus Q8_0 activations "
                              f"in and Q8_0 h out per token")
