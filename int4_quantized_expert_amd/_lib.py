@@ -215,3 +215,54 @@ def moe_membench_read(buf, blocks: int, unroll: int, sink, stream=None):
 def moe_membench_copy(src, dst, blocks: int, stream=None):
     return _check("moe_membench_copy", _lib.moe_membench_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
                                                               blocks, _stream(stream)))
+
+
+class HostExperts:
+    """Pointer arrays of moe_host_experts over per-expert pinned host tensors (kept alive here)."""
+
+    def __init__(self, w13, s13, w2, s2):
+        self._keep = (list(w13), list(s13), list(w2), list(s2))
+        E = len(self._keep[0])
+        arr = ctypes.c_void_p * E
+        self._arrs = [arr(*[t.data_ptr() for t in lst]) for lst in self._keep]
+        self.c = moe_host_experts(*[ctypes.cast(a, P) for a in self._arrs])
+
+
+class ExpertCache:
+    """moe_expert_cache_* of one layer; destroy() (or garbage collection) releases the slot pool."""
+
+    def __init__(self, cfg: Config, n_slots: int, max_tokens: int):
+        self._h = P()
+        c = cfg.c()
+        _check("moe_expert_cache_create", _lib.moe_expert_cache_create(ctypes.byref(c), int(n_slots),
+                                                                        int(max_tokens), ctypes.byref(self._h)))
+        self.E = cfg.n_experts
+
+    def forward(self, resident, host: HostExperts, x, y, ws, compute, copy, T=None, trace=False):
+        import numpy as np
+        T = x.shape[0] if T is None else T
+        hit = np.zeros(self.E, np.int8) if trace else None
+        slot = np.zeros(self.E, np.int32) if trace else None
+        _check("moe_expert_cache_forward",
+               _lib.moe_expert_cache_forward(self._h, ctypes.byref(resident), ctypes.byref(host.c), _ptr(x), T,
+                                             _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(compute),
+                                             _stream(copy), hit.ctypes.data if trace else None,
+                                             slot.ctypes.data if trace else None))
+        return (hit, slot) if trace else None
+
+    def stats(self):
+        s = moe_cache_stats()
+        _check("moe_expert_cache_stats", _lib.moe_expert_cache_stats(self._h, ctypes.byref(s)))
+        return dict(hits=s.hits, misses=s.misses, evictions=s.evictions, bytes_h2d=s.bytes_h2d, steps=s.steps,
+                    h2d_ms=s.h2d_ms)
+
+    def destroy(self):
+        if self._h:
+            _lib.moe_expert_cache_destroy(self._h)
+            self._h = P()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

@@ -52,7 +52,8 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.bk_e = take((size_t)(L.E + L.NS) * 4);
   L.bk_p0 = take((size_t)(L.E + L.NS) * 4);
   L.bk_n = take((size_t)(L.E + L.NS) * 4);
-  L.gemv = take((size_t)((L.TK + L.NS * T) / 8 + L.E + 2 * L.NS) * 8);
+  // GEMV chunks: sum over buckets of ceil(n/kGemvMaxN) <= tokens/kGemvMaxN + buckets
+  L.gemv = take((size_t)((L.TK + L.NS * T) / kGemvMaxN + std::min<int64_t>(L.E, L.TK) + 2 * L.NS) * 8);
   L.tiles = take((size_t)L.TILES * 8);
   L.meta = take(sizeof(Meta));
   L.pos_token = take((size_t)L.TK * 4);
@@ -99,7 +100,7 @@ static int check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
 // MFMA token tile: 64 tokens per wavefront for large batches, else 32.
 static int token_tile(int64_t T) { return T >= 256 ? 64 : 32; }
 
-static int32_t hip_fail(hipError_t e) {
+int32_t hip_fail(hipError_t e) {
   g_last_hip = (int32_t)e;
   return MOE_E_HIP;
 }
@@ -159,6 +160,108 @@ static void prof_mark(int call, int idx, hipStream_t st) {
 static int prof_begin() {
   if (!g_prof.on || g_prof.n >= g_prof.max_calls) return -1;
   return g_prof.n++;
+}
+
+int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, size_t ws_bytes,
+              const moe_taps* tp, Fwd* f) {
+  int rc;
+  if ((rc = check_tokens(cfg, T))) return rc;
+  f->cfg = cfg;
+  f->T = T;
+  f->L = make_layout(*cfg, T);
+  const Layout& L = f->L;
+  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
+  if (tp && (tp->gateup_sums || tp->down_sums) && (tp->sum_slot < -1 || tp->sum_slot >= L.R)) return MOE_E_ARG;
+  char* wsb = static_cast<char*>(ws);
+  f->wsb = wsb;
+  auto pick = [&](auto* tap_ptr, size_t off) -> decltype(tap_ptr) {
+    return tap_ptr ? tap_ptr : reinterpret_cast<decltype(tap_ptr)>(wsb + off);
+  };
+  f->ids = pick(tp ? tp->topk_ids : (int32_t*)nullptr, L.ids);
+  f->w = pick(tp ? tp->topk_w : (float*)nullptr, L.w);
+  f->flags = pick(tp ? tp->near_tie : (uint8_t*)nullptr, L.flags);
+  f->counts = pick(tp ? tp->counts : (int32_t*)nullptr, L.counts);
+  f->offsets = pick(tp ? tp->offsets : (int32_t*)nullptr, L.offsets);
+  f->sorted = pick(tp ? tp->sorted_slots : (int32_t*)nullptr, L.sorted);
+  f->slotpos = pick(tp ? tp->slot_pos : (int32_t*)nullptr, L.slotpos);
+  f->unique = pick(tp ? tp->unique_ids : (int32_t*)nullptr, L.unique);
+  f->nunique = pick(tp ? tp->n_unique : (int32_t*)nullptr, L.nunique);
+  f->z = reinterpret_cast<float*>(wsb + L.z);
+  f->qx = reinterpret_cast<int8_t*>(wsb + L.qx);
+  f->dx = reinterpret_cast<float*>(wsb + L.dx);
+  f->gemm_min = cfg->gemm_min_tokens > 0 ? cfg->gemm_min_tokens : kDefaultGemmMin;
+  f->tok_tile = token_tile(T);
+  f->tp = tp;
+
+  ExpertArgs& a = f->a;
+  std::memset(&a, 0, sizeof(a));
+  a.wv = wv;
+  a.E = cfg->n_experts;
+  a.H = cfg->hidden;
+  a.I = cfg->inter;
+  a.K = cfg->top_k;
+  a.T = T;
+  a.TK = T * cfg->top_k;
+  Meta* meta = reinterpret_cast<Meta*>(wsb + L.meta);
+  a.list = reinterpret_cast<const int32_t*>(wsb + L.gemv);
+  a.list_count = &meta->n_gemv;
+  a.bk_e = reinterpret_cast<const int32_t*>(wsb + L.bk_e);
+  a.bk_p0 = reinterpret_cast<const int32_t*>(wsb + L.bk_p0);
+  a.bk_n = reinterpret_cast<const int32_t*>(wsb + L.bk_n);
+  a.pos_token = reinterpret_cast<const int32_t*>(wsb + L.pos_token);
+  a.sorted = f->sorted;
+  a.qx = f->qx;
+  a.dx = f->dx;
+  a.qh = reinterpret_cast<int8_t*>(wsb + L.qh);
+  a.dh = reinterpret_cast<float*>(wsb + L.dh);
+  a.eout = reinterpret_cast<float*>(wsb + L.eout);
+  if (tp) {
+    a.t_h = tp->h;
+    a.t_qh = tp->qh;
+    a.t_dh = tp->dh;
+    a.t_eout = tp->e_out;
+    a.sum_slot = tp->sum_slot;
+    a.t_gu_sums = tp->gateup_sums;
+    a.t_dn_sums = tp->down_sums;
+  } else {
+    a.sum_slot = -1;
+  }
+  const int gemm_min = f->gemm_min, tok_tile = f->tok_tile;
+  const int64_t mfma_buckets = std::min<int64_t>(L.E, L.TK / gemm_min) + (T >= gemm_min ? L.NS : 0);
+  f->grid_tiles =
+      (T >= gemm_min) ? (int)(L.TK / tok_tile + mfma_buckets + L.NS * ((T + tok_tile - 1) / tok_tile)) : 0;
+  // GEMV work items: chunks of up to kGemvMaxN tokens of the buckets below the
+  // threshold (one per bucket when no such bucket can hold more)
+  const int64_t gemv_buckets = std::min<int64_t>(L.E, L.TK) + (T < gemm_min ? L.NS : 0);
+  f->grid_gemv =
+      (int)(gemm_min <= kGemvMaxN + 1 ? gemv_buckets
+                                      : (L.TK + (T < gemm_min ? L.NS * T : 0)) / kGemvMaxN + gemv_buckets);
+  f->gemv_chunk = std::max(1, std::min({kGemvMaxN, gemm_min - 1, (int)T}));
+  // many buckets stream at once: the GEMV keeps more blocks in flight
+  f->many = L.TK + L.NS > 40;
+  return MOE_OK;
+}
+
+hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
+                     hipStream_t stream, int call) {
+  const Layout& L = f.L;
+  bool q8_done = false;
+  hipError_t e = launch_route(x, f.T, *f.cfg, router_w, router_bias, f.z, reinterpret_cast<double*>(f.wsb + L.part),
+                              f.ids, f.w, f.flags, f.qx, f.dx, tp ? tp->qx : nullptr, &q8_done, call, prof_mark,
+                              stream);
+  prof_mark(call, 2, stream);
+  if (e == hipSuccess)
+    e = launch_dispatch(f.ids, f.T, *f.cfg, f.gemm_min, f.tok_tile, L, f.wsb, f.counts, f.offsets, f.sorted,
+                        f.slotpos, f.unique, f.nunique, stream);
+  prof_mark(call, 3, stream);
+  if (e == hipSuccess && !q8_done) e = launch_q8_0_x(x, f.T, f.cfg->hidden, f.qx, f.dx, tp ? tp->qx : nullptr, stream);
+  if (e == hipSuccess && tp && tp->dx)
+    e = hipMemcpyAsync(tp->dx, f.dx, (size_t)f.T * (f.cfg->hidden / 32) * 4, hipMemcpyDeviceToDevice, stream);
+  return e;
+}
+
+hipError_t fwd_combine(Fwd& f, float* y, hipStream_t stream) {
+  return launch_combine(f.a.eout, f.w, f.slotpos, f.T, *f.cfg, y, stream);
 }
 
 }  // namespace moe
@@ -243,122 +346,33 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   if (!wts || !x || !y) return MOE_E_NULL;
   if (!wts->router_w || !wts->router_bias || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_E_NULL;
   if (cfg->n_shared > 0 && (!wts->sh_w13 || !wts->sh_s13 || !wts->sh_w2 || !wts->sh_s2)) return MOE_E_NULL;
-  if ((rc = check_tokens(cfg, T))) return rc;
-  Layout L = make_layout(*cfg, T);
-  if ((rc = check_ws(L, ws, ws_bytes))) return rc;
-  if (taps && (taps->gateup_sums || taps->down_sums) && (taps->sum_slot < -1 || taps->sum_slot >= L.R))
-    return MOE_E_ARG;
-
-  char* wsb = static_cast<char*>(ws);
-  const moe_taps* tp = taps;
-  auto pick = [&](auto* tap_ptr, size_t off) -> decltype(tap_ptr) {
-    return tap_ptr ? tap_ptr : reinterpret_cast<decltype(tap_ptr)>(wsb + off);
-  };
-  int32_t* ids = pick(tp ? tp->topk_ids : (int32_t*)nullptr, L.ids);
-  float* w = pick(tp ? tp->topk_w : (float*)nullptr, L.w);
-  uint8_t* flags = pick(tp ? tp->near_tie : (uint8_t*)nullptr, L.flags);
-  int32_t* counts = pick(tp ? tp->counts : (int32_t*)nullptr, L.counts);
-  int32_t* offsets = pick(tp ? tp->offsets : (int32_t*)nullptr, L.offsets);
-  int32_t* sorted = pick(tp ? tp->sorted_slots : (int32_t*)nullptr, L.sorted);
-  int32_t* slotpos = pick(tp ? tp->slot_pos : (int32_t*)nullptr, L.slotpos);
-  int32_t* unique = pick(tp ? tp->unique_ids : (int32_t*)nullptr, L.unique);
-  int32_t* nunique = pick(tp ? tp->n_unique : (int32_t*)nullptr, L.nunique);
-  float* z = reinterpret_cast<float*>(wsb + L.z);
-  const int gemm_min = cfg->gemm_min_tokens > 0 ? cfg->gemm_min_tokens : kDefaultGemmMin;
-
-  ExpertArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.wv.w13 = wts->w13;
-  a.wv.s13 = wts->s13;
-  a.wv.w2 = wts->w2;
-  a.wv.s2 = wts->s2;
-  a.wv.sh_w13 = wts->sh_w13;
-  a.wv.sh_s13 = wts->sh_s13;
-  a.wv.sh_w2 = wts->sh_w2;
-  a.wv.sh_s2 = wts->sh_s2;
-  a.wv.slotmap = nullptr;
-  a.E = cfg->n_experts;
-  a.H = cfg->hidden;
-  a.I = cfg->inter;
-  a.K = cfg->top_k;
-  a.T = T;
-  a.TK = T * cfg->top_k;
-  Meta* meta = reinterpret_cast<Meta*>(wsb + L.meta);
-  a.list = reinterpret_cast<const int32_t*>(wsb + L.gemv);
-  a.list_count = &meta->n_gemv;
-  a.bk_e = reinterpret_cast<const int32_t*>(wsb + L.bk_e);
-  a.bk_p0 = reinterpret_cast<const int32_t*>(wsb + L.bk_p0);
-  a.bk_n = reinterpret_cast<const int32_t*>(wsb + L.bk_n);
-  a.pos_token = reinterpret_cast<const int32_t*>(wsb + L.pos_token);
-  a.sorted = sorted;
-  a.qx = reinterpret_cast<const int8_t*>(wsb + L.qx);
-  a.dx = reinterpret_cast<const float*>(wsb + L.dx);
-  a.qh = reinterpret_cast<int8_t*>(wsb + L.qh);
-  a.dh = reinterpret_cast<float*>(wsb + L.dh);
-  a.eout = reinterpret_cast<float*>(wsb + L.eout);
-  if (tp) {
-    a.t_h = tp->h;
-    a.t_qh = tp->qh;
-    a.t_dh = tp->dh;
-    a.t_eout = tp->e_out;
-    a.sum_slot = tp->sum_slot;
-    a.t_gu_sums = tp->gateup_sums;
-    a.t_dn_sums = tp->down_sums;
-  } else {
-    a.sum_slot = -1;
-  }
-  const int tok_tile = token_tile(T);
-  const int64_t mfma_buckets = std::min<int64_t>(L.E, L.TK / gemm_min) + (T >= gemm_min ? L.NS : 0);
-  const int grid_tiles =
-      (T >= gemm_min) ? (int)(L.TK / tok_tile + mfma_buckets + L.NS * ((T + tok_tile - 1) / tok_tile)) : 0;
-  // GEMV work items: chunks of up to kGemvMaxN tokens of the buckets below the
-  // threshold (one per bucket when no such bucket can hold more)
-  const int64_t gemv_buckets = std::min<int64_t>(L.E, L.TK) + (T < gemm_min ? L.NS : 0);
-  const int grid_gemv =
-      (int)(gemm_min <= kGemvMaxN + 1 ? gemv_buckets
-                                      : (L.TK + (T < gemm_min ? L.NS * T : 0)) / kGemvMaxN + gemv_buckets);
-  const int gemv_chunk = std::max(1, std::min({kGemvMaxN, gemm_min - 1, T}));
-  const int32_t* tiles = reinterpret_cast<const int32_t*>(wsb + L.tiles);
-  const int32_t* n_tiles = &meta->n_tiles;
-
-  // many buckets stream at once: the GEMV keeps more blocks in flight
-  const bool many = L.TK + L.NS > 40;
+  WeightView wv{wts->w13, wts->s13, wts->w2, wts->s2, wts->sh_w13, wts->sh_s13, wts->sh_w2, wts->sh_s2, nullptr};
+  Fwd f;
+  if ((rc = fwd_setup(cfg, wv, T, ws, ws_bytes, taps, &f))) return rc;
   Helper hp;
-  const bool fork = grid_tiles > 0;
+  const bool fork = f.grid_tiles > 0;
   if (fork) {
     hipError_t he = get_helper(stream, &hp);
     if (he != hipSuccess) return hip_fail(he);
   }
-
   const int call = prof_begin();
-  hipError_t e = hipSuccess;
   prof_mark(call, 0, stream);
-  bool q8_done = false;
-  int8_t* qx_ws = reinterpret_cast<int8_t*>(wsb + L.qx);
-  float* dx_ws = reinterpret_cast<float*>(wsb + L.dx);
-  e = launch_route(x, T, *cfg, wts->router_w, wts->router_bias, z, reinterpret_cast<double*>(wsb + L.part), ids, w,
-                   flags, qx_ws, dx_ws, tp ? tp->qx : nullptr, &q8_done, call, prof_mark, stream);
-  prof_mark(call, 2, stream);
-  if (e == hipSuccess)
-    e = launch_dispatch(ids, T, *cfg, gemm_min, tok_tile, L, wsb, counts, offsets, sorted, slotpos, unique, nunique,
-                        stream);
-  prof_mark(call, 3, stream);
-  if (e == hipSuccess && !q8_done) e = launch_q8_0_x(x, T, cfg->hidden, qx_ws, dx_ws, tp ? tp->qx : nullptr, stream);
-  if (e == hipSuccess && tp && tp->dx)
-    e = hipMemcpyAsync(tp->dx, dx_ws, (size_t)T * (cfg->hidden / 32) * 4, hipMemcpyDeviceToDevice, stream);
+  hipError_t e = fwd_front(f, x, wts->router_w, wts->router_bias, taps, stream, call);
   prof_mark(call, 4, stream);
+  const int32_t* tiles = reinterpret_cast<const int32_t*>(f.wsb + f.L.tiles);
+  const int32_t* n_tiles = &reinterpret_cast<Meta*>(f.wsb + f.L.meta)->n_tiles;
   if (e == hipSuccess && fork) {
     e = hipEventRecord(hp.fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.fork, 0);
     prof_mark(call, 9, hp.side);
-    if (e == hipSuccess) e = launch_mfma_gateup(a, grid_tiles, tok_tile / 32, tiles, n_tiles, hp.side);
+    if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 10, hp.side);
-    if (e == hipSuccess) e = launch_mfma_down(a, grid_tiles, tok_tile / 32, tiles, n_tiles, hp.side);
+    if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 11, hp.side);
   }
-  if (e == hipSuccess) e = launch_gemv_gateup(a, grid_gemv, many, gemv_chunk, stream);
+  if (e == hipSuccess) e = launch_gemv_gateup(f.a, f.grid_gemv, f.many, f.gemv_chunk, stream);
   prof_mark(call, 5, stream);
-  if (e == hipSuccess) e = launch_gemv_down(a, grid_gemv, many, gemv_chunk, stream);
+  if (e == hipSuccess) e = launch_gemv_down(f.a, f.grid_gemv, f.many, f.gemv_chunk, stream);
   prof_mark(call, 6, stream);
   if (e == hipSuccess && fork) {
     e = hipEventRecord(hp.join, hp.side);
@@ -370,7 +384,7 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
     prof_mark(call, 11, stream);
   }
   prof_mark(call, 7, stream);
-  if (e == hipSuccess) e = launch_combine(a.eout, w, slotpos, T, *cfg, y, stream);
+  if (e == hipSuccess) e = fwd_combine(f, y, stream);
   prof_mark(call, 8, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }

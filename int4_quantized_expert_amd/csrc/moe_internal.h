@@ -80,6 +80,34 @@ struct ExpertArgs {
   int32_t* t_dn_sums;
 };
 
+// ------------------------------------------------------------ one forward
+// Host-side state of one layer forward: workspace pointers, the expert kernels'
+// arguments and their worst-case grids. moe_layer_forward and the expert cache
+// both build it with fwd_setup and enqueue its stages.
+struct Fwd {
+  const moe_config* cfg = nullptr;
+  int32_t T = 0;
+  Layout L;
+  char* wsb = nullptr;
+  int gemm_min = 0, tok_tile = 0, grid_gemv = 0, grid_tiles = 0, gemv_chunk = 0;
+  bool many = false;
+  int32_t *ids = nullptr, *counts = nullptr, *offsets = nullptr, *sorted = nullptr, *slotpos = nullptr,
+          *unique = nullptr, *nunique = nullptr;
+  float *w = nullptr, *z = nullptr, *dx = nullptr;
+  uint8_t* flags = nullptr;
+  int8_t* qx = nullptr;
+  const moe_taps* tp = nullptr;
+  ExpertArgs a;
+};
+
+int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, size_t ws_bytes, const moe_taps* tp,
+              Fwd* f);
+// router + top-K + dispatch + Q8_0(x)
+hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
+                     hipStream_t stream, int call);
+hipError_t fwd_combine(Fwd& f, float* y, hipStream_t stream);
+int32_t hip_fail(hipError_t e);
+
 // ------------------------------------------------------------ weight layout
 // Int4 matrices are stored in tile-blocks of 64 rows x one 32-element block:
 // 1 KB contiguous, 16 bytes per row in row order. The blocks of one 64-row

@@ -152,3 +152,18 @@ def within_tol(gpu, ref, rel=1e-5, floor=1e-6):
     g = np.asarray(gpu, np.float64)
     r = np.asarray(ref, np.float64)
     return bool(np.all(np.abs(g - r) <= np.maximum(rel * np.abs(r), floor)))
+
+
+def host_experts(layer):
+    """Pinned host copies of a GpuLayer's routed experts, as moe.HostExperts (device layout)."""
+    import torch
+
+    import int4_quantized_expert_amd as moe
+    parts = []
+    for t in (layer.w13, layer.s13, layer.w2, layer.s2):
+        h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        h.copy_(t)
+        parts.append(h)
+    torch.cuda.synchronize()
+    E = layer.w13.shape[0]
+    return moe.HostExperts(*[[p[e] for e in range(E)] for p in parts]), parts
