@@ -10,6 +10,9 @@ per-row scales; Zipf(1.1) correction bias; hidden states N(0,1)):
   decode1   T=1
   mtp192    64 sequences x 3 positions, correlated (rho 0.8)
   prefill   T=2048
+  stack40   40 layers at decode T=32: layers 0-19 resident in HBM, layers 20-39 with
+            routed experts in pinned host memory behind a 64-slot LRU cache each
+            (prints its own line: tokens/s, hit rate, PCIe bytes/s)
 Weights rotate over --copies layer copies (different seeds) and every step
 uses fresh tokens, so the 256 MB last-level cache cannot serve weights from a
 previous step.
@@ -38,9 +41,15 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / int8 MFMA % (prefill
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode32", choices=["decode32", "decode1", "mtp192", "prefill"])
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; stack40: 12)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; stack40: 4)")
+    ap.add_argument("--workload", default="decode32", choices=["decode32", "decode1", "mtp192", "prefill", "stack40"])
+    ap.add_argument("--stack-layers", type=int, default=40, help="stack40: layers in the stack")
+    ap.add_argument("--streamed", type=int, default=20, help="stack40: last layers whose experts stream from host")
+    ap.add_argument("--slots", type=int, default=64, help="stack40: HBM expert slots per streamed layer")
+    ap.add_argument("--host-copies", type=int, default=12,
+                    help="stack40: distinct host copies of routed experts; streamed layer j reads copy j mod this "
+                         "(pinned host memory is capped below 20 layers' 97 GB on the measured box)")
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gemm-min", type=int, default=0)
@@ -51,7 +60,12 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                     help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a benchmark run and of "
                          "a --calibrate run into per-launch HBM bytes of the dominant kernel")
-    return ap.parse_args()
+    a = ap.parse_args()
+    if a.steps is None:
+        a.steps = 12 if a.workload == "stack40" else 50
+    if a.warmup is None:
+        a.warmup = 4 if a.workload == "stack40" else 5
+    return a
 
 
 def tokens_of(workload):
@@ -212,6 +226,91 @@ def traffic_of(kernel, workload):
     return val if (val is not None and sha == source_sha256()) else None
 
 
+def run_stack(args):
+    """Stacked decode: every step runs all layers in order at T=32; streamed layers go through their caches."""
+    import torch
+
+    import int4_quantized_expert_amd as moe
+    from synth import synth
+    from tests.harness import GpuLayer, config_of, host_experts
+
+    sh = synth.GLM
+    T, NL, NSTR = 32, args.stack_layers, args.streamed
+    cfg = config_of(sh, args.gemm_min)
+    dev = torch.device("cuda:0")
+    layers, caches, hosts = [], [], []
+    t_setup = time.perf_counter()
+    for l in range(NL):
+        g = GpuLayer(sh, seed=args.seed, layer=l)
+        if l >= NL - NSTR:
+            j = l - (NL - NSTR)
+            if j < args.host_copies:
+                hosts.append(host_experts(g))
+            else:
+                hosts.append(hosts[j % args.host_copies])
+            for name in ("w13", "s13", "w2", "s2"):  # routed experts now live on the host only
+                setattr(g, name, torch.empty(1, dtype=getattr(g, name).dtype, device=dev))
+            caches.append(moe.ExpertCache(cfg, args.slots, T))
+        layers.append(g)
+        if (l + 1) % 10 == 0:
+            print(f"stack setup: {l + 1}/{NL} layers", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+    n_steps = args.warmup + args.steps
+    xs = [[torch.from_numpy(synth.hidden_states(sh, T, seed=args.seed, step=s * 64 + l)).to(dev) for l in range(NL)]
+          for s in range(n_steps)]
+    ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+    compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    wts = [g.weights() for g in layers]
+
+    def step(s):
+        for l in range(NL):
+            if l >= NL - NSTR:
+                c = caches[l - (NL - NSTR)]
+                c.forward(wts[l], hosts[l - (NL - NSTR)][0], xs[s][l], y, ws, compute, copy)
+            else:
+                moe.moe_layer_forward(cfg, wts[l], xs[s][l], y, ws, stream=compute)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    st0 = [c.stats() for c in caches]
+    t0 = time.perf_counter()
+    for s in range(args.warmup, n_steps):
+        step(s)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st1 = [c.stats() for c in caches]
+    hits = sum(b["hits"] - a["hits"] for a, b in zip(st0, st1))
+    misses = sum(b["misses"] - a["misses"] for a, b in zip(st0, st1))
+    h2d = sum(b["bytes_h2d"] - a["bytes_h2d"] for a, b in zip(st0, st1))
+    # pinned host -> device peak of this box, one 1 GiB copy
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    peak = (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
+    ms = dt * 1e3 / args.steps
+    out = {"metric": "stacked decode tokens/s (GLM-5.2 MoE layers, T=32)", "value": round(T / (ms / 1e3), 2),
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+           "higher_is_better": True, "dtype": "i8", "data": "synthetic",
+           "config": {"workload": f"glm5.2-moe stack{NL}: {NL - NSTR} resident + {NSTR} streamed layers, "
+                                  f"{args.slots} HBM slots per streamed layer", "tokens": T,
+                      "host_copies": min(NSTR, args.host_copies)},
+           "hit_rate": round(hits / max(1, hits + misses), 4), "hits": hits, "misses": misses,
+           "h2d_bytes_per_step": round(h2d / args.steps), "h2d_gbs_over_step": round(h2d / dt / 1e9, 2),
+           "pinned_h2d_peak_gbs": round(peak, 2), "setup_s": round(t_setup, 1)}
+    print(json.dumps(out), flush=True)
+    for c in caches:
+        c.destroy()
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -222,6 +321,9 @@ def main():
         sys.exit(2)
     if args.calibrate:
         calibrate()
+        return
+    if args.workload == "stack40":
+        run_stack(args)
         return
     import torch
 

@@ -218,13 +218,14 @@ def moe_membench_copy(src, dst, blocks: int, stream=None):
 
 
 class HostExperts:
-    """Pointer arrays of moe_host_experts over per-expert pinned host tensors (kept alive here)."""
+    """Pointer arrays of moe_host_experts: per expert, pinned host pointers (int) or pinned host tensors (kept
+    alive here) for w13, s13, w2, s2."""
 
     def __init__(self, w13, s13, w2, s2):
         self._keep = (list(w13), list(s13), list(w2), list(s2))
         E = len(self._keep[0])
         arr = ctypes.c_void_p * E
-        self._arrs = [arr(*[t.data_ptr() for t in lst]) for lst in self._keep]
+        self._arrs = [arr(*[t if isinstance(t, int) else t.data_ptr() for t in lst]) for lst in self._keep]
         self.c = moe_host_experts(*[ctypes.cast(a, P) for a in self._arrs])
 
 

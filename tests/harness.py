@@ -154,16 +154,51 @@ def within_tol(gpu, ref, rel=1e-5, floor=1e-6):
     return bool(np.all(np.abs(g - r) <= np.maximum(rel * np.abs(r), floor)))
 
 
+class PinnedBlock:
+    """One exact-size pinned host allocation (hipHostMalloc), freed with the object."""
+
+    def __init__(self, nbytes: int):
+        import ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        self._hip.hipHostFree.argtypes = [ctypes.c_void_p]
+        self._hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        p = ctypes.c_void_p()
+        rc = self._hip.hipHostMalloc(ctypes.byref(p), nbytes, 0)
+        if rc != 0:
+            raise MemoryError(f"hipHostMalloc({nbytes}) failed: hip error {rc}")
+        self.ptr, self.nbytes = p.value, nbytes
+
+    def fill_from_device(self, offset: int, t):
+        """Synchronous device -> host copy of a contiguous device tensor at byte offset."""
+        n = t.numel() * t.element_size()
+        assert offset + n <= self.nbytes
+        rc = self._hip.hipMemcpy(self.ptr + offset, t.data_ptr(), n, 2)  # hipMemcpyDeviceToHost
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpy failed: hip error {rc}")
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            self._hip.hipHostFree(self.ptr)
+            self.ptr = None
+
+
 def host_experts(layer):
-    """Pinned host copies of a GpuLayer's routed experts, as moe.HostExperts (device layout)."""
+    """Pinned host copies of a GpuLayer's routed experts (device layout), as (moe.HostExperts, keep-alive)."""
     import torch
 
     import int4_quantized_expert_amd as moe
-    parts = []
-    for t in (layer.w13, layer.s13, layer.w2, layer.s2):
-        h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
-        h.copy_(t)
-        parts.append(h)
     torch.cuda.synchronize()
     E = layer.w13.shape[0]
-    return moe.HostExperts(*[[p[e] for e in range(E)] for p in parts]), parts
+    parts = (layer.w13, layer.s13, layer.w2, layer.s2)
+    sizes = [t[0].numel() * t.element_size() for t in parts]
+    per = sum(sizes)
+    blk = PinnedBlock(per * E)
+    ptrs = [[], [], [], []]
+    for e in range(E):
+        off = e * per
+        for k, t in enumerate(parts):
+            blk.fill_from_device(off, t[e])
+            ptrs[k].append(blk.ptr + off)
+            off += sizes[k]
+    return moe.HostExperts(*ptrs), blk
