@@ -9,11 +9,10 @@
 // fixed and independent of the number of tokens or a token's place in the
 // batch, so a token routes identically alone or inside any batch: H is split
 // into 64 contiguous chunks; each chunk is summed in ascending h; the 64 chunk
-// sums are added in ascending chunk order, starting from 0. Two kernel paths
-// evaluate exactly this order — chunk-parallel partial sums plus an ordered
-// reduction for small batches (the router weights are read once,
-// bandwidth-bound) and an LDS-tiled token x expert kernel for large ones
-// (fp64-FMA-bound).
+// sums are added in ascending chunk order, starting from 0. One kernel writes
+// the chunk partial sums (token groups x expert blocks x chunks, so even one
+// token spreads over 256 workgroups and large batches over thousands); the
+// top-k kernel adds them in order.
 #include <limits.h>
 
 #include "moe_internal.h"
@@ -23,15 +22,16 @@ namespace moe {
 #define CAS __attribute__((address_space(4)))
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Small batches (T < 64): lane = expert, workgroup (y) = one of the 64 chunks,
-// z = a group of kRouterTT tokens. The chunk of the group's activations is
+// Lane = expert, workgroup (y) = one of the 64 chunks, z = a group of TT tokens
+// (TT = 1, 2, 4, 8 or 16: the smallest that covers the batch, at most 16).
+// The chunk of the group's activations is
 // staged in LDS (fp64) and read by every lane at the same address; the router
 // row chunk streams through the lane once. Each (token, chunk, expert) partial
 // sum is written in fp64; the top-k kernel adds the 64 partials in ascending
 // chunk order. Workgroups of the first expert group also encode Q8_0 of the
 // activations (blocks j, j+64, ... of each of their tokens), which saves a
 // launch on the latency-bound decode path.
-constexpr int kRouterTT = 16;
+constexpr int kRouterTT = 16;  // tokens per workgroup for larger batches
 constexpr int kRouterMaxC = 128;  // chunk length staged at once (H <= 8192 in one pass)
 
 __device__ __forceinline__ uint32_t pack4q(int8_t a, int8_t b, int8_t c, int8_t d) {
@@ -39,19 +39,19 @@ __device__ __forceinline__ uint32_t pack4q(int8_t a, int8_t b, int8_t c, int8_t 
          ((uint32_t)(uint8_t)d << 24);
 }
 
-template <bool VEC4>
+template <int TT, bool VEC4>
 __global__ __launch_bounds__(64) void k_router_part(const float* __restrict__ x, int T, int H,
                                                     const float* __restrict__ Wr, int E, double* __restrict__ part,
                                                     int8_t* __restrict__ qx_perm, float* __restrict__ dx,
                                                     int8_t* __restrict__ qx_nat) {
-  __shared__ double xs[kRouterTT][kRouterMaxC];
-  const int lane = threadIdx.x, e = blockIdx.x * 64 + lane, j = blockIdx.y, t0 = blockIdx.z * kRouterTT;
+  __shared__ double xs[TT][kRouterMaxC];
+  const int lane = threadIdx.x, e = blockIdx.x * 64 + lane, j = blockIdx.y, t0 = blockIdx.z * TT;
   const int C = H / 64;
   const int ec = min(e, E - 1);
   const float* wrow = Wr + (size_t)ec * H + (size_t)j * C;
-  double p[kRouterTT];
+  double p[TT];
 #pragma unroll
-  for (int tt = 0; tt < kRouterTT; ++tt) p[tt] = 0.0;
+  for (int tt = 0; tt < TT; ++tt) p[tt] = 0.0;
   for (int c0 = 0; c0 < C; c0 += kRouterMaxC) {
     const int cw = min(kRouterMaxC, C - c0);
     // issue every load of the chunk before the first wait: the lane's router
@@ -62,20 +62,20 @@ __global__ __launch_bounds__(64) void k_router_part(const float* __restrict__ x,
       for (int u = 0; u < kRouterMaxC / 4; ++u)
         if (4 * u < cw) wreg[u] = *reinterpret_cast<const float4*>(wrow + c0 + 4 * u);
     }
-    float xr[kRouterTT * kRouterMaxC / 64];
+    float xr[TT * kRouterMaxC / 64];
 #pragma unroll
-    for (int m = 0; m < kRouterTT * kRouterMaxC / 64; ++m) {
+    for (int m = 0; m < TT * kRouterMaxC / 64; ++m) {
       const int idx = lane + 64 * m;
-      if (idx < kRouterTT * cw) {
+      if (idx < TT * cw) {
         const int tt = idx / cw, i = idx - tt * cw;
         xr[m] = x[(size_t)min(t0 + tt, T - 1) * H + (size_t)j * C + c0 + i];
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < kRouterTT * kRouterMaxC / 64; ++m) {
+    for (int m = 0; m < TT * kRouterMaxC / 64; ++m) {
       const int idx = lane + 64 * m;
-      if (idx < kRouterTT * cw) {
+      if (idx < TT * cw) {
         const int tt = idx / cw, i = idx - tt * cw;
         xs[tt][i] = (double)xr[m];
       }
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(64) void k_router_part(const float* __restrict__ x,
           const int i = 4 * u;
           const double w0 = wreg[u].x, w1 = wreg[u].y, w2 = wreg[u].z, w3 = wreg[u].w;
 #pragma unroll
-          for (int tt = 0; tt < kRouterTT; ++tt) {
+          for (int tt = 0; tt < TT; ++tt) {
             p[tt] = fma(xs[tt][i], w0, p[tt]);
             p[tt] = fma(xs[tt][i + 1], w1, p[tt]);
             p[tt] = fma(xs[tt][i + 2], w2, p[tt]);
@@ -100,19 +100,19 @@ __global__ __launch_bounds__(64) void k_router_part(const float* __restrict__ x,
       for (int i = 0; i < cw; ++i) {
         const double wv = (double)wrow[c0 + i];
 #pragma unroll
-        for (int tt = 0; tt < kRouterTT; ++tt) p[tt] = fma(xs[tt][i], wv, p[tt]);
+        for (int tt = 0; tt < TT; ++tt) p[tt] = fma(xs[tt][i], wv, p[tt]);
       }
     }
   }
   if (e < E) {
 #pragma unroll
-    for (int tt = 0; tt < kRouterTT; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
       if (t0 + tt < T) part[((size_t)(t0 + tt) * 64 + j) * E + e] = p[tt];
   }
   if (blockIdx.x == 0 && qx_perm) {
     // Q8_0 of x: lane -> (token, block) pairs of this chunk's block set
     const int nb = H / 32, nbj = (nb - j + 63) / 64;  // blocks j, j+64, ... of one token
-    for (int idx = lane; idx < kRouterTT * nbj; idx += 64) {
+    for (int idx = lane; idx < TT * nbj; idx += 64) {
       const int tt = idx / nbj, bq = j + 64 * (idx - tt * nbj), t = t0 + tt;
       if (t >= T) continue;
       const float* src = x + (size_t)t * H + (size_t)bq * 32;
@@ -164,67 +164,6 @@ __global__ __launch_bounds__(256) void k_router_reduce(const double* __restrict_
   double tot = 0.0;
   for (int j = 0; j < 64; ++j) tot += part[((size_t)t * 64 + j) * E + e];
   z[idx] = (float)tot;
-}
-
-// Large batches: 64 tokens x 32 experts per workgroup; each thread owns
-// 2 tokens x 4 experts and walks the same chunk order as the small kernel.
-constexpr int kRT_M = 64, kRT_N = 32, kRT_CH = 48;
-
-__global__ __launch_bounds__(256) void k_router_large(const float* __restrict__ x, int T, int H,
-                                                      const float* __restrict__ Wr, int E, float* __restrict__ z) {
-  __shared__ double xs[kRT_M][kRT_CH + 1];
-  __shared__ double ws[kRT_N][kRT_CH + 1];
-  const int tid = threadIdx.x, tx = tid & 7, ty = tid >> 3;
-  const int t0 = blockIdx.x * kRT_M, e0 = blockIdx.y * kRT_N;
-  const int C = H / 64;
-  double tot[2][4];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) tot[a][b] = 0.0;
-  for (int j = 0; j < 64; ++j) {
-    double p[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) p[a][b] = 0.0;
-    for (int c0 = 0; c0 < C; c0 += kRT_CH) {
-      const int cw = min(kRT_CH, C - c0);
-      __syncthreads();
-      for (int idx = tid; idx < kRT_M * cw; idx += 256) {
-        int r = idx / cw, c = idx - r * cw, t = t0 + r;
-        xs[r][c] = (t < T) ? (double)x[(size_t)t * H + (size_t)j * C + c0 + c] : 0.0;
-      }
-      for (int idx = tid; idx < kRT_N * cw; idx += 256) {
-        int r = idx / cw, c = idx - r * cw, e = e0 + r;
-        ws[r][c] = (e < E) ? (double)Wr[(size_t)e * H + (size_t)j * C + c0 + c] : 0.0;
-      }
-      __syncthreads();
-      for (int c = 0; c < cw; ++c) {
-        double xa = xs[2 * ty][c], xb2 = xs[2 * ty + 1][c];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          double wv = ws[4 * tx + b][c];
-          p[0][b] = fma(xa, wv, p[0][b]);
-          p[1][b] = fma(xb2, wv, p[1][b]);
-        }
-      }
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) tot[a][b] += p[a][b];
-  }
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    int t = t0 + 2 * ty + a;
-    if (t >= T) continue;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      int e = e0 + 4 * tx + b;
-      if (e < E) z[(size_t)t * E + e] = (float)tot[a][b];
-    }
-  }
 }
 
 // (value descending, index ascending) maximum over the wave; every lane ends
@@ -347,55 +286,42 @@ __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ z, const 
   if (lane == 0 && flags) flags[t] = fl;
 }
 
-// Register-resident top-k for the common shapes: lane l owns the EPL
-// consecutive experts l*EPL .. l*EPL+EPL-1, a group of E/G experts spans an
-// aligned power-of-two set of LG lanes. With PARTS the kernel first adds the
-// router's 64 chunk partials in ascending chunk order (the logit order every
-// router path uses) and rounds once to fp32.
-template <int EPL, bool PARTS>
-__global__ __launch_bounds__(64) void k_topk_fast(const float* __restrict__ z, const double* __restrict__ part,
-                                                  const float* __restrict__ bias, int E, int G, int KG, int K,
-                                                  float rsf, int32_t* __restrict__ ids, float* __restrict__ w,
-                                                  uint8_t* __restrict__ flags) {
-  __shared__ int sel_e[kMaxTopK];
-  __shared__ float sel_c[kMaxTopK];
-  __shared__ float sel_s[kMaxTopK];
-  const int t = blockIdx.x, lane = threadIdx.x;
+// Top-k for the common shapes, one 256-lane workgroup per token. First every
+// lane adds the 64 chunk partials of its expert in ascending chunk order and
+// rounds once to fp32 (the logit); then wavefront 0 selects in registers:
+// lane l owns the EPL consecutive experts l*EPL .. l*EPL+EPL-1, and a group of
+// E/G experts spans an aligned power-of-two set of LG lanes.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk_fast(const double* __restrict__ part, const float* __restrict__ bias,
+                                                   int E, int G, int KG, int K, float rsf, int32_t* __restrict__ ids,
+                                                   float* __restrict__ w, uint8_t* __restrict__ flags) {
+  __shared__ float s_s[kMaxExperts];
+  __shared__ float s_c[kMaxExperts];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  // every lane adds the 64 chunk partials of its expert in ascending chunk
+  // order, with all 64 loads issued before the first add
+  for (int e = tid; e < E; e += 256) {
+    double v[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) v[j] = part[((size_t)t * 64 + j) * E + e];
+    double tot = 0.0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) tot += v[j];
+    const float sv = (float)(1.0 / (1.0 + exp(-(double)(float)tot)));
+    s_s[e] = sv;
+    s_c[e] = __fadd_rn(sv, bias[e]);
+  }
+  __syncthreads();
+  if (tid >= 64) return;
+  const int lane = tid;
   const int LG = (E / G) / EPL;
   const bool has = lane * EPL < E;
   float s[EPL], c[EPL];
-  if (!PARTS) {
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = min(lane * EPL + i, E - 1);
-      s[i] = (float)(1.0 / (1.0 + exp(-(double)z[(size_t)t * E + e])));
-      c[i] = has ? __fadd_rn(s[i], bias[e]) : -INFINITY;
-    }
-  } else {
-    // add the 64 chunk partials of each owned expert in ascending chunk order;
-    // loads are issued in batches of 64 doubles per lane before the adds
-    constexpr int JB = EPL >= 64 ? 1 : 64 / EPL;
-    double tot[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) tot[i] = 0.0;
-    for (int jb = 0; jb < 64; jb += JB) {
-      double v[JB][EPL];
-#pragma unroll
-      for (int jj = 0; jj < JB; ++jj)
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          v[jj][i] = part[((size_t)t * 64 + jb + jj) * E + min(lane * EPL + i, E - 1)];
-#pragma unroll
-      for (int jj = 0; jj < JB; ++jj)
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) tot[i] += v[jj][i];
-    }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = min(lane * EPL + i, E - 1);
-      s[i] = (float)(1.0 / (1.0 + exp(-(double)(float)tot[i])));
-      c[i] = has ? __fadd_rn(s[i], bias[e]) : -INFINITY;
-    }
+  for (int i = 0; i < EPL; ++i) {
+    const int e = min(lane * EPL + i, E - 1);
+    s[i] = s_s[e];
+    c[i] = has ? s_c[e] : -INFINITY;
   }
   // group score: the two largest c of the group (insertion order within the lane,
   // then pairwise merges across the group's lanes; max/min are exact)
@@ -438,7 +364,10 @@ __global__ __launch_bounds__(64) void k_topk_fast(const float* __restrict__ z, c
     if ((double)min_kept - (double)v < 1e-6) fl |= MOE_TIE_GROUP;
   }
   const bool kept = __shfl((int)kept_rep, g * LG) != 0;
+  // slot k's expert, biased and unbiased score end up in lane k
   uint32_t taken = 0;
+  int my_e = 0;
+  float my_c = 0.0f, my_s = 0.0f, last_c = 0.0f;
   for (int k = 0; k <= K; ++k) {
     float bv = -INFINITY;
     int bi = INT_MAX;
@@ -452,7 +381,7 @@ __global__ __launch_bounds__(64) void k_topk_fast(const float* __restrict__ z, c
     }
     wave_argmax(bv, bi);
     if (k == K) {  // the best candidate left out: expert-boundary near-tie check
-      if (K < KG * (E / G) && (double)sel_c[K - 1] - (double)bv < 1e-6) fl |= MOE_TIE_EXPERT;
+      if (K < KG * (E / G) && (double)last_c - (double)bv < 1e-6) fl |= MOE_TIE_EXPERT;
       break;
     }
     const int owner = bi / EPL, slot = bi - owner * EPL;
@@ -462,20 +391,20 @@ __global__ __launch_bounds__(64) void k_topk_fast(const float* __restrict__ z, c
       if (i == slot) sv = s[i];
     sv = __shfl(sv, owner);
     if (lane == owner) taken |= 1u << slot;
-    if (lane == 0) {
-      sel_e[k] = bi;
-      sel_c[k] = bv;
-      sel_s[k] = sv;
+    if (lane == k) {
+      my_e = bi;
+      my_c = bv;
+      my_s = sv;
     }
-    __syncthreads();
+    last_c = bv;
   }
   for (int k = 0; k + 1 < K; ++k)
-    if ((double)sel_c[k] - (double)sel_c[k + 1] < 1e-6) fl |= MOE_TIE_ORDER;
+    if ((double)__shfl(my_c, k) - (double)__shfl(my_c, k + 1) < 1e-6) fl |= MOE_TIE_ORDER;
+  double sum = 0.0;
+  for (int k = 0; k < K; ++k) sum += (double)__shfl(my_s, k);
   if (lane < K) {
-    double sum = 0.0;
-    for (int k = 0; k < K; ++k) sum += (double)sel_s[k];
-    ids[(size_t)t * K + lane] = sel_e[lane];
-    w[(size_t)t * K + lane] = (float)(((double)sel_s[lane] / sum) * (double)rsf);
+    ids[(size_t)t * K + lane] = my_e;
+    w[(size_t)t * K + lane] = (float)(((double)my_s / sum) * (double)rsf);
   }
   if (lane == 0 && flags) flags[t] = fl;
 }
@@ -490,22 +419,28 @@ static int fast_epl(const moe_config& c) {
   return epl;
 }
 
-template <bool PARTS>
-static void topk_fast_launch(int epl, int T, const float* z, const double* part, const float* bias,
-                             const moe_config& c, int32_t* ids, float* w, uint8_t* flags, hipStream_t st) {
+static void topk_fast_launch(int epl, int T, const double* part, const float* bias, const moe_config& c,
+                             int32_t* ids, float* w, uint8_t* flags, hipStream_t st) {
   const int E = c.n_experts, G = c.n_group, KG = c.topk_group, K = c.top_k;
   const float r = c.routed_scaling_factor;
   switch (epl) {
-    case 1: k_topk_fast<1, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
-    case 2: k_topk_fast<2, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
-    case 4: k_topk_fast<4, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
-    case 8: k_topk_fast<8, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
-    default: k_topk_fast<16, PARTS><<<T, 64, 0, st>>>(z, part, bias, E, G, KG, K, r, ids, w, flags); break;
+    case 1: k_topk_fast<1><<<T, 256, 0, st>>>(part, bias, E, G, KG, K, r, ids, w, flags); break;
+    case 2: k_topk_fast<2><<<T, 256, 0, st>>>(part, bias, E, G, KG, K, r, ids, w, flags); break;
+    case 4: k_topk_fast<4><<<T, 256, 0, st>>>(part, bias, E, G, KG, K, r, ids, w, flags); break;
+    case 8: k_topk_fast<8><<<T, 256, 0, st>>>(part, bias, E, G, KG, K, r, ids, w, flags); break;
+    default: k_topk_fast<16><<<T, 256, 0, st>>>(part, bias, E, G, KG, K, r, ids, w, flags); break;
   }
 }
 
 // Router + top-k. For T < 64 the logits come as chunk partials and, when
 // qx_perm is given, Q8_0 of x is encoded in the same launch (*q8_done = true).
+template <int TT>
+static void router_part_launch(dim3 grid, bool vec4, const float* x, int T, int H, const float* Wr, int E,
+                               double* part, int8_t* qx_perm, float* dx, int8_t* qx_nat, hipStream_t st) {
+  if (vec4) k_router_part<TT, true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+  else k_router_part<TT, false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+}
+
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias, float* z,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
                         int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
@@ -514,30 +449,23 @@ hipError_t launch_route(const float* x, int T, const moe_config& c, const float*
   if (T <= 0) return hipSuccess;
   const int H = c.hidden, E = c.n_experts;
   const int epl = fast_epl(c);
-  if (T < kRT_M) {
-    dim3 grid((E + 63) / 64, 64, (T + kRouterTT - 1) / kRouterTT);
-    if ((H / 64) % 4 == 0)
-      k_router_part<true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
-    else
-      k_router_part<false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
-    if (q8_done && qx_perm) *q8_done = true;
-    if (mark) mark(mark_call, 1, st);
-    if (epl) {
-      topk_fast_launch<true>(epl, T, nullptr, part, bias, c, ids, w, flags, st);
-    } else {
-      k_router_reduce<<<(T * E + 255) / 256, 256, 0, st>>>(part, T, E, z);
-      k_topk<<<T, 64, 0, st>>>(z, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, ids, w,
-                               flags);
-    }
+  const int tt = T >= kRouterTT ? kRouterTT : (T > 4 ? 8 : (T > 2 ? 4 : T));
+  dim3 grid((E + 63) / 64, 64, (T + tt - 1) / tt);
+  const bool vec4 = (H / 64) % 4 == 0;
+  switch (tt) {
+    case 1: router_part_launch<1>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
+    case 2: router_part_launch<2>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
+    case 4: router_part_launch<4>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
+    case 8: router_part_launch<8>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
+    default: router_part_launch<kRouterTT>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
+  }
+  if (q8_done && qx_perm) *q8_done = true;
+  if (mark) mark(mark_call, 1, st);
+  if (epl) {
+    topk_fast_launch(epl, T, part, bias, c, ids, w, flags, st);
   } else {
-    dim3 grid((T + kRT_M - 1) / kRT_M, (E + kRT_N - 1) / kRT_N);
-    k_router_large<<<grid, 256, 0, st>>>(x, T, H, Wr, E, z);
-    if (mark) mark(mark_call, 1, st);
-    if (epl)
-      topk_fast_launch<false>(epl, T, z, nullptr, bias, c, ids, w, flags, st);
-    else
-      k_topk<<<T, 64, 0, st>>>(z, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, ids, w,
-                               flags);
+    k_router_reduce<<<(T * E + 255) / 256, 256, 0, st>>>(part, T, E, z);
+    k_topk<<<T, 64, 0, st>>>(z, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, ids, w, flags);
   }
   return hipGetLastError();
 }

@@ -62,7 +62,7 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.qh = take((size_t)L.R * L.I);
   L.dh = take((size_t)L.R * (L.I / 32) * 4);
   L.eout = take((size_t)L.R * L.H * 4);
-  L.part = take(T < 64 ? (size_t)T * 64 * L.E * 8 : 0);
+  L.part = take((size_t)T * 64 * L.E * 8);  // router chunk partials, every batch size
   L.total = off;
   return L;
 }

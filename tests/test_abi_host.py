@@ -50,6 +50,19 @@ def test_workspace_bytes():
     assert moe.moe_workspace_bytes(c, 0) == 0
 
 
+@pytest.mark.parametrize("T", [1, 63, 64, 192, 2048])
+def test_workspace_covers_every_region(T):
+    """Lower bound from what the kernels write per call: router chunk partials (T x 64 chunks x E fp64), logits,
+    per-slot Q8_0 h codes and scales, per-slot fp32 expert outputs, Q8_0 x, and the GEMV work list at its
+    worst case (chunks of up to 4 tokens) — every batch size, including the large ones."""
+    c = _glm()
+    E, K, H, I, NS = 256, 8, 6144, 2048, 1
+    R = T * K + NS * T
+    need = (T * 64 * E * 8 + T * E * 4 + R * I + R * (I // 32) * 4 + R * H * 4 + T * H + T * (H // 32) * 4
+            + ((T * K + NS * T) // 4 + min(E, T * K) + 2 * NS) * 8)
+    assert moe.moe_workspace_bytes(c, T) >= need
+
+
 @pytest.mark.parametrize("bad", [dict(hidden=100), dict(inter=96), dict(n_group=5), dict(topk_group=9),
                                  dict(top_k=40), dict(n_experts=1), dict(n_shared=9), dict(n_group=128, n_experts=128),
                                  dict(routed_scaling_factor=float("nan")), dict(top_k=33)])
