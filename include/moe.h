@@ -73,12 +73,12 @@ extern "C" {
 #define MOE_TIE_ORDER 4  /* two selected experts' biased scores within 1e-6 */
 
 typedef struct moe_config {
-  int32_t hidden;        /* H: multiple of 64 */
+  int32_t hidden;        /* H: multiple of 64, at most 16384 */
   int32_t n_experts;     /* E: 2..1024 routed experts */
   int32_t n_group;       /* G: E % G == 0, E / G >= 2, G <= 64 */
   int32_t topk_group;    /* groups kept per token, 1..G */
   int32_t top_k;         /* K: 1..32 and K <= topk_group * E / G */
-  int32_t inter;         /* I: expert intermediate size, multiple of 64 */
+  int32_t inter;         /* I: expert intermediate size, multiple of 64, at most 16384 */
   int32_t n_shared;      /* shared experts, 0..4 */
   float routed_scaling_factor;
   int32_t gemm_min_tokens; /* bucket size from which the int8-MFMA path is used;

@@ -164,17 +164,38 @@ static inline size_t gemv_lds_bytes(int n, int K, int pairs) {
   return stage > part ? stage : part;
 }
 
-// Stage codes [N][K] and scales [N][K/32] of the chunk's N (padded) tokens.
+// Staging of the chunk's N (padded) tokens: codes [N][K] and scales [N][K/32].
+// The loads go to registers first so that a workgroup can issue its first
+// weight loads before it waits for them; then they are written to LDS.
+// K <= 16384: at most two 16-byte code loads and one scale per lane and token.
 template <int N>
-__device__ __forceinline__ void stage_codes(const int8_t* const (&src)[N], const float* const (&dsrc)[N], int K,
-                                            int8_t* xs, float* xd) {
-  const int nb = K / 32;
+struct Staged {
+  v4i c[N][2];
+  float d[N];
+};
+
+template <int N>
+__device__ __forceinline__ void stage_load(const int8_t* const (&src)[N], const float* const (&dsrc)[N], int K,
+                                           Staged<N>& st) {
+  const int tid = threadIdx.x, n16 = K / 16, nb = K / 32;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const v4i* s4 = reinterpret_cast<const v4i*>(src[i]);
+    st.c[i][0] = s4[min(tid, n16 - 1)];
+    st.c[i][1] = s4[min(tid + kGemvThreads, n16 - 1)];
+    st.d[i] = dsrc[i][min(tid, nb - 1)];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void stage_store(const Staged<N>& st, int K, int8_t* xs, float* xd) {
+  const int tid = threadIdx.x, n16 = K / 16, nb = K / 32;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
     v4i* d4 = reinterpret_cast<v4i*>(xs + (size_t)i * K);
-    for (int v = threadIdx.x; v < K / 16; v += kGemvThreads) d4[v] = s4[v];
-    for (int v = threadIdx.x; v < nb; v += kGemvThreads) xd[i * nb + v] = dsrc[i][v];
+    if (tid < n16) d4[tid] = st.c[i][0];
+    if (tid + kGemvThreads < n16) d4[tid + kGemvThreads] = st.c[i][1];
+    if (tid < nb) xd[i * nb + tid] = st.d[i];
   }
   __syncthreads();
 }
@@ -188,6 +209,7 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
   const int r = tile * 64 + lane;
   int8_t* xs = reinterpret_cast<int8_t*>(lds);
   float* xd = reinterpret_cast<float*>(lds + (size_t)N * H);
+  Staged<N> st;
   {
     const int8_t* src[N];
     const float* dsrc[N];
@@ -197,8 +219,22 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
       src[i] = a.qx + (size_t)tok * H;
       dsrc[i] = a.dx + (size_t)tok * nb;
     }
-    stage_codes<N>(src, dsrc, H, xs, xd);
+    stage_load<N>(src, dsrc, H, st);
   }
+  // the first weight blocks are requested before the staged codes are waited for
+  const int ncls = w < nb ? (nb - w + kGW - 1) / kGW : 0;  // blocks of class w
+  const int last = max(ncls - 1, 0);
+  const uint8_t* gcls = w13 + tb_off(tile, min(w, nb - 1), nb) + (size_t)lane * 16;
+  const uint8_t* ucls = w13 + tb_off(I / 64 + tile, min(w, nb - 1), nb) + (size_t)lane * 16;
+  constexpr size_t step = kGW * kBlkStride;  // class stride
+  uint4 bg[PF], bu[PF];
+#pragma unroll
+  for (int kk = 0; kk < PF; ++kk) {
+    const size_t off = (size_t)min(kk, last) * step;
+    bg[kk] = *reinterpret_cast<const uint4*>(gcls + off);
+    bu[kk] = *reinterpret_cast<const uint4*>(ucls + off);
+  }
+  stage_store<N>(st, H, xs, xd);
   int tap_i = -1;
   if (TAP) {
     for (int i = 0; i < nn; ++i)
@@ -207,18 +243,7 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
   float ag[N], au[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) ag[i] = au[i] = 0.0f;
-  const int ncls = w < nb ? (nb - w + kGW - 1) / kGW : 0;  // blocks of class w
   if (ncls > 0) {
-    const uint8_t* gcls = w13 + tb_off(tile, w, nb) + (size_t)lane * 16;
-    const uint8_t* ucls = w13 + tb_off(I / 64 + tile, w, nb) + (size_t)lane * 16;
-    constexpr size_t step = kGW * kBlkStride;  // class stride
-    uint4 bg[PF], bu[PF];
-#pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const size_t off = (size_t)min(kk, ncls - 1) * step;
-      bg[kk] = *reinterpret_cast<const uint4*>(gcls + off);
-      bu[kk] = *reinterpret_cast<const uint4*>(ucls + off);
-    }
     for (int j0 = 0; j0 < ncls; j0 += PF) {
 #pragma unroll
       for (int kk = 0; kk < PF; ++kk) {
@@ -286,6 +311,7 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
   const int o = tile * 64 + lane;
   int8_t* hs = reinterpret_cast<int8_t*>(lds);
   float* hd = reinterpret_cast<float*>(lds + (size_t)N * I);
+  Staged<N> st;
   {
     const int8_t* src[N];
     const float* dsrc[N];
@@ -295,8 +321,16 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
       src[i] = a.qh + (size_t)p * I;
       dsrc[i] = a.dh + (size_t)p * nbi;
     }
-    stage_codes<N>(src, dsrc, I, hs, hd);
+    stage_load<N>(src, dsrc, I, st);
   }
+  const int ncls = w < nbi ? (nbi - w + kGW - 1) / kGW : 0;
+  const int last = max(ncls - 1, 0);
+  const uint8_t* wcls = w2 + tb_off(tile, min(w, nbi - 1), nbi) + (size_t)lane * 16;
+  constexpr size_t step = kGW * kBlkStride;
+  uint4 bw[PF];
+#pragma unroll
+  for (int kk = 0; kk < PF; ++kk) bw[kk] = *reinterpret_cast<const uint4*>(wcls + (size_t)min(kk, last) * step);
+  stage_store<N>(st, I, hs, hd);
   int tap_i = -1;
   if (TAP) {
     for (int i = 0; i < nn; ++i)
@@ -305,13 +339,7 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
   float acc[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-  const int ncls = w < nbi ? (nbi - w + kGW - 1) / kGW : 0;
   if (ncls > 0) {
-    const uint8_t* wcls = w2 + tb_off(tile, w, nbi) + (size_t)lane * 16;
-    constexpr size_t step = kGW * kBlkStride;
-    uint4 bw[PF];
-#pragma unroll
-    for (int kk = 0; kk < PF; ++kk) bw[kk] = *reinterpret_cast<const uint4*>(wcls + (size_t)min(kk, ncls - 1) * step);
     for (int j0 = 0; j0 < ncls; j0 += PF) {
 #pragma unroll
       for (int kk = 0; kk < PF; ++kk) {

@@ -11,8 +11,7 @@
 // into 64 contiguous chunks; each chunk is summed in ascending h; the 64 chunk
 // sums are added in ascending chunk order, starting from 0. One kernel writes
 // the chunk partial sums (token groups x expert blocks x chunks, so even one
-// token spreads over 256 workgroups and large batches over thousands); the
-// top-k kernel adds them in order.
+// token spreads over 256 workgroups); the top-k kernel adds them in order.
 #include <limits.h>
 
 #include "moe_internal.h"
@@ -23,16 +22,16 @@ namespace moe {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Lane = expert, workgroup (y) = one of the 64 chunks, z = a group of TT tokens
-// (TT = 1, 2, 4, 8 or 16: the smallest that covers the batch, at most 16).
-// The chunk of the group's activations is
-// staged in LDS (fp64) and read by every lane at the same address; the router
-// row chunk streams through the lane once. Each (token, chunk, expert) partial
-// sum is written in fp64; the top-k kernel adds the 64 partials in ascending
-// chunk order. Workgroups of the first expert group also encode Q8_0 of the
-// activations (blocks j, j+64, ... of each of their tokens), which saves a
-// launch on the latency-bound decode path.
-constexpr int kRouterTT = 16;  // tokens per workgroup for larger batches
-constexpr int kRouterMaxC = 128;  // chunk length staged at once (H <= 8192 in one pass)
+// (TT = 1, 2 or 4). The lane keeps its expert's row chunk of the router
+// weights in registers (read once, as fp32) and walks the chunk in ascending h;
+// the activations are the same for every lane of the workgroup, so they come
+// from scalar loads and are widened to fp64 on use. Each (token, chunk,
+// expert) partial sum is written in fp64; the top-k kernel adds the 64 partials
+// in ascending chunk order. Workgroups of the first expert block also encode
+// Q8_0 of the activations (blocks j, j+64, ... of each of their tokens), which
+// saves a launch on the latency-bound decode path.
+constexpr int kRouterTT = 4;
+constexpr int kRouterMaxC = 96;  // chunk elements held in registers per pass
 
 __device__ __forceinline__ uint32_t pack4q(int8_t a, int8_t b, int8_t c, int8_t d) {
   return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
@@ -44,63 +43,40 @@ __global__ __launch_bounds__(64) void k_router_part(const float* __restrict__ x,
                                                     const float* __restrict__ Wr, int E, double* __restrict__ part,
                                                     int8_t* __restrict__ qx_perm, float* __restrict__ dx,
                                                     int8_t* __restrict__ qx_nat) {
-  __shared__ double xs[TT][kRouterMaxC];
   const int lane = threadIdx.x, e = blockIdx.x * 64 + lane, j = blockIdx.y, t0 = blockIdx.z * TT;
   const int C = H / 64;
   const int ec = min(e, E - 1);
   const float* wrow = Wr + (size_t)ec * H + (size_t)j * C;
+  const CAS float* xr[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) xr[tt] = (const CAS float*)(x + (size_t)min(t0 + tt, T - 1) * H + (size_t)j * C);
   double p[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) p[tt] = 0.0;
   for (int c0 = 0; c0 < C; c0 += kRouterMaxC) {
     const int cw = min(kRouterMaxC, C - c0);
-    // issue every load of the chunk before the first wait: the lane's router
-    // weights (registers) and the group's activations (staged through LDS)
-    float4 wreg[kRouterMaxC / 4];
     if (VEC4) {
+      float4 wreg[kRouterMaxC / 4];
 #pragma unroll
       for (int u = 0; u < kRouterMaxC / 4; ++u)
         if (4 * u < cw) wreg[u] = *reinterpret_cast<const float4*>(wrow + c0 + 4 * u);
-    }
-    float xr[TT * kRouterMaxC / 64];
-#pragma unroll
-    for (int m = 0; m < TT * kRouterMaxC / 64; ++m) {
-      const int idx = lane + 64 * m;
-      if (idx < TT * cw) {
-        const int tt = idx / cw, i = idx - tt * cw;
-        xr[m] = x[(size_t)min(t0 + tt, T - 1) * H + (size_t)j * C + c0 + i];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < TT * kRouterMaxC / 64; ++m) {
-      const int idx = lane + 64 * m;
-      if (idx < TT * cw) {
-        const int tt = idx / cw, i = idx - tt * cw;
-        xs[tt][i] = (double)xr[m];
-      }
-    }
-    __syncthreads();
-    if (VEC4) {
 #pragma unroll
       for (int u = 0; u < kRouterMaxC / 4; ++u) {
         if (4 * u < cw) {
-          const int i = 4 * u;
-          const double w0 = wreg[u].x, w1 = wreg[u].y, w2 = wreg[u].z, w3 = wreg[u].w;
+          const double wv[4] = {(double)wreg[u].x, (double)wreg[u].y, (double)wreg[u].z, (double)wreg[u].w};
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt) {
-            p[tt] = fma(xs[tt][i], w0, p[tt]);
-            p[tt] = fma(xs[tt][i + 1], w1, p[tt]);
-            p[tt] = fma(xs[tt][i + 2], w2, p[tt]);
-            p[tt] = fma(xs[tt][i + 3], w3, p[tt]);
+          for (int k = 0; k < 4; ++k) {
+            const int i = c0 + 4 * u + k;
+#pragma unroll
+            for (int tt = 0; tt < TT; ++tt) p[tt] = fma((double)xr[tt][i], wv[k], p[tt]);
           }
         }
       }
     } else {
-      for (int i = 0; i < cw; ++i) {
-        const double wv = (double)wrow[c0 + i];
+      for (int i = c0; i < c0 + cw; ++i) {
+        const double wv = (double)wrow[i];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) p[tt] = fma(xs[tt][i], wv, p[tt]);
+        for (int tt = 0; tt < TT; ++tt) p[tt] = fma((double)xr[tt][i], wv, p[tt]);
       }
     }
   }
@@ -449,14 +425,12 @@ hipError_t launch_route(const float* x, int T, const moe_config& c, const float*
   if (T <= 0) return hipSuccess;
   const int H = c.hidden, E = c.n_experts;
   const int epl = fast_epl(c);
-  const int tt = T >= kRouterTT ? kRouterTT : (T > 4 ? 8 : (T > 2 ? 4 : T));
+  const int tt = T > 2 ? kRouterTT : T;
   dim3 grid((E + 63) / 64, 64, (T + tt - 1) / tt);
   const bool vec4 = (H / 64) % 4 == 0;
   switch (tt) {
     case 1: router_part_launch<1>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
     case 2: router_part_launch<2>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
-    case 4: router_part_launch<4>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
-    case 8: router_part_launch<8>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
     default: router_part_launch<kRouterTT>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
   }
   if (q8_done && qx_perm) *q8_done = true;

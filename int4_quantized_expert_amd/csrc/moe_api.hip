@@ -69,8 +69,8 @@ Layout make_layout(const moe_config& c, int64_t T) {
 
 int validate_config(const moe_config* c) {
   if (!c) return MOE_E_NULL;
-  if (c->hidden <= 0 || c->hidden % 64 != 0) return MOE_E_SHAPE;
-  if (c->inter <= 0 || c->inter % 64 != 0) return MOE_E_SHAPE;
+  if (c->hidden <= 0 || c->hidden % 64 != 0 || c->hidden > kMaxHidden) return MOE_E_SHAPE;
+  if (c->inter <= 0 || c->inter % 64 != 0 || c->inter > kMaxHidden) return MOE_E_SHAPE;
   if (c->n_experts < 2 || c->n_experts > kMaxExperts) return MOE_E_SHAPE;
   if (c->n_group < 1 || c->n_group > kMaxGroups || c->n_experts % c->n_group != 0) return MOE_E_SHAPE;
   if (c->n_experts / c->n_group < 2) return MOE_E_SHAPE;
