@@ -387,32 +387,65 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
 // blocks ascending, then class 1's, ...), keeps one fp32 chain for the current
 // class and folds it into the running total when the class ends: the same
 // arithmetic as the GEMV path, class by class instead of class per wavefront.
+// The walk index is wave-uniform (scalar registers); the totals, touched once
+// per class, live in the wavefront's LDS slice so the registers hold only the
+// chains, the prefetch ring and the MFMA results.
 
-// Block at position i of the class-major order; last = it ends its class.
-__device__ __forceinline__ int class_major_block(int i, int nb, bool& last) {
-  if (nb % kDotClasses == 0) {
-    const int per = nb / kDotClasses;
-    last = (i % per) == per - 1;
-    return (i % per) * kDotClasses + i / per;
-  }
-  for (int c = 0; c < kDotClasses; ++c) {
-    const int n = (nb - c + kDotClasses - 1) / kDotClasses;  // blocks of class c (0 when c >= nb)
-    if (i < n) {
-      last = i == n - 1;
-      return c + kDotClasses * i;
-    }
-    i -= n;
-  }
-  last = true;
-  return nb - 1;
+// Block after blk in the class-major walk (the next of its class, else the
+// first of the next class), clamped to a valid block past the walk's end.
+__device__ __forceinline__ int class_major_next(int blk, int nb) {
+  const int n = blk + kDotClasses;
+  return min(n < nb ? n : (blk % kDotClasses) + 1, nb - 1);
 }
 
+// Per-wavefront LDS for the class totals: [NTT][gate|up][16/4][64 lanes] float4.
+template <int NTT, int NM>
+struct MfmaTotals {
+  float4 v[NTT][NM][4][64];
+};
+
+template <int NTT, int NM>
+__device__ __forceinline__ void totals_zero(MfmaTotals<NTT, NM>& T, int lane) {
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) T.v[tt][m][g][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+// total += chain (round to nearest), chain = 0.
+__device__ __forceinline__ void fold16(float4* tot, float (&c)[16], int lane) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float4 t = tot[g * 64 + lane];
+    t.x = __fadd_rn(t.x, c[4 * g + 0]);
+    t.y = __fadd_rn(t.y, c[4 * g + 1]);
+    t.z = __fadd_rn(t.z, c[4 * g + 2]);
+    t.w = __fadd_rn(t.w, c[4 * g + 3]);
+    tot[g * 64 + lane] = t;
+    c[4 * g + 0] = c[4 * g + 1] = c[4 * g + 2] = c[4 * g + 3] = 0.0f;
+  }
+}
+
+__device__ __forceinline__ void totals_get(const float4* tot, float (&o)[16], int lane) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float4 t = tot[g * 64 + lane];
+    o[4 * g + 0] = t.x;
+    o[4 * g + 1] = t.y;
+    o[4 * g + 2] = t.z;
+    o[4 * g + 3] = t.w;
+  }
+}
 
 // 32 gate rows and the matching 32 up rows per wavefront (one 32x32 MFMA tile
-// each), NTT x 32 tokens. t32 = index of the 32-row block.
+// each), NTT x 32 tokens. t32 = index of the 32-row block. Columns past the
+// bucket's end compute on the last token (a valid address) and are never
+// stored; each column's results depend on that column alone.
 template <int NTT, int PF, bool TAP>
 __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w13, const float* s13,
-                                 int t32, int lane) {
+                                 int t32, int lane, MfmaTotals<NTT, 2>& T) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nb = H / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -426,136 +459,130 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
     const int j = t0 + tt * 32 + col;
     valid[tt] = j < k.n;
     const int p = k.p0 + min(j, k.n - 1);
-    const int tok = token_of(a, k, p);
-    xq[tt] = a.qx + (size_t)tok * H + 16 * half;
-    xd[tt] = a.dx + (size_t)tok * nb;
+    xq[tt] = a.xt + pb_off(p, 0, nb) + 16 * half;
+    xd[tt] = a.xdt + pb_sc(p, 0, nb);
     if (TAP && valid[tt] && slot_of(a, k, p) == a.sum_slot) tap_tt = tt;
   }
+  totals_zero(T, lane);
   const v16i zero = {0};
-  {
-    const int r0 = tile * 64 + s * 32;
-    constexpr size_t bs = kBlkStride;
-    const uint8_t* gbase = w13 + tb_off(tile, 0, nb) + s * 512;
-    const uint8_t* ubase = w13 + tb_off(I / 64 + tile, 0, nb) + s * 512;
-    float ag[NTT][16], au[NTT][16], tg[NTT][16], tu[NTT][16];  // class chains, totals
+  const int r0 = tile * 64 + s * 32;
+  constexpr size_t bs = kBlkStride;
+  const uint8_t* gbase = w13 + tb_off(tile, 0, nb) + s * 512 + loff;
+  const uint8_t* ubase = w13 + tb_off(I / 64 + tile, 0, nb) + s * 512 + loff;
+  float ag[NTT][16], au[NTT][16];  // class chains
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
+  for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ag[tt][i] = au[tt][i] = tg[tt][i] = tu[tt][i] = 0.0f;
-    v2i rg[PF], ru[PF];
-    v4i rb[PF][NTT];
-    float rd[PF][NTT];
-    bool unused;
+    for (int i = 0; i < 16; ++i) ag[tt][i] = au[tt][i] = 0.0f;
+  v2i rg[PF], ru[PF];
+  v4i rb[PF][NTT];
+  float rd[PF][NTT];
+  int fetch = 0;  // next block to load
 #pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const int bb = class_major_block(min(kk, nb - 1), nb, unused);
-      rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)bb * bs + loff);
-      ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)bb * bs + loff);
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)bb * 32);
-        rd[kk][tt] = xd[tt][bb];
-      }
-    }
-    for (int b0 = 0; b0 < nb; b0 += PF) {
-#pragma unroll
-      for (int kk = 0; kk < PF; ++kk) {
-        bool fold;
-        const int blk = class_major_block(b0 + kk, nb, fold);
-        const v4i Ag = unpack_a(rg[kk]), Au = unpack_a(ru[kk]);
-        v4i bv[NTT];
-        float dv[NTT];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          bv[tt] = valid[tt] ? rb[kk][tt] : v4i{0, 0, 0, 0};
-          dv[tt] = valid[tt] ? rd[kk][tt] : 0.0f;
-        }
-        const int nxt = class_major_block(min(b0 + kk + PF, nb - 1), nb, unused);
-        rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)nxt * bs + loff);
-        ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)nxt * bs + loff);
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)nxt * 32);
-          rd[kk][tt] = xd[tt][nxt];
-        }
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, bv[tt], zero, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(dv[tt], (float)Sg[i], ag[tt][i]);
-          if (TAP && tt == tap_tt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = Sg[i];
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          const v16i Su = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, bv[tt], zero, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) au[tt][i] = fmaf(dv[tt], (float)Su[i], au[tt][i]);
-          if (TAP && tt == tap_tt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = Su[i];
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (fold) {
-#pragma unroll
-          for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              tg[tt][i] = __fadd_rn(tg[tt][i], ag[tt][i]);
-              tu[tt][i] = __fadd_rn(tu[tt][i], au[tt][i]);
-              ag[tt][i] = au[tt][i] = 0.0f;
-            }
-        }
-      }
-    }
-    float sg[16], su[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sg[i] = s13[r0 + out_row(i, lane)];
-      su[i] = s13[I + r0 + out_row(i, lane)];
-    }
+  for (int kk = 0; kk < PF; ++kk) {
+    rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)fetch * bs);
+    ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)fetch * bs);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-      float h[16];
-      float amax = 0.0f;
+      rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)fetch * kPbBlkStride);
+      rd[kk][tt] = xd[tt][(size_t)fetch * kPbScStride];
+    }
+    fetch = class_major_next(fetch, nb);
+  }
+  int blk = 0;  // block being consumed
+  for (int b0 = 0; b0 < nb; b0 += PF) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        h[i] = swiglu_f(__fmul_rn(sg[i], tg[tt][i]), __fmul_rn(su[i], tu[tt][i]));
-        amax = fmaxf(amax, fabsf(h[i]));
-        __builtin_amdgcn_sched_barrier(0);  // one fp64 exp at a time keeps the epilogue's registers low
-      }
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      const float d = __fdiv_rn(amax, 127.0f);
-      const float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
-      if (!valid[tt]) continue;
-      const int p = k.p0 + t0 + tt * 32 + col;
-      const bool tp = a.t_h || a.t_qh || a.t_dh;
-      const int slot = tp ? slot_of(a, k, p) : 0;
-      int8_t* qrow = a.qh + (size_t)p * I + r0;
+    for (int kk = 0; kk < PF; ++kk) {
+      const v4i Ag = unpack_a(rg[kk]), Au = unpack_a(ru[kk]);
+      v4i bv[NTT];
+      float dv[NTT];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float rr = roundf(__fmul_rn(h[i], inv));
-        rr = fminf(fmaxf(rr, -127.0f), 127.0f);
-        const int8_t q = (int8_t)(int)rr;
-        const int m = out_row(i, lane);
-        qrow[perm32(m)] = q;
-        if (a.t_h) a.t_h[(size_t)slot * I + r0 + m] = h[i];
-        if (a.t_qh) a.t_qh[(size_t)slot * I + r0 + m] = q;
+      for (int tt = 0; tt < NTT; ++tt) {
+        bv[tt] = rb[kk][tt];
+        dv[tt] = rd[kk][tt];
       }
-      if (half == 0) {
-        a.dh[(size_t)p * (I / 32) + r0 / 32] = d;
-        if (a.t_dh) a.t_dh[(size_t)slot * (I / 32) + r0 / 32] = d;
+      rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)fetch * bs);
+      ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)fetch * bs);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)fetch * kPbBlkStride);
+        rd[kk][tt] = xd[tt][(size_t)fetch * kPbScStride];
       }
+      fetch = class_major_next(fetch, nb);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, bv[tt], zero, 0, 0, 0);
+        const v16i Su = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, bv[tt], zero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(dv[tt], (float)Sg[i], ag[tt][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) au[tt][i] = fmaf(dv[tt], (float)Su[i], au[tt][i]);
+        if (TAP && tt == tap_tt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = Sg[i];
+            a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = Su[i];
+          }
+        }
+      }
+      if (blk + kDotClasses >= nb) {  // blk ends its class
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) {
+          fold16(&T.v[tt][0][0][0], ag[tt], lane);
+          fold16(&T.v[tt][1][0][0], au[tt], lane);
+        }
+      }
+      blk = class_major_next(blk, nb);
+    }
+  }
+  float sg[16], su[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sg[i] = s13[r0 + out_row(i, lane)];
+    su[i] = s13[I + r0 + out_row(i, lane)];
+  }
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    float tg[16], tu[16], h[16];
+    totals_get(&T.v[tt][0][0][0], tg, lane);
+    totals_get(&T.v[tt][1][0][0], tu, lane);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      h[i] = swiglu_f(__fmul_rn(sg[i], tg[i]), __fmul_rn(su[i], tu[i]));
+      amax = fmaxf(amax, fabsf(h[i]));
+      __builtin_amdgcn_sched_barrier(0);  // one fp64 exp at a time keeps the epilogue's registers low
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float d = __fdiv_rn(amax, 127.0f);
+    const float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
+    if (!valid[tt]) continue;
+    const int p = k.p0 + t0 + tt * 32 + col;
+    const bool tp = a.t_h || a.t_qh || a.t_dh;
+    const int slot = tp ? slot_of(a, k, p) : 0;
+    int8_t* qrow = a.ht + pb_off(p, r0 / 32, I / 32);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float rr = roundf(__fmul_rn(h[i], inv));
+      rr = fminf(fmaxf(rr, -127.0f), 127.0f);
+      const int8_t q = (int8_t)(int)rr;
+      const int m = out_row(i, lane);
+      qrow[perm32(m)] = q;
+      if (a.t_h) a.t_h[(size_t)slot * I + r0 + m] = h[i];
+      if (a.t_qh) a.t_qh[(size_t)slot * I + r0 + m] = q;
+    }
+    if (half == 0) {
+      a.hdt[pb_sc(p, r0 / 32, I / 32)] = d;
+      if (a.t_dh) a.t_dh[(size_t)slot * (I / 32) + r0 / 32] = d;
     }
   }
 }
 
 // 32 output rows per wavefront, NTT x 32 positions. t32 = index of the
-// 32-row block.
+// 32-row block. Columns past the bucket's end as in the gate/up tile.
 template <int NTT, int PF, bool TAP>
 __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w2, const float* s2,
-                               int t32, int lane) {
+                               int t32, int lane, MfmaTotals<NTT, 1>& T) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nbi = I / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -569,97 +596,123 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
     const int j = t0 + tt * 32 + col;
     valid[tt] = j < k.n;
     const int p = k.p0 + min(j, k.n - 1);
-    hq[tt] = a.qh + (size_t)p * I + 16 * half;
-    hd[tt] = a.dh + (size_t)p * nbi;
+    hq[tt] = a.ht + pb_off(p, 0, nbi) + 16 * half;
+    hd[tt] = a.hdt + pb_sc(p, 0, nbi);
     if (TAP && valid[tt] && slot_of(a, k, p) == a.sum_slot) tap_tt = tt;
   }
+  totals_zero(T, lane);
   const v16i zero = {0};
-  {
-    const int r0 = tile * 64 + s * 32;
-    constexpr size_t bs = kBlkStride;
-    const uint8_t* wbase = w2 + tb_off(tile, 0, nbi) + s * 512;
-    float acc[NTT][16], tot[NTT][16];  // class chain, total
+  const int r0 = tile * 64 + s * 32;
+  constexpr size_t bs = kBlkStride;
+  const uint8_t* wbase = w2 + tb_off(tile, 0, nbi) + s * 512 + loff;
+  float acc[NTT][16];  // class chain
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
+  for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[tt][i] = tot[tt][i] = 0.0f;
-    v2i ra[PF];
-    v4i rb[PF][NTT];
-    float rd[PF][NTT];
-    bool unused;
+    for (int i = 0; i < 16; ++i) acc[tt][i] = 0.0f;
+  v2i ra[PF];
+  v4i rb[PF][NTT];
+  float rd[PF][NTT];
+  int fetch = 0;
 #pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const int bb = class_major_block(min(kk, nbi - 1), nbi, unused);
-      ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)bb * bs + loff);
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)bb * 32);
-        rd[kk][tt] = hd[tt][bb];
-      }
-    }
-    for (int b0 = 0; b0 < nbi; b0 += PF) {
-#pragma unroll
-      for (int kk = 0; kk < PF; ++kk) {
-        bool fold;
-        const int blk = class_major_block(b0 + kk, nbi, fold);
-        const v4i A = unpack_a(ra[kk]);
-        v4i bv[NTT];
-        float dv[NTT];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          bv[tt] = valid[tt] ? rb[kk][tt] : v4i{0, 0, 0, 0};
-          dv[tt] = valid[tt] ? rd[kk][tt] : 0.0f;
-        }
-        const int nxt = class_major_block(min(b0 + kk + PF, nbi - 1), nbi, unused);
-        ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)nxt * bs + loff);
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)nxt * 32);
-          rd[kk][tt] = hd[tt][nxt];
-        }
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bv[tt], zero, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(dv[tt], (float)S[i], acc[tt][i]);
-          if (TAP && tt == tap_tt) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = S[i];
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (fold) {
-#pragma unroll
-          for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              tot[tt][i] = __fadd_rn(tot[tt][i], acc[tt][i]);
-              acc[tt][i] = 0.0f;
-            }
-        }
-      }
-    }
-    float so[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) so[i] = s2[r0 + out_row(i, lane)];
+  for (int kk = 0; kk < PF; ++kk) {
+    ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)fetch * bs);
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-      if (!valid[tt]) continue;
-      const int p = k.p0 + t0 + tt * 32 + col;
-      float* orow = a.eout + (size_t)p * H + r0;
-      float* trow = a.t_eout ? a.t_eout + (size_t)slot_of(a, k, p) * H + r0 : nullptr;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4 v;
-        v.x = __fmul_rn(so[4 * g + 0], tot[tt][4 * g + 0]);
-        v.y = __fmul_rn(so[4 * g + 1], tot[tt][4 * g + 1]);
-        v.z = __fmul_rn(so[4 * g + 2], tot[tt][4 * g + 2]);
-        v.w = __fmul_rn(so[4 * g + 3], tot[tt][4 * g + 3]);
-        const int mm = 8 * g + 4 * half;
-        *reinterpret_cast<float4*>(orow + mm) = v;
-        if (trow) *reinterpret_cast<float4*>(trow + mm) = v;
-      }
+      rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)fetch * kPbBlkStride);
+      rd[kk][tt] = hd[tt][(size_t)fetch * kPbScStride];
     }
+    fetch = class_major_next(fetch, nbi);
+  }
+  int blk = 0;
+  for (int b0 = 0; b0 < nbi; b0 += PF) {
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) {
+      const v4i A = unpack_a(ra[kk]);
+      v4i bv[NTT];
+      float dv[NTT];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        bv[tt] = rb[kk][tt];
+        dv[tt] = rd[kk][tt];
+      }
+      ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)fetch * bs);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)fetch * kPbBlkStride);
+        rd[kk][tt] = hd[tt][(size_t)fetch * kPbScStride];
+      }
+      fetch = class_major_next(fetch, nbi);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bv[tt], zero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(dv[tt], (float)S[i], acc[tt][i]);
+        if (TAP && tt == tap_tt) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = S[i];
+        }
+      }
+      if (blk + kDotClasses >= nbi) {
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) fold16(&T.v[tt][0][0][0], acc[tt], lane);
+      }
+      blk = class_major_next(blk, nbi);
+    }
+  }
+  float so[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) so[i] = s2[r0 + out_row(i, lane)];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    if (!valid[tt]) continue;
+    float tot[16];
+    totals_get(&T.v[tt][0][0][0], tot, lane);
+    const int p = k.p0 + t0 + tt * 32 + col;
+    float* orow = a.eout + (size_t)p * H + r0;
+    float* trow = a.t_eout ? a.t_eout + (size_t)slot_of(a, k, p) * H + r0 : nullptr;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float4 v;
+      v.x = __fmul_rn(so[4 * g + 0], tot[4 * g + 0]);
+      v.y = __fmul_rn(so[4 * g + 1], tot[4 * g + 1]);
+      v.z = __fmul_rn(so[4 * g + 2], tot[4 * g + 2]);
+      v.w = __fmul_rn(so[4 * g + 3], tot[4 * g + 3]);
+      const int mm = 8 * g + 4 * half;
+      *reinterpret_cast<float4*>(orow + mm) = v;
+      if (trow) *reinterpret_cast<float4*>(trow + mm) = v;
+    }
+  }
+}
+
+// Copies the x codes and block scales of the positions of every MFMA tile
+// into the position-blocked layout, so that each B operand of the gate/up
+// tiles (32 positions x one block) is read as one contiguous KB. Blocks are
+// split over gridDim.y.
+__global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t* __restrict__ tiles,
+                                                     const int32_t* __restrict__ n_tiles, int tok_tile) {
+  const int y = blockIdx.x;
+  if (y >= *cptr(n_tiles)) return;
+  const Bucket k = load_bucket(a, cptr(tiles)[2 * y]);
+  const int t0 = cptr(tiles)[2 * y + 1];
+  const int nv = min(tok_tile, k.n - t0);
+  __shared__ int s_tok[kMfmaTokTile * 2];
+  const int tid = threadIdx.x;
+  if (tid < nv) s_tok[tid] = token_of(a, k, k.p0 + t0 + tid);
+  __syncthreads();
+  const int H = a.H, nb = H / 32;
+  const int b_lo = nb * blockIdx.y / gridDim.y, b_hi = nb * (blockIdx.y + 1) / gridDim.y;
+  const int items = (b_hi - b_lo) * nv * 2;  // 16-byte halves of (block, position)
+  for (int it = tid; it < items; it += 256) {
+    const int half = it & 1, jb = it >> 1;
+    const int j = jb % nv, b = b_lo + jb / nv;
+    const v4i v = *reinterpret_cast<const v4i*>(a.qx + (size_t)s_tok[j] * H + b * 32 + 16 * half);
+    *reinterpret_cast<v4i*>(a.xt + pb_off(k.p0 + t0 + j, b, nb) + 16 * half) = v;
+  }
+  const int sitems = (b_hi - b_lo) * nv;
+  for (int it = tid; it < sitems; it += 256) {
+    const int j = it % nv, b = b_lo + it / nv;
+    a.xdt[pb_sc(k.p0 + t0 + j, b, nb)] = a.dx[(size_t)s_tok[j] * nb + b];
   }
 }
 
@@ -710,7 +763,8 @@ __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t*
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, (size_t)a.I * a.H);
   const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
-  mfma_gateup_tile<NTT, MPF, TAP>(a, k, t0, w13, s13, tile, lane);
+  __shared__ MfmaTotals<NTT, 2> totals;
+  mfma_gateup_tile<NTT, MPF, TAP>(a, k, t0, w13, s13, tile, lane, totals);
 }
 
 template <int NTT, int MPF, bool TAP>
@@ -722,7 +776,8 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, (size_t)a.H * a.I / 2);
   const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
-  mfma_down_tile<NTT, MPF, TAP>(a, k, t0, w2, s2, tile, lane);
+  __shared__ MfmaTotals<NTT, 1> totals;
+  mfma_down_tile<NTT, MPF, TAP>(a, k, t0, w2, s2, tile, lane, totals);
 }
 
 static bool deep8(int nblocks) { return nblocks % 8 == 0; }
@@ -801,6 +856,14 @@ static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, 
     if (tap) k_down_mfma<NTT, 2, true><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_down_mfma<NTT, 2, false><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   }
+}
+
+hipError_t launch_tile_gather(const ExpertArgs& a, int grid, int tok_tile, const int32_t* tiles,
+                              const int32_t* n_tiles, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (tok_tile > 2 * kMfmaTokTile) return hipErrorInvalidValue;
+  k_tile_gather<<<dim3(grid, std::min(8, a.H / 32)), 256, 0, st>>>(a, tiles, n_tiles, tok_tile);
+  return hipGetLastError();
 }
 
 hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,

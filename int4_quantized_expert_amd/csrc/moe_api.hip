@@ -62,6 +62,11 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.qh = take((size_t)L.R * L.I);
   L.dh = take((size_t)L.R * (L.I / 32) * 4);
   L.eout = take((size_t)L.R * L.H * 4);
+  const size_t rp = (size_t)((L.R + 31) / 32) * 32;  // positions rounded up to whole 32-position groups
+  L.xt = take(rp * L.H);
+  L.xdt = take(rp * (L.H / 32) * 4);
+  L.ht = take(rp * L.I);
+  L.hdt = take(rp * (L.I / 32) * 4);
   L.part = take((size_t)T * 64 * L.E * 8);  // router chunk partials, every batch size
   L.total = off;
   return L;
@@ -215,6 +220,10 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
   a.qh = reinterpret_cast<int8_t*>(wsb + L.qh);
   a.dh = reinterpret_cast<float*>(wsb + L.dh);
   a.eout = reinterpret_cast<float*>(wsb + L.eout);
+  a.xt = reinterpret_cast<int8_t*>(wsb + L.xt);
+  a.xdt = reinterpret_cast<float*>(wsb + L.xdt);
+  a.ht = reinterpret_cast<int8_t*>(wsb + L.ht);
+  a.hdt = reinterpret_cast<float*>(wsb + L.hdt);
   if (tp) {
     a.t_h = tp->h;
     a.t_qh = tp->qh;
@@ -365,6 +374,7 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
     e = hipEventRecord(hp.fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.fork, 0);
     prof_mark(call, 9, hp.side);
+    if (e == hipSuccess) e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, hp.side);
     if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 10, hp.side);
     if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);

@@ -377,6 +377,7 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
     a.list_count = L;
     const int32_t* tiles = L + 2 + 2 * ng;
     const int32_t* n_tiles = L + 1;
+    if (e == hipSuccess && nt > 0) e = launch_tile_gather(a, nt, f.tok_tile, tiles, n_tiles, compute);
     if (e == hipSuccess && nt > 0) e = launch_mfma_gateup(a, nt, f.tok_tile / 32, tiles, n_tiles, compute);
     if (e == hipSuccess && nt > 0) e = launch_mfma_down(a, nt, f.tok_tile / 32, tiles, n_tiles, compute);
     if (e == hipSuccess && ng > 0) e = launch_gemv_gateup(a, ng, f.many, f.gemv_chunk, compute);

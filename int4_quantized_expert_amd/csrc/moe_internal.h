@@ -38,7 +38,7 @@ struct Layout {
   int64_t T = 0, E = 0, K = 0, H = 0, I = 0, NS = 0, TK = 0, R = 0, NB = 0, TILES = 0;
   size_t z = 0, ids = 0, w = 0, flags = 0, counts = 0, offsets = 0, sorted = 0, slotpos = 0, unique = 0,
          nunique = 0, bk_e = 0, bk_p0 = 0, bk_n = 0, gemv = 0, tiles = 0, meta = 0, pos_token = 0, qx = 0,
-         dx = 0, qh = 0, dh = 0, eout = 0, part = 0, total = 0;
+         dx = 0, qh = 0, dh = 0, eout = 0, xt = 0, xdt = 0, ht = 0, hdt = 0, part = 0, total = 0;
 };
 
 Layout make_layout(const moe_config& c, int64_t T);
@@ -71,6 +71,12 @@ struct ExpertArgs {
   int8_t* qh;                 // [R][I] permuted Q8_0 codes of h (written by gate-up, read by down)
   float* dh;                  // [R][I/32]
   float* eout;                // [R][H]
+  // MFMA operands in position-blocked layout: codes of position p, block b at
+  // ((p/32)*blocks + b)*1024 + (p%32)*32, scales at ((p/32)*blocks + b)*32 + p%32
+  int8_t* xt;                 // x codes of MFMA positions (written by the tile gather)
+  float* xdt;
+  int8_t* ht;                 // h codes of MFMA positions (written by gate-up, read by down)
+  float* hdt;
   // taps (nullable), indexed by slot row
   float* t_h;
   int8_t* t_qh;
@@ -117,6 +123,18 @@ __host__ __device__ __forceinline__ size_t tb_off(int tile, int blk, int nblocks
   return ((size_t)tile * nblocks + blk) * 1024;
 }
 constexpr size_t kBlkStride = 1024;  // bytes from block b to block b+1 of a tile
+
+// Q8_0 operands of the MFMA tiles are kept position-blocked: the codes of 32
+// consecutive positions for one 32-element block are one contiguous KB (32
+// bytes per position), blocks of a 32-position group follow each other; the
+// block scales use the same order with 4 bytes per position.
+__host__ __device__ __forceinline__ size_t pb_off(int p, int blk, int nblocks) {
+  return ((size_t)(p >> 5) * nblocks + blk) * 1024 + (size_t)(p & 31) * 32;
+}
+__host__ __device__ __forceinline__ size_t pb_sc(int p, int blk, int nblocks) {
+  return ((size_t)(p >> 5) * nblocks + blk) * 32 + (size_t)(p & 31);
+}
+constexpr size_t kPbBlkStride = 1024, kPbScStride = 32;  // block b -> b+1 of one position
 
 // ------------------------------------------------------------ device helpers
 
@@ -181,6 +199,8 @@ hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int g
                            int32_t* unique, int32_t* nunique, hipStream_t st);
 hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
 hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
+hipError_t launch_tile_gather(const ExpertArgs& a, int grid, int tok_tile, const int32_t* tiles,
+                              const int32_t* n_tiles, hipStream_t st);
 hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
                               hipStream_t st);
 hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
