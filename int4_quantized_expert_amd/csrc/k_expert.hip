@@ -112,6 +112,19 @@ __device__ __forceinline__ v4i unpack_a(v2i w) {
   return r;
 }
 
+// The MFMA A operand: the same order as unpack_a, but each nibble lands in the
+// high half of its byte, i.e. as the int8 value 16 * n (no sign fix-up needed).
+// The MFMA tiles compensate with operand block scales stored divided by 16, so
+// every product d * S they accumulate is the same as with unscaled codes.
+__device__ __forceinline__ v4i unpack_a16(v2i w) {
+  v4i r;
+  r.x = (int)(((uint32_t)w.x << 4) & 0xF0F0F0F0u);
+  r.y = (int)((uint32_t)w.x & 0xF0F0F0F0u);
+  r.z = (int)(((uint32_t)w.y << 4) & 0xF0F0F0F0u);
+  r.w = (int)((uint32_t)w.y & 0xF0F0F0F0u);
+  return r;
+}
+
 __device__ __forceinline__ int out_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 // SwiGLU + Q8_0 of h for 64 consecutive rows held one per lane; writes the
@@ -439,6 +452,56 @@ __device__ __forceinline__ void totals_get(const float4* tot, float (&o)[16], in
   }
 }
 
+// Raw buffer resources over wave-uniform bases: a block's loads take the block
+// offset in a scalar register and the lane's offset in a vector register, so
+// the K walk needs no per-lane address arithmetic. Every offset used stays
+// far below the record limit.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ v2i buf_v2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ v4i buf_v4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
+// Loads of K block blk: weights at blk * 1 KB + lane offset, operand codes at
+// blk * 1 KB + lane offset, scales at blk * 128 B + lane offset.
+template <int NTT>
+__device__ __forceinline__ void load_operands(__amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t dr, int blk,
+                                              const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT], v4i (&rb)[NTT],
+                                              float (&rd)[NTT]) {
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    rb[tt] = buf_v4(xr, xo[tt], (uint32_t)blk * kPbBlkStride);
+    rd[tt] = buf_f32(dr, xso[tt], (uint32_t)blk * kPbScStride * 4);
+  }
+}
+
+template <int NTT>
+__device__ __forceinline__ void load_gu_block(__amdgpu_buffer_rsrc_t gr, __amdgpu_buffer_rsrc_t ur,
+                                              __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t dr, int blk,
+                                              uint32_t loff, const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT],
+                                              v2i& rg, v2i& ru, v4i (&rb)[NTT], float (&rd)[NTT]) {
+  rg = buf_v2(gr, loff, (uint32_t)blk * kBlkStride);
+  ru = buf_v2(ur, loff, (uint32_t)blk * kBlkStride);
+  load_operands<NTT>(xr, dr, blk, xo, xso, rb, rd);
+}
+
+template <int NTT>
+__device__ __forceinline__ void load_dn_block(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr,
+                                              __amdgpu_buffer_rsrc_t dr, int blk, uint32_t loff,
+                                              const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT], v2i& ra,
+                                              v4i (&rb)[NTT], float (&rd)[NTT]) {
+  ra = buf_v2(wr, loff, (uint32_t)blk * kBlkStride);
+  load_operands<NTT>(xr, dr, blk, xo, xso, rb, rd);
+}
+
 // 32 gate rows and the matching 32 up rows per wavefront (one 32x32 MFMA tile
 // each), NTT x 32 tokens. t32 = index of the 32-row block. Columns past the
 // bucket's end compute on the last token (a valid address) and are never
@@ -450,8 +513,12 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   const int H = a.H, I = a.I, nb = H / 32;
   const int col = lane & 31, half = lane >> 5;
   const uint32_t loff = (uint32_t)col * 16 + 8 * half;
-  const int8_t* xq[NTT];
-  const float* xd[NTT];
+  // Operand addresses: a wave-uniform base per block (scalar registers) plus a
+  // 32-bit lane offset from the tile's first 32-position group.
+  const int g0 = (k.p0 + t0) >> 5;
+  const int8_t* xbase = a.xt + pb_off(g0 * 32, 0, nb);
+  const char* dbase = reinterpret_cast<const char*>(a.xdt + pb_sc(g0 * 32, 0, nb));
+  uint32_t xo[NTT], xso[NTT];
   bool valid[NTT];
   int tap_tt = -1;
 #pragma unroll
@@ -459,16 +526,16 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
     const int j = t0 + tt * 32 + col;
     valid[tt] = j < k.n;
     const int p = k.p0 + min(j, k.n - 1);
-    xq[tt] = a.xt + pb_off(p, 0, nb) + 16 * half;
-    xd[tt] = a.xdt + pb_sc(p, 0, nb);
+    xo[tt] = (uint32_t)(pb_off(p, 0, nb) - pb_off(g0 * 32, 0, nb)) + 16 * half;
+    xso[tt] = (uint32_t)(pb_sc(p, 0, nb) - pb_sc(g0 * 32, 0, nb)) * 4;
     if (TAP && valid[tt] && slot_of(a, k, p) == a.sum_slot) tap_tt = tt;
   }
   totals_zero(T, lane);
   const v16i zero = {0};
   const int r0 = tile * 64 + s * 32;
-  constexpr size_t bs = kBlkStride;
-  const uint8_t* gbase = w13 + tb_off(tile, 0, nb) + s * 512 + loff;
-  const uint8_t* ubase = w13 + tb_off(I / 64 + tile, 0, nb) + s * 512 + loff;
+  const auto gr = buf_rsrc(w13 + tb_off(tile, 0, nb) + s * 512);
+  const auto ur = buf_rsrc(w13 + tb_off(I / 64 + tile, 0, nb) + s * 512);
+  const auto xr = buf_rsrc(xbase), dr = buf_rsrc(dbase);
   float ag[NTT][16], au[NTT][16];  // class chains
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
@@ -480,51 +547,33 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   int fetch = 0;  // next block to load
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
-    rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)fetch * bs);
-    ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)fetch * bs);
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-      rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)fetch * kPbBlkStride);
-      rd[kk][tt] = xd[tt][(size_t)fetch * kPbScStride];
-    }
+    load_gu_block(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
     fetch = class_major_next(fetch, nb);
   }
   int blk = 0;  // block being consumed
   for (int b0 = 0; b0 < nb; b0 += PF) {
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const v4i Ag = unpack_a(rg[kk]), Au = unpack_a(ru[kk]);
-      v4i bv[NTT];
-      float dv[NTT];
+      const v4i Ag = unpack_a16(rg[kk]), Au = unpack_a16(ru[kk]);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        bv[tt] = rb[kk][tt];
-        dv[tt] = rd[kk][tt];
-      }
-      rg[kk] = *reinterpret_cast<const v2i*>(gbase + (size_t)fetch * bs);
-      ru[kk] = *reinterpret_cast<const v2i*>(ubase + (size_t)fetch * bs);
+        const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, rb[kk][tt], zero, 0, 0, 0);  // 16 x block sums
+        const v16i Su = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, rb[kk][tt], zero, 0, 0, 0);
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        rb[kk][tt] = *reinterpret_cast<const v4i*>(xq[tt] + (size_t)fetch * kPbBlkStride);
-        rd[kk][tt] = xd[tt][(size_t)fetch * kPbScStride];
-      }
-      fetch = class_major_next(fetch, nb);
+        for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(rd[kk][tt], (float)Sg[i], ag[tt][i]);
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, bv[tt], zero, 0, 0, 0);
-        const v16i Su = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, bv[tt], zero, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(dv[tt], (float)Sg[i], ag[tt][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) au[tt][i] = fmaf(dv[tt], (float)Su[i], au[tt][i]);
+        for (int i = 0; i < 16; ++i) au[tt][i] = fmaf(rd[kk][tt], (float)Su[i], au[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = Sg[i];
-            a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = Su[i];
+            a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = Sg[i] >> 4;
+            a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = Su[i] >> 4;
           }
         }
       }
+      // refill the slot just consumed
+      load_gu_block(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
+      fetch = class_major_next(fetch, nb);
       if (blk + kDotClasses >= nb) {  // blk ends its class
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) {
@@ -572,7 +621,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
       if (a.t_qh) a.t_qh[(size_t)slot * I + r0 + m] = q;
     }
     if (half == 0) {
-      a.hdt[pb_sc(p, r0 / 32, I / 32)] = d;
+      a.hdt[pb_sc(p, r0 / 32, I / 32)] = __fmul_rn(d, 0.0625f);  // scale / 16: see unpack_a16
       if (a.t_dh) a.t_dh[(size_t)slot * (I / 32) + r0 / 32] = d;
     }
   }
@@ -587,8 +636,10 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   const int H = a.H, I = a.I, nbi = I / 32;
   const int col = lane & 31, half = lane >> 5;
   const uint32_t loff = (uint32_t)col * 16 + 8 * half;
-  const int8_t* hq[NTT];
-  const float* hd[NTT];
+  const int g0 = (k.p0 + t0) >> 5;
+  const int8_t* xbase = a.ht + pb_off(g0 * 32, 0, nbi);
+  const char* dbase = reinterpret_cast<const char*>(a.hdt + pb_sc(g0 * 32, 0, nbi));
+  uint32_t xo[NTT], xso[NTT];
   bool valid[NTT];
   int tap_tt = -1;
 #pragma unroll
@@ -596,15 +647,15 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
     const int j = t0 + tt * 32 + col;
     valid[tt] = j < k.n;
     const int p = k.p0 + min(j, k.n - 1);
-    hq[tt] = a.ht + pb_off(p, 0, nbi) + 16 * half;
-    hd[tt] = a.hdt + pb_sc(p, 0, nbi);
+    xo[tt] = (uint32_t)(pb_off(p, 0, nbi) - pb_off(g0 * 32, 0, nbi)) + 16 * half;
+    xso[tt] = (uint32_t)(pb_sc(p, 0, nbi) - pb_sc(g0 * 32, 0, nbi)) * 4;
     if (TAP && valid[tt] && slot_of(a, k, p) == a.sum_slot) tap_tt = tt;
   }
   totals_zero(T, lane);
   const v16i zero = {0};
   const int r0 = tile * 64 + s * 32;
-  constexpr size_t bs = kBlkStride;
-  const uint8_t* wbase = w2 + tb_off(tile, 0, nbi) + s * 512 + loff;
+  const auto wr = buf_rsrc(w2 + tb_off(tile, 0, nbi) + s * 512);
+  const auto xr = buf_rsrc(xbase), dr = buf_rsrc(dbase);
   float acc[NTT][16];  // class chain
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
@@ -616,43 +667,26 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   int fetch = 0;
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
-    ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)fetch * bs);
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) {
-      rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)fetch * kPbBlkStride);
-      rd[kk][tt] = hd[tt][(size_t)fetch * kPbScStride];
-    }
+    load_dn_block(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
     fetch = class_major_next(fetch, nbi);
   }
   int blk = 0;
   for (int b0 = 0; b0 < nbi; b0 += PF) {
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const v4i A = unpack_a(ra[kk]);
-      v4i bv[NTT];
-      float dv[NTT];
+      const v4i A = unpack_a16(ra[kk]);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        bv[tt] = rb[kk][tt];
-        dv[tt] = rd[kk][tt];
-      }
-      ra[kk] = *reinterpret_cast<const v2i*>(wbase + (size_t)fetch * bs);
+        const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, rb[kk][tt], zero, 0, 0, 0);  // 16 x block sums
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        rb[kk][tt] = *reinterpret_cast<const v4i*>(hq[tt] + (size_t)fetch * kPbBlkStride);
-        rd[kk][tt] = hd[tt][(size_t)fetch * kPbScStride];
-      }
-      fetch = class_major_next(fetch, nbi);
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, bv[tt], zero, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(dv[tt], (float)S[i], acc[tt][i]);
+        for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(rd[kk][tt], (float)S[i], acc[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = S[i];
+          for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = S[i] >> 4;
         }
       }
+      load_dn_block(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
+      fetch = class_major_next(fetch, nbi);
       if (blk + kDotClasses >= nbi) {
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) fold16(&T.v[tt][0][0][0], acc[tt], lane);
@@ -687,8 +721,9 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
 
 // Copies the x codes and block scales of the positions of every MFMA tile
 // into the position-blocked layout, so that each B operand of the gate/up
-// tiles (32 positions x one block) is read as one contiguous KB. Blocks are
-// split over gridDim.y.
+// tiles (32 positions x one block) is read as one contiguous KB; the scales
+// are stored divided by 16 (exact: a power of two) to pair with unpack_a16.
+// Blocks are split over gridDim.y.
 __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t* __restrict__ tiles,
                                                      const int32_t* __restrict__ n_tiles, int tok_tile) {
   const int y = blockIdx.x;
@@ -712,7 +747,7 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
   const int sitems = (b_hi - b_lo) * nv;
   for (int it = tid; it < sitems; it += 256) {
     const int j = it % nv, b = b_lo + it / nv;
-    a.xdt[pb_sc(k.p0 + t0 + j, b, nb)] = a.dx[(size_t)s_tok[j] * nb + b];
+    a.xdt[pb_sc(k.p0 + t0 + j, b, nb)] = __fmul_rn(a.dx[(size_t)s_tok[j] * nb + b], 0.0625f);  // see unpack_a16
   }
 }
 
@@ -720,8 +755,8 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
 // Separate GEMV and MFMA kernels keep each path's register budget (and so its
 // occupancy) independent; the host runs the two chains on two streams so they
 // overlap. TAP instantiations write block-sum taps and are launched only when
-// those taps are requested. The MFMA path prefetches 8 blocks for 32-token
-// tiles, 4 for 64.
+// those taps are requested. The MFMA path keeps 4 blocks in flight for
+// 32-token tiles, 2 for 64 (the depth must divide the block count; 2 always does).
 
 // PF: blocks in flight per wavefront (chosen by the host).
 template <int PF, bool TAP>
@@ -764,7 +799,10 @@ __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t*
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, (size_t)a.I * a.H);
   const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
   __shared__ MfmaTotals<NTT, 2> totals;
-  mfma_gateup_tile<NTT, MPF, TAP>(a, k, t0, w13, s13, tile, lane, totals);
+  if (NTT == 2 && k.n - t0 <= 32)  // a bucket's last tile with one 32-token half: skip the empty one
+    mfma_gateup_tile<1, MPF, TAP>(a, k, t0, w13, s13, tile, lane, reinterpret_cast<MfmaTotals<1, 2>&>(totals));
+  else
+    mfma_gateup_tile<NTT, MPF, TAP>(a, k, t0, w13, s13, tile, lane, totals);
 }
 
 template <int NTT, int MPF, bool TAP>
@@ -777,10 +815,12 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, (size_t)a.H * a.I / 2);
   const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
   __shared__ MfmaTotals<NTT, 1> totals;
-  mfma_down_tile<NTT, MPF, TAP>(a, k, t0, w2, s2, tile, lane, totals);
+  if (NTT == 2 && k.n - t0 <= 32)
+    mfma_down_tile<1, MPF, TAP>(a, k, t0, w2, s2, tile, lane, reinterpret_cast<MfmaTotals<1, 1>&>(totals));
+  else
+    mfma_down_tile<NTT, MPF, TAP>(a, k, t0, w2, s2, tile, lane, totals);
 }
 
-static bool deep8(int nblocks) { return nblocks % 8 == 0; }
 
 // Blocks in flight per wavefront: about 4 KB of weights per wavefront when
 // many buckets stream at once (2 blocks of the two gate/up streams, 4 of the
@@ -834,8 +874,8 @@ template <int NTT>
 static void mfma_gateup_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
-  constexpr int MPF = NTT == 1 ? 8 : 4;
-  if (deep8(a.H / 32)) {
+  constexpr int MPF = NTT == 1 ? 4 : 2;
+  if ((a.H / 32) % MPF == 0) {
     if (tap) k_gateup_mfma<NTT, MPF, true><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_gateup_mfma<NTT, MPF, false><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   } else {
@@ -848,8 +888,8 @@ template <int NTT>
 static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                              hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
-  constexpr int MPF = NTT == 1 ? 8 : 4;
-  if (deep8(a.I / 32)) {
+  constexpr int MPF = NTT == 1 ? 4 : 2;
+  if ((a.I / 32) % MPF == 0) {
     if (tap) k_down_mfma<NTT, MPF, true><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_down_mfma<NTT, MPF, false><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   } else {

@@ -74,9 +74,9 @@ struct ExpertArgs {
   // MFMA operands in position-blocked layout: codes of position p, block b at
   // ((p/32)*blocks + b)*1024 + (p%32)*32, scales at ((p/32)*blocks + b)*32 + p%32
   int8_t* xt;                 // x codes of MFMA positions (written by the tile gather)
-  float* xdt;
+  float* xdt;                 // their block scales / 16 (the MFMA A operand holds 16 x the weight codes)
   int8_t* ht;                 // h codes of MFMA positions (written by gate-up, read by down)
-  float* hdt;
+  float* hdt;                 // block scales / 16, as xdt
   // taps (nullable), indexed by slot row
   float* t_h;
   int8_t* t_qh;
