@@ -5,13 +5,17 @@
 // 실행하기", how MoE works: 8 routed experts per token).
 //
 // Logits: the router weights stay fp32 and the products x*w are exact in fp64,
-// so the dot is accumulated in fp64 and rounded once to fp32. Its order is
+// so the dot is accumulated in fp64 and rounded once to fp32. Its structure is
 // fixed and independent of the number of tokens or a token's place in the
 // batch, so a token routes identically alone or inside any batch: H is split
-// into 64 contiguous chunks; each chunk is summed in ascending h; the 64 chunk
-// sums are added in ascending chunk order, starting from 0. One kernel writes
-// the chunk partial sums (token groups x expert blocks x chunks, so even one
-// token spreads over 256 workgroups); the top-k kernel adds them in order.
+// into 64 contiguous chunks; each chunk is accumulated by a fixed sequence of
+// fp64 MFMA steps of four products each; the 64 chunk sums are added in
+// ascending chunk order, starting from 0. One kernel writes the chunk partial
+// sums (token blocks x expert blocks x chunks, so even one token spreads over
+// 256 workgroups); the top-k kernel adds them in order. The logits agree with
+// an exact fp64 dot to far below fp32 resolution, so they round to the same
+// fp32 value except when the exact dot lies within ~1e-16 relative of a
+// rounding boundary.
 #include <limits.h>
 
 #include "moe_internal.h"
@@ -19,117 +23,142 @@
 namespace moe {
 
 #define CAS __attribute__((address_space(4)))
-typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Lane = expert, workgroup (y) = one of the 64 chunks, z = a group of TT tokens
-// (TT = 1, 2 or 4). The lane keeps its expert's row chunk of the router
-// weights in registers (read once, as fp32) and walks the chunk in ascending h;
-// the activations are the same for every lane of the workgroup, so they come
-// from scalar loads and are widened to fp64 on use. Each (token, chunk,
-// expert) partial sum is written in fp64; the top-k kernel adds the 64 partials
-// in ascending chunk order. Workgroups of the first expert block also encode
-// Q8_0 of the activations (blocks j, j+64, ... of each of their tokens), which
-// saves a launch on the latency-bound decode path.
-constexpr int kRouterTT = 4;
-constexpr int kRouterMaxC = 96;  // chunk elements held in registers per pass
+constexpr int kRouterMfmaWideT = 256;  // from this batch size a router workgroup takes 32 tokens
 
 __device__ __forceinline__ uint32_t pack4q(int8_t a, int8_t b, int8_t c, int8_t d) {
   return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
          ((uint32_t)(uint8_t)d << 24);
 }
 
-template <int TT, bool VEC4>
-__global__ __launch_bounds__(64) void k_router_part(const float* __restrict__ x, int T, int H,
+// Q8_0 of x for tokens [t0, t0 + nt) restricted to the blocks j, j + 64, ... of
+// chunk j: lane -> (token, block) pairs. Called by the expert-block-0
+// workgroups of the router kernels, which saves a launch on the decode path.
+__device__ __forceinline__ void q8_x_chunk(const float* __restrict__ x, int T, int H, int j, int t0, int nt, int lane,
+                                           int8_t* __restrict__ qx_perm, float* __restrict__ dx,
+                                           int8_t* __restrict__ qx_nat) {
+  // Q8_0 of x: lane -> (token, block) pairs of this chunk's block set
+  const int nb = H / 32, nbj = (nb - j + 63) / 64;  // blocks j, j+64, ... of one token
+  for (int idx = lane; idx < nt * nbj; idx += 64) {
+    const int tt = idx / nbj, bq = j + 64 * (idx - tt * nbj), t = t0 + tt;
+    if (t >= T) continue;
+    const float* src = x + (size_t)t * H + (size_t)bq * 32;
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 q4 = reinterpret_cast<const float4*>(src)[i];
+      v[4 * i] = q4.x; v[4 * i + 1] = q4.y; v[4 * i + 2] = q4.z; v[4 * i + 3] = q4.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float d = __fdiv_rn(amax, 127.0f);
+    const float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
+    int8_t q[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float r = roundf(__fmul_rn(v[i], inv));
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      q[i] = (int8_t)(int)r;
+    }
+    uint32_t wv[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      wv[2 * g] = pack4q(q[8 * g], q[8 * g + 2], q[8 * g + 4], q[8 * g + 6]);
+      wv[2 * g + 1] = pack4q(q[8 * g + 1], q[8 * g + 3], q[8 * g + 5], q[8 * g + 7]);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(qx_perm + (size_t)t * H + (size_t)bq * 32);
+    dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+    dx[(size_t)t * nb + bq] = d;
+    if (qx_nat) {
+      uint32_t nv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) nv[i] = pack4q(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
+      uint4* nd = reinterpret_cast<uint4*>(qx_nat + (size_t)t * H + (size_t)bq * 32);
+      nd[0] = make_uint4(nv[0], nv[1], nv[2], nv[3]);
+      nd[1] = make_uint4(nv[4], nv[5], nv[6], nv[7]);
+    }
+  }
+}
+
+// Chunk partials on the fp64 matrix cores: v_mfma_f64_16x16x4f64 multiplies
+// 16 tokens x 4 h by 4 h x 16 experts. Lane l feeds token / expert l % 16 and
+// k slot g = l / 16; within a group of 16 h of the chunk, step s (0..3) puts
+// h = 16q + 4g + s in slot g, so each lane loads one float4 per row and group.
+// A workgroup (one wavefront) covers 16 * TB tokens x 64 experts of one chunk.
+// Every (token, expert) result takes the same sequence of MFMA steps wherever
+// its token sits in the batch, so routing stays batch-invariant. Lanes past E
+// or T read a clamped valid row and store nothing.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
+template <int TB, bool VEC4>
+__global__ __launch_bounds__(64) void k_router_mfma(const float* __restrict__ x, int T, int H,
                                                     const float* __restrict__ Wr, int E, double* __restrict__ part,
                                                     int8_t* __restrict__ qx_perm, float* __restrict__ dx,
                                                     int8_t* __restrict__ qx_nat) {
-  const int lane = threadIdx.x, e = blockIdx.x * 64 + lane, j = blockIdx.y, t0 = blockIdx.z * TT;
+  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  const int e0 = blockIdx.x * 64, j = blockIdx.y, t0 = blockIdx.z * 16 * TB;
   const int C = H / 64;
-  const int ec = min(e, E - 1);
-  const float* wrow = Wr + (size_t)ec * H + (size_t)j * C;
-  const CAS float* xr[TT];
+  const float* xrow[TB];
+  const float* wrow[4];
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) xr[tt] = (const CAS float*)(x + (size_t)min(t0 + tt, T - 1) * H + (size_t)j * C);
-  double p[TT];
+  for (int bt = 0; bt < TB; ++bt) xrow[bt] = x + (size_t)min(t0 + 16 * bt + r, T - 1) * H + (size_t)j * C;
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) p[tt] = 0.0;
-  for (int c0 = 0; c0 < C; c0 += kRouterMaxC) {
-    const int cw = min(kRouterMaxC, C - c0);
-    if (VEC4) {
-      float4 wreg[kRouterMaxC / 4];
+  for (int be = 0; be < 4; ++be) wrow[be] = Wr + (size_t)min(e0 + 16 * be + r, E - 1) * H + (size_t)j * C;
+  v4d acc[TB][4];
 #pragma unroll
-      for (int u = 0; u < kRouterMaxC / 4; ++u)
-        if (4 * u < cw) wreg[u] = *reinterpret_cast<const float4*>(wrow + c0 + 4 * u);
+  for (int bt = 0; bt < TB; ++bt)
 #pragma unroll
-      for (int u = 0; u < kRouterMaxC / 4; ++u) {
-        if (4 * u < cw) {
-          const double wv[4] = {(double)wreg[u].x, (double)wreg[u].y, (double)wreg[u].z, (double)wreg[u].w};
+    for (int be = 0; be < 4; ++be) acc[bt][be] = v4d{0.0, 0.0, 0.0, 0.0};
+  for (int h0 = 0; h0 < C; h0 += 16) {
+    float xa[TB][4], wb[4][4];
+    const int hl = h0 + 4 * g;  // this lane's first h of the group
+    if (VEC4 && h0 + 16 <= C) {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int i = c0 + 4 * u + k;
-#pragma unroll
-            for (int tt = 0; tt < TT; ++tt) p[tt] = fma((double)xr[tt][i], wv[k], p[tt]);
-          }
-        }
+      for (int bt = 0; bt < TB; ++bt) {
+        const float4 v = *reinterpret_cast<const float4*>(xrow[bt] + hl);
+        xa[bt][0] = v.x; xa[bt][1] = v.y; xa[bt][2] = v.z; xa[bt][3] = v.w;
       }
-    } else {
-      for (int i = c0; i < c0 + cw; ++i) {
-        const double wv = (double)wrow[i];
 #pragma unroll
-        for (int tt = 0; tt < TT; ++tt) p[tt] = fma((double)xr[tt][i], wv, p[tt]);
+      for (int be = 0; be < 4; ++be) {
+        const float4 v = *reinterpret_cast<const float4*>(wrow[be] + hl);
+        wb[be][0] = v.x; wb[be][1] = v.y; wb[be][2] = v.z; wb[be][3] = v.w;
+      }
+    } else {  // ragged group: h beyond the chunk contributes 0 * 0
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool in = hl + q < C;
+#pragma unroll
+        for (int bt = 0; bt < TB; ++bt) xa[bt][q] = in ? xrow[bt][hl + q] : 0.0f;
+#pragma unroll
+        for (int be = 0; be < 4; ++be) wb[be][q] = in ? wrow[be][hl + q] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int bt = 0; bt < TB; ++bt) {
+        const double av = (double)xa[bt][st];
+#pragma unroll
+        for (int be = 0; be < 4; ++be)
+          acc[bt][be] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, (double)wb[be][st], acc[bt][be], 0, 0, 0);
       }
     }
   }
-  if (e < E) {
+  // lane l holds rows (tokens) l / 16 + 4 i, column (expert) l % 16 of each 16 x 16 block
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
-      if (t0 + tt < T) part[((size_t)(t0 + tt) * 64 + j) * E + e] = p[tt];
-  }
-  if (blockIdx.x == 0 && qx_perm) {
-    // Q8_0 of x: lane -> (token, block) pairs of this chunk's block set
-    const int nb = H / 32, nbj = (nb - j + 63) / 64;  // blocks j, j+64, ... of one token
-    for (int idx = lane; idx < TT * nbj; idx += 64) {
-      const int tt = idx / nbj, bq = j + 64 * (idx - tt * nbj), t = t0 + tt;
-      if (t >= T) continue;
-      const float* src = x + (size_t)t * H + (size_t)bq * 32;
-      float v[32];
+  for (int bt = 0; bt < TB; ++bt)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 q4 = reinterpret_cast<const float4*>(src)[i];
-        v[4 * i] = q4.x; v[4 * i + 1] = q4.y; v[4 * i + 2] = q4.z; v[4 * i + 3] = q4.w;
-      }
-      float amax = 0.0f;
+    for (int be = 0; be < 4; ++be) {
+      const int e = e0 + 16 * be + r;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-      const float d = __fdiv_rn(amax, 127.0f);
-      const float inv = (d == 0.0f) ? 0.0f : __fdiv_rn(1.0f, d);
-      int8_t q[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        float r = roundf(__fmul_rn(v[i], inv));
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        q[i] = (int8_t)(int)r;
-      }
-      uint32_t wv[8];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        wv[2 * g] = pack4q(q[8 * g], q[8 * g + 2], q[8 * g + 4], q[8 * g + 6]);
-        wv[2 * g + 1] = pack4q(q[8 * g + 1], q[8 * g + 3], q[8 * g + 5], q[8 * g + 7]);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(qx_perm + (size_t)t * H + (size_t)bq * 32);
-      dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-      dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
-      dx[(size_t)t * nb + bq] = d;
-      if (qx_nat) {
-        uint32_t nv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) nv[i] = pack4q(q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]);
-        uint4* nd = reinterpret_cast<uint4*>(qx_nat + (size_t)t * H + (size_t)bq * 32);
-        nd[0] = make_uint4(nv[0], nv[1], nv[2], nv[3]);
-        nd[1] = make_uint4(nv[4], nv[5], nv[6], nv[7]);
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * bt + g + 4 * i;
+        if (t < T && e < E) part[((size_t)t * 64 + j) * E + e] = acc[bt][be][i];
       }
     }
-  }
+  if (blockIdx.x == 0 && qx_perm) q8_x_chunk(x, T, H, j, t0, 16 * TB, lane, qx_perm, dx, qx_nat);
 }
 
 __global__ __launch_bounds__(256) void k_router_reduce(const double* __restrict__ part, int T, int E,
@@ -410,12 +439,6 @@ static void topk_fast_launch(int epl, int T, const double* part, const float* bi
 
 // Router + top-k. For T < 64 the logits come as chunk partials and, when
 // qx_perm is given, Q8_0 of x is encoded in the same launch (*q8_done = true).
-template <int TT>
-static void router_part_launch(dim3 grid, bool vec4, const float* x, int T, int H, const float* Wr, int E,
-                               double* part, int8_t* qx_perm, float* dx, int8_t* qx_nat, hipStream_t st) {
-  if (vec4) k_router_part<TT, true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
-  else k_router_part<TT, false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
-}
 
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias, float* z,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
@@ -425,13 +448,15 @@ hipError_t launch_route(const float* x, int T, const moe_config& c, const float*
   if (T <= 0) return hipSuccess;
   const int H = c.hidden, E = c.n_experts;
   const int epl = fast_epl(c);
-  const int tt = T > 2 ? kRouterTT : T;
-  dim3 grid((E + 63) / 64, 64, (T + tt - 1) / tt);
   const bool vec4 = (H / 64) % 4 == 0;
-  switch (tt) {
-    case 1: router_part_launch<1>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
-    case 2: router_part_launch<2>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
-    default: router_part_launch<kRouterTT>(grid, vec4, x, T, H, Wr, E, part, qx_perm, dx, qx_nat, st); break;
+  const int tb = T >= kRouterMfmaWideT ? 2 : 1;  // 16-token blocks per workgroup
+  dim3 grid((E + 63) / 64, 64, (T + 16 * tb - 1) / (16 * tb));
+  if (tb == 2) {
+    if (vec4) k_router_mfma<2, true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    else k_router_mfma<2, false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+  } else {
+    if (vec4) k_router_mfma<1, true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    else k_router_mfma<1, false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
   }
   if (q8_done && qx_perm) *q8_done = true;
   if (mark) mark(mark_call, 1, st);
