@@ -22,6 +22,13 @@ STAGES = ("router", "topk", "dispatch", "q8_x", "gateup_gemv", "down_gemv", "gat
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+# torch ships its own HIP runtime under the same soname as the system one; the
+# library must bind to the runtime torch uses (tensors and streams come from
+# torch), so torch is loaded first whenever it is installed.
+try:
+    import torch  # noqa: F401
+except ImportError:
+    pass
 _lib = ctypes.CDLL(LIB_PATH)
 
 P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float

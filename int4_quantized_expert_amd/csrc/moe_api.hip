@@ -39,7 +39,6 @@ Layout make_layout(const moe_config& c, int64_t T) {
     off = align256(off + std::max<size_t>(bytes, 1));
     return o;
   };
-  L.z = take((size_t)T * L.E * 4);
   L.ids = take((size_t)L.TK * 4);
   L.w = take((size_t)L.TK * 4);
   L.flags = take((size_t)T);
@@ -67,7 +66,7 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.xdt = take(rp * (L.H / 32) * 4);
   L.ht = take(rp * L.I);
   L.hdt = take(rp * (L.I / 32) * 4);
-  L.part = take((size_t)T * 64 * L.E * 8);  // router chunk partials, every batch size
+  L.part = take((size_t)T * kRouterChunks * L.E * 8);  // router chunk partials, every batch size
   L.total = off;
   return L;
 }
@@ -191,7 +190,6 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
   f->slotpos = pick(tp ? tp->slot_pos : (int32_t*)nullptr, L.slotpos);
   f->unique = pick(tp ? tp->unique_ids : (int32_t*)nullptr, L.unique);
   f->nunique = pick(tp ? tp->n_unique : (int32_t*)nullptr, L.nunique);
-  f->z = reinterpret_cast<float*>(wsb + L.z);
   f->qx = reinterpret_cast<int8_t*>(wsb + L.qx);
   f->dx = reinterpret_cast<float*>(wsb + L.dx);
   f->gemm_min = cfg->gemm_min_tokens > 0 ? cfg->gemm_min_tokens : kDefaultGemmMin;
@@ -255,7 +253,7 @@ hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float*
                      hipStream_t stream, int call) {
   const Layout& L = f.L;
   bool q8_done = false;
-  hipError_t e = launch_route(x, f.T, *f.cfg, router_w, router_bias, f.z, reinterpret_cast<double*>(f.wsb + L.part),
+  hipError_t e = launch_route(x, f.T, *f.cfg, router_w, router_bias, reinterpret_cast<double*>(f.wsb + L.part),
                               f.ids, f.w, f.flags, f.qx, f.dx, tp ? tp->qx : nullptr, &q8_done, call, prof_mark,
                               stream);
   prof_mark(call, 2, stream);
@@ -327,8 +325,7 @@ int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float
   Layout L = make_layout(*cfg, T);
   if ((rc = check_ws(L, ws, ws_bytes))) return rc;
   char* wsb = static_cast<char*>(ws);
-  float* z = reinterpret_cast<float*>(wsb + L.z);
-  hipError_t e = launch_route(x, T, *cfg, router_w, router_bias, z, reinterpret_cast<double*>(wsb + L.part), topk_ids,
+  hipError_t e = launch_route(x, T, *cfg, router_w, router_bias, reinterpret_cast<double*>(wsb + L.part), topk_ids,
                               topk_w, near_tie, nullptr, nullptr, nullptr, nullptr, -1, nullptr, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }

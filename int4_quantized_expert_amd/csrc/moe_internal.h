@@ -17,6 +17,7 @@ constexpr int kMaxGroups = 64;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 4;
 constexpr int kMfmaTokTile = 32;     // smallest token tile of the int8-MFMA path
+constexpr int kRouterChunks = 64;  // contiguous H chunks of the router dot (fixed summation structure)
 constexpr int kDefaultGemmMin = 8;   // bucket size from which the MFMA path runs
 constexpr int kMaxHidden = 16384;  // hidden and inter sizes (GEMV stages two 16-byte loads per lane)
 constexpr int kGemvMaxN = 4;         // tokens per GEMV work item (chunk)
@@ -36,7 +37,7 @@ struct Meta {
 // Device workspace layout for T tokens (all offsets 256-byte aligned).
 struct Layout {
   int64_t T = 0, E = 0, K = 0, H = 0, I = 0, NS = 0, TK = 0, R = 0, NB = 0, TILES = 0;
-  size_t z = 0, ids = 0, w = 0, flags = 0, counts = 0, offsets = 0, sorted = 0, slotpos = 0, unique = 0,
+  size_t ids = 0, w = 0, flags = 0, counts = 0, offsets = 0, sorted = 0, slotpos = 0, unique = 0,
          nunique = 0, bk_e = 0, bk_p0 = 0, bk_n = 0, gemv = 0, tiles = 0, meta = 0, pos_token = 0, qx = 0,
          dx = 0, qh = 0, dh = 0, eout = 0, xt = 0, xdt = 0, ht = 0, hdt = 0, part = 0, total = 0;
 };
@@ -100,7 +101,7 @@ struct Fwd {
   bool many = false;
   int32_t *ids = nullptr, *counts = nullptr, *offsets = nullptr, *sorted = nullptr, *slotpos = nullptr,
           *unique = nullptr, *nunique = nullptr;
-  float *w = nullptr, *z = nullptr, *dx = nullptr;
+  float *w = nullptr, *dx = nullptr;
   uint8_t* flags = nullptr;
   int8_t* qx = nullptr;
   const moe_taps* tp = nullptr;
@@ -190,7 +191,7 @@ hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float
 hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hipStream_t st);
 hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed, float* scales,
                              hipStream_t st);
-hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias, float* z,
+hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
                         int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
                         hipStream_t st);

@@ -103,8 +103,9 @@ def test_router_tiny(T):
     assert np.allclose(w.astype(np.float64).sum(1), 2.5, rtol=1e-6)
 
 
-@pytest.mark.parametrize("T", [1, 32, 192])
+@pytest.mark.parametrize("T", [1, 32, 192, 256, 300])
 def test_router_glm(T):
+    """T >= 256 takes the 32-token x 64-expert router tiles; 300 ends in a ragged token block."""
     x = synth.hidden_states(synth.GLM, T, seed=100 + T)
     ids, w, fl, rids, rw, rfl = _router_case(synth.GLM, x)
     clean = (rfl & (O.TIE_EXPERT | O.TIE_GROUP)) == 0
