@@ -30,6 +30,8 @@ import time
 
 import numpy as np
 
+DEFAULT_GEMM_MIN = 5  # the library default of moe_config.gemm_min_tokens
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -98,7 +100,7 @@ def routing_stats(moe, cfg, layer, x_dev, ws, gemm_min):
             torch.empty(E, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev)]
     moe.moe_dispatch(cfg, ids, *outs, ws)
     counts = outs[0].cpu().numpy()
-    gm = gemm_min if gemm_min > 0 else 8
+    gm = gemm_min if gemm_min > 0 else DEFAULT_GEMM_MIN
     nz = counts[counts > 0]
     return dict(U=int(nz.size), gemv_experts=int((nz < gm).sum()) + (1 if T < gm else 0),
                 mfma_experts=int((nz >= gm).sum()) + (1 if T >= gm else 0),
@@ -420,7 +422,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"glm5.2-moe-layer {args.workload}", "tokens": T, "hidden": H, "experts": E,
                    "groups": shape.n_group, "topk_group": shape.topk_group, "top_k": shape.top_k, "inter": I,
-                   "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or 8,
+                   "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or DEFAULT_GEMM_MIN,
                    "layer_copies": args.copies},
         "layer_hbm_gbs": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9), 1),
         "layer_hbm_frac": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9) / HBM_PEAK_GBS, 4),

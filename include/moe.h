@@ -82,7 +82,9 @@ typedef struct moe_config {
   int32_t n_shared;      /* shared experts, 0..4 */
   float routed_scaling_factor;
   int32_t gemm_min_tokens; /* bucket size from which the int8-MFMA path is used;
-                              <= 0 selects the default. Never changes results. */
+                              <= 0 selects the default (5: a bucket that would
+                              need two GEMV chunks takes one MFMA tile instead).
+                              Never changes results. */
 } moe_config;
 
 /* A layer's weights. Routed arrays hold E experts back to back; shared arrays

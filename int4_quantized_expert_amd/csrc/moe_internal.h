@@ -18,7 +18,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 4;
 constexpr int kMfmaTokTile = 32;     // smallest token tile of the int8-MFMA path
 constexpr int kRouterChunks = 64;  // contiguous H chunks of the router dot (fixed summation structure)
-constexpr int kDefaultGemmMin = 8;   // bucket size from which the MFMA path runs
+constexpr int kDefaultGemmMin = 5;   // bucket size from which the MFMA path runs (a GEMV chunk holds at most 4)
 constexpr int kMaxHidden = 16384;  // hidden and inter sizes (GEMV stages two 16-byte loads per lane)
 constexpr int kGemvMaxN = 4;         // tokens per GEMV work item (chunk)
 constexpr int kDotClasses = 8;       // fp32 accumulation classes of a dot: block b is in class b % 8
