@@ -25,14 +25,26 @@ __global__ __launch_bounds__(64) void k_combine(const float* __restrict__ eout, 
     acc.z = __fadd_rn(acc.z, v.z);
     acc.w = __fadd_rn(acc.w, v.w);
   }
-  for (int k = 0; k < K; ++k) {
-    const float wk = w[(size_t)t * K + k];
-    const size_t p = (size_t)slotpos[(size_t)t * K + k];
-    const float4 v = *reinterpret_cast<const float4*>(eout + p * H + o);
-    acc.x = fmaf(wk, v.x, acc.x);
-    acc.y = fmaf(wk, v.y, acc.y);
-    acc.z = fmaf(wk, v.z, acc.z);
-    acc.w = fmaf(wk, v.w, acc.w);
+  // slots in batches of KB with all their loads in flight, added in slot order
+  constexpr int KB = 8;
+  for (int k0 = 0; k0 < K; k0 += KB) {
+    float wk[KB];
+    float4 v[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int k = min(k0 + u, K - 1);
+      wk[u] = w[(size_t)t * K + k];
+      v[u] = *reinterpret_cast<const float4*>(eout + (size_t)slotpos[(size_t)t * K + k] * H + o);
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (k0 + u < K) {
+        acc.x = fmaf(wk[u], v[u].x, acc.x);
+        acc.y = fmaf(wk[u], v[u].y, acc.y);
+        acc.z = fmaf(wk[u], v[u].z, acc.z);
+        acc.w = fmaf(wk[u], v[u].w, acc.w);
+      }
+    }
   }
   *reinterpret_cast<float4*>(y + (size_t)t * H + o) = acc;
 }
