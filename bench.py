@@ -287,6 +287,7 @@ def run_stack(args):
     hits = sum(b["hits"] - a["hits"] for a, b in zip(st0, st1))
     misses = sum(b["misses"] - a["misses"] for a, b in zip(st0, st1))
     h2d = sum(b["bytes_h2d"] - a["bytes_h2d"] for a, b in zip(st0, st1))
+    h2d_ms = sum(b["h2d_ms"] - a["h2d_ms"] for a, b in zip(st0, st1))
     # pinned host -> device peak of this machine, one 1 GiB copy
     src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -307,7 +308,11 @@ def run_stack(args):
                       "host_copies": min(NSTR, args.host_copies)},
            "hit_rate": round(hits / max(1, hits + misses), 4), "hits": hits, "misses": misses,
            "h2d_bytes_per_step": round(h2d / args.steps), "h2d_gbs_over_step": round(h2d / dt / 1e9, 2),
-           "pinned_h2d_peak_gbs": round(peak, 2), "setup_s": round(t_setup, 1)}
+           "pinned_h2d_peak_gbs": round(peak, 2),
+           # time the copy stream spent moving experts, summed over layers, per step; the rest of the step is
+           # compute that did not overlap a copy
+           "h2d_busy_ms_per_step": round(h2d_ms / args.steps, 2),
+           "h2d_busy_frac": round(h2d_ms / args.steps / ms, 4), "setup_s": round(t_setup, 1)}
     print(json.dumps(out), flush=True)
     for c in caches:
         c.destroy()
@@ -431,6 +436,14 @@ def main():
         "ms_per_step_all_stage_events": round(ms_staged, 5),
         "roofline": roof,
     }
+    # layer-level view: every expert's int8 ops (MFMA and v_dot4 paths) against the dense int8 MFMA peak, and the
+    # larger of the HBM and MFMA lower bounds against the measured step
+    ops_layer = 2.0 * (T * shape.top_k + shape.n_shared * T) * (2 * I * H + H * I)
+    t_mem = layer_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = ops_layer / (INT8_PEAK_TOPS * 1e12)
+    out["layer_int8_ops"] = ops_layer
+    out["layer_int8_mfma_frac"] = round(ops_layer / (ms_step / 1e3) / (INT8_PEAK_TOPS * 1e12), 4)
+    out["combined_roofline_frac"] = round(float(np.mean(np.maximum(t_mem, t_mfma))) / (ms_step / 1e3), 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed)
     print(json.dumps(out), flush=True)
