@@ -367,14 +367,22 @@ int orc_layer_forward(const orc_cfg* c, int32_t T, const float* x, const float* 
  *    first, lower expert id first on equal age;
  *  - consumption order: hits (ascending), then misses in placement order;
  *  - when misses outnumber offered slots, the j-th extra miss takes the slot of
- *    the j-th expert in consumption order, after that expert has been used
- *    (wait_for names it);
- *  - every needed expert gets last use = step. */
+ *    the j-th unpinned expert in consumption order, after that expert has been
+ *    used (wait_for names it);
+ *  - every needed expert gets last use = step.
+ * Learning cache ("Show HN", learning-cache section: the experts a workload is
+ * routed to are recorded, and the most used ones are pinned into spare memory
+ * at start): usage counts the positions routed to each expert over the recorded
+ * steps; a pin call makes the hottest experts resident and exempt from eviction
+ * (see orc_lru_pin_hottest); pinned slots are never offered to misses. */
 struct orc_lru {
   int32_t E, S;
   int32_t* slot_of;   /* [E], -1 if not resident */
   int32_t* expert_in; /* [S], -1 if free */
   int64_t* last_use;  /* [E] */
+  int64_t* usage;     /* [E] positions routed to each expert, summed over recorded steps */
+  uint8_t* pinned;    /* [E] 1 = pinned: resident and never evicted */
+  int32_t n_pinned;
   int64_t hits, misses, evictions;
 };
 
@@ -386,6 +394,8 @@ orc_lru* orc_lru_new(int32_t n_experts, int32_t n_slots) {
   L->slot_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_experts);
   L->expert_in = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_slots);
   L->last_use = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_experts);
+  L->usage = (int64_t*)calloc((size_t)n_experts, sizeof(int64_t));
+  L->pinned = (uint8_t*)calloc((size_t)n_experts, 1);
   for (int32_t e = 0; e < n_experts; ++e) { L->slot_of[e] = -1; L->last_use[e] = -1; }
   for (int32_t s = 0; s < n_slots; ++s) L->expert_in[s] = -1;
   return L;
@@ -393,7 +403,7 @@ orc_lru* orc_lru_new(int32_t n_experts, int32_t n_slots) {
 
 void orc_lru_free(orc_lru* L) {
   if (!L) return;
-  free(L->slot_of); free(L->expert_in); free(L->last_use); free(L);
+  free(L->slot_of); free(L->expert_in); free(L->last_use); free(L->usage); free(L->pinned); free(L);
 }
 
 int orc_lru_step(orc_lru* L, int64_t step, const int32_t* needed, int32_t n_needed, uint8_t* is_hit,
@@ -413,7 +423,7 @@ int orc_lru_step(orc_lru* L, int64_t step, const int32_t* needed, int32_t n_need
   int32_t* vict = (int32_t*)malloc(sizeof(int32_t) * (size_t)L->S);
   int32_t n_vict = 0;
   for (int32_t e = 0; e < L->E; ++e)
-    if (L->slot_of[e] >= 0 && !in_need[e]) vict[n_vict++] = e;
+    if (L->slot_of[e] >= 0 && !in_need[e] && !L->pinned[e]) vict[n_vict++] = e;
   for (int32_t a = 1; a < n_vict; ++a) { /* insertion sort by (last_use, id) */
     int32_t v = vict[a], b = a - 1;
     while (b >= 0 && (L->last_use[vict[b]] > L->last_use[v] ||
@@ -424,7 +434,7 @@ int orc_lru_step(orc_lru* L, int64_t step, const int32_t* needed, int32_t n_need
     vict[b + 1] = v;
   }
   for (int32_t a = 0; a < n_vict; ++a) offer[n_offer++] = L->slot_of[vict[a]];
-  /* consumption order: hits first */
+  /* consumption order: hits first; a pinned expert's slot is never handed on */
   int32_t* consumed = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_needed + 1));
   int32_t n_cons = 0;
   for (int32_t i = 0; i < n_needed; ++i) {
@@ -434,7 +444,7 @@ int orc_lru_step(orc_lru* L, int64_t step, const int32_t* needed, int32_t n_need
       slot[i] = L->slot_of[e];
       evicted[i] = -1;
       wait_for[i] = -1;
-      consumed[n_cons++] = e;
+      if (!L->pinned[e]) consumed[n_cons++] = e;
       L->hits++;
     } else {
       is_hit[i] = 0;
@@ -467,6 +477,89 @@ int orc_lru_step(orc_lru* L, int64_t step, const int32_t* needed, int32_t n_need
   }
   for (int32_t i = 0; i < n_needed; ++i) L->last_use[needed[i]] = step;
   free(in_need); free(offer); free(vict); free(consumed);
+  return 0;
+}
+
+void orc_lru_record_usage(orc_lru* L, const int32_t* needed, const int32_t* counts, int32_t n_needed) {
+  for (int32_t i = 0; i < n_needed; ++i) L->usage[needed[i]] += counts[i];
+}
+
+void orc_lru_set_usage(orc_lru* L, const int64_t* usage) {
+  memcpy(L->usage, usage, sizeof(int64_t) * (size_t)L->E);
+}
+
+void orc_lru_usage(const orc_lru* L, int64_t* usage) {
+  memcpy(usage, L->usage, sizeof(int64_t) * (size_t)L->E);
+}
+
+/* The learning cache's pin: the n_pin experts with the highest usage (lower id on
+ * equal usage) become pinned, every earlier pin is released. A chosen expert
+ * already resident keeps its slot; the others, in ascending id, take a free slot
+ * (ascending), else the slot of an unpinned resident that was not chosen, oldest
+ * last use first (lower id on equal age). chosen[] receives the pinned ids
+ * ascending, slot[] their slots, loaded[] 1 where the expert had to be brought in,
+ * evicted[] the expert whose slot it took or -1. */
+int orc_lru_pin_hottest(orc_lru* L, int32_t n_pin, int32_t* chosen, int32_t* slot, uint8_t* loaded,
+                        int32_t* evicted) {
+  if (n_pin < 0 || n_pin >= L->S || n_pin > L->E) return -2;
+  int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)L->E);
+  for (int32_t e = 0; e < L->E; ++e) order[e] = e;
+  for (int32_t a = 1; a < L->E; ++a) { /* insertion sort by (usage desc, id asc) */
+    int32_t v = order[a], b = a - 1;
+    while (b >= 0 && (L->usage[order[b]] < L->usage[v] || (L->usage[order[b]] == L->usage[v] && order[b] > v))) {
+      order[b + 1] = order[b];
+      --b;
+    }
+    order[b + 1] = v;
+  }
+  uint8_t* pick = (uint8_t*)calloc((size_t)L->E, 1);
+  for (int32_t k = 0; k < n_pin; ++k) pick[order[k]] = 1;
+  for (int32_t e = 0; e < L->E; ++e) L->pinned[e] = 0;
+  /* slots on offer: free ascending, then unpinned residents not chosen by (last_use, id) */
+  int32_t* offer = (int32_t*)malloc(sizeof(int32_t) * (size_t)L->S);
+  int32_t n_offer = 0;
+  for (int32_t s = 0; s < L->S; ++s)
+    if (L->expert_in[s] < 0) offer[n_offer++] = s;
+  const int32_t n_free = n_offer;
+  int32_t* vict = (int32_t*)malloc(sizeof(int32_t) * (size_t)L->S);
+  int32_t n_vict = 0;
+  for (int32_t e = 0; e < L->E; ++e)
+    if (L->slot_of[e] >= 0 && !pick[e]) vict[n_vict++] = e;
+  for (int32_t a = 1; a < n_vict; ++a) {
+    int32_t v = vict[a], b = a - 1;
+    while (b >= 0 && (L->last_use[vict[b]] > L->last_use[v] ||
+                      (L->last_use[vict[b]] == L->last_use[v] && vict[b] > v))) {
+      vict[b + 1] = vict[b];
+      --b;
+    }
+    vict[b + 1] = v;
+  }
+  for (int32_t a = 0; a < n_vict; ++a) offer[n_offer++] = L->slot_of[vict[a]];
+  int32_t k = 0, placed = 0;
+  for (int32_t e = 0; e < L->E; ++e) {
+    if (!pick[e]) continue;
+    chosen[k] = e;
+    evicted[k] = -1;
+    loaded[k] = 0;
+    if (L->slot_of[e] < 0) {
+      const int32_t s = offer[placed];
+      const int32_t victim = placed < n_free ? -1 : L->expert_in[s];
+      ++placed;
+      if (victim >= 0) {
+        L->slot_of[victim] = -1;
+        L->evictions++;
+      }
+      L->expert_in[s] = e;
+      L->slot_of[e] = s;
+      loaded[k] = 1;
+      evicted[k] = victim;
+    }
+    slot[k] = L->slot_of[e];
+    L->pinned[e] = 1;
+    ++k;
+  }
+  L->n_pinned = n_pin;
+  free(order); free(pick); free(offer); free(vict);
   return 0;
 }
 

@@ -102,6 +102,12 @@ orc_lru* orc_lru_new(int32_t n_experts, int32_t n_slots);
 void orc_lru_free(orc_lru* L);
 int orc_lru_step(orc_lru* L, int64_t step, const int32_t* needed, int32_t n_needed, uint8_t* is_hit,
                  int32_t* slot, int32_t* evicted, int32_t* wait_for);
+/* learning cache: usage = positions routed per expert over recorded steps; pin the hottest */
+void orc_lru_record_usage(orc_lru* L, const int32_t* needed, const int32_t* counts, int32_t n_needed);
+void orc_lru_set_usage(orc_lru* L, const int64_t* usage);
+void orc_lru_usage(const orc_lru* L, int64_t* usage);
+int orc_lru_pin_hottest(orc_lru* L, int32_t n_pin, int32_t* chosen, int32_t* slot, uint8_t* loaded,
+                        int32_t* evicted);
 void orc_lru_counters(const orc_lru* L, int64_t* hits, int64_t* misses, int64_t* evictions);
 void orc_lru_resident(const orc_lru* L, int32_t* slot_of);
 

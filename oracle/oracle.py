@@ -54,6 +54,10 @@ def lib():
         L.orc_lru_free.argtypes = [P]
         L.orc_lru_step.argtypes = [P, I64, P, I32, P, P, P, P]
         L.orc_lru_counters.argtypes = [P, P, P, P]
+        L.orc_lru_record_usage.argtypes = [P, P, P, I32]
+        L.orc_lru_set_usage.argtypes = [P, P]
+        L.orc_lru_usage.argtypes = [P, P]
+        L.orc_lru_pin_hottest.argtypes = [P, I32, P, P, P, P]
         L.orc_lru_resident.argtypes = [P, P]
         _lib = L
     return _lib
@@ -283,6 +287,31 @@ class LRU:
         if rc != 0:
             raise ValueError("needed list must be unique expert ids")
         return dict(needed=nd, hit=hit.astype(bool), slot=slot, evicted=ev, wait_for=wf)
+
+    def record_usage(self, needed, counts):
+        nd = _c(np.asarray(needed), np.int32)
+        ct = _c(np.asarray(counts), np.int32)
+        lib().orc_lru_record_usage(self.h, _p(nd), _p(ct), nd.size)
+
+    def set_usage(self, usage):
+        u = _c(np.asarray(usage), np.int64)
+        assert u.size == self.E
+        lib().orc_lru_set_usage(self.h, _p(u))
+
+    def usage(self):
+        out = np.empty(self.E, np.int64)
+        lib().orc_lru_usage(self.h, _p(out))
+        return out
+
+    def pin_hottest(self, n_pin):
+        ch = np.zeros(max(n_pin, 1), np.int32)
+        sl = np.zeros(max(n_pin, 1), np.int32)
+        ld = np.zeros(max(n_pin, 1), np.uint8)
+        ev = np.zeros(max(n_pin, 1), np.int32)
+        rc = lib().orc_lru_pin_hottest(self.h, n_pin, _p(ch), _p(sl), _p(ld), _p(ev))
+        if rc != 0:
+            raise ValueError("n_pin must be in [0, n_slots)")
+        return dict(pinned=ch[:n_pin], slot=sl[:n_pin], loaded=ld[:n_pin].astype(bool), evicted=ev[:n_pin])
 
     def counters(self):
         a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()

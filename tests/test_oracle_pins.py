@@ -519,6 +519,95 @@ def test_lru_invariants_and_large_capacity():
     assert L.counters()["misses"] == len(seen) and L.counters()["evictions"] == 0
 
 
+def test_lru_pin_golden():
+    g = HW["lru_pin_trace"]
+    L = O.LRU(g["E"], g["slots"])
+    for s, (need, cnt) in enumerate(zip(g["steps_before_pin"], g["counts_before_pin"])):
+        L.step(s, need)
+        L.record_usage(need, cnt)
+    assert list(L.usage()) == g["expected_usage"]
+    p = L.pin_hottest(g["n_pin"])
+    assert list(p["pinned"]) == g["expected_pinned"]
+    assert list(p["slot"]) == g["expected_pin_slots"]
+    assert list(p["loaded"]) == g["expected_pin_loaded"]
+    assert list(p["evicted"]) == g["expected_pin_evicted"]
+    r = L.step(len(g["steps_before_pin"]), g["step_after_pin"])
+    assert list(r["hit"]) == g["expected_hits"]
+    assert list(r["slot"]) == g["expected_slots"]
+    assert list(r["evicted"]) == g["expected_evicted"]
+    assert list(r["wait_for"]) == g["expected_wait_for"]
+    assert L.counters() == g["expected_counters"]
+    assert list(L.resident()) == g["expected_resident"]
+
+
+def test_lru_pin_picks_most_used_lower_id_on_ties():
+    rng = np.random.default_rng(21)
+    E, S = 40, 12
+    for trial in range(20):
+        L = O.LRU(E, S)
+        usage = rng.integers(0, 6, size=E).astype(np.int64)  # small range: many ties
+        L.set_usage(usage)
+        assert np.array_equal(L.usage(), usage)
+        n = int(rng.integers(0, S))
+        p = L.pin_hottest(n)
+        want = np.lexsort((np.arange(E), -usage))[:n]
+        assert np.array_equal(p["pinned"], np.sort(want))
+        assert np.all(p["loaded"])  # the cache was empty: every pin is loaded into a free slot
+        assert sorted(p["slot"].tolist()) == list(range(n))
+    with pytest.raises(ValueError):
+        O.LRU(E, S).pin_hottest(S)
+
+
+def test_lru_pinned_experts_stay_and_hit():
+    rng = np.random.default_rng(22)
+    E, S, P = 64, 16, 6
+    L = O.LRU(E, S)
+    for s in range(20):  # learn
+        need = np.unique(rng.zipf(1.3, size=24) % E)
+        L.step(s, need)
+        L.record_usage(need, rng.integers(1, 5, size=need.size))
+    p = L.pin_hottest(P)
+    pinned = dict(zip(p["pinned"].tolist(), p["slot"].tolist()))
+    for s in range(20, 80):
+        need = np.unique(rng.zipf(1.3, size=24) % E)
+        r = L.step(s, need)
+        res = L.resident()
+        for e, sl in pinned.items():
+            assert res[e] == sl  # never moved or evicted
+        for e, h, ev, wf in zip(r["needed"], r["hit"], r["evicted"], r["wait_for"]):
+            if int(e) in pinned:
+                assert h
+            assert int(ev) not in pinned and int(wf) not in pinned
+        assert (res >= 0).sum() <= S
+
+
+def test_lru_pins_leave_a_textbook_lru_on_the_other_slots():
+    """Single requests: pinned experts always hit; the rest behave as a textbook LRU of S - P slots."""
+    rng = np.random.default_rng(23)
+    E, S = 16, 5
+    for P in (1, 2, 4):
+        L = O.LRU(E, S)
+        usage = np.zeros(E, np.int64)
+        usage[[3, 7, 11, 13][:P]] = [9, 8, 7, 6][:P]
+        L.set_usage(usage)
+        pinned = set(L.pin_hottest(P)["pinned"].tolist())
+        od = OrderedDict()
+        for s in range(400):
+            e = int(rng.integers(0, E))
+            r = L.step(s, [e])
+            if e in pinned:
+                assert r["hit"][0]
+                continue
+            hit = e in od
+            if hit:
+                od.move_to_end(e)
+            else:
+                if len(od) >= S - P:
+                    od.popitem(last=False)
+                od[e] = True
+            assert bool(r["hit"][0]) == hit
+
+
 # ---------------------------------------------------------------- page sizes
 
 def test_page_size_arithmetic():
