@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--stack-layers", type=int, default=40, help="stack40: layers in the stack")
     ap.add_argument("--streamed", type=int, default=20, help="stack40: last layers whose experts stream from host")
     ap.add_argument("--slots", type=int, default=64, help="stack40: HBM expert slots per streamed layer")
+    ap.add_argument("--pin", type=int, default=None,
+                    help="stack40: after the warm-up steps (which record usage) pin this many of the most used "
+                         "experts per streamed layer (learning cache); default %(default)s = 3/4 of the slots")
     ap.add_argument("--host-copies", type=int, default=12,
                     help="stack40: distinct host copies of routed experts; streamed layer j reads copy j mod this "
                          "(pinned host memory is capped below 20 layers' 97 GB on the measured box)")
@@ -295,6 +298,10 @@ def run_stack(args):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    n_pin = args.slots * 3 // 4 if args.pin is None else args.pin
+    if n_pin > 0:  # learning cache: the warm-up steps recorded each layer's usage
+        for j, c in enumerate(caches):
+            c.pin_hottest(n_pin, hosts[j][0], copy)
     st0 = [c.stats() for c in caches]
     t0 = time.perf_counter()
     for s in range(args.warmup, n_steps):
@@ -322,8 +329,9 @@ def run_stack(args):
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
            "higher_is_better": True, "dtype": "i8", "data": "synthetic",
            "config": {"workload": f"glm5.2-moe stack{NL}: {NL - NSTR} resident + {NSTR} streamed layers, "
-                                  f"{args.slots} HBM slots per streamed layer", "tokens": T,
-                      "host_copies": min(NSTR, args.host_copies)},
+                                  f"{args.slots} HBM slots per streamed layer, {n_pin} pinned by usage", "tokens": T,
+                      "host_copies": min(NSTR, args.host_copies), "pinned_per_layer": n_pin,
+                      "learning_steps": args.warmup},
            "hit_rate": round(hits / max(1, hits + misses), 4), "hits": hits, "misses": misses,
            "h2d_bytes_per_step": round(h2d / args.steps), "h2d_gbs_over_step": round(h2d / dt / 1e9, 2),
            "pinned_h2d_peak_gbs": round(peak, 2),

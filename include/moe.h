@@ -18,6 +18,8 @@
  *      to it; expert readahead overlapping the next expert's load with the
  *      current multiply.
  *  [C] same page, disk-streaming MoE: per-layer LRU expert cache.
+ *  [D] same page, learning cache: the experts a workload is routed to are
+ *      recorded, and the most used ones are pinned into spare memory.
  *
  * Conventions for every call:
  *  - All array arguments are DEVICE pointers owned by the caller unless marked
@@ -175,10 +177,11 @@ int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, 
 /* Whole layer [A][B]: y [T][H] = sum over shared experts of FFN_s(x) (weight
  * 1, added first) + sum_k topk_w[t][k] * FFN_{id(t,k)}(x[t]) in slot order,
  * where FFN(x) = W2 . Q8_0(silu(W1 . Q8_0(x)) * (W3 . Q8_0(x))) with int4 rows
- * dotted against int8 activations: exact int32 sums per 32-element block,
- * then acc = fma(d_block, sum, acc) in ascending block order from 0 and one
- * multiply by the row scale; silu(g)*u = g*u/(1+exp(-g)) in fp64, rounded
- * once. Each unique expert's weights are read once for all its tokens.
+ * dotted against int8 activations: exact int32 sums per 32-element block;
+ * block b belongs to class b mod 8, each class accumulates
+ * acc = fma(d_block, sum, acc) over its blocks in ascending order from 0, the
+ * eight class totals are added in class order from 0, and one multiply by the
+ * row scale follows; silu(g)*u = g*u/(1+exp(-g)) in fp64, rounded once. Each unique expert's weights are read once for all its tokens.
  * taps may be NULL. */
 int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
                           void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream);
@@ -192,9 +195,10 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
  * compute of experts already resident), and runs the same kernels as
  * moe_layer_forward, so outputs are bit-identical to the all-resident layer.
  * Policy: hits are computed first; a miss takes a free slot, else the slot of
- * a resident expert not needed this step (oldest last use first, lower id
- * first); when misses outnumber such slots, a later miss reuses the slot of an
- * expert already consumed this step, after that expert's compute.
+ * an unpinned resident expert not needed this step (oldest last use first,
+ * lower id first); when misses outnumber such slots, a later miss reuses the
+ * slot of an unpinned expert already consumed this step, after that expert's
+ * compute.
  * ---------------------------------------------------------------------- */
 typedef struct moe_expert_cache moe_expert_cache;
 
@@ -213,7 +217,9 @@ typedef struct moe_cache_stats {
   int64_t evictions;
   int64_t bytes_h2d;
   int64_t steps;
-  double h2d_ms; /* summed host->device copy time of the last step (event-timed), 0 if unknown */
+  double h2d_ms;  /* summed over all forward calls: the span of each call's host->device copies on the copy
+                     stream (event-timed, first copy issued to last copy done) */
+  int64_t pinned; /* experts pinned by the last moe_expert_cache_pin_hottest */
 } moe_cache_stats;
 
 /* Allocates the HBM slot pool (n_slots experts) and its bookkeeping; the only
@@ -228,6 +234,25 @@ int32_t moe_expert_cache_forward(moe_expert_cache* cache, const moe_layer_weight
                                  size_t ws_bytes, hipStream_t compute, hipStream_t copy, int8_t* trace_is_hit,
                                  int32_t* trace_slot);
 int32_t moe_expert_cache_stats(const moe_expert_cache* cache, moe_cache_stats* out /* host */);
+
+/* Learning cache [D]. Every moe_expert_cache_forward adds, per routed expert, the number of
+ * positions routed to it: its usage. moe_expert_cache_usage copies the E
+ * counters out (host int64[E]); moe_expert_cache_set_usage replaces them (to
+ * restore counters saved from an earlier run; MOE_E_ARG if any is negative).
+ * moe_expert_cache_pin_hottest pins the n_pin experts with the highest usage
+ * (lower id on equal usage), 0 <= n_pin < n_slots, releasing earlier pins: an
+ * expert already resident keeps its slot, the others (ascending id) take a
+ * free slot, else the slot of an unpinned resident that was not chosen (oldest
+ * last use first, lower id on equal age), and are copied from `host` on the
+ * `copy` stream. It synchronizes the device first (no earlier forward may
+ * still use a slot it hands over) and returns when the copies are done. Pinned
+ * experts stay resident and are never offered to a miss; the other slots keep
+ * the LRU policy above. n_pin = 0 releases every pin. Errors: MOE_E_NULL,
+ * MOE_E_ARG (n_pin out of range, wrong device), MOE_E_HIP. */
+int32_t moe_expert_cache_usage(const moe_expert_cache* cache, int64_t* usage /* host [E] */);
+int32_t moe_expert_cache_set_usage(moe_expert_cache* cache, const int64_t* usage /* host [E] */);
+int32_t moe_expert_cache_pin_hottest(moe_expert_cache* cache, int32_t n_pin, const moe_host_experts* host,
+                                     hipStream_t copy);
 void moe_expert_cache_destroy(moe_expert_cache* cache);
 
 /* ------------------------------------------------------------------------

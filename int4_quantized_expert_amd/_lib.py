@@ -56,7 +56,7 @@ class moe_host_experts(ctypes.Structure):
 
 class moe_cache_stats(ctypes.Structure):
     _fields_ = [("hits", I64), ("misses", I64), ("evictions", I64), ("bytes_h2d", I64), ("steps", I64),
-                ("h2d_ms", ctypes.c_double)]
+                ("h2d_ms", ctypes.c_double), ("pinned", I64)]
 
 
 def _sig(name, res, args):
@@ -78,6 +78,9 @@ _sig("moe_layer_forward", I32, [P, P, P, I32, P, P, SZ, P, P])
 _sig("moe_expert_cache_create", I32, [P, I32, I32, ctypes.POINTER(P)])
 _sig("moe_expert_cache_forward", I32, [P, P, P, P, I32, P, P, SZ, P, P, P, P])
 _sig("moe_expert_cache_stats", I32, [P, P])
+_sig("moe_expert_cache_usage", I32, [P, P])
+_sig("moe_expert_cache_set_usage", I32, [P, P])
+_sig("moe_expert_cache_pin_hottest", I32, [P, I32, P, P])
 _sig("moe_expert_cache_destroy", None, [P])
 _sig("moe_prof_enable", I32, [I32, ctypes.c_uint32])
 _sig("moe_prof_read", I32, [P, I32, P])
@@ -87,7 +90,8 @@ _sig("moe_membench_copy", I32, [P, P, SZ, I32, P])
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_workspace_bytes", "moe_quantize_int4",
             "moe_quantize_q8_0", "moe_router", "moe_dispatch", "moe_layer_forward", "moe_expert_cache_create",
-            "moe_expert_cache_forward", "moe_expert_cache_stats", "moe_expert_cache_destroy", "moe_prof_enable",
+            "moe_expert_cache_forward", "moe_expert_cache_stats", "moe_expert_cache_usage", "moe_expert_cache_set_usage",
+            "moe_expert_cache_pin_hottest", "moe_expert_cache_destroy", "moe_prof_enable",
             "moe_prof_read", "moe_prof_disable", "moe_membench_read", "moe_membench_copy")
 
 
@@ -262,7 +266,24 @@ class ExpertCache:
         s = moe_cache_stats()
         _check("moe_expert_cache_stats", _lib.moe_expert_cache_stats(self._h, ctypes.byref(s)))
         return dict(hits=s.hits, misses=s.misses, evictions=s.evictions, bytes_h2d=s.bytes_h2d, steps=s.steps,
-                    h2d_ms=s.h2d_ms)
+                    h2d_ms=s.h2d_ms, pinned=s.pinned)
+
+    def usage(self):
+        """Positions routed to each expert over every forward (host int64 [E])."""
+        import numpy as np
+        out = np.zeros(self.E, np.int64)
+        _check("moe_expert_cache_usage", _lib.moe_expert_cache_usage(self._h, out.ctypes.data))
+        return out
+
+    def set_usage(self, usage):
+        import numpy as np
+        u = np.ascontiguousarray(usage, dtype=np.int64)
+        assert u.shape == (self.E,)
+        _check("moe_expert_cache_set_usage", _lib.moe_expert_cache_set_usage(self._h, u.ctypes.data))
+
+    def pin_hottest(self, n_pin: int, host: HostExperts, copy):
+        _check("moe_expert_cache_pin_hottest",
+               _lib.moe_expert_cache_pin_hottest(self._h, int(n_pin), ctypes.byref(host.c), _stream(copy)))
 
     def destroy(self):
         if self._h:

@@ -19,15 +19,21 @@
 //
 // Policy, one call per step: needed = unique experts ascending; hits are the
 // resident ones; misses take free slots (ascending), then the slots of
-// resident experts not needed this step (oldest last use first, lower id on
-// equal age); when misses outnumber those slots, the j-th extra miss reuses
-// the slot of the j-th expert consumed this step (hits ascending, then misses
-// in placement order), once that expert's phase has run. All needed experts
-// get last use = this step.
+// unpinned resident experts not needed this step (oldest last use first,
+// lower id on equal age); when misses outnumber those slots, the j-th extra
+// miss reuses the slot of the j-th unpinned expert consumed this step (hits
+// ascending, then misses in placement order), once that expert's phase has
+// run. All needed experts get last use = this step.
 //
-// Ordering: a miss reuses the slot of an expert consumed S positions earlier
-// (S = slots), so with chunks of S/2 a chunk's copies never wait for the phase
-// right before it and copying overlaps computing.
+// Learning cache ("Show HN", learning-cache section: the experts a workload
+// routes to are recorded, and the most used are pinned into spare memory):
+// every forward adds the positions routed to each expert to its usage;
+// moe_expert_cache_pin_hottest pins the most used experts, which then stay
+// resident and are never offered to a miss.
+//
+// Ordering: a miss reuses the slot of an expert consumed U positions earlier
+// (U = unpinned slots), so with chunks of U/2 a chunk's copies never wait for
+// the phase right before it and copying overlaps computing.
 #include <algorithm>
 #include <cstring>
 #include <vector>
@@ -56,7 +62,11 @@ struct moe_expert_cache {
   // host LRU state
   std::vector<int32_t> slot_of, expert_in;
   std::vector<int64_t> last_use;
+  std::vector<int64_t> usage;   // positions routed per expert, all forwards (learning cache)
+  std::vector<uint8_t> pinned;  // resident and never offered to a miss
+  int n_pinned = 0;
   int64_t step = 0, hits = 0, misses = 0, evictions = 0, bytes_h2d = 0;
+  double h2d_ms_done = 0.0;  // copy spans of the steps before the last one
 };
 
 namespace {
@@ -110,17 +120,19 @@ void lru_step(moe_expert_cache* c, const int32_t* needed, int n, Placement& P) {
   const size_t n_free = offer.size();
   std::vector<int32_t> vict;
   for (int e = 0; e < c->E; ++e)
-    if (c->slot_of[e] >= 0 && !in_need[e]) vict.push_back(e);
+    if (c->slot_of[e] >= 0 && !in_need[e] && !c->pinned[e]) vict.push_back(e);
   std::stable_sort(vict.begin(), vict.end(), [&](int a, int b) {
     return c->last_use[a] != c->last_use[b] ? c->last_use[a] < c->last_use[b] : a < b;
   });
   for (int e : vict) offer.push_back(c->slot_of[e]);
-  std::vector<int32_t> consumed;  // needed indices
+  std::vector<int32_t> consumed;  // needed indices, in consumption order
+  std::vector<int32_t> reuse;     // consumption positions of unpinned experts (slots a later miss may take)
   for (int i = 0; i < n; ++i) {
     const int e = needed[i];
     if (c->slot_of[e] >= 0) {
       P.hit[i] = 1;
       P.slot[i] = c->slot_of[e];
+      if (!c->pinned[e]) reuse.push_back((int32_t)consumed.size());
       consumed.push_back(i);
       c->hits++;
     }
@@ -135,7 +147,7 @@ void lru_step(moe_expert_cache* c, const int32_t* needed, int n, Placement& P) {
       s = offer[placed];
       victim = placed < n_free ? -1 : c->expert_in[s];
     } else {
-      const int ci = (int)overflow++;
+      const int ci = reuse[overflow++];
       victim = needed[consumed[ci]];
       s = c->slot_of[victim];
       P.wait_for[i] = ci;
@@ -148,6 +160,7 @@ void lru_step(moe_expert_cache* c, const int32_t* needed, int n, Placement& P) {
     c->expert_in[s] = e;
     c->slot_of[e] = s;
     P.slot[i] = s;
+    reuse.push_back((int32_t)consumed.size());
     consumed.push_back(i);
     c->misses++;
   }
@@ -207,6 +220,8 @@ int32_t moe_expert_cache_create(const moe_config* cfg, int32_t n_slots, int32_t 
   c->slot_of.assign(c->E, -1);
   c->expert_in.assign(c->S, -1);
   c->last_use.assign(c->E, -1);
+  c->usage.assign(c->E, 0);
+  c->pinned.assign(c->E, 0);
   // lists: every phase's GEMV chunks and tiles, bounded by the all-in-one-phase worst case per phase
   const int64_t TK = (int64_t)max_tokens * cfg->top_k, NS = cfg->n_shared;
   const int64_t buckets = std::min<int64_t>(c->E, TK) + NS;
@@ -262,6 +277,13 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
     e = hipMemcpyAsync(c->h_back + 2 * E, f.nunique, sizeof(int32_t), hipMemcpyDeviceToHost, compute);
   if (e == hipSuccess) e = hipStreamSynchronize(compute);
   if (e != hipSuccess) return hip_fail(e);
+  // the previous step's copies are complete (its phases waited for them): bank their span
+  if (c->h2d_timed) {
+    float ms = 0.0f;
+    if ((e = hipEventElapsedTime(&ms, c->ev_h2d0, c->ev_h2d1)) != hipSuccess) return hip_fail(e);
+    c->h2d_ms_done += ms;
+    c->h2d_timed = false;
+  }
   const int nu = c->h_back[2 * E];
   const int32_t* needed = c->h_back;
   const int32_t* counts = c->h_back + E;
@@ -271,7 +293,8 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
     if (!host->w13[needed[i]] || !host->s13[needed[i]] || !host->w2[needed[i]] || !host->s2[needed[i]])
       return MOE_E_NULL;
 
-  // 3: placement
+  // 3: usage, placement
+  for (int i = 0; i < nu; ++i) c->usage[needed[i]] += counts[needed[i]];
   Placement P;
   lru_step(c, needed, nu, P);
   c->step++;
@@ -286,7 +309,7 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
   }
 
   // phases: 0 = hits + shared experts; then misses in consumption order, chunks of B
-  const int B = std::max(1, c->S / 2);
+  const int B = std::max(1, (c->S - c->n_pinned) / 2);
   const int n_miss = nu - P.n_hits;
   const int n_chunks = (n_miss + B - 1) / B;
   const int n_phases = 1 + n_chunks;
@@ -397,15 +420,90 @@ int32_t moe_expert_cache_stats(const moe_expert_cache* c, moe_cache_stats* out) 
   out->evictions = c->evictions;
   out->bytes_h2d = c->bytes_h2d;
   out->steps = c->step;
-  out->h2d_ms = 0.0;
+  out->pinned = c->n_pinned;
+  out->h2d_ms = c->h2d_ms_done;
   if (c->h2d_timed) {
     float ms = 0.0f;
     hipError_t e = hipEventSynchronize(c->ev_h2d1);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, c->ev_h2d0, c->ev_h2d1);
     if (e != hipSuccess) return hip_fail(e);
-    out->h2d_ms = ms;
+    out->h2d_ms += ms;
   }
   return MOE_OK;
+}
+
+int32_t moe_expert_cache_usage(const moe_expert_cache* c, int64_t* usage) {
+  if (!c || !usage) return MOE_E_NULL;
+  std::memcpy(usage, c->usage.data(), sizeof(int64_t) * c->E);
+  return MOE_OK;
+}
+
+int32_t moe_expert_cache_set_usage(moe_expert_cache* c, const int64_t* usage) {
+  if (!c || !usage) return MOE_E_NULL;
+  for (int e = 0; e < c->E; ++e)
+    if (usage[e] < 0) return MOE_E_ARG;
+  std::memcpy(c->usage.data(), usage, sizeof(int64_t) * c->E);
+  return MOE_OK;
+}
+
+int32_t moe_expert_cache_pin_hottest(moe_expert_cache* c, int32_t n_pin, const moe_host_experts* host,
+                                     hipStream_t copy) {
+  if (!c || !host) return MOE_E_NULL;
+  if (!host->w13 || !host->s13 || !host->w2 || !host->s2) return MOE_E_NULL;
+  if (n_pin < 0 || n_pin >= c->S) return MOE_E_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return MOE_E_ARG;
+  const int E = c->E;
+  // the most used, lower id on equal usage
+  std::vector<int32_t> order(E);
+  for (int e = 0; e < E; ++e) order[e] = e;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return c->usage[a] != c->usage[b] ? c->usage[a] > c->usage[b] : a < b; });
+  std::vector<char> pick(E, 0);
+  for (int k = 0; k < n_pin; ++k) pick[order[k]] = 1;
+  for (int e = 0; e < E; ++e)
+    if (pick[e] && c->slot_of[e] < 0 && (!host->w13[e] || !host->s13[e] || !host->w2[e] || !host->s2[e]))
+      return MOE_E_NULL;
+  // no kernel or copy of an earlier forward may still use a slot handed over here
+  hipError_t r = hipDeviceSynchronize();
+  if (r != hipSuccess) return hip_fail(r);
+  std::vector<int32_t> offer;
+  for (int s = 0; s < c->S; ++s)
+    if (c->expert_in[s] < 0) offer.push_back(s);
+  const size_t n_free = offer.size();
+  std::vector<int32_t> vict;
+  for (int e = 0; e < E; ++e)
+    if (c->slot_of[e] >= 0 && !pick[e]) vict.push_back(e);
+  std::stable_sort(vict.begin(), vict.end(), [&](int a, int b) {
+    return c->last_use[a] != c->last_use[b] ? c->last_use[a] < c->last_use[b] : a < b;
+  });
+  for (int e : vict) offer.push_back(c->slot_of[e]);
+  size_t placed = 0;
+  for (int e = 0; e < E && r == hipSuccess; ++e) {
+    c->pinned[e] = pick[e];
+    if (!pick[e] || c->slot_of[e] >= 0) continue;
+    const int s = offer[placed];
+    const int victim = placed < n_free ? -1 : c->expert_in[s];
+    ++placed;
+    if (victim >= 0) {
+      c->slot_of[victim] = -1;
+      c->evictions++;
+    }
+    c->expert_in[s] = e;
+    c->slot_of[e] = s;
+    r = hipMemcpyAsync(c->pool_w13 + c->b13 * s, host->w13[e], c->b13, hipMemcpyHostToDevice, copy);
+    if (r == hipSuccess)
+      r = hipMemcpyAsync(reinterpret_cast<char*>(c->pool_s13) + c->bs13 * s, host->s13[e], c->bs13,
+                         hipMemcpyHostToDevice, copy);
+    if (r == hipSuccess) r = hipMemcpyAsync(c->pool_w2 + c->b2 * s, host->w2[e], c->b2, hipMemcpyHostToDevice, copy);
+    if (r == hipSuccess)
+      r = hipMemcpyAsync(reinterpret_cast<char*>(c->pool_s2) + c->bs2 * s, host->s2[e], c->bs2,
+                         hipMemcpyHostToDevice, copy);
+    c->bytes_h2d += (int64_t)(c->b13 + c->bs13 + c->b2 + c->bs2);
+  }
+  c->n_pinned = n_pin;
+  if (r == hipSuccess) r = hipStreamSynchronize(copy);
+  return r == hipSuccess ? MOE_OK : hip_fail(r);
 }
 
 void moe_expert_cache_destroy(moe_expert_cache* c) {

@@ -1,7 +1,9 @@
 """Per-layer LRU expert cache: routed experts in pinned host memory, an HBM slot pool, copies on a side stream.
 
 Checks, every step: the layer output equals the all-resident layer bit for bit (tier invariance); the hits
-and slots equal the oracle's LRU simulator fed the same needed-expert lists; the counters add up."""
+and slots equal the oracle's LRU simulator fed the same needed-expert lists; the counters add up. With the
+learning cache: recorded usage equals the simulator's (positions per expert from the oracle's router), and
+after a pin call every later step still matches the simulator given the same pins."""
 import numpy as np
 import pytest
 
@@ -33,7 +35,16 @@ def _resident_y(layer, cfg, xd, ws):
     return y.cpu().numpy()
 
 
-def _run_steps(layer, hx, n_slots, xs, gemm_min=0):
+def _oracle_counts(sh, x):
+    """Positions routed to each expert, from the oracle's router (the same seeded router weights and bias)."""
+    ids, _, _ = O.route(O.Cfg.of(sh), O.router_logits(x, synth.router_weights(sh, 0)), synth.router_bias(sh, 0))
+    return np.bincount(ids.ravel(), minlength=sh.n_experts)
+
+
+def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False, set_usage=None):
+    """pins: {step: n_pin} pin calls made before that step; set_usage: {step: usage} loaded before that step
+    into both the cache and the simulator; usage_check: record usage in the simulator from the oracle's
+    routing and compare it with the cache's at every pin."""
     sh = layer.shape
     cfg = config_of(sh, gemm_min)
     Tmax = max(x.shape[0] for x in xs)
@@ -41,8 +52,17 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0):
     sim = O.LRU(sh.n_experts, n_slots)
     ws = torch.empty(moe.moe_workspace_bytes(cfg, Tmax), dtype=torch.uint8, device=DEV)
     compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
-    hits = misses = 0
+    hits = misses = loaded = 0
     for step, x in enumerate(xs):
+        if set_usage and step in set_usage:
+            cache.set_usage(set_usage[step])
+            sim.set_usage(set_usage[step])
+        if pins and step in pins:
+            if usage_check:
+                assert np.array_equal(cache.usage(), sim.usage()), step
+            cache.pin_hottest(pins[step], hx, copy)
+            loaded += int(sim.pin_hottest(pins[step])["loaded"].sum())
+            assert cache.stats()["pinned"] == pins[step]
         xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
         y_ref = _resident_y(layer, cfg, xd, ws)
         y = torch.empty((x.shape[0], sh.hidden), dtype=torch.float32, device=DEV)
@@ -51,6 +71,10 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0):
         assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32)), step
         needed = np.nonzero(hit >= 0)[0].astype(np.int32)
         r = sim.step(step, needed)
+        if usage_check:
+            counts = _oracle_counts(sh, x)
+            assert np.array_equal(np.nonzero(counts)[0], needed), step
+            sim.record_usage(needed, counts[needed])
         assert np.array_equal(hit[needed].astype(bool), r["hit"]), step
         assert np.array_equal(slot[needed], r["slot"]), step
         hits += int(r["hit"].sum())
@@ -59,7 +83,9 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0):
     assert st["hits"] == hits and st["misses"] == misses and st["steps"] == len(xs)
     assert st["evictions"] == sim.counters()["evictions"]
     per = sh.inter * sh.hidden + 2 * sh.inter * 4 + sh.hidden * sh.inter // 2 + sh.hidden * 4
-    assert st["bytes_h2d"] == misses * per
+    assert st["bytes_h2d"] == (misses + loaded) * per
+    if usage_check:
+        assert np.array_equal(cache.usage(), sim.usage())
     cache.destroy()
     return st
 
@@ -88,6 +114,16 @@ def test_cache_tiny_mfma_and_ragged(tiny):
     _run_steps(layer, hx, 4, xs, gemm_min=1)
 
 
+@pytest.mark.parametrize("n_slots,pins", [(6, {8: 3}), (4, {5: 2, 10: 0, 12: 3}), (1, {6: 0})])
+def test_cache_tiny_learning_pins(tiny, n_slots, pins):
+    """Usage recorded over steps equals the simulator's; pinning the most used experts (and releasing pins)
+    leaves every later step equal to the simulator with the same pins, and the output bit-exact."""
+    layer, (hx, _) = tiny
+    xs = [synth.hidden_states(synth.TINY, 8, seed=2, step=s) for s in range(16)]
+    st = _run_steps(layer, hx, n_slots, xs, pins=pins, usage_check=True)
+    assert st["pinned"] == pins[max(pins)]
+
+
 def test_cache_rejects_bad_args(tiny):
     layer, (hx, _) = tiny
     cfg = config_of(synth.TINY)
@@ -105,6 +141,12 @@ def test_cache_rejects_bad_args(tiny):
     with pytest.raises(moe.MoeError) as e:
         cache.forward(layer.weights(), hx, x[:8], y[:8], ws, s, s)  # one stream for both roles
     assert e.value.rc == moe.MOE_E_ARG
+    with pytest.raises(moe.MoeError) as e:
+        cache.pin_hottest(4, hx, s)  # at least one slot must stay unpinned
+    assert e.value.rc == moe.MOE_E_ARG
+    with pytest.raises(moe.MoeError) as e:
+        cache.set_usage(np.full(16, -1, np.int64))
+    assert e.value.rc == moe.MOE_E_ARG
     cache.destroy()
 
 
@@ -115,4 +157,8 @@ def test_cache_glm_decode32():
     xs = [synth.hidden_states(synth.GLM, 32, seed=0, step=s) for s in range(4)]
     st = _run_steps(layer, hx, 64, xs)
     assert st["misses"] > 0
+    # learning cache at the GLM shape: 48 of the 64 slots pinned from a seeded usage profile
+    usage = np.random.default_rng(5).zipf(1.2, size=256).astype(np.int64)
+    st = _run_steps(layer, hx, 64, xs + xs[:2], set_usage={2: usage}, pins={2: 48})
+    assert st["pinned"] == 48
     del keep
