@@ -38,6 +38,49 @@ void orc_quant_int4_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, 
   }
 }
 
+/* int8 expert weights ("Show HN", implemented features: int8 / packed int4
+ * weights with per-row scales; the MTP head must be int8): symmetric per row,
+ * s = amax/127, q = clamp(round-half-away(w * (1/s)), -127, 127), the
+ * product taken as one fp32 multiply, as for int4. */
+void orc_quant_int8_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, float* s) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* row = w + r * cols;
+    float amax = 0.0f;
+    for (int64_t k = 0; k < cols; ++k) {
+      float a = fabsf(row[k]);
+      if (a > amax) amax = a;
+    }
+    float sc = amax / 127.0f;
+    float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
+    for (int64_t k = 0; k < cols; ++k) {
+      float v = roundf(row[k] * inv);
+      if (v > 127.0f) v = 127.0f;
+      if (v < -127.0f) v = -127.0f;
+      q[r * cols + k] = (int8_t)v;
+    }
+    s[r] = sc;
+  }
+}
+
+/* Row-tiled int8 layout of a [rows][cols] matrix: tiles of 64 rows; for each
+ * 32-element block, the 64 rows' 32-byte blocks are adjacent. Byte j of block
+ * b of row r sits at ((r/64) * (cols/32) + b) * 2048 + (r%64) * 32 + j, and
+ * inside each group of 8 bytes the group's even elements come first, then its
+ * odd ones (element 2i at byte i, element 2i+1 at byte 4+i). */
+void orc_unpack_int8_tiled64(const uint8_t* in, int64_t rows, int64_t cols, int8_t* q) {
+  int64_t nb = cols / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      const int8_t* src = (const int8_t*)(in + ((r / 64) * nb + b) * 2048 + (r % 64) * 32);
+      int8_t* dst = q + r * cols + b * 32;
+      for (int g = 0; g < 4; ++g)
+        for (int i = 0; i < 4; ++i) {
+          dst[8 * g + 2 * i] = src[8 * g + i];
+          dst[8 * g + 2 * i + 1] = src[8 * g + 4 + i];
+        }
+    }
+}
+
 /* Two int4 values per byte, element 2j in the low nibble, two's complement. */
 void orc_pack_int4(const int8_t* q, int64_t n, uint8_t* out) {
   for (int64_t j = 0; j < n / 2; ++j)

@@ -53,6 +53,8 @@ typedef struct {
 
 /* int4 per-row symmetric quantization of fp32 rows [rows][cols]: q in [-7,7], scale per row */
 void orc_quant_int4_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, float* s);
+void orc_quant_int8_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, float* s);
+void orc_unpack_int8_tiled64(const uint8_t* in, int64_t rows, int64_t cols, int8_t* q);
 /* canonical nibble packing: byte j = (q[2j] & 15) | (q[2j+1] & 15) << 4, two's complement */
 void orc_pack_int4(const int8_t* q, int64_t n, uint8_t* out);
 void orc_unpack_int4(const uint8_t* in, int64_t n, int8_t* q);

@@ -37,6 +37,8 @@ def lib():
         L.orc_pack_int4.argtypes = [P, I64, P]
         L.orc_unpack_int4.argtypes = [P, I64, P]
         L.orc_unpack_int4_tiled64.argtypes = [P, I64, I64, P]
+        L.orc_quant_int8_rows.argtypes = [P, I64, I64, P, P]
+        L.orc_unpack_int8_tiled64.argtypes = [P, I64, I64, P]
         L.orc_q8_0.argtypes = [P, I64, P, P]
         L.orc_router_logits.argtypes = [P, I32, I32, P, I32, P]
         L.orc_route.argtypes = [P, P, P, I32, P, P, P, P, P]
@@ -106,6 +108,23 @@ def pack_int4(q):
     out = np.empty(q.size // 2, np.uint8)
     lib().orc_pack_int4(_p(q), q.size, _p(out))
     return out
+
+
+def quant_int8_rows(w):
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), np.int8)
+    sc = np.empty(rows, np.float32)
+    lib().orc_quant_int8_rows(_p(w), rows, cols, _p(q), _p(sc))
+    return q, sc
+
+
+def unpack_int8_tiled64(b, rows, cols):
+    b = _c(b, np.uint8).reshape(-1)
+    assert b.size == rows * cols
+    q = np.empty((rows, cols), np.int8)
+    lib().orc_unpack_int8_tiled64(_p(b), rows, cols, _p(q))
+    return q
 
 
 def unpack_int4(b, n):

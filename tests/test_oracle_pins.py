@@ -87,6 +87,46 @@ def test_int4_quant_golden_and_bounds():
     assert s[0] == 0.25 and np.array_equal(q[0], k[0].astype(np.int8))
 
 
+def test_int8_quant_golden_and_bounds():
+    g = HW["int8_halfway"]
+    row = np.zeros((1, 32), np.float32)
+    row[0, :len(g["row_head"])] = g["row_head"]
+    q, s = O.quant_int8_rows(row)
+    assert s[0] == g["expected_s"]
+    assert list(q[0, :len(g["expected_q_head"])]) == g["expected_q_head"]
+    w = synth.normal(64 * 256, 3, 78, 0.02).reshape(64, 256)
+    w[9] = 0.0
+    q, s = O.quant_int8_rows(w)
+    assert s[9] == 0 and not q[9].any()
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    amax = np.abs(w).max(1)
+    am = np.argmax(np.abs(w), 1)
+    for r in range(64):
+        if r == 9:
+            continue
+        assert abs(int(q[r, am[r]])) == 127
+        err = np.abs(w[r].astype(np.float64) - s[r] * q[r].astype(np.float64))
+        assert err.max() <= s[r] / 2 * (1 + 1e-6) + 1e-12
+        assert abs(s[r] - amax[r] / 127) <= 2 * U * amax[r] / 127
+
+
+def test_int8_tiled64_layout_against_its_formula():
+    """A plain packer written from the documented address formula, then the oracle's reader."""
+    rng = np.random.default_rng(31)
+    rows, cols = 128, 96
+    q = rng.integers(-127, 128, size=(rows, cols)).astype(np.int8)
+    buf = np.zeros(rows * cols, np.uint8)
+    nb = cols // 32
+    for r in range(rows):
+        for b in range(nb):
+            base = ((r // 64) * nb + b) * 2048 + (r % 64) * 32
+            for e in range(32):
+                g, m = divmod(e, 8)
+                pos = 8 * g + (m // 2 if m % 2 == 0 else 4 + m // 2)
+                buf[base + pos] = np.uint8(int(q[r, b * 32 + e]) & 0xFF)
+    assert np.array_equal(O.unpack_int8_tiled64(buf, rows, cols), q)
+
+
 def test_q8_0_golden_and_bounds():
     g = HW["q8_0_halfway"]
     blk = np.zeros(64, np.float32)
