@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--gemm-min", type=int, default=0)
+    ap.add_argument("--weight-bits", type=int, default=4, choices=[4, 8],
+                    help="expert weight codes: 4 (row-tiled int4, the default) or 8 (row-tiled int8)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -114,7 +116,7 @@ def routing_stats(moe, cfg, layer, x_dev, ws, gemm_min):
 SAMPLE_TOKENS = 8  # tokens of the CPU sample (each distinct expert they route to is generated once)
 
 
-def cpu_baseline(shape, x, seconds, seed):
+def cpu_baseline(shape, x, seconds, seed, weight_bits=4):
     """The oracle as it stands, single-threaded, over the first SAMPLE_TOKENS tokens of the first batch: they are
     routed once and each distinct expert they need is generated once (outside the timing); then passes over
     them are timed until `seconds` of oracle time have been spent."""
@@ -132,7 +134,8 @@ def cpu_baseline(shape, x, seconds, seed):
             w13, w2 = synth.shared_w13(shape, e, seed, 0), synth.shared_w2(shape, e, seed, 0)
         else:
             w13, w2 = synth.expert_w13(shape, e, seed, 0), synth.expert_w2(shape, e, seed, 0)
-        return O.quant_int4_rows(w13) + O.quant_int4_rows(w2)
+        quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
+        return quant(w13) + quant(w2)
 
     experts = {int(e): gen(int(e), False) for e in np.unique(ids_all)}
     shared = gen(0, True)
@@ -155,7 +158,7 @@ def cpu_baseline(shape, x, seconds, seed):
     return dict(value=done / t_oracle, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{done} tokens ({passes} pass(es) over the first {T} tokens of the first batch), each: "
                        f"fp64 router over "
-                       f"{shape.n_experts} experts, {shape.top_k} routed + 1 shared int4xint8 expert FFNs, combine; "
+                       f"{shape.n_experts} experts, {shape.top_k} routed + 1 shared int{weight_bits}xint8 expert FFNs, combine; "
                        f"{t_oracle:.1f} s of single-threaded oracle time (weight generation excluded)")
 
 
@@ -356,6 +359,9 @@ def main():
         calibrate()
         return
     if args.workload == "stack40":
+        if args.weight_bits != 4:
+            print("stack40 streams int4 experts only (--weight-bits 4).", file=sys.stderr)
+            sys.exit(2)
         run_stack(args)
         return
     import torch
@@ -367,8 +373,9 @@ def main():
     shape = synth.GLM
     T = tokens_of(args.workload)
     dev = torch.device("cuda:0")
-    cfg = config_of(shape, args.gemm_min)
-    layers = [GpuLayer(shape, seed=args.seed + c) for c in range(args.copies)]
+    WB = args.weight_bits
+    cfg = config_of(shape, args.gemm_min, WB)
+    layers = [GpuLayer(shape, seed=args.seed + c, weight_bits=WB) for c in range(args.copies)]
     n_in = args.warmup + args.steps
     xs_host = make_inputs(shape, args.workload, min(n_in, 64), args.seed)
     xs = [torch.from_numpy(x).to(dev) for x in xs_host]
@@ -389,6 +396,8 @@ def main():
     # dominant kernel: the gate-up launch of the path that moves most bytes; the
     # timed region records HIP events around it only (on the stream it runs on)
     kname = "gateup_mfma" if args.workload == "prefill" else "gateup_gemv"
+    # counter summaries are per kernel, workload and weight width
+    pmc_workload = args.workload if WB == 4 else f"{args.workload}_int8w"
     kidx = moe.STAGES.index(kname)
 
     def timed(stages):
@@ -413,8 +422,8 @@ def main():
     ms_staged, prof_all = timed(None)
 
     H, I, E = shape.hidden, shape.inter, shape.n_experts
-    w13_bytes = I * H + 2 * I * 4  # int4 gate+up rows + fp32 row scales
-    w2_bytes = H * I // 2 + H * 4
+    w13_bytes = 2 * I * H * WB // 8 + 2 * I * 4  # gate+up codes + fp32 row scales
+    w2_bytes = H * I * WB // 8 + H * 4
     U = np.array([s["U"] for s in stats], np.float64)
     layer_bytes = (E * H * 4 + E * 4) + (U + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 4
     stage_ms = prof_all.mean(0)
@@ -423,7 +432,7 @@ def main():
         kt = prof[:, kidx] / 1e3
         achieved = float(np.mean(ops / kt) / 1e12)
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
-                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic_of("k_" + kname, args.workload),
+                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
                     kernel="k_" + kname,
                     kernel_ms=round(float(kt.mean() * 1e3), 4),
                     per_unit="2*2I*H int8 ops per (token, expert) on the MFMA path")
@@ -433,7 +442,7 @@ def main():
         kt = prof[:, kidx] / 1e3
         achieved = float(np.mean(gb / kt) / 1e9)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_of("k_" + kname, args.workload),
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
                     kernel="k_" + kname, algorithmic_bytes=round(float(gb.mean()), 1),
                     kernel_ms=round(float(kt.mean() * 1e3), 4),
                     per_unit=f"{w13_bytes} B of gate/up weights+scales per GEMV-path expert, plus Q8_0 activations "
@@ -454,7 +463,7 @@ def main():
         "config": {"workload": f"glm5.2-moe-layer {args.workload}", "tokens": T, "hidden": H, "experts": E,
                    "groups": shape.n_group, "topk_group": shape.topk_group, "top_k": shape.top_k, "inter": I,
                    "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or DEFAULT_GEMM_MIN,
-                   "layer_copies": args.copies},
+                   "layer_copies": args.copies, "weight_bits": WB},
         "layer_hbm_gbs": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9), 1),
         "layer_hbm_frac": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9) / HBM_PEAK_GBS, 4),
         "unique_experts_mean": round(float(U.mean()), 2),
@@ -471,7 +480,7 @@ def main():
     out["layer_int8_mfma_frac"] = round(ops_layer / (ms_step / 1e3) / (INT8_PEAK_TOPS * 1e12), 4)
     out["combined_roofline_frac"] = round(float(np.mean(np.maximum(t_mem, t_mfma))) / (ms_step / 1e3), 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed)
+        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB)
     print(json.dumps(out), flush=True)
 
 

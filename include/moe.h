@@ -20,6 +20,9 @@
  *  [C] same page, disk-streaming MoE: per-layer LRU expert cache.
  *  [D] same page, learning cache: the experts a workload is routed to are
  *      recorded, and the most used ones are pinned into spare memory.
+ *  [D2] same page, implemented features: int8 and packed int4 weights with
+ *      per-row scales; the MTP head must be int8 (int4 drafts are almost
+ *      never accepted).
  *
  * Conventions for every call:
  *  - All array arguments are DEVICE pointers owned by the caller unless marked
@@ -47,6 +50,13 @@
  * adjacent. Byte j of block b of row r is at
  *     ((r / 64) * (K / 32) + b) * 1024 + (r % 64) * 16 + j.
  * One fp32 scale per row. moe_quantize_int4() produces this layout.
+ *
+ * Weight layout ("row-tiled int8", the MTP head's precision [D2]): the same
+ * tiling with 32 bytes per row and block; inside each group of 8 bytes the
+ * group's even elements come first, then its odd ones (element 8g + 2i at
+ * byte 8g + i, element 8g + 2i + 1 at byte 8g + 4 + i). Byte j of block b of
+ * row r is at ((r / 64) * (K / 32) + b) * 2048 + (r % 64) * 32 + j. One fp32
+ * scale per row. moe_quantize_int8() produces this layout.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -87,14 +97,17 @@ typedef struct moe_config {
                               <= 0 selects the default (5: a bucket that would
                               need two GEMV chunks takes one MFMA tile instead).
                               Never changes results. */
+  int32_t weight_bits;   /* expert weight codes: 4 (row-tiled int4; <= 0 selects it) or 8
+                            (row-tiled int8, [D2]); routed and shared experts alike */
 } moe_config;
 
 /* A layer's weights. Routed arrays hold E experts back to back; shared arrays
  * hold n_shared experts back to back (may be NULL when n_shared == 0).
  *   router_w [E][H] fp32 row-major;  router_bias [E] fp32 (selection only)
  *   w13      per expert: row-tiled int4 of [2I][H] (gate rows 0..I-1, up rows I..2I-1), I*H bytes
+ *            (int8: 2*I*H bytes)
  *   s13      per expert: [2I] fp32 row scales
- *   w2       per expert: row-tiled int4 of [H][I] (down projection), H*I/2 bytes
+ *   w2       per expert: row-tiled int4 of [H][I] (down projection), H*I/2 bytes (int8: H*I bytes)
  *   s2       per expert: [H] fp32 row scales                                      */
 typedef struct moe_layer_weights {
   const float* router_w;
@@ -148,6 +161,13 @@ size_t moe_workspace_bytes(const moe_config* cfg, int32_t max_tokens);
  * s = amax/7, q = round-half-away(w * (1/s)) clamped to [-7,7], s = 0 for an
  * all-zero row. rows % 64 == 0, cols % 32 == 0. */
 int32_t moe_quantize_int4(const float* w, int32_t rows, int32_t cols, uint8_t* packed, float* scales,
+                          hipStream_t stream);
+
+/* Converter: fp32 rows w [rows][cols] -> row-tiled int8 (rows*cols bytes) +
+ * per-row fp32 scales [D2]: s = amax/127, q = round-half-away(w * (1/s))
+ * clamped to [-127,127], s = 0 for an all-zero row. rows % 64 == 0,
+ * cols % 32 == 0. */
+int32_t moe_quantize_int8(const float* w, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
                           hipStream_t stream);
 
 /* Q8_0 of n fp32 values (n % 32 == 0) [B]: per 32-block d = amax/127,

@@ -28,6 +28,8 @@
 // ascending order from +0; the class totals are added in class order from +0;
 // one multiply by the row scale. So a bucket's result does not depend on the
 // path it takes.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -125,6 +127,54 @@ __device__ __forceinline__ v4i unpack_a16(v2i w) {
   return r;
 }
 
+// One lane's codes of one K block (16 bytes of int4 or 32 of int8), and the
+// block dot against a block of permuted activation codes. int4: a word of
+// eight nibbles splits into two int8 words holding 16*q (sum shifted right by
+// 4, exact); int8: the codes are stored in the activations' permuted order,
+// so word k pairs with activation word k.
+template <int W>
+struct WBlk {
+  uint4 v[W / 4];
+};
+template <int W>
+__device__ __forceinline__ void load_wblk(WBlk<W>& b, const uint8_t* p) {
+#pragma unroll
+  for (int i = 0; i < W / 4; ++i) b.v[i] = reinterpret_cast<const uint4*>(p)[i];
+}
+template <int W>
+struct WPrep;
+template <>
+struct WPrep<4> {
+  int lo[4], hi[4];
+};
+template <>
+struct WPrep<8> {
+  uint4 a, b;
+};
+__device__ __forceinline__ void prep_wblk(const WBlk<4>& b, WPrep<4>& p) {
+  split16(b.v[0].x, p.lo[0], p.hi[0]);
+  split16(b.v[0].y, p.lo[1], p.hi[1]);
+  split16(b.v[0].z, p.lo[2], p.hi[2]);
+  split16(b.v[0].w, p.lo[3], p.hi[3]);
+}
+__device__ __forceinline__ void prep_wblk(const WBlk<8>& b, WPrep<8>& p) {
+  p.a = b.v[0];
+  p.b = b.v[1];
+}
+__device__ __forceinline__ int wdot(const WPrep<4>& p, v4i xa, v4i xb) { return dot_block16(p.lo, p.hi, xa, xb) >> 4; }
+__device__ __forceinline__ int wdot(const WPrep<8>& p, v4i xa, v4i xb) {
+  int s = 0;
+  s = __builtin_amdgcn_sdot4((int)p.a.x, xa.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)p.a.y, xa.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)p.a.z, xa.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)p.a.w, xa.w, s, false);
+  s = __builtin_amdgcn_sdot4((int)p.b.x, xb.x, s, false);
+  s = __builtin_amdgcn_sdot4((int)p.b.y, xb.y, s, false);
+  s = __builtin_amdgcn_sdot4((int)p.b.z, xb.z, s, false);
+  s = __builtin_amdgcn_sdot4((int)p.b.w, xb.w, s, false);
+  return s;
+}
+
 __device__ __forceinline__ int out_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 // SwiGLU + Q8_0 of h for 64 consecutive rows held one per lane; writes the
@@ -213,7 +263,7 @@ __device__ __forceinline__ void stage_store(const Staged<N>& st, int K, int8_t* 
   __syncthreads();
 }
 
-template <int N, int PF, bool TAP>
+template <int N, int PF, bool TAP, int W>
 __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
                                                 const uint8_t* w13, const float* s13, int tile, char* lds) {
   const int H = a.H, I = a.I, nb = H / 32;
@@ -237,15 +287,15 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
   // the first weight blocks are requested before the staged codes are waited for
   const int ncls = w < nb ? (nb - w + kGW - 1) / kGW : 0;  // blocks of class w
   const int last = max(ncls - 1, 0);
-  const uint8_t* gcls = w13 + tb_off(tile, min(w, nb - 1), nb) + (size_t)lane * 16;
-  const uint8_t* ucls = w13 + tb_off(I / 64 + tile, min(w, nb - 1), nb) + (size_t)lane * 16;
-  constexpr size_t step = kGW * kBlkStride;  // class stride
-  uint4 bg[PF], bu[PF];
+  const uint8_t* gcls = w13 + tbw_off<W>(tile, min(w, nb - 1), nb) + (size_t)lane * (4 * W);
+  const uint8_t* ucls = w13 + tbw_off<W>(I / 64 + tile, min(w, nb - 1), nb) + (size_t)lane * (4 * W);
+  constexpr size_t step = kGW * kTileBlock<W>;  // class stride
+  WBlk<W> bg[PF], bu[PF];
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
     const size_t off = (size_t)min(kk, last) * step;
-    bg[kk] = *reinterpret_cast<const uint4*>(gcls + off);
-    bu[kk] = *reinterpret_cast<const uint4*>(ucls + off);
+    load_wblk<W>(bg[kk], gcls + off);
+    load_wblk<W>(bu[kk], ucls + off);
   }
   stage_store<N>(st, H, xs, xd);
   int tap_i = -1;
@@ -263,26 +313,19 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
         const int j = j0 + kk;
         const bool live = j < ncls;
         const int blk = w + kGW * min(j, ncls - 1);
-        const uint4 g4 = bg[kk], u4 = bu[kk];
+        WPrep<W> pg, pu;
+        prep_wblk(bg[kk], pg);
+        prep_wblk(bu[kk], pu);
         const size_t noff = (size_t)min(j + PF, ncls - 1) * step;  // past the end: a repeat (cache hit)
-        bg[kk] = *reinterpret_cast<const uint4*>(gcls + noff);
-        bu[kk] = *reinterpret_cast<const uint4*>(ucls + noff);
-        int gl[4], gh[4], ul[4], uh[4];
-        split16(g4.x, gl[0], gh[0]);
-        split16(g4.y, gl[1], gh[1]);
-        split16(g4.z, gl[2], gh[2]);
-        split16(g4.w, gl[3], gh[3]);
-        split16(u4.x, ul[0], uh[0]);
-        split16(u4.y, ul[1], uh[1]);
-        split16(u4.z, ul[2], uh[2]);
-        split16(u4.w, ul[3], uh[3]);
+        load_wblk<W>(bg[kk], gcls + noff);
+        load_wblk<W>(bu[kk], ucls + noff);
 #pragma unroll
         for (int i = 0; i < N; ++i) {
           const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)blk * 32);
           const v4i xa = xb4[0], xb = xb4[1];
           const float d = xd[i * nb + blk];
-          const int Sg = dot_block16(gl, gh, xa, xb) >> 4;
-          const int Su = dot_block16(ul, uh, xa, xb) >> 4;
+          const int Sg = wdot(pg, xa, xb);
+          const int Su = wdot(pu, xa, xb);
           if (live) {
             ag[i] = fmaf(d, (float)Sg, ag[i]);
             au[i] = fmaf(d, (float)Su, au[i]);
@@ -316,7 +359,7 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
   }
 }
 
-template <int N, int PF, bool TAP>
+template <int N, int PF, bool TAP, int W>
 __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
                                               const uint8_t* w2, const float* s2, int tile, char* lds) {
   const int H = a.H, I = a.I, nbi = I / 32;
@@ -338,11 +381,11 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
   }
   const int ncls = w < nbi ? (nbi - w + kGW - 1) / kGW : 0;
   const int last = max(ncls - 1, 0);
-  const uint8_t* wcls = w2 + tb_off(tile, min(w, nbi - 1), nbi) + (size_t)lane * 16;
-  constexpr size_t step = kGW * kBlkStride;
-  uint4 bw[PF];
+  const uint8_t* wcls = w2 + tbw_off<W>(tile, min(w, nbi - 1), nbi) + (size_t)lane * (4 * W);
+  constexpr size_t step = kGW * kTileBlock<W>;
+  WBlk<W> bw[PF];
 #pragma unroll
-  for (int kk = 0; kk < PF; ++kk) bw[kk] = *reinterpret_cast<const uint4*>(wcls + (size_t)min(kk, last) * step);
+  for (int kk = 0; kk < PF; ++kk) load_wblk<W>(bw[kk], wcls + (size_t)min(kk, last) * step);
   stage_store<N>(st, I, hs, hd);
   int tap_i = -1;
   if (TAP) {
@@ -359,17 +402,13 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
         const int j = j0 + kk;
         const bool live = j < ncls;
         const int blk = w + kGW * min(j, ncls - 1);
-        const uint4 w4 = bw[kk];
-        bw[kk] = *reinterpret_cast<const uint4*>(wcls + (size_t)min(j + PF, ncls - 1) * step);
-        int lo[4], hi[4];
-        split16(w4.x, lo[0], hi[0]);
-        split16(w4.y, lo[1], hi[1]);
-        split16(w4.z, lo[2], hi[2]);
-        split16(w4.w, lo[3], hi[3]);
+        WPrep<W> pw;
+        prep_wblk(bw[kk], pw);
+        load_wblk<W>(bw[kk], wcls + (size_t)min(j + PF, ncls - 1) * step);
 #pragma unroll
         for (int i = 0; i < N; ++i) {
           const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)blk * 32);
-          const int S = dot_block16(lo, hi, hb4[0], hb4[1]) >> 4;
+          const int S = wdot(pw, hb4[0], hb4[1]);
           if (live) {
             acc[i] = fmaf(hd[i * nbi + blk], (float)S, acc[i]);
             if (TAP && i == tap_i) a.t_dn_sums[(size_t)o * nbi + blk] = S;
@@ -483,22 +522,47 @@ __device__ __forceinline__ void load_operands(__amdgpu_buffer_rsrc_t xr, __amdgp
   }
 }
 
-template <int NTT>
+// The A operand of one block: int4 loads the lane's 8 bytes and unpacks them
+// to 16 x the codes (unpack_a16); int8 loads the lane's 16 bytes as they are.
+// Lane offset: row (lane % 32) and half (lane / 32) of the block.
+template <int W>
+using ARaw = typename std::conditional<W == 4, v2i, v4i>::type;
+template <int W>
+__device__ __forceinline__ uint32_t a_lane_off(int col, int half) {
+  return (uint32_t)col * (4 * W) + (uint32_t)(2 * W) * half;
+}
+template <int W>
+__device__ __forceinline__ ARaw<W> load_a(__amdgpu_buffer_rsrc_t r, uint32_t loff, int blk) {
+  if constexpr (W == 4) return buf_v2(r, loff, (uint32_t)blk * (uint32_t)kTileBlock<4>);
+  else return buf_v4(r, loff, (uint32_t)blk * (uint32_t)kTileBlock<8>);
+}
+template <int W>
+__device__ __forceinline__ v4i a_operand(ARaw<W> w) {
+  if constexpr (W == 4) return unpack_a16(w);
+  else return w;
+}
+// MFMA block sums in units of the true sum: int4 tiles hold 16 x the sums.
+template <int W>
+__device__ __forceinline__ int true_sum(int s) {
+  return W == 4 ? s >> 4 : s;
+}
+
+template <int NTT, int W>
 __device__ __forceinline__ void load_gu_block(__amdgpu_buffer_rsrc_t gr, __amdgpu_buffer_rsrc_t ur,
                                               __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t dr, int blk,
                                               uint32_t loff, const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT],
-                                              v2i& rg, v2i& ru, v4i (&rb)[NTT], float (&rd)[NTT]) {
-  rg = buf_v2(gr, loff, (uint32_t)blk * kBlkStride);
-  ru = buf_v2(ur, loff, (uint32_t)blk * kBlkStride);
+                                              ARaw<W>& rg, ARaw<W>& ru, v4i (&rb)[NTT], float (&rd)[NTT]) {
+  rg = load_a<W>(gr, loff, blk);
+  ru = load_a<W>(ur, loff, blk);
   load_operands<NTT>(xr, dr, blk, xo, xso, rb, rd);
 }
 
-template <int NTT>
+template <int NTT, int W>
 __device__ __forceinline__ void load_dn_block(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr,
                                               __amdgpu_buffer_rsrc_t dr, int blk, uint32_t loff,
-                                              const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT], v2i& ra,
+                                              const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT], ARaw<W>& ra,
                                               v4i (&rb)[NTT], float (&rd)[NTT]) {
-  ra = buf_v2(wr, loff, (uint32_t)blk * kBlkStride);
+  ra = load_a<W>(wr, loff, blk);
   load_operands<NTT>(xr, dr, blk, xo, xso, rb, rd);
 }
 
@@ -506,13 +570,13 @@ __device__ __forceinline__ void load_dn_block(__amdgpu_buffer_rsrc_t wr, __amdgp
 // each), NTT x 32 tokens. t32 = index of the 32-row block. Columns past the
 // bucket's end compute on the last token (a valid address) and are never
 // stored; each column's results depend on that column alone.
-template <int NTT, int PF, bool TAP>
+template <int NTT, int PF, bool TAP, int W>
 __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w13, const float* s13,
                                  int t32, int lane, MfmaTotals<NTT, 2>& T) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nb = H / 32;
   const int col = lane & 31, half = lane >> 5;
-  const uint32_t loff = (uint32_t)col * 16 + 8 * half;
+  const uint32_t loff = a_lane_off<W>(col, half);
   // Operand addresses: a wave-uniform base per block (scalar registers) plus a
   // 32-bit lane offset from the tile's first 32-position group.
   const int g0 = (k.p0 + t0) >> 5;
@@ -533,31 +597,31 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   totals_zero(T, lane);
   const v16i zero = {0};
   const int r0 = tile * 64 + s * 32;
-  const auto gr = buf_rsrc(w13 + tb_off(tile, 0, nb) + s * 512);
-  const auto ur = buf_rsrc(w13 + tb_off(I / 64 + tile, 0, nb) + s * 512);
+  const auto gr = buf_rsrc(w13 + tbw_off<W>(tile, 0, nb) + s * 32 * (4 * W));
+  const auto ur = buf_rsrc(w13 + tbw_off<W>(I / 64 + tile, 0, nb) + s * 32 * (4 * W));
   const auto xr = buf_rsrc(xbase), dr = buf_rsrc(dbase);
   float ag[NTT][16], au[NTT][16];  // class chains
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) ag[tt][i] = au[tt][i] = 0.0f;
-  v2i rg[PF], ru[PF];
+  ARaw<W> rg[PF], ru[PF];
   v4i rb[PF][NTT];
   float rd[PF][NTT];
   int fetch = 0;  // next block to load
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
-    load_gu_block(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
+    load_gu_block<NTT, W>(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
     fetch = class_major_next(fetch, nb);
   }
   int blk = 0;  // block being consumed
   for (int b0 = 0; b0 < nb; b0 += PF) {
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const v4i Ag = unpack_a16(rg[kk]), Au = unpack_a16(ru[kk]);
+      const v4i Ag = a_operand<W>(rg[kk]), Au = a_operand<W>(ru[kk]);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, rb[kk][tt], zero, 0, 0, 0);  // 16 x block sums
+        const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, rb[kk][tt], zero, 0, 0, 0);  // (16 x) block sums
         const v16i Su = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, rb[kk][tt], zero, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(rd[kk][tt], (float)Sg[i], ag[tt][i]);
@@ -566,13 +630,13 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
         if (TAP && tt == tap_tt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = Sg[i] >> 4;
-            a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = Su[i] >> 4;
+            a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = true_sum<W>(Sg[i]);
+            a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = true_sum<W>(Su[i]);
           }
         }
       }
       // refill the slot just consumed
-      load_gu_block(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
+      load_gu_block<NTT, W>(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
       fetch = class_major_next(fetch, nb);
       if (blk + kDotClasses >= nb) {  // blk ends its class
 #pragma unroll
@@ -621,7 +685,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
       if (a.t_qh) a.t_qh[(size_t)slot * I + r0 + m] = q;
     }
     if (half == 0) {
-      a.hdt[pb_sc(p, r0 / 32, I / 32)] = __fmul_rn(d, 0.0625f);  // scale / 16: see unpack_a16
+      a.hdt[pb_sc(p, r0 / 32, I / 32)] = __fmul_rn(d, a.op_scale);  // 1/16 for int4: see unpack_a16
       if (a.t_dh) a.t_dh[(size_t)slot * (I / 32) + r0 / 32] = d;
     }
   }
@@ -629,13 +693,13 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
 
 // 32 output rows per wavefront, NTT x 32 positions. t32 = index of the
 // 32-row block. Columns past the bucket's end as in the gate/up tile.
-template <int NTT, int PF, bool TAP>
+template <int NTT, int PF, bool TAP, int W>
 __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w2, const float* s2,
                                int t32, int lane, MfmaTotals<NTT, 1>& T) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nbi = I / 32;
   const int col = lane & 31, half = lane >> 5;
-  const uint32_t loff = (uint32_t)col * 16 + 8 * half;
+  const uint32_t loff = a_lane_off<W>(col, half);
   const int g0 = (k.p0 + t0) >> 5;
   const int8_t* xbase = a.ht + pb_off(g0 * 32, 0, nbi);
   const char* dbase = reinterpret_cast<const char*>(a.hdt + pb_sc(g0 * 32, 0, nbi));
@@ -654,27 +718,27 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   totals_zero(T, lane);
   const v16i zero = {0};
   const int r0 = tile * 64 + s * 32;
-  const auto wr = buf_rsrc(w2 + tb_off(tile, 0, nbi) + s * 512);
+  const auto wr = buf_rsrc(w2 + tbw_off<W>(tile, 0, nbi) + s * 32 * (4 * W));
   const auto xr = buf_rsrc(xbase), dr = buf_rsrc(dbase);
   float acc[NTT][16];  // class chain
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[tt][i] = 0.0f;
-  v2i ra[PF];
+  ARaw<W> ra[PF];
   v4i rb[PF][NTT];
   float rd[PF][NTT];
   int fetch = 0;
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
-    load_dn_block(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
+    load_dn_block<NTT, W>(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
     fetch = class_major_next(fetch, nbi);
   }
   int blk = 0;
   for (int b0 = 0; b0 < nbi; b0 += PF) {
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const v4i A = unpack_a16(ra[kk]);
+      const v4i A = a_operand<W>(ra[kk]);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, rb[kk][tt], zero, 0, 0, 0);  // 16 x block sums
@@ -682,10 +746,10 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
         for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(rd[kk][tt], (float)S[i], acc[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = S[i] >> 4;
+          for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = true_sum<W>(S[i]);
         }
       }
-      load_dn_block(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
+      load_dn_block<NTT, W>(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
       fetch = class_major_next(fetch, nbi);
       if (blk + kDotClasses >= nbi) {
 #pragma unroll
@@ -747,7 +811,7 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
   const int sitems = (b_hi - b_lo) * nv;
   for (int it = tid; it < sitems; it += 256) {
     const int j = it % nv, b = b_lo + it / nv;
-    a.xdt[pb_sc(k.p0 + t0 + j, b, nb)] = __fmul_rn(a.dx[(size_t)s_tok[j] * nb + b], 0.0625f);  // see unpack_a16
+    a.xdt[pb_sc(k.p0 + t0 + j, b, nb)] = __fmul_rn(a.dx[(size_t)s_tok[j] * nb + b], a.op_scale);  // see unpack_a16
   }
 }
 
@@ -759,66 +823,67 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
 // 32-token tiles, 2 for 64 (the depth must divide the block count; 2 always does).
 
 // PF: blocks in flight per wavefront (chosen by the host).
-template <int PF, bool TAP>
+// W: weight code width (4 or 8), chosen by the host from the configuration.
+template <int PF, bool TAP, int W>
 __global__ __launch_bounds__(kGemvThreads) void k_gateup_gemv(ExpertArgs a) {
   extern __shared__ char gemv_lds[];
   const int li = blockIdx.y, tile = blockIdx.x;
   if (li >= *cptr(a.list_count)) return;
   const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
   const int c0 = cptr(a.list)[2 * li + 1];
-  const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, (size_t)a.I * a.H);
+  const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
   const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
   const int nn = min(kGemvMaxN, k.n - c0);
-  if (nn == 1) gemv_gateup_run<1, PF, TAP>(a, k, c0, nn, w13, s13, tile, gemv_lds);
-  else if (nn == 2) gemv_gateup_run<2, PF, TAP>(a, k, c0, nn, w13, s13, tile, gemv_lds);
-  else gemv_gateup_run<kGemvMaxN, PF, TAP>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  if (nn == 1) gemv_gateup_run<1, PF, TAP, W>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  else if (nn == 2) gemv_gateup_run<2, PF, TAP, W>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  else gemv_gateup_run<kGemvMaxN, PF, TAP, W>(a, k, c0, nn, w13, s13, tile, gemv_lds);
 }
 
-template <int PF, bool TAP>
+template <int PF, bool TAP, int W>
 __global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
   extern __shared__ char gemv_lds[];
   const int li = blockIdx.y, tile = blockIdx.x;
   if (li >= *cptr(a.list_count)) return;
   const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
   const int c0 = cptr(a.list)[2 * li + 1];
-  const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, (size_t)a.H * a.I / 2);
+  const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
   const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
   const int nn = min(kGemvMaxN, k.n - c0);
-  if (nn == 1) gemv_down_run<1, PF, TAP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
-  else if (nn == 2) gemv_down_run<2, PF, TAP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
-  else gemv_down_run<kGemvMaxN, PF, TAP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  if (nn == 1) gemv_down_run<1, PF, TAP, W>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else if (nn == 2) gemv_down_run<2, PF, TAP, W>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else gemv_down_run<kGemvMaxN, PF, TAP, W>(a, k, c0, nn, w2, s2, tile, gemv_lds);
 }
 
-template <int NTT, int MPF, bool TAP>
+template <int NTT, int MPF, bool TAP, int W>
 __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
                                                     const int32_t* __restrict__ n_tiles) {
   const int y = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
   if (y >= *cptr(n_tiles)) return;
   const Bucket k = load_bucket(a, cptr(tiles)[2 * y]);
   const int t0 = cptr(tiles)[2 * y + 1];
-  const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, (size_t)a.I * a.H);
+  const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
   const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
   __shared__ MfmaTotals<NTT, 2> totals;
   if (NTT == 2 && k.n - t0 <= 32)  // a bucket's last tile with one 32-token half: skip the empty one
-    mfma_gateup_tile<1, MPF, TAP>(a, k, t0, w13, s13, tile, lane, reinterpret_cast<MfmaTotals<1, 2>&>(totals));
+    mfma_gateup_tile<1, MPF, TAP, W>(a, k, t0, w13, s13, tile, lane, reinterpret_cast<MfmaTotals<1, 2>&>(totals));
   else
-    mfma_gateup_tile<NTT, MPF, TAP>(a, k, t0, w13, s13, tile, lane, totals);
+    mfma_gateup_tile<NTT, MPF, TAP, W>(a, k, t0, w13, s13, tile, lane, totals);
 }
 
-template <int NTT, int MPF, bool TAP>
+template <int NTT, int MPF, bool TAP, int W>
 __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
                                                   const int32_t* __restrict__ n_tiles) {
   const int y = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
   if (y >= *cptr(n_tiles)) return;
   const Bucket k = load_bucket(a, cptr(tiles)[2 * y]);
   const int t0 = cptr(tiles)[2 * y + 1];
-  const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, (size_t)a.H * a.I / 2);
+  const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
   const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
   __shared__ MfmaTotals<NTT, 1> totals;
   if (NTT == 2 && k.n - t0 <= 32)
-    mfma_down_tile<1, MPF, TAP>(a, k, t0, w2, s2, tile, lane, reinterpret_cast<MfmaTotals<1, 1>&>(totals));
+    mfma_down_tile<1, MPF, TAP, W>(a, k, t0, w2, s2, tile, lane, reinterpret_cast<MfmaTotals<1, 1>&>(totals));
   else
-    mfma_down_tile<NTT, MPF, TAP>(a, k, t0, w2, s2, tile, lane, totals);
+    mfma_down_tile<NTT, MPF, TAP, W>(a, k, t0, w2, s2, tile, lane, totals);
 }
 
 
@@ -836,14 +901,26 @@ static int gemv_pf(int nblocks, int want) {
 
 template <int PF>
 static void gateup_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_t st) {
-  if (a.t_gu_sums) k_gateup_gemv<PF, true><<<g, kGemvThreads, lds, st>>>(a);
-  else k_gateup_gemv<PF, false><<<g, kGemvThreads, lds, st>>>(a);
+  const bool tap = a.t_gu_sums != nullptr;
+  if (a.wbits == 8) {
+    if (tap) k_gateup_gemv<PF, true, 8><<<g, kGemvThreads, lds, st>>>(a);
+    else k_gateup_gemv<PF, false, 8><<<g, kGemvThreads, lds, st>>>(a);
+  } else {
+    if (tap) k_gateup_gemv<PF, true, 4><<<g, kGemvThreads, lds, st>>>(a);
+    else k_gateup_gemv<PF, false, 4><<<g, kGemvThreads, lds, st>>>(a);
+  }
 }
 
 template <int PF>
 static void down_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_t st) {
-  if (a.t_dn_sums) k_down_gemv<PF, true><<<g, kGemvThreads, lds, st>>>(a);
-  else k_down_gemv<PF, false><<<g, kGemvThreads, lds, st>>>(a);
+  const bool tap = a.t_dn_sums != nullptr;
+  if (a.wbits == 8) {
+    if (tap) k_down_gemv<PF, true, 8><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 8><<<g, kGemvThreads, lds, st>>>(a);
+  } else {
+    if (tap) k_down_gemv<PF, true, 4><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 4><<<g, kGemvThreads, lds, st>>>(a);
+  }
 }
 
 hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
@@ -870,31 +947,31 @@ hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_ch
   return hipGetLastError();
 }
 
-template <int NTT>
+template <int NTT, int W>
 static void mfma_gateup_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
   constexpr int MPF = NTT == 1 ? 4 : 2;
   if ((a.H / 32) % MPF == 0) {
-    if (tap) k_gateup_mfma<NTT, MPF, true><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_gateup_mfma<NTT, MPF, false><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_gateup_mfma<NTT, MPF, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_gateup_mfma<NTT, MPF, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   } else {
-    if (tap) k_gateup_mfma<NTT, 2, true><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_gateup_mfma<NTT, 2, false><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_gateup_mfma<NTT, 2, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_gateup_mfma<NTT, 2, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   }
 }
 
-template <int NTT>
+template <int NTT, int W>
 static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                              hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
   constexpr int MPF = NTT == 1 ? 4 : 2;
   if ((a.I / 32) % MPF == 0) {
-    if (tap) k_down_mfma<NTT, MPF, true><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_down_mfma<NTT, MPF, false><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_down_mfma<NTT, MPF, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_down_mfma<NTT, MPF, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   } else {
-    if (tap) k_down_mfma<NTT, 2, true><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_down_mfma<NTT, 2, false><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_down_mfma<NTT, 2, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_down_mfma<NTT, 2, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   }
 }
 
@@ -910,8 +987,13 @@ hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int3
                               hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(a.I / 32, grid);
-  if (ntt == 2) mfma_gateup_launch<2>(a, g, tiles, n_tiles, st);
-  else mfma_gateup_launch<1>(a, g, tiles, n_tiles, st);
+  if (a.wbits == 8) {
+    if (ntt == 2) mfma_gateup_launch<2, 8>(a, g, tiles, n_tiles, st);
+    else mfma_gateup_launch<1, 8>(a, g, tiles, n_tiles, st);
+  } else {
+    if (ntt == 2) mfma_gateup_launch<2, 4>(a, g, tiles, n_tiles, st);
+    else mfma_gateup_launch<1, 4>(a, g, tiles, n_tiles, st);
+  }
   return hipGetLastError();
 }
 
@@ -919,8 +1001,13 @@ hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_
                             hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(a.H / 32, grid);
-  if (ntt == 2) mfma_down_launch<2>(a, g, tiles, n_tiles, st);
-  else mfma_down_launch<1>(a, g, tiles, n_tiles, st);
+  if (a.wbits == 8) {
+    if (ntt == 2) mfma_down_launch<2, 8>(a, g, tiles, n_tiles, st);
+    else mfma_down_launch<1, 8>(a, g, tiles, n_tiles, st);
+  } else {
+    if (ntt == 2) mfma_down_launch<2, 4>(a, g, tiles, n_tiles, st);
+    else mfma_down_launch<1, 4>(a, g, tiles, n_tiles, st);
+  }
   return hipGetLastError();
 }
 

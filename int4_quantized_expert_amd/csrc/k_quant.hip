@@ -96,6 +96,45 @@ __global__ __launch_bounds__(256) void k_quant_int4(const float* __restrict__ w,
   }
 }
 
+// Per-row symmetric int8 (the MTP head's precision): one workgroup per row;
+// amax over the row, then each lane encodes its 32-element blocks into the
+// row-tiled int8 layout, each 8-byte group with its even elements first.
+__global__ __launch_bounds__(256) void k_quant_int8(const float* __restrict__ w, int cols,
+                                                    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int r = blockIdx.x;
+  const int nb = cols / 32;
+  const float* row = w + (size_t)r * cols;
+  float amax = 0.0f;
+  for (int k = threadIdx.x; k < cols; k += blockDim.x) amax = fmaxf(amax, fabsf(row[k]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(amax, 127.0f);
+  const float inv = (s == 0.0f) ? 0.0f : __fdiv_rn(1.0f, s);
+  if (threadIdx.x == 0) scales[r] = s;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const float* src = row + b * 32;
+    int8_t q[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float qf = roundf(__fmul_rn(src[i], inv));
+      q[i] = (int8_t)(int)fminf(fmaxf(qf, -127.0f), 127.0f);
+    }
+    uint32_t wv[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      wv[2 * g] = pack4(q[8 * g], q[8 * g + 2], q[8 * g + 4], q[8 * g + 6]);
+      wv[2 * g + 1] = pack4(q[8 * g + 1], q[8 * g + 3], q[8 * g + 5], q[8 * g + 7]);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(codes + tbw_off<8>(r / 64, b, nb) + (size_t)(r % 64) * 32);
+    dst[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    dst[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+  }
+}
+
 __global__ void k_q8_0_plain(const float* __restrict__ x, int64_t nblocks, int8_t* __restrict__ q,
                              float* __restrict__ d) {
   int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -124,6 +163,12 @@ hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hip
   int64_t nb = n / 32;
   if (nb == 0) return hipSuccess;
   k_q8_0_plain<<<(unsigned)((nb + 255) / 256), 256, 0, st>>>(x, nb, q, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int8(const float* w, int rows, int cols, uint8_t* codes, float* scales, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  k_quant_int8<<<rows, 256, 0, st>>>(w, cols, codes, scales);
   return hipGetLastError();
 }
 

@@ -83,6 +83,7 @@ int validate_config(const moe_config* c) {
   if (c->top_k > c->topk_group * (c->n_experts / c->n_group)) return MOE_E_SHAPE;
   if (c->n_shared < 0 || c->n_shared > kMaxShared) return MOE_E_SHAPE;
   if (!std::isfinite(c->routed_scaling_factor) || c->routed_scaling_factor <= 0.0f) return MOE_E_ARG;
+  if (c->weight_bits > 0 && c->weight_bits != 4 && c->weight_bits != 8) return MOE_E_ARG;
   return MOE_OK;
 }
 
@@ -205,6 +206,8 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
   a.K = cfg->top_k;
   a.T = T;
   a.TK = T * cfg->top_k;
+  a.wbits = cfg->weight_bits == 8 ? 8 : 4;
+  a.op_scale = a.wbits == 8 ? 1.0f : 0.0625f;
   Meta* meta = reinterpret_cast<Meta*>(wsb + L.meta);
   a.list = reinterpret_cast<const int32_t*>(wsb + L.gemv);
   a.list_count = &meta->n_gemv;
@@ -305,6 +308,14 @@ int32_t moe_quantize_int4(const float* w, int32_t rows, int32_t cols, uint8_t* p
   if (!w || !packed || !scales) return MOE_E_NULL;
   if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 32 != 0) return MOE_E_SHAPE;
   hipError_t e = launch_quant_int4(w, rows, cols, packed, scales, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_quantize_int8(const float* w, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
+                          hipStream_t stream) {
+  if (!w || !codes || !scales) return MOE_E_NULL;
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 32 != 0) return MOE_E_SHAPE;
+  hipError_t e = launch_quant_int8(w, rows, cols, codes, scales, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -60,6 +60,8 @@ struct WeightView {
 struct ExpertArgs {
   WeightView wv;
   int32_t E, H, I, K, T, TK;
+  int32_t wbits;    // expert weight code width: 4 or 8
+  float op_scale;   // factor on the MFMA operand scales: 1/16 for int4 (A holds 16 q), 1 for int8
   const int32_t* list;        // GEMV work list: (bucket, first token) pairs, chunks of up to kGemvMaxN tokens
   const int32_t* list_count;  // device count of list entries
   const int32_t* bk_e;
@@ -125,6 +127,18 @@ __host__ __device__ __forceinline__ size_t tb_off(int tile, int blk, int nblocks
 }
 constexpr size_t kBlkStride = 1024;  // bytes from block b to block b+1 of a tile
 
+// The same tiling for W-bit codes: a tile-block is 64 rows x 32 elements, 16
+// (int4) or 32 (int8) bytes per row.
+template <int W>
+constexpr size_t kTileBlock = (size_t)1024 * W / 4;
+template <int W>
+__host__ __device__ __forceinline__ size_t tbw_off(int tile, int blk, int nblocks) {
+  return ((size_t)tile * nblocks + blk) * kTileBlock<W>;
+}
+// Bytes of one expert's gate/up and down codes.
+__host__ __device__ __forceinline__ size_t w13_bytes(int H, int I, int wbits) { return (size_t)I * H * wbits / 4; }
+__host__ __device__ __forceinline__ size_t w2_bytes(int H, int I, int wbits) { return (size_t)H * I * wbits / 8; }
+
 // Q8_0 operands of the MFMA tiles are kept position-blocked: the codes of 32
 // consecutive positions for one 32-element block are one contiguous KB (32
 // bytes per position), blocks of a 32-position group follow each other; the
@@ -189,6 +203,7 @@ __device__ __forceinline__ const float* expert_s2(const WeightView& v, int ex, i
 hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float* d, int8_t* q_nat,
                          hipStream_t st);
 hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hipStream_t st);
+hipError_t launch_quant_int8(const float* w, int rows, int cols, uint8_t* codes, float* scales, hipStream_t st);
 hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed, float* scales,
                              hipStream_t st);
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,

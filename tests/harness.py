@@ -1,6 +1,7 @@
-"""Test/bench harness: builds a layer on the GPU through the library's converter
-(moe_quantize_int4) from the seeded generator, and the oracle's counterpart
-(the same fp32 weights quantized by the C oracle) for parity checks.
+"""Test/bench harness: builds a layer on the GPU through the library's converters
+(moe_quantize_int4, or moe_quantize_int8 for int8 experts) from the seeded
+generator, and the oracle's counterpart (the same fp32 weights quantized by the
+C oracle) for parity checks.
 
 Only tests, the smoke check and bench.py import this module.
 """
@@ -13,16 +14,18 @@ from synth import synth
 _ORACLE_CACHE: dict = {}
 
 
-def config_of(shape, gemm_min: int = 0):
+def config_of(shape, gemm_min: int = 0, weight_bits: int = 4):
     import int4_quantized_expert_amd as moe
     return moe.Config(shape.hidden, shape.n_experts, shape.n_group, shape.topk_group, shape.top_k, shape.inter,
-                      shape.n_shared, shape.rsf, gemm_min)
+                      shape.n_shared, shape.rsf, gemm_min, weight_bits)
 
 
 class GpuLayer:
-    """Device-resident layer: router fp32, routed and shared experts in row-tiled int4 with fp32 row scales."""
+    """Device-resident layer: router fp32, routed and shared experts in row-tiled int4 (or int8, weight_bits=8)
+    with fp32 row scales."""
 
-    def __init__(self, shape, seed: int = 0, layer: int = 0, device: str = "cuda", n_shared: int | None = None):
+    def __init__(self, shape, seed: int = 0, layer: int = 0, device: str = "cuda", n_shared: int | None = None,
+                 weight_bits: int = 4):
         import torch
 
         import int4_quantized_expert_amd as moe
@@ -30,17 +33,21 @@ class GpuLayer:
         H, I, E = shape.hidden, shape.inter, shape.n_experts
         NS = shape.n_shared if n_shared is None else n_shared
         self.NS = NS
+        assert weight_bits in (4, 8)
+        self.weight_bits = weight_bits
+        b13, b2 = I * H * weight_bits // 4, H * I * weight_bits // 8
+        quant = moe.moe_quantize_int8 if weight_bits == 8 else moe.moe_quantize_int4
         dev = torch.device(device)
         self.router_w = torch.from_numpy(synth.router_weights(shape, seed, layer)).to(dev)
         self.bias = torch.from_numpy(synth.router_bias(shape, seed, layer)).to(dev)
-        self.w13 = torch.empty((E, I * H), dtype=torch.uint8, device=dev)
+        self.w13 = torch.empty((E, b13), dtype=torch.uint8, device=dev)
         self.s13 = torch.empty((E, 2 * I), dtype=torch.float32, device=dev)
-        self.w2 = torch.empty((E, H * I // 2), dtype=torch.uint8, device=dev)
+        self.w2 = torch.empty((E, b2), dtype=torch.uint8, device=dev)
         self.s2 = torch.empty((E, H), dtype=torch.float32, device=dev)
         ns = max(NS, 1)
-        self.sh_w13 = torch.empty((ns, I * H), dtype=torch.uint8, device=dev)
+        self.sh_w13 = torch.empty((ns, b13), dtype=torch.uint8, device=dev)
         self.sh_s13 = torch.empty((ns, 2 * I), dtype=torch.float32, device=dev)
-        self.sh_w2 = torch.empty((ns, H * I // 2), dtype=torch.uint8, device=dev)
+        self.sh_w2 = torch.empty((ns, b2), dtype=torch.uint8, device=dev)
         self.sh_s2 = torch.empty((ns, H), dtype=torch.float32, device=dev)
         scratch = torch.empty((2 * I, H), dtype=torch.float32, device=dev)
         scratch2 = torch.empty((H, I), dtype=torch.float32, device=dev)
@@ -53,9 +60,9 @@ class GpuLayer:
                 k13, k2, idx = synth.SH_W13, synth.SH_W2, s
                 dst = (self.sh_w13[s], self.sh_s13[s], self.sh_w2[s], self.sh_s2[s])
             synth.gpu_normal_(scratch, seed, synth.stream_id(k13, layer, idx), shape.w_sigma, cuda_stream=st)
-            moe.moe_quantize_int4(scratch, dst[0], dst[1])
+            quant(scratch, dst[0], dst[1])
             synth.gpu_normal_(scratch2, seed, synth.stream_id(k2, layer, idx), shape.w_sigma, cuda_stream=st)
-            moe.moe_quantize_int4(scratch2, dst[2], dst[3])
+            quant(scratch2, dst[2], dst[3])
         del scratch, scratch2
         torch.cuda.synchronize()
 
@@ -76,29 +83,31 @@ class GpuLayer:
         return n
 
 
-def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = False):
-    """(q13, s13, q2, s2) of routed expert e (or shared expert e) from the host generator + oracle quantizer."""
+def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = False, weight_bits: int = 4):
+    """(q13, s13, q2, s2) of routed expert e (or shared expert e) from the host generator + oracle quantizer
+    (per-row int4, or per-row int8 for weight_bits=8)."""
     from oracle import oracle as O
-    key = (shape, e, seed, layer, shared)
+    key = (shape, e, seed, layer, shared, weight_bits)
     if key not in _ORACLE_CACHE:
         if shared:
             w13, w2 = synth.shared_w13(shape, e, seed, layer), synth.shared_w2(shape, e, seed, layer)
         else:
             w13, w2 = synth.expert_w13(shape, e, seed, layer), synth.expert_w2(shape, e, seed, layer)
-        q13, s13 = O.quant_int4_rows(w13)
-        q2, s2 = O.quant_int4_rows(w2)
+        quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
+        q13, s13 = quant(w13)
+        q2, s2 = quant(w2)
         if len(_ORACLE_CACHE) > 48:
             _ORACLE_CACHE.clear()
         _ORACLE_CACHE[key] = (q13, s13, q2, s2)
     return _ORACLE_CACHE[key]
 
 
-def oracle_layer(shape, seed: int = 0, layer: int = 0, n_shared: int | None = None):
+def oracle_layer(shape, seed: int = 0, layer: int = 0, n_shared: int | None = None, weight_bits: int = 4):
     """Whole layer in the oracle's unpacked form (small shapes only)."""
     from oracle import oracle as O
     NS = shape.n_shared if n_shared is None else n_shared
-    parts = [oracle_expert(shape, e, seed, layer) for e in range(shape.n_experts)]
-    sh = [oracle_expert(shape, s, seed, layer, shared=True) for s in range(NS)]
+    parts = [oracle_expert(shape, e, seed, layer, weight_bits=weight_bits) for e in range(shape.n_experts)]
+    sh = [oracle_expert(shape, s, seed, layer, shared=True, weight_bits=weight_bits) for s in range(NS)]
     H, I = shape.hidden, shape.inter
 
     def stack(lst, i, shp, dt):
@@ -111,7 +120,8 @@ def oracle_layer(shape, seed: int = 0, layer: int = 0, n_shared: int | None = No
                     stack(sh, 2, (H, I), np.int8), stack(sh, 3, (H,), np.float32))
 
 
-def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n_shared: int | None = None):
+def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n_shared: int | None = None,
+                  weight_bits: int = 4):
     """Oracle outputs for selected tokens of a batch, one token at a time (any size).
 
     Returns dict per token: ids, w, flags, rows {k: e_out row}, shared rows, y."""
@@ -128,10 +138,10 @@ def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n
         qx, dx = O.q8_0(xt[0])
         rows, shrows = [], []
         for k in range(shape.top_k):
-            q13, s13, q2, s2 = oracle_expert(shape, int(ids[0, k]), seed, layer)
+            q13, s13, q2, s2 = oracle_expert(shape, int(ids[0, k]), seed, layer, weight_bits=weight_bits)
             rows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
         for s in range(NS):
-            q13, s13, q2, s2 = oracle_expert(shape, s, seed, layer, shared=True)
+            q13, s13, q2, s2 = oracle_expert(shape, s, seed, layer, shared=True, weight_bits=weight_bits)
             shrows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
         er = np.stack(rows)[None]
         es = np.stack(shrows)[:, None] if NS else None

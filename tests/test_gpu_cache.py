@@ -46,7 +46,7 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False,
     into both the cache and the simulator; usage_check: record usage in the simulator from the oracle's
     routing and compare it with the cache's at every pin."""
     sh = layer.shape
-    cfg = config_of(sh, gemm_min)
+    cfg = config_of(sh, gemm_min, layer.weight_bits)
     Tmax = max(x.shape[0] for x in xs)
     cache = moe.ExpertCache(cfg, n_slots, Tmax)
     sim = O.LRU(sh.n_experts, n_slots)
@@ -82,12 +82,20 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False,
     st = cache.stats()
     assert st["hits"] == hits and st["misses"] == misses and st["steps"] == len(xs)
     assert st["evictions"] == sim.counters()["evictions"]
-    per = sh.inter * sh.hidden + 2 * sh.inter * 4 + sh.hidden * sh.inter // 2 + sh.hidden * 4
+    per = sum(t[0].numel() * t.element_size() for t in (layer.w13, layer.s13, layer.w2, layer.s2))
+    wb = layer.weight_bits
+    assert per == sh.inter * sh.hidden * wb // 4 + 2 * sh.inter * 4 + sh.hidden * sh.inter * wb // 8 + sh.hidden * 4
     assert st["bytes_h2d"] == (misses + loaded) * per
     if usage_check:
         assert np.array_equal(cache.usage(), sim.usage())
     cache.destroy()
     return st
+
+
+@pytest.fixture(scope="module")
+def tiny8():
+    layer = GpuLayer(synth.TINY, weight_bits=8)
+    return layer, host_experts(layer)
 
 
 @pytest.mark.parametrize("n_slots", [4, 1, 16])
@@ -112,6 +120,15 @@ def test_cache_tiny_mfma_and_ragged(tiny):
     layer, (hx, _) = tiny
     xs = [synth.hidden_states(synth.TINY, T, seed=1, step=s) for s, T in enumerate([8, 1, 16, 3, 8])]
     _run_steps(layer, hx, 4, xs, gemm_min=1)
+
+
+@pytest.mark.parametrize("gemm_min", [0, 1])
+def test_cache_tiny_int8_weights(tiny8, gemm_min):
+    """int8 experts through the cache: slots sized for int8, copies of the int8 bytes, output equal to the
+    all-resident int8 layer; with pins."""
+    layer, (hx, _) = tiny8
+    xs = [synth.hidden_states(synth.TINY, T, seed=4, step=s) for s, T in enumerate([8, 1, 16, 3, 8, 8, 5])]
+    _run_steps(layer, hx, 4, xs, gemm_min=gemm_min, pins={4: 2}, usage_check=True)
 
 
 @pytest.mark.parametrize("n_slots,pins", [(6, {8: 3}), (4, {5: 2, 10: 0, 12: 3}), (1, {6: 0})])
