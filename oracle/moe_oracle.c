@@ -62,6 +62,43 @@ void orc_quant_int8_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, 
   }
 }
 
+/* Grouped int4 scales ("Show HN", benchmarks: grouped scales win back most of
+ * the accuracy the int4 container loses; the pages fix neither the group size
+ * nor the scale format). Reading: each row is cut into groups of `group`
+ * consecutive elements along K, and each group is quantized like a row of
+ * orc_quant_int4_rows: s = amax/7, q = clamp(round-half-away(w * (1/s)),
+ * -7, 7), s = 0 and q = 0 for an all-zero group. s is [rows][cols/group]. With
+ * group = cols this is orc_quant_int4_rows. */
+void orc_quant_int4_grouped(const float* w, int64_t rows, int64_t cols, int64_t group, int8_t* q, float* s) {
+  const int64_t ng = cols / group;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < ng; ++g) {
+      const float* v = w + r * cols + g * group;
+      float amax = 0.0f;
+      for (int64_t k = 0; k < group; ++k) {
+        float a = fabsf(v[k]);
+        if (a > amax) amax = a;
+      }
+      float sc = amax / 7.0f;
+      float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
+      for (int64_t k = 0; k < group; ++k) {
+        float t = roundf(v[k] * inv);
+        if (t > 7.0f) t = 7.0f;
+        if (t < -7.0f) t = -7.0f;
+        q[r * cols + g * group + k] = (int8_t)t;
+      }
+      s[r * ng + g] = sc;
+    }
+}
+
+/* Group scales in the device layout: for each tile of 64 rows and each group,
+ * the 64 rows' scales are adjacent; the scale of row r, group g sits at
+ * index ((r/64) * ng + g) * 64 + r%64. Output [rows][ng]. */
+void orc_unpack_scales_tiled64(const float* in, int64_t rows, int64_t ng, float* s) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < ng; ++g) s[r * ng + g] = in[((r / 64) * ng + g) * 64 + r % 64];
+}
+
 /* Row-tiled int8 layout of a [rows][cols] matrix: tiles of 64 rows; for each
  * 32-element block, the 64 rows' 32-byte blocks are adjacent. Byte j of block
  * b of row r sits at ((r/64) * (cols/32) + b) * 2048 + (r%64) * 32 + j, and
@@ -295,6 +332,29 @@ float orc_dot_q4q8(const int8_t* q4, float srow, const int8_t* q8, const float* 
   return srow * total;
 }
 
+/* The same dot with grouped weight scales (see orc_quant_int4_grouped). The
+ * reading keeps the class structure above and moves the weight scale into the
+ * blocks: block b contributes fmaf(d8[b] * sg[g(b)], S_b, acc), where the
+ * product of the activation block scale and the scale of the group holding
+ * block b is rounded to fp32 first; there is no row scale at the end. sg holds
+ * the row's n/group scales; group is a multiple of 32. */
+float orc_dot_q4q8_grouped(const int8_t* q4, const float* sg, int64_t group, const int8_t* q8, const float* d8,
+                           int64_t n) {
+  const int64_t nb = n / 32;
+  float total = 0.0f;
+  for (int c = 0; c < ORC_DOT_CLASSES; ++c) {
+    float acc = 0.0f;
+    for (int64_t blk = c; blk < nb; blk += ORC_DOT_CLASSES) {
+      int32_t S = 0;
+      for (int i = 0; i < 32; ++i) S += (int32_t)q4[blk * 32 + i] * (int32_t)q8[blk * 32 + i];
+      const float scale = d8[blk] * sg[(blk * 32) / group];
+      acc = fmaf(scale, (float)S, acc);
+    }
+    total = total + acc;
+  }
+  return total;
+}
+
 /* SwiGLU gate: silu(g) * u = g * u / (1 + exp(-g)), in fp64, rounded once. */
 float orc_swiglu(float g, float u) {
   return (float)(((double)g * (double)u) / (1.0 + exp(-(double)g)));
@@ -308,15 +368,29 @@ float orc_swiglu(float g, float u) {
 void orc_expert_token(int32_t H, int32_t I, const int8_t* q13, const float* s13, const int8_t* q2,
                       const float* s2, const int8_t* qx, const float* dx, float* h, int8_t* qh, float* dh,
                       float* out, int32_t* S13, int32_t* S2) {
+  orc_expert_token_g(H, I, 0, q13, s13, q2, s2, qx, dx, h, qh, dh, out, S13, S2);
+}
+
+/* group = 0: one scale per row (s13 [2I], s2 [H]); group > 0: grouped scales
+ * (s13 [2I][H/group], s2 [H][I/group]). */
+static float expert_dot(const int8_t* q, const float* s, int64_t row, int32_t group, const int8_t* q8,
+                        const float* d8, int64_t n) {
+  if (group == 0) return orc_dot_q4q8(q + row * n, s[row], q8, d8, n);
+  return orc_dot_q4q8_grouped(q + row * n, s + row * (n / group), group, q8, d8, n);
+}
+
+void orc_expert_token_g(int32_t H, int32_t I, int32_t group, const int8_t* q13, const float* s13, const int8_t* q2,
+                        const float* s2, const int8_t* qx, const float* dx, float* h, int8_t* qh, float* dh,
+                        float* out, int32_t* S13, int32_t* S2) {
   for (int32_t r = 0; r < I; ++r) {
-    float g = orc_dot_q4q8(q13 + (int64_t)r * H, s13[r], qx, dx, H);
-    float u = orc_dot_q4q8(q13 + (int64_t)(I + r) * H, s13[I + r], qx, dx, H);
+    float g = expert_dot(q13, s13, r, group, qx, dx, H);
+    float u = expert_dot(q13, s13, (int64_t)I + r, group, qx, dx, H);
     h[r] = orc_swiglu(g, u);
   }
   if (S13)
     for (int32_t r = 0; r < 2 * I; ++r) orc_block_sums(q13 + (int64_t)r * H, qx, H, S13 + (int64_t)r * (H / 32));
   orc_q8_0(h, I, qh, dh);
-  for (int32_t o = 0; o < H; ++o) out[o] = orc_dot_q4q8(q2 + (int64_t)o * I, s2[o], qh, dh, I);
+  for (int32_t o = 0; o < H; ++o) out[o] = expert_dot(q2, s2, o, group, qh, dh, I);
   if (S2)
     for (int32_t o = 0; o < H; ++o) orc_block_sums(q2 + (int64_t)o * I, qh, I, S2 + (int64_t)o * (I / 32));
 }
@@ -347,8 +421,10 @@ int orc_layer_forward(const orc_cfg* c, int32_t T, const float* x, const float* 
                       const int8_t* q13, const float* s13, const int8_t* q2, const float* s2,
                       const int8_t* sq13, const float* ss13, const int8_t* sq2, const float* ss2, float* y,
                       const orc_taps* taps) {
-  int32_t H = c->hidden, E = c->n_experts, K = c->top_k, I = c->inter, NS = c->n_shared;
+  int32_t H = c->hidden, E = c->n_experts, K = c->top_k, I = c->inter, NS = c->n_shared, G = c->group;
   if (H % 32 != 0 || I % 32 != 0 || T < 0 || NS < 0) return -2;
+  if (G < 0 || (G > 0 && (G % 32 != 0 || H % G != 0 || I % G != 0))) return -2;
+  const int64_t ns13 = (int64_t)2 * I * (G ? H / G : 1), ns2 = (int64_t)H * (G ? I / G : 1);
   int64_t R = (int64_t)T * K + (int64_t)NS * T;
   orc_taps own;
   memset(&own, 0, sizeof(own));
@@ -374,13 +450,13 @@ int orc_layer_forward(const orc_cfg* c, int32_t T, const float* x, const float* 
       for (int32_t k = 0; k < K; ++k) {
         int64_t row = (int64_t)t * K + k;
         int32_t e = ids[row];
-        orc_expert_token(H, I, q13 + e * m13, s13 + (int64_t)e * 2 * I, q2 + e * m2, s2 + (int64_t)e * H, qxt,
-                         dxt, h + row * I, qh + row * I, dh + row * (I / 32), eo + row * H, NULL, NULL);
+        orc_expert_token_g(H, I, G, q13 + e * m13, s13 + e * ns13, q2 + e * m2, s2 + e * ns2, qxt, dxt,
+                           h + row * I, qh + row * I, dh + row * (I / 32), eo + row * H, NULL, NULL);
       }
       for (int32_t s = 0; s < NS; ++s) {
         int64_t row = (int64_t)T * K + (int64_t)s * T + t;
-        orc_expert_token(H, I, sq13 + s * m13, ss13 + (int64_t)s * 2 * I, sq2 + s * m2, ss2 + (int64_t)s * H,
-                         qxt, dxt, h + row * I, qh + row * I, dh + row * (I / 32), eo + row * H, NULL, NULL);
+        orc_expert_token_g(H, I, G, sq13 + s * m13, ss13 + s * ns13, sq2 + s * m2, ss2 + s * ns2, qxt, dxt,
+                           h + row * I, qh + row * I, dh + row * (I / 32), eo + row * H, NULL, NULL);
       }
     }
     orc_combine(T, K, H, NS, eo, eo + (int64_t)T * K * H, w, y);

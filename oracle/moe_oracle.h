@@ -44,6 +44,7 @@ typedef struct {
   int32_t inter;      /* I */
   int32_t n_shared;
   float rsf;          /* routed_scaling_factor */
+  int32_t group;      /* 0: one weight scale per row; else one per group of this many elements along K */
 } orc_cfg;
 
 /* near-tie flag bits reported per token by orc_route */
@@ -54,6 +55,10 @@ typedef struct {
 /* int4 per-row symmetric quantization of fp32 rows [rows][cols]: q in [-7,7], scale per row */
 void orc_quant_int4_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, float* s);
 void orc_quant_int8_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, float* s);
+/* int4 with one scale per group of `group` elements along each row: s [rows][cols/group] */
+void orc_quant_int4_grouped(const float* w, int64_t rows, int64_t cols, int64_t group, int8_t* q, float* s);
+/* read group scales from the device layout [rows/64][ng][64] into [rows][ng] */
+void orc_unpack_scales_tiled64(const float* in, int64_t rows, int64_t ng, float* s);
 void orc_unpack_int8_tiled64(const uint8_t* in, int64_t rows, int64_t cols, int8_t* q);
 /* canonical nibble packing: byte j = (q[2j] & 15) | (q[2j+1] & 15) << 4, two's complement */
 void orc_pack_int4(const int8_t* q, int64_t n, uint8_t* out);
@@ -73,10 +78,16 @@ void orc_block_sums(const int8_t* a, const int8_t* b, int64_t n, int32_t* S);
 /* fp32 accumulation classes of a dot: block b is in class b mod 8 */
 #define ORC_DOT_CLASSES 8
 float orc_dot_q4q8(const int8_t* q4, float srow, const int8_t* q8, const float* d8, int64_t n);
+float orc_dot_q4q8_grouped(const int8_t* q4, const float* sg, int64_t group, const int8_t* q8, const float* d8,
+                           int64_t n);
 float orc_swiglu(float g, float u);
 void orc_expert_token(int32_t H, int32_t I, const int8_t* q13, const float* s13, const int8_t* q2,
                       const float* s2, const int8_t* qx, const float* dx, float* h, int8_t* qh, float* dh,
                       float* out, int32_t* S13, int32_t* S2);
+/* group = 0: per-row scales; else grouped scales s13 [2I][H/group], s2 [H][I/group] */
+void orc_expert_token_g(int32_t H, int32_t I, int32_t group, const int8_t* q13, const float* s13, const int8_t* q2,
+                        const float* s2, const int8_t* qx, const float* dx, float* h, int8_t* qh, float* dh,
+                        float* out, int32_t* S13, int32_t* S2);
 void orc_combine(int32_t T, int32_t K, int32_t H, int32_t n_shared, const float* e_routed,
                  const float* e_shared, const float* w, float* y);
 

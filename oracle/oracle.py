@@ -21,7 +21,7 @@ TIE_EXPERT, TIE_GROUP, TIE_ORDER = 1, 2, 4
 class OrcCfg(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32), ("rsf", ctypes.c_float)]
+                ("n_shared", ctypes.c_int32), ("rsf", ctypes.c_float), ("group", ctypes.c_int32)]
 
 
 class OrcTaps(ctypes.Structure):
@@ -39,6 +39,11 @@ def lib():
         L.orc_unpack_int4_tiled64.argtypes = [P, I64, I64, P]
         L.orc_quant_int8_rows.argtypes = [P, I64, I64, P, P]
         L.orc_unpack_int8_tiled64.argtypes = [P, I64, I64, P]
+        L.orc_quant_int4_grouped.argtypes = [P, I64, I64, I64, P, P]
+        L.orc_unpack_scales_tiled64.argtypes = [P, I64, I64, P]
+        L.orc_dot_q4q8_grouped.argtypes = [P, P, I64, P, P, I64]
+        L.orc_dot_q4q8_grouped.restype = F
+        L.orc_expert_token_g.argtypes = [I32, I32, I32] + [P] * 12
         L.orc_q8_0.argtypes = [P, I64, P, P]
         L.orc_router_logits.argtypes = [P, I32, I32, P, I32, P]
         L.orc_route.argtypes = [P, P, P, I32, P, P, P, P, P]
@@ -83,15 +88,16 @@ class Cfg:
     inter: int
     n_shared: int
     rsf: float
+    group: int = 0  # 0: one weight scale per row; else one per group of this many elements along K
 
     def c(self):
         return OrcCfg(self.hidden, self.n_experts, self.n_group, self.topk_group, self.top_k, self.inter,
-                      self.n_shared, self.rsf)
+                      self.n_shared, self.rsf, self.group)
 
     @staticmethod
-    def of(shape):
+    def of(shape, group: int = 0):
         return Cfg(shape.hidden, shape.n_experts, shape.n_group, shape.topk_group, shape.top_k, shape.inter,
-                   shape.n_shared, shape.rsf)
+                   shape.n_shared, shape.rsf, group)
 
 
 def quant_int4_rows(w):
@@ -117,6 +123,25 @@ def quant_int8_rows(w):
     sc = np.empty(rows, np.float32)
     lib().orc_quant_int8_rows(_p(w), rows, cols, _p(q), _p(sc))
     return q, sc
+
+
+def quant_int4_grouped(w, group):
+    """(codes [rows][cols] int8, scales [rows][cols/group] fp32)."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    assert group > 0 and cols % group == 0
+    q = np.empty((rows, cols), np.int8)
+    sc = np.empty((rows, cols // group), np.float32)
+    lib().orc_quant_int4_grouped(_p(w), rows, cols, group, _p(q), _p(sc))
+    return q, sc
+
+
+def unpack_scales_tiled64(b, rows, ng):
+    b = _c(b, np.float32).reshape(-1)
+    assert b.size == rows * ng
+    sc = np.empty((rows, ng), np.float32)
+    lib().orc_unpack_scales_tiled64(_p(b), rows, ng, _p(sc))
+    return sc
 
 
 def unpack_int8_tiled64(b, rows, cols):
@@ -211,11 +236,20 @@ def dot_q4q8(q4, srow, q8, d8):
     return np.float32(lib().orc_dot_q4q8(_p(q4), float(srow), _p(q8), _p(d8), q4.size))
 
 
+def dot_q4q8_grouped(q4, sg, group, q8, d8):
+    q4 = _c(q4, np.int8)
+    sg = _c(sg, np.float32)
+    q8 = _c(q8, np.int8)
+    d8 = _c(d8, np.float32)
+    return np.float32(lib().orc_dot_q4q8_grouped(_p(q4), _p(sg), group, _p(q8), _p(d8), q4.size))
+
+
 def swiglu(g, u):
     return np.float32(lib().orc_swiglu(float(g), float(u)))
 
 
 def expert_token(q13, s13, q2, s2, qx, dx, want_sums=False):
+    """s13 [2I] and s2 [H]: per-row scales; s13 [2I][H/G] and s2 [H][I/G]: grouped scales."""
     q13 = _c(q13, np.int8)
     s13 = _c(s13, np.float32)
     q2 = _c(q2, np.int8)
@@ -230,8 +264,12 @@ def expert_token(q13, s13, q2, s2, qx, dx, want_sums=False):
     out = np.empty(H, np.float32)
     S13 = np.empty((2 * I, H // 32), np.int32) if want_sums else None
     S2 = np.empty((H, I // 32), np.int32) if want_sums else None
-    lib().orc_expert_token(H, I, _p(q13), _p(s13), _p(q2), _p(s2), _p(qx), _p(dx), _p(h), _p(qh), _p(dh),
-                           _p(out), _p(S13), _p(S2))
+    group = 0
+    if s13.ndim == 2:
+        group = H // s13.shape[1]
+        assert s13.shape == (2 * I, H // group) and s2.shape == (H, I // group)
+    lib().orc_expert_token_g(H, I, group, _p(q13), _p(s13), _p(q2), _p(s2), _p(qx), _p(dx), _p(h), _p(qh), _p(dh),
+                             _p(out), _p(S13), _p(S2))
     r = dict(h=h, qh=qh, dh=dh, out=out)
     if want_sums:
         r.update(S13=S13, S2=S2)
@@ -251,7 +289,8 @@ def combine(e_routed, e_shared, w):
 
 @dataclass
 class LayerQ:
-    """A layer's weights in the oracle's unpacked form: int8 codes + fp32 row scales."""
+    """A layer's weights in the oracle's unpacked form: int8 codes + fp32 scales (per row, or per group with
+    Cfg.group > 0: s13 [E][2I][H/G], s2 [E][H][I/G])."""
     router_w: np.ndarray  # [E][H] fp32
     bias: np.ndarray      # [E] fp32
     q13: np.ndarray       # [E][2I][H] int8

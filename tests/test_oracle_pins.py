@@ -127,6 +127,60 @@ def test_int8_tiled64_layout_against_its_formula():
     assert np.array_equal(O.unpack_int8_tiled64(buf, rows, cols), q)
 
 
+def test_int4_grouped_golden():
+    g = HW["int4_grouped_hand"]
+    row = np.zeros((1, g["cols"]), np.float32)
+    for k, v in g["nonzero"].items():
+        row[0, int(k)] = v
+    q, s = O.quant_int4_grouped(row, g["group"])
+    assert s.shape == (1, g["cols"] // g["group"])
+    assert np.array_equal(s[0], np.array(g["expected_s"], np.float32))
+    want = np.zeros(g["cols"], np.int8)
+    for k, v in g["expected_q"].items():
+        want[int(k)] = v
+    assert np.array_equal(q[0], want)
+
+
+def test_int4_grouped_whole_row_group_is_per_row():
+    """One group spanning the row is exactly the per-row quantizer."""
+    w = synth.normal(64 * 256, 5, 61, 0.02).reshape(64, 256)
+    w[7] = 0.0
+    q, s = O.quant_int4_grouped(w, 256)
+    qr, sr = O.quant_int4_rows(w)
+    assert np.array_equal(q, qr) and np.array_equal(s[:, 0].view(np.uint32), sr.view(np.uint32))
+
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_int4_grouped_bounds(group):
+    """Every group reaches +-7 at its largest element, codes stay in [-7, 7], and the reconstruction error of
+    each element is at most half its group's step."""
+    w = synth.normal(64 * 512, 6, 62, 0.02).reshape(64, 512)
+    w[3, :group] = 0.0  # one all-zero group
+    q, s = O.quant_int4_grouped(w, group)
+    assert q.min() >= -7 and q.max() <= 7
+    ng = 512 // group
+    sg = np.repeat(s, group, axis=1).astype(np.float64)
+    err = np.abs(w.astype(np.float64) - sg * q)
+    assert np.all(err <= sg / 2 * (1 + 4 * U) + 1e-30)
+    amax = np.abs(w.reshape(64, ng, group)).max(2)
+    assert np.all(s == (amax / np.float32(7.0)).astype(np.float32))
+    big = np.abs(q.reshape(64, ng, group)).max(2)
+    assert np.all(big[amax > 0] == 7) and np.all(big[amax == 0] == 0)
+    # finer groups never lose to one scale per row on the row's worst element
+    _, sr = O.quant_int4_rows(w)
+    assert np.all(err.max(1) <= sr.astype(np.float64) / 2 * (1 + 4 * U))
+
+
+def test_scales_tiled64_golden():
+    g = HW["scales_tiled64"]
+    rows, ng = g["rows"], g["ng"]
+    buf = np.arange(rows * ng, dtype=np.float32)
+    sc = O.unpack_scales_tiled64(buf, rows, ng)
+    for r, gi, idx in g["points"]:
+        assert sc[r, gi] == idx
+    assert np.array_equal(np.sort(sc.ravel()), buf)  # a bijection
+
+
 def test_q8_0_golden_and_bounds():
     g = HW["q8_0_halfway"]
     blk = np.zeros(64, np.float32)
@@ -370,6 +424,61 @@ def test_dot_closed_form_constant():
         assert abs(float(v) - exact) <= gamma(n // 32 + 2) * abs(exact) + 1e-9
 
 
+def test_dot_grouped_golden():
+    g = HW["dot_grouped_hand"]
+    nb = g["n_blocks"]
+    q4 = np.zeros(32 * nb, np.int8)
+    q8 = np.zeros(32 * nb, np.int8)
+    for b in range(nb):
+        q4[32 * b] = 1
+        q8[32 * b] = g["block_sums"][b]
+    v = O.dot_q4q8_grouped(q4, np.array(g["sg"], np.float32), g["group"], q8, np.array(g["d8"], np.float32))
+    assert v == np.float32(g["expected"])
+
+
+@pytest.mark.parametrize("case", ["dot_order", "dot_classes", "dot_class_chain_order"])
+def test_dot_grouped_equal_power_of_two_scales_is_per_row_dot(case):
+    """Equal group scales that are a power of two scale every product exactly, so the grouped dot equals the
+    per-row dot with that row scale bit for bit; on the hand-worked class goldens this pins the class order."""
+    g = HW[case]
+    nb = g.get("n_blocks", 3)
+    q4 = np.zeros(32 * nb, np.int8)
+    q8 = np.zeros(32 * nb, np.int8)
+    for b in range(nb):
+        q4[32 * b] = 1
+        q8[32 * b] = g["block_sums"][b]
+    d8 = np.array(g["d8"], np.float32)
+    for sigma in (1.0, 0.25, 8.0):
+        for group in (32, 32 * nb):
+            sg = np.full(nb * 32 // group, sigma, np.float32)
+            v = O.dot_q4q8_grouped(q4, sg, group, q8, d8)
+            assert v == O.dot_q4q8(q4, sigma, q8, d8)
+            if sigma == 1.0 and g.get("srow") == 1.0:
+                assert v == np.float32(g["expected"])
+
+
+def test_dot_grouped_vs_dequantized_fp64_bound():
+    rng = np.random.default_rng(15)
+    for n, group in ((64, 32), (2048, 32), (2048, 128), (6144, 64)):
+        for _ in range(10):
+            q4 = rng.integers(-7, 8, n).astype(np.int8)
+            x = synth.normal(n, int(rng.integers(1 << 30)), 98, 1.0)
+            q8, d8 = O.q8_0(x)
+            sg = rng.uniform(0.001, 0.01, n // group).astype(np.float32)
+            v = O.dot_q4q8_grouped(q4, sg, group, q8, d8)
+            S = (q4.astype(np.int64) * q8.astype(np.int64)).reshape(-1, 32).sum(1)
+            sb = np.repeat(sg, group // 32).astype(np.float64)
+            terms = d8.astype(np.float64) * sb * S
+            exact = float(np.sum(terms))
+            bound = gamma(n // 32 + 2) * float(np.abs(terms).sum())
+            assert abs(float(v) - exact) <= bound
+            # the group of a block matters: scales taken per block index instead would be caught
+            if n // group > 1:
+                wrong = float(np.sum(d8.astype(np.float64) * np.resize(sg, n // 32).astype(np.float64) * S))
+                if abs(wrong - exact) > 10 * bound:
+                    assert abs(float(v) - wrong) > bound
+
+
 def test_swiglu_special_cases():
     assert O.swiglu(0.0, 5.0) == 0.0
     assert O.swiglu(30.0, 1.5) == np.float32(45.0)
@@ -490,6 +599,36 @@ def test_layer_batch_invariance_and_permutation(tiny):
         assert np.array_equal(O.layer_forward(cfg, x[t:t + 1], tiny, taps=False)[0], y[t])
     perm = np.array([3, 0, 7, 1, 6, 2, 5, 4])
     assert np.array_equal(O.layer_forward(cfg, x[perm], tiny, taps=False), y[perm])
+
+
+def test_layer_grouped_matches_per_pair_evaluation():
+    """The layer with grouped scales equals its pieces evaluated one (token, expert) pair at a time on sliced
+    arrays (router, Q8_0, grouped expert FFN, combine): pins the layer's per-expert scale strides."""
+    sh = synth.TINY
+    G = 64
+    cfg = O.Cfg.of(sh, group=G)
+    parts = []
+    for e in range(sh.n_experts):
+        parts.append(O.quant_int4_grouped(synth.expert_w13(sh, e), G) + O.quant_int4_grouped(synth.expert_w2(sh, e), G))
+    sh13, shs13 = O.quant_int4_grouped(synth.shared_w13(sh, 0), G)
+    sh2, shs2 = O.quant_int4_grouped(synth.shared_w2(sh, 0), G)
+    L = O.LayerQ(synth.router_weights(sh), synth.router_bias(sh), np.stack([p[0] for p in parts]),
+                 np.stack([p[1] for p in parts]), np.stack([p[2] for p in parts]), np.stack([p[3] for p in parts]),
+                 sh13[None], shs13[None], sh2[None], shs2[None])
+    x = synth.hidden_states(sh, 6, seed=12)
+    y, t = O.layer_forward(cfg, x, L)
+    ids, w, _ = O.route(cfg, O.router_logits(x, L.router_w), L.bias)
+    for tt in range(6):
+        qx, dx = O.q8_0(x[tt])
+        rows = [O.expert_token(*parts[e], qx, dx)["out"] for e in ids[tt]]
+        shr = O.expert_token(sh13, shs13, sh2, shs2, qx, dx)["out"]
+        for k in range(sh.top_k):
+            assert np.array_equal(t["e_out"][tt * sh.top_k + k], rows[k])
+        yy = O.combine(np.stack(rows)[None], shr[None, None], w[tt:tt + 1])[0]
+        assert np.array_equal(y[tt], yy)
+    # and differs from the per-row layer of the same weights
+    y_row = O.layer_forward(O.Cfg.of(sh), x, _tiny_layer(), taps=False)
+    assert not np.array_equal(y, y_row)
 
 
 def test_layer_zero_input_closed_form(tiny):
