@@ -62,9 +62,11 @@ void orc_quant_int8_rows(const float* w, int64_t rows, int64_t cols, int8_t* q, 
   }
 }
 
-/* Grouped int4 scales ("Show HN", benchmarks: grouped scales win back most of
- * the accuracy the int4 container loses; the pages fix neither the group size
- * nor the scale format). Reading: each row is cut into groups of `group`
+/* Grouped int4 scales ("Colibri: 25GB RAM을 탑재한 노트북에서 744B AI 모델
+ * 실행하기", section on the quality cost of int4: grouped scales win back most
+ * of the accuracy int4 loses; "Show HN", quality benchmarks and remaining
+ * measurements: grouped-scale quantization is the named next step). The pages
+ * fix neither the group size nor the scale format. Reading: each row is cut into groups of `group`
  * consecutive elements along K, and each group is quantized like a row of
  * orc_quant_int4_rows: s = amax/7, q = clamp(round-half-away(w * (1/s)),
  * -7, 7), s = 0 and q = 0 for an all-zero group. s is [rows][cols/group]. With
