@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--gemm-min", type=int, default=0)
     ap.add_argument("--weight-bits", type=int, default=4, choices=[4, 8],
                     help="expert weight codes: 4 (row-tiled int4, the default) or 8 (row-tiled int8)")
+    ap.add_argument("--group-size", type=int, default=0,
+                    help="int4 only: one weight scale per this many elements along K (0: one per row)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
@@ -116,7 +118,7 @@ def routing_stats(moe, cfg, layer, x_dev, ws, gemm_min):
 SAMPLE_TOKENS = 8  # tokens of the CPU sample (each distinct expert they route to is generated once)
 
 
-def cpu_baseline(shape, x, seconds, seed, weight_bits=4):
+def cpu_baseline(shape, x, seconds, seed, weight_bits=4, group_size=0):
     """The oracle as it stands, single-threaded, over the first SAMPLE_TOKENS tokens of the first batch: they are
     routed once and each distinct expert they need is generated once (outside the timing); then passes over
     them are timed until `seconds` of oracle time have been spent."""
@@ -134,6 +136,8 @@ def cpu_baseline(shape, x, seconds, seed, weight_bits=4):
             w13, w2 = synth.shared_w13(shape, e, seed, 0), synth.shared_w2(shape, e, seed, 0)
         else:
             w13, w2 = synth.expert_w13(shape, e, seed, 0), synth.expert_w2(shape, e, seed, 0)
+        if group_size:
+            return O.quant_int4_grouped(w13, group_size) + O.quant_int4_grouped(w2, group_size)
         quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
         return quant(w13) + quant(w2)
 
@@ -158,7 +162,8 @@ def cpu_baseline(shape, x, seconds, seed, weight_bits=4):
     return dict(value=done / t_oracle, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{done} tokens ({passes} pass(es) over the first {T} tokens of the first batch), each: "
                        f"fp64 router over "
-                       f"{shape.n_experts} experts, {shape.top_k} routed + 1 shared int{weight_bits}xint8 expert FFNs, combine; "
+                       f"{shape.n_experts} experts, {shape.top_k} routed + 1 shared int{weight_bits}xint8 expert FFNs"
+                       f"{f' (scales per {group_size})' if group_size else ''}, combine; "
                        f"{t_oracle:.1f} s of single-threaded oracle time (weight generation excluded)")
 
 
@@ -359,8 +364,8 @@ def main():
         calibrate()
         return
     if args.workload == "stack40":
-        if args.weight_bits != 4:
-            print("stack40 streams int4 experts only (--weight-bits 4).", file=sys.stderr)
+        if args.weight_bits != 4 or args.group_size:
+            print("stack40 streams int4 experts with row scales only.", file=sys.stderr)
             sys.exit(2)
         run_stack(args)
         return
@@ -373,9 +378,9 @@ def main():
     shape = synth.GLM
     T = tokens_of(args.workload)
     dev = torch.device("cuda:0")
-    WB = args.weight_bits
-    cfg = config_of(shape, args.gemm_min, WB)
-    layers = [GpuLayer(shape, seed=args.seed + c, weight_bits=WB) for c in range(args.copies)]
+    WB, GSZ = args.weight_bits, args.group_size
+    cfg = config_of(shape, args.gemm_min, WB, GSZ)
+    layers = [GpuLayer(shape, seed=args.seed + c, weight_bits=WB, group_size=GSZ) for c in range(args.copies)]
     n_in = args.warmup + args.steps
     xs_host = make_inputs(shape, args.workload, min(n_in, 64), args.seed)
     xs = [torch.from_numpy(x).to(dev) for x in xs_host]
@@ -397,7 +402,7 @@ def main():
     # timed region records HIP events around it only (on the stream it runs on)
     kname = "gateup_mfma" if args.workload == "prefill" else "gateup_gemv"
     # counter summaries are per kernel, workload and weight width
-    pmc_workload = args.workload if WB == 4 else f"{args.workload}_int8w"
+    pmc_workload = args.workload + ("_int8w" if WB == 8 else "") + (f"_g{GSZ}" if GSZ else "")
     kidx = moe.STAGES.index(kname)
 
     def timed(stages):
@@ -422,8 +427,9 @@ def main():
     ms_staged, prof_all = timed(None)
 
     H, I, E = shape.hidden, shape.inter, shape.n_experts
-    w13_bytes = 2 * I * H * WB // 8 + 2 * I * 4  # gate+up codes + fp32 row scales
-    w2_bytes = H * I * WB // 8 + H * 4
+    # gate+up codes + fp32 scales (one per row, or one per group of GSZ along K)
+    w13_bytes = 2 * I * H * WB // 8 + (2 * I * (H // GSZ) if GSZ else 2 * I) * 4
+    w2_bytes = H * I * WB // 8 + (H * (I // GSZ) if GSZ else H) * 4
     U = np.array([s["U"] for s in stats], np.float64)
     layer_bytes = (E * H * 4 + E * 4) + (U + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 4
     stage_ms = prof_all.mean(0)
@@ -463,7 +469,7 @@ def main():
         "config": {"workload": f"glm5.2-moe-layer {args.workload}", "tokens": T, "hidden": H, "experts": E,
                    "groups": shape.n_group, "topk_group": shape.topk_group, "top_k": shape.top_k, "inter": I,
                    "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or DEFAULT_GEMM_MIN,
-                   "layer_copies": args.copies, "weight_bits": WB},
+                   "layer_copies": args.copies, "weight_bits": WB, "group_size": GSZ},
         "layer_hbm_gbs": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9), 1),
         "layer_hbm_frac": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9) / HBM_PEAK_GBS, 4),
         "unique_experts_mean": round(float(U.mean()), 2),
@@ -480,7 +486,7 @@ def main():
     out["layer_int8_mfma_frac"] = round(ops_layer / (ms_step / 1e3) / (INT8_PEAK_TOPS * 1e12), 4)
     out["combined_roofline_frac"] = round(float(np.mean(np.maximum(t_mem, t_mfma))) / (ms_step / 1e3), 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB)
+        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB, GSZ)
     print(json.dumps(out), flush=True)
 
 

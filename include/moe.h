@@ -23,6 +23,9 @@
  *  [D2] same page, implemented features: int8 and packed int4 weights with
  *      per-row scales; the MTP head must be int8 (int4 drafts are almost
  *      never accepted).
+ *  [D3] "Colibri: 25GB RAM을 탑재한 노트북에서 744B AI 모델 실행하기", section on
+ *      the quality cost of int4: grouped scales recover most of the accuracy
+ *      int4 loses (group size and scale format not given).
  *
  * Conventions for every call:
  *  - All array arguments are DEVICE pointers owned by the caller unless marked
@@ -57,6 +60,13 @@
  * byte 8g + i, element 8g + 2i + 1 at byte 8g + 4 + i). Byte j of block b of
  * row r is at ((r / 64) * (K / 32) + b) * 2048 + (r % 64) * 32 + j. One fp32
  * scale per row. moe_quantize_int8() produces this layout.
+ *
+ * Grouped scales (int4 only, [D3]): with group_size G > 0 each row carries one
+ * fp32 scale per G consecutive elements instead of one per row, stored tiled
+ * like the codes: for each tile of 64 rows and each group, the 64 rows'
+ * scales are adjacent; the scale of row r, group g is at index
+ *     ((r / 64) * (K / G) + g) * 64 + r % 64.
+ * moe_quantize_int4_grouped() produces codes and scales.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -99,6 +109,10 @@ typedef struct moe_config {
                               Never changes results. */
   int32_t weight_bits;   /* expert weight codes: 4 (row-tiled int4; <= 0 selects it) or 8
                             (row-tiled int8, [D2]); routed and shared experts alike */
+  int32_t group_size;    /* <= 0: one weight scale per row. Else int4 only: one scale per group of
+                            group_size elements along K [D3]; a power of two times 32 that divides
+                            H and I. The dot then scales block b's exact sum by
+                            fp32(d_b * s_group(b)) in its class chain, with no row scale. */
 } moe_config;
 
 /* A layer's weights. Routed arrays hold E experts back to back; shared arrays
@@ -106,9 +120,9 @@ typedef struct moe_config {
  *   router_w [E][H] fp32 row-major;  router_bias [E] fp32 (selection only)
  *   w13      per expert: row-tiled int4 of [2I][H] (gate rows 0..I-1, up rows I..2I-1), I*H bytes
  *            (int8: 2*I*H bytes)
- *   s13      per expert: [2I] fp32 row scales
+ *   s13      per expert: [2I] fp32 row scales (grouped: 2I*H/G tiled group scales)
  *   w2       per expert: row-tiled int4 of [H][I] (down projection), H*I/2 bytes (int8: H*I bytes)
- *   s2       per expert: [H] fp32 row scales                                      */
+ *   s2       per expert: [H] fp32 row scales (grouped: H*I/G tiled group scales)   */
 typedef struct moe_layer_weights {
   const float* router_w;
   const float* router_bias;
@@ -162,6 +176,13 @@ size_t moe_workspace_bytes(const moe_config* cfg, int32_t max_tokens);
  * all-zero row. rows % 64 == 0, cols % 32 == 0. */
 int32_t moe_quantize_int4(const float* w, int32_t rows, int32_t cols, uint8_t* packed, float* scales,
                           hipStream_t stream);
+
+/* Converter: fp32 rows w [rows][cols] -> row-tiled int4 (rows*cols/2 bytes)
+ * + tiled group scales (rows*cols/group fp32) [D3]: each group of `group`
+ * elements along a row is quantized like a row of moe_quantize_int4.
+ * rows % 64 == 0, group a power of two times 32, cols % group == 0. */
+int32_t moe_quantize_int4_grouped(const float* w, int32_t rows, int32_t cols, int32_t group, uint8_t* packed,
+                                  float* scales, hipStream_t stream);
 
 /* Converter: fp32 rows w [rows][cols] -> row-tiled int8 (rows*cols bytes) +
  * per-row fp32 scales [D2]: s = amax/127, q = round-half-away(w * (1/s))

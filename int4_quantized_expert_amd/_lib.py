@@ -37,7 +37,7 @@ P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 class moe_config(ctypes.Structure):
     _fields_ = [("hidden", I32), ("n_experts", I32), ("n_group", I32), ("topk_group", I32), ("top_k", I32),
                 ("inter", I32), ("n_shared", I32), ("routed_scaling_factor", F32), ("gemm_min_tokens", I32),
-                ("weight_bits", I32)]
+                ("weight_bits", I32), ("group_size", I32)]
 
 
 class moe_layer_weights(ctypes.Structure):
@@ -73,6 +73,7 @@ _sig("moe_last_hip_error", I32, [])
 _sig("moe_workspace_bytes", SZ, [P, I32])
 _sig("moe_quantize_int4", I32, [P, I32, I32, P, P, P])
 _sig("moe_quantize_int8", I32, [P, I32, I32, P, P, P])
+_sig("moe_quantize_int4_grouped", I32, [P, I32, I32, I32, P, P, P])
 _sig("moe_quantize_q8_0", I32, [P, I64, P, P, P])
 _sig("moe_router", I32, [P, P, I32, P, P, P, P, P, P, SZ, P])
 _sig("moe_dispatch", I32, [P, P, I32, P, P, P, P, P, P, P, SZ, P])
@@ -91,7 +92,7 @@ _sig("moe_membench_read", I32, [P, SZ, I32, I32, P, P])
 _sig("moe_membench_copy", I32, [P, P, SZ, I32, P])
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_workspace_bytes", "moe_quantize_int4",
-            "moe_quantize_int8", "moe_quantize_q8_0", "moe_router", "moe_dispatch", "moe_layer_forward",
+            "moe_quantize_int8", "moe_quantize_int4_grouped", "moe_quantize_q8_0", "moe_router", "moe_dispatch", "moe_layer_forward",
             "moe_expert_cache_create",
             "moe_expert_cache_forward", "moe_expert_cache_stats", "moe_expert_cache_usage", "moe_expert_cache_set_usage",
             "moe_expert_cache_pin_hottest", "moe_expert_cache_destroy", "moe_prof_enable",
@@ -140,10 +141,12 @@ class Config:
     routed_scaling_factor: float
     gemm_min_tokens: int = 0
     weight_bits: int = 4
+    group_size: int = 0
 
     def c(self):
         return moe_config(self.hidden, self.n_experts, self.n_group, self.topk_group, self.top_k, self.inter,
-                          self.n_shared, self.routed_scaling_factor, self.gemm_min_tokens, self.weight_bits)
+                          self.n_shared, self.routed_scaling_factor, self.gemm_min_tokens, self.weight_bits,
+                          self.group_size)
 
 
 def moe_version():
@@ -165,6 +168,13 @@ def moe_quantize_int8(w, codes, scales, stream=None):
     rows, cols = w.shape
     return _check("moe_quantize_int8",
                   _lib.moe_quantize_int8(_ptr(w), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_quantize_int4_grouped(w, group, packed, scales, stream=None):
+    rows, cols = w.shape
+    return _check("moe_quantize_int4_grouped",
+                  _lib.moe_quantize_int4_grouped(_ptr(w), rows, cols, int(group), _ptr(packed), _ptr(scales),
+                                                 _stream(stream)))
 
 
 def moe_quantize_q8_0(x, q, d, stream=None):

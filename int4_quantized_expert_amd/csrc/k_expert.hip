@@ -263,7 +263,11 @@ __device__ __forceinline__ void stage_store(const Staged<N>& st, int K, int8_t* 
   __syncthreads();
 }
 
-template <int N, int PF, bool TAP, int W>
+// GS: grouped weight scales. Each lane (one row) then also streams its row's
+// scale of every block's group beside the weights, and a block's activation
+// scale is multiplied by it before the block's fused multiply-add; there is no
+// row scale at the end.
+template <int N, int PF, bool TAP, int W, bool GS>
 __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
                                                 const uint8_t* w13, const float* s13, int tile, char* lds) {
   const int H = a.H, I = a.I, nb = H / 32;
@@ -290,12 +294,21 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
   const uint8_t* gcls = w13 + tbw_off<W>(tile, min(w, nb - 1), nb) + (size_t)lane * (4 * W);
   const uint8_t* ucls = w13 + tbw_off<W>(I / 64 + tile, min(w, nb - 1), nb) + (size_t)lane * (4 * W);
   constexpr size_t step = kGW * kTileBlock<W>;  // class stride
+  const int gsh = GS ? a.gshift : 0, ngs = GS ? nb >> gsh : 0;
+  const float* gsc = s13 + (size_t)tile * ngs * 64 + lane;             // group scales of the gate row
+  const float* usc = s13 + (size_t)(I / 64 + tile) * ngs * 64 + lane;  // and of the up row
   WBlk<W> bg[PF], bu[PF];
+  float sgq[PF], suq[PF];
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
     const size_t off = (size_t)min(kk, last) * step;
     load_wblk<W>(bg[kk], gcls + off);
     load_wblk<W>(bu[kk], ucls + off);
+    if constexpr (GS) {
+      const size_t so = (size_t)((min(w, nb - 1) + kGW * min(kk, last)) >> gsh) * 64;
+      sgq[kk] = gsc[so];
+      suq[kk] = usc[so];
+    }
   }
   stage_store<N>(st, H, xs, xd);
   int tap_i = -1;
@@ -316,9 +329,15 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
         WPrep<W> pg, pu;
         prep_wblk(bg[kk], pg);
         prep_wblk(bu[kk], pu);
+        const float cg = GS ? sgq[kk] : 0.0f, cu = GS ? suq[kk] : 0.0f;
         const size_t noff = (size_t)min(j + PF, ncls - 1) * step;  // past the end: a repeat (cache hit)
         load_wblk<W>(bg[kk], gcls + noff);
         load_wblk<W>(bu[kk], ucls + noff);
+        if constexpr (GS) {
+          const size_t so = (size_t)((w + kGW * min(j + PF, ncls - 1)) >> gsh) * 64;
+          sgq[kk] = gsc[so];
+          suq[kk] = usc[so];
+        }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
           const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)blk * 32);
@@ -327,8 +346,8 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
           const int Sg = wdot(pg, xa, xb);
           const int Su = wdot(pu, xa, xb);
           if (live) {
-            ag[i] = fmaf(d, (float)Sg, ag[i]);
-            au[i] = fmaf(d, (float)Su, au[i]);
+            ag[i] = fmaf(GS ? __fmul_rn(d, cg) : d, (float)Sg, ag[i]);
+            au[i] = fmaf(GS ? __fmul_rn(d, cu) : d, (float)Su, au[i]);
             if (TAP && i == tap_i) {
               a.t_gu_sums[(size_t)r * nb + blk] = Sg;
               a.t_gu_sums[(size_t)(I + r) * nb + blk] = Su;
@@ -355,11 +374,15 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
       g = __fadd_rn(g, part[(c * 2 * N + 2 * w) * 64 + lane]);
       u = __fadd_rn(u, part[(c * 2 * N + 2 * w + 1) * 64 + lane]);
     }
-    store_h_lanes(a, k, k.p0 + c0 + w, r, lane, __fmul_rn(s13[r], g), __fmul_rn(s13[I + r], u));
+    if (!GS) {
+      g = __fmul_rn(s13[r], g);
+      u = __fmul_rn(s13[I + r], u);
+    }
+    store_h_lanes(a, k, k.p0 + c0 + w, r, lane, g, u);
   }
 }
 
-template <int N, int PF, bool TAP, int W>
+template <int N, int PF, bool TAP, int W, bool GS>
 __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
                                               const uint8_t* w2, const float* s2, int tile, char* lds) {
   const int H = a.H, I = a.I, nbi = I / 32;
@@ -383,9 +406,15 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
   const int last = max(ncls - 1, 0);
   const uint8_t* wcls = w2 + tbw_off<W>(tile, min(w, nbi - 1), nbi) + (size_t)lane * (4 * W);
   constexpr size_t step = kGW * kTileBlock<W>;
+  const int gsh = GS ? a.gshift : 0, ngs = GS ? nbi >> gsh : 0;
+  const float* osc = s2 + (size_t)tile * ngs * 64 + lane;  // group scales of the output row
   WBlk<W> bw[PF];
+  float soq[PF];
 #pragma unroll
-  for (int kk = 0; kk < PF; ++kk) load_wblk<W>(bw[kk], wcls + (size_t)min(kk, last) * step);
+  for (int kk = 0; kk < PF; ++kk) {
+    load_wblk<W>(bw[kk], wcls + (size_t)min(kk, last) * step);
+    if constexpr (GS) soq[kk] = osc[(size_t)((min(w, nbi - 1) + kGW * min(kk, last)) >> gsh) * 64];
+  }
   stage_store<N>(st, I, hs, hd);
   int tap_i = -1;
   if (TAP) {
@@ -404,13 +433,16 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
         const int blk = w + kGW * min(j, ncls - 1);
         WPrep<W> pw;
         prep_wblk(bw[kk], pw);
+        const float co = GS ? soq[kk] : 0.0f;
         load_wblk<W>(bw[kk], wcls + (size_t)min(j + PF, ncls - 1) * step);
+        if constexpr (GS) soq[kk] = osc[(size_t)((w + kGW * min(j + PF, ncls - 1)) >> gsh) * 64];
 #pragma unroll
         for (int i = 0; i < N; ++i) {
           const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)blk * 32);
           const int S = wdot(pw, hb4[0], hb4[1]);
           if (live) {
-            acc[i] = fmaf(hd[i * nbi + blk], (float)S, acc[i]);
+            const float d = hd[i * nbi + blk];
+            acc[i] = fmaf(GS ? __fmul_rn(d, co) : d, (float)S, acc[i]);
             if (TAP && i == tap_i) a.t_dn_sums[(size_t)o * nbi + blk] = S;
           }
         }
@@ -427,7 +459,7 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
     float e = 0.0f;
 #pragma unroll
     for (int c = 0; c < kGW; ++c) e = __fadd_rn(e, part[(c * N + w) * 64 + lane]);
-    e = __fmul_rn(s2[o], e);
+    if (!GS) e = __fmul_rn(s2[o], e);
     const int p = k.p0 + c0 + w;
     a.eout[(size_t)p * H + o] = e;
     if (a.t_eout) a.t_eout[(size_t)slot_of(a, k, p) * H + o] = e;
@@ -547,6 +579,36 @@ __device__ __forceinline__ int true_sum(int s) {
   return W == 4 ? s >> 4 : s;
 }
 
+// Grouped weight scales on the MFMA path. Each lane streams one scale per
+// block (gate row lane for lanes 0-31, up row lane-32 for lanes 32-63; every
+// lane of the down tile its row lane%32) in the prefetch ring; at use the
+// wavefront passes them through a 64-float LDS slot (scales_put), and each
+// lane reads the 16 rows it holds in the MFMA result (scales_get): rows
+// 8q + 4*half + j, j = 0..3, one float4 per q. Two slots alternate, and the
+// wavefront-level fence in scales_put orders a slot's write after the reads
+// of its previous use and before its new reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void scales_put(float* slot, float mine, int lane) {
+  slot[lane] = mine;
+  wave_sync();
+}
+
+__device__ __forceinline__ void scales_get(const float* slot, int half, float (&s16)[16], int base) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(slot + base + 8 * q + 4 * half);
+    s16[4 * q + 0] = v.x;
+    s16[4 * q + 1] = v.y;
+    s16[4 * q + 2] = v.z;
+    s16[4 * q + 3] = v.w;
+  }
+}
+
 template <int NTT, int W>
 __device__ __forceinline__ void load_gu_block(__amdgpu_buffer_rsrc_t gr, __amdgpu_buffer_rsrc_t ur,
                                               __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t dr, int blk,
@@ -570,9 +632,9 @@ __device__ __forceinline__ void load_dn_block(__amdgpu_buffer_rsrc_t wr, __amdgp
 // each), NTT x 32 tokens. t32 = index of the 32-row block. Columns past the
 // bucket's end compute on the last token (a valid address) and are never
 // stored; each column's results depend on that column alone.
-template <int NTT, int PF, bool TAP, int W>
+template <int NTT, int PF, bool TAP, int W, bool GS>
 __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w13, const float* s13,
-                                 int t32, int lane, MfmaTotals<NTT, 2>& T) {
+                                 int t32, int lane, MfmaTotals<NTT, 2>& T, float* scl) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nb = H / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -608,10 +670,16 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   ARaw<W> rg[PF], ru[PF];
   v4i rb[PF][NTT];
   float rd[PF][NTT];
+  // grouped scales: lanes 0-31 the gate rows', lanes 32-63 the up rows' (see scales_via_lds)
+  const int gsh = GS ? a.gshift : 0, ngs = GS ? nb >> gsh : 0;
+  const auto sr = buf_rsrc(s13);
+  const uint32_t soff = (uint32_t)(((half ? I / 64 + tile : tile) * ngs * 64 + s * 32 + col) * 4);
+  float rs[PF];
   int fetch = 0;  // next block to load
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
     load_gu_block<NTT, W>(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
+    if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
     fetch = class_major_next(fetch, nb);
   }
   int blk = 0;  // block being consumed
@@ -619,14 +687,22 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
       const v4i Ag = a_operand<W>(rg[kk]), Au = a_operand<W>(ru[kk]);
+      float gs16[16], us16[16];
+      if constexpr (GS) {
+        float* slot = scl + 64 * (kk & 1);
+        scales_put(slot, rs[kk], lane);
+        scales_get(slot, half, gs16, 0);
+        scales_get(slot, half, us16, 32);
+      }
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, rb[kk][tt], zero, 0, 0, 0);  // (16 x) block sums
         const v16i Su = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, rb[kk][tt], zero, 0, 0, 0);
+        const float d = rd[kk][tt];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(rd[kk][tt], (float)Sg[i], ag[tt][i]);
+        for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(GS ? __fmul_rn(d, gs16[i]) : d, (float)Sg[i], ag[tt][i]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) au[tt][i] = fmaf(rd[kk][tt], (float)Su[i], au[tt][i]);
+        for (int i = 0; i < 16; ++i) au[tt][i] = fmaf(GS ? __fmul_rn(d, us16[i]) : d, (float)Su[i], au[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -637,6 +713,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
       }
       // refill the slot just consumed
       load_gu_block<NTT, W>(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
+      if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
       fetch = class_major_next(fetch, nb);
       if (blk + kDotClasses >= nb) {  // blk ends its class
 #pragma unroll
@@ -648,11 +725,11 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
       blk = class_major_next(blk, nb);
     }
   }
-  float sg[16], su[16];
+  float sg[16], su[16];  // row scales (one scale per row only)
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    sg[i] = s13[r0 + out_row(i, lane)];
-    su[i] = s13[I + r0 + out_row(i, lane)];
+    sg[i] = GS ? 1.0f : s13[r0 + out_row(i, lane)];
+    su[i] = GS ? 1.0f : s13[I + r0 + out_row(i, lane)];
   }
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
@@ -662,7 +739,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      h[i] = swiglu_f(__fmul_rn(sg[i], tg[i]), __fmul_rn(su[i], tu[i]));
+      h[i] = GS ? swiglu_f(tg[i], tu[i]) : swiglu_f(__fmul_rn(sg[i], tg[i]), __fmul_rn(su[i], tu[i]));
       amax = fmaxf(amax, fabsf(h[i]));
       __builtin_amdgcn_sched_barrier(0);  // one fp64 exp at a time keeps the epilogue's registers low
     }
@@ -693,9 +770,9 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
 
 // 32 output rows per wavefront, NTT x 32 positions. t32 = index of the
 // 32-row block. Columns past the bucket's end as in the gate/up tile.
-template <int NTT, int PF, bool TAP, int W>
+template <int NTT, int PF, bool TAP, int W, bool GS>
 __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w2, const float* s2,
-                               int t32, int lane, MfmaTotals<NTT, 1>& T) {
+                               int t32, int lane, MfmaTotals<NTT, 1>& T, float* scl) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nbi = I / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -728,10 +805,15 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   ARaw<W> ra[PF];
   v4i rb[PF][NTT];
   float rd[PF][NTT];
+  const int gsh = GS ? a.gshift : 0, ngs = GS ? nbi >> gsh : 0;
+  const auto sr = buf_rsrc(s2);
+  const uint32_t soff = (uint32_t)((tile * ngs * 64 + s * 32 + col) * 4);  // row r0 + lane % 32
+  float rs[PF];
   int fetch = 0;
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
     load_dn_block<NTT, W>(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
+    if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
     fetch = class_major_next(fetch, nbi);
   }
   int blk = 0;
@@ -739,17 +821,25 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
       const v4i A = a_operand<W>(ra[kk]);
+      float os16[16];
+      if constexpr (GS) {
+        float* slot = scl + 64 * (kk & 1);
+        scales_put(slot, rs[kk], lane);
+        scales_get(slot, half, os16, 0);
+      }
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, rb[kk][tt], zero, 0, 0, 0);  // 16 x block sums
+        const float d = rd[kk][tt];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(rd[kk][tt], (float)S[i], acc[tt][i]);
+        for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(GS ? __fmul_rn(d, os16[i]) : d, (float)S[i], acc[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = true_sum<W>(S[i]);
         }
       }
       load_dn_block<NTT, W>(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
+      if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
       fetch = class_major_next(fetch, nbi);
       if (blk + kDotClasses >= nbi) {
 #pragma unroll
@@ -758,9 +848,9 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
       blk = class_major_next(blk, nbi);
     }
   }
-  float so[16];
+  float so[16];  // row scales (one scale per row only)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) so[i] = s2[r0 + out_row(i, lane)];
+  for (int i = 0; i < 16; ++i) so[i] = GS ? 1.0f : s2[r0 + out_row(i, lane)];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
     if (!valid[tt]) continue;
@@ -772,10 +862,10 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       float4 v;
-      v.x = __fmul_rn(so[4 * g + 0], tot[4 * g + 0]);
-      v.y = __fmul_rn(so[4 * g + 1], tot[4 * g + 1]);
-      v.z = __fmul_rn(so[4 * g + 2], tot[4 * g + 2]);
-      v.w = __fmul_rn(so[4 * g + 3], tot[4 * g + 3]);
+      v.x = GS ? tot[4 * g + 0] : __fmul_rn(so[4 * g + 0], tot[4 * g + 0]);
+      v.y = GS ? tot[4 * g + 1] : __fmul_rn(so[4 * g + 1], tot[4 * g + 1]);
+      v.z = GS ? tot[4 * g + 2] : __fmul_rn(so[4 * g + 2], tot[4 * g + 2]);
+      v.w = GS ? tot[4 * g + 3] : __fmul_rn(so[4 * g + 3], tot[4 * g + 3]);
       const int mm = 8 * g + 4 * half;
       *reinterpret_cast<float4*>(orow + mm) = v;
       if (trow) *reinterpret_cast<float4*>(trow + mm) = v;
@@ -823,8 +913,9 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
 // 32-token tiles, 2 for 64 (the depth must divide the block count; 2 always does).
 
 // PF: blocks in flight per wavefront (chosen by the host).
-// W: weight code width (4 or 8), chosen by the host from the configuration.
-template <int PF, bool TAP, int W>
+// W: weight code width (4 or 8); GS: grouped weight scales (int4 only). Both
+// chosen by the host from the configuration.
+template <int PF, bool TAP, int W, bool GS>
 __global__ __launch_bounds__(kGemvThreads) void k_gateup_gemv(ExpertArgs a) {
   extern __shared__ char gemv_lds[];
   const int li = blockIdx.y, tile = blockIdx.x;
@@ -832,14 +923,14 @@ __global__ __launch_bounds__(kGemvThreads) void k_gateup_gemv(ExpertArgs a) {
   const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
   const int c0 = cptr(a.list)[2 * li + 1];
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
-  const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
+  const float* s13 = expert_s13(a.wv, k.ex, a.E, s13_count(a.H, a.I, GS ? a.gshift : -1));
   const int nn = min(kGemvMaxN, k.n - c0);
-  if (nn == 1) gemv_gateup_run<1, PF, TAP, W>(a, k, c0, nn, w13, s13, tile, gemv_lds);
-  else if (nn == 2) gemv_gateup_run<2, PF, TAP, W>(a, k, c0, nn, w13, s13, tile, gemv_lds);
-  else gemv_gateup_run<kGemvMaxN, PF, TAP, W>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  if (nn == 1) gemv_gateup_run<1, PF, TAP, W, GS>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  else if (nn == 2) gemv_gateup_run<2, PF, TAP, W, GS>(a, k, c0, nn, w13, s13, tile, gemv_lds);
+  else gemv_gateup_run<kGemvMaxN, PF, TAP, W, GS>(a, k, c0, nn, w13, s13, tile, gemv_lds);
 }
 
-template <int PF, bool TAP, int W>
+template <int PF, bool TAP, int W, bool GS>
 __global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
   extern __shared__ char gemv_lds[];
   const int li = blockIdx.y, tile = blockIdx.x;
@@ -847,14 +938,14 @@ __global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
   const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
   const int c0 = cptr(a.list)[2 * li + 1];
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
-  const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
+  const float* s2 = expert_s2(a.wv, k.ex, a.E, s2_count(a.H, a.I, GS ? a.gshift : -1));
   const int nn = min(kGemvMaxN, k.n - c0);
-  if (nn == 1) gemv_down_run<1, PF, TAP, W>(a, k, c0, nn, w2, s2, tile, gemv_lds);
-  else if (nn == 2) gemv_down_run<2, PF, TAP, W>(a, k, c0, nn, w2, s2, tile, gemv_lds);
-  else gemv_down_run<kGemvMaxN, PF, TAP, W>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  if (nn == 1) gemv_down_run<1, PF, TAP, W, GS>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else if (nn == 2) gemv_down_run<2, PF, TAP, W, GS>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else gemv_down_run<kGemvMaxN, PF, TAP, W, GS>(a, k, c0, nn, w2, s2, tile, gemv_lds);
 }
 
-template <int NTT, int MPF, bool TAP, int W>
+template <int NTT, int MPF, bool TAP, int W, bool GS>
 __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
                                                     const int32_t* __restrict__ n_tiles) {
   const int y = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
@@ -862,15 +953,21 @@ __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t*
   const Bucket k = load_bucket(a, cptr(tiles)[2 * y]);
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
-  const float* s13 = expert_s13(a.wv, k.ex, a.E, 2 * a.I);
+  const float* s13 = expert_s13(a.wv, k.ex, a.E, s13_count(a.H, a.I, GS ? a.gshift : -1));
   __shared__ MfmaTotals<NTT, 2> totals;
+  float* sc = nullptr;  // two 64-float slots for the group scales (GS only: no LDS otherwise)
+  if constexpr (GS) {
+    __shared__ float scl[2 * 64];
+    sc = scl;
+  }
   if (NTT == 2 && k.n - t0 <= 32)  // a bucket's last tile with one 32-token half: skip the empty one
-    mfma_gateup_tile<1, MPF, TAP, W>(a, k, t0, w13, s13, tile, lane, reinterpret_cast<MfmaTotals<1, 2>&>(totals));
+    mfma_gateup_tile<1, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane,
+                                         reinterpret_cast<MfmaTotals<1, 2>&>(totals), sc);
   else
-    mfma_gateup_tile<NTT, MPF, TAP, W>(a, k, t0, w13, s13, tile, lane, totals);
+    mfma_gateup_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane, totals, sc);
 }
 
-template <int NTT, int MPF, bool TAP, int W>
+template <int NTT, int MPF, bool TAP, int W, bool GS>
 __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
                                                   const int32_t* __restrict__ n_tiles) {
   const int y = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
@@ -878,14 +975,19 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
   const Bucket k = load_bucket(a, cptr(tiles)[2 * y]);
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
-  const float* s2 = expert_s2(a.wv, k.ex, a.E, a.H);
+  const float* s2 = expert_s2(a.wv, k.ex, a.E, s2_count(a.H, a.I, GS ? a.gshift : -1));
   __shared__ MfmaTotals<NTT, 1> totals;
+  float* sc = nullptr;
+  if constexpr (GS) {
+    __shared__ float scl[2 * 64];
+    sc = scl;
+  }
   if (NTT == 2 && k.n - t0 <= 32)
-    mfma_down_tile<1, MPF, TAP, W>(a, k, t0, w2, s2, tile, lane, reinterpret_cast<MfmaTotals<1, 1>&>(totals));
+    mfma_down_tile<1, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, reinterpret_cast<MfmaTotals<1, 1>&>(totals),
+                                       sc);
   else
-    mfma_down_tile<NTT, MPF, TAP, W>(a, k, t0, w2, s2, tile, lane, totals);
+    mfma_down_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, totals, sc);
 }
-
 
 // Blocks in flight per wavefront: about 4 KB of weights per wavefront when
 // many buckets stream at once (2 blocks of the two gate/up streams, 4 of the
@@ -899,15 +1001,19 @@ static int gemv_pf(int nblocks, int want) {
   return want;
 }
 
+// Weight formats: int4 with row scales, int4 with grouped scales, int8 with row scales.
 template <int PF>
 static void gateup_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
   if (a.wbits == 8) {
-    if (tap) k_gateup_gemv<PF, true, 8><<<g, kGemvThreads, lds, st>>>(a);
-    else k_gateup_gemv<PF, false, 8><<<g, kGemvThreads, lds, st>>>(a);
+    if (tap) k_gateup_gemv<PF, true, 8, false><<<g, kGemvThreads, lds, st>>>(a);
+    else k_gateup_gemv<PF, false, 8, false><<<g, kGemvThreads, lds, st>>>(a);
+  } else if (a.gshift >= 0) {
+    if (tap) k_gateup_gemv<PF, true, 4, true><<<g, kGemvThreads, lds, st>>>(a);
+    else k_gateup_gemv<PF, false, 4, true><<<g, kGemvThreads, lds, st>>>(a);
   } else {
-    if (tap) k_gateup_gemv<PF, true, 4><<<g, kGemvThreads, lds, st>>>(a);
-    else k_gateup_gemv<PF, false, 4><<<g, kGemvThreads, lds, st>>>(a);
+    if (tap) k_gateup_gemv<PF, true, 4, false><<<g, kGemvThreads, lds, st>>>(a);
+    else k_gateup_gemv<PF, false, 4, false><<<g, kGemvThreads, lds, st>>>(a);
   }
 }
 
@@ -915,11 +1021,14 @@ template <int PF>
 static void down_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
   if (a.wbits == 8) {
-    if (tap) k_down_gemv<PF, true, 8><<<g, kGemvThreads, lds, st>>>(a);
-    else k_down_gemv<PF, false, 8><<<g, kGemvThreads, lds, st>>>(a);
+    if (tap) k_down_gemv<PF, true, 8, false><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 8, false><<<g, kGemvThreads, lds, st>>>(a);
+  } else if (a.gshift >= 0) {
+    if (tap) k_down_gemv<PF, true, 4, true><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 4, true><<<g, kGemvThreads, lds, st>>>(a);
   } else {
-    if (tap) k_down_gemv<PF, true, 4><<<g, kGemvThreads, lds, st>>>(a);
-    else k_down_gemv<PF, false, 4><<<g, kGemvThreads, lds, st>>>(a);
+    if (tap) k_down_gemv<PF, true, 4, false><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 4, false><<<g, kGemvThreads, lds, st>>>(a);
   }
 }
 
@@ -947,31 +1056,31 @@ hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_ch
   return hipGetLastError();
 }
 
-template <int NTT, int W>
+template <int NTT, int W, bool GS>
 static void mfma_gateup_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
   constexpr int MPF = NTT == 1 ? 4 : 2;
   if ((a.H / 32) % MPF == 0) {
-    if (tap) k_gateup_mfma<NTT, MPF, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_gateup_mfma<NTT, MPF, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_gateup_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_gateup_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   } else {
-    if (tap) k_gateup_mfma<NTT, 2, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_gateup_mfma<NTT, 2, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_gateup_mfma<NTT, 2, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_gateup_mfma<NTT, 2, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   }
 }
 
-template <int NTT, int W>
+template <int NTT, int W, bool GS>
 static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                              hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
   constexpr int MPF = NTT == 1 ? 4 : 2;
   if ((a.I / 32) % MPF == 0) {
-    if (tap) k_down_mfma<NTT, MPF, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_down_mfma<NTT, MPF, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_down_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_down_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   } else {
-    if (tap) k_down_mfma<NTT, 2, true, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_down_mfma<NTT, 2, false, W><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_down_mfma<NTT, 2, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    else k_down_mfma<NTT, 2, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
   }
 }
 
@@ -988,11 +1097,14 @@ hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int3
   if (grid <= 0) return hipSuccess;
   dim3 g(a.I / 32, grid);
   if (a.wbits == 8) {
-    if (ntt == 2) mfma_gateup_launch<2, 8>(a, g, tiles, n_tiles, st);
-    else mfma_gateup_launch<1, 8>(a, g, tiles, n_tiles, st);
+    if (ntt == 2) mfma_gateup_launch<2, 8, false>(a, g, tiles, n_tiles, st);
+    else mfma_gateup_launch<1, 8, false>(a, g, tiles, n_tiles, st);
+  } else if (a.gshift >= 0) {
+    if (ntt == 2) mfma_gateup_launch<2, 4, true>(a, g, tiles, n_tiles, st);
+    else mfma_gateup_launch<1, 4, true>(a, g, tiles, n_tiles, st);
   } else {
-    if (ntt == 2) mfma_gateup_launch<2, 4>(a, g, tiles, n_tiles, st);
-    else mfma_gateup_launch<1, 4>(a, g, tiles, n_tiles, st);
+    if (ntt == 2) mfma_gateup_launch<2, 4, false>(a, g, tiles, n_tiles, st);
+    else mfma_gateup_launch<1, 4, false>(a, g, tiles, n_tiles, st);
   }
   return hipGetLastError();
 }
@@ -1002,11 +1114,14 @@ hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_
   if (grid <= 0) return hipSuccess;
   dim3 g(a.H / 32, grid);
   if (a.wbits == 8) {
-    if (ntt == 2) mfma_down_launch<2, 8>(a, g, tiles, n_tiles, st);
-    else mfma_down_launch<1, 8>(a, g, tiles, n_tiles, st);
+    if (ntt == 2) mfma_down_launch<2, 8, false>(a, g, tiles, n_tiles, st);
+    else mfma_down_launch<1, 8, false>(a, g, tiles, n_tiles, st);
+  } else if (a.gshift >= 0) {
+    if (ntt == 2) mfma_down_launch<2, 4, true>(a, g, tiles, n_tiles, st);
+    else mfma_down_launch<1, 4, true>(a, g, tiles, n_tiles, st);
   } else {
-    if (ntt == 2) mfma_down_launch<2, 4>(a, g, tiles, n_tiles, st);
-    else mfma_down_launch<1, 4>(a, g, tiles, n_tiles, st);
+    if (ntt == 2) mfma_down_launch<2, 4, false>(a, g, tiles, n_tiles, st);
+    else mfma_down_launch<1, 4, false>(a, g, tiles, n_tiles, st);
   }
   return hipGetLastError();
 }

@@ -135,6 +135,37 @@ __global__ __launch_bounds__(256) void k_quant_int8(const float* __restrict__ w,
   }
 }
 
+// Grouped int4 scales: one lane per (row, group); each group is quantized like
+// a row of k_quant_int4. Codes go to the row-tiled layout, scales to the tiled
+// group-scale layout.
+__global__ __launch_bounds__(256) void k_quant_int4_grouped(const float* __restrict__ w, int rows, int cols,
+                                                            int group, uint8_t* __restrict__ packed,
+                                                            float* __restrict__ scales) {
+  const int ng = cols / group, nb = cols / 32;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * ng) return;
+  const int r = (int)(idx / ng), g = (int)(idx % ng);
+  const float* src = w + (size_t)r * cols + (size_t)g * group;
+  float amax = 0.0f;
+  for (int k = 0; k < group; ++k) amax = fmaxf(amax, fabsf(src[k]));
+  const float s = __fdiv_rn(amax, 7.0f);
+  const float inv = (s == 0.0f) ? 0.0f : __fdiv_rn(1.0f, s);
+  scales[((size_t)(r / 64) * ng + g) * 64 + r % 64] = s;
+  for (int j = 0; j < group / 32; ++j) {
+    const int b = g * (group / 32) + j;
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      float qf = roundf(__fmul_rn(src[j * 32 + i], inv));
+      qf = fminf(fmaxf(qf, -7.0f), 7.0f);
+      const uint32_t nib = (uint32_t)((int)qf) & 0xFu;
+      wv[i >> 3] |= nib << (4 * (i & 7));
+    }
+    const size_t off = tb_off(r / 64, b, nb) + (size_t)(r % 64) * 16;
+    *reinterpret_cast<uint4*>(packed + off) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+}
+
 __global__ void k_q8_0_plain(const float* __restrict__ x, int64_t nblocks, int8_t* __restrict__ q,
                              float* __restrict__ d) {
   int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -169,6 +200,14 @@ hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hip
 hipError_t launch_quant_int8(const float* w, int rows, int cols, uint8_t* codes, float* scales, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   k_quant_int8<<<rows, 256, 0, st>>>(w, cols, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int4_grouped(const float* w, int rows, int cols, int group, uint8_t* packed, float* scales,
+                                     hipStream_t st) {
+  const int64_t n = (int64_t)rows * (cols / group);
+  if (n == 0) return hipSuccess;
+  k_quant_int4_grouped<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(w, rows, cols, group, packed, scales);
   return hipGetLastError();
 }
 

@@ -84,6 +84,11 @@ int validate_config(const moe_config* c) {
   if (c->n_shared < 0 || c->n_shared > kMaxShared) return MOE_E_SHAPE;
   if (!std::isfinite(c->routed_scaling_factor) || c->routed_scaling_factor <= 0.0f) return MOE_E_ARG;
   if (c->weight_bits > 0 && c->weight_bits != 4 && c->weight_bits != 8) return MOE_E_ARG;
+  if (c->group_size > 0) {  // grouped scales: int4 only, 32 * 2^k dividing H and I
+    const int g = c->group_size;
+    if (c->weight_bits == 8 || g % 32 != 0 || ((g / 32) & (g / 32 - 1)) != 0) return MOE_E_ARG;
+    if (c->hidden % g != 0 || c->inter % g != 0) return MOE_E_SHAPE;
+  }
   return MOE_OK;
 }
 
@@ -208,6 +213,7 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
   a.TK = T * cfg->top_k;
   a.wbits = cfg->weight_bits == 8 ? 8 : 4;
   a.op_scale = a.wbits == 8 ? 1.0f : 0.0625f;
+  a.gshift = gshift_of(*cfg);
   Meta* meta = reinterpret_cast<Meta*>(wsb + L.meta);
   a.list = reinterpret_cast<const int32_t*>(wsb + L.gemv);
   a.list_count = &meta->n_gemv;
@@ -308,6 +314,15 @@ int32_t moe_quantize_int4(const float* w, int32_t rows, int32_t cols, uint8_t* p
   if (!w || !packed || !scales) return MOE_E_NULL;
   if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 32 != 0) return MOE_E_SHAPE;
   hipError_t e = launch_quant_int4(w, rows, cols, packed, scales, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_quantize_int4_grouped(const float* w, int32_t rows, int32_t cols, int32_t group, uint8_t* packed,
+                                  float* scales, hipStream_t stream) {
+  if (!w || !packed || !scales) return MOE_E_NULL;
+  if (group <= 0 || group % 32 != 0 || ((group / 32) & (group / 32 - 1)) != 0) return MOE_E_ARG;
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % group != 0) return MOE_E_SHAPE;
+  hipError_t e = launch_quant_int4_grouped(w, rows, cols, group, packed, scales, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -215,9 +215,9 @@ int32_t moe_expert_cache_create(const moe_config* cfg, int32_t n_slots, int32_t 
   const size_t H = cfg->hidden, I = cfg->inter;
   const int wbits = cfg->weight_bits == 8 ? 8 : 4;
   c->b13 = w13_bytes((int)H, (int)I, wbits);  // 2I rows of H codes
-  c->bs13 = 2 * I * 4;
+  c->bs13 = s13_count((int)H, (int)I, gshift_of(*cfg)) * 4;
   c->b2 = w2_bytes((int)H, (int)I, wbits);
-  c->bs2 = H * 4;
+  c->bs2 = s2_count((int)H, (int)I, gshift_of(*cfg)) * 4;
   c->slot_of.assign(c->E, -1);
   c->expert_in.assign(c->S, -1);
   c->last_use.assign(c->E, -1);

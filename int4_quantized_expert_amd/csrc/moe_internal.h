@@ -62,6 +62,7 @@ struct ExpertArgs {
   int32_t E, H, I, K, T, TK;
   int32_t wbits;    // expert weight code width: 4 or 8
   float op_scale;   // factor on the MFMA operand scales: 1/16 for int4 (A holds 16 q), 1 for int8
+  int32_t gshift;   // grouped weight scales: log2(group / 32); -1: one scale per row
   const int32_t* list;        // GEMV work list: (bucket, first token) pairs, chunks of up to kGemvMaxN tokens
   const int32_t* list_count;  // device count of list entries
   const int32_t* bk_e;
@@ -138,6 +139,21 @@ __host__ __device__ __forceinline__ size_t tbw_off(int tile, int blk, int nblock
 // Bytes of one expert's gate/up and down codes.
 __host__ __device__ __forceinline__ size_t w13_bytes(int H, int I, int wbits) { return (size_t)I * H * wbits / 4; }
 __host__ __device__ __forceinline__ size_t w2_bytes(int H, int I, int wbits) { return (size_t)H * I * wbits / 8; }
+// fp32 weight scales per expert: one per row, or one per (row, group) with
+// grouped scales (tiled: row r, group g at ((r/64)*groups + g)*64 + r%64)
+__host__ __device__ __forceinline__ size_t s13_count(int H, int I, int gshift) {
+  return gshift < 0 ? (size_t)2 * I : (size_t)2 * I * ((H / 32) >> gshift);
+}
+__host__ __device__ __forceinline__ size_t s2_count(int H, int I, int gshift) {
+  return gshift < 0 ? (size_t)H : (size_t)H * ((I / 32) >> gshift);
+}
+// log2(group / 32) of a validated config, -1 for one scale per row
+inline int gshift_of(const moe_config& c) {
+  if (c.group_size <= 0) return -1;
+  int sh = 0;
+  while ((32 << sh) < c.group_size) ++sh;
+  return sh;
+}
 
 // Q8_0 operands of the MFMA tiles are kept position-blocked: the codes of 32
 // consecutive positions for one 32-element block are one contiguous KB (32
@@ -204,6 +220,8 @@ hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float
                          hipStream_t st);
 hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hipStream_t st);
 hipError_t launch_quant_int8(const float* w, int rows, int cols, uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_int4_grouped(const float* w, int rows, int cols, int group, uint8_t* packed, float* scales,
+                                     hipStream_t st);
 hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed, float* scales,
                              hipStream_t st);
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,

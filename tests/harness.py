@@ -14,18 +14,18 @@ from synth import synth
 _ORACLE_CACHE: dict = {}
 
 
-def config_of(shape, gemm_min: int = 0, weight_bits: int = 4):
+def config_of(shape, gemm_min: int = 0, weight_bits: int = 4, group_size: int = 0):
     import int4_quantized_expert_amd as moe
     return moe.Config(shape.hidden, shape.n_experts, shape.n_group, shape.topk_group, shape.top_k, shape.inter,
-                      shape.n_shared, shape.rsf, gemm_min, weight_bits)
+                      shape.n_shared, shape.rsf, gemm_min, weight_bits, group_size)
 
 
 class GpuLayer:
     """Device-resident layer: router fp32, routed and shared experts in row-tiled int4 (or int8, weight_bits=8)
-    with fp32 row scales."""
+    with fp32 row scales, or int4 with tiled group scales (group_size > 0)."""
 
     def __init__(self, shape, seed: int = 0, layer: int = 0, device: str = "cuda", n_shared: int | None = None,
-                 weight_bits: int = 4):
+                 weight_bits: int = 4, group_size: int = 0):
         import torch
 
         import int4_quantized_expert_amd as moe
@@ -33,22 +33,27 @@ class GpuLayer:
         H, I, E = shape.hidden, shape.inter, shape.n_experts
         NS = shape.n_shared if n_shared is None else n_shared
         self.NS = NS
-        assert weight_bits in (4, 8)
-        self.weight_bits = weight_bits
+        assert weight_bits in (4, 8) and (group_size == 0 or weight_bits == 4)
+        self.weight_bits, self.group_size = weight_bits, group_size
         b13, b2 = I * H * weight_bits // 4, H * I * weight_bits // 8
-        quant = moe.moe_quantize_int8 if weight_bits == 8 else moe.moe_quantize_int4
+        n13, n2 = (2 * I * H // group_size, H * I // group_size) if group_size else (2 * I, H)
+        if group_size:
+            def quant(w, codes, scales):
+                moe.moe_quantize_int4_grouped(w, group_size, codes, scales)
+        else:
+            quant = moe.moe_quantize_int8 if weight_bits == 8 else moe.moe_quantize_int4
         dev = torch.device(device)
         self.router_w = torch.from_numpy(synth.router_weights(shape, seed, layer)).to(dev)
         self.bias = torch.from_numpy(synth.router_bias(shape, seed, layer)).to(dev)
         self.w13 = torch.empty((E, b13), dtype=torch.uint8, device=dev)
-        self.s13 = torch.empty((E, 2 * I), dtype=torch.float32, device=dev)
+        self.s13 = torch.empty((E, n13), dtype=torch.float32, device=dev)
         self.w2 = torch.empty((E, b2), dtype=torch.uint8, device=dev)
-        self.s2 = torch.empty((E, H), dtype=torch.float32, device=dev)
+        self.s2 = torch.empty((E, n2), dtype=torch.float32, device=dev)
         ns = max(NS, 1)
         self.sh_w13 = torch.empty((ns, b13), dtype=torch.uint8, device=dev)
-        self.sh_s13 = torch.empty((ns, 2 * I), dtype=torch.float32, device=dev)
+        self.sh_s13 = torch.empty((ns, n13), dtype=torch.float32, device=dev)
         self.sh_w2 = torch.empty((ns, b2), dtype=torch.uint8, device=dev)
-        self.sh_s2 = torch.empty((ns, H), dtype=torch.float32, device=dev)
+        self.sh_s2 = torch.empty((ns, n2), dtype=torch.float32, device=dev)
         scratch = torch.empty((2 * I, H), dtype=torch.float32, device=dev)
         scratch2 = torch.empty((H, I), dtype=torch.float32, device=dev)
         st = torch.cuda.current_stream().cuda_stream
@@ -83,17 +88,22 @@ class GpuLayer:
         return n
 
 
-def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = False, weight_bits: int = 4):
+def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = False, weight_bits: int = 4,
+                  group_size: int = 0):
     """(q13, s13, q2, s2) of routed expert e (or shared expert e) from the host generator + oracle quantizer
-    (per-row int4, or per-row int8 for weight_bits=8)."""
+    (per-row int4, per-row int8 for weight_bits=8, or int4 with [rows][cols/G] group scales)."""
     from oracle import oracle as O
-    key = (shape, e, seed, layer, shared, weight_bits)
+    key = (shape, e, seed, layer, shared, weight_bits, group_size)
     if key not in _ORACLE_CACHE:
         if shared:
             w13, w2 = synth.shared_w13(shape, e, seed, layer), synth.shared_w2(shape, e, seed, layer)
         else:
             w13, w2 = synth.expert_w13(shape, e, seed, layer), synth.expert_w2(shape, e, seed, layer)
-        quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
+        if group_size:
+            def quant(w):
+                return O.quant_int4_grouped(w, group_size)
+        else:
+            quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
         q13, s13 = quant(w13)
         q2, s2 = quant(w2)
         if len(_ORACLE_CACHE) > 48:
@@ -102,26 +112,30 @@ def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = F
     return _ORACLE_CACHE[key]
 
 
-def oracle_layer(shape, seed: int = 0, layer: int = 0, n_shared: int | None = None, weight_bits: int = 4):
+def oracle_layer(shape, seed: int = 0, layer: int = 0, n_shared: int | None = None, weight_bits: int = 4,
+                 group_size: int = 0):
     """Whole layer in the oracle's unpacked form (small shapes only)."""
     from oracle import oracle as O
     NS = shape.n_shared if n_shared is None else n_shared
-    parts = [oracle_expert(shape, e, seed, layer, weight_bits=weight_bits) for e in range(shape.n_experts)]
-    sh = [oracle_expert(shape, s, seed, layer, shared=True, weight_bits=weight_bits) for s in range(NS)]
+    kw = dict(weight_bits=weight_bits, group_size=group_size)
+    parts = [oracle_expert(shape, e, seed, layer, **kw) for e in range(shape.n_experts)]
+    sh = [oracle_expert(shape, s, seed, layer, shared=True, **kw) for s in range(NS)]
     H, I = shape.hidden, shape.inter
+    g13 = (2 * I, H // group_size) if group_size else (2 * I,)
+    g2 = (H, I // group_size) if group_size else (H,)
 
     def stack(lst, i, shp, dt):
         return np.stack([p[i] for p in lst]) if lst else np.zeros((0,) + shp, dt)
 
     return O.LayerQ(synth.router_weights(shape, seed, layer), synth.router_bias(shape, seed, layer),
-                    stack(parts, 0, (2 * I, H), np.int8), stack(parts, 1, (2 * I,), np.float32),
-                    stack(parts, 2, (H, I), np.int8), stack(parts, 3, (H,), np.float32),
-                    stack(sh, 0, (2 * I, H), np.int8), stack(sh, 1, (2 * I,), np.float32),
-                    stack(sh, 2, (H, I), np.int8), stack(sh, 3, (H,), np.float32))
+                    stack(parts, 0, (2 * I, H), np.int8), stack(parts, 1, g13, np.float32),
+                    stack(parts, 2, (H, I), np.int8), stack(parts, 3, g2, np.float32),
+                    stack(sh, 0, (2 * I, H), np.int8), stack(sh, 1, g13, np.float32),
+                    stack(sh, 2, (H, I), np.int8), stack(sh, 3, g2, np.float32))
 
 
 def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n_shared: int | None = None,
-                  weight_bits: int = 4):
+                  weight_bits: int = 4, group_size: int = 0):
     """Oracle outputs for selected tokens of a batch, one token at a time (any size).
 
     Returns dict per token: ids, w, flags, rows {k: e_out row}, shared rows, y."""
@@ -138,10 +152,12 @@ def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n
         qx, dx = O.q8_0(xt[0])
         rows, shrows = [], []
         for k in range(shape.top_k):
-            q13, s13, q2, s2 = oracle_expert(shape, int(ids[0, k]), seed, layer, weight_bits=weight_bits)
+            q13, s13, q2, s2 = oracle_expert(shape, int(ids[0, k]), seed, layer, weight_bits=weight_bits,
+                                             group_size=group_size)
             rows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
         for s in range(NS):
-            q13, s13, q2, s2 = oracle_expert(shape, s, seed, layer, shared=True, weight_bits=weight_bits)
+            q13, s13, q2, s2 = oracle_expert(shape, s, seed, layer, shared=True, weight_bits=weight_bits,
+                                             group_size=group_size)
             shrows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
         er = np.stack(rows)[None]
         es = np.stack(shrows)[:, None] if NS else None

@@ -46,7 +46,7 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False,
     into both the cache and the simulator; usage_check: record usage in the simulator from the oracle's
     routing and compare it with the cache's at every pin."""
     sh = layer.shape
-    cfg = config_of(sh, gemm_min, layer.weight_bits)
+    cfg = config_of(sh, gemm_min, layer.weight_bits, layer.group_size)
     Tmax = max(x.shape[0] for x in xs)
     cache = moe.ExpertCache(cfg, n_slots, Tmax)
     sim = O.LRU(sh.n_experts, n_slots)
@@ -83,8 +83,9 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False,
     assert st["hits"] == hits and st["misses"] == misses and st["steps"] == len(xs)
     assert st["evictions"] == sim.counters()["evictions"]
     per = sum(t[0].numel() * t.element_size() for t in (layer.w13, layer.s13, layer.w2, layer.s2))
-    wb = layer.weight_bits
-    assert per == sh.inter * sh.hidden * wb // 4 + 2 * sh.inter * 4 + sh.hidden * sh.inter * wb // 8 + sh.hidden * 4
+    wb, G = layer.weight_bits, layer.group_size
+    nsc = (2 * sh.inter * sh.hidden // G + sh.hidden * sh.inter // G) if G else 2 * sh.inter + sh.hidden
+    assert per == sh.inter * sh.hidden * wb // 4 + sh.hidden * sh.inter * wb // 8 + 4 * nsc
     assert st["bytes_h2d"] == (misses + loaded) * per
     if usage_check:
         assert np.array_equal(cache.usage(), sim.usage())
@@ -120,6 +121,15 @@ def test_cache_tiny_mfma_and_ragged(tiny):
     layer, (hx, _) = tiny
     xs = [synth.hidden_states(synth.TINY, T, seed=1, step=s) for s, T in enumerate([8, 1, 16, 3, 8])]
     _run_steps(layer, hx, 4, xs, gemm_min=1)
+
+
+@pytest.mark.parametrize("gemm_min", [0, 1])
+def test_cache_tiny_grouped_scales(gemm_min):
+    """int4 experts with group scales through the cache: the slots carry the larger scale arrays."""
+    layer = GpuLayer(synth.TINY, group_size=32)
+    hx, _keep = host_experts(layer)
+    xs = [synth.hidden_states(synth.TINY, T, seed=6, step=s) for s, T in enumerate([8, 16, 3, 8, 1])]
+    _run_steps(layer, hx, 4, xs, gemm_min=gemm_min, pins={3: 1}, usage_check=True)
 
 
 @pytest.mark.parametrize("gemm_min", [0, 1])
