@@ -198,10 +198,47 @@ void orc_router_logits(const float* x, int32_t T, int32_t H, const float* Wr, in
  *  to sum 1 and multiplied by routed_scaling_factor (fp64, rounded once).
  *  Ties go to the lower index (groups and experts); slot order is c descending.
  * Returns 0, or -2 for an invalid shape. */
+/* Adaptive expert top-p ("Show HN", usage options: --topp 0.7 keeps fewer
+ * experts per token and cuts disk traffic by 30-40%; the pages give no
+ * definition). Reading: q_k = s_k / sum_j s_j over the K selected slots (the
+ * fp64 quotient of the weights); visit the slots by q descending, lower slot
+ * first on equal q, and keep each while the fp64 sum of the q already kept is
+ * below topp (so the shortest such prefix whose sum reaches topp is kept, and
+ * at least one slot). Kept slots get w_k = fp32((s_k / sum_kept) * rsf), with
+ * sum_kept the fp64 sum of the kept s in slot order; dropped slots get keep 0
+ * and w 0. topp <= 0 or >= 1 keeps every slot with the usual weights. */
+void orc_topp_weights(const float* s_sel, int32_t K, float topp, float rsf, int32_t* keep, float* w) {
+  double sum = 0.0;
+  for (int32_t k = 0; k < K; ++k) sum += (double)s_sel[k];
+  for (int32_t k = 0; k < K; ++k) keep[k] = 1;
+  if (topp > 0.0f && topp < 1.0f) {
+    uint8_t visited[64] = {0};
+    double cum = 0.0;
+    for (int32_t r = 0; r < K; ++r) {
+      int32_t best = -1;
+      double bq = 0.0;
+      for (int32_t k = 0; k < K; ++k) {
+        double q = (double)s_sel[k] / sum;
+        if (!visited[k] && (best < 0 || q > bq)) {
+          best = k;
+          bq = q;
+        }
+      }
+      visited[best] = 1;
+      if (cum < (double)topp) cum += bq;
+      else keep[best] = 0;
+    }
+  }
+  double kept = 0.0;
+  for (int32_t k = 0; k < K; ++k)
+    if (keep[k]) kept += (double)s_sel[k];
+  for (int32_t k = 0; k < K; ++k) w[k] = keep[k] ? (float)(((double)s_sel[k] / kept) * (double)rsf) : 0.0f;
+}
+
 int orc_route(const orc_cfg* c, const float* z, const float* bias, int32_t T, int32_t* ids, float* w,
               uint8_t* flags, float* s_out, float* c_out) {
   int32_t E = c->n_experts, G = c->n_group, KG = c->topk_group, K = c->top_k;
-  if (G <= 0 || E % G != 0 || E / G < 2 || KG < 1 || KG > G || K < 1 || K > KG * (E / G)) return -2;
+  if (G <= 0 || E % G != 0 || E / G < 2 || KG < 1 || KG > G || K < 1 || K > KG * (E / G) || K > 64) return -2;
   int32_t n = E / G;
   float* s = (float*)malloc(sizeof(float) * (size_t)E);
   float* cb = (float*)malloc(sizeof(float) * (size_t)E);
@@ -256,9 +293,12 @@ int orc_route(const orc_cfg* c, const float* z, const float* bias, int32_t T, in
     }
     for (int32_t k = 0; k + 1 < K; ++k)
       if ((double)cb[sel[k]] - (double)cb[sel[k + 1]] < 1e-6) fl |= ORC_TIE_ORDER;
-    double sum = 0.0;
-    for (int32_t k = 0; k < K; ++k) sum += (double)s[sel[k]];
-    for (int32_t k = 0; k < K; ++k) w[(int64_t)t * K + k] = (float)(((double)s[sel[k]] / sum) * (double)c->rsf);
+    float s_sel[64];
+    int32_t keep[64];
+    for (int32_t k = 0; k < K; ++k) s_sel[k] = s[sel[k]];
+    orc_topp_weights(s_sel, K, c->topp, c->rsf, keep, w + (int64_t)t * K);
+    for (int32_t k = 0; k < K; ++k)
+      if (!keep[k]) sel[k] = -1;
     if (flags) flags[t] = fl;
     if (s_out) memcpy(s_out + (int64_t)t * E, s, sizeof(float) * (size_t)E);
     if (c_out) memcpy(c_out + (int64_t)t * E, cb, sizeof(float) * (size_t)E);
@@ -274,19 +314,27 @@ int orc_route(const orc_cfg* c, const float* z, const float* bias, int32_t T, in
  * to it): slot j = t*K + k. counts[e] = slots routed to e; offsets = exclusive
  * prefix sum (offsets[E] = T*K); sorted_slots lists the slots expert by expert,
  * ascending j inside each expert (a stable counting sort); slot_pos is its
- * inverse; unique_ids lists the experts with a non-zero count, ascending. */
+ * inverse; unique_ids lists the experts with a non-zero count, ascending.
+ * A slot with id -1 (dropped by adaptive top-p) is in no bucket: slot_pos = -1,
+ * and offsets[E] counts the other slots. */
 int orc_dispatch(int32_t T, int32_t K, int32_t E, const int32_t* ids, int32_t* counts, int32_t* offsets,
                  int32_t* sorted_slots, int32_t* slot_pos, int32_t* unique_ids, int32_t* n_unique) {
   int64_t S = (int64_t)T * K;
+  if (E <= 0 || S < 0) return -2;
   for (int64_t j = 0; j < S; ++j)
-    if (ids[j] < 0 || ids[j] >= E) return -2;
+    if (ids[j] < -1 || ids[j] >= E) return -2;
   for (int32_t e = 0; e < E; ++e) counts[e] = 0;
-  for (int64_t j = 0; j < S; ++j) counts[ids[j]]++;
+  for (int64_t j = 0; j < S; ++j)
+    if (ids[j] >= 0) counts[ids[j]]++;
   offsets[0] = 0;
   for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
   int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
   for (int64_t j = 0; j < S; ++j) {
     int32_t e = ids[j];
+    if (e < 0) {
+      slot_pos[j] = -1;
+      continue;
+    }
     int32_t p = offsets[e] + fill[e]++;
     sorted_slots[p] = (int32_t)j;
     slot_pos[j] = p;
@@ -404,13 +452,22 @@ void orc_expert_token_g(int32_t H, int32_t I, int32_t group, const int8_t* q13, 
  * e_shared is [n_shared][T][H]. */
 void orc_combine(int32_t T, int32_t K, int32_t H, int32_t n_shared, const float* e_routed,
                  const float* e_shared, const float* w, float* y) {
+  orc_combine_ids(T, K, H, n_shared, e_routed, e_shared, w, NULL, y);
+}
+
+/* The same with the slot ids: slots with id -1 (dropped by adaptive top-p)
+ * add nothing. ids may be NULL (every slot contributes). */
+void orc_combine_ids(int32_t T, int32_t K, int32_t H, int32_t n_shared, const float* e_routed,
+                     const float* e_shared, const float* w, const int32_t* ids, float* y) {
   for (int32_t t = 0; t < T; ++t)
     for (int32_t o = 0; o < H; ++o) {
       float acc = 0.0f;
       if (n_shared > 0) acc = e_shared[(int64_t)t * H + o];
       for (int32_t s = 1; s < n_shared; ++s) acc = acc + e_shared[((int64_t)s * T + t) * H + o];
-      for (int32_t k = 0; k < K; ++k)
+      for (int32_t k = 0; k < K; ++k) {
+        if (ids && ids[(int64_t)t * K + k] < 0) continue;
         acc = fmaf(w[(int64_t)t * K + k], e_routed[((int64_t)t * K + k) * H + o], acc);
+      }
       y[(int64_t)t * H + o] = acc;
     }
 }
@@ -452,6 +509,13 @@ int orc_layer_forward(const orc_cfg* c, int32_t T, const float* x, const float* 
       for (int32_t k = 0; k < K; ++k) {
         int64_t row = (int64_t)t * K + k;
         int32_t e = ids[row];
+        if (e < 0) {  // dropped by adaptive top-p: nothing computed, rows left zero
+          memset(h + row * I, 0, sizeof(float) * (size_t)I);
+          memset(qh + row * I, 0, (size_t)I);
+          memset(dh + row * (I / 32), 0, sizeof(float) * (size_t)(I / 32));
+          memset(eo + row * H, 0, sizeof(float) * (size_t)H);
+          continue;
+        }
         orc_expert_token_g(H, I, G, q13 + e * m13, s13 + e * ns13, q2 + e * m2, s2 + e * ns2, qxt, dxt,
                            h + row * I, qh + row * I, dh + row * (I / 32), eo + row * H, NULL, NULL);
       }
@@ -461,7 +525,7 @@ int orc_layer_forward(const orc_cfg* c, int32_t T, const float* x, const float* 
                            h + row * I, qh + row * I, dh + row * (I / 32), eo + row * H, NULL, NULL);
       }
     }
-    orc_combine(T, K, H, NS, eo, eo + (int64_t)T * K * H, w, y);
+    orc_combine_ids(T, K, H, NS, eo, eo + (int64_t)T * K * H, w, ids, y);
   }
   if (!tp->z) free(z);
   if (!tp->ids) free(ids);

@@ -45,6 +45,7 @@ typedef struct {
   int32_t n_shared;
   float rsf;          /* routed_scaling_factor */
   int32_t group;      /* 0: one weight scale per row; else one per group of this many elements along K */
+  float topp;         /* adaptive expert top-p in (0, 1); otherwise every selected slot is kept */
 } orc_cfg;
 
 /* near-tie flag bits reported per token by orc_route */
@@ -69,6 +70,9 @@ void orc_unpack_int4_tiled64(const uint8_t* in, int64_t rows, int64_t cols, int8
 void orc_q8_0(const float* v, int64_t n, int8_t* q, float* d);
 
 void orc_router_logits(const float* x, int32_t T, int32_t H, const float* Wr, int32_t E, float* z);
+/* keep mask and weights of K selected slots (unbiased scores s_sel, slot order) under adaptive top-p */
+void orc_topp_weights(const float* s_sel, int32_t K, float topp, float rsf, int32_t* keep, float* w);
+/* ids of slots dropped by adaptive top-p are -1, their weights 0 */
 int orc_route(const orc_cfg* c, const float* z, const float* bias, int32_t T, int32_t* ids, float* w,
               uint8_t* flags, float* s_out, float* c_out);
 int orc_dispatch(int32_t T, int32_t K, int32_t E, const int32_t* ids, int32_t* counts, int32_t* offsets,
@@ -90,6 +94,8 @@ void orc_expert_token_g(int32_t H, int32_t I, int32_t group, const int8_t* q13, 
                         float* out, int32_t* S13, int32_t* S2);
 void orc_combine(int32_t T, int32_t K, int32_t H, int32_t n_shared, const float* e_routed,
                  const float* e_shared, const float* w, float* y);
+void orc_combine_ids(int32_t T, int32_t K, int32_t H, int32_t n_shared, const float* e_routed,
+                     const float* e_shared, const float* w, const int32_t* ids, float* y);
 
 typedef struct {
   float* z;          /* [T][E] */

@@ -21,7 +21,8 @@ TIE_EXPERT, TIE_GROUP, TIE_ORDER = 1, 2, 4
 class OrcCfg(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32), ("rsf", ctypes.c_float), ("group", ctypes.c_int32)]
+                ("n_shared", ctypes.c_int32), ("rsf", ctypes.c_float), ("group", ctypes.c_int32),
+                ("topp", ctypes.c_float)]
 
 
 class OrcTaps(ctypes.Structure):
@@ -55,6 +56,8 @@ def lib():
         L.orc_swiglu.restype = F
         L.orc_expert_token.argtypes = [I32, I32] + [P] * 12
         L.orc_combine.argtypes = [I32, I32, I32, I32, P, P, P, P]
+        L.orc_combine_ids.argtypes = [I32, I32, I32, I32, P, P, P, P, P]
+        L.orc_topp_weights.argtypes = [P, I32, F, F, P, P]
         L.orc_layer_forward.argtypes = [P, I32] + [P] * 12 + [P]
         L.orc_lru_new.argtypes = [I32, I32]
         L.orc_lru_new.restype = P
@@ -89,15 +92,16 @@ class Cfg:
     n_shared: int
     rsf: float
     group: int = 0  # 0: one weight scale per row; else one per group of this many elements along K
+    topp: float = 0.0  # adaptive expert top-p in (0, 1); otherwise off
 
     def c(self):
         return OrcCfg(self.hidden, self.n_experts, self.n_group, self.topk_group, self.top_k, self.inter,
-                      self.n_shared, self.rsf, self.group)
+                      self.n_shared, self.rsf, self.group, self.topp)
 
     @staticmethod
-    def of(shape, group: int = 0):
+    def of(shape, group: int = 0, topp: float = 0.0):
         return Cfg(shape.hidden, shape.n_experts, shape.n_group, shape.topk_group, shape.top_k, shape.inter,
-                   shape.n_shared, shape.rsf, group)
+                   shape.n_shared, shape.rsf, group, topp)
 
 
 def quant_int4_rows(w):
@@ -205,12 +209,21 @@ def route(cfg: Cfg, z, bias, want_scores=False):
     return ids, w, fl
 
 
+def topp_weights(s_sel, topp, rsf):
+    """(keep [K] int32, w [K] fp32) of K selected slots' unbiased scores under adaptive top-p."""
+    s_sel = _c(s_sel, np.float32)
+    keep = np.empty(s_sel.size, np.int32)
+    w = np.empty(s_sel.size, np.float32)
+    lib().orc_topp_weights(_p(s_sel), s_sel.size, float(topp), float(rsf), _p(keep), _p(w))
+    return keep, w
+
+
 def dispatch(ids, E):
     ids = _c(ids, np.int32)
     T, K = ids.shape
     counts = np.empty(E, np.int32)
     offsets = np.empty(E + 1, np.int32)
-    ss = np.empty(T * K, np.int32)
+    ss = np.full(T * K, -1, np.int32)  # entries past offsets[E] (slots dropped by top-p) stay -1
     sp = np.empty(T * K, np.int32)
     uq = np.empty(E, np.int32)
     nu = np.zeros(1, np.int32)
@@ -276,14 +289,16 @@ def expert_token(q13, s13, q2, s2, qx, dx, want_sums=False):
     return r
 
 
-def combine(e_routed, e_shared, w):
+def combine(e_routed, e_shared, w, ids=None):
+    """ids (optional, [T][K]): slots with id -1 add nothing."""
     e_routed = _c(e_routed, np.float32)
     w = _c(w, np.float32)
     T, K, H = e_routed.shape
     NS = 0 if e_shared is None else e_shared.shape[0]
     es = None if e_shared is None else _c(e_shared, np.float32)
+    ids = None if ids is None else _c(ids, np.int32)
     y = np.empty((T, H), np.float32)
-    lib().orc_combine(T, K, H, NS, _p(e_routed), _p(es), _p(w), _p(y))
+    lib().orc_combine_ids(T, K, H, NS, _p(e_routed), _p(es), _p(w), _p(ids), _p(y))
     return y
 
 

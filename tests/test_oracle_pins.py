@@ -328,6 +328,98 @@ def test_route_near_tie_flags():
     assert f3[0] & O.TIE_ORDER
 
 
+@pytest.mark.parametrize("i", range(3))
+def test_topp_golden(i):
+    g = HW["topp_cases"]["cases"][i]
+    keep, w = O.topp_weights(np.array(g["s_sel"], np.float32), g["topp"], g["rsf"])
+    assert np.array_equal(keep, np.array(g["keep"], np.int32))
+    assert np.array_equal(w, np.array(g["w"], np.float32))
+
+
+def test_topp_off_is_the_router_weighting_and_tiny_p_keeps_one():
+    sh = synth.TINY
+    cfg = O.Cfg.of(sh)
+    x = synth.hidden_states(sh, 16, seed=40)
+    ids, w, _, sc, _ = O.route(cfg, O.router_logits(x, synth.router_weights(sh)), synth.router_bias(sh),
+                               want_scores=True)
+    for t in range(16):
+        s_sel = sc[t, ids[t]]
+        for off in (0.0, 1.0, 1.5, -0.25):
+            keep, ww = O.topp_weights(s_sel, off, sh.rsf)
+            assert keep.all() and np.array_equal(ww, w[t])
+        keep, ww = O.topp_weights(s_sel, 1e-9, sh.rsf)
+        assert keep.sum() == 1 and ww[keep == 1][0] == np.float32(sh.rsf)
+        assert np.argmax(keep) == np.argmax(s_sel)  # first maximum: the lower slot on ties
+
+
+@pytest.mark.parametrize("topp", [0.3, 0.7, 0.9])
+def test_topp_keeps_the_shortest_heaviest_prefix(topp):
+    rng = np.random.default_rng(int(topp * 100))
+    for _ in range(200):
+        K = int(rng.integers(1, 17))
+        s_sel = rng.uniform(0.01, 1.0, K).astype(np.float32)
+        if K > 3:
+            s_sel[2] = s_sel[1]  # a tie
+        keep, w = O.topp_weights(s_sel, topp, 2.5)
+        q = s_sel.astype(np.float64) / s_sel.astype(np.float64).sum()
+        order = sorted(range(K), key=lambda k: (-q[k], k))
+        m = int(keep.sum())
+        assert m >= 1 and set(np.nonzero(keep)[0]) == set(order[:m])
+        cum = q[order[:m]].sum()
+        assert cum >= np.float32(topp) - 1e-12 or m == K
+        assert q[order[:m - 1]].sum() < np.float32(topp) + 1e-12
+        assert np.all(w[keep == 0] == 0) and np.all(w[keep == 1] > 0)
+        assert abs(float(w.astype(np.float64).sum()) - 2.5) <= 2.5 * K * 2.0 ** -23
+
+
+def test_route_with_topp_drops_slots_of_the_full_selection():
+    sh = synth.TINY
+    x = synth.hidden_states(sh, 32, seed=41)
+    z = O.router_logits(x, synth.router_weights(sh))
+    ids0, w0, f0 = O.route(O.Cfg.of(sh), z, synth.router_bias(sh))
+    ids, w, f = O.route(O.Cfg.of(sh, topp=0.6), z, synth.router_bias(sh))
+    assert np.array_equal(f, f0)
+    kept = ids >= 0
+    assert np.array_equal(ids[kept], ids0[kept]) and np.all(w[~kept] == 0)
+    assert kept.any(1).all() and (~kept).any()  # every token keeps a slot; some slots drop
+
+
+def test_dispatch_with_dropped_slots_vs_sort():
+    rng = np.random.default_rng(8)
+    T, K, E = 40, 4, 16
+    ids = rng.integers(0, E, (T, K)).astype(np.int32)
+    ids[rng.random((T, K)) < 0.3] = -1
+    d = O.dispatch(ids, E)
+    flat = ids.ravel()
+    valid = np.nonzero(flat >= 0)[0]
+    order = valid[np.argsort(flat[valid], kind="stable")]
+    n = valid.size
+    assert d["offsets"][E] == n and np.array_equal(d["sorted_slots"][:n], order)
+    assert np.all(d["sorted_slots"][n:] == -1)
+    assert np.all(d["slot_pos"][flat < 0] == -1)
+    assert np.array_equal(d["slot_pos"][order], np.arange(n))
+    assert np.array_equal(d["counts"], np.bincount(flat[valid], minlength=E))
+    with pytest.raises(ValueError):
+        O.dispatch(np.full((2, 2), -2, np.int32), E)
+
+
+def test_combine_skips_dropped_slots():
+    rng = np.random.default_rng(9)
+    T, K, H = 5, 4, 64
+    er = rng.normal(size=(T, K, H)).astype(np.float32)
+    es = rng.normal(size=(1, T, H)).astype(np.float32)
+    w = rng.uniform(0.1, 1.0, (T, K)).astype(np.float32)
+    ids = np.zeros((T, K), np.int32)
+    assert np.array_equal(O.combine(er, es, w, ids), O.combine(er, es, w))
+    ids[:, 1] = -1
+    er2 = er.copy()
+    er2[:, 1] = np.nan  # a dropped slot's row is never read
+    w2 = w.copy()
+    w2[:, 1] = 0.0
+    ref = O.combine(np.delete(er, 1, axis=1), es, np.delete(w2, 1, axis=1))
+    assert np.array_equal(O.combine(er2, es, w2, ids), ref)
+
+
 def test_route_rejects_bad_shapes():
     with pytest.raises(ValueError):
         O.route(O.Cfg(32, 10, 4, 2, 2, 32, 0, 1.0), np.zeros((1, 10), np.float32), np.zeros(10, np.float32))
@@ -629,6 +721,29 @@ def test_layer_grouped_matches_per_pair_evaluation():
     # and differs from the per-row layer of the same weights
     y_row = O.layer_forward(O.Cfg.of(sh), x, _tiny_layer(), taps=False)
     assert not np.array_equal(y, y_row)
+
+
+def test_layer_topp_matches_per_pair_evaluation(tiny):
+    """With adaptive top-p the layer computes only the kept slots and combines them with the renormalised
+    weights: equal to per-pair evaluation of the kept (token, expert) pairs and the combine over them."""
+    sh = synth.TINY
+    cfg = O.Cfg.of(sh, topp=0.55)
+    x = synth.hidden_states(sh, 12, seed=13)
+    y, t = O.layer_forward(cfg, x, tiny)
+    ids, w, _ = O.route(cfg, O.router_logits(x, tiny.router_w), tiny.bias)
+    assert np.array_equal(t["ids"], ids) and (ids < 0).any()
+    for tt in range(12):
+        qx, dx = O.q8_0(x[tt])
+        rows = []
+        for k in range(sh.top_k):
+            e = ids[tt, k]
+            r = np.zeros(sh.hidden, np.float32) if e < 0 else \
+                O.expert_token(tiny.q13[e], tiny.s13[e], tiny.q2[e], tiny.s2[e], qx, dx)["out"]
+            assert np.array_equal(t["e_out"][tt * sh.top_k + k], r)
+            rows.append(r)
+        shr = O.expert_token(tiny.sq13[0], tiny.ss13[0], tiny.sq2[0], tiny.ss2[0], qx, dx)["out"]
+        yy = O.combine(np.stack(rows)[None], shr[None, None], w[tt:tt + 1], ids[tt:tt + 1])
+        assert np.array_equal(y[tt], yy[0])
 
 
 def test_layer_zero_input_closed_form(tiny):
