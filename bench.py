@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--gemm-min", type=int, default=0)
     ap.add_argument("--weight-bits", type=int, default=4, choices=[4, 8],
                     help="expert weight codes: 4 (row-tiled int4, the default) or 8 (row-tiled int8)")
+    ap.add_argument("--topp", type=float, default=0.0,
+                    help="adaptive expert top-p in (0, 1): keep the heaviest slots up to this weight (0: off)")
     ap.add_argument("--group-size", type=int, default=0,
                     help="int4 only: one weight scale per this many elements along K (0: one per row)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
@@ -118,13 +120,13 @@ def routing_stats(moe, cfg, layer, x_dev, ws, gemm_min):
 SAMPLE_TOKENS = 8  # tokens of the CPU sample (each distinct expert they route to is generated once)
 
 
-def cpu_baseline(shape, x, seconds, seed, weight_bits=4, group_size=0):
+def cpu_baseline(shape, x, seconds, seed, weight_bits=4, group_size=0, topp=0.0):
     """The oracle as it stands, single-threaded, over the first SAMPLE_TOKENS tokens of the first batch: they are
     routed once and each distinct expert they need is generated once (outside the timing); then passes over
     them are timed until `seconds` of oracle time have been spent."""
     from oracle import oracle as O
     from synth import synth
-    cfg = O.Cfg.of(shape)
+    cfg = O.Cfg.of(shape, topp=topp)
     Wr = synth.router_weights(shape, seed)
     bias = synth.router_bias(shape, seed)
     x = x[:SAMPLE_TOKENS]
@@ -141,7 +143,7 @@ def cpu_baseline(shape, x, seconds, seed, weight_bits=4, group_size=0):
         quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
         return quant(w13) + quant(w2)
 
-    experts = {int(e): gen(int(e), False) for e in np.unique(ids_all)}
+    experts = {int(e): gen(int(e), False) for e in np.unique(ids_all) if e >= 0}
     shared = gen(0, True)
     done, t_oracle, passes = 0, 0.0, 0
     while t_oracle < seconds and passes < 20:
@@ -151,9 +153,10 @@ def cpu_baseline(shape, x, seconds, seed, weight_bits=4, group_size=0):
             z = O.router_logits(xt, Wr)
             ids, w, _ = O.route(cfg, z, bias)
             qx, dx = O.q8_0(xt[0])
-            rows = [O.expert_token(*experts[int(e)], qx, dx)["out"] for e in ids[0]]
+            rows = [O.expert_token(*experts[int(e)], qx, dx)["out"] if e >= 0 else np.zeros(shape.hidden, np.float32)
+                    for e in ids[0]]
             rows.append(O.expert_token(*shared, qx, dx)["out"])
-            O.combine(np.stack(rows[:-1])[None], np.stack(rows[-1:])[:, None], w)
+            O.combine(np.stack(rows[:-1])[None], np.stack(rows[-1:])[:, None], w, ids)
             t_oracle += time.perf_counter() - t0
             done += 1
             if t_oracle >= seconds:
@@ -364,7 +367,7 @@ def main():
         calibrate()
         return
     if args.workload == "stack40":
-        if args.weight_bits != 4 or args.group_size:
+        if args.weight_bits != 4 or args.group_size or args.topp:
             print("stack40 streams int4 experts with row scales only.", file=sys.stderr)
             sys.exit(2)
         run_stack(args)
@@ -379,7 +382,7 @@ def main():
     T = tokens_of(args.workload)
     dev = torch.device("cuda:0")
     WB, GSZ = args.weight_bits, args.group_size
-    cfg = config_of(shape, args.gemm_min, WB, GSZ)
+    cfg = config_of(shape, args.gemm_min, WB, GSZ, args.topp)
     layers = [GpuLayer(shape, seed=args.seed + c, weight_bits=WB, group_size=GSZ) for c in range(args.copies)]
     n_in = args.warmup + args.steps
     xs_host = make_inputs(shape, args.workload, min(n_in, 64), args.seed)
@@ -402,7 +405,8 @@ def main():
     # timed region records HIP events around it only (on the stream it runs on)
     kname = "gateup_mfma" if args.workload == "prefill" else "gateup_gemv"
     # counter summaries are per kernel, workload and weight width
-    pmc_workload = args.workload + ("_int8w" if WB == 8 else "") + (f"_g{GSZ}" if GSZ else "")
+    pmc_workload = args.workload + ("_int8w" if WB == 8 else "") + (f"_g{GSZ}" if GSZ else "") + \
+        (f"_topp{args.topp:g}" if 0 < args.topp < 1 else "")
     kidx = moe.STAGES.index(kname)
 
     def timed(stages):
@@ -469,24 +473,27 @@ def main():
         "config": {"workload": f"glm5.2-moe-layer {args.workload}", "tokens": T, "hidden": H, "experts": E,
                    "groups": shape.n_group, "topk_group": shape.topk_group, "top_k": shape.top_k, "inter": I,
                    "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or DEFAULT_GEMM_MIN,
-                   "layer_copies": args.copies, "weight_bits": WB, "group_size": GSZ},
+                   "layer_copies": args.copies, "weight_bits": WB, "group_size": GSZ, "topp": args.topp},
         "layer_hbm_gbs": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9), 1),
         "layer_hbm_frac": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9) / HBM_PEAK_GBS, 4),
         "unique_experts_mean": round(float(U.mean()), 2),
+        "routed_slots_mean": round(float(np.mean([st["counts"].sum() for st in stats])), 2),
         "stage_ms": {n: round(float(v), 5) for n, v in zip(moe.STAGES, stage_ms)},
         "ms_per_step_all_stage_events": round(ms_staged, 5),
         "roofline": roof,
     }
     # layer-level view: every expert's int8 ops (MFMA and v_dot4 paths) against the dense int8 MFMA peak, and the
     # larger of the HBM and MFMA lower bounds against the measured step
-    ops_layer = 2.0 * (T * shape.top_k + shape.n_shared * T) * (2 * I * H + H * I)
+    routed = float(np.mean([st["counts"].sum() for st in stats]))  # T*K, or fewer with adaptive top-p
+    ops_layer = 2.0 * (routed + shape.n_shared * T) * (2 * I * H + H * I)
     t_mem = layer_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = ops_layer / (INT8_PEAK_TOPS * 1e12)
     out["layer_int8_ops"] = ops_layer
     out["layer_int8_mfma_frac"] = round(ops_layer / (ms_step / 1e3) / (INT8_PEAK_TOPS * 1e12), 4)
     out["combined_roofline_frac"] = round(float(np.mean(np.maximum(t_mem, t_mfma))) / (ms_step / 1e3), 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB, GSZ)
+        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB, GSZ,
+                                           args.topp)
     print(json.dumps(out), flush=True)
 
 

@@ -23,6 +23,8 @@
  *  [D2] same page, implemented features: int8 and packed int4 weights with
  *      per-row scales; the MTP head must be int8 (int4 drafts are almost
  *      never accepted).
+ *  [D4] "Show HN", useful options: --topp 0.7, adaptive expert top-p, cuts
+ *      disk traffic by 30-40% (no definition given).
  *  [D3] "Colibri: 25GB RAM을 탑재한 노트북에서 744B AI 모델 실행하기", section on
  *      the quality cost of int4: grouped scales recover most of the accuracy
  *      int4 loses (group size and scale format not given).
@@ -113,6 +115,11 @@ typedef struct moe_config {
                             group_size elements along K [D3]; a power of two times 32 that divides
                             H and I. The dot then scales block b's exact sum by
                             fp32(d_b * s_group(b)) in its class chain, with no row scale. */
+  float topp;            /* adaptive expert top-p [D4]: in (0, 1) a token keeps only the slots, taken by
+                            normalised weight descending (lower slot first on ties), while the fp64 sum of
+                            the kept weights is below topp, and its kept weights are renormalised over the
+                            kept scores (times routed_scaling_factor); dropped slots have id -1 and weight
+                            0 and are computed by no expert. <= 0 or >= 1: every slot kept. */
 } moe_config;
 
 /* A layer's weights. Routed arrays hold E experts back to back; shared arrays
@@ -199,7 +206,9 @@ int32_t moe_quantize_q8_0(const float* x, int64_t n, int8_t* q, float* d, hipStr
  * fixed order independent of T and of the token's position), s = sigmoid(z),
  * c = s + bias; group score = top-2 sum of c per group; keep topk_group
  * groups; top-K experts by c among them (ties to the lower index; slot order
- * c descending); weights = s / sum(s) * routed_scaling_factor.
+ * c descending); weights = s / sum(s) * routed_scaling_factor. With adaptive
+ * top-p (cfg->topp in (0, 1), [D4]) dropped slots get id -1 and weight 0 and
+ * the kept weights are renormalised over the kept s.
  * x [T][H] fp32; topk_ids [T][K] int32; topk_w [T][K] fp32; near_tie [T]
  * (nullable). T >= 1. */
 int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float* router_w,
@@ -210,7 +219,9 @@ int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float
  * exclusive prefix sum; sorted_slots groups slots by expert, ascending slot
  * inside each expert (stable, deterministic, no float atomics); slot_pos its
  * inverse; unique_ids the experts with a non-zero count, ascending (rest -1);
- * n_unique [1]. topk_ids values must lie in [0, E). */
+ * n_unique [1]. A slot whose id is outside [0, E) (-1: dropped by adaptive
+ * top-p) is in no bucket: slot_pos -1, and offsets[E] counts the other slots;
+ * sorted_slots past offsets[E] is not written. */
 int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, int32_t* counts, int32_t* offsets,
                      int32_t* sorted_slots, int32_t* slot_pos, int32_t* unique_ids, int32_t* n_unique, void* ws,
                      size_t ws_bytes, hipStream_t stream);

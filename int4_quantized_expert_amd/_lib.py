@@ -37,7 +37,7 @@ P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 class moe_config(ctypes.Structure):
     _fields_ = [("hidden", I32), ("n_experts", I32), ("n_group", I32), ("topk_group", I32), ("top_k", I32),
                 ("inter", I32), ("n_shared", I32), ("routed_scaling_factor", F32), ("gemm_min_tokens", I32),
-                ("weight_bits", I32), ("group_size", I32)]
+                ("weight_bits", I32), ("group_size", I32), ("topp", F32)]
 
 
 class moe_layer_weights(ctypes.Structure):
@@ -142,11 +142,12 @@ class Config:
     gemm_min_tokens: int = 0
     weight_bits: int = 4
     group_size: int = 0
+    topp: float = 0.0
 
     def c(self):
         return moe_config(self.hidden, self.n_experts, self.n_group, self.topk_group, self.top_k, self.inter,
                           self.n_shared, self.routed_scaling_factor, self.gemm_min_tokens, self.weight_bits,
-                          self.group_size)
+                          self.group_size, self.topp)
 
 
 def moe_version():

@@ -2,7 +2,8 @@
 // expert (weight 1, always on; "Show HN: 느린 컴퓨터에서 GLM 5.2 실행하기",
 // implemented features: shared expert) first, further shared experts added in
 // index order, then each routed output with its router weight in slot order,
-// one fused multiply-add each. A gather in fixed order — no atomics — so the
+// one fused multiply-add each; a slot with no position (dropped by adaptive
+// top-p) adds nothing. A gather in fixed order — no atomics — so the
 // result does not depend on scheduling. Bandwidth-bound: each lane moves one
 // float4 of every contributing row.
 #include "moe_internal.h"
@@ -30,15 +31,18 @@ __global__ __launch_bounds__(64) void k_combine(const float* __restrict__ eout, 
   for (int k0 = 0; k0 < K; k0 += KB) {
     float wk[KB];
     float4 v[KB];
+    bool on[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int k = min(k0 + u, K - 1);
+      const int sp = slotpos[(size_t)t * K + k];
+      on[u] = k0 + u < K && sp >= 0;
       wk[u] = w[(size_t)t * K + k];
-      v[u] = *reinterpret_cast<const float4*>(eout + (size_t)slotpos[(size_t)t * K + k] * H + o);
+      v[u] = *reinterpret_cast<const float4*>(eout + (size_t)max(sp, 0) * H + o);
     }
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      if (k0 + u < K) {
+      if (on[u]) {
         acc.x = fmaf(wk[u], v[u].x, acc.x);
         acc.y = fmaf(wk[u], v[u].y, acc.y);
         acc.z = fmaf(wk[u], v[u].z, acc.z);

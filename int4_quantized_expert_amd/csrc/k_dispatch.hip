@@ -12,6 +12,10 @@
 // expert list, the GEMV work list ((bucket, first token) pairs in chunks of up
 // to kGemvMaxN tokens, for buckets below the MFMA threshold) and the MFMA tile list
 // ((bucket, first token) pairs).
+//
+// Slots whose id is outside [0, E) (adaptive top-p writes -1 for a dropped
+// slot) belong to no bucket: they are not counted, their slot_pos is -1, and
+// offsets[E] is the number of the other slots.
 #include "moe_internal.h"
 
 namespace moe {
@@ -43,7 +47,10 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
   const int E = a.E, TK = a.T * a.K;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
-  for (int j = tid; j < TK; j += 256) atomicAdd(&hist[a.ids[j]], 1);
+  for (int j = tid; j < TK; j += 256) {
+    const int id = a.ids[j];
+    if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);
+  }
   __syncthreads();
   // exclusive prefix sum over experts: 4 per thread, then a block scan
   int loc[4], sum = 0;
@@ -70,7 +77,7 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
     int e = tid * 4 + i;
     if (e < E) off[e] = excl + loc[i];
   }
-  if (tid == 0) off[E] = TK;
+  if (tid == 0) off[E] = wsum[0] + wsum[1] + wsum[2] + wsum[3];  // slots in buckets
   __syncthreads();
 
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -81,7 +88,7 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
     if (lane == 0) {
       a.counts[e] = cnt;
       a.offsets[e] = pos;
-      if (e == E - 1) a.offsets[E] = TK;
+      if (e == E - 1) a.offsets[E] = off[E];
     }
     const int end = pos + cnt;
     for (int jb = 0; jb < TK && pos < end; jb += 64) {
@@ -99,6 +106,8 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
   }
 
   if (blockIdx.x == 0) {
+    for (int j = tid; j < TK; j += 256)
+      if ((unsigned)a.ids[j] >= (unsigned)E) a.slotpos[j] = -1;
     __shared__ int s_nu;
     if (wave == 0) {
       int nu = 0;

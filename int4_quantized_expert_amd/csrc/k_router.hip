@@ -202,8 +202,12 @@ __global__ __launch_bounds__(64) void k_router_mfma(const float* __restrict__ x,
 // scores, so the whole selection is a few synchronised passes rather than a
 // chain of wave-wide reductions. Near-tie flags: kept/dropped group boundary,
 // chosen/next expert boundary, adjacent chosen experts (differences < 1e-6).
+// Adaptive top-p (0 < topp < 1): one lane visits the K slots by q = s / sum
+// descending (lower slot first on equal q) and keeps each while the fp64 sum
+// of the kept q is below topp; kept slots are renormalised over the kept s
+// (slot order), dropped slots get id -1 and weight 0.
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, const float* __restrict__ bias, int E,
-                                              int G, int KG, int K, float rsf, int32_t* __restrict__ ids,
+                                              int G, int KG, int K, float rsf, float topp, int32_t* __restrict__ ids,
                                               float* __restrict__ w, uint8_t* __restrict__ flags) {
   __shared__ float s_s[kMaxExperts];
   __shared__ float s_c[kMaxExperts];
@@ -214,6 +218,9 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
   __shared__ int s_sel[kMaxTopK];
   __shared__ float s_selc[kMaxTopK + 1];
   __shared__ float s_sels[kMaxTopK];
+  __shared__ int s_keep[kMaxTopK];
+  __shared__ double s_q[kMaxTopK];  // s / sum of the selected slots (adaptive top-p)
+  __shared__ double s_sum;
   const int t = blockIdx.x, tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) {
     double v[kRouterChunks];
@@ -275,7 +282,39 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
     }
   }
   __syncthreads();
+  const bool use_topp = topp > 0.0f && topp < 1.0f;
+  if (use_topp && tid < K) {
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) sum += (double)s_sels[k];
+    s_q[tid] = (double)s_sels[tid] / sum;
+  }
+  __syncthreads();
   if (tid == 0) {
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) sum += (double)s_sels[k];
+    for (int k = 0; k < K; ++k) s_keep[k] = 1;
+    if (use_topp) {
+      uint32_t visited = 0u;  // K <= 32
+      double cum = 0.0;
+      for (int r = 0; r < K; ++r) {
+        int best = -1;
+        double bq = 0.0;
+        for (int k = 0; k < K; ++k) {
+          const double q = s_q[k];
+          if (!((visited >> k) & 1u) && (best < 0 || q > bq)) {
+            best = k;
+            bq = q;
+          }
+        }
+        visited |= 1u << best;
+        if (cum < (double)topp) cum += bq;
+        else s_keep[best] = 0;
+      }
+      sum = 0.0;
+      for (int k = 0; k < K; ++k)
+        if (s_keep[k]) sum += (double)s_sels[k];
+    }
+    s_sum = sum;
     uint8_t fl = 0;
     if (KG < G && (double)s_grank[KG - 1] - (double)s_grank[KG] < 1e-6) fl |= MOE_TIE_GROUP;
     if (K < KG * n && (double)s_selc[K - 1] - (double)s_selc[K] < 1e-6) fl |= MOE_TIE_EXPERT;
@@ -283,11 +322,11 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
       if ((double)s_selc[k] - (double)s_selc[k + 1] < 1e-6) fl |= MOE_TIE_ORDER;
     if (flags) flags[t] = fl;
   }
+  __syncthreads();
   if (tid < K) {
-    double sum = 0.0;
-    for (int k = 0; k < K; ++k) sum += (double)s_sels[k];
-    ids[(size_t)t * K + tid] = s_sel[tid];
-    w[(size_t)t * K + tid] = (float)(((double)s_sels[tid] / sum) * (double)rsf);
+    const bool keep = s_keep[tid] != 0;
+    ids[(size_t)t * K + tid] = keep ? s_sel[tid] : -1;
+    w[(size_t)t * K + tid] = keep ? (float)(((double)s_sels[tid] / s_sum) * (double)rsf) : 0.0f;
   }
 }
 
@@ -315,8 +354,8 @@ hipError_t launch_route(const float* x, int T, const moe_config& c, const float*
   }
   if (q8_done && qx_perm) *q8_done = true;
   if (mark) mark(mark_call, 1, st);
-  k_topk<<<T, 256, 0, st>>>(part, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, ids, w,
-                            flags);
+  k_topk<<<T, 256, 0, st>>>(part, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, c.topp, ids,
+                            w, flags);
   return hipGetLastError();
 }
 

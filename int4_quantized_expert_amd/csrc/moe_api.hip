@@ -84,6 +84,7 @@ int validate_config(const moe_config* c) {
   if (c->n_shared < 0 || c->n_shared > kMaxShared) return MOE_E_SHAPE;
   if (!std::isfinite(c->routed_scaling_factor) || c->routed_scaling_factor <= 0.0f) return MOE_E_ARG;
   if (c->weight_bits > 0 && c->weight_bits != 4 && c->weight_bits != 8) return MOE_E_ARG;
+  if (!std::isfinite(c->topp)) return MOE_E_ARG;
   if (c->group_size > 0) {  // grouped scales: int4 only, 32 * 2^k dividing H and I
     const int g = c->group_size;
     if (c->weight_bits == 8 || g % 32 != 0 || ((g / 32) & (g / 32 - 1)) != 0) return MOE_E_ARG;

@@ -14,10 +14,10 @@ from synth import synth
 _ORACLE_CACHE: dict = {}
 
 
-def config_of(shape, gemm_min: int = 0, weight_bits: int = 4, group_size: int = 0):
+def config_of(shape, gemm_min: int = 0, weight_bits: int = 4, group_size: int = 0, topp: float = 0.0):
     import int4_quantized_expert_amd as moe
     return moe.Config(shape.hidden, shape.n_experts, shape.n_group, shape.topk_group, shape.top_k, shape.inter,
-                      shape.n_shared, shape.rsf, gemm_min, weight_bits, group_size)
+                      shape.n_shared, shape.rsf, gemm_min, weight_bits, group_size, topp)
 
 
 class GpuLayer:
@@ -135,13 +135,13 @@ def oracle_layer(shape, seed: int = 0, layer: int = 0, n_shared: int | None = No
 
 
 def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n_shared: int | None = None,
-                  weight_bits: int = 4, group_size: int = 0):
+                  weight_bits: int = 4, group_size: int = 0, topp: float = 0.0):
     """Oracle outputs for selected tokens of a batch, one token at a time (any size).
 
     Returns dict per token: ids, w, flags, rows {k: e_out row}, shared rows, y."""
     from oracle import oracle as O
     NS = shape.n_shared if n_shared is None else n_shared
-    cfg = O.Cfg.of(shape)
+    cfg = O.Cfg.of(shape, topp=topp)
     Wr = synth.router_weights(shape, seed, layer)
     bias = synth.router_bias(shape, seed, layer)
     out = {}
@@ -152,6 +152,9 @@ def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n
         qx, dx = O.q8_0(xt[0])
         rows, shrows = [], []
         for k in range(shape.top_k):
+            if ids[0, k] < 0:  # dropped by adaptive top-p
+                rows.append(np.zeros(shape.hidden, np.float32))
+                continue
             q13, s13, q2, s2 = oracle_expert(shape, int(ids[0, k]), seed, layer, weight_bits=weight_bits,
                                              group_size=group_size)
             rows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
@@ -161,7 +164,7 @@ def oracle_tokens(shape, x: np.ndarray, tokens, seed: int = 0, layer: int = 0, n
             shrows.append(O.expert_token(q13, s13, q2, s2, qx, dx)["out"])
         er = np.stack(rows)[None]
         es = np.stack(shrows)[:, None] if NS else None
-        y = O.combine(er, es, w)[0]
+        y = O.combine(er, es, w, ids)[0]
         out[t] = dict(ids=ids[0], w=w[0], flags=int(fl[0]), z=z[0], rows=np.stack(rows),
                       shrows=np.stack(shrows) if NS else None, y=y)
     return out

@@ -35,18 +35,20 @@ def _resident_y(layer, cfg, xd, ws):
     return y.cpu().numpy()
 
 
-def _oracle_counts(sh, x):
+def _oracle_counts(sh, x, topp=0.0):
     """Positions routed to each expert, from the oracle's router (the same seeded router weights and bias)."""
-    ids, _, _ = O.route(O.Cfg.of(sh), O.router_logits(x, synth.router_weights(sh, 0)), synth.router_bias(sh, 0))
-    return np.bincount(ids.ravel(), minlength=sh.n_experts)
+    ids, _, _ = O.route(O.Cfg.of(sh, topp=topp), O.router_logits(x, synth.router_weights(sh, 0)),
+                        synth.router_bias(sh, 0))
+    ids = ids.ravel()
+    return np.bincount(ids[ids >= 0], minlength=sh.n_experts)
 
 
-def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False, set_usage=None):
+def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False, set_usage=None, topp=0.0):
     """pins: {step: n_pin} pin calls made before that step; set_usage: {step: usage} loaded before that step
     into both the cache and the simulator; usage_check: record usage in the simulator from the oracle's
     routing and compare it with the cache's at every pin."""
     sh = layer.shape
-    cfg = config_of(sh, gemm_min, layer.weight_bits, layer.group_size)
+    cfg = config_of(sh, gemm_min, layer.weight_bits, layer.group_size, topp)
     Tmax = max(x.shape[0] for x in xs)
     cache = moe.ExpertCache(cfg, n_slots, Tmax)
     sim = O.LRU(sh.n_experts, n_slots)
@@ -72,7 +74,7 @@ def _run_steps(layer, hx, n_slots, xs, gemm_min=0, pins=None, usage_check=False,
         needed = np.nonzero(hit >= 0)[0].astype(np.int32)
         r = sim.step(step, needed)
         if usage_check:
-            counts = _oracle_counts(sh, x)
+            counts = _oracle_counts(sh, x, topp)
             assert np.array_equal(np.nonzero(counts)[0], needed), step
             sim.record_usage(needed, counts[needed])
         assert np.array_equal(hit[needed].astype(bool), r["hit"]), step
@@ -121,6 +123,14 @@ def test_cache_tiny_mfma_and_ragged(tiny):
     layer, (hx, _) = tiny
     xs = [synth.hidden_states(synth.TINY, T, seed=1, step=s) for s, T in enumerate([8, 1, 16, 3, 8])]
     _run_steps(layer, hx, 4, xs, gemm_min=1)
+
+
+@pytest.mark.parametrize("gemm_min", [0, 1])
+def test_cache_tiny_topp(tiny, gemm_min):
+    """Adaptive top-p through the cache: only kept slots' experts are needed, usage counts kept positions."""
+    layer, (hx, _) = tiny
+    xs = [synth.hidden_states(synth.TINY, T, seed=7, step=s) for s, T in enumerate([8, 16, 3, 8, 1, 8])]
+    _run_steps(layer, hx, 4, xs, gemm_min=gemm_min, pins={3: 2}, usage_check=True, topp=0.6)
 
 
 @pytest.mark.parametrize("gemm_min", [0, 1])
