@@ -101,14 +101,16 @@ def _run(layer, x, gemm_min=0, sum_slot=-1, want_taps=True):
     return _np(y), {k: _np(v) for k, v in bufs.items()}
 
 
+@pytest.mark.parametrize("T", [16, 64])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("gemm_min", [1000, 1, 4])
-def test_grouped_layer_tiny_all_stages(G, gemm_min):
-    """Every tap bit-exact against the oracle with group scales, on the GEMV path, the MFMA path and a mix."""
+def test_grouped_layer_tiny_all_stages(G, gemm_min, T):
+    """Every tap bit-exact against the oracle with group scales, on the GEMV path, the MFMA path (T = 64: buckets
+    past one 32-position tile) and a mix."""
     layer, ref = _tiny(G)
     sh = synth.TINY
     K = sh.top_k
-    x = synth.hidden_states(sh, 16, seed=31)
+    x = synth.hidden_states(sh, T, seed=31)
     slot = 6
     y, tp = _run(layer, x, gemm_min, sum_slot=slot)
     yr, tr = O.layer_forward(O.Cfg.of(sh, group=G), x, ref)

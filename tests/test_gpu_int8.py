@@ -99,7 +99,7 @@ def _run(layer, x, gemm_min=0, sum_slot=-1, want_taps=True):
     return _np(y), {k: _np(v) for k, v in bufs.items()}
 
 
-@pytest.mark.parametrize("T", [8, 16])
+@pytest.mark.parametrize("T", [8, 16, 64])
 @pytest.mark.parametrize("gemm_min", [1000, 1, 4])
 def test_int8_layer_tiny_all_stages(tiny8, tiny8_ref, gemm_min, T):
     """Every tap bit-exact against the oracle with int8 experts: block sums of int8 x int8 are exact in int32

@@ -204,13 +204,14 @@ def _run_layer(layer, shape, x, gemm_min=0, sum_slot=-1, want_taps=True):
     return _np(y), {k: _np(v) for k, v in bufs.items()}
 
 
-@pytest.mark.parametrize("T", [8, 16])
+@pytest.mark.parametrize("T", [8, 16, 64])
 @pytest.mark.parametrize("gemm_min", [1000, 1, 4])
 def test_layer_tiny_all_stages(tiny_gpu, tiny_ref, gemm_min, T):
     """Every tap bit-exact against the oracle; the GEMV path (gemm_min=1000, buckets split into chunks of up to 4
     tokens), the MFMA path (gemm_min=1) and a mix give the same bits. The tiny shape has one block per
     accumulation class in gate/up and four empty classes in down; T=8 runs the few-bucket GEMV depth, T=16 the
-    many-bucket one."""
+    many-bucket one. T=64 gives buckets of up to 38 positions: MFMA tiles that are full, part-filled and a
+    second tile with a ragged tail."""
     sh = synth.TINY
     K = sh.top_k
     x = synth.hidden_states(sh, T)
