@@ -35,6 +35,7 @@ struct DispatchArgs {
   int32_t* gemv;
   int32_t* tiles;
   int32_t* pos_token;
+  int32_t shared_in_lists;  // 0: the shared experts run ahead of dispatch (launch_shared_setup)
   Meta* meta;
 };
 
@@ -126,17 +127,19 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
         nu += __popcll(mask);
       }
       for (int u = nu + lane; u < E; u += 64) a.unique[u] = -1;
-      for (int s = lane; s < a.NS; s += 64) {
-        a.bk_e[nu + s] = E + s;
-        a.bk_p0[nu + s] = TK + s * a.T;
-        a.bk_n[nu + s] = a.T;
+      if (a.shared_in_lists) {
+        for (int s = lane; s < a.NS; s += 64) {  // shared bucket s sits at index E + s
+          a.bk_e[E + s] = E + s;
+          a.bk_p0[E + s] = TK + s * a.T;
+          a.bk_n[E + s] = a.T;
+        }
       }
       if (lane == 0) s_nu = nu;
     }
     __syncthreads();
     if (wave == 0) {
       const int nu = s_nu;
-      const int nbk = nu + a.NS;
+      const int nbk = nu + (a.shared_in_lists ? a.NS : 0);  // list entry b >= nu: shared bucket E + b - nu
       int ng = 0, nt = 0;
       for (int bb = 0; bb < nbk; bb += 64) {
         int b = bb + lane;
@@ -151,8 +154,9 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
           if (lane >= o) incg += v;
         }
         const int exg = ng + incg - nch;
+        const int bi = b < nu ? b : E + (b - nu);
         for (int q = 0; q < nch; ++q) {
-          a.gemv[2 * (exg + q)] = b;
+          a.gemv[2 * (exg + q)] = bi;
           a.gemv[2 * (exg + q) + 1] = q * kGemvMaxN;
         }
         ng += __shfl(incg, 63);
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
         }
         int ex = nt + inc - ntile;
         for (int q = 0; q < ntile; ++q) {
-          a.tiles[2 * (ex + q)] = b;
+          a.tiles[2 * (ex + q)] = bi;
           a.tiles[2 * (ex + q) + 1] = q * a.tok_tile;
         }
         nt += __shfl(inc, 63);
@@ -181,10 +185,40 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
   }
 }
 
+// Shared experts (always on, every token) do not depend on routing: their
+// bucket entries (index E + s, positions TK + s*T .. +T) and MFMA tiles are
+// written here, so their expert work can start as soon as Q8_0(x) exists.
+__global__ __launch_bounds__(64) void k_shared_setup(int32_t* __restrict__ bk_e, int32_t* __restrict__ bk_p0,
+                                                     int32_t* __restrict__ bk_n, int32_t* __restrict__ tiles,
+                                                     Meta* __restrict__ meta, int E, int NS, int T, int TK,
+                                                     int tok_tile) {
+  const int per = (T + tok_tile - 1) / tok_tile;
+  for (int s = threadIdx.x; s < NS; s += 64) {
+    bk_e[E + s] = E + s;
+    bk_p0[E + s] = TK + s * T;
+    bk_n[E + s] = T;
+  }
+  for (int i = threadIdx.x; i < NS * per; i += 64) {
+    tiles[2 * i] = E + i / per;
+    tiles[2 * i + 1] = (i % per) * tok_tile;
+  }
+  if (threadIdx.x == 0) meta->n_tiles_sh = NS * per;
+}
+
+hipError_t launch_shared_setup(const moe_config& c, int T, int tok_tile, const Layout& L, char* ws, hipStream_t st) {
+  if (c.n_shared <= 0 || T <= 0) return hipSuccess;
+  k_shared_setup<<<1, 64, 0, st>>>(reinterpret_cast<int32_t*>(ws + L.bk_e), reinterpret_cast<int32_t*>(ws + L.bk_p0),
+                                   reinterpret_cast<int32_t*>(ws + L.bk_n), reinterpret_cast<int32_t*>(ws + L.tiles_sh),
+                                   reinterpret_cast<Meta*>(ws + L.meta), c.n_experts, c.n_shared, T, T * c.top_k,
+                                   tok_tile);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
                            const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
-                           int32_t* unique, int32_t* nunique, hipStream_t st) {
+                           int32_t* unique, int32_t* nunique, hipStream_t st, bool shared_in_lists) {
   DispatchArgs a;
+  a.shared_in_lists = shared_in_lists ? 1 : 0;
   a.ids = ids;
   a.T = T;
   a.K = c.top_k;

@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
                         int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
-                        hipStream_t st) {
+                        hipStream_t st, hipEvent_t after_router) {
   if (q8_done) *q8_done = false;
   if (T <= 0) return hipSuccess;
   const int H = c.hidden, E = c.n_experts;
@@ -353,6 +353,10 @@ hipError_t launch_route(const float* x, int T, const moe_config& c, const float*
     else k_router_mfma<1, 4, 1, false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
   }
   if (q8_done && qx_perm) *q8_done = true;
+  if (after_router) {  // x and its Q8_0 codes are ready here
+    const hipError_t e = hipEventRecord(after_router, st);
+    if (e != hipSuccess) return e;
+  }
   if (mark) mark(mark_call, 1, st);
   k_topk<<<T, 256, 0, st>>>(part, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, c.topp, ids,
                             w, flags);

@@ -336,7 +336,7 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
         nb.push_back(counts[needed[P.order[q]]]);
       }
       for (int s = 0; s < NS; ++s) {
-        bk.push_back(nu + s);
+        bk.push_back(E + s);  // shared bucket s sits at index E + s
         nb.push_back(T);
       }
     } else {
