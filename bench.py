@@ -17,8 +17,8 @@ Weights rotate over --copies layer copies (different seeds) and every step
 uses fresh tokens, so the 256 MB last-level cache cannot serve weights from a
 previous step.
 
-Prints one JSON line (rank 0). Multi-GPU runs are not supported: this build
-measures one GPU.
+Prints one JSON line (rank 0). Multi-GPU runs are not supported: the library
+runs on one GPU.
 """
 from __future__ import annotations
 
@@ -361,7 +361,7 @@ def main():
         pmc_summary(*args.pmc_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (--gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.calibrate:
         calibrate()

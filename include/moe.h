@@ -88,7 +88,7 @@ extern "C" {
 #define MOE_E_WORKSPACE (-3)   /* workspace missing, misaligned or too small */
 #define MOE_E_HIP (-4)         /* a HIP runtime call failed */
 #define MOE_E_NOMEM (-5)       /* allocation failed (expert cache only) */
-#define MOE_E_UNSUPPORTED (-6) /* valid request this build does not handle */
+#define MOE_E_UNSUPPORTED (-6) /* valid request this library version does not handle */
 #define MOE_E_ARG (-7)         /* invalid scalar argument */
 
 /* Router flag bits written per token (moe_router near_tie output). */
