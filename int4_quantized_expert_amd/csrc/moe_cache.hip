@@ -46,7 +46,11 @@ struct moe_expert_cache {
   moe_config cfg;
   int E = 0, S = 0, max_tokens = 0, device = -1;
   size_t b13 = 0, bs13 = 0, b2 = 0, bs2 = 0;  // bytes of one expert's w13, s13, w2, s2
-  uint8_t* pool_w13 = nullptr;
+  // one HBM pool of S slots, each [w13 | s13 | w2 | s2] (every part a multiple
+  // of 256 bytes), so a host copy laid out the same way moves in one transfer
+  uint8_t* pool = nullptr;
+  size_t slot_bytes = 0;
+  uint8_t* pool_w13 = nullptr;  // slot 0's parts; slot s at + s * slot_bytes
   float* pool_s13 = nullptr;
   uint8_t* pool_w2 = nullptr;
   float* pool_s2 = nullptr;
@@ -73,10 +77,7 @@ namespace {
 
 void cache_release(moe_expert_cache* c) {
   if (!c) return;
-  hipFree(c->pool_w13);
-  hipFree(c->pool_s13);
-  hipFree(c->pool_w2);
-  hipFree(c->pool_s2);
+  hipFree(c->pool);
   hipFree(c->d_slotmap);
   hipFree(c->d_lists);
   hipHostFree(c->h_back);
@@ -194,6 +195,25 @@ size_t build_lists(const std::vector<int32_t>& buckets, const std::vector<int32_
   return 2 + 2 * (size_t)ng + 2 * (size_t)nt;
 }
 
+// Host -> slot s copy of routed expert ex on the copy stream: one transfer when
+// the caller's four parts lie back to back in the slot's order (w13, s13, w2,
+// s2), as moe_host_experts allows; four transfers otherwise.
+hipError_t copy_expert(moe_expert_cache* c, const moe_host_experts* host, int ex, int s, hipStream_t copy) {
+  uint8_t* dst = c->pool + c->slot_bytes * (size_t)s;
+  const char* w13 = static_cast<const char*>(static_cast<const void*>(host->w13[ex]));
+  const char* s13 = static_cast<const char*>(static_cast<const void*>(host->s13[ex]));
+  const char* w2 = static_cast<const char*>(static_cast<const void*>(host->w2[ex]));
+  const char* s2 = static_cast<const char*>(static_cast<const void*>(host->s2[ex]));
+  c->bytes_h2d += (int64_t)c->slot_bytes;
+  if (s13 == w13 + c->b13 && w2 == s13 + c->bs13 && s2 == w2 + c->b2)
+    return hipMemcpyAsync(dst, w13, c->slot_bytes, hipMemcpyHostToDevice, copy);
+  hipError_t r = hipMemcpyAsync(dst, w13, c->b13, hipMemcpyHostToDevice, copy);
+  if (r == hipSuccess) r = hipMemcpyAsync(dst + c->b13, s13, c->bs13, hipMemcpyHostToDevice, copy);
+  if (r == hipSuccess) r = hipMemcpyAsync(dst + c->b13 + c->bs13, w2, c->b2, hipMemcpyHostToDevice, copy);
+  if (r == hipSuccess) r = hipMemcpyAsync(dst + c->b13 + c->bs13 + c->b2, s2, c->bs2, hipMemcpyHostToDevice, copy);
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,10 +250,14 @@ int32_t moe_expert_cache_create(const moe_config* cfg, int32_t n_slots, int32_t 
   const int64_t phases = 1 + (buckets + std::max(1, n_slots / 2) - 1) / std::max(1, n_slots / 2);
   c->list_ints = (size_t)(per_phase * phases);
   hipError_t e = hipGetDevice(&c->device);
-  if (e == hipSuccess) e = hipMalloc(&c->pool_w13, c->b13 * n_slots);
-  if (e == hipSuccess) e = hipMalloc(&c->pool_s13, c->bs13 * n_slots);
-  if (e == hipSuccess) e = hipMalloc(&c->pool_w2, c->b2 * n_slots);
-  if (e == hipSuccess) e = hipMalloc(&c->pool_s2, c->bs2 * n_slots);
+  c->slot_bytes = c->b13 + c->bs13 + c->b2 + c->bs2;
+  if (e == hipSuccess) e = hipMalloc(&c->pool, c->slot_bytes * n_slots);
+  if (e == hipSuccess) {
+    c->pool_w13 = c->pool;
+    c->pool_s13 = reinterpret_cast<float*>(c->pool + c->b13);
+    c->pool_w2 = c->pool + c->b13 + c->bs13;
+    c->pool_s2 = reinterpret_cast<float*>(c->pool + c->b13 + c->bs13 + c->b2);
+  }
   if (e == hipSuccess) e = hipMalloc(&c->d_slotmap, sizeof(int32_t) * c->E);
   if (e == hipSuccess) e = hipMalloc(&c->d_lists, sizeof(int32_t) * c->list_ints);
   if (e == hipSuccess) e = hipHostMalloc(&c->h_back, sizeof(int32_t) * (2 * c->E + 1), hipHostMallocDefault);
@@ -263,7 +287,7 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev != c->device) return MOE_E_ARG;
   WeightView wv{c->pool_w13, c->pool_s13, c->pool_w2, c->pool_s2, res->sh_w13, res->sh_s13, res->sh_w2, res->sh_s2,
-                c->d_slotmap};
+                c->d_slotmap, c->slot_bytes};
   Fwd f;
   int rc = fwd_setup(cfg, wv, T, ws, ws_bytes, nullptr, &f);
   if (rc) return rc;
@@ -371,16 +395,7 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
       const int q0 = P.n_hits + (ph - 1) * B, q1 = std::min(nu, q0 + B);
       for (int q = q0; q < q1 && r == hipSuccess; ++q) {
         const int i = P.order[q], ex = needed[i], s = P.slot[i];
-        r = hipMemcpyAsync(c->pool_w13 + c->b13 * s, host->w13[ex], c->b13, hipMemcpyHostToDevice, copy);
-        if (r == hipSuccess)
-          r = hipMemcpyAsync(reinterpret_cast<char*>(c->pool_s13) + c->bs13 * s, host->s13[ex], c->bs13,
-                             hipMemcpyHostToDevice, copy);
-        if (r == hipSuccess)
-          r = hipMemcpyAsync(c->pool_w2 + c->b2 * s, host->w2[ex], c->b2, hipMemcpyHostToDevice, copy);
-        if (r == hipSuccess)
-          r = hipMemcpyAsync(reinterpret_cast<char*>(c->pool_s2) + c->bs2 * s, host->s2[ex], c->bs2,
-                             hipMemcpyHostToDevice, copy);
-        c->bytes_h2d += (int64_t)(c->b13 + c->bs13 + c->b2 + c->bs2);
+        r = copy_expert(c, host, ex, s, copy);
       }
       if (r == hipSuccess) r = hipEventRecord(c->ev_copied[ph], copy);
       ++copied;
@@ -492,15 +507,7 @@ int32_t moe_expert_cache_pin_hottest(moe_expert_cache* c, int32_t n_pin, const m
     }
     c->expert_in[s] = e;
     c->slot_of[e] = s;
-    r = hipMemcpyAsync(c->pool_w13 + c->b13 * s, host->w13[e], c->b13, hipMemcpyHostToDevice, copy);
-    if (r == hipSuccess)
-      r = hipMemcpyAsync(reinterpret_cast<char*>(c->pool_s13) + c->bs13 * s, host->s13[e], c->bs13,
-                         hipMemcpyHostToDevice, copy);
-    if (r == hipSuccess) r = hipMemcpyAsync(c->pool_w2 + c->b2 * s, host->w2[e], c->b2, hipMemcpyHostToDevice, copy);
-    if (r == hipSuccess)
-      r = hipMemcpyAsync(reinterpret_cast<char*>(c->pool_s2) + c->bs2 * s, host->s2[e], c->bs2,
-                         hipMemcpyHostToDevice, copy);
-    c->bytes_h2d += (int64_t)(c->b13 + c->bs13 + c->b2 + c->bs2);
+    r = copy_expert(c, host, e, s, copy);
   }
   c->n_pinned = n_pin;
   if (r == hipSuccess) r = hipStreamSynchronize(copy);

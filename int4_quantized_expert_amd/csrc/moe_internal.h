@@ -56,6 +56,9 @@ struct WeightView {
   const uint8_t* sh_w2;
   const float* sh_s2;
   const int32_t* slotmap;  // nullable: routed expert -> index into w13/s13/w2/s2
+  // bytes between consecutive routed experts (slots) in all four arrays; 0:
+  // each array packs its experts back to back (stride = one expert's part)
+  size_t slot_stride = 0;
 };
 
 struct ExpertArgs {
@@ -201,25 +204,27 @@ __device__ __forceinline__ float swiglu_f(float g, float u) {
   return (float)(((double)g * (double)u) / (1.0 + exp(-(double)g)));
 }
 
+// Routed expert ex (through the slot map when one is given) or shared expert
+// ex - E; bytes / n: one expert's part of that array.
+__device__ __forceinline__ size_t routed_off(const WeightView& v, int ex, size_t part_bytes) {
+  const int s = v.slotmap ? v.slotmap[ex] : ex;
+  return (size_t)s * (v.slot_stride ? v.slot_stride : part_bytes);
+}
 __device__ __forceinline__ const uint8_t* expert_w13(const WeightView& v, int ex, int E, size_t bytes) {
   if (ex >= E) return v.sh_w13 + (size_t)(ex - E) * bytes;
-  int s = v.slotmap ? v.slotmap[ex] : ex;
-  return v.w13 + (size_t)s * bytes;
+  return v.w13 + routed_off(v, ex, bytes);
 }
-__device__ __forceinline__ const float* expert_s13(const WeightView& v, int ex, int E, int n) {
+__device__ __forceinline__ const float* expert_s13(const WeightView& v, int ex, int E, size_t n) {
   if (ex >= E) return v.sh_s13 + (size_t)(ex - E) * n;
-  int s = v.slotmap ? v.slotmap[ex] : ex;
-  return v.s13 + (size_t)s * n;
+  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s13) + routed_off(v, ex, n * 4));
 }
 __device__ __forceinline__ const uint8_t* expert_w2(const WeightView& v, int ex, int E, size_t bytes) {
   if (ex >= E) return v.sh_w2 + (size_t)(ex - E) * bytes;
-  int s = v.slotmap ? v.slotmap[ex] : ex;
-  return v.w2 + (size_t)s * bytes;
+  return v.w2 + routed_off(v, ex, bytes);
 }
-__device__ __forceinline__ const float* expert_s2(const WeightView& v, int ex, int E, int n) {
+__device__ __forceinline__ const float* expert_s2(const WeightView& v, int ex, int E, size_t n) {
   if (ex >= E) return v.sh_s2 + (size_t)(ex - E) * n;
-  int s = v.slotmap ? v.slotmap[ex] : ex;
-  return v.s2 + (size_t)s * n;
+  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(v.s2) + routed_off(v, ex, n * 4));
 }
 
 // ------------------------------------------------------------ launchers

@@ -212,8 +212,11 @@ class PinnedBlock:
             self.ptr = None
 
 
-def host_experts(layer):
-    """Pinned host copies of a GpuLayer's routed experts (device layout), as (moe.HostExperts, keep-alive)."""
+def host_experts(layer, order=(0, 1, 2, 3)):
+    """Pinned host copies of a GpuLayer's routed experts (device layout), as (moe.HostExperts, keep-alive).
+
+    Each expert's parts (0 w13, 1 s13, 2 w2, 3 s2) lie back to back in `order`; the default is the cache
+    slot's own order, which lets a miss move in one transfer."""
     import torch
 
     import int4_quantized_expert_amd as moe
@@ -223,11 +226,11 @@ def host_experts(layer):
     sizes = [t[0].numel() * t.element_size() for t in parts]
     per = sum(sizes)
     blk = PinnedBlock(per * E)
-    ptrs = [[], [], [], []]
+    ptrs = [[None] * E for _ in range(4)]
     for e in range(E):
         off = e * per
-        for k, t in enumerate(parts):
-            blk.fill_from_device(off, t[e])
-            ptrs[k].append(blk.ptr + off)
+        for k in order:
+            blk.fill_from_device(off, parts[k][e])
+            ptrs[k][e] = blk.ptr + off
             off += sizes[k]
     return moe.HostExperts(*ptrs), blk

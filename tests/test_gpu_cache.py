@@ -125,6 +125,16 @@ def test_cache_tiny_mfma_and_ragged(tiny):
     _run_steps(layer, hx, 4, xs, gemm_min=1)
 
 
+def test_cache_tiny_parts_not_in_slot_order(tiny):
+    """Host parts in another order (w2, s2, w13, s13): misses move in four transfers; results and counts as
+    with one transfer."""
+    layer, _ = tiny
+    hx, _keep = host_experts(layer, order=(2, 3, 0, 1))
+    xs = [synth.hidden_states(synth.TINY, T, seed=8, step=s) for s, T in enumerate([8, 16, 3, 8])]
+    _run_steps(layer, hx, 4, xs, gemm_min=0)
+    _run_steps(layer, hx, 4, xs, gemm_min=1, pins={2: 2}, usage_check=True)
+
+
 @pytest.mark.parametrize("gemm_min", [0, 1])
 def test_cache_tiny_topp(tiny, gemm_min):
     """Adaptive top-p through the cache: only kept slots' experts are needed, usage counts kept positions."""
