@@ -170,14 +170,18 @@ def cpu_baseline(shape, x, seconds, seed, weight_bits=4, group_size=0, topp=0.0)
                        f"{t_oracle:.1f} s of single-threaded oracle time (weight generation excluded)")
 
 
-KERNEL_SRC = os.path.join(ROOT, "int4_quantized_expert_amd", "csrc", "k_expert.hip")
+# sources the expert kernels are compiled from (their HBM counters go stale when either changes)
+KERNEL_SRC = [os.path.join(ROOT, "int4_quantized_expert_amd", "csrc", f) for f in ("k_expert.hip", "moe_internal.h")]
 CAL_BYTES = 1 << 30
 
 
 def source_sha256():
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def calibrate():
