@@ -198,9 +198,11 @@ __global__ __launch_bounds__(64) void k_router_mfma(const float* __restrict__ x,
 // groups with the highest (score desc, index asc) are kept; the K experts of
 // the kept groups by (c desc, index asc) are chosen, slot k = rank k; weights
 // are the unbiased s normalised in fp64 (ascending slots) and scaled by
-// routed_scaling_factor. Ranks are counted against the LDS copies of the
-// scores, so the whole selection is a few synchronised passes rather than a
-// chain of wave-wide reductions. Near-tie flags: kept/dropped group boundary,
+// routed_scaling_factor. Group top-2 sums are shuffle reductions over aligned
+// lane groups (a serial scan when the group size is not a power of two up to
+// 64); groups are ranked against their LDS copies; each expert of the kept
+// groups counts, over a compacted copy of their scores, the ones that beat it.
+// Near-tie flags: kept/dropped group boundary,
 // chosen/next expert boundary, adjacent chosen experts (differences < 1e-6).
 // Adaptive top-p (0 < topp < 1): one lane visits the K slots by q = s / sum
 // descending (lower slot first on equal q) and keeps each while the fp64 sum
@@ -211,7 +213,6 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
                                               float* __restrict__ w, uint8_t* __restrict__ flags) {
   __shared__ float s_s[kMaxExperts];
   __shared__ float s_c[kMaxExperts];
-  __shared__ float s_m[kMaxExperts];  // c inside kept groups, -inf elsewhere
   __shared__ float s_gs[kMaxGroups];
   __shared__ float s_grank[kMaxGroups];  // group scores by rank
   __shared__ int s_kept[kMaxGroups];
@@ -235,7 +236,24 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
   }
   __syncthreads();
   const int n = E / G;
-  if (tid < G) {
+  const int lane = tid & 63, wave = tid >> 6;
+  if (n <= 64 && (n & (n - 1)) == 0) {
+    // groups of n = 2^j experts are aligned runs of n lanes: the group top-2 is
+    // a shuffle reduction (largest, then the largest with the first lane that
+    // holds the largest taken out, so a repeated maximum counts twice)
+    const uint64_t gmask = n == 64 ? ~0ull : ((1ull << n) - 1) << (lane & ~(n - 1));
+    for (int base = 0; base < E; base += 256) {
+      const int e = base + tid;
+      const float v = e < E ? s_c[e] : -INFINITY;
+      float m1 = v;
+      for (int o = n >> 1; o >= 1; o >>= 1) m1 = fmaxf(m1, __shfl_xor(m1, o));
+      const uint64_t eq = __ballot(v == m1) & gmask;
+      const int first = __ffsll((unsigned long long)eq) - 1;
+      float m2 = lane == first ? -INFINITY : v;
+      for (int o = n >> 1; o >= 1; o >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, o));
+      if (e < E && (lane & (n - 1)) == 0) s_gs[e / n] = __fadd_rn(m1, m2);
+    }
+  } else if (tid < G) {
     float top1 = -INFINITY, top2 = -INFINITY;
     for (int e = tid * n; e < (tid + 1) * n; ++e) {
       const float v = s_c[e];
@@ -260,18 +278,41 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
     s_grank[rk] = v;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) s_m[e] = s_kept[e / n] ? s_c[e] : -INFINITY;
+  // experts of the kept groups, best first by (c desc, index asc): their c are
+  // compacted in expert order (kept groups ascending), then each candidate
+  // counts the entries that beat it, a higher c or an equal c earlier in the
+  // array, with 16-byte broadcast reads and no branches. Rank k is slot k;
+  // rank K is the best expert left out.
+  __shared__ int s_kpos[kMaxGroups];  // position of a kept group among the kept groups
+  __shared__ __align__(16) float s_cand[kMaxExperts];
+  if (wave == 0) {
+    const bool kg = lane < G && s_kept[lane];
+    const uint64_t km = __ballot(kg);
+    if (lane < G) s_kpos[lane] = __popcll(km & ((1ull << lane) - 1));
+  }
+  __syncthreads();
+  const int nc = KG * n;  // candidates
+  for (int e = tid; e < E; e += 256) {
+    const int g = e / n;
+    if (s_kept[g]) s_cand[s_kpos[g] * n + (e - g * n)] = s_c[e];
+  }
+  for (int j = nc + tid; j < ((nc + 3) & ~3); j += 256) s_cand[j] = -INFINITY;  // pad to whole float4
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
-    if (!s_kept[e / n]) continue;
+    const int g = e / n;
+    if (!s_kept[g]) continue;
     const float v = s_c[e];
+    const int me = s_kpos[g] * n + (e - g * n);
     int rk = 0;
-    for (int g2 = 0; g2 < G; ++g2) {
-      if (!s_kept[g2]) continue;
-      for (int e2 = g2 * n; e2 < (g2 + 1) * n; ++e2) {
-        const float o = s_m[e2];
-        rk += (o > v) || (o == v && e2 < e);
-      }
+    const float4* c4 = reinterpret_cast<const float4*>(s_cand);
+#pragma unroll 8
+    for (int j4 = 0; j4 < (nc + 3) >> 2; ++j4) {
+      const float4 o = c4[j4];
+      const int j = 4 * j4;
+      rk += (o.x > v) | ((o.x == v) & (j + 0 < me));
+      rk += (o.y > v) | ((o.y == v) & (j + 1 < me));
+      rk += (o.z > v) | ((o.z == v) & (j + 2 < me));
+      rk += (o.w > v) | ((o.w == v) & (j + 3 < me));
     }
     if (rk < K) {
       s_sel[rk] = e;
