@@ -151,7 +151,8 @@ static hipError_t get_helper(hipStream_t st, Helper* out) {
 // ------------------------------------------------------------------ profiling
 // Per call: 9 events on the caller's stream (start, after router, top-k,
 // dispatch, q8-x, GEMV gate-up, GEMV down, after the join, end) and 3 on the
-// helper stream (MFMA chain start, after gate-up, after down).
+// helper stream around the routed tiles' MFMA gate-up and down launches (the
+// shared experts' tiles, which run ahead of dispatch, are not timed).
 constexpr int kProfEv = 12;
 // stage -> (first event, second event): main-stream stages, then the MFMA chain, then combine
 static const int kStageEv[MOE_N_STAGES][2] = {{0, 1}, {1, 2}, {2, 3}, {3, 4}, {4, 5},
@@ -409,7 +410,6 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   if (e == hipSuccess && fork) {
     if (early) {
       e = hipStreamWaitEvent(hp.side, hp.fork, 0);
-      prof_mark(call, 9, hp.side);
       if (e == hipSuccess) e = launch_shared_setup(*f.cfg, f.T, f.tok_tile, f.L, f.wsb, hp.side);
       if (e == hipSuccess) e = launch_tile_gather(f.a, f.grid_tiles_sh, f.tok_tile, tiles_sh, n_tiles_sh, hp.side);
       if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles_sh, f.tok_tile / 32, tiles_sh, n_tiles_sh, hp.side);
@@ -419,9 +419,9 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
     } else {
       e = hipEventRecord(hp.fork, stream);
       if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.fork, 0);
-      prof_mark(call, 9, hp.side);
     }
     if (e == hipSuccess) e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, hp.side);
+    prof_mark(call, 9, hp.side);  // the MFMA stages time the routed tiles' gate/up and down launches
     if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 10, hp.side);
     if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
