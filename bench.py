@@ -113,11 +113,11 @@ def routing_stats(moe, cfg, layer, x_dev, ws, gemm_min):
     counts = outs[0].cpu().numpy()
     gm = gemm_min if gemm_min > 0 else DEFAULT_GEMM_MIN
     nz = counts[counts > 0]
-    return dict(U=int(nz.size), gemv_experts=int((nz < gm).sum()) + (1 if T < gm else 0),
-                mfma_experts=int((nz >= gm).sum()) + (1 if T >= gm else 0),
-                gemv_tokens=int(nz[nz < gm].sum()) + (T if T < gm else 0),
-                mfma_tokens=int(nz[nz >= gm].sum()) + (T if T >= gm else 0),
-                routed_mfma_tokens=int(nz[nz >= gm].sum()), counts=counts)
+    NS = cfg.n_shared  # each shared expert is one bucket of all T tokens
+    return dict(U=int(nz.size), gemv_experts=int((nz < gm).sum()) + (NS if T < gm else 0),
+                mfma_experts=int((nz >= gm).sum()) + (NS if T >= gm else 0),
+                gemv_tokens=int(nz[nz < gm].sum()) + (NS * T if T < gm else 0),
+                mfma_tokens=int(nz[nz >= gm].sum()) + (NS * T if T >= gm else 0), counts=counts)
 
 
 SAMPLE_TOKENS = 8  # tokens of the CPU sample (each distinct expert they route to is generated once)
@@ -445,18 +445,18 @@ def main():
     layer_bytes = (E * H * 4 + E * 4) + (U + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 4
     stage_ms = prof_all.mean(0)
     if args.workload == "prefill":
-        # the timed launch is the routed tiles' gate/up (the shared experts' tiles run ahead of dispatch)
-        ops = np.array([2.0 * s["routed_mfma_tokens"] * 2 * I * H for s in stats])
+        # the timed launch is the MFMA gate/up of every bucket from the threshold up, the shared experts' included
+        ops = np.array([2.0 * s["mfma_tokens"] * 2 * I * H for s in stats])
         kt = prof[:, kidx] / 1e3
         achieved = float(np.mean(ops / kt) / 1e12)
         # the exact block epilogue: one int->fp32 conversion and one fused multiply-add per (row, token, block)
-        valu = np.array([2.0 * s["routed_mfma_tokens"] * 2 * I * (H // 32) for s in stats])
+        valu = np.array([2.0 * s["mfma_tokens"] * 2 * I * (H // 32) for s in stats])
         valu_frac = float(np.mean(valu / kt) / VALU_PEAK_OPS)
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
                     frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
                     kernel="k_" + kname,
                     kernel_ms=round(float(kt.mean() * 1e3), 4),
-                    per_unit="2*2I*H int8 ops per (token, routed expert) in the routed MFMA gate/up launch",
+                    per_unit="2*2I*H int8 ops per (token, expert) in the MFMA gate/up launch",
                     valu_epilogue=dict(ops_per_launch=float(valu.mean()), peak=VALU_PEAK_OPS, frac=round(valu_frac, 4),
                                        per_unit="2 VALU lane-ops (convert + FMA) per (row, token, 32-block)"))
     else:

@@ -7,7 +7,10 @@
 // the counts are exact and order-free) and its exclusive prefix sum; wavefront
 // w then owns expert e = 4*block + w and walks the slots in ascending order,
 // placing its matches with a ballot prefix count — a stable counting sort
-// with no cross-workgroup synchronization and no float atomics. Workgroup 0
+// with no cross-workgroup synchronization and no float atomics. Up to
+// kDispLdsSlots slots the ids are copied into LDS as 16-bit values while the
+// histogram is built, so each wavefront's walk reads LDS instead of issuing a
+// dependent global load per 64 slots. Workgroup 0
 // additionally emits the bucket tables the expert kernels consume: the unique
 // expert list, the GEMV work list ((bucket, first token) pairs in chunks of up
 // to kGemvMaxN tokens, for buckets below the MFMA threshold) and the MFMA tile list
@@ -35,22 +38,38 @@ struct DispatchArgs {
   int32_t* gemv;
   int32_t* tiles;
   int32_t* pos_token;
-  int32_t shared_in_lists;  // 0: the shared experts run ahead of dispatch (launch_shared_setup)
   Meta* meta;
 };
 
+// T*K up to this: ids staged in LDS as 16-bit values (48 KB, with the 12 KB of tables under 64 KB)
+constexpr int kDispLdsSlots = 24576;
+
+template <bool LDS>
 __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
   __shared__ int hist[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int uq[kMaxExperts];
   __shared__ int wsum[4];
+  extern __shared__ int16_t s_ids[];  // LDS: T*K ids, -1 for a slot in no bucket (E <= kMaxExperts < 2^15)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, TK = a.T * a.K;
   for (int e = tid; e < E; e += 256) hist[e] = 0;
   __syncthreads();
-  for (int j = tid; j < TK; j += 256) {
-    const int id = a.ids[j];
-    if ((unsigned)id < (unsigned)E) atomicAdd(&hist[id], 1);
+  constexpr int U = 16;  // loads issued before their ids are counted
+  for (int j0 = 0; j0 < TK; j0 += 256 * U) {
+    int idv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 256 * u + tid;
+      idv[u] = j < TK ? a.ids[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 256 * u + tid;
+      const bool in = (unsigned)idv[u] < (unsigned)E;
+      if (LDS && j < TK) s_ids[j] = (int16_t)(in ? idv[u] : -1);
+      if (in) atomicAdd(&hist[idv[u]], 1);
+    }
   }
   __syncthreads();
   // exclusive prefix sum over experts: 4 per thread, then a block scan
@@ -92,23 +111,32 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
       if (e == E - 1) a.offsets[E] = off[E];
     }
     const int end = pos + cnt;
-    for (int jb = 0; jb < TK && pos < end; jb += 64) {
-      int j = jb + lane;
-      bool m = (j < TK) && (a.ids[j] == e);
-      uint64_t mask = __ballot(m);
-      if (m) {
-        int p = pos + __popcll(mask & lt);
-        a.sorted[p] = j;
-        a.slotpos[j] = p;
-        a.pos_token[p] = j / a.K;
+    for (int jb = 0; jb < TK && pos < end; jb += 256) {
+      int idv[4];  // four groups of 64 slots read before they are used
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + 64 * u + lane;
+        idv[u] = j < TK ? (LDS ? (int)s_ids[j] : a.ids[j]) : -1;
       }
-      pos += __popcll(mask);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = jb + 64 * u + lane;
+        const bool m = idv[u] == e;
+        const uint64_t mask = __ballot(m);
+        if (m) {
+          const int p = pos + __popcll(mask & lt);
+          a.sorted[p] = j;
+          a.slotpos[j] = p;
+          a.pos_token[p] = j / a.K;
+        }
+        pos += __popcll(mask);
+      }
     }
   }
 
   if (blockIdx.x == 0) {
     for (int j = tid; j < TK; j += 256)
-      if ((unsigned)a.ids[j] >= (unsigned)E) a.slotpos[j] = -1;
+      if (LDS ? s_ids[j] < 0 : (unsigned)a.ids[j] >= (unsigned)E) a.slotpos[j] = -1;
     __shared__ int s_nu;
     if (wave == 0) {
       int nu = 0;
@@ -127,19 +155,17 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
         nu += __popcll(mask);
       }
       for (int u = nu + lane; u < E; u += 64) a.unique[u] = -1;
-      if (a.shared_in_lists) {
-        for (int s = lane; s < a.NS; s += 64) {  // shared bucket s sits at index E + s
-          a.bk_e[E + s] = E + s;
-          a.bk_p0[E + s] = TK + s * a.T;
-          a.bk_n[E + s] = a.T;
-        }
+      for (int s = lane; s < a.NS; s += 64) {  // shared bucket s sits at index E + s
+        a.bk_e[E + s] = E + s;
+        a.bk_p0[E + s] = TK + s * a.T;
+        a.bk_n[E + s] = a.T;
       }
       if (lane == 0) s_nu = nu;
     }
     __syncthreads();
     if (wave == 0) {
       const int nu = s_nu;
-      const int nbk = nu + (a.shared_in_lists ? a.NS : 0);  // list entry b >= nu: shared bucket E + b - nu
+      const int nbk = nu + a.NS;  // list entry b >= nu: shared bucket E + b - nu
       int ng = 0, nt = 0;
       for (int bb = 0; bb < nbk; bb += 64) {
         int b = bb + lane;
@@ -185,40 +211,10 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
   }
 }
 
-// Shared experts (always on, every token) do not depend on routing: their
-// bucket entries (index E + s, positions TK + s*T .. +T) and MFMA tiles are
-// written here, so their expert work can start as soon as Q8_0(x) exists.
-__global__ __launch_bounds__(64) void k_shared_setup(int32_t* __restrict__ bk_e, int32_t* __restrict__ bk_p0,
-                                                     int32_t* __restrict__ bk_n, int32_t* __restrict__ tiles,
-                                                     Meta* __restrict__ meta, int E, int NS, int T, int TK,
-                                                     int tok_tile) {
-  const int per = (T + tok_tile - 1) / tok_tile;
-  for (int s = threadIdx.x; s < NS; s += 64) {
-    bk_e[E + s] = E + s;
-    bk_p0[E + s] = TK + s * T;
-    bk_n[E + s] = T;
-  }
-  for (int i = threadIdx.x; i < NS * per; i += 64) {
-    tiles[2 * i] = E + i / per;
-    tiles[2 * i + 1] = (i % per) * tok_tile;
-  }
-  if (threadIdx.x == 0) meta->n_tiles_sh = NS * per;
-}
-
-hipError_t launch_shared_setup(const moe_config& c, int T, int tok_tile, const Layout& L, char* ws, hipStream_t st) {
-  if (c.n_shared <= 0 || T <= 0) return hipSuccess;
-  k_shared_setup<<<1, 64, 0, st>>>(reinterpret_cast<int32_t*>(ws + L.bk_e), reinterpret_cast<int32_t*>(ws + L.bk_p0),
-                                   reinterpret_cast<int32_t*>(ws + L.bk_n), reinterpret_cast<int32_t*>(ws + L.tiles_sh),
-                                   reinterpret_cast<Meta*>(ws + L.meta), c.n_experts, c.n_shared, T, T * c.top_k,
-                                   tok_tile);
-  return hipGetLastError();
-}
-
 hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
                            const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
-                           int32_t* unique, int32_t* nunique, hipStream_t st, bool shared_in_lists) {
+                           int32_t* unique, int32_t* nunique, hipStream_t st) {
   DispatchArgs a;
-  a.shared_in_lists = shared_in_lists ? 1 : 0;
   a.ids = ids;
   a.T = T;
   a.K = c.top_k;
@@ -239,7 +235,11 @@ hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int g
   a.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   a.pos_token = reinterpret_cast<int32_t*>(ws + L.pos_token);
   a.meta = reinterpret_cast<Meta*>(ws + L.meta);
-  k_dispatch<<<(c.n_experts + 3) / 4, 256, 0, st>>>(a);
+  const int64_t TK = (int64_t)T * c.top_k;
+  if (TK <= kDispLdsSlots)
+    k_dispatch<true><<<(c.n_experts + 3) / 4, 256, (size_t)TK * sizeof(int16_t), st>>>(a);
+  else
+    k_dispatch<false><<<(c.n_experts + 3) / 4, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -9,10 +9,12 @@
 // fixed and independent of the number of tokens or a token's place in the
 // batch, so a token routes identically alone or inside any batch: H is split
 // into 64 contiguous chunks; each chunk is accumulated by a fixed sequence of
-// fp64 MFMA steps of four products each; the 64 chunk sums are added in
-// ascending chunk order, starting from 0. One kernel writes the chunk partial
-// sums (token blocks x expert blocks x chunks, so even one token spreads over
-// 256 workgroups); the top-k kernel adds them in order. The logits agree with
+// fp64 MFMA steps of four products each; each run of four consecutive chunks
+// is added in ascending order, ((c0 + c1) + c2) + c3, giving 16 partial sums,
+// which are added in ascending order starting from 0. One kernel computes the
+// chunks (one wavefront each; token blocks x expert blocks x chunks, so even
+// one token spreads over 256 wavefronts) and writes the 16 partial sums; the
+// top-k kernel adds them. The logits agree with
 // an exact fp64 dot to far below fp32 resolution, so they round to the same
 // fp32 value except when the exact dot lies within ~1e-16 relative of a
 // rounding boundary.
@@ -24,7 +26,11 @@ namespace moe {
 
 #define CAS __attribute__((address_space(4)))
 
-constexpr int kRouterMfmaWideT = 256;  // from this batch size a router workgroup takes 32 tokens x 64 experts
+// Router tile per wavefront: 16 tokens x 64 experts; 32 x 64 from kRouterMfmaWideT tokens (weights read half
+// as often); 16 x 16 up to kRouterMfmaNarrowT tokens (four times the wavefronts for a small batch, measured
+// 13.3 -> 9.5 us at one token). The tile changes neither the MFMA steps of a (token, expert) nor their order.
+constexpr int kRouterMfmaWideT = 256;
+constexpr int kRouterMfmaNarrowT = 32;
 
 __device__ __forceinline__ uint32_t pack4q(int8_t a, int8_t b, int8_t c, int8_t d) {
   return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
@@ -89,7 +95,9 @@ __device__ __forceinline__ void q8_x_chunk(const float* __restrict__ x, int T, i
 // A workgroup (one wavefront) covers 16 * TB tokens x 16 * EB experts of one chunk.
 // Every (token, expert) result takes the same sequence of MFMA steps wherever
 // its token sits in the batch, so routing stays batch-invariant. Lanes past E
-// or T read a clamped valid row and store nothing.
+// or T read a clamped valid row and store nothing. A workgroup holds
+// kRouterWaves wavefronts on consecutive chunks; wavefronts 1.. leave their
+// sums in LDS and wavefront 0 adds them to its own in chunk order.
 typedef double v4d __attribute__((ext_vector_type(4)));
 
 // FULL: the chunk is whole groups of 16 h (H a multiple of 1024); the K walk
@@ -114,12 +122,15 @@ __device__ __forceinline__ void router_group_mfma(v4d (&acc)[TB][EB], const floa
 }
 
 template <int TB, int EB, int PD, bool FULL>
-__global__ __launch_bounds__(64) void k_router_mfma(const float* __restrict__ x, int T, int H,
-                                                    const float* __restrict__ Wr, int E, double* __restrict__ part,
-                                                    int8_t* __restrict__ qx_perm, float* __restrict__ dx,
-                                                    int8_t* __restrict__ qx_nat) {
-  const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
-  const int e0 = blockIdx.x * 16 * EB, j = blockIdx.y, t0 = blockIdx.z * 16 * TB;
+__global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const float* __restrict__ x, int T, int H,
+                                                                   const float* __restrict__ Wr, int E,
+                                                                   double* __restrict__ part,
+                                                                   int8_t* __restrict__ qx_perm,
+                                                                   float* __restrict__ dx,
+                                                                   int8_t* __restrict__ qx_nat) {
+  __shared__ v4d s_acc[kRouterWaves - 1][TB * EB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, r = lane & 15, g = lane >> 4;
+  const int e0 = blockIdx.x * 16 * EB, jp = blockIdx.y, j = jp * kRouterWaves + wave, t0 = blockIdx.z * 16 * TB;
   const int C = H / kRouterChunks, NG = (C + 15) / 16;  // chunk length, groups of 16 h
   const float* xrow[TB];
   const float* wrow[EB];
@@ -148,11 +159,13 @@ __global__ __launch_bounds__(64) void k_router_mfma(const float* __restrict__ x,
       for (int kk = 0; kk < PD; ++kk) {
         if (q0 + kk < NG) {
           router_group_mfma<TB, EB>(acc, rx[kk], rw[kk]);
-          const int q = min(q0 + kk + PD, NG - 1);
+          const int q = q0 + kk + PD;
+          if (q < NG) {
 #pragma unroll
-          for (int bt = 0; bt < TB; ++bt) rx[kk][bt] = *reinterpret_cast<const float4*>(xrow[bt] + 16 * q);
+            for (int bt = 0; bt < TB; ++bt) rx[kk][bt] = *reinterpret_cast<const float4*>(xrow[bt] + 16 * q);
 #pragma unroll
-          for (int be = 0; be < EB; ++be) rw[kk][be] = *reinterpret_cast<const float4*>(wrow[be] + 16 * q);
+            for (int be = 0; be < EB; ++be) rw[kk][be] = *reinterpret_cast<const float4*>(wrow[be] + 16 * q);
+          }
         }
       }
     }
@@ -176,24 +189,39 @@ __global__ __launch_bounds__(64) void k_router_mfma(const float* __restrict__ x,
       router_group_mfma<TB, EB>(acc, xa, wb);
     }
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int bt = 0; bt < TB; ++bt)
+#pragma unroll
+      for (int be = 0; be < EB; ++be) s_acc[wave - 1][bt * EB + be][lane] = acc[bt][be];
+  }
+  if (blockIdx.x == 0 && qx_perm) q8_x_chunk(x, T, H, j, t0, 16 * TB, lane, qx_perm, dx, qx_nat);
+  __syncthreads();
+  if (wave > 0) return;
   // lane l holds rows (tokens) l / 16 + 4 i, column (expert) l % 16 of each 16 x 16 block
 #pragma unroll
   for (int bt = 0; bt < TB; ++bt)
 #pragma unroll
     for (int be = 0; be < EB; ++be) {
+      v4d sum = acc[bt][be];
+#pragma unroll
+      for (int w = 0; w < kRouterWaves - 1; ++w) {
+        const v4d o = s_acc[w][bt * EB + be][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] = __dadd_rn(sum[i], o[i]);
+      }
       const int e = e0 + 16 * be + r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * bt + g + 4 * i;
-        if (t < T && e < E) part[((size_t)t * kRouterChunks + j) * E + e] = acc[bt][be][i];
+        if (t < T && e < E) part[((size_t)t * kRouterParts + jp) * E + e] = sum[i];
       }
     }
-  if (blockIdx.x == 0 && qx_perm) q8_x_chunk(x, T, H, j, t0, 16 * TB, lane, qx_perm, dx, qx_nat);
 }
 
-// Top-k, one 256-lane workgroup per token. Every lane adds the chunk partials
-// of its experts in ascending chunk order (all loads issued first) and rounds
-// once to fp32: the logit z. s = sigmoid(z) in fp64 rounded to fp32, c = s +
+// Top-k, one 256-lane workgroup per token. Every lane adds the 16 partial sums
+// of its experts in ascending order (all loads issued first) and rounds once
+// to fp32: the logit z. s = sigmoid(z) in fp64 rounded to fp32, c = s +
 // bias. Group score = sum of the two largest c of the group; the topk_group
 // groups with the highest (score desc, index asc) are kept; the K experts of
 // the kept groups by (c desc, index asc) are chosen, slot k = rank k; weights
@@ -224,12 +252,12 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
   __shared__ double s_sum;
   const int t = blockIdx.x, tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) {
-    double v[kRouterChunks];
+    double v[kRouterParts];
 #pragma unroll
-    for (int j = 0; j < kRouterChunks; ++j) v[j] = part[((size_t)t * kRouterChunks + j) * E + e];
+    for (int j = 0; j < kRouterParts; ++j) v[j] = part[((size_t)t * kRouterParts + j) * E + e];
     double tot = 0.0;
 #pragma unroll
-    for (int j = 0; j < kRouterChunks; ++j) tot += v[j];
+    for (int j = 0; j < kRouterParts; ++j) tot += v[j];
     const float sv = (float)(1.0 / (1.0 + exp(-(double)(float)tot)));
     s_s[e] = sv;
     s_c[e] = __fadd_rn(sv, bias[e]);
@@ -377,27 +405,26 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
                         int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
-                        hipStream_t st, hipEvent_t after_router) {
+                        hipStream_t st) {
   if (q8_done) *q8_done = false;
   if (T <= 0) return hipSuccess;
   const int H = c.hidden, E = c.n_experts;
   const bool full = (H / kRouterChunks) % 16 == 0;
-  // 16 tokens x 64 experts per workgroup; 32 x 64 from kRouterMfmaWideT tokens
-  const bool wide = T >= kRouterMfmaWideT;
-  const int tb = wide ? 2 : 1, eb = 4;
-  dim3 grid((E + 16 * eb - 1) / (16 * eb), kRouterChunks, (T + 16 * tb - 1) / (16 * tb));
+  const bool wide = T >= kRouterMfmaWideT, narrow = T <= kRouterMfmaNarrowT;
+  const int tb = wide ? 2 : 1, eb = narrow ? 1 : 4;
+  dim3 grid((E + 16 * eb - 1) / (16 * eb), kRouterParts, (T + 16 * tb - 1) / (16 * tb));
+  const int nt = 64 * kRouterWaves;
   if (wide) {
-    if (full) k_router_mfma<2, 4, 2, true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
-    else k_router_mfma<2, 4, 1, false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    if (full) k_router_mfma<2, 4, 2, true><<<grid, nt, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    else k_router_mfma<2, 4, 1, false><<<grid, nt, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+  } else if (narrow) {
+    if (full) k_router_mfma<1, 1, 2, true><<<grid, nt, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    else k_router_mfma<1, 1, 1, false><<<grid, nt, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
   } else {
-    if (full) k_router_mfma<1, 4, 2, true><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
-    else k_router_mfma<1, 4, 1, false><<<grid, 64, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    if (full) k_router_mfma<1, 4, 2, true><<<grid, nt, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
+    else k_router_mfma<1, 4, 1, false><<<grid, nt, 0, st>>>(x, T, H, Wr, E, part, qx_perm, dx, qx_nat);
   }
   if (q8_done && qx_perm) *q8_done = true;
-  if (after_router) {  // x and its Q8_0 codes are ready here
-    const hipError_t e = hipEventRecord(after_router, st);
-    if (e != hipSuccess) return e;
-  }
   if (mark) mark(mark_call, 1, st);
   k_topk<<<T, 256, 0, st>>>(part, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, c.topp, ids,
                             w, flags);

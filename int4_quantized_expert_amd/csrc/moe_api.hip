@@ -54,7 +54,6 @@ Layout make_layout(const moe_config& c, int64_t T) {
   // GEMV chunks: sum over buckets of ceil(n/kGemvMaxN) <= tokens/kGemvMaxN + buckets
   L.gemv = take((size_t)((L.TK + L.NS * T) / kGemvMaxN + std::min<int64_t>(L.E, L.TK) + 2 * L.NS) * 8);
   L.tiles = take((size_t)L.TILES * 8);
-  L.tiles_sh = take((size_t)L.NS * ((T + kMfmaTokTile - 1) / kMfmaTokTile) * 8);  // shared tiles (>= 32 positions)
   L.meta = take(sizeof(Meta));
   L.pos_token = take((size_t)L.TK * 4);
   L.qx = take((size_t)T * L.H);
@@ -67,7 +66,7 @@ Layout make_layout(const moe_config& c, int64_t T) {
   L.xdt = take(rp * (L.H / 32) * 4);
   L.ht = take(rp * L.I);
   L.hdt = take(rp * (L.I / 32) * 4);
-  L.part = take((size_t)T * kRouterChunks * L.E * 8);  // router chunk partials, every batch size
+  L.part = take((size_t)T * kRouterParts * L.E * 8);  // router partial sums, every batch size
   L.total = off;
   return L;
 }
@@ -124,7 +123,7 @@ int32_t hip_fail(hipError_t e) {
 // stream) pair needs them and are kept until the process ends.
 struct Helper {
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, routed = nullptr, join = nullptr;  // after router, after dispatch, chain done
+  hipEvent_t fork = nullptr, join = nullptr;  // after dispatch, chain done
 };
 static std::mutex g_helper_mu;
 static std::map<std::pair<int, hipStream_t>, Helper> g_helpers;
@@ -140,7 +139,6 @@ static hipError_t get_helper(hipStream_t st, Helper* out) {
     Helper h;
     if ((e = hipStreamCreateWithFlags(&h.side, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&h.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&h.routed, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&h.join, hipEventDisableTiming)) != hipSuccess) return e;
     it = g_helpers.emplace(key, h).first;
   }
@@ -151,8 +149,7 @@ static hipError_t get_helper(hipStream_t st, Helper* out) {
 // ------------------------------------------------------------------ profiling
 // Per call: 9 events on the caller's stream (start, after router, top-k,
 // dispatch, q8-x, GEMV gate-up, GEMV down, after the join, end) and 3 on the
-// helper stream around the routed tiles' MFMA gate-up and down launches (the
-// shared experts' tiles, which run ahead of dispatch, are not timed).
+// helper stream around the MFMA gate-up and down launches.
 constexpr int kProfEv = 12;
 // stage -> (first event, second event): main-stream stages, then the MFMA chain, then combine
 static const int kStageEv[MOE_N_STAGES][2] = {{0, 1}, {1, 2}, {2, 3}, {3, 4}, {4, 5},
@@ -250,9 +247,6 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
   const int64_t mfma_buckets = std::min<int64_t>(L.E, L.TK / gemm_min) + (T >= gemm_min ? L.NS : 0);
   f->grid_tiles =
       (T >= gemm_min) ? (int)(L.TK / tok_tile + mfma_buckets + L.NS * ((T + tok_tile - 1) / tok_tile)) : 0;
-  // a shared expert takes the MFMA path exactly when T >= gemm_min
-  f->early_shared = T >= gemm_min && L.NS > 0;
-  f->grid_tiles_sh = f->early_shared ? (int)(L.NS * ((T + tok_tile - 1) / tok_tile)) : 0;
   // GEMV work items: chunks of up to kGemvMaxN tokens of the buckets below the
   // threshold (one per bucket when no such bucket can hold more)
   const int64_t gemv_buckets = std::min<int64_t>(L.E, L.TK) + (T < gemm_min ? L.NS : 0);
@@ -266,17 +260,16 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
 }
 
 hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
-                     hipStream_t stream, int call, bool shared_in_lists, hipEvent_t after_router) {
+                     hipStream_t stream, int call) {
   const Layout& L = f.L;
   bool q8_done = false;
   hipError_t e = launch_route(x, f.T, *f.cfg, router_w, router_bias, reinterpret_cast<double*>(f.wsb + L.part),
                               f.ids, f.w, f.flags, f.qx, f.dx, tp ? tp->qx : nullptr, &q8_done, call, prof_mark,
-                              stream, after_router);
-  if (e == hipSuccess && after_router && !q8_done) e = hipErrorInvalidValue;  // Q8_0(x) must exist at the event
+                              stream);
   prof_mark(call, 2, stream);
   if (e == hipSuccess)
     e = launch_dispatch(f.ids, f.T, *f.cfg, f.gemm_min, f.tok_tile, L, f.wsb, f.counts, f.offsets, f.sorted,
-                        f.slotpos, f.unique, f.nunique, stream, shared_in_lists);
+                        f.slotpos, f.unique, f.nunique, stream);
   prof_mark(call, 3, stream);
   if (e == hipSuccess && !q8_done) e = launch_q8_0_x(x, f.T, f.cfg->hidden, f.qx, f.dx, tp ? tp->qx : nullptr, stream);
   if (e == hipSuccess && tp && tp->dx)
@@ -397,31 +390,15 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   }
   const int call = prof_begin();
   prof_mark(call, 0, stream);
-  // the shared experts' MFMA work forks off right after the router (it needs
-  // Q8_0(x), not the routing) and runs while top-k and dispatch do
-  const bool early = fork && f.early_shared;
-  hipError_t e = fwd_front(f, x, wts->router_w, wts->router_bias, taps, stream, call, !early,
-                           early ? hp.fork : nullptr);
+  hipError_t e = fwd_front(f, x, wts->router_w, wts->router_bias, taps, stream, call);
   prof_mark(call, 4, stream);
   const int32_t* tiles = reinterpret_cast<const int32_t*>(f.wsb + f.L.tiles);
   const int32_t* n_tiles = &reinterpret_cast<Meta*>(f.wsb + f.L.meta)->n_tiles;
-  const int32_t* tiles_sh = reinterpret_cast<const int32_t*>(f.wsb + f.L.tiles_sh);
-  const int32_t* n_tiles_sh = &reinterpret_cast<Meta*>(f.wsb + f.L.meta)->n_tiles_sh;
   if (e == hipSuccess && fork) {
-    if (early) {
-      e = hipStreamWaitEvent(hp.side, hp.fork, 0);
-      if (e == hipSuccess) e = launch_shared_setup(*f.cfg, f.T, f.tok_tile, f.L, f.wsb, hp.side);
-      if (e == hipSuccess) e = launch_tile_gather(f.a, f.grid_tiles_sh, f.tok_tile, tiles_sh, n_tiles_sh, hp.side);
-      if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles_sh, f.tok_tile / 32, tiles_sh, n_tiles_sh, hp.side);
-      if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles_sh, f.tok_tile / 32, tiles_sh, n_tiles_sh, hp.side);
-      if (e == hipSuccess) e = hipEventRecord(hp.routed, stream);
-      if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.routed, 0);
-    } else {
-      e = hipEventRecord(hp.fork, stream);
-      if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.fork, 0);
-    }
+    e = hipEventRecord(hp.fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.fork, 0);
     if (e == hipSuccess) e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, hp.side);
-    prof_mark(call, 9, hp.side);  // the MFMA stages time the routed tiles' gate/up and down launches
+    prof_mark(call, 9, hp.side);  // the MFMA stages time the gate/up and down launches, not the gather
     if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 10, hp.side);
     if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);

@@ -18,6 +18,8 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 4;
 constexpr int kMfmaTokTile = 32;     // smallest token tile of the int8-MFMA path
 constexpr int kRouterChunks = 64;  // contiguous H chunks of the router dot (fixed summation structure)
+constexpr int kRouterWaves = 4;    // consecutive chunks per router workgroup, added in order in LDS
+constexpr int kRouterParts = kRouterChunks / kRouterWaves;  // stored partial sums per (token, expert)
 constexpr int kDefaultGemmMin = 5;   // bucket size from which the MFMA path runs (a GEMV chunk holds at most 4)
 constexpr int kMaxHidden = 16384;  // hidden and inter sizes (GEMV stages two 16-byte loads per lane)
 constexpr int kGemvMaxN = 4;         // tokens per GEMV work item (chunk)
@@ -32,14 +34,13 @@ struct Meta {
   int32_t n_buckets;
   int32_t n_gemv;
   int32_t n_tiles;
-  int32_t n_tiles_sh;  // MFMA tiles of the shared experts when they run ahead of dispatch
 };
 
 // Device workspace layout for T tokens (all offsets 256-byte aligned).
 struct Layout {
   int64_t T = 0, E = 0, K = 0, H = 0, I = 0, NS = 0, TK = 0, R = 0, NB = 0, TILES = 0;
   size_t ids = 0, w = 0, flags = 0, counts = 0, offsets = 0, sorted = 0, slotpos = 0, unique = 0,
-         nunique = 0, bk_e = 0, bk_p0 = 0, bk_n = 0, gemv = 0, tiles = 0, tiles_sh = 0, meta = 0, pos_token = 0, qx = 0,
+         nunique = 0, bk_e = 0, bk_p0 = 0, bk_n = 0, gemv = 0, tiles = 0, meta = 0, pos_token = 0, qx = 0,
          dx = 0, qh = 0, dh = 0, eout = 0, xt = 0, xdt = 0, ht = 0, hdt = 0, part = 0, total = 0;
 };
 
@@ -105,11 +106,6 @@ struct Fwd {
   Layout L;
   char* wsb = nullptr;
   int gemm_min = 0, tok_tile = 0, grid_gemv = 0, grid_tiles = 0, gemv_chunk = 0;
-  // shared experts on the MFMA path start right after the router (they do not
-  // depend on routing): their bucket entries and tiles come from
-  // launch_shared_setup, and dispatch leaves them out of its lists
-  bool early_shared = false;
-  int grid_tiles_sh = 0;
   bool many = false;
   int32_t *ids = nullptr, *counts = nullptr, *offsets = nullptr, *sorted = nullptr, *slotpos = nullptr,
           *unique = nullptr, *nunique = nullptr;
@@ -124,8 +120,7 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
               Fwd* f);
 // router + top-K + dispatch + Q8_0(x)
 hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
-                     hipStream_t stream, int call,
-                     bool shared_in_lists = true, hipEvent_t after_router = nullptr);
+                     hipStream_t stream, int call);
 hipError_t fwd_combine(Fwd& f, float* y, hipStream_t stream);
 int32_t hip_fail(hipError_t e);
 
@@ -239,13 +234,10 @@ hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
                         int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
-                        hipStream_t st, hipEvent_t after_router = nullptr);
+                        hipStream_t st);
 hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
                            const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
-                           int32_t* unique, int32_t* nunique, hipStream_t st, bool shared_in_lists = true);
-// Bucket entries (index E + s) and the MFMA tile list of the shared experts,
-// for the shared chain that runs before dispatch.
-hipError_t launch_shared_setup(const moe_config& c, int T, int tok_tile, const Layout& L, char* ws, hipStream_t st);
+                           int32_t* unique, int32_t* nunique, hipStream_t st);
 hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
 hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
 hipError_t launch_tile_gather(const ExpertArgs& a, int grid, int tok_tile, const int32_t* tiles,

@@ -52,7 +52,7 @@ def test_workspace_bytes():
 
 @pytest.mark.parametrize("T", [1, 63, 64, 192, 2048])
 def test_workspace_covers_every_region(T):
-    """Lower bound from what the kernels write per call: router chunk partials (T x 64 chunks x E fp64),
+    """Lower bound from what the kernels write per call: router partial sums (T x 16 x E fp64),
     per-slot Q8_0 h codes and scales, per-slot fp32 expert outputs, Q8_0 x, the GEMV work list at its
     worst case (chunks of up to 4 tokens), and the position-blocked x and h operands of the MFMA tiles (whole
     32-position groups) — every batch size, including the large ones."""
@@ -60,7 +60,7 @@ def test_workspace_covers_every_region(T):
     E, K, H, I, NS = 256, 8, 6144, 2048, 1
     R = T * K + NS * T
     RP = (R + 31) // 32 * 32
-    need = (T * 64 * E * 8 + R * I + R * (I // 32) * 4 + R * H * 4 + T * H + T * (H // 32) * 4
+    need = (T * 16 * E * 8 + R * I + R * (I // 32) * 4 + R * H * 4 + T * H + T * (H // 32) * 4
             + ((T * K + NS * T) // 4 + min(E, T * K) + 2 * NS) * 8
             + RP * H + RP * (H // 32) * 4 + RP * I + RP * (I // 32) * 4)
     assert moe.moe_workspace_bytes(c, T) >= need
