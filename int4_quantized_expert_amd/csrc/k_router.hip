@@ -13,7 +13,7 @@
 // is added in ascending order, ((c0 + c1) + c2) + c3, giving 16 partial sums,
 // which are added in ascending order starting from 0. One kernel computes the
 // chunks (one wavefront each; token blocks x expert blocks x chunks, so even
-// one token spreads over 256 wavefronts) and writes the 16 partial sums; the
+// one token spreads over 1,024 wavefronts) and writes the 16 partial sums; the
 // top-k kernel adds them. The logits agree with
 // an exact fp64 dot to far below fp32 resolution, so they round to the same
 // fp32 value except when the exact dot lies within ~1e-16 relative of a
@@ -38,14 +38,14 @@ __device__ __forceinline__ uint32_t pack4q(int8_t a, int8_t b, int8_t c, int8_t 
 }
 
 // Q8_0 of x for tokens [t0, t0 + nt) restricted to the blocks j, j + 64, ... of
-// chunk j: lane -> (token, block) pairs. Called by the expert-block-0
-// workgroups of the router kernel, which saves a launch on the decode path.
-__device__ __forceinline__ void q8_x_chunk(const float* __restrict__ x, int T, int H, int j, int t0, int nt, int lane,
-                                           int8_t* __restrict__ qx_perm, float* __restrict__ dx,
-                                           int8_t* __restrict__ qx_nat) {
-  // Q8_0 of x: lane -> (token, block) pairs of this chunk's block set
+// chunk j: item idx -> (token, block). The wavefronts of chunk j in every
+// expert block share the items (first = lane + 64 * expert block, step = 64 *
+// expert blocks), which saves a launch on the decode path.
+__device__ __forceinline__ void q8_x_chunk(const float* __restrict__ x, int T, int H, int j, int t0, int nt,
+                                           int first, int step, int8_t* __restrict__ qx_perm,
+                                           float* __restrict__ dx, int8_t* __restrict__ qx_nat) {
   const int nb = H / 32, nbj = (nb - j + kRouterChunks - 1) / kRouterChunks;  // blocks j, j+NC, ... of one token
-  for (int idx = lane; idx < nt * nbj; idx += 64) {
+  for (int idx = first; idx < nt * nbj; idx += step) {
     const int tt = idx / nbj, bq = j + kRouterChunks * (idx - tt * nbj), t = t0 + tt;
     if (t >= T) continue;
     const float* src = x + (size_t)t * H + (size_t)bq * 32;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const float* 
 #pragma unroll
       for (int be = 0; be < EB; ++be) s_acc[wave - 1][bt * EB + be][lane] = acc[bt][be];
   }
-  if (blockIdx.x == 0 && qx_perm) q8_x_chunk(x, T, H, j, t0, 16 * TB, lane, qx_perm, dx, qx_nat);
+  if (qx_perm) q8_x_chunk(x, T, H, j, t0, 16 * TB, lane + 64 * blockIdx.x, 64 * gridDim.x, qx_perm, dx, qx_nat);
   __syncthreads();
   if (wave > 0) return;
   // lane l holds rows (tokens) l / 16 + 4 i, column (expert) l % 16 of each 16 x 16 block
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
   }
 }
 
-// Router + top-k. The logits come as chunk partials and, when qx_perm is
+// Router + top-k. The logits come as 16 partial sums and, when qx_perm is
 // given, Q8_0 of x is encoded in the same launch (*q8_done = true).
 
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,
