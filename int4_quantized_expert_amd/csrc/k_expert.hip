@@ -477,9 +477,12 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
 
 // Block after blk in the class-major walk (the next of its class, else the
 // first of the next class), clamped to a valid block past the walk's end.
+// Branch-free (blk >= 0, kDotClasses a power of two), so a loop slot that
+// advances it stays one basic block.
 __device__ __forceinline__ int class_major_next(int blk, int nb) {
-  const int n = blk + kDotClasses;
-  return min(n < nb ? n : (blk % kDotClasses) + 1, nb - 1);
+  static_assert((kDotClasses & (kDotClasses - 1)) == 0, "kDotClasses must be a power of two");
+  const int n = blk + kDotClasses, wrap = (blk & (kDotClasses - 1)) + 1;
+  return min(n < nb ? n : wrap, nb - 1);
 }
 
 // Per-wavefront LDS for the class totals: [NTT][gate|up][16/4][64 lanes] float4.
@@ -552,6 +555,25 @@ __device__ __forceinline__ void load_operands(__amdgpu_buffer_rsrc_t xr, __amdgp
     rb[tt] = buf_v4(xr, xo[tt], (uint32_t)blk * kPbBlkStride);
     rd[tt] = buf_f32(dr, xso[tt], (uint32_t)blk * kPbScStride * 4);
   }
+}
+
+// The ring refill inside the MFMA loops is split: operand codes right after
+// the MFMAs that read them, scales only after the epilogue's last use of the
+// old ones, behind a scheduling barrier. Otherwise the compiler issues the
+// scale loads early into other registers and copies them back at the end of
+// the loop, which makes every iteration wait for all loads in flight.
+template <int NTT>
+__device__ __forceinline__ void load_codes(__amdgpu_buffer_rsrc_t xr, int blk, const uint32_t (&xo)[NTT],
+                                           v4i (&rb)[NTT]) {
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) rb[tt] = buf_v4(xr, xo[tt], (uint32_t)blk * kPbBlkStride);
+}
+template <int NTT>
+__device__ __forceinline__ void load_scales(__amdgpu_buffer_rsrc_t dr, int blk, const uint32_t (&xso)[NTT],
+                                            float (&rd)[NTT]) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) rd[tt] = buf_f32(dr, xso[tt], (uint32_t)blk * kPbScStride * 4);
 }
 
 // The A operand of one block: int4 loads the lane's 8 bytes and unpacks them
@@ -677,9 +699,12 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   float rs[PF];
   int fetch = 0;  // next block to load
 #pragma unroll
-  for (int kk = 0; kk < PF; ++kk) {
-    load_gu_block<NTT, W>(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
+  for (int kk = 0; kk < PF; ++kk) {  // loads in the loop's order
+    rg[kk] = load_a<W>(gr, loff, fetch);
+    ru[kk] = load_a<W>(ur, loff, fetch);
+    load_codes<NTT>(xr, fetch, xo, rb[kk]);
     if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
+    load_scales<NTT>(dr, fetch, xso, rd[kk]);
     fetch = class_major_next(fetch, nb);
   }
   int blk = 0;  // block being consumed
@@ -694,26 +719,35 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
         scales_get(slot, half, gs16, 0);
         scales_get(slot, half, us16, 32);
       }
+      v16i Sg[NTT], Su[NTT];  // (16 x) block sums
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        const v16i Sg = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, rb[kk][tt], zero, 0, 0, 0);  // (16 x) block sums
-        const v16i Su = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, rb[kk][tt], zero, 0, 0, 0);
+        Sg[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Ag, rb[kk][tt], zero, 0, 0, 0);
+        Su[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, rb[kk][tt], zero, 0, 0, 0);
+      }
+      // refill the slot just consumed: codes now, scales after their last use
+      rg[kk] = load_a<W>(gr, loff, fetch);
+      ru[kk] = load_a<W>(ur, loff, fetch);
+      load_codes<NTT>(xr, fetch, xo, rb[kk]);
+      if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
         const float d = rd[kk][tt];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ag[tt][i] = fmaf(GS ? __fmul_rn(d, gs16[i]) : d, (float)Sg[i], ag[tt][i]);
+        for (int i = 0; i < 16; ++i)
+          ag[tt][i] = fmaf(GS ? __fmul_rn(d, gs16[i]) : d, (float)Sg[tt][i], ag[tt][i]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) au[tt][i] = fmaf(GS ? __fmul_rn(d, us16[i]) : d, (float)Su[i], au[tt][i]);
+        for (int i = 0; i < 16; ++i)
+          au[tt][i] = fmaf(GS ? __fmul_rn(d, us16[i]) : d, (float)Su[tt][i], au[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = true_sum<W>(Sg[i]);
-            a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = true_sum<W>(Su[i]);
+            a.t_gu_sums[(size_t)(r0 + out_row(i, lane)) * nb + blk] = true_sum<W>(Sg[tt][i]);
+            a.t_gu_sums[(size_t)(I + r0 + out_row(i, lane)) * nb + blk] = true_sum<W>(Su[tt][i]);
           }
         }
       }
-      // refill the slot just consumed
-      load_gu_block<NTT, W>(gr, ur, xr, dr, fetch, loff, xo, xso, rg[kk], ru[kk], rb[kk], rd[kk]);
-      if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
+      load_scales<NTT>(dr, fetch, xso, rd[kk]);
       fetch = class_major_next(fetch, nb);
       if (blk + kDotClasses >= nb) {  // blk ends its class
 #pragma unroll
@@ -811,9 +845,11 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   float rs[PF];
   int fetch = 0;
 #pragma unroll
-  for (int kk = 0; kk < PF; ++kk) {
-    load_dn_block<NTT, W>(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
+  for (int kk = 0; kk < PF; ++kk) {  // loads in the loop's order
+    ra[kk] = load_a<W>(wr, loff, fetch);
+    load_codes<NTT>(xr, fetch, xo, rb[kk]);
     if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
+    load_scales<NTT>(dr, fetch, xso, rd[kk]);
     fetch = class_major_next(fetch, nbi);
   }
   int blk = 0;
@@ -827,19 +863,26 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
         scales_put(slot, rs[kk], lane);
         scales_get(slot, half, os16, 0);
       }
+      v16i S[NTT];  // (16 x) block sums
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) S[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, rb[kk][tt], zero, 0, 0, 0);
+      // refill the slot just consumed: codes now, scales after their last use
+      ra[kk] = load_a<W>(wr, loff, fetch);
+      load_codes<NTT>(xr, fetch, xo, rb[kk]);
+      if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
-        const v16i S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, rb[kk][tt], zero, 0, 0, 0);  // 16 x block sums
         const float d = rd[kk][tt];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[tt][i] = fmaf(GS ? __fmul_rn(d, os16[i]) : d, (float)S[i], acc[tt][i]);
+        for (int i = 0; i < 16; ++i)
+          acc[tt][i] = fmaf(GS ? __fmul_rn(d, os16[i]) : d, (float)S[tt][i], acc[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = true_sum<W>(S[i]);
+          for (int i = 0; i < 16; ++i)
+            a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = true_sum<W>(S[tt][i]);
         }
       }
-      load_dn_block<NTT, W>(wr, xr, dr, fetch, loff, xo, xso, ra[kk], rb[kk], rd[kk]);
-      if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
+      load_scales<NTT>(dr, fetch, xso, rd[kk]);
       fetch = class_major_next(fetch, nbi);
       if (blk + kDotClasses >= nbi) {
 #pragma unroll
@@ -1060,7 +1103,7 @@ template <int NTT, int W, bool GS>
 static void mfma_gateup_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
-  constexpr int MPF = NTT == 1 ? 4 : 2;
+  constexpr int MPF = 4;  // blocks in flight (measured: 2 for 64-position tiles is 3% slower)
   if ((a.H / 32) % MPF == 0) {
     if (tap) k_gateup_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_gateup_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
@@ -1074,7 +1117,7 @@ template <int NTT, int W, bool GS>
 static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                              hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
-  constexpr int MPF = NTT == 1 ? 4 : 2;
+  constexpr int MPF = 4;  // blocks in flight (measured: 2 for 64-position tiles is 3% slower)
   if ((a.I / 32) % MPF == 0) {
     if (tap) k_down_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_down_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
