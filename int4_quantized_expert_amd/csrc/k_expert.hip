@@ -952,8 +952,8 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
 // Separate GEMV and MFMA kernels keep each path's register budget (and so its
 // occupancy) independent; the host runs the two chains on two streams so they
 // overlap. TAP instantiations write block-sum taps and are launched only when
-// those taps are requested. The MFMA path keeps 4 blocks in flight for
-// 32-token tiles, 2 for 64 (the depth must divide the block count; 2 always does).
+// those taps are requested. The MFMA path keeps 4 blocks in flight, or 2
+// when 4 does not divide the block count (2 always does).
 
 // PF: blocks in flight per wavefront (chosen by the host).
 // W: weight code width (4 or 8); GS: grouped weight scales (int4 only). Both
@@ -1103,7 +1103,7 @@ template <int NTT, int W, bool GS>
 static void mfma_gateup_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
-  constexpr int MPF = 4;  // blocks in flight (measured: 2 for 64-position tiles is 3% slower)
+  constexpr int MPF = 4;  // blocks in flight (2 measured 3% slower for 64-position tiles)
   if ((a.H / 32) % MPF == 0) {
     if (tap) k_gateup_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_gateup_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
@@ -1117,7 +1117,7 @@ template <int NTT, int W, bool GS>
 static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                              hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
-  constexpr int MPF = 4;  // blocks in flight (measured: 2 for 64-position tiles is 3% slower)
+  constexpr int MPF = 4;  // blocks in flight (2 measured 3% slower for 64-position tiles)
   if ((a.I / 32) % MPF == 0) {
     if (tap) k_down_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_down_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
