@@ -1,7 +1,8 @@
 """GPU parity for the 64-position MFMA tiles (batches of 256 tokens and more):
 both prefetch depths of their block ring (4 blocks when the block count is a
 multiple of 4, 2 otherwise) for gate/up and down, with int4 row scales, int4
-grouped scales and int8 weights. Every tap of every token without a router
+grouped scales and int8 weights, up to batches whose dispatch reads the ids
+from global memory. Every tap of every token without a router
 near-tie is compared bit for bit with the oracle.
 """
 import numpy as np
@@ -29,9 +30,14 @@ SHAPES = {
 }
 
 
-@pytest.mark.parametrize("name", list(SHAPES))
-@pytest.mark.parametrize("wb,gs", [(4, 0), (4, 64), (8, 0)])
-@pytest.mark.parametrize("T,gemm_min", [(300, 1), (257, 70)])
+# Every shape and weight format at T = 300 (all MFMA) and 257 (mixed); large batches for one int4 and one int8
+# shape: T = 3200 with top-4 is 12,800 slots, T = 6200 is 24,800, past the 24,576 up to which dispatch keeps
+# the ids in LDS, so it reads them from global memory.
+CASES = [(n, wb, gs, T, gm) for n in SHAPES for (wb, gs) in ((4, 0), (4, 64), (8, 0)) for (T, gm) in ((300, 1), (257, 70))]
+CASES += [(n, wb, 0, T, gm) for (n, wb) in (("ring4", 4), ("mixed", 8)) for (T, gm) in ((3200, 1), (6200, 5))]
+
+
+@pytest.mark.parametrize("name,wb,gs,T,gemm_min", CASES)
 def test_wide_tiles_all_taps_bitexact(name, wb, gs, T, gemm_min):
     sh = SHAPES[name]
     seed = 70 + T
