@@ -359,50 +359,44 @@ void orc_block_sums(const int8_t* a, const int8_t* b, int64_t n, int32_t* S) {
   }
 }
 
-/* Dequant-on-use integer dot ("Show HN", implemented features: int8 x int4
- * integer dots with per-row scales, dequantized on use). The pages fix no fp32
- * order; the reading used here: block sums are exact int32; block b belongs to
- * class b mod ORC_DOT_CLASSES; each class scales its blocks' sums by the
- * activation block scale and accumulates them in ascending block order with one
- * fused multiply-add each, starting from +0; the class totals are added in
- * ascending class order, starting from +0; the row scale multiplies the sum
- * once. */
+/* Dequant-on-use integer dot ("Show HN: 느린 컴퓨터에서 GLM 5.2 실행하기",
+ * implemented features: integer-dot kernels on Q8_0-style int8 activations
+ * against int8 / packed int4 weights with per-row scales, dequantized on use).
+ * Each 32-element block has an exact int32 sum S_b of its code products; the
+ * dequantized dot is s_row * sum_b d_b * S_b. The pages fix no fp32 order, so
+ * the reading is the plain one: one running sum over the blocks in ascending
+ * order, starting from +0, each block added with one fused multiply-add of its
+ * activation scale and its sum; then one multiply by the row scale (constant
+ * along the row, so it is applied once at the end). */
 float orc_dot_q4q8(const int8_t* q4, float srow, const int8_t* q8, const float* d8, int64_t n) {
   const int64_t nb = n / 32;
-  float total = 0.0f;
-  for (int c = 0; c < ORC_DOT_CLASSES; ++c) {
-    float acc = 0.0f;
-    for (int64_t blk = c; blk < nb; blk += ORC_DOT_CLASSES) {
-      int32_t S = 0;
-      for (int i = 0; i < 32; ++i) S += (int32_t)q4[blk * 32 + i] * (int32_t)q8[blk * 32 + i];
-      acc = fmaf(d8[blk], (float)S, acc);
-    }
-    total = total + acc;
+  float acc = 0.0f;
+  for (int64_t blk = 0; blk < nb; ++blk) {
+    int32_t S = 0;
+    for (int i = 0; i < 32; ++i) S += (int32_t)q4[blk * 32 + i] * (int32_t)q8[blk * 32 + i];
+    acc = fmaf(d8[blk], (float)S, acc);
   }
-  return srow * total;
+  return srow * acc;
 }
 
 /* The same dot with grouped weight scales (see orc_quant_int4_grouped). The
- * reading keeps the class structure above and moves the weight scale into the
- * blocks: block b contributes fmaf(d8[b] * sg[g(b)], S_b, acc), where the
- * product of the activation block scale and the scale of the group holding
- * block b is rounded to fp32 first; there is no row scale at the end. sg holds
- * the row's n/group scales; group is a multiple of 32. */
+ * weight scale now changes along the row, so it cannot be taken out of the
+ * sum: each block is dequantized with the product of its two scales, the
+ * activation block scale and the scale of the weight group holding the block
+ * (rounded to fp32), and added to the one ascending running sum from +0 with a
+ * fused multiply-add; there is no row scale. sg holds the row's n/group
+ * scales; group is a multiple of 32. */
 float orc_dot_q4q8_grouped(const int8_t* q4, const float* sg, int64_t group, const int8_t* q8, const float* d8,
                            int64_t n) {
   const int64_t nb = n / 32;
-  float total = 0.0f;
-  for (int c = 0; c < ORC_DOT_CLASSES; ++c) {
-    float acc = 0.0f;
-    for (int64_t blk = c; blk < nb; blk += ORC_DOT_CLASSES) {
-      int32_t S = 0;
-      for (int i = 0; i < 32; ++i) S += (int32_t)q4[blk * 32 + i] * (int32_t)q8[blk * 32 + i];
-      const float scale = d8[blk] * sg[(blk * 32) / group];
-      acc = fmaf(scale, (float)S, acc);
-    }
-    total = total + acc;
+  float acc = 0.0f;
+  for (int64_t blk = 0; blk < nb; ++blk) {
+    int32_t S = 0;
+    for (int i = 0; i < 32; ++i) S += (int32_t)q4[blk * 32 + i] * (int32_t)q8[blk * 32 + i];
+    const float scale = d8[blk] * sg[(blk * 32) / group];
+    acc = fmaf(scale, (float)S, acc);
   }
-  return total;
+  return acc;
 }
 
 /* SwiGLU gate: silu(g) * u = g * u / (1 + exp(-g)), in fp64, rounded once. */

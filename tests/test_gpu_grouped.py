@@ -1,8 +1,8 @@
 """GPU parity for grouped int4 weight scales (group_size G > 0): one fp32 scale per
 G elements along each row, the quality fix the colibrì pages point to ("Colibri:
 25GB RAM을 탑재한 노트북에서 744B AI 모델 실행하기", section on the quality cost of
-int4). The dot scales each block's exact sum by fp32(d_b * s_group(b)) in its
-class chain, with no row scale.
+int4). The dot scales each block's exact sum by fp32(d_b * s_group(b)) in one
+ascending running sum, with no row scale.
 
 The encoder (codes and tiled scales) is bit-exact against the oracle's; every tap
 of the tiny layer is bit-exact on the GEMV, MFMA and mixed paths for G = 32, 64

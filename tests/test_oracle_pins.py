@@ -472,8 +472,8 @@ def test_dot_golden_order():
     assert v == np.float32(g["expected"])
 
 
-@pytest.mark.parametrize("case", ["dot_classes", "dot_class_chain_order"])
-def test_dot_golden_classes(case):
+@pytest.mark.parametrize("case", ["dot_single_chain", "dot_single_chain_halves", "dot_fused_step"])
+def test_dot_golden_single_chain(case):
     g = HW[case]
     nb = g["n_blocks"]
     q4 = np.zeros(32 * nb, np.int8)
@@ -516,8 +516,9 @@ def test_dot_closed_form_constant():
         assert abs(float(v) - exact) <= gamma(n // 32 + 2) * abs(exact) + 1e-9
 
 
-def test_dot_grouped_golden():
-    g = HW["dot_grouped_hand"]
+@pytest.mark.parametrize("case", ["dot_grouped_hand", "dot_grouped_scale_product"])
+def test_dot_grouped_golden(case):
+    g = HW[case]
     nb = g["n_blocks"]
     q4 = np.zeros(32 * nb, np.int8)
     q8 = np.zeros(32 * nb, np.int8)
@@ -528,10 +529,10 @@ def test_dot_grouped_golden():
     assert v == np.float32(g["expected"])
 
 
-@pytest.mark.parametrize("case", ["dot_order", "dot_classes", "dot_class_chain_order"])
+@pytest.mark.parametrize("case", ["dot_order", "dot_single_chain", "dot_single_chain_halves"])
 def test_dot_grouped_equal_power_of_two_scales_is_per_row_dot(case):
     """Equal group scales that are a power of two scale every product exactly, so the grouped dot equals the
-    per-row dot with that row scale bit for bit; on the hand-worked class goldens this pins the class order."""
+    per-row dot with that row scale bit for bit; on the hand-worked chain goldens this pins the block order."""
     g = HW[case]
     nb = g.get("n_blocks", 3)
     q4 = np.zeros(32 * nb, np.int8)
