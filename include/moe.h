@@ -114,7 +114,8 @@ typedef struct moe_config {
   int32_t group_size;    /* <= 0: one weight scale per row. Else int4 only: one scale per group of
                             group_size elements along K [D3]; a power of two times 32 that divides
                             H and I. The dot then scales block b's exact sum by
-                            fp32(d_b * s_group(b)) in its class chain, with no row scale. */
+                            fp32(d_b * s_group(b)) in its one ascending running sum, with no
+                            row scale. */
   float topp;            /* adaptive expert top-p [D4]: in (0, 1) a token keeps only the slots, taken by
                             normalised weight descending (lower slot first on ties), while the fp64 sum of
                             the kept weights is below topp, and its kept weights are renormalised over the
@@ -229,11 +230,11 @@ int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, 
 /* Whole layer [A][B]: y [T][H] = sum over shared experts of FFN_s(x) (weight
  * 1, added first) + sum_k topk_w[t][k] * FFN_{id(t,k)}(x[t]) in slot order,
  * where FFN(x) = W2 . Q8_0(silu(W1 . Q8_0(x)) * (W3 . Q8_0(x))) with int4 rows
- * dotted against int8 activations: exact int32 sums per 32-element block;
- * block b belongs to class b mod 8, each class accumulates
- * acc = fma(d_block, sum, acc) over its blocks in ascending order from 0, the
- * eight class totals are added in class order from 0, and one multiply by the
- * row scale follows; silu(g)*u = g*u/(1+exp(-g)) in fp64, rounded once. Each unique expert's weights are read once for all its tokens.
+ * dotted against int8 activations: exact int32 sums per 32-element block; one
+ * running sum over the blocks in ascending order from +0,
+ * acc = fma(d_block, sum, acc), then one multiply by the row scale;
+ * silu(g)*u = g*u/(1+exp(-g)) in fp64, rounded once. Each unique expert's
+ * weights are read once for all its tokens.
  * taps may be NULL. */
 int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
                           void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream);

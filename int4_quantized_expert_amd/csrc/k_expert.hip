@@ -11,9 +11,10 @@
 // Grids are sized for the worst case and workgroups beyond the device-side
 // counts exit at once, so the bucket structure never travels back to the host.
 //
-// GEMV (few tokens, HBM-bound): one lane owns one weight row of a 64-row
-// tile; the tile's eight wavefronts take its K blocks round-robin and merge
-// their exact block sums through LDS (details at the GEMV section).
+// GEMV (few tokens, HBM-bound): a 512-lane workgroup streams one 64-row tile;
+// each lane computes exact block sums of one (row, block) per step, and the
+// sums are turned around in LDS so that one lane runs the whole fp32 chain of
+// a (row, token) (details at the GEMV section).
 //
 // MFMA (many tokens): v_mfma_i32_32x32x32_i8 contracts exactly one 32-element
 // Q8_0 block, giving the exact int32 block sums of a 32-row x 32-token tile.
@@ -23,11 +24,9 @@
 // codes already have, so A and B pair the same elements register by register.
 // The result is 16 values per lane: column l%32, rows 8*(i/4) + 4*(l/32) + i%4.
 //
-// Both paths run the same fp32 arithmetic: block b belongs to class b % 8;
-// each class accumulates fma(d_block, S_block, acc) over its blocks in
-// ascending order from +0; the class totals are added in class order from +0;
-// one multiply by the row scale. So a bucket's result does not depend on the
-// path it takes.
+// Both paths run the same fp32 arithmetic: one running sum over the blocks in
+// ascending order from +0, acc = fma(d_block, S_block, acc), then one multiply
+// by the row scale. So a bucket's result does not depend on the path it takes.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -197,37 +196,71 @@ __device__ __forceinline__ void store_h_lanes(const ExpertArgs& a, const Bucket&
   }
 }
 
+// Orders LDS writes of some lanes of a wavefront before later LDS reads of
+// other lanes of the same wavefront (and those reads before later writes). A
+// wavefront's LDS operations execute in issue order; the fences only keep the
+// compiler from moving them across.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ------------------------------------------------------------------ GEMV paths
 // Few tokens per expert: HBM-bound. A 512-lane workgroup owns one 64-row tile
-// (one lane per row); its eight wavefronts are the eight accumulation classes
-// of the dot: wavefront w walks blocks w, w+8, w+16, ... with its own fp32
-// chain, so per step the workgroup reads one contiguous 8 KB run of each
-// weight stream and no wavefront waits for another until the end, where the
-// class totals meet in LDS and are added in class order. Keeping few requests
-// in flight (PF blocks per wavefront) and adjacent is what lets many buckets
-// stream near the HBM ceiling; deep per-lane queues measurably lose.
+// and streams it as one contiguous run: at step j its eight wavefronts read
+// blocks 8j .. 8j+7, and wavefront w takes rows 8w .. 8w+7 of each, so lane l
+// loads 16 bytes of row 8w + l%8, block 8j + l/8 (one full 128-byte line per
+// group of 8 lanes, 1 KB per instruction, 8 KB per workgroup and step).
+// Keeping few requests in flight (PF steps per wavefront) and adjacent is what
+// lets many buckets stream near the HBM ceiling.
 //
-// The chunk's activation codes and scales are staged in LDS once; the block a
-// wavefront needs is the same for all its lanes, so those reads broadcast.
+// Each lane computes the exact int32 block sums of its (row, block) for every
+// token of the chunk. The fp32 dot is one ascending chain per (projection,
+// token, row), so the sums of a step are turned around in the wavefront's own
+// LDS slice: the lane that owns a chain reads its row's 8 sums of the step and
+// adds them in block order, fmaf(d_b, S_b, acc), from +0 at step 0. A chain
+// never leaves its lane and no wavefront waits for another until the end.
+//
+// The chunk's activation codes and scales are staged in LDS once; the lanes
+// of one block read the same 32 bytes, so those reads broadcast.
 //
 // Unpacking: a word of 8 nibbles splits with a shift and two masks into two
 // words of int8 lanes holding 16*q; v_dot4 multiplies them against the
 // activation codes, which are stored permuted to match; the block sum is
 // shifted right by 4 (exact).
-constexpr int kGW = kDotClasses;  // wavefronts per tile
+constexpr int kGW = 8;  // wavefronts per tile, 8 rows each
 constexpr int kGemvThreads = 64 * kGW;
 
-// Bytes of dynamic LDS for a GEMV launch whose chunks hold at most n tokens
-// (rounded up to the instantiated 1, 2 or 4) over K inputs; pairs = outputs per
-// token (2 for gate/up, 1 for down).
-static inline size_t gemv_lds_bytes(int n, int K, int pairs) {
-  const int nc = n <= 1 ? 1 : (n <= 2 ? 2 : kGemvMaxN);
-  const size_t stage = (size_t)nc * ((size_t)K + (size_t)(K / 32) * 4);
-  const size_t part = (size_t)kGW * pairs * nc * 64 * 4;
-  return stage > part ? stage : part;
+// Dynamic LDS of a GEMV workgroup for chunks of NC tokens over K inputs with
+// P projections (2 gate/up, 1 down): staged codes [NC][K], staged scales
+// [NC][nbp] (rows padded to 8 blocks), per wavefront the turned-around block
+// sums [8*P*NC chains][8 blocks] and (grouped scales) [P][8 rows][8 blocks]
+// weight scales, and for gate/up the chain results [NC][2][64] that pair gate
+// with up.
+struct GemvLdsPlan {
+  size_t xs, xd, tb, sg, hx, total;
+};
+__host__ __device__ __forceinline__ GemvLdsPlan gemv_lds_plan(int NC, int K, int P, bool GS) {
+  const int nb = K / 32, nbp = (nb + 7) & ~7;
+  GemvLdsPlan L;
+  L.xs = 0;
+  L.xd = L.xs + (size_t)NC * K;
+  L.tb = L.xd + (size_t)NC * nbp * 4;
+  L.sg = L.tb + (size_t)kGW * (8 * P * NC) * 8 * 4;
+  L.hx = L.sg + (GS ? (size_t)kGW * P * 64 * 4 : 0);
+  L.total = L.hx + (P == 2 ? (size_t)NC * 2 * 64 * 4 : 0);
+  return L;
 }
 
-// Staging of the chunk's N (padded) tokens: codes [N][K] and scales [N][K/32].
+// Bytes of dynamic LDS for a GEMV launch whose chunks hold at most n tokens
+// (rounded up to the instantiated 1, 2 or 4).
+static inline size_t gemv_lds_bytes(int n, int K, int pairs, bool gs) {
+  const int nc = n <= 1 ? 1 : (n <= 2 ? 2 : kGemvMaxN);
+  return gemv_lds_plan(nc, K, pairs, gs).total;
+}
+
+// Staging of the chunk's N (padded) tokens: codes [N][K] and scales [N][nbp].
 // The loads go to registers first so that a workgroup can issue its first
 // weight loads before it waits for them; then they are written to LDS.
 // K <= 16384: at most two 16-byte code loads and one scale per lane and token.
@@ -252,30 +285,67 @@ __device__ __forceinline__ void stage_load(const int8_t* const (&src)[N], const 
 
 template <int N>
 __device__ __forceinline__ void stage_store(const Staged<N>& st, int K, int8_t* xs, float* xd) {
-  const int tid = threadIdx.x, n16 = K / 16, nb = K / 32;
+  const int tid = threadIdx.x, n16 = K / 16, nb = K / 32, nbp = (nb + 7) & ~7;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     v4i* d4 = reinterpret_cast<v4i*>(xs + (size_t)i * K);
     if (tid < n16) d4[tid] = st.c[i][0];
     if (tid + kGemvThreads < n16) d4[tid + kGemvThreads] = st.c[i][1];
-    if (tid < nb) xd[i * nb + tid] = st.d[i];
+    if (tid < nb) xd[i * nbp + tid] = st.d[i];
   }
   __syncthreads();
 }
 
-// GS: grouped weight scales. Each lane (one row) then also streams its row's
-// scale of every block's group beside the weights, and a block's activation
-// scale is multiplied by it before the block's fused multiply-add; there is no
-// row scale at the end.
+// One step of the chains: lane c owns chain c = ((projection * N + token) << 3)
+// | row (row of the wavefront's 8) when c < 8*P*N. It reads its row's 8
+// turned-around block sums of the step and the token's 8 activation block
+// scales (and, with grouped weight scales, the row's 8 block weight scales)
+// and adds the first nv blocks in ascending order.
+template <int N, int P, bool GS>
+__device__ __forceinline__ void chain_step(float& acc, const float* tb, const float* xd, const float* sgw, int c,
+                                           int nbp, int j, int nv) {
+  if (c >= 8 * P * N) return;
+  constexpr int LN = N == 1 ? 0 : (N == 2 ? 1 : 2);
+  const int t = (c >> 3) & (N - 1), p = c >> (3 + LN), rl = c & 7;
+  const float4* s4 = reinterpret_cast<const float4*>(tb + c * 8);
+  const float4* d4 = reinterpret_cast<const float4*>(xd + t * nbp + 8 * j);
+  const float4 s0 = s4[0], s1 = s4[1], d0 = d4[0], d1 = d4[1];
+  const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  float dv[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+  if constexpr (GS) {
+    const float4* g4 = reinterpret_cast<const float4*>(sgw + (p * 8 + rl) * 8);
+    const float4 g0 = g4[0], g1 = g4[1];
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dv[q] = __fmul_rn(dv[q], gv[q]);
+  }
+  if (nv == 8) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc = fmaf(dv[q], sv[q], acc);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < nv) acc = fmaf(dv[q], sv[q], acc);
+  }
+}
+
+// GS: grouped weight scales. Each loading lane also streams its row's scale of
+// its block's group beside the weights and leaves it in the wavefront's LDS
+// slice for the chain, which multiplies the activation block scale by it before
+// the block's fused multiply-add; there is no row scale at the end.
 template <int N, int PF, bool TAP, int W, bool GS>
 __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
                                                 const uint8_t* w13, const float* s13, int tile, char* lds) {
-  const int H = a.H, I = a.I, nb = H / 32;
+  const int H = a.H, I = a.I, nb = H / 32, nbp = (nb + 7) & ~7;
   // the wavefront index is uniform: say so, so that its branches stay scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int r = tile * 64 + lane;
-  int8_t* xs = reinterpret_cast<int8_t*>(lds);
-  float* xd = reinterpret_cast<float*>(lds + (size_t)N * H);
+  const int rl = lane & 7, bs = lane >> 3, row = w * 8 + rl;  // loading lane: row of the tile, block of the step
+  const GemvLdsPlan LP = gemv_lds_plan(N, H, 2, GS);
+  int8_t* xs = reinterpret_cast<int8_t*>(lds + LP.xs);
+  float* xd = reinterpret_cast<float*>(lds + LP.xd);
+  float* tb = reinterpret_cast<float*>(lds + LP.tb) + (size_t)w * (16 * N) * 8;
+  float* sgw = reinterpret_cast<float*>(lds + LP.sg) + (size_t)w * 2 * 64;
+  float* hx = reinterpret_cast<float*>(lds + LP.hx);
   Staged<N> st;
   {
     const int8_t* src[N];
@@ -289,25 +359,22 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
     stage_load<N>(src, dsrc, H, st);
   }
   // the first weight blocks are requested before the staged codes are waited for
-  const int ncls = w < nb ? (nb - w + kGW - 1) / kGW : 0;  // blocks of class w
-  const int last = max(ncls - 1, 0);
-  const uint8_t* gcls = w13 + tbw_off<W>(tile, min(w, nb - 1), nb) + (size_t)lane * (4 * W);
-  const uint8_t* ucls = w13 + tbw_off<W>(I / 64 + tile, min(w, nb - 1), nb) + (size_t)lane * (4 * W);
-  constexpr size_t step = kGW * kTileBlock<W>;  // class stride
+  const int nsteps = (nb + 7) >> 3;
+  const uint8_t* gb = w13 + tbw_off<W>(tile, 0, nb) + (size_t)row * (4 * W);
+  const uint8_t* ub = w13 + tbw_off<W>(I / 64 + tile, 0, nb) + (size_t)row * (4 * W);
   const int gsh = GS ? a.gshift : 0, ngs = GS ? nb >> gsh : 0;
-  const float* gsc = s13 + (size_t)tile * ngs * 64 + lane;             // group scales of the gate row
-  const float* usc = s13 + (size_t)(I / 64 + tile) * ngs * 64 + lane;  // and of the up row
+  const float* gsc = s13 + (size_t)tile * ngs * 64 + row;             // group scales of the gate row
+  const float* usc = s13 + (size_t)(I / 64 + tile) * ngs * 64 + row;  // and of the up row
   WBlk<W> bg[PF], bu[PF];
   float sgq[PF], suq[PF];
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
-    const size_t off = (size_t)min(kk, last) * step;
-    load_wblk<W>(bg[kk], gcls + off);
-    load_wblk<W>(bu[kk], ucls + off);
+    const int b = min(8 * min(kk, nsteps - 1) + bs, nb - 1);
+    load_wblk<W>(bg[kk], gb + (size_t)b * kTileBlock<W>);
+    load_wblk<W>(bu[kk], ub + (size_t)b * kTileBlock<W>);
     if constexpr (GS) {
-      const size_t so = (size_t)((min(w, nb - 1) + kGW * min(kk, last)) >> gsh) * 64;
-      sgq[kk] = gsc[so];
-      suq[kk] = usc[so];
+      sgq[kk] = gsc[(size_t)(b >> gsh) * 64];
+      suq[kk] = usc[(size_t)(b >> gsh) * 64];
     }
   }
   stage_store<N>(st, H, xs, xd);
@@ -316,80 +383,71 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
     for (int i = 0; i < nn; ++i)
       if (slot_of(a, k, k.p0 + c0 + i) == a.sum_slot) tap_i = i;
   }
-  float ag[N], au[N];
+  float acc = 0.0f;  // this lane's chain (lane < 16 N)
+  for (int j0 = 0; j0 < nsteps; j0 += PF) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) ag[i] = au[i] = 0.0f;
-  if (ncls > 0) {
-    for (int j0 = 0; j0 < ncls; j0 += PF) {
-#pragma unroll
-      for (int kk = 0; kk < PF; ++kk) {
-        const int j = j0 + kk;
-        const bool live = j < ncls;
-        const int blk = w + kGW * min(j, ncls - 1);
+    for (int kk = 0; kk < PF; ++kk) {
+      const int j = j0 + kk;
+      if (j < nsteps) {
+        const int blk = 8 * j + bs;
+        const int bq = min(blk, nb - 1);
         WPrep<W> pg, pu;
         prep_wblk(bg[kk], pg);
         prep_wblk(bu[kk], pu);
         const float cg = GS ? sgq[kk] : 0.0f, cu = GS ? suq[kk] : 0.0f;
-        const size_t noff = (size_t)min(j + PF, ncls - 1) * step;  // past the end: a repeat (cache hit)
-        load_wblk<W>(bg[kk], gcls + noff);
-        load_wblk<W>(bu[kk], ucls + noff);
+        const int bn = min(8 * min(j + PF, nsteps - 1) + bs, nb - 1);  // past the end: a repeat (cache hit)
+        load_wblk<W>(bg[kk], gb + (size_t)bn * kTileBlock<W>);
+        load_wblk<W>(bu[kk], ub + (size_t)bn * kTileBlock<W>);
         if constexpr (GS) {
-          const size_t so = (size_t)((w + kGW * min(j + PF, ncls - 1)) >> gsh) * 64;
-          sgq[kk] = gsc[so];
-          suq[kk] = usc[so];
+          sgq[kk] = gsc[(size_t)(bn >> gsh) * 64];
+          suq[kk] = usc[(size_t)(bn >> gsh) * 64];
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-          const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)blk * 32);
+          const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)bq * 32);
           const v4i xa = xb4[0], xb = xb4[1];
-          const float d = xd[i * nb + blk];
           const int Sg = wdot(pg, xa, xb);
           const int Su = wdot(pu, xa, xb);
-          if (live) {
-            ag[i] = fmaf(GS ? __fmul_rn(d, cg) : d, (float)Sg, ag[i]);
-            au[i] = fmaf(GS ? __fmul_rn(d, cu) : d, (float)Su, au[i]);
-            if (TAP && i == tap_i) {
-              a.t_gu_sums[(size_t)r * nb + blk] = Sg;
-              a.t_gu_sums[(size_t)(I + r) * nb + blk] = Su;
-            }
+          tb[((i << 3) | rl) * 8 + bs] = (float)Sg;
+          tb[(((N + i) << 3) | rl) * 8 + bs] = (float)Su;
+          if (TAP && i == tap_i && blk < nb) {
+            a.t_gu_sums[(size_t)(tile * 64 + row) * nb + blk] = Sg;
+            a.t_gu_sums[(size_t)(I + tile * 64 + row) * nb + blk] = Su;
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (GS) {
+          sgw[rl * 8 + bs] = cg;
+          sgw[(8 + rl) * 8 + bs] = cu;
+        }
+        wave_sync();
+        chain_step<N, 2, GS>(acc, tb, xd, sgw, lane, nbp, j, min(8, nb - 8 * j));
+        wave_sync();
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // class totals meet in LDS: part[class][2*token + projection][row]
+  // chain results meet in LDS: hx[token][gate|up][row]; the row scale multiplies once
+  if (lane < 16 * N) {
+    constexpr int LN = N == 1 ? 0 : (N == 2 ? 1 : 2);
+    const int t = (lane >> 3) & (N - 1), pj = lane >> (3 + LN), rr = w * 8 + (lane & 7);
+    hx[(t * 2 + pj) * 64 + rr] = GS ? acc : __fmul_rn(s13[pj * I + tile * 64 + rr], acc);
+  }
   __syncthreads();
-  float* part = reinterpret_cast<float*>(lds);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    part[(w * 2 * N + 2 * i) * 64 + lane] = ag[i];
-    part[(w * 2 * N + 2 * i + 1) * 64 + lane] = au[i];
-  }
-  __syncthreads();
-  if (w < nn) {
-    float g = 0.0f, u = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kGW; ++c) {
-      g = __fadd_rn(g, part[(c * 2 * N + 2 * w) * 64 + lane]);
-      u = __fadd_rn(u, part[(c * 2 * N + 2 * w + 1) * 64 + lane]);
-    }
-    if (!GS) {
-      g = __fmul_rn(s13[r], g);
-      u = __fmul_rn(s13[I + r], u);
-    }
-    store_h_lanes(a, k, k.p0 + c0 + w, r, lane, g, u);
-  }
+  if (w < nn) store_h_lanes(a, k, k.p0 + c0 + w, tile * 64 + lane, lane, hx[(w * 2) * 64 + lane],
+                            hx[(w * 2 + 1) * 64 + lane]);
 }
 
 template <int N, int PF, bool TAP, int W, bool GS>
 __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
                                               const uint8_t* w2, const float* s2, int tile, char* lds) {
-  const int H = a.H, I = a.I, nbi = I / 32;
+  const int H = a.H, I = a.I, nbi = I / 32, nbp = (nbi + 7) & ~7;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int o = tile * 64 + lane;
-  int8_t* hs = reinterpret_cast<int8_t*>(lds);
-  float* hd = reinterpret_cast<float*>(lds + (size_t)N * I);
+  const int rl = lane & 7, bs = lane >> 3, row = w * 8 + rl;
+  const GemvLdsPlan LP = gemv_lds_plan(N, I, 1, GS);
+  int8_t* hs = reinterpret_cast<int8_t*>(lds + LP.xs);
+  float* hd = reinterpret_cast<float*>(lds + LP.xd);
+  float* tb = reinterpret_cast<float*>(lds + LP.tb) + (size_t)w * (8 * N) * 8;
+  float* sgw = reinterpret_cast<float*>(lds + LP.sg) + (size_t)w * 64;
   Staged<N> st;
   {
     const int8_t* src[N];
@@ -402,18 +460,17 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
     }
     stage_load<N>(src, dsrc, I, st);
   }
-  const int ncls = w < nbi ? (nbi - w + kGW - 1) / kGW : 0;
-  const int last = max(ncls - 1, 0);
-  const uint8_t* wcls = w2 + tbw_off<W>(tile, min(w, nbi - 1), nbi) + (size_t)lane * (4 * W);
-  constexpr size_t step = kGW * kTileBlock<W>;
+  const int nsteps = (nbi + 7) >> 3;
+  const uint8_t* wb = w2 + tbw_off<W>(tile, 0, nbi) + (size_t)row * (4 * W);
   const int gsh = GS ? a.gshift : 0, ngs = GS ? nbi >> gsh : 0;
-  const float* osc = s2 + (size_t)tile * ngs * 64 + lane;  // group scales of the output row
+  const float* osc = s2 + (size_t)tile * ngs * 64 + row;  // group scales of the output row
   WBlk<W> bw[PF];
   float soq[PF];
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
-    load_wblk<W>(bw[kk], wcls + (size_t)min(kk, last) * step);
-    if constexpr (GS) soq[kk] = osc[(size_t)((min(w, nbi - 1) + kGW * min(kk, last)) >> gsh) * 64];
+    const int b = min(8 * min(kk, nsteps - 1) + bs, nbi - 1);
+    load_wblk<W>(bw[kk], wb + (size_t)b * kTileBlock<W>);
+    if constexpr (GS) soq[kk] = osc[(size_t)(b >> gsh) * 64];
   }
   stage_store<N>(st, I, hs, hd);
   int tap_i = -1;
@@ -421,110 +478,49 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
     for (int i = 0; i < nn; ++i)
       if (slot_of(a, k, k.p0 + c0 + i) == a.sum_slot) tap_i = i;
   }
-  float acc[N];
+  float acc = 0.0f;
+  for (int j0 = 0; j0 < nsteps; j0 += PF) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
-  if (ncls > 0) {
-    for (int j0 = 0; j0 < ncls; j0 += PF) {
-#pragma unroll
-      for (int kk = 0; kk < PF; ++kk) {
-        const int j = j0 + kk;
-        const bool live = j < ncls;
-        const int blk = w + kGW * min(j, ncls - 1);
+    for (int kk = 0; kk < PF; ++kk) {
+      const int j = j0 + kk;
+      if (j < nsteps) {
+        const int blk = 8 * j + bs;
+        const int bq = min(blk, nbi - 1);
         WPrep<W> pw;
         prep_wblk(bw[kk], pw);
         const float co = GS ? soq[kk] : 0.0f;
-        load_wblk<W>(bw[kk], wcls + (size_t)min(j + PF, ncls - 1) * step);
-        if constexpr (GS) soq[kk] = osc[(size_t)((w + kGW * min(j + PF, ncls - 1)) >> gsh) * 64];
+        const int bn = min(8 * min(j + PF, nsteps - 1) + bs, nbi - 1);
+        load_wblk<W>(bw[kk], wb + (size_t)bn * kTileBlock<W>);
+        if constexpr (GS) soq[kk] = osc[(size_t)(bn >> gsh) * 64];
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-          const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)blk * 32);
+          const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)bq * 32);
           const int S = wdot(pw, hb4[0], hb4[1]);
-          if (live) {
-            const float d = hd[i * nbi + blk];
-            acc[i] = fmaf(GS ? __fmul_rn(d, co) : d, (float)S, acc[i]);
-            if (TAP && i == tap_i) a.t_dn_sums[(size_t)o * nbi + blk] = S;
-          }
+          tb[((i << 3) | rl) * 8 + bs] = (float)S;
+          if (TAP && i == tap_i && blk < nbi) a.t_dn_sums[(size_t)(tile * 64 + row) * nbi + blk] = S;
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (GS) sgw[rl * 8 + bs] = co;
+        wave_sync();
+        chain_step<N, 1, GS>(acc, tb, hd, sgw, lane, nbp, j, min(8, nbi - 8 * j));
+        wave_sync();
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  __syncthreads();
-  float* part = reinterpret_cast<float*>(lds);  // part[class][token][row]
-#pragma unroll
-  for (int i = 0; i < N; ++i) part[(w * N + i) * 64 + lane] = acc[i];
-  __syncthreads();
-  if (w < nn) {
-    float e = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kGW; ++c) e = __fadd_rn(e, part[(c * N + w) * 64 + lane]);
-    if (!GS) e = __fmul_rn(s2[o], e);
-    const int p = k.p0 + c0 + w;
-    a.eout[(size_t)p * H + o] = e;
-    if (a.t_eout) a.t_eout[(size_t)slot_of(a, k, p) * H + o] = e;
+  if (lane < 8 * N) {
+    const int t = lane >> 3, o = tile * 64 + w * 8 + (lane & 7);
+    if (t < nn) {
+      const float e = GS ? acc : __fmul_rn(s2[o], acc);
+      const int p = k.p0 + c0 + t;
+      a.eout[(size_t)p * H + o] = e;
+      if (a.t_eout) a.t_eout[(size_t)slot_of(a, k, p) * H + o] = e;
+    }
   }
 }
 
 // ------------------------------------------------------------------ MFMA paths
-// One wavefront walks all K blocks of its tile in class-major order (class 0's
-// blocks ascending, then class 1's, ...), keeps one fp32 chain for the current
-// class and folds it into the running total when the class ends: the same
-// arithmetic as the GEMV path, class by class instead of class per wavefront.
-// The walk index is wave-uniform (scalar registers); the totals, touched once
-// per class, live in the wavefront's LDS slice so the registers hold only the
-// chains, the prefetch ring and the MFMA results.
-
-// Block after blk in the class-major walk (the next of its class, else the
-// first of the next class), clamped to a valid block past the walk's end.
-// Branch-free (blk >= 0, kDotClasses a power of two), so a loop slot that
-// advances it stays one basic block.
-__device__ __forceinline__ int class_major_next(int blk, int nb) {
-  static_assert((kDotClasses & (kDotClasses - 1)) == 0, "kDotClasses must be a power of two");
-  const int n = blk + kDotClasses, wrap = (blk & (kDotClasses - 1)) + 1;
-  return min(n < nb ? n : wrap, nb - 1);
-}
-
-// Per-wavefront LDS for the class totals: [NTT][gate|up][16/4][64 lanes] float4.
-template <int NTT, int NM>
-struct MfmaTotals {
-  float4 v[NTT][NM][4][64];
-};
-
-template <int NTT, int NM>
-__device__ __forceinline__ void totals_zero(MfmaTotals<NTT, NM>& T, int lane) {
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) T.v[tt][m][g][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-}
-
-// total += chain (round to nearest), chain = 0.
-__device__ __forceinline__ void fold16(float4* tot, float (&c)[16], int lane) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float4 t = tot[g * 64 + lane];
-    t.x = __fadd_rn(t.x, c[4 * g + 0]);
-    t.y = __fadd_rn(t.y, c[4 * g + 1]);
-    t.z = __fadd_rn(t.z, c[4 * g + 2]);
-    t.w = __fadd_rn(t.w, c[4 * g + 3]);
-    tot[g * 64 + lane] = t;
-    c[4 * g + 0] = c[4 * g + 1] = c[4 * g + 2] = c[4 * g + 3] = 0.0f;
-  }
-}
-
-__device__ __forceinline__ void totals_get(const float4* tot, float (&o)[16], int lane) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const float4 t = tot[g * 64 + lane];
-    o[4 * g + 0] = t.x;
-    o[4 * g + 1] = t.y;
-    o[4 * g + 2] = t.z;
-    o[4 * g + 3] = t.w;
-  }
-}
+// One wavefront walks all K blocks of its tile in ascending order and keeps
+// one fp32 chain per result element: the same arithmetic as the GEMV path.
 
 // Raw buffer resources over wave-uniform bases: a block's loads take the block
 // offset in a scalar register and the lane's offset in a vector register, so
@@ -609,11 +605,6 @@ __device__ __forceinline__ int true_sum(int s) {
 // 8q + 4*half + j, j = 0..3, one float4 per q. Two slots alternate, and the
 // wavefront-level fence in scales_put orders a slot's write after the reads
 // of its previous use and before its new reads.
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __device__ __forceinline__ void scales_put(float* slot, float mine, int lane) {
   slot[lane] = mine;
@@ -656,7 +647,7 @@ __device__ __forceinline__ void load_dn_block(__amdgpu_buffer_rsrc_t wr, __amdgp
 // stored; each column's results depend on that column alone.
 template <int NTT, int PF, bool TAP, int W, bool GS>
 __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w13, const float* s13,
-                                 int t32, int lane, MfmaTotals<NTT, 2>& T, float* scl) {
+                                 int t32, int lane, float* scl) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nb = H / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -678,13 +669,12 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
     xso[tt] = (uint32_t)(pb_sc(p, 0, nb) - pb_sc(g0 * 32, 0, nb)) * 4;
     if (TAP && valid[tt] && slot_of(a, k, p) == a.sum_slot) tap_tt = tt;
   }
-  totals_zero(T, lane);
   const v16i zero = {0};
   const int r0 = tile * 64 + s * 32;
   const auto gr = buf_rsrc(w13 + tbw_off<W>(tile, 0, nb) + s * 32 * (4 * W));
   const auto ur = buf_rsrc(w13 + tbw_off<W>(I / 64 + tile, 0, nb) + s * 32 * (4 * W));
   const auto xr = buf_rsrc(xbase), dr = buf_rsrc(dbase);
-  float ag[NTT][16], au[NTT][16];  // class chains
+  float ag[NTT][16], au[NTT][16];  // one chain per result element
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -705,7 +695,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
     load_codes<NTT>(xr, fetch, xo, rb[kk]);
     if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
     load_scales<NTT>(dr, fetch, xso, rd[kk]);
-    fetch = class_major_next(fetch, nb);
+    fetch = min(fetch + 1, nb - 1);  // past the end: a repeat (cache hit)
   }
   int blk = 0;  // block being consumed
   for (int b0 = 0; b0 < nb; b0 += PF) {
@@ -748,15 +738,8 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
         }
       }
       load_scales<NTT>(dr, fetch, xso, rd[kk]);
-      fetch = class_major_next(fetch, nb);
-      if (blk + kDotClasses >= nb) {  // blk ends its class
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          fold16(&T.v[tt][0][0][0], ag[tt], lane);
-          fold16(&T.v[tt][1][0][0], au[tt], lane);
-        }
-      }
-      blk = class_major_next(blk, nb);
+      fetch = min(fetch + 1, nb - 1);
+      ++blk;
     }
   }
   float sg[16], su[16];  // row scales (one scale per row only)
@@ -767,9 +750,9 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   }
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
-    float tg[16], tu[16], h[16];
-    totals_get(&T.v[tt][0][0][0], tg, lane);
-    totals_get(&T.v[tt][1][0][0], tu, lane);
+    const float(&tg)[16] = ag[tt];
+    const float(&tu)[16] = au[tt];
+    float h[16];
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -806,7 +789,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
 // 32-row block. Columns past the bucket's end as in the gate/up tile.
 template <int NTT, int PF, bool TAP, int W, bool GS>
 __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w2, const float* s2,
-                               int t32, int lane, MfmaTotals<NTT, 1>& T, float* scl) {
+                               int t32, int lane, float* scl) {
   const int tile = t32 >> 1, s = t32 & 1;
   const int H = a.H, I = a.I, nbi = I / 32;
   const int col = lane & 31, half = lane >> 5;
@@ -826,12 +809,11 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
     xso[tt] = (uint32_t)(pb_sc(p, 0, nbi) - pb_sc(g0 * 32, 0, nbi)) * 4;
     if (TAP && valid[tt] && slot_of(a, k, p) == a.sum_slot) tap_tt = tt;
   }
-  totals_zero(T, lane);
   const v16i zero = {0};
   const int r0 = tile * 64 + s * 32;
   const auto wr = buf_rsrc(w2 + tbw_off<W>(tile, 0, nbi) + s * 32 * (4 * W));
   const auto xr = buf_rsrc(xbase), dr = buf_rsrc(dbase);
-  float acc[NTT][16];  // class chain
+  float acc[NTT][16];  // one chain per result element
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
@@ -850,7 +832,7 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
     load_codes<NTT>(xr, fetch, xo, rb[kk]);
     if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
     load_scales<NTT>(dr, fetch, xso, rd[kk]);
-    fetch = class_major_next(fetch, nbi);
+    fetch = min(fetch + 1, nbi - 1);
   }
   int blk = 0;
   for (int b0 = 0; b0 < nbi; b0 += PF) {
@@ -883,12 +865,8 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
         }
       }
       load_scales<NTT>(dr, fetch, xso, rd[kk]);
-      fetch = class_major_next(fetch, nbi);
-      if (blk + kDotClasses >= nbi) {
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) fold16(&T.v[tt][0][0][0], acc[tt], lane);
-      }
-      blk = class_major_next(blk, nbi);
+      fetch = min(fetch + 1, nbi - 1);
+      ++blk;
     }
   }
   float so[16];  // row scales (one scale per row only)
@@ -897,8 +875,7 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
     if (!valid[tt]) continue;
-    float tot[16];
-    totals_get(&T.v[tt][0][0][0], tot, lane);
+    const float(&tot)[16] = acc[tt];
     const int p = k.p0 + t0 + tt * 32 + col;
     float* orow = a.eout + (size_t)p * H + r0;
     float* trow = a.t_eout ? a.t_eout + (size_t)slot_of(a, k, p) * H + r0 : nullptr;
@@ -997,17 +974,15 @@ __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t*
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
   const float* s13 = expert_s13(a.wv, k.ex, a.E, s13_count(a.H, a.I, GS ? a.gshift : -1));
-  __shared__ MfmaTotals<NTT, 2> totals;
   float* sc = nullptr;  // two 64-float slots for the group scales (GS only: no LDS otherwise)
   if constexpr (GS) {
     __shared__ float scl[2 * 64];
     sc = scl;
   }
   if (NTT == 2 && k.n - t0 <= 32)  // a bucket's last tile with one 32-token half: skip the empty one
-    mfma_gateup_tile<1, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane,
-                                         reinterpret_cast<MfmaTotals<1, 2>&>(totals), sc);
+    mfma_gateup_tile<1, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane, sc);
   else
-    mfma_gateup_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane, totals, sc);
+    mfma_gateup_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane, sc);
 }
 
 template <int NTT, int MPF, bool TAP, int W, bool GS>
@@ -1019,28 +994,26 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
   const float* s2 = expert_s2(a.wv, k.ex, a.E, s2_count(a.H, a.I, GS ? a.gshift : -1));
-  __shared__ MfmaTotals<NTT, 1> totals;
   float* sc = nullptr;
   if constexpr (GS) {
     __shared__ float scl[2 * 64];
     sc = scl;
   }
   if (NTT == 2 && k.n - t0 <= 32)
-    mfma_down_tile<1, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, reinterpret_cast<MfmaTotals<1, 1>&>(totals),
-                                       sc);
+    mfma_down_tile<1, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, sc);
   else
-    mfma_down_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, totals, sc);
+    mfma_down_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, sc);
 }
 
 // Blocks in flight per wavefront: about 4 KB of weights per wavefront when
 // many buckets stream at once (2 blocks of the two gate/up streams, 4 of the
 // single down stream), half that with a few buckets, where fewer queued
-// requests finish sooner. A depth is used only if it divides the class length.
+// requests finish sooner. A depth is used only if it divides the step count.
 constexpr int kPfGateupMany = 2, kPfGateupFew = 1, kPfDownMany = 4, kPfDownFew = 2;
 
 static int gemv_pf(int nblocks, int want) {
-  const int per_class = (nblocks + kGW - 1) / kGW;
-  while (want > 1 && per_class % want != 0) want >>= 1;
+  const int steps = (nblocks + 7) / 8;
+  while (want > 1 && steps % want != 0) want >>= 1;
   return want;
 }
 
@@ -1078,7 +1051,7 @@ static void down_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_
 hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(a.I / 64, grid);
-  const size_t lds = gemv_lds_bytes(max_chunk, a.H, 2);
+  const size_t lds = gemv_lds_bytes(max_chunk, a.H, 2, a.gshift >= 0);
   switch (gemv_pf(a.H / 32, many ? kPfGateupMany : kPfGateupFew)) {
     case 4: gateup_gemv_launch<4>(a, g, lds, st); break;
     case 2: gateup_gemv_launch<2>(a, g, lds, st); break;
@@ -1090,7 +1063,7 @@ hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_
 hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(a.H / 64, grid);
-  const size_t lds = gemv_lds_bytes(max_chunk, a.I, 1);
+  const size_t lds = gemv_lds_bytes(max_chunk, a.I, 1, a.gshift >= 0);
   switch (gemv_pf(a.I / 32, many ? kPfDownMany : kPfDownFew)) {
     case 4: down_gemv_launch<4>(a, g, lds, st); break;
     case 2: down_gemv_launch<2>(a, g, lds, st); break;

@@ -40,6 +40,7 @@ extern "C" int32_t moe_membench_read(const void* buf, size_t bytes, int32_t bloc
                                      hipStream_t stream) {
   if (!buf || !sink) return MOE_E_NULL;
   if (bytes % 16 != 0 || blocks <= 0) return MOE_E_SHAPE;
+  if (!aligned16(buf)) return MOE_E_ARG;
   const uint4* s = static_cast<const uint4*>(buf);
   switch (unroll) {
     case 1: k_read<1><<<blocks, 256, 0, stream>>>(s, bytes / 16, sink); break;
@@ -49,13 +50,14 @@ extern "C" int32_t moe_membench_read(const void* buf, size_t bytes, int32_t bloc
     default: return MOE_E_ARG;
   }
   hipError_t e = hipGetLastError();
-  return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
 extern "C" int32_t moe_membench_copy(const void* src, void* dst, size_t bytes, int32_t blocks, hipStream_t stream) {
   if (!src || !dst) return MOE_E_NULL;
   if (bytes % 16 != 0 || blocks <= 0) return MOE_E_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_E_ARG;
   k_copy<<<blocks, 256, 0, stream>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst), bytes / 16);
   hipError_t e = hipGetLastError();
-  return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
 }

@@ -348,6 +348,7 @@ int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float
   int rc = validate_config(cfg);
   if (rc) return rc;
   if (!x || !router_w || !router_bias || !topk_ids || !topk_w) return MOE_E_NULL;
+  if (!aligned16(x) || !aligned16(router_w)) return MOE_E_ARG;
   if ((rc = check_tokens(cfg, T))) return rc;
   Layout L = make_layout(*cfg, T);
   if ((rc = check_ws(L, ws, ws_bytes))) return rc;
@@ -379,6 +380,7 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   if (!wts || !x || !y) return MOE_E_NULL;
   if (!wts->router_w || !wts->router_bias || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_E_NULL;
   if (cfg->n_shared > 0 && (!wts->sh_w13 || !wts->sh_s13 || !wts->sh_w2 || !wts->sh_s2)) return MOE_E_NULL;
+  if (!layer_ptrs_aligned(wts, x, y, true)) return MOE_E_ARG;
   WeightView wv{wts->w13, wts->s13, wts->w2, wts->s2, wts->sh_w13, wts->sh_s13, wts->sh_w2, wts->sh_s2, nullptr};
   Fwd f;
   if ((rc = fwd_setup(cfg, wv, T, ws, ws_bytes, taps, &f))) return rc;

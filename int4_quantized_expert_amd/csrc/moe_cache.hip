@@ -282,6 +282,7 @@ int32_t moe_expert_cache_forward(moe_expert_cache* c, const moe_layer_weights* r
   if (!res->router_w || !res->router_bias) return MOE_E_NULL;
   if (cfg->n_shared > 0 && (!res->sh_w13 || !res->sh_s13 || !res->sh_w2 || !res->sh_s2)) return MOE_E_NULL;
   if (!host->w13 || !host->s13 || !host->w2 || !host->s2) return MOE_E_NULL;
+  if (!layer_ptrs_aligned(res, x, y, false)) return MOE_E_ARG;
   if (T < 1 || T > c->max_tokens) return MOE_E_SHAPE;
   if (compute == copy) return MOE_E_ARG;
   int dev = -1;

@@ -23,7 +23,6 @@ constexpr int kRouterParts = kRouterChunks / kRouterWaves;  // stored partial su
 constexpr int kDefaultGemmMin = 5;   // bucket size from which the MFMA path runs (a GEMV chunk holds at most 4)
 constexpr int kMaxHidden = 16384;  // hidden and inter sizes (GEMV stages two 16-byte loads per lane)
 constexpr int kGemvMaxN = 4;         // tokens per GEMV work item (chunk)
-constexpr int kDotClasses = 8;       // fp32 accumulation classes of a dot: block b is in class b % 8
 
 // Bucket b: routed unique experts b < n_unique (ascending expert id), then the
 // shared experts. bk_e = expert index (E + s for shared expert s), bk_p0 =
@@ -123,6 +122,16 @@ hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float*
                      hipStream_t stream, int call);
 hipError_t fwd_combine(Fwd& f, float* y, hipStream_t stream);
 int32_t hip_fail(hipError_t e);
+// Arrays the kernels read or write as 16-byte vectors must start on a 16-byte boundary.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// x, y, router weights and the weight codes of a layer (16-byte vector access)
+inline bool layer_ptrs_aligned(const moe_layer_weights* w, const float* x, const float* y, bool routed) {
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w->router_w)) return false;
+  if (routed && (!aligned16(w->w13) || !aligned16(w->w2))) return false;
+  if (w->sh_w13 && !aligned16(w->sh_w13)) return false;
+  if (w->sh_w2 && !aligned16(w->sh_w2)) return false;
+  return true;
+}
 
 // ------------------------------------------------------------ weight layout
 // Int4 matrices are stored in tile-blocks of 64 rows x one 32-element block:
