@@ -47,6 +47,9 @@
  *    stream) and kept until the process ends.
  *  - Stateless calls are re-entrant on distinct streams; a cache object is not
  *    thread-safe.
+ *  - x, y, router_w and the int4 / int8 weight code arrays are read or written
+ *    as 16-byte vectors and must start on a 16-byte boundary (MOE_E_ARG
+ *    otherwise); torch allocations are 256-byte aligned.
  *
  * Weight layout ("row-tiled int4", rows of K int4 values, K % 32 == 0,
  * rows % 64 == 0): two's-complement nibbles, element 2j of a 32-element block
@@ -238,6 +241,22 @@ int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, 
  * taps may be NULL. */
 int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
                           void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * forward as moe_layer_forward, with the same results bit for bit, but with
+ * its workspace in a fixed array of the library, MOE_NOALLOC_WORKSPACE_BYTES
+ * per GPU (held from the library's first use of that GPU until the process
+ * ends), so the caller passes inputs and outputs only. It calls no allocating
+ * routine: no helper stream either, both expert chains run on `stream`.
+ * Errors: as moe_layer_forward; MOE_E_WORKSPACE when moe_workspace_bytes(cfg,
+ * T) exceeds MOE_NOALLOC_WORKSPACE_BYTES (GLM-5.2 shape: T up to 192).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, two threads) race and must be serialized by the caller.
+ * Nothing in the array needs to start at zero; every call writes what it reads. */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)128 << 20)
+int32_t moe_layer_forward_noalloc(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T,
+                                  float* y, const moe_taps* taps, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Per-layer LRU expert cache [A][C]: routed experts live in pinned host

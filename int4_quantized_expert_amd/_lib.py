@@ -78,6 +78,7 @@ _sig("moe_quantize_q8_0", I32, [P, I64, P, P, P])
 _sig("moe_router", I32, [P, P, I32, P, P, P, P, P, P, SZ, P])
 _sig("moe_dispatch", I32, [P, P, I32, P, P, P, P, P, P, P, SZ, P])
 _sig("moe_layer_forward", I32, [P, P, P, I32, P, P, SZ, P, P])
+_sig("moe_layer_forward_noalloc", I32, [P, P, P, I32, P, P, P])
 _sig("moe_expert_cache_create", I32, [P, I32, I32, ctypes.POINTER(P)])
 _sig("moe_expert_cache_forward", I32, [P, P, P, P, I32, P, P, SZ, P, P, P, P])
 _sig("moe_expert_cache_stats", I32, [P, P])
@@ -93,7 +94,7 @@ _sig("moe_membench_copy", I32, [P, P, SZ, I32, P])
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_workspace_bytes", "moe_quantize_int4",
             "moe_quantize_int8", "moe_quantize_int4_grouped", "moe_quantize_q8_0", "moe_router", "moe_dispatch", "moe_layer_forward",
-            "moe_expert_cache_create",
+            "moe_layer_forward_noalloc", "moe_expert_cache_create",
             "moe_expert_cache_forward", "moe_expert_cache_stats", "moe_expert_cache_usage", "moe_expert_cache_set_usage",
             "moe_expert_cache_pin_hottest", "moe_expert_cache_destroy", "moe_prof_enable",
             "moe_prof_read", "moe_prof_disable", "moe_membench_read", "moe_membench_copy")
@@ -219,6 +220,18 @@ def moe_layer_forward(cfg: Config, weights: moe_layer_weights, x, y, ws, tap: mo
                   _lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(weights), _ptr(x), T, _ptr(y), _ptr(ws),
                                          ws.numel() * ws.element_size(), ctypes.byref(tap) if tap else None,
                                          _stream(stream)))
+
+
+NOALLOC_WORKSPACE_BYTES = 128 << 20  # MOE_NOALLOC_WORKSPACE_BYTES
+
+
+def moe_layer_forward_noalloc(cfg: Config, weights: moe_layer_weights, x, y, tap: moe_taps | None = None,
+                              stream=None, T: int | None = None):
+    c = cfg.c()
+    T = x.shape[0] if T is None else T
+    return _check("moe_layer_forward_noalloc",
+                  _lib.moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(weights), _ptr(x), T, _ptr(y),
+                                                 ctypes.byref(tap) if tap else None, _stream(stream)))
 
 
 def moe_prof_enable(max_calls: int, stages=None):

@@ -373,8 +373,15 @@ int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, 
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
-int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
-                          void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream) {
+}  // extern "C"
+
+namespace moe {
+
+// One resident-layer forward on `stream`. With use_helper the MFMA chain runs on
+// the helper stream beside the GEMV chain (fork/join); without it both chains
+// run one after the other on `stream` and nothing is created.
+int32_t layer_forward_impl(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
+                           void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream, bool use_helper) {
   int rc = validate_config(cfg);
   if (rc) return rc;
   if (!wts || !x || !y) return MOE_E_NULL;
@@ -385,7 +392,7 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   Fwd f;
   if ((rc = fwd_setup(cfg, wv, T, ws, ws_bytes, taps, &f))) return rc;
   Helper hp;
-  const bool fork = f.grid_tiles > 0;
+  const bool fork = use_helper && f.grid_tiles > 0;
   if (fork) {
     hipError_t he = get_helper(stream, &hp);
     if (he != hipSuccess) return hip_fail(he);
@@ -406,6 +413,11 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
     if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 11, hp.side);
   }
+  if (e == hipSuccess && !use_helper && f.grid_tiles > 0) {  // the MFMA chain on the caller's stream
+    e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, stream);
+    if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, stream);
+    if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, stream);
+  }
   if (e == hipSuccess) e = launch_gemv_gateup(f.a, f.grid_gemv, f.many, f.gemv_chunk, stream);
   prof_mark(call, 5, stream);
   if (e == hipSuccess) e = launch_gemv_down(f.a, f.grid_gemv, f.many, f.gemv_chunk, stream);
@@ -423,6 +435,15 @@ int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, c
   if (e == hipSuccess) e = fwd_combine(f, y, stream);
   prof_mark(call, 8, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+int32_t moe_layer_forward(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
+                          void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream) {
+  return layer_forward_impl(cfg, wts, x, T, y, ws, ws_bytes, taps, stream, true);
 }
 
 int32_t moe_prof_enable(int32_t max_calls, uint32_t stage_mask) {

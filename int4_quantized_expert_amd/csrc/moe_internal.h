@@ -121,6 +121,9 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
 hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
                      hipStream_t stream, int call);
 hipError_t fwd_combine(Fwd& f, float* y, hipStream_t stream);
+// moe_layer_forward with or without the helper stream (see moe_api.hip)
+int32_t layer_forward_impl(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
+                           void* ws, size_t ws_bytes, const moe_taps* taps, hipStream_t stream, bool use_helper);
 int32_t hip_fail(hipError_t e);
 // Arrays the kernels read or write as 16-byte vectors must start on a 16-byte boundary.
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -99,3 +99,33 @@ def test_validation_before_any_device_work():
     assert rc == L.MOE_E_WORKSPACE
     rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(wts), x, 0, x, x, 1 << 40, None, None)
     assert rc == L.MOE_E_SHAPE
+
+
+def test_noalloc_validation_before_any_device_work():
+    c = _glm().c()
+    w = L.moe_layer_weights()
+    rc = L._lib.moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(w), None, 4, None, None, None)
+    assert rc == L.MOE_E_NULL
+    bad = _glm(hidden=100).c()
+    rc = L._lib.moe_layer_forward_noalloc(ctypes.byref(bad), ctypes.byref(w), None, 4, None, None, None)
+    assert rc == L.MOE_E_SHAPE
+    x = ctypes.c_void_p(4096)
+    wts = L.moe_layer_weights(*([4096] * 10))
+    # the GLM shape at 2048 tokens needs more than the fixed array holds
+    assert moe.moe_workspace_bytes(_glm(), 2048) > moe.NOALLOC_WORKSPACE_BYTES
+    rc = L._lib.moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(wts), x, 2048, x, None, None)
+    assert rc == L.MOE_E_WORKSPACE
+    rc = L._lib.moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(wts), x, 0, x, None, None)
+    assert rc == L.MOE_E_SHAPE
+
+
+def test_misaligned_inputs_rejected_before_any_device_work():
+    c = _glm().c()
+    x = ctypes.c_void_p(4096)
+    wts = L.moe_layer_weights(*([4096] * 10))
+    rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(wts), ctypes.c_void_p(4100), 4, x, x, 1 << 40,
+                                  None, None)
+    assert rc == L.MOE_E_ARG
+    wts2 = L.moe_layer_weights(*([4096, 4096, 4104] + [4096] * 7))
+    rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(wts2), x, 4, x, x, 1 << 40, None, None)
+    assert rc == L.MOE_E_ARG
