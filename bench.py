@@ -47,7 +47,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50; stack40: 12)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; stack40: 4)")
-    ap.add_argument("--workload", default="decode32", choices=["decode32", "decode1", "mtp192", "prefill", "stack40"])
+    ap.add_argument("--workload", default="decode32", choices=["decode32", "decode1", "mtp192", "prefill", "stack40"],
+                    help="the headline workload of the JSON line")
+    ap.add_argument("--configs", default=None,
+                    help="comma-separated further workloads measured in the same run and reported under 'configs' "
+                         "(default with the decode32 headline: decode1,mtp192,prefill,stack40; '' for none)")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps of each further workload")
     ap.add_argument("--stack-layers", type=int, default=40, help="stack40: layers in the stack")
     ap.add_argument("--streamed", type=int, default=20, help="stack40: last layers whose experts stream from host")
     ap.add_argument("--slots", type=int, default=64, help="stack40: HBM expert slots per streamed layer")
@@ -78,6 +83,12 @@ def parse():
         a.steps = 12 if a.workload == "stack40" else 50
     if a.warmup is None:
         a.warmup = 4 if a.workload == "stack40" else 5
+    if a.configs is None:
+        a.configs = "decode1,mtp192,prefill,stack40" if a.workload == "decode32" else ""
+    a.configs = [w for w in a.configs.split(",") if w and w != a.workload]
+    bad = [w for w in a.configs if w not in ("decode32", "decode1", "mtp192", "prefill", "stack40")]
+    if bad:
+        ap.error(f"unknown workloads in --configs: {bad}")
     return a
 
 
@@ -362,6 +373,200 @@ def run_stack(args):
         c.destroy()
 
 
+def heat_summary(stats):
+    """Expert heat of the timed steps: how many routed positions the unique experts get (bucket sizes), the
+    hottest experts' counts and the share of positions the hottest 8 experts take."""
+    edges = [(1, 1), (2, 2), (3, 4), (5, 8), (9, 16), (17, 32), (33, 64), (65, 128), (129, 1 << 30)]
+    hist = {f"{lo}" if lo == hi else (f"{lo}-{hi}" if hi < 1 << 30 else f"{lo}+"): 0.0 for lo, hi in edges}
+    hot, share = [], []
+    for st in stats:
+        c = st["counts"][st["counts"] > 0]
+        for (lo, hi), k in zip(edges, hist):
+            hist[k] += float(((c >= lo) & (c <= hi)).sum()) / len(stats)
+        srt = np.sort(c)[::-1]
+        hot.append(srt[:5].astype(np.float64))
+        share.append(float(srt[:8].sum()) / max(1.0, float(c.sum())))
+    return dict(bucket_sizes={k: round(v, 2) for k, v in hist.items()},
+                hottest5_mean=[round(float(v), 1) for v in np.mean(hot, axis=0)],
+                top8_share=round(float(np.mean(share)), 4))
+
+
+def measured_hbm_peak(moe, torch):
+    """Best streaming read rate of plain grid-stride read kernels over 4 GiB (GB/s), a few launch shapes."""
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for blocks in (2048, 4096, 8192):
+        for unroll in (2, 4, 8):
+            moe.moe_membench_read(buf, blocks, unroll, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                moe.moe_membench_read(buf, blocks, unroll, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, 3 * n / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del buf
+    return round(best, 1)
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return dict(cpu_model=model, nproc=os.cpu_count(), nproc_available=avail)
+
+
+def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_measured):
+    """One workload's timed pass and its roofline figures (the JSON fields of a bench line, without the CPU
+    baseline)."""
+    T = tokens_of(workload)
+    dev = torch.device("cuda:0")
+    WB, GSZ = args.weight_bits, args.group_size
+    n_in = args.warmup + steps
+    xs_host = make_inputs(shape, workload, min(n_in, 64), args.seed)
+    xs = [torch.from_numpy(x).to(dev) for x in xs_host]
+    ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, shape.hidden), dtype=torch.float32, device=dev)
+    ncopy = len(layers)
+
+    # routing statistics of every timed step (outside the timed region)
+    stats = []
+    for s in range(steps):
+        i = args.warmup + s
+        stats.append(routing_stats(moe, cfg, layers[i % ncopy], xs[i % len(xs)], ws, args.gemm_min))
+
+    stream = torch.cuda.current_stream()
+    for s in range(args.warmup):
+        moe.moe_layer_forward(cfg, wts[s % ncopy], xs[s % len(xs)], y, ws)
+    torch.cuda.synchronize()
+    # dominant kernel: the gate-up launch of the path that moves most bytes; the
+    # timed region records HIP events around it only (on the stream it runs on)
+    kname = "gateup_mfma" if workload == "prefill" else "gateup_gemv"
+    # counter summaries are per kernel, workload and weight width
+    pmc_workload = workload + ("_int8w" if WB == 8 else "") + (f"_g{GSZ}" if GSZ else "") + \
+        (f"_topp{args.topp:g}" if 0 < args.topp < 1 else "")
+    kidx = moe.STAGES.index(kname)
+
+    def timed(stages):
+        moe.moe_prof_enable(steps, stages)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(steps):
+            i = args.warmup + s
+            moe.moe_layer_forward(cfg, wts[i % ncopy], xs[i % len(xs)], y, ws)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        p = moe.moe_prof_read(steps)
+        moe.moe_prof_disable()
+        return ms, p
+
+    ms_step, prof = timed([kname])
+    # per-stage breakdown: a second pass over the same steps with every stage's
+    # events (their own cost inflates it; not part of the timed value)
+    ms_staged, prof_all = timed(None)
+
+    H, I, E = shape.hidden, shape.inter, shape.n_experts
+    # gate+up codes + fp32 scales (one per row, or one per group of GSZ along K)
+    w13_bytes = 2 * I * H * WB // 8 + (2 * I * (H // GSZ) if GSZ else 2 * I) * 4
+    w2_bytes = H * I * WB // 8 + (H * (I // GSZ) if GSZ else H) * 4
+    U = np.array([s["U"] for s in stats], np.float64)
+    layer_bytes = (E * H * 4 + E * 4) + (U + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 4
+    stage_ms = prof_all.mean(0)
+    if workload == "prefill":
+        # the timed launch is the MFMA gate/up of every bucket from the threshold up, the shared experts' included
+        ops = np.array([2.0 * s["mfma_tokens"] * 2 * I * H for s in stats])
+        kt = prof[:, kidx] / 1e3
+        achieved = float(np.mean(ops / kt) / 1e12)
+        # the exact block epilogue: one int->fp32 conversion and one fused multiply-add per (row, token, block)
+        valu = np.array([2.0 * s["mfma_tokens"] * 2 * I * (H // 32) for s in stats])
+        valu_frac = float(np.mean(valu / kt) / VALU_PEAK_OPS)
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
+                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
+                    kernel="k_" + kname,
+                    kernel_ms=round(float(kt.mean() * 1e3), 4),
+                    per_unit="2*2I*H int8 ops per (token, expert) in the MFMA gate/up launch",
+                    valu_epilogue=dict(ops_per_launch=float(valu.mean()), peak=VALU_PEAK_OPS, frac=round(valu_frac, 4),
+                                       per_unit="2 VALU lane-ops (convert + FMA) per (row, token, 32-block)"))
+    else:
+        gb = np.array([s["gemv_experts"] * w13_bytes + s["gemv_tokens"] * (H + H // 32 * 4 + I + I // 32 * 4)
+                       for s in stats], np.float64)
+        kt = prof[:, kidx] / 1e3
+        achieved = float(np.mean(gb / kt) / 1e9)
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
+                    kernel="k_" + kname, algorithmic_bytes=round(float(gb.mean()), 1),
+                    kernel_ms=round(float(kt.mean() * 1e3), 4),
+                    frac_of_measured_peak=round(achieved / hbm_measured, 4) if hbm_measured else None,
+                    per_unit=f"{w13_bytes} B of gate/up weights+scales per GEMV-path expert, plus Q8_0 activations "
+                             f"in and Q8_0 h out per token")
+    layer_gbs = float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9)
+    out = {
+        "value": round(T / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "steps": steps,
+        "ms_per_step": round(ms_step, 5),
+        "config": {"workload": f"glm5.2-moe-layer {workload}", "tokens": T, "hidden": H, "experts": E,
+                   "groups": shape.n_group, "topk_group": shape.topk_group, "top_k": shape.top_k, "inter": I,
+                   "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or DEFAULT_GEMM_MIN,
+                   "layer_copies": ncopy, "weight_bits": WB, "group_size": GSZ, "topp": args.topp},
+        "layer_hbm_gbs": round(layer_gbs, 1),
+        "layer_hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+        "layer_hbm_frac_of_measured_peak": round(layer_gbs / hbm_measured, 4) if hbm_measured else None,
+        "unique_experts_mean": round(float(U.mean()), 2),
+        "routed_slots_mean": round(float(np.mean([st["counts"].sum() for st in stats])), 2),
+        "heat": heat_summary(stats),
+        "stage_ms": {n: round(float(v), 5) for n, v in zip(moe.STAGES, stage_ms)},
+        "ms_per_step_all_stage_events": round(ms_staged, 5),
+        "roofline": roof,
+    }
+    # layer-level view: every expert's int8 ops (MFMA and v_dot4 paths) against the dense int8 MFMA peak, and the
+    # larger of the HBM and MFMA lower bounds against the measured step
+    routed = float(np.mean([st["counts"].sum() for st in stats]))  # T*K, or fewer with adaptive top-p
+    ops_layer = 2.0 * (routed + shape.n_shared * T) * (2 * I * H + H * I)
+    t_mem = layer_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = ops_layer / (INT8_PEAK_TOPS * 1e12)
+    out["layer_int8_ops"] = ops_layer
+    out["layer_int8_mfma_frac"] = round(ops_layer / (ms_step / 1e3) / (INT8_PEAK_TOPS * 1e12), 4)
+    out["combined_roofline_frac"] = round(float(np.mean(np.maximum(t_mem, t_mfma))) / (ms_step / 1e3), 4)
+    del ws, xs
+    return out, xs_host
+
+
+def stack_child(args):
+    """The 40-layer stack in a child process of its own (its pinned host copies and 120 GB of device memory are
+    released with it, and a failure there cannot take the main line down). Returns its JSON or an error."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", "stack40", "--steps", "8", "--warmup", "4",
+           "--seed", str(args.seed)]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=420)
+    except subprocess.TimeoutExpired:
+        return {"error": "stack40 child exceeded 420 s"}
+    for line in reversed(r.stdout.strip().splitlines()):
+        if line.startswith("{"):
+            try:
+                return json.loads(line)
+            except ValueError:
+                break
+    return {"error": f"stack40 child exited {r.returncode}: {r.stderr.strip()[-300:]}"}
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -386,127 +591,37 @@ def main():
     from tests.harness import GpuLayer, config_of
 
     shape = synth.GLM
-    T = tokens_of(args.workload)
-    dev = torch.device("cuda:0")
     WB, GSZ = args.weight_bits, args.group_size
     cfg = config_of(shape, args.gemm_min, WB, GSZ, args.topp)
+    hbm_measured = measured_hbm_peak(moe, torch)
     layers = [GpuLayer(shape, seed=args.seed + c, weight_bits=WB, group_size=GSZ) for c in range(args.copies)]
-    n_in = args.warmup + args.steps
-    xs_host = make_inputs(shape, args.workload, min(n_in, 64), args.seed)
-    xs = [torch.from_numpy(x).to(dev) for x in xs_host]
-    ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
-    y = torch.empty((T, shape.hidden), dtype=torch.float32, device=dev)
     wts = [l.weights() for l in layers]
-
-    # routing statistics of every timed step (outside the timed region)
-    stats = []
-    for s in range(args.steps):
-        i = args.warmup + s
-        stats.append(routing_stats(moe, cfg, layers[i % args.copies], xs[i % len(xs)], ws, args.gemm_min))
-
-    stream = torch.cuda.current_stream()
-    for s in range(args.warmup):
-        moe.moe_layer_forward(cfg, wts[s % args.copies], xs[s % len(xs)], y, ws)
-    torch.cuda.synchronize()
-    # dominant kernel: the gate-up launch of the path that moves most bytes; the
-    # timed region records HIP events around it only (on the stream it runs on)
-    kname = "gateup_mfma" if args.workload == "prefill" else "gateup_gemv"
-    # counter summaries are per kernel, workload and weight width
-    pmc_workload = args.workload + ("_int8w" if WB == 8 else "") + (f"_g{GSZ}" if GSZ else "") + \
-        (f"_topp{args.topp:g}" if 0 < args.topp < 1 else "")
-    kidx = moe.STAGES.index(kname)
-
-    def timed(stages):
-        moe.moe_prof_enable(args.steps, stages)
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for s in range(args.steps):
-            i = args.warmup + s
-            moe.moe_layer_forward(cfg, wts[i % args.copies], xs[i % len(xs)], y, ws)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / args.steps
-        p = moe.moe_prof_read(args.steps)
-        moe.moe_prof_disable()
-        return ms, p
-
-    ms_step, prof = timed([kname])
-    # per-stage breakdown: a second pass over the same steps with every stage's
-    # events (their own cost inflates it; not part of the timed value)
-    ms_staged, prof_all = timed(None)
-
-    H, I, E = shape.hidden, shape.inter, shape.n_experts
-    # gate+up codes + fp32 scales (one per row, or one per group of GSZ along K)
-    w13_bytes = 2 * I * H * WB // 8 + (2 * I * (H // GSZ) if GSZ else 2 * I) * 4
-    w2_bytes = H * I * WB // 8 + (H * (I // GSZ) if GSZ else H) * 4
-    U = np.array([s["U"] for s in stats], np.float64)
-    layer_bytes = (E * H * 4 + E * 4) + (U + 1) * (w13_bytes + w2_bytes) + 2 * T * H * 4
-    stage_ms = prof_all.mean(0)
-    if args.workload == "prefill":
-        # the timed launch is the MFMA gate/up of every bucket from the threshold up, the shared experts' included
-        ops = np.array([2.0 * s["mfma_tokens"] * 2 * I * H for s in stats])
-        kt = prof[:, kidx] / 1e3
-        achieved = float(np.mean(ops / kt) / 1e12)
-        # the exact block epilogue: one int->fp32 conversion and one fused multiply-add per (row, token, block)
-        valu = np.array([2.0 * s["mfma_tokens"] * 2 * I * (H // 32) for s in stats])
-        valu_frac = float(np.mean(valu / kt) / VALU_PEAK_OPS)
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
-                    frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
-                    kernel="k_" + kname,
-                    kernel_ms=round(float(kt.mean() * 1e3), 4),
-                    per_unit="2*2I*H int8 ops per (token, expert) in the MFMA gate/up launch",
-                    valu_epilogue=dict(ops_per_launch=float(valu.mean()), peak=VALU_PEAK_OPS, frac=round(valu_frac, 4),
-                                       per_unit="2 VALU lane-ops (convert + FMA) per (row, token, 32-block)"))
-    else:
-        gb = np.array([s["gemv_experts"] * w13_bytes + s["gemv_tokens"] * (H + H // 32 * 4 + I + I // 32 * 4)
-                       for s in stats], np.float64)
-        kt = prof[:, kidx] / 1e3
-        achieved = float(np.mean(gb / kt) / 1e9)
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
-                    kernel="k_" + kname, algorithmic_bytes=round(float(gb.mean()), 1),
-                    kernel_ms=round(float(kt.mean() * 1e3), 4),
-                    per_unit=f"{w13_bytes} B of gate/up weights+scales per GEMV-path expert, plus Q8_0 activations "
-                             f"in and Q8_0 h out per token")
-    out = {
-        "metric": METRIC,
-        "value": round(T / (ms_step / 1e3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "i8",
-        "data": "synthetic",
-        "config": {"workload": f"glm5.2-moe-layer {args.workload}", "tokens": T, "hidden": H, "experts": E,
-                   "groups": shape.n_group, "topk_group": shape.topk_group, "top_k": shape.top_k, "inter": I,
-                   "shared": shape.n_shared, "rsf": shape.rsf, "gemm_min_tokens": args.gemm_min or DEFAULT_GEMM_MIN,
-                   "layer_copies": args.copies, "weight_bits": WB, "group_size": GSZ, "topp": args.topp},
-        "layer_hbm_gbs": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9), 1),
-        "layer_hbm_frac": round(float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9) / HBM_PEAK_GBS, 4),
-        "unique_experts_mean": round(float(U.mean()), 2),
-        "routed_slots_mean": round(float(np.mean([st["counts"].sum() for st in stats])), 2),
-        "stage_ms": {n: round(float(v), 5) for n, v in zip(moe.STAGES, stage_ms)},
-        "ms_per_step_all_stage_events": round(ms_staged, 5),
-        "roofline": roof,
-    }
-    # layer-level view: every expert's int8 ops (MFMA and v_dot4 paths) against the dense int8 MFMA peak, and the
-    # larger of the HBM and MFMA lower bounds against the measured step
-    routed = float(np.mean([st["counts"].sum() for st in stats]))  # T*K, or fewer with adaptive top-p
-    ops_layer = 2.0 * (routed + shape.n_shared * T) * (2 * I * H + H * I)
-    t_mem = layer_bytes / (HBM_PEAK_GBS * 1e9)
-    t_mfma = ops_layer / (INT8_PEAK_TOPS * 1e12)
-    out["layer_int8_ops"] = ops_layer
-    out["layer_int8_mfma_frac"] = round(ops_layer / (ms_step / 1e3) / (INT8_PEAK_TOPS * 1e12), 4)
-    out["combined_roofline_frac"] = round(float(np.mean(np.maximum(t_mem, t_mfma))) / (ms_step / 1e3), 4)
+    head, xs_host = measure(args, args.workload, args.steps, moe, torch, shape, cfg, layers, wts, hbm_measured)
+    out = {"metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
+           "steps": head.pop("steps"), "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic"}
+    out.update(head)
+    out["hbm_measured_peak_gbs"] = hbm_measured
+    out["hbm_measured_peak_how"] = "best of plain grid-stride read kernels over 4 GiB (2048-8192 workgroups x 256 " \
+                                   "lanes, 2-8 16-byte loads in flight per lane)"
+    configs = {}
+    for w in args.configs:
+        if w == "stack40":
+            continue
+        print(f"bench: measuring {w}", file=sys.stderr, flush=True)
+        configs[w], _ = measure(args, w, args.config_steps, moe, torch, shape, cfg, layers, wts, hbm_measured)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB, GSZ,
-                                           args.topp)
+        cb = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB, GSZ, args.topp)
+        cb.update(host_cpu())
+        out["cpu_baseline"] = cb
+    if "stack40" in args.configs:
+        del wts, layers
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        print("bench: measuring stack40 in a child process", file=sys.stderr, flush=True)
+        configs["stack40"] = stack_child(args)
+    if configs:
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
 
 

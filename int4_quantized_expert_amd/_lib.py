@@ -121,6 +121,43 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+class ArgError(ValueError):
+    """A tensor handed to the binding does not match what the C entry point will read or write."""
+
+
+_DT = {}
+
+
+def _dtype(name):
+    import torch
+    if not _DT:
+        _DT.update(f32=torch.float32, i32=torch.int32, i8=torch.int8, u8=torch.uint8)
+    return _DT[name]
+
+
+def _need(t, name, dtype=None, numel=None, rows=None, cols=None):
+    """Checks a device tensor before its raw pointer reaches the library: on the GPU, contiguous, of the element
+    type the entry point reads, and at least as large as the call will touch (the library only sees pointers,
+    so a short or strided buffer would become out-of-bounds device accesses)."""
+    if t is None:
+        raise ArgError(f"{name}: a device tensor is required")
+    if not getattr(t, "is_cuda", False):
+        raise ArgError(f"{name}: must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ArgError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != _dtype(dtype):
+        raise ArgError(f"{name}: dtype {t.dtype}, expected {_dtype(dtype)}")
+    if numel is not None and t.numel() < numel:
+        raise ArgError(f"{name}: {t.numel()} elements, the call touches {numel}")
+    if rows is not None and (t.dim() != 2 or t.shape[0] < rows or (cols is not None and t.shape[1] != cols)):
+        raise ArgError(f"{name}: shape {tuple(t.shape)}, expected [>= {rows}, {cols}]")
+    return t
+
+
+def _opt(t, name, dtype, numel):
+    return None if t is None else _need(t, name, dtype, numel)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -160,31 +197,59 @@ def moe_workspace_bytes(cfg: Config, max_tokens: int) -> int:
     return int(_lib.moe_workspace_bytes(ctypes.byref(c), int(max_tokens)))
 
 
+def _quant_args(w, out, scales, out_numel, sc_numel, names):
+    _need(w, "w", "f32")
+    if w.dim() != 2:
+        raise ArgError(f"w: 2-D [rows][cols] expected, got {tuple(w.shape)}")
+    _need(out, names[0], None, None)
+    if out.numel() * out.element_size() < out_numel:
+        raise ArgError(f"{names[0]}: {out.numel() * out.element_size()} bytes, the call writes {out_numel}")
+    _need(scales, "scales", "f32", sc_numel)
+
+
 def moe_quantize_int4(w, packed, scales, stream=None):
     rows, cols = w.shape
+    _quant_args(w, packed, scales, rows * cols // 2, rows, ("packed",))
     return _check("moe_quantize_int4",
                   _lib.moe_quantize_int4(_ptr(w), rows, cols, _ptr(packed), _ptr(scales), _stream(stream)))
 
 
 def moe_quantize_int8(w, codes, scales, stream=None):
     rows, cols = w.shape
+    _quant_args(w, codes, scales, rows * cols, rows, ("codes",))
     return _check("moe_quantize_int8",
                   _lib.moe_quantize_int8(_ptr(w), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
 
 
 def moe_quantize_int4_grouped(w, group, packed, scales, stream=None):
     rows, cols = w.shape
+    g = int(group)
+    # an invalid group size is the library's to reject (MOE_E_ARG / MOE_E_SHAPE); size the scales only for a valid one
+    _quant_args(w, packed, scales, rows * cols // 2, rows * (cols // g) if g > 0 and cols % g == 0 else 0, ("packed",))
     return _check("moe_quantize_int4_grouped",
                   _lib.moe_quantize_int4_grouped(_ptr(w), rows, cols, int(group), _ptr(packed), _ptr(scales),
                                                  _stream(stream)))
 
 
 def moe_quantize_q8_0(x, q, d, stream=None):
+    _need(x, "x", "f32")
+    _need(q, "q", "i8", x.numel())
+    _need(d, "d", "f32", x.numel() // 32)
     return _check("moe_quantize_q8_0", _lib.moe_quantize_q8_0(_ptr(x), x.numel(), _ptr(q), _ptr(d), _stream(stream)))
 
 
 def moe_router(cfg: Config, x, router_w, router_bias, topk_ids, topk_w, near_tie, ws, stream=None):
     c = cfg.c()
+    _need(x, "x", "f32")
+    _need(ws, "ws")
+    if _lib.moe_workspace_bytes(ctypes.byref(c), 1) > 0:  # an invalid configuration is the library's to reject
+        _need(x, "x", "f32", rows=1, cols=cfg.hidden)
+        T, E, K = x.shape[0], cfg.n_experts, cfg.top_k
+        _need(router_w, "router_w", "f32", E * cfg.hidden)
+        _need(router_bias, "router_bias", "f32", E)
+        _need(topk_ids, "topk_ids", "i32", T * K)
+        _need(topk_w, "topk_w", "f32", T * K)
+        _opt(near_tie, "near_tie", "u8", T)
     return _check("moe_router", _lib.moe_router(ctypes.byref(c), _ptr(x), x.shape[0], _ptr(router_w),
                                                 _ptr(router_bias), _ptr(topk_ids), _ptr(topk_w), _ptr(near_tie),
                                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
@@ -193,29 +258,98 @@ def moe_router(cfg: Config, x, router_w, router_bias, topk_ids, topk_w, near_tie
 def moe_dispatch(cfg: Config, topk_ids, counts, offsets, sorted_slots, slot_pos, unique_ids, n_unique, ws,
                  stream=None):
     c = cfg.c()
+    _need(topk_ids, "topk_ids", "i32")
+    _need(ws, "ws")
+    if _lib.moe_workspace_bytes(ctypes.byref(c), 1) > 0:  # an invalid configuration is the library's to reject
+        _need(topk_ids, "topk_ids", "i32", rows=1, cols=cfg.top_k)
+        T, E, K = topk_ids.shape[0], cfg.n_experts, cfg.top_k
+        for t, n, k in ((counts, "counts", E), (offsets, "offsets", E + 1), (sorted_slots, "sorted_slots", T * K),
+                        (slot_pos, "slot_pos", T * K), (unique_ids, "unique_ids", E), (n_unique, "n_unique", 1)):
+            _need(t, n, "i32", k)
     return _check("moe_dispatch", _lib.moe_dispatch(ctypes.byref(c), _ptr(topk_ids), topk_ids.shape[0], _ptr(counts),
                                                     _ptr(offsets), _ptr(sorted_slots), _ptr(slot_pos),
                                                     _ptr(unique_ids), _ptr(n_unique), _ptr(ws),
                                                     ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def layer_weights(router_w, router_bias, w13, s13, w2, s2, sh_w13=None, sh_s13=None, sh_w2=None, sh_s2=None):
+def layer_weights(router_w, router_bias, w13, s13, w2, s2, sh_w13=None, sh_s13=None, sh_w2=None, sh_s2=None,
+                  cfg: Config | None = None):
+    """moe_layer_weights from device tensors. With cfg, every tensor is checked against the sizes the layer reads
+    (routed arrays for E experts, shared arrays for n_shared): element type, device, contiguity, size."""
+    if cfg is not None:
+        E, H, I, NS = cfg.n_experts, cfg.hidden, cfg.inter, cfg.n_shared
+        wb = cfg.weight_bits if cfg.weight_bits > 0 else 4
+        G = cfg.group_size if cfg.group_size > 0 else 0
+        b13, b2 = I * H * wb // 4, H * I * wb // 8
+        n13, n2 = (2 * I * H // G, H * I // G) if G else (2 * I, H)
+        _need(router_w, "router_w", "f32", E * H)
+        _need(router_bias, "router_bias", "f32", E)
+        for t, n, dt, k in ((w13, "w13", "u8", E * b13), (s13, "s13", "f32", E * n13), (w2, "w2", "u8", E * b2),
+                            (s2, "s2", "f32", E * n2)):
+            _need(t, n, dt, k)
+        if NS:
+            for t, n, dt, k in ((sh_w13, "sh_w13", "u8", NS * b13), (sh_s13, "sh_s13", "f32", NS * n13),
+                                (sh_w2, "sh_w2", "u8", NS * b2), (sh_s2, "sh_s2", "f32", NS * n2)):
+                _need(t, n, dt, k)
     return moe_layer_weights(*[_ptr(t) for t in (router_w, router_bias, w13, s13, w2, s2, sh_w13, sh_s13, sh_w2,
                                                  sh_s2)])
 
 
+# element type and size (in terms of T, K, H, I, E, R = T*K + n_shared*T) of each tap buffer
+_TAP_SPEC = {
+    "topk_ids": ("i32", lambda T, K, H, I, E, R: T * K), "topk_w": ("f32", lambda T, K, H, I, E, R: T * K),
+    "near_tie": ("u8", lambda T, K, H, I, E, R: T), "qx": ("i8", lambda T, K, H, I, E, R: T * H),
+    "dx": ("f32", lambda T, K, H, I, E, R: T * H // 32), "h": ("f32", lambda T, K, H, I, E, R: R * I),
+    "qh": ("i8", lambda T, K, H, I, E, R: R * I), "dh": ("f32", lambda T, K, H, I, E, R: R * I // 32),
+    "e_out": ("f32", lambda T, K, H, I, E, R: R * H),
+    "gateup_sums": ("i32", lambda T, K, H, I, E, R: 2 * I * (H // 32)),
+    "down_sums": ("i32", lambda T, K, H, I, E, R: H * (I // 32)),
+    "counts": ("i32", lambda T, K, H, I, E, R: E), "offsets": ("i32", lambda T, K, H, I, E, R: E + 1),
+    "sorted_slots": ("i32", lambda T, K, H, I, E, R: T * K), "slot_pos": ("i32", lambda T, K, H, I, E, R: T * K),
+    "unique_ids": ("i32", lambda T, K, H, I, E, R: E), "n_unique": ("i32", lambda T, K, H, I, E, R: 1),
+}
+
+
 def taps(sum_slot=-1, **bufs):
+    """moe_taps from device tensors; moe_layer_forward checks each one's type and size against the call."""
     t = moe_taps()
     t.sum_slot = sum_slot
     for k, v in bufs.items():
+        if k not in _TAP_SPEC:
+            raise ArgError(f"unknown tap {k}")
         setattr(t, k, None if v is None else v.data_ptr())
+    t._bufs = {k: v for k, v in bufs.items() if v is not None}
     return t
+
+
+def _check_forward_args(cfg: Config, x, y, T, ws, tap):
+    """What the library cannot see behind its raw pointers: x and y hold T rows of H fp32 on the GPU, the
+    workspace and tap buffers are device tensors of the right type and size. An invalid configuration or T < 1
+    is left to the library, which rejects it with its own code before any device work."""
+    _need(x, "x", "f32")
+    _need(y, "y", "f32")
+    if T > x.shape[0] or T > y.shape[0]:
+        raise ArgError(f"T = {T} above the rows of x ({x.shape[0]}) or y ({y.shape[0]})")
+    if ws is not None:
+        _need(ws, "ws")
+    c = cfg.c()
+    if T < 1 or _lib.moe_workspace_bytes(ctypes.byref(c), 1) == 0:
+        return
+    _need(x, "x", "f32", rows=T, cols=cfg.hidden)
+    _need(y, "y", "f32", rows=T, cols=cfg.hidden)
+    if tap is not None:
+        K, H, I, E = cfg.top_k, cfg.hidden, cfg.inter, cfg.n_experts
+        R = T * K + cfg.n_shared * T
+        for k, v in getattr(tap, "_bufs", {}).items():
+            dt, size = _TAP_SPEC[k]
+            _need(v, k, dt, size(T, K, H, I, E, R))
 
 
 def moe_layer_forward(cfg: Config, weights: moe_layer_weights, x, y, ws, tap: moe_taps | None = None, stream=None,
                       T: int | None = None):
     c = cfg.c()
     T = x.shape[0] if T is None else T
+    _check_forward_args(cfg, x, y, T, ws, tap)
     return _check("moe_layer_forward",
                   _lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(weights), _ptr(x), T, _ptr(y), _ptr(ws),
                                          ws.numel() * ws.element_size(), ctypes.byref(tap) if tap else None,
@@ -229,6 +363,7 @@ def moe_layer_forward_noalloc(cfg: Config, weights: moe_layer_weights, x, y, tap
                               stream=None, T: int | None = None):
     c = cfg.c()
     T = x.shape[0] if T is None else T
+    _check_forward_args(cfg, x, y, T, None, tap)
     return _check("moe_layer_forward_noalloc",
                   _lib.moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(weights), _ptr(x), T, _ptr(y),
                                                  ctypes.byref(tap) if tap else None, _stream(stream)))
@@ -253,11 +388,17 @@ def moe_prof_disable():
 
 
 def moe_membench_read(buf, blocks: int, unroll: int, sink, stream=None):
+    _need(buf, "buf")
+    _need(sink, "sink", None, 1)
     return _check("moe_membench_read", _lib.moe_membench_read(_ptr(buf), buf.numel() * buf.element_size(), blocks,
                                                               unroll, _ptr(sink), _stream(stream)))
 
 
 def moe_membench_copy(src, dst, blocks: int, stream=None):
+    _need(src, "src")
+    _need(dst, "dst")
+    if dst.numel() * dst.element_size() < src.numel() * src.element_size():
+        raise ArgError("dst: smaller than src")
     return _check("moe_membench_copy", _lib.moe_membench_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
                                                               blocks, _stream(stream)))
 
@@ -287,6 +428,9 @@ class ExpertCache:
     def forward(self, resident, host: HostExperts, x, y, ws, compute, copy, T=None, trace=False):
         import numpy as np
         T = x.shape[0] if T is None else T
+        _need(x, "x", "f32", rows=T)
+        _need(y, "y", "f32", rows=T, cols=x.shape[1])
+        _need(ws, "ws")
         hit = np.zeros(self.E, np.int8) if trace else None
         slot = np.zeros(self.E, np.int32) if trace else None
         _check("moe_expert_cache_forward",

@@ -186,6 +186,45 @@ void orc_router_logits(const float* x, int32_t T, int32_t H, const float* Wr, in
     }
 }
 
+/* Where several results are correct: the logit is a sum of H products, exact
+ * in fp64, whose fp64 sum any evaluation order computes to within
+ * gamma_H * sum_h |x_h w_h| of the exact value (gamma_H = H u / (1 - H u),
+ * u = 2^-53: the standard bound for recursive summation in any order, Higham,
+ * Accuracy and Stability of Numerical Algorithms, on summation). Two
+ * evaluations can therefore differ by twice that, and when the fp32 rounding
+ * is not the same over that whole interval around the oracle's sum, another
+ * correct evaluation may round the logit to the neighbouring fp32 value. flag
+ * [T][E] is 1 for such logits; z is the same as orc_router_logits'. */
+void orc_router_logits_boundary(const float* x, int32_t T, int32_t H, const float* Wr, int32_t E, float* z,
+                                uint8_t* flag) {
+  const double u = ldexp(1.0, -53), gam = (double)H * u / (1.0 - (double)H * u);
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t e = 0; e < E; ++e) {
+      double acc = 0.0, mag = 0.0;
+      for (int32_t h = 0; h < H; ++h) {
+        const double p = (double)x[(int64_t)t * H + h] * (double)Wr[(int64_t)e * H + h];
+        acc += p;
+        mag += fabs(p);
+      }
+      const double err = 2.0 * gam * mag;
+      z[(int64_t)t * E + e] = (float)acc;
+      flag[(int64_t)t * E + e] = (uint8_t)((float)(acc - err) != (float)(acc + err));
+    }
+}
+
+/* The same question for the SwiGLU: g*u/(1+exp(-g)) is evaluated in fp64 and
+ * rounded once; an fp64 exp from another library may differ from this one by
+ * an ulp or two, so a value within 2^-48 (relative, sixteen fp64 ulps) of the
+ * midpoint between two fp32 neighbours may round either way. flag[i] = 1 for
+ * such (g[i], u[i]). */
+void orc_swiglu_boundary(const float* g, const float* u, int64_t n, uint8_t* flag) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double v = ((double)g[i] * (double)u[i]) / (1.0 + exp(-(double)g[i]));
+    const double d = fabs(v) * ldexp(1.0, -48);
+    flag[i] = (uint8_t)((float)(v - d) != (float)(v + d));
+  }
+}
+
 /* DeepSeek-V3-style sigmoid router with aux-loss-free bias correction
  * ("Show HN: 느린 컴퓨터에서 GLM 5.2 실행하기", implemented features: sigmoid
  * router, noaux_tc, routed_scaling_factor). The pages name the method but give
@@ -423,18 +462,35 @@ static float expert_dot(const int8_t* q, const float* s, int64_t row, int32_t gr
   return orc_dot_q4q8_grouped(q + row * n, s + row * (n / group), group, q8, d8, n);
 }
 
+/* The gate and up projections of one token: g[r] = gate row r . x, u[r] = up
+ * row r . x, each the dequant-on-use dot above. */
+void orc_gateup_token(int32_t H, int32_t I, int32_t group, const int8_t* q13, const float* s13, const int8_t* qx,
+                      const float* dx, float* g, float* u) {
+  for (int32_t r = 0; r < I; ++r) {
+    g[r] = expert_dot(q13, s13, r, group, qx, dx, H);
+    u[r] = expert_dot(q13, s13, (int64_t)I + r, group, qx, dx, H);
+  }
+}
+
+/* The down projection of one token's Q8_0 h: out[o] = down row o . h. */
+void orc_down_token(int32_t H, int32_t I, int32_t group, const int8_t* q2, const float* s2, const int8_t* qh,
+                    const float* dh, float* out) {
+  for (int32_t o = 0; o < H; ++o) out[o] = expert_dot(q2, s2, o, group, qh, dh, I);
+}
+
 void orc_expert_token_g(int32_t H, int32_t I, int32_t group, const int8_t* q13, const float* s13, const int8_t* q2,
                         const float* s2, const int8_t* qx, const float* dx, float* h, int8_t* qh, float* dh,
                         float* out, int32_t* S13, int32_t* S2) {
-  for (int32_t r = 0; r < I; ++r) {
-    float g = expert_dot(q13, s13, r, group, qx, dx, H);
-    float u = expert_dot(q13, s13, (int64_t)I + r, group, qx, dx, H);
-    h[r] = orc_swiglu(g, u);
-  }
+  float* g = (float*)malloc(sizeof(float) * (size_t)I);
+  float* u = (float*)malloc(sizeof(float) * (size_t)I);
+  orc_gateup_token(H, I, group, q13, s13, qx, dx, g, u);
+  for (int32_t r = 0; r < I; ++r) h[r] = orc_swiglu(g[r], u[r]);
+  free(g);
+  free(u);
   if (S13)
     for (int32_t r = 0; r < 2 * I; ++r) orc_block_sums(q13 + (int64_t)r * H, qx, H, S13 + (int64_t)r * (H / 32));
   orc_q8_0(h, I, qh, dh);
-  for (int32_t o = 0; o < H; ++o) out[o] = expert_dot(q2, s2, o, group, qh, dh, I);
+  orc_down_token(H, I, group, q2, s2, qh, dh, out);
   if (S2)
     for (int32_t o = 0; o < H; ++o) orc_block_sums(q2 + (int64_t)o * I, qh, I, S2 + (int64_t)o * (I / 32));
 }

@@ -70,6 +70,11 @@ void orc_unpack_int4_tiled64(const uint8_t* in, int64_t rows, int64_t cols, int8
 void orc_q8_0(const float* v, int64_t n, int8_t* q, float* d);
 
 void orc_router_logits(const float* x, int32_t T, int32_t H, const float* Wr, int32_t E, float* z);
+/* the same logits, and flag[T][E] = 1 where another fp64 summation order may round to the next fp32 value */
+void orc_router_logits_boundary(const float* x, int32_t T, int32_t H, const float* Wr, int32_t E, float* z,
+                                uint8_t* flag);
+/* flag[i] = 1 where the fp64 SwiGLU of (g[i], u[i]) lies within 2^-48 (relative) of an fp32 rounding midpoint */
+void orc_swiglu_boundary(const float* g, const float* u, int64_t n, uint8_t* flag);
 /* keep mask and weights of K selected slots (unbiased scores s_sel, slot order) under adaptive top-p */
 void orc_topp_weights(const float* s_sel, int32_t K, float topp, float rsf, int32_t* keep, float* w);
 /* ids of slots dropped by adaptive top-p are -1, their weights 0 */
@@ -91,6 +96,11 @@ void orc_expert_token(int32_t H, int32_t I, const int8_t* q13, const float* s13,
 void orc_expert_token_g(int32_t H, int32_t I, int32_t group, const int8_t* q13, const float* s13, const int8_t* q2,
                         const float* s2, const int8_t* qx, const float* dx, float* h, int8_t* qh, float* dh,
                         float* out, int32_t* S13, int32_t* S2);
+/* the two halves of orc_expert_token_g: gate/up projections (before the SwiGLU) and the down projection */
+void orc_gateup_token(int32_t H, int32_t I, int32_t group, const int8_t* q13, const float* s13, const int8_t* qx,
+                      const float* dx, float* g, float* u);
+void orc_down_token(int32_t H, int32_t I, int32_t group, const int8_t* q2, const float* s2, const int8_t* qh,
+                    const float* dh, float* out);
 void orc_combine(int32_t T, int32_t K, int32_t H, int32_t n_shared, const float* e_routed,
                  const float* e_shared, const float* w, float* y);
 void orc_combine_ids(int32_t T, int32_t K, int32_t H, int32_t n_shared, const float* e_routed,

@@ -47,6 +47,10 @@ def lib():
         L.orc_expert_token_g.argtypes = [I32, I32, I32] + [P] * 12
         L.orc_q8_0.argtypes = [P, I64, P, P]
         L.orc_router_logits.argtypes = [P, I32, I32, P, I32, P]
+        L.orc_router_logits_boundary.argtypes = [P, I32, I32, P, I32, P, P]
+        L.orc_swiglu_boundary.argtypes = [P, P, I64, P]
+        L.orc_gateup_token.argtypes = [I32, I32, I32, P, P, P, P, P, P]
+        L.orc_down_token.argtypes = [I32, I32, I32, P, P, P, P, P]
         L.orc_route.argtypes = [P, P, P, I32, P, P, P, P, P]
         L.orc_dispatch.argtypes = [I32, I32, I32, P, P, P, P, P, P, P]
         L.orc_block_sums.argtypes = [P, P, I64, P]
@@ -190,6 +194,61 @@ def router_logits(x, Wr):
     return z
 
 
+def router_logits_boundary(x, Wr):
+    """(z [T][E] as router_logits, flag [T][E] uint8: 1 where another fp64 summation order may round the logit
+    to the neighbouring fp32 value)."""
+    x = _c(x, np.float32)
+    Wr = _c(Wr, np.float32)
+    T, H = x.shape
+    E = Wr.shape[0]
+    z = np.empty((T, E), np.float32)
+    fl = np.empty((T, E), np.uint8)
+    lib().orc_router_logits_boundary(_p(x), T, H, _p(Wr), E, _p(z), _p(fl))
+    return z, fl
+
+
+def swiglu_boundary(g, u):
+    """uint8 flags: 1 where the fp64 SwiGLU of (g, u) lies within 2^-48 (relative) of an fp32 midpoint."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    fl = np.empty(g.shape, np.uint8)
+    lib().orc_swiglu_boundary(_p(g), _p(u), g.size, _p(fl))
+    return fl
+
+
+def _group_of(H, I, s13, s2):
+    if s13.ndim == 2:
+        group = H // s13.shape[1]
+        assert s13.shape == (2 * I, H // group) and s2.shape == (H, I // group)
+        return group
+    return 0
+
+
+def gateup_token(q13, s13, qx, dx):
+    """(g [I], u [I]): the gate and up projections of one token (s13 [2I] row scales or [2I][H/G] group scales)."""
+    q13 = _c(q13, np.int8)
+    s13 = _c(s13, np.float32)
+    I2, H = q13.shape
+    I = I2 // 2
+    group = H // s13.shape[1] if s13.ndim == 2 else 0
+    g = np.empty(I, np.float32)
+    u = np.empty(I, np.float32)
+    lib().orc_gateup_token(H, I, group, _p(q13), _p(s13), _p(_c(qx, np.int8)), _p(_c(dx, np.float32)), _p(g),
+                           _p(u))
+    return g, u
+
+
+def down_token(q2, s2, qh, dh):
+    """out [H]: the down projection of one token's Q8_0 h (s2 [H] row scales or [H][I/G] group scales)."""
+    q2 = _c(q2, np.int8)
+    s2 = _c(s2, np.float32)
+    H, I = q2.shape
+    group = I // s2.shape[1] if s2.ndim == 2 else 0
+    out = np.empty(H, np.float32)
+    lib().orc_down_token(H, I, group, _p(q2), _p(s2), _p(_c(qh, np.int8)), _p(_c(dh, np.float32)), _p(out))
+    return out
+
+
 def route(cfg: Cfg, z, bias, want_scores=False):
     z = _c(z, np.float32)
     bias = _c(bias, np.float32)
@@ -277,10 +336,7 @@ def expert_token(q13, s13, q2, s2, qx, dx, want_sums=False):
     out = np.empty(H, np.float32)
     S13 = np.empty((2 * I, H // 32), np.int32) if want_sums else None
     S2 = np.empty((H, I // 32), np.int32) if want_sums else None
-    group = 0
-    if s13.ndim == 2:
-        group = H // s13.shape[1]
-        assert s13.shape == (2 * I, H // group) and s2.shape == (H, I // group)
+    group = _group_of(H, I, s13, s2)
     lib().orc_expert_token_g(H, I, group, _p(q13), _p(s13), _p(q2), _p(s2), _p(qx), _p(dx), _p(h), _p(qh), _p(dh),
                              _p(out), _p(S13), _p(S2))
     r = dict(h=h, qh=qh, dh=dh, out=out)

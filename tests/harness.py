@@ -88,17 +88,39 @@ class GpuLayer:
         return n
 
 
+def _gen_weights(shape, e, seed, layer, shared):
+    """fp32 (w13 [2I][H], w2 [H][I]) of one expert from the seeded generator: its device fill when a GPU is
+    present (bit-identical to the host fill, which a GPU test checks; only the generator's draws, none of the
+    method's arithmetic), else its host fill."""
+    try:
+        import torch
+        gpu = torch.cuda.is_available()
+    except ImportError:
+        gpu = False
+    if not gpu:
+        if shared:
+            return synth.shared_w13(shape, e, seed, layer), synth.shared_w2(shape, e, seed, layer)
+        return synth.expert_w13(shape, e, seed, layer), synth.expert_w2(shape, e, seed, layer)
+    k13, k2 = (synth.SH_W13, synth.SH_W2) if shared else (synth.W13, synth.W2)
+    H, I = shape.hidden, shape.inter
+    a = torch.empty((2 * I, H), dtype=torch.float32, device="cuda")
+    b = torch.empty((H, I), dtype=torch.float32, device="cuda")
+    synth.gpu_normal_(a, seed, synth.stream_id(k13, layer, e), shape.w_sigma)
+    synth.gpu_normal_(b, seed, synth.stream_id(k2, layer, e), shape.w_sigma)
+    return a.cpu().numpy(), b.cpu().numpy()
+
+
+ORACLE_CACHE_MAX = 48
+
+
 def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = False, weight_bits: int = 4,
                   group_size: int = 0):
-    """(q13, s13, q2, s2) of routed expert e (or shared expert e) from the host generator + oracle quantizer
+    """(q13, s13, q2, s2) of routed expert e (or shared expert e) from the seeded generator + oracle quantizer
     (per-row int4, per-row int8 for weight_bits=8, or int4 with [rows][cols/G] group scales)."""
     from oracle import oracle as O
     key = (shape, e, seed, layer, shared, weight_bits, group_size)
     if key not in _ORACLE_CACHE:
-        if shared:
-            w13, w2 = synth.shared_w13(shape, e, seed, layer), synth.shared_w2(shape, e, seed, layer)
-        else:
-            w13, w2 = synth.expert_w13(shape, e, seed, layer), synth.expert_w2(shape, e, seed, layer)
+        w13, w2 = _gen_weights(shape, e, seed, layer, shared)
         if group_size:
             def quant(w):
                 return O.quant_int4_grouped(w, group_size)
@@ -106,7 +128,7 @@ def oracle_expert(shape, e: int, seed: int = 0, layer: int = 0, shared: bool = F
             quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
         q13, s13 = quant(w13)
         q2, s2 = quant(w2)
-        if len(_ORACLE_CACHE) > 48:
+        if len(_ORACLE_CACHE) > ORACLE_CACHE_MAX:
             _ORACLE_CACHE.clear()
         _ORACLE_CACHE[key] = (q13, s13, q2, s2)
     return _ORACLE_CACHE[key]
@@ -234,3 +256,149 @@ def host_experts(layer, order=(0, 1, 2, 3)):
             ptrs[k][e] = blk.ptr + off
             off += sizes[k]
     return moe.HostExperts(*ptrs), blk
+
+
+# ------------------------------------------------------------------ several correct results
+def tie_choice_ok(shape, c, oracle_ids, gpu_ids, eps=1e-6):
+    """Whether one token's GPU selection (K expert ids in slot order) differs from the oracle's only inside the
+    tie set of the oracle's biased scores c [E] (fp32), at the 1e-6 near-tie threshold:
+      - K distinct ids from at most topk_group groups, each group within eps of being kept (its top-2 sum at
+        least the topk_group-th group score minus eps);
+      - every id within eps of the oracle's K-th selected score, or in a group that was itself a tie;
+      - every oracle id the GPU left out within eps of the best candidate left out, or in a tied group;
+      - slot order by score descending, an inversion allowed only within eps.
+    Returns (ok, reason)."""
+    E, G, KG, K = shape.n_experts, shape.n_group, shape.topk_group, shape.top_k
+    n = E // G
+    c = np.asarray(c, np.float32)
+    o = [int(v) for v in oracle_ids if v >= 0]
+    g_ids = [int(v) for v in gpu_ids if v >= 0]
+    if len(set(g_ids)) != len(g_ids) or any(v < 0 or v >= E for v in g_ids) or len(g_ids) != len(o):
+        return False, "ids not distinct, out of range or of another count"
+    gs = np.array([np.float32(np.sort(c[j * n:(j + 1) * n])[-1]) + np.float32(np.sort(c[j * n:(j + 1) * n])[-2])
+                   for j in range(G)], np.float32)
+    order = sorted(range(G), key=lambda j: (-float(gs[j]), j))
+    kept = order[:KG]
+    b_in = float(gs[kept[-1]])
+    b_out = float(gs[order[KG]]) if KG < G else -np.inf
+    tied_group = {j for j in range(G) if KG < G and (abs(float(gs[j]) - b_in) < eps or abs(float(gs[j]) - b_out) < eps)}
+    possible_group = {j for j in range(G) if float(gs[j]) >= b_in - eps}
+    used = {v // n for v in g_ids}
+    if len(used) > KG:
+        return False, f"ids from {len(used)} groups, at most {KG} are kept"
+    if not used <= possible_group:
+        return False, f"ids from groups {sorted(used - possible_group)} that are not within eps of being kept"
+    cand = [e for e in range(E) if e // n in kept]
+    cand_sorted = sorted(cand, key=lambda e: (-float(c[e]), e))
+    c_k = float(c[o[-1]]) if o else 0.0
+    left = [e for e in cand_sorted if e not in o]
+    c_next = float(c[left[0]]) if left else -np.inf
+    for e in set(g_ids) - set(o):
+        if not (float(c[e]) >= c_k - eps or (e // n) in tied_group):
+            return False, f"expert {e} (score {float(c[e])}) is not tied with the selection boundary {c_k}"
+    for e in set(o) - set(g_ids):
+        if not (float(c[e]) - c_next < eps or (e // n) in tied_group):
+            return False, f"oracle expert {e} (score {float(c[e])}) dropped without a tie (next {c_next})"
+    for a, b in zip(g_ids, g_ids[1:]):
+        if float(c[a]) < float(c[b]) - eps:
+            return False, f"slot order inverted beyond eps: {a} ({float(c[a])}) before {b} ({float(c[b])})"
+    return True, ""
+
+
+def ulp_dist32(a, b):
+    """Distance in fp32 units in the last place between arrays of finite fp32 values (same-sign lattice)."""
+    ia = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+    return np.abs(ia - ib)
+
+
+def pool_map(fn, items, workers=None):
+    """Map over a thread pool: the oracle's ctypes calls release the GIL, so independent oracle evaluations run
+    on several host cores at once (the oracle itself stays single-threaded)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    items = list(items)
+    n = workers or min(16, os.cpu_count() or 4, max(1, len(items)))
+    if n <= 1:
+        return [fn(i) for i in items]
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        return list(ex.map(fn, items))
+
+
+def oracle_router_all(shape, x, seed=0, layer=0, topp=0.0, group=0):
+    """The oracle's router over every token: z, boundary flags of z, ids, w, near-tie flags, s and c scores."""
+    from oracle import oracle as O
+    Wr = synth.router_weights(shape, seed, layer)
+    bias = synth.router_bias(shape, seed, layer)
+    T = x.shape[0]
+    chunks = [(i, min(T, i + 64)) for i in range(0, T, 64)]
+    parts = pool_map(lambda ab: O.router_logits_boundary(x[ab[0]:ab[1]], Wr), chunks)
+    z = np.concatenate([p[0] for p in parts])
+    zb = np.concatenate([p[1] for p in parts])
+    ids, w, fl, s, c = O.route(O.Cfg.of(shape, group=group, topp=topp), z, bias, want_scores=True)
+    return dict(z=z, zb=zb, ids=ids, w=w, flags=fl, s=s, c=c)
+
+
+def oracle_slots(shape, x, pairs, seed=0, layer=0, weight_bits=4, group_size=0):
+    """Teacher-forced expert evaluations: pairs is a list of (token, expert, shared) triples (expert = the
+    GPU's id; shared expert index when shared). Per pair: h, qh, dh, out and g/u SwiGLU boundary flags, from the
+    oracle's own Q8_0 of x[token]. Experts are generated and quantized once each, on a thread pool."""
+    from oracle import oracle as O
+    by_e = {}
+    for i, (t, e, sh) in enumerate(pairs):
+        by_e.setdefault((int(e), bool(sh)), []).append((i, int(t)))
+    qx_all = {}
+    for t in sorted({int(t) for t, _, _ in pairs}):
+        qx_all[t] = O.q8_0(x[t])
+    keys = sorted(by_e)
+    out = [None] * len(pairs)
+    # generate on the calling thread (device fills), quantize and evaluate on the pool, in batches
+    batch = 16
+    for b0 in range(0, len(keys), batch):
+        ks = keys[b0:b0 + batch]
+        raw = {k: _gen_weights(shape, k[0], seed, layer, k[1]) for k in ks if
+               (shape, k[0], seed, layer, k[1], weight_bits, group_size) not in _ORACLE_CACHE}
+
+        def work(k):
+            ck = (shape, k[0], seed, layer, k[1], weight_bits, group_size)
+            if ck in _ORACLE_CACHE:
+                q13, s13, q2, s2 = _ORACLE_CACHE[ck]
+            else:
+                w13, w2 = raw[k]
+                if group_size:
+                    q13, s13 = O.quant_int4_grouped(w13, group_size)
+                    q2, s2 = O.quant_int4_grouped(w2, group_size)
+                else:
+                    quant = O.quant_int8_rows if weight_bits == 8 else O.quant_int4_rows
+                    q13, s13 = quant(w13)
+                    q2, s2 = quant(w2)
+            res = []
+            for i, t in by_e[k]:
+                qx, dx = qx_all[t]
+                r = O.expert_token(q13, s13, q2, s2, qx, dx)
+                g, u = O.gateup_token(q13, s13, qx, dx)
+                r["hb"] = O.swiglu_boundary(g, u)
+                res.append((i, r))
+            return ck, (q13, s13, q2, s2), res
+
+        for ck, q, res in pool_map(work, ks):
+            if len(_ORACLE_CACHE) < ORACLE_CACHE_MAX:
+                _ORACLE_CACHE[ck] = q
+            for i, r in res:
+                out[i] = r
+        del raw
+    return out
+
+
+def oracle_down_forced(shape, pairs, qh_rows, dh_rows, seed=0, layer=0, weight_bits=4, group_size=0):
+    """Teacher-forced down projection: the oracle's down rows for the (token, expert, shared) pairs applied to
+    the GPU's own Q8_0 h (qh_rows [n][I], dh_rows [n][I/32])."""
+    from oracle import oracle as O
+    res = []
+    for i, (t, e, sh) in enumerate(pairs):
+        q13, s13, q2, s2 = oracle_expert(shape, int(e), seed, layer, shared=bool(sh), weight_bits=weight_bits,
+                                         group_size=group_size)
+        res.append(O.down_token(q2, s2, qh_rows[i], dh_rows[i]))
+    return res

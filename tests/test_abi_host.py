@@ -129,3 +129,19 @@ def test_misaligned_inputs_rejected_before_any_device_work():
     wts2 = L.moe_layer_weights(*([4096, 4096, 4104] + [4096] * 7))
     rc = L._lib.moe_layer_forward(ctypes.byref(c), ctypes.byref(wts2), x, 4, x, x, 1 << 40, None, None)
     assert rc == L.MOE_E_ARG
+
+
+def test_binding_checks_tensors_before_the_library():
+    """The binding hands raw pointers to the library, so it refuses tensors that are not on the GPU, of the
+    wrong element type, strided, or smaller than the call touches, and a T above the rows of x."""
+    import torch
+    c = _glm()
+    x = torch.zeros((4, 6144), dtype=torch.float32)
+    with pytest.raises(moe.ArgError):
+        moe.moe_layer_forward(c, L.moe_layer_weights(), x, x, x)
+    with pytest.raises(moe.ArgError):
+        moe.moe_quantize_q8_0(x, x, x)
+    with pytest.raises(moe.ArgError):
+        L._need(x, "x", "f32")  # host tensor
+    with pytest.raises(moe.ArgError):
+        moe.taps(no_such_tap=x)

@@ -915,3 +915,112 @@ def test_page_size_arithmetic():
     assert abs(per_token / 1e9 - g["gb_changed_per_token"]) / g["gb_changed_per_token"] < 0.05
     assert abs(g["routed_experts_total"] * per_expert / 1e9 - g["gb_on_disk"]) / g["gb_on_disk"] < 0.05
     assert g["routed_experts_total"] == (g["moe_layers"] + 1) * g["experts_per_layer"]
+
+
+# ------------------------------------------------------- where several results are correct
+
+def _f32_nearest(fr):
+    """The fp32 value nearest to the exact rational fr (ties to even), by exact comparison with its neighbours."""
+    from fractions import Fraction
+    f = np.float32(float(fr))
+    best = None
+    for cand in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - fr)
+        key = (d, int(np.float32(cand).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return np.float32(best[1])
+
+
+def test_router_boundary_flags_constructed():
+    # 1 + 2^-24 is the exact midpoint of 1 and 1 + 2^-23: flagged; 1 + 2^-20 is an fp32 value: not flagged
+    x = np.array([[1.0, 1.0]], np.float32)
+    W = np.array([[1.0, 2.0 ** -24], [1.0, 2.0 ** -20]], np.float32)
+    z, fl = O.router_logits_boundary(x, W)
+    assert list(fl[0]) == [1, 0]
+    assert z[0, 1] == np.float32(1.0 + 2.0 ** -20)
+    assert np.array_equal(z, O.router_logits(x, W))
+
+
+def test_router_boundary_flags_cover_every_rounding_change():
+    """Where a logit is not flagged, the correctly rounded exact sum (fractions) is the oracle's logit; flagged
+    logits are rare on the GLM-like value range."""
+    from fractions import Fraction
+    x = synth.normal(6 * 256, 0, 21, 1.0).reshape(6, 256)
+    W = synth.normal(40 * 256, 0, 22, 0.02).reshape(40, 256)
+    z, fl = O.router_logits_boundary(x, W)
+    for t in range(6):
+        for e in range(40):
+            exact = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[t], W[e])), Fraction(0))
+            if not fl[t, e]:
+                assert z[t, e] == _f32_nearest(exact), (t, e)
+    assert fl.mean() < 0.02
+
+
+def test_swiglu_boundary_constructed():
+    # g = 64 + 2^-6, u = 1 + 2^-12: exp(-g) vanishes against 1 in fp64, so the value is g*u = 64 + 2^-5 + 2^-18
+    # exactly, the midpoint of two fp32 neighbours (ulp 2^-17 at 64): flagged. u = 1 gives g, an fp32 value.
+    g = np.array([64 + 2.0 ** -6, 64 + 2.0 ** -6, 0.0], np.float32)
+    u = np.array([1 + 2.0 ** -12, 1.0, 3.0], np.float32)
+    assert list(O.swiglu_boundary(g, u)) == [1, 0, 0]
+
+
+def test_swiglu_boundary_vs_long_double():
+    """Unflagged SwiGLU values equal the extended-precision value rounded once to fp32."""
+    rng = np.random.default_rng(31)
+    g = rng.normal(0, 3, 20000).astype(np.float32)
+    u = rng.normal(0, 3, 20000).astype(np.float32)
+    fl = O.swiglu_boundary(g, u)
+    gl, ul = g.astype(np.longdouble), u.astype(np.longdouble)
+    ref = (gl * ul / (np.longdouble(1) + np.exp(-gl))).astype(np.float32)
+    got = np.array([O.swiglu(a, b) for a, b in zip(g, u)], np.float32)
+    ok = fl == 0
+    assert np.array_equal(got[ok].view(np.uint32), ref[ok].view(np.uint32))
+    assert fl.sum() <= 2
+
+
+@pytest.mark.parametrize("group", [0, 64])
+def test_gateup_and_down_compose_the_expert(group):
+    sh = synth.TINY
+    w13, w2 = synth.expert_w13(sh, 2), synth.expert_w2(sh, 2)
+    if group:
+        q13, s13 = O.quant_int4_grouped(w13, group)
+        q2, s2 = O.quant_int4_grouped(w2, group)
+    else:
+        (q13, s13), (q2, s2) = O.quant_int4_rows(w13), O.quant_int4_rows(w2)
+    x = synth.hidden_states(sh, 2, step=3)
+    for t in range(2):
+        qx, dx = O.q8_0(x[t])
+        r = O.expert_token(q13, s13, q2, s2, qx, dx)
+        g, u = O.gateup_token(q13, s13, qx, dx)
+        h = np.array([O.swiglu(a, b) for a, b in zip(g, u)], np.float32)
+        assert np.array_equal(h.view(np.uint32), r["h"].view(np.uint32))
+        out = O.down_token(q2, s2, r["qh"], r["dh"])
+        assert np.array_equal(out.view(np.uint32), r["out"].view(np.uint32))
+        # the gate value of row 0 is the plain dot of its row
+        ref = O.dot_q4q8_grouped(q13[0], s13[0], group, qx, dx) if group else O.dot_q4q8(q13[0], s13[0], qx, dx)
+        assert g[0] == ref
+
+
+def test_tie_choice_checker_on_hand_ties():
+    """The validity check used for near-tie tokens accepts a choice inside the tie set and refuses others."""
+    from tests.harness import tie_choice_ok
+    g = HW["router_expert_tie"]  # experts 1, 2 and 4 tie at c = 0.625; the oracle takes 1 and 2
+    sh = synth.Shape(32, g["E"], g["G"], g["topk_group"], g["K"], 32, 0, g["rsf"])
+    ids, w, fl, s, c = _route_one(g["E"], g["G"], g["topk_group"], g["K"], g["rsf"], g["z"], g["bias"])
+    assert tie_choice_ok(sh, c[0], ids[0], [1, 2])[0]
+    assert tie_choice_ok(sh, c[0], ids[0], [1, 4])[0]   # another expert of the tie
+    assert tie_choice_ok(sh, c[0], ids[0], [2, 1])[0]   # slot order inside the tie
+    assert not tie_choice_ok(sh, c[0], ids[0], [1, 3])[0]  # expert 3 scores 0.5: no tie
+    assert not tie_choice_ok(sh, c[0], ids[0], [1, 1])[0]
+    g = HW["router_group_tie"]  # both groups score 1.125; the oracle keeps group 0 (experts 0, 1)
+    sh = synth.Shape(32, g["E"], g["G"], g["topk_group"], g["K"], 32, 0, g["rsf"])
+    ids, w, fl, s, c = _route_one(g["E"], g["G"], g["topk_group"], g["K"], g["rsf"], g["z"], g["bias"])
+    assert tie_choice_ok(sh, c[0], ids[0], [2, 3])[0]   # the other group of the tie
+    assert not tie_choice_ok(sh, c[0], ids[0], [0, 2])[0]  # two groups when one is kept
+    g = HW["router_clear"]  # no tie at all: only the oracle's own choice passes
+    sh = synth.Shape(32, g["E"], g["G"], g["topk_group"], g["K"], 32, 0, g["rsf"])
+    ids, w, fl, s, c = _route_one(g["E"], g["G"], g["topk_group"], g["K"], g["rsf"], g["z"], g["bias"])
+    assert tie_choice_ok(sh, c[0], ids[0], list(ids[0]))[0]
+    assert not tie_choice_ok(sh, c[0], ids[0], [3, 2])[0]
+    assert not tie_choice_ok(sh, c[0], ids[0], [0, 1])[0]

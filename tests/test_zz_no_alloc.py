@@ -5,6 +5,8 @@ library's fixed device array; its outputs must equal moe_layer_forward's bit for
 bit. Each case makes two calls in a row on that array, the second with fewer
 tokens, so that the second call runs over what the first one left behind.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -61,9 +63,14 @@ def test_noalloc_rejects_what_does_not_fit_before_any_work():
     layer = _layer("GLM")
     x = _x(synth.GLM, 8, 0)
     y = torch.zeros((8, synth.GLM.hidden), dtype=torch.float32, device=DEV)
-    with pytest.raises(moe.MoeError) as ei:
-        moe.moe_layer_forward_noalloc(cfg, layer.weights(), x, y, T=T)
-    assert ei.value.rc == moe.MOE_E_WORKSPACE
+    c = cfg.c()
+    w = layer.weights()
+    # straight through the C ABI: the binding itself refuses T above the rows of x
+    rc = moe._lib._lib.moe_layer_forward_noalloc(ctypes.byref(c), ctypes.byref(w), moe._lib._ptr(x), T,
+                                                 moe._lib._ptr(y), None, moe._lib._stream(None))
+    assert rc == moe.MOE_E_WORKSPACE
+    with pytest.raises(moe.ArgError):
+        moe.moe_layer_forward_noalloc(cfg, w, x, y, T=T)
     torch.cuda.synchronize()
     assert not bool(y.any())  # nothing was enqueued
 
