@@ -53,6 +53,8 @@ def parse():
                     help="comma-separated further workloads measured in the same run and reported under 'configs' "
                          "(default with the decode32 headline: decode1,mtp192,prefill,stack40; '' for none)")
     ap.add_argument("--config-steps", type=int, default=20, help="timed steps of each further workload")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps replayed as HIP graphs (one captured graph per step, same inputs)")
     ap.add_argument("--stack-layers", type=int, default=40, help="stack40: layers in the stack")
     ap.add_argument("--streamed", type=int, default=20, help="stack40: last layers whose experts stream from host")
     ap.add_argument("--slots", type=int, default=64, help="stack40: HBM expert slots per streamed layer")
@@ -476,10 +478,52 @@ def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_meas
         moe.moe_prof_disable()
         return ms, p
 
-    ms_step, prof = timed([kname])
-    # per-stage breakdown: a second pass over the same steps with every stage's
+    def clean():
+        """The timed value: the same steps with no stage events at all."""
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for s in range(steps):
+            i = args.warmup + s
+            moe.moe_layer_forward(cfg, wts[i % ncopy], xs[i % len(xs)], y, ws)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms_step = clean()
+    # the dominant kernel's launch durations: events around that launch only
+    ms_kernel_pass, prof = timed([kname])
+    # per-stage breakdown: a third pass over the same steps with every stage's
     # events (their own cost inflates it; not part of the timed value)
     ms_staged, prof_all = timed(None)
+    ms_graph = None
+    if args.graph:
+        # each step captured once as a HIP graph (the library's launches, helper-stream fork and join included),
+        # then the same steps replayed back to back
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            moe.moe_layer_forward(cfg, wts[0], xs[0], y, ws)  # helper stream and events of this stream exist now
+        torch.cuda.synchronize()
+        graphs = []
+        for s in range(steps):
+            i = args.warmup + s
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                moe.moe_layer_forward(cfg, wts[i % ncopy], xs[i % len(xs)], y, ws)
+            graphs.append(g)
+        for g in graphs[:3]:
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for g in graphs:
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = t0.elapsed_time(t1) / steps
+        del graphs
 
     H, I, E = shape.hidden, shape.inter, shape.n_experts
     # gate+up codes + fp32 scales (one per row, or one per group of GSZ along K)
@@ -532,7 +576,9 @@ def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_meas
         "routed_slots_mean": round(float(np.mean([st["counts"].sum() for st in stats])), 2),
         "heat": heat_summary(stats),
         "stage_ms": {n: round(float(v), 5) for n, v in zip(moe.STAGES, stage_ms)},
+        "ms_per_step_kernel_events": round(ms_kernel_pass, 5),
         "ms_per_step_all_stage_events": round(ms_staged, 5),
+        "ms_per_step_graph_replay": round(ms_graph, 5) if ms_graph else None,
         "roofline": roof,
     }
     # layer-level view: every expert's int8 ops (MFMA and v_dot4 paths) against the dense int8 MFMA peak, and the

@@ -1005,6 +1005,10 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
     mfma_down_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, sc);
 }
 
+// MFMA tiles: blocks in flight per wavefront (the gate/up tile is VALU-bound:
+// 2 blocks, or 3-4 wavefronts per SIMD instead of 2, measured no faster).
+constexpr int kMpfGateup = 4, kMpfDown = 4;
+
 // Blocks in flight per wavefront: about 4 KB of weights per wavefront when
 // many buckets stream at once (2 blocks of the two gate/up streams, 4 of the
 // single down stream), half that with a few buckets, where fewer queued
@@ -1076,7 +1080,7 @@ template <int NTT, int W, bool GS>
 static void mfma_gateup_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
-  constexpr int MPF = 4;  // blocks in flight (2 measured 3% slower for 64-position tiles)
+  constexpr int MPF = kMpfGateup;
   if ((a.H / 32) % MPF == 0) {
     if (tap) k_gateup_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_gateup_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
@@ -1090,7 +1094,7 @@ template <int NTT, int W, bool GS>
 static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
                              hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
-  constexpr int MPF = 4;  // blocks in flight (2 measured 3% slower for 64-position tiles)
+  constexpr int MPF = kMpfDown;
   if ((a.I / 32) % MPF == 0) {
     if (tap) k_down_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
     else k_down_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
