@@ -23,24 +23,6 @@
 
 namespace moe {
 
-struct DispatchArgs {
-  const int32_t* ids;
-  int32_t T, K, E, NS, gemm_min, tok_tile;
-  int32_t* counts;
-  int32_t* offsets;
-  int32_t* sorted;
-  int32_t* slotpos;
-  int32_t* unique;
-  int32_t* nunique;
-  int32_t* bk_e;
-  int32_t* bk_p0;
-  int32_t* bk_n;
-  int32_t* gemv;
-  int32_t* tiles;
-  int32_t* pos_token;
-  Meta* meta;
-};
-
 // T*K up to this: ids staged in LDS as 16-bit values (48 KB, with the 12 KB of tables under 64 KB)
 constexpr int kDispLdsSlots = 24576;
 
@@ -211,9 +193,9 @@ __global__ __launch_bounds__(256) void k_dispatch(DispatchArgs a) {
   }
 }
 
-hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
-                           const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
-                           int32_t* unique, int32_t* nunique, hipStream_t st) {
+DispatchArgs dispatch_args(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
+                           const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                           int32_t* slotpos, int32_t* unique, int32_t* nunique) {
   DispatchArgs a;
   a.ids = ids;
   a.T = T;
@@ -235,7 +217,11 @@ hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int g
   a.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
   a.pos_token = reinterpret_cast<int32_t*>(ws + L.pos_token);
   a.meta = reinterpret_cast<Meta*>(ws + L.meta);
-  const int64_t TK = (int64_t)T * c.top_k;
+  return a;
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, const moe_config& c, hipStream_t st) {
+  const int64_t TK = (int64_t)a.T * c.top_k;
   if (TK <= kDispLdsSlots)
     k_dispatch<true><<<(c.n_experts + 3) / 4, 256, (size_t)TK * sizeof(int16_t), st>>>(a);
   else

@@ -219,6 +219,68 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const float* 
     }
 }
 
+// Dispatch of a single token (T = 1) by its top-K workgroup, from the slots in
+// LDS: the kept slots hold distinct experts, so every bucket holds one
+// position and the stable counting sort of k_dispatch reduces to the rank of
+// each kept id among the kept ids. Writes the same arrays as k_dispatch.
+__device__ void dispatch_one_token(const DispatchArgs& a, const int* sel, const int* keep, int tid) {
+  const int E = a.E, K = a.K, lane = tid & 63;
+  // lane k < K of every wavefront holds slot k's expert (-1 when dropped); the loops below read the slots
+  // with readlane (K <= 32), so each lane reads LDS once
+  const int mine = lane < K && keep[lane] ? sel[lane] : -1;
+  const int nv = __popcll(__ballot(mine >= 0));  // kept slots
+  for (int e = tid; e < E; e += 256) {
+    int c = 0, off = 0;
+    for (int k = 0; k < K; ++k) {
+      const int s = __builtin_amdgcn_readlane(mine, k);
+      c += s == e;
+      off += s >= 0 && s < e;
+    }
+    a.counts[e] = c;
+    a.offsets[e] = off;
+    if (c) {
+      a.unique[off] = e;
+      a.bk_e[off] = e;
+      a.bk_p0[off] = off;
+      a.bk_n[off] = 1;
+    }
+  }
+  for (int u = nv + tid; u < E; u += 256) a.unique[u] = -1;
+  if (tid < K) {
+    int p = -1;
+    if (mine >= 0) {
+      p = 0;
+      for (int k = 0; k < K; ++k) {
+        const int s = __builtin_amdgcn_readlane(mine, k);
+        p += s >= 0 && s < mine;
+      }
+      a.sorted[p] = tid;
+      a.pos_token[p] = 0;
+    }
+    a.slotpos[tid] = p;
+  }
+  const int nbk = nv + a.NS;  // list entry b >= nv: shared bucket E + b - nv
+  const bool gemv = 1 < a.gemm_min;
+  for (int s = tid; s < a.NS; s += 256) {
+    a.bk_e[E + s] = E + s;
+    a.bk_p0[E + s] = K + s;
+    a.bk_n[E + s] = 1;
+  }
+  for (int b = tid; b < nbk; b += 256) {
+    int32_t* list = gemv ? a.gemv : a.tiles;
+    list[2 * b] = b < nv ? b : E + (b - nv);
+    list[2 * b + 1] = 0;
+  }
+  if (tid == 0) {
+    a.offsets[E] = nv;
+    a.nunique[0] = nv;
+    a.meta->n_unique = nv;
+    a.meta->n_buckets = nbk;
+    a.meta->n_gemv = gemv ? nbk : 0;
+    a.meta->n_tiles = gemv ? 0 : nbk;
+  }
+}
+
 // Top-k, one 256-lane workgroup per token. Every lane adds the 16 partial sums
 // of its experts in ascending order (all loads issued first) and rounds once
 // to fp32: the logit z. s = sigmoid(z) in fp64 rounded to fp32, c = s +
@@ -232,13 +294,17 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const float* 
 // groups counts, over a compacted copy of their scores, the ones that beat it.
 // Near-tie flags: kept/dropped group boundary,
 // chosen/next expert boundary, adjacent chosen experts (differences < 1e-6).
+// Without top-p, wavefront 0 finishes from registers (slot k in lane k): the
+// fp64 sum in slot order through readlane, the order flag by one ballot.
 // Adaptive top-p (0 < topp < 1): one lane visits the K slots by q = s / sum
 // descending (lower slot first on equal q) and keeps each while the fp64 sum
 // of the kept q is below topp; kept slots are renormalised over the kept s
 // (slot order), dropped slots get id -1 and weight 0.
+// DISP (one token, one workgroup): the workgroup goes on to the dispatch.
+template <bool DISP>
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, const float* __restrict__ bias, int E,
                                               int G, int KG, int K, float rsf, float topp, int32_t* __restrict__ ids,
-                                              float* __restrict__ w, uint8_t* __restrict__ flags) {
+                                              float* __restrict__ w, uint8_t* __restrict__ flags, DispatchArgs da) {
   __shared__ float s_s[kMaxExperts];
   __shared__ float s_c[kMaxExperts];
   __shared__ float s_gs[kMaxGroups];
@@ -352,37 +418,60 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
   }
   __syncthreads();
   const bool use_topp = topp > 0.0f && topp < 1.0f;
-  if (use_topp && tid < K) {
+  if (!use_topp) {
+    // every slot kept: wavefront 0 holds slot k in lane k and reads the slots with readlane (K <= 32)
+    if (wave == 0) {
+      const float sv = lane < K ? s_sels[lane] : 0.0f, cv = lane < K ? s_selc[lane] : 0.0f;
+      double sum = 0.0;  // in slot order
+      for (int k = 0; k < K; ++k)
+        sum += (double)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), k));
+      const float cn = __shfl_down(cv, 1);  // the next slot's score
+      const uint64_t ord = __ballot(lane + 1 < K && (double)cv - (double)cn < 1e-6);
+      if (lane == 0) {
+        uint8_t fl = ord ? MOE_TIE_ORDER : 0;
+        if (KG < G && (double)s_grank[KG - 1] - (double)s_grank[KG] < 1e-6) fl |= MOE_TIE_GROUP;
+        if (K < KG * n && (double)s_selc[K - 1] - (double)s_selc[K] < 1e-6) fl |= MOE_TIE_EXPERT;
+        if (flags) flags[t] = fl;
+      }
+      if (lane < K) {
+        ids[(size_t)t * K + lane] = s_sel[lane];
+        w[(size_t)t * K + lane] = (float)(((double)sv / sum) * (double)rsf);
+        s_keep[lane] = 1;
+      }
+    }
+    if constexpr (DISP) {
+      __syncthreads();
+      dispatch_one_token(da, s_sel, s_keep, tid);
+    }
+    return;
+  }
+  if (tid < K) {
     double sum = 0.0;
     for (int k = 0; k < K; ++k) sum += (double)s_sels[k];
     s_q[tid] = (double)s_sels[tid] / sum;
   }
   __syncthreads();
   if (tid == 0) {
-    double sum = 0.0;
-    for (int k = 0; k < K; ++k) sum += (double)s_sels[k];
     for (int k = 0; k < K; ++k) s_keep[k] = 1;
-    if (use_topp) {
-      uint32_t visited = 0u;  // K <= 32
-      double cum = 0.0;
-      for (int r = 0; r < K; ++r) {
-        int best = -1;
-        double bq = 0.0;
-        for (int k = 0; k < K; ++k) {
-          const double q = s_q[k];
-          if (!((visited >> k) & 1u) && (best < 0 || q > bq)) {
-            best = k;
-            bq = q;
-          }
+    uint32_t visited = 0u;  // K <= 32
+    double cum = 0.0;
+    for (int r = 0; r < K; ++r) {
+      int best = -1;
+      double bq = 0.0;
+      for (int k = 0; k < K; ++k) {
+        const double q = s_q[k];
+        if (!((visited >> k) & 1u) && (best < 0 || q > bq)) {
+          best = k;
+          bq = q;
         }
-        visited |= 1u << best;
-        if (cum < (double)topp) cum += bq;
-        else s_keep[best] = 0;
       }
-      sum = 0.0;
-      for (int k = 0; k < K; ++k)
-        if (s_keep[k]) sum += (double)s_sels[k];
+      visited |= 1u << best;
+      if (cum < (double)topp) cum += bq;
+      else s_keep[best] = 0;
     }
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k)
+      if (s_keep[k]) sum += (double)s_sels[k];
     s_sum = sum;
     uint8_t fl = 0;
     if (KG < G && (double)s_grank[KG - 1] - (double)s_grank[KG] < 1e-6) fl |= MOE_TIE_GROUP;
@@ -397,16 +486,20 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
     ids[(size_t)t * K + tid] = keep ? s_sel[tid] : -1;
     w[(size_t)t * K + tid] = keep ? (float)(((double)s_sels[tid] / s_sum) * (double)rsf) : 0.0f;
   }
+  if constexpr (DISP) dispatch_one_token(da, s_sel, s_keep, tid);
 }
 
 // Router + top-k. The logits come as 16 partial sums and, when qx_perm is
-// given, Q8_0 of x is encoded in the same launch (*q8_done = true).
+// given, Q8_0 of x is encoded in the same launch (*q8_done = true). One token
+// with disp given: the top-K workgroup also dispatches (*dispatched = true),
+// which saves the dispatch launch and its re-read of the ids.
 
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
-                        int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
-                        hipStream_t st) {
+                        int8_t* qx_nat, bool* q8_done, const DispatchArgs* disp, bool* dispatched, int mark_call,
+                        void (*mark)(int, int, hipStream_t), hipStream_t st) {
   if (q8_done) *q8_done = false;
+  if (dispatched) *dispatched = false;
   if (T <= 0) return hipSuccess;
   const int H = c.hidden, E = c.n_experts;
   const bool full = (H / kRouterChunks) % 16 == 0;
@@ -426,8 +519,14 @@ hipError_t launch_route(const float* x, int T, const moe_config& c, const float*
   }
   if (q8_done && qx_perm) *q8_done = true;
   if (mark) mark(mark_call, 1, st);
-  k_topk<<<T, 256, 0, st>>>(part, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, c.topp, ids,
-                            w, flags);
+  if (disp && T == 1) {
+    k_topk<true><<<1, 256, 0, st>>>(part, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, c.topp,
+                                    ids, w, flags, *disp);
+    if (dispatched) *dispatched = true;
+  } else {
+    k_topk<false><<<T, 256, 0, st>>>(part, bias, E, c.n_group, c.topk_group, c.top_k, c.routed_scaling_factor, c.topp,
+                                     ids, w, flags, DispatchArgs{});
+  }
   return hipGetLastError();
 }
 

@@ -262,14 +262,14 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
 hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
                      hipStream_t stream, int call) {
   const Layout& L = f.L;
-  bool q8_done = false;
+  bool q8_done = false, dispatched = false;
+  const DispatchArgs da = dispatch_args(f.ids, f.T, *f.cfg, f.gemm_min, f.tok_tile, L, f.wsb, f.counts, f.offsets,
+                                        f.sorted, f.slotpos, f.unique, f.nunique);
   hipError_t e = launch_route(x, f.T, *f.cfg, router_w, router_bias, reinterpret_cast<double*>(f.wsb + L.part),
-                              f.ids, f.w, f.flags, f.qx, f.dx, tp ? tp->qx : nullptr, &q8_done, call, prof_mark,
-                              stream);
+                              f.ids, f.w, f.flags, f.qx, f.dx, tp ? tp->qx : nullptr, &q8_done, &da, &dispatched,
+                              call, prof_mark, stream);
   prof_mark(call, 2, stream);
-  if (e == hipSuccess)
-    e = launch_dispatch(f.ids, f.T, *f.cfg, f.gemm_min, f.tok_tile, L, f.wsb, f.counts, f.offsets, f.sorted,
-                        f.slotpos, f.unique, f.nunique, stream);
+  if (e == hipSuccess && !dispatched) e = launch_dispatch(da, *f.cfg, stream);
   prof_mark(call, 3, stream);
   if (e == hipSuccess && !q8_done) e = launch_q8_0_x(x, f.T, f.cfg->hidden, f.qx, f.dx, tp ? tp->qx : nullptr, stream);
   if (e == hipSuccess && tp && tp->dx)
@@ -354,7 +354,8 @@ int32_t moe_router(const moe_config* cfg, const float* x, int32_t T, const float
   if ((rc = check_ws(L, ws, ws_bytes))) return rc;
   char* wsb = static_cast<char*>(ws);
   hipError_t e = launch_route(x, T, *cfg, router_w, router_bias, reinterpret_cast<double*>(wsb + L.part), topk_ids,
-                              topk_w, near_tie, nullptr, nullptr, nullptr, nullptr, -1, nullptr, stream);
+                              topk_w, near_tie, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, -1, nullptr,
+                              stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
@@ -368,8 +369,9 @@ int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, 
   Layout L = make_layout(*cfg, T);
   if ((rc = check_ws(L, ws, ws_bytes))) return rc;
   int gemm_min = cfg->gemm_min_tokens > 0 ? cfg->gemm_min_tokens : kDefaultGemmMin;
-  hipError_t e = launch_dispatch(topk_ids, T, *cfg, gemm_min, token_tile(T), L, static_cast<char*>(ws), counts, offsets,
-                                 sorted_slots, slot_pos, unique_ids, n_unique, stream);
+  hipError_t e = launch_dispatch(dispatch_args(topk_ids, T, *cfg, gemm_min, token_tile(T), L, static_cast<char*>(ws),
+                                               counts, offsets, sorted_slots, slot_pos, unique_ids, n_unique),
+                                 *cfg, stream);
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -35,6 +35,26 @@ struct Meta {
   int32_t n_tiles;
 };
 
+// Outputs of the batch-union dispatch (k_dispatch, or the top-K workgroup
+// itself for a single token) and its parameters.
+struct DispatchArgs {
+  const int32_t* ids;
+  int32_t T, K, E, NS, gemm_min, tok_tile;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted;
+  int32_t* slotpos;
+  int32_t* unique;
+  int32_t* nunique;
+  int32_t* bk_e;
+  int32_t* bk_p0;
+  int32_t* bk_n;
+  int32_t* gemv;
+  int32_t* tiles;
+  int32_t* pos_token;
+  Meta* meta;
+};
+
 // Device workspace layout for T tokens (all offsets 256-byte aligned).
 struct Layout {
   int64_t T = 0, E = 0, K = 0, H = 0, I = 0, NS = 0, TK = 0, R = 0, NB = 0, TILES = 0;
@@ -243,13 +263,16 @@ hipError_t launch_quant_int4_grouped(const float* w, int rows, int cols, int gro
                                      hipStream_t st);
 hipError_t launch_quant_int4(const float* w, int rows, int cols, uint8_t* packed, float* scales,
                              hipStream_t st);
+// Router + top-K; with disp given and T == 1 the top-K workgroup also writes
+// the dispatch arrays (*dispatched = true).
 hipError_t launch_route(const float* x, int T, const moe_config& c, const float* Wr, const float* bias,
                         double* part, int32_t* ids, float* w, uint8_t* flags, int8_t* qx_perm, float* dx,
-                        int8_t* qx_nat, bool* q8_done, int mark_call, void (*mark)(int, int, hipStream_t),
-                        hipStream_t st);
-hipError_t launch_dispatch(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
-                           const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* slotpos,
-                           int32_t* unique, int32_t* nunique, hipStream_t st);
+                        int8_t* qx_nat, bool* q8_done, const DispatchArgs* disp, bool* dispatched, int mark_call,
+                        void (*mark)(int, int, hipStream_t), hipStream_t st);
+DispatchArgs dispatch_args(const int32_t* ids, int T, const moe_config& c, int gemm_min, int tok_tile,
+                           const Layout& L, char* ws, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                           int32_t* slotpos, int32_t* unique, int32_t* nunique);
+hipError_t launch_dispatch(const DispatchArgs& a, const moe_config& c, hipStream_t st);
 hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
 hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
 hipError_t launch_tile_gather(const ExpertArgs& a, int grid, int tok_tile, const int32_t* tiles,

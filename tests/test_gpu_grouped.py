@@ -101,17 +101,17 @@ def _run(layer, x, gemm_min=0, sum_slot=-1, want_taps=True):
     return _np(y), {k: _np(v) for k, v in bufs.items()}
 
 
-@pytest.mark.parametrize("T", [16, 64])
+@pytest.mark.parametrize("T", [1, 16, 64])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("gemm_min", [1000, 1, 4])
 def test_grouped_layer_tiny_all_stages(G, gemm_min, T):
     """Every tap bit-exact against the oracle with group scales, on the GEMV path, the MFMA path (T = 64: buckets
-    past one 32-position tile) and a mix."""
+    past one 32-position tile) and a mix; T = 1 takes the one-token dispatch."""
     layer, ref = _tiny(G)
     sh = synth.TINY
     K = sh.top_k
     x = synth.hidden_states(sh, T, seed=31)
-    slot = 6
+    slot = 6 if T > 1 else 2
     y, tp = _run(layer, x, gemm_min, sum_slot=slot)
     yr, tr = O.layer_forward(O.Cfg.of(sh, group=G), x, ref)
     assert not (tr["flags"] & (O.TIE_EXPERT | O.TIE_GROUP)).any()

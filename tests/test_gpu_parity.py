@@ -216,18 +216,9 @@ def _run_layer(layer, shape, x, gemm_min=0, sum_slot=-1, want_taps=True):
     return _np(y), {k: _np(v) for k, v in bufs.items()}
 
 
-@pytest.mark.parametrize("T", [8, 16, 64])
-@pytest.mark.parametrize("gemm_min", [1000, 1, 4])
-def test_layer_tiny_all_stages(tiny_gpu, tiny_ref, gemm_min, T):
-    """Every tap bit-exact against the oracle; the GEMV path (gemm_min=1000, buckets split into chunks of up to 4
-    tokens), the MFMA path (gemm_min=1) and a mix give the same bits. The tiny shape has one block per
-    accumulation class in gate/up and four empty classes in down; T=8 runs the few-bucket GEMV depth, T=16 the
-    many-bucket one. T=64 gives buckets of up to 38 positions: MFMA tiles that are full, part-filled and a
-    second tile with a ragged tail."""
+def _check_all_stages(tiny_gpu, tiny_ref, x, gemm_min, slot):
     sh = synth.TINY
-    K = sh.top_k
-    x = synth.hidden_states(sh, T)
-    slot = 5
+    T, K = x.shape[0], sh.top_k
     y, tp = _run_layer(tiny_gpu, sh, x, gemm_min, sum_slot=slot)
     yr, tr = O.layer_forward(O.Cfg.of(sh), x, tiny_ref)
     assert not (tr["flags"] & (O.TIE_EXPERT | O.TIE_GROUP)).any()
@@ -243,13 +234,40 @@ def test_layer_tiny_all_stages(tiny_gpu, tiny_ref, gemm_min, T):
     d = O.dispatch(tr["ids"], sh.n_experts)
     for k in ("counts", "offsets", "sorted_slots", "slot_pos", "unique_ids"):
         assert np.array_equal(tp[k], d[k]), k
-    # block sums of one slot: exact int32
-    e = tr["ids"].reshape(-1)[slot]
-    q13, q2 = tiny_ref.q13[e], tiny_ref.q2[e]
-    S13 = (q13.astype(np.int64) * tr["qx"][slot // K].astype(np.int64)[None]).reshape(2 * sh.inter, -1, 32).sum(2)
+    # block sums of one slot (a routed slot, or a shared expert's row): exact int32
+    if slot < T * K:
+        e = tr["ids"].reshape(-1)[slot]
+        q13, q2 = tiny_ref.q13[e], tiny_ref.q2[e]
+        t = slot // K
+    else:
+        s, t = divmod(slot - T * K, T)
+        q13, q2 = tiny_ref.sq13[s], tiny_ref.sq2[s]
+    S13 = (q13.astype(np.int64) * tr["qx"][t].astype(np.int64)[None]).reshape(2 * sh.inter, -1, 32).sum(2)
     S2 = (q2.astype(np.int64) * tr["qh"][slot].astype(np.int64)[None]).reshape(sh.hidden, -1, 32).sum(2)
     assert np.array_equal(tp["gateup_sums"], S13)
     assert np.array_equal(tp["down_sums"], S2)
+
+
+@pytest.mark.parametrize("T", [8, 16, 64])
+@pytest.mark.parametrize("gemm_min", [1000, 1, 4])
+def test_layer_tiny_all_stages(tiny_gpu, tiny_ref, gemm_min, T):
+    """Every tap bit-exact against the oracle; the GEMV path (gemm_min=1000, buckets split into chunks of up to 4
+    tokens), the MFMA path (gemm_min=1) and a mix give the same bits. The tiny shape has one block per
+    accumulation class in gate/up and four empty classes in down; T=8 runs the few-bucket GEMV depth, T=16 the
+    many-bucket one. T=64 gives buckets of up to 38 positions: MFMA tiles that are full, part-filled and a
+    second tile with a ragged tail."""
+    _check_all_stages(tiny_gpu, tiny_ref, synth.hidden_states(synth.TINY, T), gemm_min, 5)
+
+
+@pytest.mark.parametrize("seed", [0, 3])
+@pytest.mark.parametrize("slot", [2, 4])
+@pytest.mark.parametrize("gemm_min", [1000, 1, 0])
+def test_layer_tiny_one_token(tiny_gpu, tiny_ref, gemm_min, slot, seed):
+    """One token: the top-K workgroup writes the dispatch arrays itself (the dispatch launch is skipped), both for
+    the GEMV work list (gemm_min 0 or 1000) and for MFMA tiles (gemm_min=1). Every tap bit-exact, block sums of a
+    routed slot (2) and of the shared expert (4)."""
+    x = synth.hidden_states(synth.TINY, 1, seed=70 + seed)
+    _check_all_stages(tiny_gpu, tiny_ref, x, gemm_min, slot)
 
 
 def test_layer_tiny_batch_invariance(tiny_gpu):

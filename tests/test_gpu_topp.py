@@ -130,6 +130,31 @@ def test_topp_layer_tiny_all_stages(tiny, gemm_min, topp):
     assert np.array_equal(tp["counts"], np.bincount(tr["ids"][tr["ids"] >= 0], minlength=sh.n_experts))
 
 
+@pytest.mark.parametrize("gemm_min", [1000, 1])
+def test_topp_layer_tiny_one_token(tiny, gemm_min):
+    """One token at a time with adaptive top-p: the top-K workgroup dispatches only the kept slots (dropped slots
+    have no position and no share in the combine)."""
+    layer, ref = tiny
+    sh = synth.TINY
+    dropped = 0
+    for seed in range(8):
+        x = synth.hidden_states(sh, 1, seed=200 + seed)
+        y, tp = _run(layer, x, 0.5, gemm_min)
+        yr, tr = O.layer_forward(O.Cfg.of(sh, topp=0.5), x, ref)
+        if tr["flags"][0] & (O.TIE_EXPERT | O.TIE_GROUP):
+            continue
+        assert np.array_equal(tp["topk_ids"], tr["ids"])
+        assert np.array_equal(tp["topk_w"].view(np.uint32), tr["w"].view(np.uint32))
+        kept = np.concatenate([tr["ids"].ravel() >= 0, np.ones(layer.NS, bool)])
+        dropped += int((~kept).sum())
+        for k in ("h", "e_out"):
+            assert np.array_equal(tp[k][kept].view(np.uint32), tr[k][kept].view(np.uint32)), (seed, k)
+        assert np.array_equal(y.view(np.uint32), yr.view(np.uint32)), seed
+        assert np.array_equal(tp["counts"], np.bincount(tr["ids"][tr["ids"] >= 0], minlength=sh.n_experts))
+        assert tp["n_unique"][0] == (tr["ids"] >= 0).sum()
+    assert dropped > 0
+
+
 def test_topp_off_values_equal_no_topp(tiny):
     layer, _ = tiny
     x = synth.hidden_states(synth.TINY, 16, seed=71)
