@@ -135,10 +135,14 @@ template <int W>
 struct WBlk {
   uint4 v[W / 4];
 };
+// Weight codes are streamed once per work item: non-temporal loads, which keep
+// them from displacing reused data in the caches (the decode GEMV and the
+// streaming peak both measured ~10% faster with them).
 template <int W>
 __device__ __forceinline__ void load_wblk(WBlk<W>& b, const uint8_t* p) {
 #pragma unroll
-  for (int i = 0; i < W / 4; ++i) b.v[i] = reinterpret_cast<const uint4*>(p)[i];
+  for (int i = 0; i < W / 4; ++i)
+    b.v[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p) + i));
 }
 template <int W>
 struct WPrep;
@@ -530,11 +534,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
+// AUX: cache policy bits of the load; kLoadNT marks it non-temporal.
+constexpr int kLoadNT = 2;
+template <int AUX = 0>
 __device__ __forceinline__ v2i buf_v2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, AUX));
 }
+template <int AUX = 0>
 __device__ __forceinline__ v4i buf_v4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
 }
 __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
@@ -581,10 +589,14 @@ template <int W>
 __device__ __forceinline__ uint32_t a_lane_off(int col, int half) {
   return (uint32_t)col * (4 * W) + (uint32_t)(2 * W) * half;
 }
-template <int W>
+// NT: the tile is its bucket's only one, so its weights are read once (non-temporal loads); tiles of larger
+// buckets read the same weights one after the other and keep them cached (non-temporal there measured 4%
+// slower at prefill, 2% faster at MTP verify where nearly all buckets fit one tile).
+template <int W, bool NT>
 __device__ __forceinline__ ARaw<W> load_a(__amdgpu_buffer_rsrc_t r, uint32_t loff, int blk) {
-  if constexpr (W == 4) return buf_v2(r, loff, (uint32_t)blk * (uint32_t)kTileBlock<4>);
-  else return buf_v4(r, loff, (uint32_t)blk * (uint32_t)kTileBlock<8>);
+  constexpr int aux = NT ? kLoadNT : 0;
+  if constexpr (W == 4) return buf_v2<aux>(r, loff, (uint32_t)blk * (uint32_t)kTileBlock<4>);
+  else return buf_v4<aux>(r, loff, (uint32_t)blk * (uint32_t)kTileBlock<8>);
 }
 template <int W>
 __device__ __forceinline__ v4i a_operand(ARaw<W> w) {
@@ -622,30 +634,11 @@ __device__ __forceinline__ void scales_get(const float* slot, int half, float (&
   }
 }
 
-template <int NTT, int W>
-__device__ __forceinline__ void load_gu_block(__amdgpu_buffer_rsrc_t gr, __amdgpu_buffer_rsrc_t ur,
-                                              __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t dr, int blk,
-                                              uint32_t loff, const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT],
-                                              ARaw<W>& rg, ARaw<W>& ru, v4i (&rb)[NTT], float (&rd)[NTT]) {
-  rg = load_a<W>(gr, loff, blk);
-  ru = load_a<W>(ur, loff, blk);
-  load_operands<NTT>(xr, dr, blk, xo, xso, rb, rd);
-}
-
-template <int NTT, int W>
-__device__ __forceinline__ void load_dn_block(__amdgpu_buffer_rsrc_t wr, __amdgpu_buffer_rsrc_t xr,
-                                              __amdgpu_buffer_rsrc_t dr, int blk, uint32_t loff,
-                                              const uint32_t (&xo)[NTT], const uint32_t (&xso)[NTT], ARaw<W>& ra,
-                                              v4i (&rb)[NTT], float (&rd)[NTT]) {
-  ra = load_a<W>(wr, loff, blk);
-  load_operands<NTT>(xr, dr, blk, xo, xso, rb, rd);
-}
-
 // 32 gate rows and the matching 32 up rows per wavefront (one 32x32 MFMA tile
 // each), NTT x 32 tokens. t32 = index of the 32-row block. Columns past the
 // bucket's end compute on the last token (a valid address) and are never
 // stored; each column's results depend on that column alone.
-template <int NTT, int PF, bool TAP, int W, bool GS>
+template <int NTT, int PF, bool TAP, int W, bool GS, bool NT>
 __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w13, const float* s13,
                                  int t32, int lane, float* scl) {
   const int tile = t32 >> 1, s = t32 & 1;
@@ -690,8 +683,8 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   int fetch = 0;  // next block to load
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {  // loads in the loop's order
-    rg[kk] = load_a<W>(gr, loff, fetch);
-    ru[kk] = load_a<W>(ur, loff, fetch);
+    rg[kk] = load_a<W, NT>(gr, loff, fetch);
+    ru[kk] = load_a<W, NT>(ur, loff, fetch);
     load_codes<NTT>(xr, fetch, xo, rb[kk]);
     if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
     load_scales<NTT>(dr, fetch, xso, rd[kk]);
@@ -716,8 +709,8 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
         Su[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Au, rb[kk][tt], zero, 0, 0, 0);
       }
       // refill the slot just consumed: codes now, scales after their last use
-      rg[kk] = load_a<W>(gr, loff, fetch);
-      ru[kk] = load_a<W>(ur, loff, fetch);
+      rg[kk] = load_a<W, NT>(gr, loff, fetch);
+      ru[kk] = load_a<W, NT>(ur, loff, fetch);
       load_codes<NTT>(xr, fetch, xo, rb[kk]);
       if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
 #pragma unroll
@@ -787,7 +780,7 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
 
 // 32 output rows per wavefront, NTT x 32 positions. t32 = index of the
 // 32-row block. Columns past the bucket's end as in the gate/up tile.
-template <int NTT, int PF, bool TAP, int W, bool GS>
+template <int NTT, int PF, bool TAP, int W, bool GS, bool NT>
 __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w2, const float* s2,
                                int t32, int lane, float* scl) {
   const int tile = t32 >> 1, s = t32 & 1;
@@ -828,7 +821,7 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   int fetch = 0;
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {  // loads in the loop's order
-    ra[kk] = load_a<W>(wr, loff, fetch);
+    ra[kk] = load_a<W, NT>(wr, loff, fetch);
     load_codes<NTT>(xr, fetch, xo, rb[kk]);
     if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
     load_scales<NTT>(dr, fetch, xso, rd[kk]);
@@ -849,7 +842,7 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) S[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, rb[kk][tt], zero, 0, 0, 0);
       // refill the slot just consumed: codes now, scales after their last use
-      ra[kk] = load_a<W>(wr, loff, fetch);
+      ra[kk] = load_a<W, NT>(wr, loff, fetch);
       load_codes<NTT>(xr, fetch, xo, rb[kk]);
       if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
 #pragma unroll
@@ -929,8 +922,8 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
 // Separate GEMV and MFMA kernels keep each path's register budget (and so its
 // occupancy) independent; the host runs the two chains on two streams so they
 // overlap. TAP instantiations write block-sum taps and are launched only when
-// those taps are requested. The MFMA path keeps 4 blocks in flight, or 2
-// when 4 does not divide the block count (2 always does).
+// those taps are requested. The MFMA gate/up tile keeps 4 blocks in flight
+// (2 when 4 does not divide the block count; 2 always does), the down tile 2.
 
 // PF: blocks in flight per wavefront (chosen by the host).
 // W: weight code width (4 or 8); GS: grouped weight scales (int4 only). Both
@@ -979,10 +972,15 @@ __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t*
     __shared__ float scl[2 * 64];
     sc = scl;
   }
-  if (NTT == 2 && k.n - t0 <= 32)  // a bucket's last tile with one 32-token half: skip the empty one
-    mfma_gateup_tile<1, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane, sc);
-  else
-    mfma_gateup_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w13, s13, tile, lane, sc);
+  // a bucket's last tile with one 32-token half runs as a 32-token tile (the empty half skipped). With 32-token
+  // tiles, the only tile of a bucket of up to 32 tokens streams its weights non-temporally (the 64-token kernels,
+  // used at prefill, keep one tile form per half: a third instantiation crashes the compiler's AGPR-copy rewrite)
+  if (NTT == 1 || k.n - t0 <= 32) {
+    if (NTT == 1 && k.n <= 32) mfma_gateup_tile<1, MPF, TAP, W, GS, true>(a, k, t0, w13, s13, tile, lane, sc);
+    else mfma_gateup_tile<1, MPF, TAP, W, GS, false>(a, k, t0, w13, s13, tile, lane, sc);
+  } else {
+    mfma_gateup_tile<NTT, MPF, TAP, W, GS, false>(a, k, t0, w13, s13, tile, lane, sc);
+  }
 }
 
 template <int NTT, int MPF, bool TAP, int W, bool GS>
@@ -999,15 +997,18 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
     __shared__ float scl[2 * 64];
     sc = scl;
   }
-  if (NTT == 2 && k.n - t0 <= 32)
-    mfma_down_tile<1, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, sc);
-  else
-    mfma_down_tile<NTT, MPF, TAP, W, GS>(a, k, t0, w2, s2, tile, lane, sc);
+  if (NTT == 1 || k.n - t0 <= 32) {  // as in the gate/up kernel
+    if (NTT == 1 && k.n <= 32) mfma_down_tile<1, MPF, TAP, W, GS, true>(a, k, t0, w2, s2, tile, lane, sc);
+    else mfma_down_tile<1, MPF, TAP, W, GS, false>(a, k, t0, w2, s2, tile, lane, sc);
+  } else {
+    mfma_down_tile<NTT, MPF, TAP, W, GS, false>(a, k, t0, w2, s2, tile, lane, sc);
+  }
 }
 
 // MFMA tiles: blocks in flight per wavefront (the gate/up tile is VALU-bound:
-// 2 blocks, or 3-4 wavefronts per SIMD instead of 2, measured no faster).
-constexpr int kMpfGateup = 4, kMpfDown = 4;
+// 2 blocks, or 3-4 wavefronts per SIMD instead of 2, measured no faster; the
+// down tile with 2 measured 0.5% faster at prefill than with 4, 8 slower).
+constexpr int kMpfGateup = 4, kMpfDown = 2;
 
 // Blocks in flight per wavefront: about 4 KB of weights per wavefront when
 // many buckets stream at once (2 blocks of the two gate/up streams, 4 of the

@@ -7,7 +7,10 @@ namespace moe {
 
 // Every lane reads UNR 16-byte words per iteration of a grid-stride loop and
 // folds them into one word that is written only if it matches a value the
-// data never produces (so the loads cannot be optimised away).
+// data never produces (so the loads cannot be optimised away). The loads are
+// non-temporal, as the expert kernels' weight streams are (~11% more
+// bandwidth than plain loads on this chip).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 template <int UNR>
 __global__ __launch_bounds__(256) void k_read(const uint4* __restrict__ src, size_t n16, uint32_t* __restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -16,12 +19,13 @@ __global__ __launch_bounds__(256) void k_read(const uint4* __restrict__ src, siz
   for (; i + (UNR - 1) * stride < n16; i += UNR * stride) {
     uint4 v[UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < UNR; ++u)
+      v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i + u * stride));
 #pragma unroll
     for (int u = 0; u < UNR; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
-    uint4 v = src[i];
+    uint4 v = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i));
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
