@@ -778,12 +778,15 @@ __device__ void mfma_gateup_tile(const ExpertArgs& a, const Bucket& k, int t0, c
   }
 }
 
-// 32 output rows per wavefront, NTT x 32 positions. t32 = index of the
-// 32-row block. Columns past the bucket's end as in the gate/up tile.
+// 64 output rows per wavefront (two 32x32 MFMA tiles, rows r0 .. r0+31 and
+// r0+32 .. r0+63 of one 64-row weight tile), NTT x 32 positions: the two
+// weight operands share each activation operand, which halves the activation
+// loads per MFMA against one 32-row tile per wavefront (the 32-row form waited
+// on those loads ~70% of its cycles at prefill). Columns past the bucket's end
+// as in the gate/up tile.
 template <int NTT, int PF, bool TAP, int W, bool GS, bool NT>
 __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, const uint8_t* w2, const float* s2,
-                               int t32, int lane, float* scl) {
-  const int tile = t32 >> 1, s = t32 & 1;
+                               int tile, int lane, float* scl) {
   const int H = a.H, I = a.I, nbi = I / 32;
   const int col = lane & 31, half = lane >> 5;
   const uint32_t loff = a_lane_off<W>(col, half);
@@ -803,25 +806,28 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
     if (TAP && valid[tt] && slot_of(a, k, p) == a.sum_slot) tap_tt = tt;
   }
   const v16i zero = {0};
-  const int r0 = tile * 64 + s * 32;
-  const auto wr = buf_rsrc(w2 + tbw_off<W>(tile, 0, nbi) + s * 32 * (4 * W));
+  const int r0 = tile * 64;
+  const auto wr0 = buf_rsrc(w2 + tbw_off<W>(tile, 0, nbi));
+  const auto wr1 = buf_rsrc(w2 + tbw_off<W>(tile, 0, nbi) + 32 * (4 * W));
   const auto xr = buf_rsrc(xbase), dr = buf_rsrc(dbase);
-  float acc[NTT][16];  // one chain per result element
+  float a0[NTT][16], a1[NTT][16];  // one chain per result element: rows r0 + m, r0 + 32 + m
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[tt][i] = 0.0f;
-  ARaw<W> ra[PF];
+    for (int i = 0; i < 16; ++i) a0[tt][i] = a1[tt][i] = 0.0f;
+  ARaw<W> ra0[PF], ra1[PF];
   v4i rb[PF][NTT];
   float rd[PF][NTT];
+  // grouped scales: lane l streams row r0 + l (lanes 0-31 the first 32 rows, 32-63 the second)
   const int gsh = GS ? a.gshift : 0, ngs = GS ? nbi >> gsh : 0;
   const auto sr = buf_rsrc(s2);
-  const uint32_t soff = (uint32_t)((tile * ngs * 64 + s * 32 + col) * 4);  // row r0 + lane % 32
+  const uint32_t soff = (uint32_t)((tile * ngs * 64 + lane) * 4);
   float rs[PF];
   int fetch = 0;
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {  // loads in the loop's order
-    ra[kk] = load_a<W, NT>(wr, loff, fetch);
+    ra0[kk] = load_a<W, NT>(wr0, loff, fetch);
+    ra1[kk] = load_a<W, NT>(wr1, loff, fetch);
     load_codes<NTT>(xr, fetch, xo, rb[kk]);
     if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
     load_scales<NTT>(dr, fetch, xso, rd[kk]);
@@ -831,30 +837,38 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
   for (int b0 = 0; b0 < nbi; b0 += PF) {
 #pragma unroll
     for (int kk = 0; kk < PF; ++kk) {
-      const v4i A = a_operand<W>(ra[kk]);
-      float os16[16];
+      const v4i A0 = a_operand<W>(ra0[kk]), A1 = a_operand<W>(ra1[kk]);
+      float os0[16], os1[16];
       if constexpr (GS) {
         float* slot = scl + 64 * (kk & 1);
         scales_put(slot, rs[kk], lane);
-        scales_get(slot, half, os16, 0);
+        scales_get(slot, half, os0, 0);
+        scales_get(slot, half, os1, 32);
       }
-      v16i S[NTT];  // (16 x) block sums
+      v16i S0[NTT], S1[NTT];  // (16 x) block sums
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) S[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, rb[kk][tt], zero, 0, 0, 0);
+      for (int tt = 0; tt < NTT; ++tt) {
+        S0[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A0, rb[kk][tt], zero, 0, 0, 0);
+        S1[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A1, rb[kk][tt], zero, 0, 0, 0);
+      }
       // refill the slot just consumed: codes now, scales after their last use
-      ra[kk] = load_a<W, NT>(wr, loff, fetch);
+      ra0[kk] = load_a<W, NT>(wr0, loff, fetch);
+      ra1[kk] = load_a<W, NT>(wr1, loff, fetch);
       load_codes<NTT>(xr, fetch, xo, rb[kk]);
       if constexpr (GS) rs[kk] = buf_f32(sr, soff, (uint32_t)(fetch >> gsh) * 256);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) {
         const float d = rd[kk][tt];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          acc[tt][i] = fmaf(GS ? __fmul_rn(d, os16[i]) : d, (float)S[tt][i], acc[tt][i]);
+        for (int i = 0; i < 16; ++i) a0[tt][i] = fmaf(GS ? __fmul_rn(d, os0[i]) : d, (float)S0[tt][i], a0[tt][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a1[tt][i] = fmaf(GS ? __fmul_rn(d, os1[i]) : d, (float)S1[tt][i], a1[tt][i]);
         if (TAP && tt == tap_tt) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = true_sum<W>(S[tt][i]);
+          for (int i = 0; i < 16; ++i) {
+            a.t_dn_sums[(size_t)(r0 + out_row(i, lane)) * nbi + blk] = true_sum<W>(S0[tt][i]);
+            a.t_dn_sums[(size_t)(r0 + 32 + out_row(i, lane)) * nbi + blk] = true_sum<W>(S1[tt][i]);
+          }
         }
       }
       load_scales<NTT>(dr, fetch, xso, rd[kk]);
@@ -862,26 +876,26 @@ __device__ void mfma_down_tile(const ExpertArgs& a, const Bucket& k, int t0, con
       ++blk;
     }
   }
-  float so[16];  // row scales (one scale per row only)
-#pragma unroll
-  for (int i = 0; i < 16; ++i) so[i] = GS ? 1.0f : s2[r0 + out_row(i, lane)];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
     if (!valid[tt]) continue;
-    const float(&tot)[16] = acc[tt];
     const int p = k.p0 + t0 + tt * 32 + col;
     float* orow = a.eout + (size_t)p * H + r0;
     float* trow = a.t_eout ? a.t_eout + (size_t)slot_of(a, k, p) * H + r0 : nullptr;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float4 v;
-      v.x = GS ? tot[4 * g + 0] : __fmul_rn(so[4 * g + 0], tot[4 * g + 0]);
-      v.y = GS ? tot[4 * g + 1] : __fmul_rn(so[4 * g + 1], tot[4 * g + 1]);
-      v.z = GS ? tot[4 * g + 2] : __fmul_rn(so[4 * g + 2], tot[4 * g + 2]);
-      v.w = GS ? tot[4 * g + 3] : __fmul_rn(so[4 * g + 3], tot[4 * g + 3]);
-      const int mm = 8 * g + 4 * half;
-      *reinterpret_cast<float4*>(orow + mm) = v;
-      if (trow) *reinterpret_cast<float4*>(trow + mm) = v;
+    for (int hh = 0; hh < 2; ++hh) {
+      const float(&tot)[16] = hh ? a1[tt] : a0[tt];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int mm = 32 * hh + 8 * g + 4 * half;  // rows mm .. mm+3 of the 64-row tile
+        float4 v;
+        v.x = GS ? tot[4 * g + 0] : __fmul_rn(s2[r0 + mm + 0], tot[4 * g + 0]);
+        v.y = GS ? tot[4 * g + 1] : __fmul_rn(s2[r0 + mm + 1], tot[4 * g + 1]);
+        v.z = GS ? tot[4 * g + 2] : __fmul_rn(s2[r0 + mm + 2], tot[4 * g + 2]);
+        v.w = GS ? tot[4 * g + 3] : __fmul_rn(s2[r0 + mm + 3], tot[4 * g + 3]);
+        *reinterpret_cast<float4*>(orow + mm) = v;
+        if (trow) *reinterpret_cast<float4*>(trow + mm) = v;
+      }
     }
   }
 }
@@ -1133,7 +1147,7 @@ hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int3
 hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
                             hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  dim3 g(a.H / 32, grid);
+  dim3 g(a.H / 64, grid);  // 64-row tiles
   if (a.wbits == 8) {
     if (ntt == 2) mfma_down_launch<2, 8, false>(a, g, tiles, n_tiles, st);
     else mfma_down_launch<1, 8, false>(a, g, tiles, n_tiles, st);
