@@ -48,6 +48,7 @@ __device__ __forceinline__ const CAS T* cptr(const T* p) {
 struct Bucket {
   int ex, p0, n;
   bool shared;
+  const int* sl;  // a routed bucket found by its own workgroup: the slots of its positions (LDS), else null
 };
 
 __device__ __forceinline__ Bucket load_bucket(const ExpertArgs& a, int b) {
@@ -56,15 +57,18 @@ __device__ __forceinline__ Bucket load_bucket(const ExpertArgs& a, int b) {
   k.p0 = cptr(a.bk_p0)[b];
   k.n = cptr(a.bk_n)[b];
   k.shared = k.ex >= a.E;
+  k.sl = nullptr;
   return k;
 }
 
 __device__ __forceinline__ int token_of(const ExpertArgs& a, const Bucket& k, int p) {
-  return k.shared ? (p - a.TK) % a.T : cptr(a.pos_token)[p];
+  if (k.shared) return (p - a.TK) % a.T;
+  return k.sl ? k.sl[p - k.p0] / a.K : cptr(a.pos_token)[p];
 }
 
 __device__ __forceinline__ int slot_of(const ExpertArgs& a, const Bucket& k, int p) {
-  return k.shared ? p : cptr(a.sorted)[p];
+  if (k.shared) return p;
+  return k.sl ? k.sl[p - k.p0] : cptr(a.sorted)[p];
 }
 
 // Does the block-sum tap slot fall in positions [p, p+n) of this bucket?
@@ -939,16 +943,67 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
 // those taps are requested. The MFMA gate/up tile keeps 4 blocks in flight
 // (2 when 4 does not divide the block count; 2 always does), the down tile 2.
 
+// A GEMV gate/up workgroup that finds its bucket from the top-K ids alone, so
+// that it can start before the dispatch has run (small batches, a.self_min >
+// 0): workgroup row y is routed expert y or shared expert y - E. The positions
+// of routed expert e are the slots holding e in ascending slot order, after
+// the slots of the lower experts (the dispatch's stable counting sort), so the
+// workgroup counts, over all T*K ids, the ids below e and those equal to e and
+// keeps the slot of each match. Only buckets of fewer than self_min <=
+// kGemvMaxN + 1 positions take the GEMV path, one chunk each.
+__device__ bool self_bucket(const ExpertArgs& a, int y, Bucket& k, int* s_slot, int* s_cnt) {
+  const int E = a.E, TK = a.TK, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (y >= E) {
+    k = Bucket{y, TK + (y - E) * a.T, a.T, true, nullptr};
+    return a.T < a.self_min;
+  }
+  const uint64_t lower_lanes = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int below = 0, eq = 0;
+  for (int j0 = 0; j0 < TK; j0 += kGemvThreads) {
+    const int j = j0 + tid;
+    const int id = j < TK ? a.ids[j] : -1;  // -1: a slot dropped by adaptive top-p
+    const uint64_t m_eq = __ballot(id == y), m_lt = __ballot(id >= 0 && id < y);
+    if (lane == 0) {
+      s_cnt[w] = __popcll(m_eq);
+      s_cnt[kGW + w] = __popcll(m_lt);
+    }
+    __syncthreads();
+    int pre = 0, n_eq = 0, n_lt = 0;
+#pragma unroll
+    for (int v = 0; v < kGW; ++v) {
+      pre += v < w ? s_cnt[v] : 0;
+      n_eq += s_cnt[v];
+      n_lt += s_cnt[kGW + v];
+    }
+    if (id == y) {
+      const int r = eq + pre + __popcll(m_eq & lower_lanes);
+      if (r < kGemvMaxN) s_slot[r] = j;
+    }
+    eq += n_eq;
+    below += n_lt;
+    __syncthreads();  // s_cnt is reused; s_slot is complete after the last round
+  }
+  k = Bucket{y, below, eq, false, s_slot};
+  return eq > 0 && eq < a.self_min;
+}
+
 // PF: blocks in flight per wavefront (chosen by the host).
 // W: weight code width (4 or 8); GS: grouped weight scales (int4 only). Both
 // chosen by the host from the configuration.
 template <int PF, bool TAP, int W, bool GS>
 __global__ __launch_bounds__(kGemvThreads) void k_gateup_gemv(ExpertArgs a) {
   extern __shared__ char gemv_lds[];
+  __shared__ int s_self[kGemvMaxN + 2 * kGW];
   const int li = blockIdx.y, tile = blockIdx.x;
-  if (li >= *cptr(a.list_count)) return;
-  const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
-  const int c0 = cptr(a.list)[2 * li + 1];
+  Bucket k;
+  int c0 = 0;
+  if (a.self_min > 0) {
+    if (!self_bucket(a, li, k, s_self, s_self + kGemvMaxN)) return;
+  } else {
+    if (li >= *cptr(a.list_count)) return;
+    k = load_bucket(a, cptr(a.list)[2 * li]);
+    c0 = cptr(a.list)[2 * li + 1];
+  }
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
   const float* s13 = expert_s13(a.wv, k.ex, a.E, s13_count(a.H, a.I, GS ? a.gshift : -1));
   const int nn = min(kGemvMaxN, k.n - c0);
@@ -1024,11 +1079,13 @@ __global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* _
 // down tile with 2 measured 0.5% faster at prefill than with 4, 8 slower).
 constexpr int kMpfGateup = 4, kMpfDown = 2;
 
-// Blocks in flight per wavefront: about 4 KB of weights per wavefront when
-// many buckets stream at once (2 blocks of the two gate/up streams, 4 of the
-// single down stream), half that with a few buckets, where fewer queued
-// requests finish sooner. A depth is used only if it divides the step count.
-constexpr int kPfGateupMany = 2, kPfGateupFew = 1, kPfDownMany = 4, kPfDownFew = 2;
+// Steps in flight per wavefront (a step is 1 KB of weights per stream and
+// wavefront): 2 when many buckets stream at once, 1 for the two gate/up
+// streams with a few buckets, where fewer queued requests finish sooner. With
+// non-temporal weight loads the down GEMV measured 1.6% (decode, 32 tokens)
+// and 2.2% (MTP) faster at 2 than at 4; deeper gate/up rings were slower. A
+// depth is used only if it divides the step count.
+constexpr int kPfGateupMany = 2, kPfGateupFew = 1, kPfDownMany = 2, kPfDownFew = 2;
 
 static int gemv_pf(int nblocks, int want) {
   const int steps = (nblocks + 7) / 8;

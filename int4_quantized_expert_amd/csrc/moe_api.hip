@@ -123,7 +123,7 @@ int32_t hip_fail(hipError_t e) {
 // stream) pair needs them and are kept until the process ends.
 struct Helper {
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;  // after dispatch, chain done
+  hipEvent_t fork = nullptr, join = nullptr, disp = nullptr;  // fork point, side chain done, dispatch done
 };
 static std::mutex g_helper_mu;
 static std::map<std::pair<int, hipStream_t>, Helper> g_helpers;
@@ -140,6 +140,7 @@ static hipError_t get_helper(hipStream_t st, Helper* out) {
     if ((e = hipStreamCreateWithFlags(&h.side, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&h.fork, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&h.join, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&h.disp, hipEventDisableTiming)) != hipSuccess) return e;
     it = g_helpers.emplace(key, h).first;
   }
   *out = it->second;
@@ -259,17 +260,23 @@ int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, 
   return MOE_OK;
 }
 
+static DispatchArgs fwd_dispatch_args(const Fwd& f) {
+  return dispatch_args(f.ids, f.T, *f.cfg, f.gemm_min, f.tok_tile, f.L, f.wsb, f.counts, f.offsets, f.sorted,
+                       f.slotpos, f.unique, f.nunique);
+}
+
+hipError_t fwd_dispatch(Fwd& f, hipStream_t stream) { return launch_dispatch(fwd_dispatch_args(f), *f.cfg, stream); }
+
 hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
-                     hipStream_t stream, int call) {
+                     hipStream_t stream, int call, bool defer_dispatch) {
   const Layout& L = f.L;
   bool q8_done = false, dispatched = false;
-  const DispatchArgs da = dispatch_args(f.ids, f.T, *f.cfg, f.gemm_min, f.tok_tile, L, f.wsb, f.counts, f.offsets,
-                                        f.sorted, f.slotpos, f.unique, f.nunique);
+  const DispatchArgs da = fwd_dispatch_args(f);
   hipError_t e = launch_route(x, f.T, *f.cfg, router_w, router_bias, reinterpret_cast<double*>(f.wsb + L.part),
-                              f.ids, f.w, f.flags, f.qx, f.dx, tp ? tp->qx : nullptr, &q8_done, &da, &dispatched,
-                              call, prof_mark, stream);
+                              f.ids, f.w, f.flags, f.qx, f.dx, tp ? tp->qx : nullptr, &q8_done,
+                              defer_dispatch ? nullptr : &da, &dispatched, call, prof_mark, stream);
   prof_mark(call, 2, stream);
-  if (e == hipSuccess && !dispatched) e = launch_dispatch(da, *f.cfg, stream);
+  if (e == hipSuccess && !dispatched && !defer_dispatch) e = launch_dispatch(da, *f.cfg, stream);
   prof_mark(call, 3, stream);
   if (e == hipSuccess && !q8_done) e = launch_q8_0_x(x, f.T, f.cfg->hidden, f.qx, f.dx, tp ? tp->qx : nullptr, stream);
   if (e == hipSuccess && tp && tp->dx)
@@ -379,6 +386,11 @@ int32_t moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T, 
 
 namespace moe {
 
+// Top-K slots (T*K) up to which the gate/up GEMV finds its own buckets: one pass over the ids at the start of
+// each of its workgroups (decode with 32 tokens: 0.547 -> 0.543 ms; at 1,536 slots, three passes per
+// workgroup, MTP verify measured 1.008 -> 1.027 ms, so larger batches keep the dispatch in front).
+constexpr int kSelfDispatchMaxSlots = 512;
+
 // One resident-layer forward on `stream`. With use_helper the MFMA chain runs on
 // the helper stream beside the GEMV chain (fork/join); without it both chains
 // run one after the other on `stream` and nothing is created.
@@ -394,34 +406,49 @@ int32_t layer_forward_impl(const moe_config* cfg, const moe_layer_weights* wts, 
   Fwd f;
   if ((rc = fwd_setup(cfg, wv, T, ws, ws_bytes, taps, &f))) return rc;
   Helper hp;
-  const bool fork = use_helper && f.grid_tiles > 0;
+  // Small batches: the gate/up GEMV workgroups find their buckets from the top-K ids, so the GEMV chain starts
+  // right after top-K and the dispatch runs beside it (on the helper stream, ahead of the MFMA chain, or after
+  // the gate/up GEMV on the caller's stream); the down GEMV, the MFMA chain and the combine use its tables.
+  const bool self = f.T > 1 && f.gemm_min <= kGemvMaxN + 1 && f.L.TK <= kSelfDispatchMaxSlots;
+  const bool fork = use_helper && (f.grid_tiles > 0 || self);
   if (fork) {
     hipError_t he = get_helper(stream, &hp);
     if (he != hipSuccess) return hip_fail(he);
   }
   const int call = prof_begin();
   prof_mark(call, 0, stream);
-  hipError_t e = fwd_front(f, x, wts->router_w, wts->router_bias, taps, stream, call);
+  hipError_t e = fwd_front(f, x, wts->router_w, wts->router_bias, taps, stream, call, self);
   prof_mark(call, 4, stream);
   const int32_t* tiles = reinterpret_cast<const int32_t*>(f.wsb + f.L.tiles);
   const int32_t* n_tiles = &reinterpret_cast<Meta*>(f.wsb + f.L.meta)->n_tiles;
   if (e == hipSuccess && fork) {
     e = hipEventRecord(hp.fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(hp.side, hp.fork, 0);
-    if (e == hipSuccess) e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, hp.side);
+    if (e == hipSuccess && self) e = fwd_dispatch(f, hp.side);
+    if (e == hipSuccess && self) e = hipEventRecord(hp.disp, hp.side);
+    if (e == hipSuccess && f.grid_tiles > 0) e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, hp.side);
     prof_mark(call, 9, hp.side);  // the MFMA stages time the gate/up and down launches, not the gather
     if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 10, hp.side);
     if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
     prof_mark(call, 11, hp.side);
   }
+  ExpertArgs ga = f.a;  // gate/up GEMV arguments
+  int ggrid = f.grid_gemv;
+  if (self) {
+    ga.ids = f.ids;
+    ga.self_min = f.gemm_min;
+    ggrid = (int)(f.L.E + f.L.NS);
+  }
+  if (e == hipSuccess) e = launch_gemv_gateup(ga, ggrid, f.many, f.gemv_chunk, stream);
+  prof_mark(call, 5, stream);
+  if (e == hipSuccess && self && !use_helper) e = fwd_dispatch(f, stream);
   if (e == hipSuccess && !use_helper && f.grid_tiles > 0) {  // the MFMA chain on the caller's stream
     e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, stream);
     if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, stream);
     if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, stream);
   }
-  if (e == hipSuccess) e = launch_gemv_gateup(f.a, f.grid_gemv, f.many, f.gemv_chunk, stream);
-  prof_mark(call, 5, stream);
+  if (e == hipSuccess && self && use_helper) e = hipStreamWaitEvent(stream, hp.disp, 0);
   if (e == hipSuccess) e = launch_gemv_down(f.a, f.grid_gemv, f.many, f.gemv_chunk, stream);
   prof_mark(call, 6, stream);
   if (e == hipSuccess && fork) {

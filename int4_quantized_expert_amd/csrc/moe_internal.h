@@ -89,6 +89,8 @@ struct ExpertArgs {
   int32_t gshift;   // grouped weight scales: log2(group / 32); -1: one scale per row
   const int32_t* list;        // GEMV work list: (bucket, first token) pairs, chunks of up to kGemvMaxN tokens
   const int32_t* list_count;  // device count of list entries
+  const int32_t* ids;         // [T*K] top-K ids (read by the gate/up GEMV when self_min > 0)
+  int32_t self_min;           // > 0: gate/up GEMV workgroups find their buckets from ids (gemm_min, <= kGemvMaxN + 1)
   const int32_t* bk_e;
   const int32_t* bk_p0;
   const int32_t* bk_n;
@@ -137,9 +139,10 @@ struct Fwd {
 
 int fwd_setup(const moe_config* cfg, const WeightView& wv, int32_t T, void* ws, size_t ws_bytes, const moe_taps* tp,
               Fwd* f);
-// router + top-K + dispatch + Q8_0(x)
+// router + top-K + Q8_0(x), and the dispatch unless defer_dispatch (then fwd_dispatch launches it)
 hipError_t fwd_front(Fwd& f, const float* x, const float* router_w, const float* router_bias, const moe_taps* tp,
-                     hipStream_t stream, int call);
+                     hipStream_t stream, int call, bool defer_dispatch = false);
+hipError_t fwd_dispatch(Fwd& f, hipStream_t stream);
 hipError_t fwd_combine(Fwd& f, float* y, hipStream_t stream);
 // moe_layer_forward with or without the helper stream (see moe_api.hip)
 int32_t layer_forward_impl(const moe_config* cfg, const moe_layer_weights* wts, const float* x, int32_t T, float* y,
