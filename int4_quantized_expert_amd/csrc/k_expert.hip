@@ -403,12 +403,14 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
         prep_wblk(bg[kk], pg);
         prep_wblk(bu[kk], pu);
         const float cg = GS ? sgq[kk] : 0.0f, cu = GS ? suq[kk] : 0.0f;
-        const int bn = min(8 * min(j + PF, nsteps - 1) + bs, nb - 1);  // past the end: a repeat (cache hit)
-        load_wblk<W>(bg[kk], gb + (size_t)bn * kTileBlock<W>);
-        load_wblk<W>(bu[kk], ub + (size_t)bn * kTileBlock<W>);
-        if constexpr (GS) {
-          sgq[kk] = gsc[(size_t)(bn >> gsh) * 64];
-          suq[kk] = usc[(size_t)(bn >> gsh) * 64];
+        if (j + PF < nsteps) {  // refill with step j + PF; the last PF steps load nothing more
+          const int bn = min(8 * (j + PF) + bs, nb - 1);
+          load_wblk<W>(bg[kk], gb + (size_t)bn * kTileBlock<W>);
+          load_wblk<W>(bu[kk], ub + (size_t)bn * kTileBlock<W>);
+          if constexpr (GS) {
+            sgq[kk] = gsc[(size_t)(bn >> gsh) * 64];
+            suq[kk] = usc[(size_t)(bn >> gsh) * 64];
+          }
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -497,9 +499,11 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
         WPrep<W> pw;
         prep_wblk(bw[kk], pw);
         const float co = GS ? soq[kk] : 0.0f;
-        const int bn = min(8 * min(j + PF, nsteps - 1) + bs, nbi - 1);
-        load_wblk<W>(bw[kk], wb + (size_t)bn * kTileBlock<W>);
-        if constexpr (GS) soq[kk] = osc[(size_t)(bn >> gsh) * 64];
+        if (j + PF < nsteps) {  // as in the gate/up GEMV
+          const int bn = min(8 * (j + PF) + bs, nbi - 1);
+          load_wblk<W>(bw[kk], wb + (size_t)bn * kTileBlock<W>);
+          if constexpr (GS) soq[kk] = osc[(size_t)(bn >> gsh) * 64];
+        }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
           const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)bq * 32);
