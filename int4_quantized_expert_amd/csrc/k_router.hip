@@ -281,6 +281,16 @@ __device__ void dispatch_one_token(const DispatchArgs& a, const int* sel, const 
   }
 }
 
+// Candidate key of the top-K ranking: the order-preserving bits of score c
+// (larger c, larger key; -0 taken as +0 so that equal scores tie) above the
+// complement of the candidate's position, which breaks ties toward the lower
+// position.
+__device__ __forceinline__ uint64_t cand_key(float c, int pos) {
+  uint32_t u = __float_as_uint(__fadd_rn(c, 0.0f));
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
+}
+
 // Top-k, one 256-lane workgroup per token. Every lane adds the 16 partial sums
 // of its experts in ascending order (all loads issued first) and rounds once
 // to fp32: the logit z. s = sigmoid(z) in fp64 rounded to fp32, c = s +
@@ -291,7 +301,8 @@ __device__ void dispatch_one_token(const DispatchArgs& a, const int* sel, const 
 // routed_scaling_factor. Group top-2 sums are shuffle reductions over aligned
 // lane groups (a serial scan when the group size is not a power of two up to
 // 64); groups are ranked against their LDS copies; each expert of the kept
-// groups counts, over a compacted copy of their scores, the ones that beat it.
+// groups counts, over compacted 64-bit keys of their scores, the ones that
+// beat it.
 // Near-tie flags: kept/dropped group boundary,
 // chosen/next expert boundary, adjacent chosen experts (differences < 1e-6).
 // Without top-p, wavefront 0 finishes from registers (slot k in lane k): the
@@ -372,42 +383,39 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
     s_grank[rk] = v;
   }
   __syncthreads();
-  // experts of the kept groups, best first by (c desc, index asc): their c are
-  // compacted in expert order (kept groups ascending), then each candidate
-  // counts the entries that beat it, a higher c or an equal c earlier in the
-  // array, with 16-byte broadcast reads and no branches. Rank k is slot k;
-  // rank K is the best expert left out.
+  // experts of the kept groups, best first by (c desc, index asc): each gets a
+  // 64-bit key, the order-preserving bits of c above the complement of its
+  // position in the compacted candidate array (kept groups ascending, experts
+  // ascending within a group), so a larger key is a higher c or an equal c at a
+  // lower expert index. Each candidate counts the keys above its own with one
+  // 64-bit compare per entry. Rank k is slot k; rank K is the best expert left
+  // out.
   __shared__ int s_kpos[kMaxGroups];  // position of a kept group among the kept groups
-  __shared__ __align__(16) float s_cand[kMaxExperts];
+  __shared__ __align__(16) uint64_t s_key[kMaxExperts];
   if (wave == 0) {
     const bool kg = lane < G && s_kept[lane];
     const uint64_t km = __ballot(kg);
     if (lane < G) s_kpos[lane] = __popcll(km & ((1ull << lane) - 1));
   }
   __syncthreads();
-  const int nc = KG * n;  // candidates
+  const int nc = KG * n, ncp = (nc + 1) & ~1;  // candidates, padded to whole pairs
   for (int e = tid; e < E; e += 256) {
     const int g = e / n;
-    if (s_kept[g]) s_cand[s_kpos[g] * n + (e - g * n)] = s_c[e];
+    if (s_kept[g]) {
+      const int pos = s_kpos[g] * n + (e - g * n);
+      s_key[pos] = cand_key(s_c[e], pos);
+    }
   }
-  for (int j = nc + tid; j < ((nc + 3) & ~3); j += 256) s_cand[j] = -INFINITY;  // pad to whole float4
+  for (int j = nc + tid; j < ncp; j += 256) s_key[j] = 0;  // below every real key
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
     const int g = e / n;
     if (!s_kept[g]) continue;
     const float v = s_c[e];
-    const int me = s_kpos[g] * n + (e - g * n);
+    const uint64_t mine = cand_key(v, s_kpos[g] * n + (e - g * n));
     int rk = 0;
-    const float4* c4 = reinterpret_cast<const float4*>(s_cand);
 #pragma unroll 8
-    for (int j4 = 0; j4 < (nc + 3) >> 2; ++j4) {
-      const float4 o = c4[j4];
-      const int j = 4 * j4;
-      rk += (o.x > v) | ((o.x == v) & (j + 0 < me));
-      rk += (o.y > v) | ((o.y == v) & (j + 1 < me));
-      rk += (o.z > v) | ((o.z == v) & (j + 2 < me));
-      rk += (o.w > v) | ((o.w == v) & (j + 3 < me));
-    }
+    for (int j = 0; j < ncp; j += 2) rk += (int)(s_key[j] > mine) + (int)(s_key[j + 1] > mine);
     if (rk < K) {
       s_sel[rk] = e;
       s_selc[rk] = v;
