@@ -317,3 +317,49 @@ def test_layer_rejects_bad_args(tiny_gpu):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_layer_forward(cfg, tiny_gpu.weights(), x, y, ws, T=0)
     assert ei.value.rc == moe.MOE_E_SHAPE
+
+
+SPLIT = synth.Shape(1024, 16, 4, 2, 4, 1024, 1, 2.5, bias_kind="uniform")
+
+
+@pytest.mark.parametrize("weight_bits", [4, 8])
+@pytest.mark.parametrize("slot", [1, 4])
+def test_layer_one_token_multi_step(weight_bits, slot):
+    """One token at a size whose GEMVs walk several K steps (4 steps of 8 blocks for gate/up and for down, where the
+    tiny shape has one): every tap bit-exact against the oracle with int4 and int8 weights, block sums of a routed
+    slot (1) and of the shared expert (4) included, so a block lost or reordered between steps fails."""
+    sh = SPLIT
+    H, I, K, E, NS = sh.hidden, sh.inter, sh.top_k, sh.n_experts, sh.n_shared
+    layer = GpuLayer(sh, seed=21, weight_bits=weight_bits)
+    ref = oracle_layer(sh, seed=21, weight_bits=weight_bits)
+    for seed in (0, 1):
+        x = synth.hidden_states(sh, 1, seed=300 + seed)
+        cfg = config_of(sh, 0, weight_bits)
+        R = K + NS
+        bufs = dict(topk_ids=torch.empty((1, K), dtype=torch.int32, device=DEV),
+                    topk_w=torch.empty((1, K), dtype=torch.float32, device=DEV),
+                    qx=torch.empty((1, H), dtype=torch.int8, device=DEV),
+                    h=torch.empty((R, I), dtype=torch.float32, device=DEV),
+                    qh=torch.empty((R, I), dtype=torch.int8, device=DEV),
+                    e_out=torch.empty((R, H), dtype=torch.float32, device=DEV),
+                    gateup_sums=torch.empty((2 * I, H // 32), dtype=torch.int32, device=DEV),
+                    down_sums=torch.empty((H, I // 32), dtype=torch.int32, device=DEV))
+        y = torch.empty((1, H), dtype=torch.float32, device=DEV)
+        moe.moe_layer_forward(cfg, layer.weights(), _t(x), y, _ws(cfg, 1), moe.taps(slot, **bufs))
+        g = {k: _np(v) for k, v in bufs.items()}
+        yr, tr = O.layer_forward(O.Cfg.of(sh), x, ref)
+        assert not (tr["flags"] & (O.TIE_EXPERT | O.TIE_GROUP)).any()
+        assert np.array_equal(g["topk_ids"], tr["ids"])
+        assert np.array_equal(g["qx"], tr["qx"])
+        for k in ("h", "e_out"):
+            assert np.array_equal(g[k].view(np.uint32), tr[k].view(np.uint32)), (seed, k)
+        assert np.array_equal(g["qh"], tr["qh"])
+        assert np.array_equal(_np(y).view(np.uint32), yr.view(np.uint32)), seed
+        if slot < K:
+            q13, q2 = ref.q13[tr["ids"][0, slot]], ref.q2[tr["ids"][0, slot]]
+        else:
+            q13, q2 = ref.sq13[slot - K], ref.sq2[slot - K]
+        S13 = (q13.astype(np.int64) * tr["qx"][0].astype(np.int64)[None]).reshape(2 * I, -1, 32).sum(2)
+        S2 = (q2.astype(np.int64) * tr["qh"][slot].astype(np.int64)[None]).reshape(H, -1, 32).sum(2)
+        assert np.array_equal(g["gateup_sums"], S13)
+        assert np.array_equal(g["down_sums"], S2)
