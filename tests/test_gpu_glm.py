@@ -255,3 +255,16 @@ def test_glm_token_alone_equals_in_batch(glm):
     for t in (0, 77, 191):
         ya = _forward(glm, x[t:t + 1])
         assert np.array_equal(ya[0].view(np.uint32), yb[t].view(np.uint32)), t
+
+
+@pytest.mark.parametrize("T", [64, 65])
+def test_glm_self_dispatch_limit(glm, T):
+    """T = 64 is the largest batch (512 slots) whose gate/up GEMV workgroups find their buckets from the top-K ids
+    while the dispatch runs beside them; T = 65 keeps the dispatch in front. Sampled tokens against the oracle
+    (dispatch arrays and qx in full), and the GEMV-only and MFMA-only paths give the same bits."""
+    x = synth.hidden_states(SH, T, seed=0, step=8 + T)
+    _check(glm, x, np.linspace(0, T - 1, 16).round().astype(int), tag=f"self-dispatch limit T={T}")
+    y0 = _forward(glm, x)
+    for gm in (1000, 1):
+        y1 = _forward(glm, x, gemm_min=gm)
+        assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32)), gm
