@@ -42,9 +42,10 @@
  *  - The forward path allocates no device memory: the caller passes a
  *    workspace of at least moe_workspace_bytes() bytes (device, 256-byte
  *    aligned). Buckets large enough for the int8-MFMA path run on a helper
- *    stream that forks from and joins back into the caller's stream; the
- *    helper stream and two events are created on first use per (device,
- *    stream) and kept until the process ends.
+ *    stream that forks from and joins back into the caller's stream (for
+ *    batches of up to 512 top-K slots the dispatch runs there too, beside
+ *    the gate/up GEMV); the helper stream and three events are created on
+ *    first use per (device, stream) and kept until the process ends.
  *  - Stateless calls are re-entrant on distinct streams; a cache object is not
  *    thread-safe.
  *  - x, y, router_w and the int4 / int8 weight code arrays are read or written
@@ -336,7 +337,9 @@ void moe_expert_cache_destroy(moe_expert_cache* cache);
  * [n_calls][MOE_N_STAGES] (host), in the order router-logits, top-k, dispatch,
  * q8-x, GEMV gate-up, GEMV down (caller's stream), MFMA gate-up, MFMA down
  * (helper stream, overlapping the GEMV stages; 0 when no bucket reaches the
- * MFMA threshold), combine. stage_mask selects the stages to time (bit s =
+ * MFMA threshold), combine. Dispatch reads ~0 where it does not run on the
+ * caller's stream in front (one token: inside top-k; up to 512 slots: on the
+ * helper stream, and the GEMV down stage then includes the wait for it). stage_mask selects the stages to time (bit s =
  * stage s; 0 selects all): only the events those stages need are recorded, so
  * a narrow mask keeps the timed stream close to an unprofiled one. Stages left
  * out read as NaN. Process-wide, not thread-safe; for benchmarks only.
