@@ -11,8 +11,8 @@
 // Grids are sized for the worst case and workgroups beyond the device-side
 // counts exit at once, so the bucket structure never travels back to the host.
 //
-// GEMV (few tokens, HBM-bound): a 512-lane workgroup streams one 64-row tile;
-// each lane computes exact block sums of one (row, block) per step, and the
+// GEMV (few tokens, HBM-bound): a 512-lane workgroup streams the 64-row tiles
+// of gate and up, or two 64-row tiles of down, side by side; each lane computes exact block sums of one (row, block) per step, and the
 // sums are turned around in LDS so that one lane runs the whole fp32 chain of
 // a (row, token) (details at the GEMV section).
 //
@@ -215,13 +215,17 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // ------------------------------------------------------------------ GEMV paths
-// Few tokens per expert: HBM-bound. A 512-lane workgroup owns one 64-row tile
-// and streams it as one contiguous run: at step j its eight wavefronts read
-// blocks 8j .. 8j+7, and wavefront w takes rows 8w .. 8w+7 of each, so lane l
-// loads 16 bytes of row 8w + l%8, block 8j + l/8 (one full 128-byte line per
-// group of 8 lanes, 1 KB per instruction, 8 KB per workgroup and step).
-// Keeping few requests in flight (PF steps per wavefront) and adjacent is what
-// lets many buckets stream near the HBM ceiling.
+// Few tokens per expert: HBM-bound. A 512-lane workgroup owns two 64-row tiles
+// (gate/up: the gate and the up tile of the same rows; down: two consecutive
+// output tiles, or one when H/64 is odd) and streams each as one contiguous
+// run: at step j its eight wavefronts read blocks 8j .. 8j+7, and wavefront w
+// takes rows 8w .. 8w+7 of each, so lane l loads 16 bytes of row 8w + l%8,
+// block 8j + l/8 of every tile (one full 128-byte line per group of 8 lanes,
+// 1 KB per instruction, 8 KB per tile, workgroup and step). Keeping few
+// requests in flight (PF steps per wavefront) and adjacent is what lets many
+// buckets stream near the HBM ceiling. Down tiles paired this way measured
+// 1-2% faster per step than one tile per workgroup (half the workgroups, twice
+// the bytes per step).
 //
 // Each lane computes the exact int32 block sums of its (row, block) for every
 // token of the chunk. The fp32 dot is one ascending chain per (projection,
@@ -241,15 +245,16 @@ constexpr int kGW = 8;  // wavefronts per tile, 8 rows each
 constexpr int kGemvThreads = 64 * kGW;
 
 // Dynamic LDS of a GEMV workgroup for chunks of NC tokens over K inputs with
-// P projections (2 gate/up, 1 down): staged codes [NC][K], staged scales
+// P weight streams per loading lane (gate/up: the gate and the up row; down:
+// one row of each of its 1 or 2 tiles): staged codes [NC][K], staged scales
 // [NC][nbp] (rows padded to 8 blocks), per wavefront the turned-around block
 // sums [8*P*NC chains][8 blocks] and (grouped scales) [P][8 rows][8 blocks]
-// weight scales, and for gate/up the chain results [NC][2][64] that pair gate
-// with up.
+// weight scales, and with HX (gate/up) the chain results [NC][2][64] that pair
+// gate with up.
 struct GemvLdsPlan {
   size_t xs, xd, tb, sg, hx, total;
 };
-__host__ __device__ __forceinline__ GemvLdsPlan gemv_lds_plan(int NC, int K, int P, bool GS) {
+__host__ __device__ __forceinline__ GemvLdsPlan gemv_lds_plan(int NC, int K, int P, bool GS, bool HX) {
   const int nb = K / 32, nbp = (nb + 7) & ~7;
   GemvLdsPlan L;
   L.xs = 0;
@@ -257,15 +262,15 @@ __host__ __device__ __forceinline__ GemvLdsPlan gemv_lds_plan(int NC, int K, int
   L.tb = L.xd + (size_t)NC * nbp * 4;
   L.sg = L.tb + (size_t)kGW * (8 * P * NC) * 8 * 4;
   L.hx = L.sg + (GS ? (size_t)kGW * P * 64 * 4 : 0);
-  L.total = L.hx + (P == 2 ? (size_t)NC * 2 * 64 * 4 : 0);
+  L.total = L.hx + (HX ? (size_t)NC * 2 * 64 * 4 : 0);
   return L;
 }
 
 // Bytes of dynamic LDS for a GEMV launch whose chunks hold at most n tokens
 // (rounded up to the instantiated 1, 2 or 4).
-static inline size_t gemv_lds_bytes(int n, int K, int pairs, bool gs) {
+static inline size_t gemv_lds_bytes(int n, int K, int streams, bool gs, bool hx) {
   const int nc = n <= 1 ? 1 : (n <= 2 ? 2 : kGemvMaxN);
-  return gemv_lds_plan(nc, K, pairs, gs).total;
+  return gemv_lds_plan(nc, K, streams, gs, hx).total;
 }
 
 // Staging of the chunk's N (padded) tokens: codes [N][K] and scales [N][nbp].
@@ -348,7 +353,7 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
   // the wavefront index is uniform: say so, so that its branches stay scalar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int rl = lane & 7, bs = lane >> 3, row = w * 8 + rl;  // loading lane: row of the tile, block of the step
-  const GemvLdsPlan LP = gemv_lds_plan(N, H, 2, GS);
+  const GemvLdsPlan LP = gemv_lds_plan(N, H, 2, GS, true);
   int8_t* xs = reinterpret_cast<int8_t*>(lds + LP.xs);
   float* xd = reinterpret_cast<float*>(lds + LP.xd);
   float* tb = reinterpret_cast<float*>(lds + LP.tb) + (size_t)w * (16 * N) * 8;
@@ -447,17 +452,20 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
                             hx[(w * 2 + 1) * 64 + lane]);
 }
 
-template <int N, int PF, bool TAP, int W, bool GS>
+// TP (1 or 2): 64-row tiles per workgroup. With two, every loading lane streams
+// the same (row, block) of both tiles, as the gate/up GEMV streams its gate and
+// up rows, and the chains of the second tile follow those of the first.
+template <int N, int PF, bool TAP, int W, bool GS, int TP>
 __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket& k, int c0, int nn,
-                                              const uint8_t* w2, const float* s2, int tile, char* lds) {
+                                              const uint8_t* w2, const float* s2, int tile2, char* lds) {
   const int H = a.H, I = a.I, nbi = I / 32, nbp = (nbi + 7) & ~7;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int rl = lane & 7, bs = lane >> 3, row = w * 8 + rl;
-  const GemvLdsPlan LP = gemv_lds_plan(N, I, 1, GS);
+  const GemvLdsPlan LP = gemv_lds_plan(N, I, TP, GS, false);
   int8_t* hs = reinterpret_cast<int8_t*>(lds + LP.xs);
   float* hd = reinterpret_cast<float*>(lds + LP.xd);
-  float* tb = reinterpret_cast<float*>(lds + LP.tb) + (size_t)w * (8 * N) * 8;
-  float* sgw = reinterpret_cast<float*>(lds + LP.sg) + (size_t)w * 64;
+  float* tb = reinterpret_cast<float*>(lds + LP.tb) + (size_t)w * (8 * TP * N) * 8;
+  float* sgw = reinterpret_cast<float*>(lds + LP.sg) + (size_t)w * TP * 64;
   Staged<N> st;
   {
     const int8_t* src[N];
@@ -471,16 +479,24 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
     stage_load<N>(src, dsrc, I, st);
   }
   const int nsteps = (nbi + 7) >> 3;
-  const uint8_t* wb = w2 + tbw_off<W>(tile, 0, nbi) + (size_t)row * (4 * W);
   const int gsh = GS ? a.gshift : 0, ngs = GS ? nbi >> gsh : 0;
-  const float* osc = s2 + (size_t)tile * ngs * 64 + row;  // group scales of the output row
-  WBlk<W> bw[PF];
-  float soq[PF];
+  const uint8_t* wb[TP];
+  const float* osc[TP];  // group scales of the output row
+#pragma unroll
+  for (int q = 0; q < TP; ++q) {
+    wb[q] = w2 + tbw_off<W>(TP * tile2 + q, 0, nbi) + (size_t)row * (4 * W);
+    osc[q] = s2 + (size_t)(TP * tile2 + q) * ngs * 64 + row;
+  }
+  WBlk<W> bw[TP][PF];
+  float soq[TP][PF];
 #pragma unroll
   for (int kk = 0; kk < PF; ++kk) {
     const int b = min(8 * min(kk, nsteps - 1) + bs, nbi - 1);
-    load_wblk<W>(bw[kk], wb + (size_t)b * kTileBlock<W>);
-    if constexpr (GS) soq[kk] = osc[(size_t)(b >> gsh) * 64];
+#pragma unroll
+    for (int q = 0; q < TP; ++q) {
+      load_wblk<W>(bw[q][kk], wb[q] + (size_t)b * kTileBlock<W>);
+      if constexpr (GS) soq[q][kk] = osc[q][(size_t)(b >> gsh) * 64];
+    }
   }
   stage_store<N>(st, I, hs, hd);
   int tap_i = -1;
@@ -496,31 +512,48 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
       if (j < nsteps) {
         const int blk = 8 * j + bs;
         const int bq = min(blk, nbi - 1);
-        WPrep<W> pw;
-        prep_wblk(bw[kk], pw);
-        const float co = GS ? soq[kk] : 0.0f;
+        WPrep<W> pw[TP];
+        float co[TP];
+#pragma unroll
+        for (int q = 0; q < TP; ++q) {
+          prep_wblk(bw[q][kk], pw[q]);
+          co[q] = GS ? soq[q][kk] : 0.0f;
+        }
         if (j + PF < nsteps) {  // as in the gate/up GEMV
           const int bn = min(8 * (j + PF) + bs, nbi - 1);
-          load_wblk<W>(bw[kk], wb + (size_t)bn * kTileBlock<W>);
-          if constexpr (GS) soq[kk] = osc[(size_t)(bn >> gsh) * 64];
+#pragma unroll
+          for (int q = 0; q < TP; ++q) {
+            load_wblk<W>(bw[q][kk], wb[q] + (size_t)bn * kTileBlock<W>);
+            if constexpr (GS) soq[q][kk] = osc[q][(size_t)(bn >> gsh) * 64];
+          }
         }
 #pragma unroll
         for (int i = 0; i < N; ++i) {
           const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)bq * 32);
-          const int S = wdot(pw, hb4[0], hb4[1]);
-          tb[((i << 3) | rl) * 8 + bs] = (float)S;
-          if (TAP && i == tap_i && blk < nbi) a.t_dn_sums[(size_t)(tile * 64 + row) * nbi + blk] = S;
+          const v4i ha = hb4[0], hb = hb4[1];
+#pragma unroll
+          for (int q = 0; q < TP; ++q) {
+            const int S = wdot(pw[q], ha, hb);
+            tb[(((q * N + i) << 3) | rl) * 8 + bs] = (float)S;
+            if (TAP && i == tap_i && blk < nbi)
+              a.t_dn_sums[(size_t)((TP * tile2 + q) * 64 + row) * nbi + blk] = S;
+          }
         }
-        if constexpr (GS) sgw[rl * 8 + bs] = co;
+        if constexpr (GS) {
+#pragma unroll
+          for (int q = 0; q < TP; ++q) sgw[(q * 8 + rl) * 8 + bs] = co[q];
+        }
         wave_sync();
-        chain_step<N, 1, GS>(acc, tb, hd, sgw, lane, nbp, j, min(8, nbi - 8 * j));
+        chain_step<N, TP, GS>(acc, tb, hd, sgw, lane, nbp, j, min(8, nbi - 8 * j));
         wave_sync();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  if (lane < 8 * N) {
-    const int t = lane >> 3, o = tile * 64 + w * 8 + (lane & 7);
+  if (lane < 8 * TP * N) {
+    constexpr int LN = N == 1 ? 0 : (N == 2 ? 1 : 2);
+    const int t = (lane >> 3) & (N - 1), q = lane >> (3 + LN);
+    const int o = (TP * tile2 + q) * 64 + w * 8 + (lane & 7);
     if (t < nn) {
       const float e = GS ? acc : __fmul_rn(s2[o], acc);
       const int p = k.p0 + c0 + t;
@@ -1016,7 +1049,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gateup_gemv(ExpertArgs a) {
   else gemv_gateup_run<kGemvMaxN, PF, TAP, W, GS>(a, k, c0, nn, w13, s13, tile, gemv_lds);
 }
 
-template <int PF, bool TAP, int W, bool GS>
+template <int PF, bool TAP, int W, bool GS, int TP>
 __global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
   extern __shared__ char gemv_lds[];
   const int li = blockIdx.y, tile = blockIdx.x;
@@ -1026,9 +1059,9 @@ __global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
   const float* s2 = expert_s2(a.wv, k.ex, a.E, s2_count(a.H, a.I, GS ? a.gshift : -1));
   const int nn = min(kGemvMaxN, k.n - c0);
-  if (nn == 1) gemv_down_run<1, PF, TAP, W, GS>(a, k, c0, nn, w2, s2, tile, gemv_lds);
-  else if (nn == 2) gemv_down_run<2, PF, TAP, W, GS>(a, k, c0, nn, w2, s2, tile, gemv_lds);
-  else gemv_down_run<kGemvMaxN, PF, TAP, W, GS>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  if (nn == 1) gemv_down_run<1, PF, TAP, W, GS, TP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else if (nn == 2) gemv_down_run<2, PF, TAP, W, GS, TP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
+  else gemv_down_run<kGemvMaxN, PF, TAP, W, GS, TP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
 }
 
 template <int NTT, int MPF, bool TAP, int W, bool GS>
@@ -1113,25 +1146,36 @@ static void gateup_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStrea
   }
 }
 
-template <int PF>
+template <int PF, int TP>
 static void down_gemv_launch(const ExpertArgs& a, dim3 g, size_t lds, hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
   if (a.wbits == 8) {
-    if (tap) k_down_gemv<PF, true, 8, false><<<g, kGemvThreads, lds, st>>>(a);
-    else k_down_gemv<PF, false, 8, false><<<g, kGemvThreads, lds, st>>>(a);
+    if (tap) k_down_gemv<PF, true, 8, false, TP><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 8, false, TP><<<g, kGemvThreads, lds, st>>>(a);
   } else if (a.gshift >= 0) {
-    if (tap) k_down_gemv<PF, true, 4, true><<<g, kGemvThreads, lds, st>>>(a);
-    else k_down_gemv<PF, false, 4, true><<<g, kGemvThreads, lds, st>>>(a);
+    if (tap) k_down_gemv<PF, true, 4, true, TP><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 4, true, TP><<<g, kGemvThreads, lds, st>>>(a);
   } else {
-    if (tap) k_down_gemv<PF, true, 4, false><<<g, kGemvThreads, lds, st>>>(a);
-    else k_down_gemv<PF, false, 4, false><<<g, kGemvThreads, lds, st>>>(a);
+    if (tap) k_down_gemv<PF, true, 4, false, TP><<<g, kGemvThreads, lds, st>>>(a);
+    else k_down_gemv<PF, false, 4, false, TP><<<g, kGemvThreads, lds, st>>>(a);
+  }
+}
+
+template <int TP>
+static void down_gemv_pf(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
+  const dim3 g(a.H / (64 * TP), grid);
+  const size_t lds = gemv_lds_bytes(max_chunk, a.I, TP, a.gshift >= 0, false);
+  switch (gemv_pf(a.I / 32, many ? kPfDownMany : kPfDownFew)) {
+    case 4: down_gemv_launch<4, TP>(a, g, lds, st); break;
+    case 2: down_gemv_launch<2, TP>(a, g, lds, st); break;
+    default: down_gemv_launch<1, TP>(a, g, lds, st); break;
   }
 }
 
 hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   dim3 g(a.I / 64, grid);
-  const size_t lds = gemv_lds_bytes(max_chunk, a.H, 2, a.gshift >= 0);
+  const size_t lds = gemv_lds_bytes(max_chunk, a.H, 2, a.gshift >= 0, true);
   switch (gemv_pf(a.H / 32, many ? kPfGateupMany : kPfGateupFew)) {
     case 4: gateup_gemv_launch<4>(a, g, lds, st); break;
     case 2: gateup_gemv_launch<2>(a, g, lds, st); break;
@@ -1142,13 +1186,8 @@ hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_
 
 hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  dim3 g(a.H / 64, grid);
-  const size_t lds = gemv_lds_bytes(max_chunk, a.I, 1, a.gshift >= 0);
-  switch (gemv_pf(a.I / 32, many ? kPfDownMany : kPfDownFew)) {
-    case 4: down_gemv_launch<4>(a, g, lds, st); break;
-    case 2: down_gemv_launch<2>(a, g, lds, st); break;
-    default: down_gemv_launch<1>(a, g, lds, st); break;
-  }
+  if ((a.H / 64) % 2 == 0) down_gemv_pf<2>(a, grid, many, max_chunk, st);
+  else down_gemv_pf<1>(a, grid, many, max_chunk, st);
   return hipGetLastError();
 }
 
