@@ -1064,19 +1064,26 @@ __global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
   else gemv_down_run<kGemvMaxN, PF, TAP, W, GS, TP>(a, k, c0, nn, w2, s2, tile, gemv_lds);
 }
 
-template <int NTT, int MPF, bool TAP, int W, bool GS>
-__global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
+// MW: wavefronts per workgroup, each with its own tile (consecutive row blocks of
+// the same token tile); the workgroup has no barrier. Grids are sized for the
+// worst case, so for small batches most of their workgroups exit at once:
+// grouping four tiles per workgroup launches a quarter as many of them beside
+// the GEMV chain.
+template <int NTT, int MPF, bool TAP, int W, bool GS, int MW>
+__global__ __launch_bounds__(64 * MW) void k_gateup_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
                                                     const int32_t* __restrict__ n_tiles) {
-  const int y = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
+  const int wv = MW > 1 ? (int)threadIdx.x >> 6 : 0, lane = MW > 1 ? (int)threadIdx.x & 63 : (int)threadIdx.x;
+  const int y = blockIdx.y, tile = MW > 1 ? (int)blockIdx.x * MW + wv : (int)blockIdx.x;
   if (y >= *cptr(n_tiles)) return;
+  if (MW > 1 && tile >= a.I / 32) return;
   const Bucket k = load_bucket(a, cptr(tiles)[2 * y]);
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
   const float* s13 = expert_s13(a.wv, k.ex, a.E, s13_count(a.H, a.I, GS ? a.gshift : -1));
   float* sc = nullptr;  // two 64-float slots for the group scales (GS only: no LDS otherwise)
   if constexpr (GS) {
-    __shared__ float scl[2 * 64];
-    sc = scl;
+    __shared__ float scl[MW][2 * 64];
+    sc = scl[wv];
   }
   // a bucket's last tile with one 32-token half runs as a 32-token tile (the empty half skipped). With 32-token
   // tiles, the only tile of a bucket of up to 32 tokens streams its weights non-temporally (the 64-token kernels,
@@ -1089,19 +1096,21 @@ __global__ __launch_bounds__(64) void k_gateup_mfma(ExpertArgs a, const int32_t*
   }
 }
 
-template <int NTT, int MPF, bool TAP, int W, bool GS>
-__global__ __launch_bounds__(64) void k_down_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
+template <int NTT, int MPF, bool TAP, int W, bool GS, int MW>
+__global__ __launch_bounds__(64 * MW) void k_down_mfma(ExpertArgs a, const int32_t* __restrict__ tiles,
                                                   const int32_t* __restrict__ n_tiles) {
-  const int y = blockIdx.y, tile = blockIdx.x, lane = threadIdx.x;
+  const int wv = MW > 1 ? (int)threadIdx.x >> 6 : 0, lane = MW > 1 ? (int)threadIdx.x & 63 : (int)threadIdx.x;
+  const int y = blockIdx.y, tile = MW > 1 ? (int)blockIdx.x * MW + wv : (int)blockIdx.x;
   if (y >= *cptr(n_tiles)) return;
+  if (MW > 1 && tile >= a.H / 64) return;
   const Bucket k = load_bucket(a, cptr(tiles)[2 * y]);
   const int t0 = cptr(tiles)[2 * y + 1];
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
   const float* s2 = expert_s2(a.wv, k.ex, a.E, s2_count(a.H, a.I, GS ? a.gshift : -1));
   float* sc = nullptr;
   if constexpr (GS) {
-    __shared__ float scl[2 * 64];
-    sc = scl;
+    __shared__ float scl[MW][2 * 64];
+    sc = scl[wv];
   }
   if (NTT == 1 || k.n - t0 <= 32) {  // as in the gate/up kernel
     if (NTT == 1 && k.n <= 32) mfma_down_tile<1, MPF, TAP, W, GS, true>(a, k, t0, w2, s2, tile, lane, sc);
@@ -1191,32 +1200,51 @@ hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_ch
   return hipGetLastError();
 }
 
-template <int NTT, int W, bool GS>
-static void mfma_gateup_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
+template <int NTT, int W, bool GS, int MW>
+static void mfma_gateup_launch(const ExpertArgs& a, int grid, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
   constexpr int MPF = kMpfGateup;
+  const dim3 g((a.I / 32 + MW - 1) / MW, grid);
   if ((a.H / 32) % MPF == 0) {
-    if (tap) k_gateup_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_gateup_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_gateup_mfma<NTT, MPF, true, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
+    else k_gateup_mfma<NTT, MPF, false, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
   } else {
-    if (tap) k_gateup_mfma<NTT, 2, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_gateup_mfma<NTT, 2, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_gateup_mfma<NTT, 2, true, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
+    else k_gateup_mfma<NTT, 2, false, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
   }
 }
 
-template <int NTT, int W, bool GS>
-static void mfma_down_launch(const ExpertArgs& a, dim3 g, const int32_t* tiles, const int32_t* n_tiles,
+template <int NTT, int W, bool GS, int MW>
+static void mfma_down_launch(const ExpertArgs& a, int grid, const int32_t* tiles, const int32_t* n_tiles,
                              hipStream_t st) {
   const bool tap = a.t_dn_sums != nullptr;
   constexpr int MPF = kMpfDown;
+  const dim3 g((a.H / 64 + MW - 1) / MW, grid);  // 64-row tiles
   if ((a.I / 32) % MPF == 0) {
-    if (tap) k_down_mfma<NTT, MPF, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_down_mfma<NTT, MPF, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_down_mfma<NTT, MPF, true, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
+    else k_down_mfma<NTT, MPF, false, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
   } else {
-    if (tap) k_down_mfma<NTT, 2, true, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
-    else k_down_mfma<NTT, 2, false, W, GS><<<g, 64, 0, st>>>(a, tiles, n_tiles);
+    if (tap) k_down_mfma<NTT, 2, true, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
+    else k_down_mfma<NTT, 2, false, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
   }
+}
+
+// Small batches (grouped: four tiles per workgroup) take the 32-token tiles only.
+template <int W, bool GS>
+static void mfma_gateup_pick(const ExpertArgs& a, int grid, int ntt, bool grouped, const int32_t* tiles,
+                             const int32_t* n_tiles, hipStream_t st) {
+  if (ntt == 2) mfma_gateup_launch<2, W, GS, 1>(a, grid, tiles, n_tiles, st);
+  else if (grouped) mfma_gateup_launch<1, W, GS, 4>(a, grid, tiles, n_tiles, st);
+  else mfma_gateup_launch<1, W, GS, 1>(a, grid, tiles, n_tiles, st);
+}
+
+template <int W, bool GS>
+static void mfma_down_pick(const ExpertArgs& a, int grid, int ntt, bool grouped, const int32_t* tiles,
+                           const int32_t* n_tiles, hipStream_t st) {
+  if (ntt == 2) mfma_down_launch<2, W, GS, 1>(a, grid, tiles, n_tiles, st);
+  else if (grouped) mfma_down_launch<1, W, GS, 4>(a, grid, tiles, n_tiles, st);
+  else mfma_down_launch<1, W, GS, 1>(a, grid, tiles, n_tiles, st);
 }
 
 hipError_t launch_tile_gather(const ExpertArgs& a, int grid, int tok_tile, const int32_t* tiles,
@@ -1227,37 +1255,21 @@ hipError_t launch_tile_gather(const ExpertArgs& a, int grid, int tok_tile, const
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
-                              hipStream_t st) {
+hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, bool grouped, const int32_t* tiles,
+                              const int32_t* n_tiles, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  dim3 g(a.I / 32, grid);
-  if (a.wbits == 8) {
-    if (ntt == 2) mfma_gateup_launch<2, 8, false>(a, g, tiles, n_tiles, st);
-    else mfma_gateup_launch<1, 8, false>(a, g, tiles, n_tiles, st);
-  } else if (a.gshift >= 0) {
-    if (ntt == 2) mfma_gateup_launch<2, 4, true>(a, g, tiles, n_tiles, st);
-    else mfma_gateup_launch<1, 4, true>(a, g, tiles, n_tiles, st);
-  } else {
-    if (ntt == 2) mfma_gateup_launch<2, 4, false>(a, g, tiles, n_tiles, st);
-    else mfma_gateup_launch<1, 4, false>(a, g, tiles, n_tiles, st);
-  }
+  if (a.wbits == 8) mfma_gateup_pick<8, false>(a, grid, ntt, grouped, tiles, n_tiles, st);
+  else if (a.gshift >= 0) mfma_gateup_pick<4, true>(a, grid, ntt, grouped, tiles, n_tiles, st);
+  else mfma_gateup_pick<4, false>(a, grid, ntt, grouped, tiles, n_tiles, st);
   return hipGetLastError();
 }
 
-hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
-                            hipStream_t st) {
+hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, bool grouped, const int32_t* tiles,
+                            const int32_t* n_tiles, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  dim3 g(a.H / 64, grid);  // 64-row tiles
-  if (a.wbits == 8) {
-    if (ntt == 2) mfma_down_launch<2, 8, false>(a, g, tiles, n_tiles, st);
-    else mfma_down_launch<1, 8, false>(a, g, tiles, n_tiles, st);
-  } else if (a.gshift >= 0) {
-    if (ntt == 2) mfma_down_launch<2, 4, true>(a, g, tiles, n_tiles, st);
-    else mfma_down_launch<1, 4, true>(a, g, tiles, n_tiles, st);
-  } else {
-    if (ntt == 2) mfma_down_launch<2, 4, false>(a, g, tiles, n_tiles, st);
-    else mfma_down_launch<1, 4, false>(a, g, tiles, n_tiles, st);
-  }
+  if (a.wbits == 8) mfma_down_pick<8, false>(a, grid, ntt, grouped, tiles, n_tiles, st);
+  else if (a.gshift >= 0) mfma_down_pick<4, true>(a, grid, ntt, grouped, tiles, n_tiles, st);
+  else mfma_down_pick<4, false>(a, grid, ntt, grouped, tiles, n_tiles, st);
   return hipGetLastError();
 }
 

@@ -410,6 +410,9 @@ int32_t layer_forward_impl(const moe_config* cfg, const moe_layer_weights* wts, 
   // right after top-K and the dispatch runs beside it (on the helper stream, ahead of the MFMA chain, or after
   // the gate/up GEMV on the caller's stream); the down GEMV, the MFMA chain and the combine use its tables.
   const bool self = f.T > 1 && f.gemm_min <= kGemvMaxN + 1 && f.L.TK <= kSelfDispatchMaxSlots;
+  // Up to the same slot count the MFMA grids (sized for the worst case) are mostly empty: four tiles per
+  // workgroup (decode with 32 tokens: 0.527 -> 0.519 ms; at MTP verify and prefill one per workgroup is faster)
+  const bool grouped = f.L.TK <= kSelfDispatchMaxSlots;
   const bool fork = use_helper && (f.grid_tiles > 0 || self);
   if (fork) {
     hipError_t he = get_helper(stream, &hp);
@@ -428,9 +431,9 @@ int32_t layer_forward_impl(const moe_config* cfg, const moe_layer_weights* wts, 
     if (e == hipSuccess && self) e = hipEventRecord(hp.disp, hp.side);
     if (e == hipSuccess && f.grid_tiles > 0) e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, hp.side);
     prof_mark(call, 9, hp.side);  // the MFMA stages time the gate/up and down launches, not the gather
-    if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
+    if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, grouped, tiles, n_tiles, hp.side);
     prof_mark(call, 10, hp.side);
-    if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, hp.side);
+    if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, grouped, tiles, n_tiles, hp.side);
     prof_mark(call, 11, hp.side);
   }
   ExpertArgs ga = f.a;  // gate/up GEMV arguments
@@ -445,8 +448,8 @@ int32_t layer_forward_impl(const moe_config* cfg, const moe_layer_weights* wts, 
   if (e == hipSuccess && self && !use_helper) e = fwd_dispatch(f, stream);
   if (e == hipSuccess && !use_helper && f.grid_tiles > 0) {  // the MFMA chain on the caller's stream
     e = launch_tile_gather(f.a, f.grid_tiles, f.tok_tile, tiles, n_tiles, stream);
-    if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, stream);
-    if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, tiles, n_tiles, stream);
+    if (e == hipSuccess) e = launch_mfma_gateup(f.a, f.grid_tiles, f.tok_tile / 32, grouped, tiles, n_tiles, stream);
+    if (e == hipSuccess) e = launch_mfma_down(f.a, f.grid_tiles, f.tok_tile / 32, grouped, tiles, n_tiles, stream);
   }
   if (e == hipSuccess && self && use_helper) e = hipStreamWaitEvent(stream, hp.disp, 0);
   if (e == hipSuccess) e = launch_gemv_down(f.a, f.grid_gemv, f.many, f.gemv_chunk, stream);

@@ -280,10 +280,11 @@ hipError_t launch_gemv_gateup(const ExpertArgs& a, int grid, bool many, int max_
 hipError_t launch_gemv_down(const ExpertArgs& a, int grid, bool many, int max_chunk, hipStream_t st);
 hipError_t launch_tile_gather(const ExpertArgs& a, int grid, int tok_tile, const int32_t* tiles,
                               const int32_t* n_tiles, hipStream_t st);
-hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
-                              hipStream_t st);
-hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, const int32_t* tiles, const int32_t* n_tiles,
-                            hipStream_t st);
+// grouped: four 32-token tiles per workgroup (for small batches, whose worst-case grids are mostly empty)
+hipError_t launch_mfma_gateup(const ExpertArgs& a, int grid, int ntt, bool grouped, const int32_t* tiles,
+                              const int32_t* n_tiles, hipStream_t st);
+hipError_t launch_mfma_down(const ExpertArgs& a, int grid, int ntt, bool grouped, const int32_t* tiles,
+                            const int32_t* n_tiles, hipStream_t st);
 hipError_t launch_combine(const float* eout, const float* w, const int32_t* slotpos, int T, const moe_config& c,
                           float* y, hipStream_t st);
 

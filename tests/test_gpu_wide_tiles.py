@@ -2,8 +2,11 @@
 both prefetch depths of their block ring (4 blocks when the block count is a
 multiple of 4, 2 otherwise) for gate/up and down, with int4 row scales, int4
 grouped scales and int8 weights, up to batches whose dispatch reads the ids
-from global memory. Every tap of every token without a router
-near-tie is compared bit for bit with the oracle.
+from global memory; and the 32-position tiles of small batches (T*K <= 512),
+which run four tiles per workgroup, on shapes whose row-block counts are not
+multiples of four (5 or 6 down tiles, 6 gate/up row blocks), so that some
+wavefronts of the last workgroup have no tile. Every tap of every token
+without a router near-tie is compared bit for bit with the oracle.
 """
 import numpy as np
 import pytest
@@ -35,6 +38,8 @@ SHAPES = {
 # the ids in LDS, so it reads them from global memory.
 CASES = [(n, wb, gs, T, gm) for n in SHAPES for (wb, gs) in ((4, 0), (4, 64), (8, 0)) for (T, gm) in ((300, 1), (257, 70))]
 CASES += [(n, wb, 0, T, gm) for (n, wb) in (("ring4", 4), ("mixed", 8)) for (T, gm) in ((3200, 1), (6200, 5))]
+# small batches: all buckets (gemm_min 1) or those of 3+ tokens on the grouped 32-position tiles
+CASES += [(n, wb, gs, 40, gm) for n in ("ring2", "mixed") for (wb, gs) in ((4, 0), (4, 64), (8, 0)) for gm in (1, 3)]
 
 
 @pytest.mark.parametrize("name,wb,gs,T,gemm_min", CASES)
