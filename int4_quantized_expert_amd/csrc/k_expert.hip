@@ -1123,7 +1123,10 @@ __global__ __launch_bounds__(64 * MW) void k_down_mfma(ExpertArgs a, const int32
 // MFMA tiles: blocks in flight per wavefront (the gate/up tile is VALU-bound:
 // 2 blocks, or 3-4 wavefronts per SIMD instead of 2, measured no faster; the
 // down tile with 2 measured 0.5% faster at prefill than with 4, 8 slower).
-constexpr int kMpfGateup = 4, kMpfDown = 2;
+// The one-per-workgroup 32-token gate/up tile (MTP-sized batches) keeps 2: 96
+// instead of 118 VGPRs, 5 wavefronts per SIMD instead of 4 (MTP verify 0.6%
+// faster per step).
+constexpr int kMpfGateup = 4, kMpfGateup32 = 2, kMpfDown = 2;
 
 // Steps in flight per wavefront (a step is 1 KB of weights per stream and
 // wavefront): 2 when many buckets stream at once, 1 for the two gate/up
@@ -1204,7 +1207,7 @@ template <int NTT, int W, bool GS, int MW>
 static void mfma_gateup_launch(const ExpertArgs& a, int grid, const int32_t* tiles, const int32_t* n_tiles,
                                hipStream_t st) {
   const bool tap = a.t_gu_sums != nullptr;
-  constexpr int MPF = kMpfGateup;
+  constexpr int MPF = (NTT == 1 && MW == 1) ? kMpfGateup32 : kMpfGateup;
   const dim3 g((a.I / 32 + MW - 1) / MW, grid);
   if ((a.H / 32) % MPF == 0) {
     if (tap) k_gateup_mfma<NTT, MPF, true, W, GS, MW><<<g, 64 * MW, 0, st>>>(a, tiles, n_tiles);
