@@ -454,9 +454,11 @@ def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_meas
     for s in range(args.warmup):
         moe.moe_layer_forward(cfg, wts[s % ncopy], xs[s % len(xs)], y, ws)
     torch.cuda.synchronize()
-    # dominant kernel: the gate-up launch of the path that moves most bytes; the
-    # timed region records HIP events around it only (on the stream it runs on)
-    kname = "gateup_mfma" if workload == "prefill" else "gateup_gemv"
+    # dominant kernel: the gate-up launch of the path that moves most bytes (the path
+    # with more experts on average); the timed region records HIP events around it
+    # only (on the stream it runs on)
+    mfma_major = np.mean([s["mfma_experts"] for s in stats]) > np.mean([s["gemv_experts"] for s in stats])
+    kname = "gateup_mfma" if mfma_major else "gateup_gemv"
     # counter summaries are per kernel, workload and weight width
     pmc_workload = workload + ("_int8w" if WB == 8 else "") + (f"_g{GSZ}" if GSZ else "") + \
         (f"_topp{args.topp:g}" if 0 < args.topp < 1 else "")
@@ -548,8 +550,10 @@ def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_meas
                     valu_epilogue=dict(ops_per_launch=float(valu.mean()), peak=VALU_PEAK_OPS, frac=round(valu_frac, 4),
                                        per_unit="2 VALU lane-ops (convert + FMA) per (row, token, 32-block)"))
     else:
-        gb = np.array([s["gemv_experts"] * w13_bytes + s["gemv_tokens"] * (H + H // 32 * 4 + I + I // 32 * 4)
-                       for s in stats], np.float64)
+        # HBM-bound (decode on the GEMV path, MTP verify on the MFMA path): the path's experts' gate/up weights
+        # and scales, Q8_0 activations in and Q8_0 h out per token
+        ne, nt = ("mfma_experts", "mfma_tokens") if kname == "gateup_mfma" else ("gemv_experts", "gemv_tokens")
+        gb = np.array([s[ne] * w13_bytes + s[nt] * (H + H // 32 * 4 + I + I // 32 * 4) for s in stats], np.float64)
         kt = prof[:, kidx] / 1e3
         achieved = float(np.mean(gb / kt) / 1e9)
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -557,8 +561,8 @@ def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_meas
                     kernel="k_" + kname, algorithmic_bytes=round(float(gb.mean()), 1),
                     kernel_ms=round(float(kt.mean() * 1e3), 4),
                     frac_of_measured_peak=round(achieved / hbm_measured, 4) if hbm_measured else None,
-                    per_unit=f"{w13_bytes} B of gate/up weights+scales per GEMV-path expert, plus Q8_0 activations "
-                             f"in and Q8_0 h out per token")
+                    per_unit=f"{w13_bytes} B of gate/up weights+scales per {'MFMA' if kname == 'gateup_mfma' else 'GEMV'}"
+                             f"-path expert, plus Q8_0 activations in and Q8_0 h out per token")
     layer_gbs = float(np.mean(layer_bytes / (ms_step / 1e3)) / 1e9)
     out = {
         "value": round(T / (ms_step / 1e3), 1),
