@@ -203,6 +203,24 @@ int32_t moe_quantize_int4_grouped(const float* w, int32_t rows, int32_t cols, in
 int32_t moe_quantize_int8(const float* w, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
                           hipStream_t stream);
 
+/* Converters for callers that already hold quantized experts in the canonical
+ * packing of the pages' formats ("Show HN: 느린 컴퓨터에서 GLM 5.2 실행하기",
+ * implemented features: packed int4 and int8 weights with per-row scales):
+ * row-major [rows][cols], rows contiguous along K; int4 as two's-complement
+ * nibbles, element 2j in the low nibble of byte j (cols/2 bytes per row); int8
+ * one byte per element. They write the row-tiled device layouts above. A pure
+ * byte permutation: codes are copied, never re-quantized, so a layer built from
+ * canonical codes gives the same results as one encoded by moe_quantize_*.
+ * Per-row scales need no conversion (the device layout is [rows] as well).
+ * rows % 64 == 0, cols % 32 == 0; rowmajor and tiled 16-byte aligned and not
+ * overlapping. Errors: MOE_E_NULL, MOE_E_SHAPE, MOE_E_ARG (misaligned). */
+int32_t moe_tile_int4(const uint8_t* rowmajor, int32_t rows, int32_t cols, uint8_t* tiled, hipStream_t stream);
+int32_t moe_tile_int8(const int8_t* rowmajor, int32_t rows, int32_t cols, uint8_t* tiled, hipStream_t stream);
+/* Group scales [rows][n_groups] row-major -> the tiled group-scale layout
+ * [rows/64][n_groups][64] of moe_quantize_int4_grouped. rows % 64 == 0. */
+int32_t moe_tile_group_scales(const float* rowmajor, int32_t rows, int32_t n_groups, float* tiled,
+                              hipStream_t stream);
+
 /* Q8_0 of n fp32 values (n % 32 == 0) [B]: per 32-block d = amax/127,
  * q = round-half-away(v * (1/d)) clamped to [-127,127]; natural order. */
 int32_t moe_quantize_q8_0(const float* x, int64_t n, int8_t* q, float* d, hipStream_t stream);

@@ -75,6 +75,9 @@ _sig("moe_quantize_int4", I32, [P, I32, I32, P, P, P])
 _sig("moe_quantize_int8", I32, [P, I32, I32, P, P, P])
 _sig("moe_quantize_int4_grouped", I32, [P, I32, I32, I32, P, P, P])
 _sig("moe_quantize_q8_0", I32, [P, I64, P, P, P])
+_sig("moe_tile_int4", I32, [P, I32, I32, P, P])
+_sig("moe_tile_int8", I32, [P, I32, I32, P, P])
+_sig("moe_tile_group_scales", I32, [P, I32, I32, P, P])
 _sig("moe_router", I32, [P, P, I32, P, P, P, P, P, P, SZ, P])
 _sig("moe_dispatch", I32, [P, P, I32, P, P, P, P, P, P, P, SZ, P])
 _sig("moe_layer_forward", I32, [P, P, P, I32, P, P, SZ, P, P])
@@ -93,7 +96,8 @@ _sig("moe_membench_read", I32, [P, SZ, I32, I32, P, P])
 _sig("moe_membench_copy", I32, [P, P, SZ, I32, P])
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_workspace_bytes", "moe_quantize_int4",
-            "moe_quantize_int8", "moe_quantize_int4_grouped", "moe_quantize_q8_0", "moe_router", "moe_dispatch", "moe_layer_forward",
+            "moe_quantize_int8", "moe_quantize_int4_grouped", "moe_quantize_q8_0",
+            "moe_tile_int4", "moe_tile_int8", "moe_tile_group_scales", "moe_router", "moe_dispatch", "moe_layer_forward",
             "moe_layer_forward_noalloc", "moe_expert_cache_create",
             "moe_expert_cache_forward", "moe_expert_cache_stats", "moe_expert_cache_usage", "moe_expert_cache_set_usage",
             "moe_expert_cache_pin_hottest", "moe_expert_cache_destroy", "moe_prof_enable",
@@ -236,6 +240,43 @@ def moe_quantize_q8_0(x, q, d, stream=None):
     _need(q, "q", "i8", x.numel())
     _need(d, "d", "f32", x.numel() // 32)
     return _check("moe_quantize_q8_0", _lib.moe_quantize_q8_0(_ptr(x), x.numel(), _ptr(q), _ptr(d), _stream(stream)))
+
+
+def _tile_args(src, dst, nbytes, src_dtype, names):
+    """Both buffers on the GPU, contiguous, of the element type, and holding the `nbytes` the call reads and writes."""
+    _need(src, names[0], src_dtype)
+    _need(dst, names[1], "u8")
+    for t, n in ((src, names[0]), (dst, names[1])):
+        if t.numel() * t.element_size() < nbytes:
+            raise ArgError(f"{n}: {t.numel() * t.element_size()} bytes, the call touches {nbytes}")
+
+
+def moe_tile_int4(rowmajor, rows: int, cols: int, tiled, stream=None):
+    """Canonical row-major packed int4 [rows][cols/2] bytes -> the row-tiled layout (byte permutation)."""
+    _tile_args(rowmajor, tiled, int(rows) * int(cols) // 2, "u8", ("rowmajor", "tiled"))
+    return _check("moe_tile_int4", _lib.moe_tile_int4(_ptr(rowmajor), int(rows), int(cols), _ptr(tiled),
+                                                      _stream(stream)))
+
+
+def moe_tile_int8(rowmajor, tiled, stream=None):
+    """Canonical row-major int8 codes [rows][cols] -> the row-tiled int8 layout (byte permutation)."""
+    _need(rowmajor, "rowmajor", "i8")
+    if rowmajor.dim() != 2:
+        raise ArgError(f"rowmajor: 2-D [rows][cols] expected, got {tuple(rowmajor.shape)}")
+    rows, cols = rowmajor.shape
+    _tile_args(rowmajor, tiled, rows * cols, "i8", ("rowmajor", "tiled"))
+    return _check("moe_tile_int8", _lib.moe_tile_int8(_ptr(rowmajor), rows, cols, _ptr(tiled), _stream(stream)))
+
+
+def moe_tile_group_scales(rowmajor, tiled, stream=None):
+    """Group scales [rows][n_groups] fp32 -> the tiled group-scale layout [rows/64][n_groups][64]."""
+    _need(rowmajor, "rowmajor", "f32")
+    if rowmajor.dim() != 2:
+        raise ArgError(f"rowmajor: 2-D [rows][n_groups] expected, got {tuple(rowmajor.shape)}")
+    rows, ng = rowmajor.shape
+    _need(tiled, "tiled", "f32", rows * ng)
+    return _check("moe_tile_group_scales", _lib.moe_tile_group_scales(_ptr(rowmajor), rows, ng, _ptr(tiled),
+                                                                      _stream(stream)))
 
 
 def moe_router(cfg: Config, x, router_w, router_bias, topk_ids, topk_w, near_tie, ws, stream=None):

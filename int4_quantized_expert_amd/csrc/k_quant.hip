@@ -182,6 +182,76 @@ __global__ void k_q8_0_plain(const float* __restrict__ x, int64_t nblocks, int8_
   d[b] = db;
 }
 
+// Canonical row-major codes -> the row-tiled device layouts. A pure byte
+// permutation, nothing is re-quantized. One lane per (64-row tile, block, row)
+// in the order of the tiled output, so the writes are contiguous.
+__global__ __launch_bounds__(256) void k_tile_int4(const uint8_t* __restrict__ src, int64_t n, int cols,
+                                                   uint8_t* __restrict__ dst) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int nb = cols / 32;
+  const int64_t tile = idx / ((int64_t)nb * 64);
+  const int b = (int)((idx / 64) % nb), rr = (int)(idx % 64);
+  const int64_t row = tile * 64 + rr;
+  const uint4 v = *reinterpret_cast<const uint4*>(src + row * (cols / 2) + (size_t)b * 16);
+  *reinterpret_cast<uint4*>(dst + tb_off((int)tile, b, nb) + (size_t)rr * 16) = v;
+}
+
+// int8: each group of 8 bytes of a block is reordered to its even elements,
+// then its odd ones (the activations' permuted order).
+__global__ __launch_bounds__(256) void k_tile_int8(const uint8_t* __restrict__ src, int64_t n, int cols,
+                                                   uint8_t* __restrict__ dst) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int nb = cols / 32;
+  const int64_t tile = idx / ((int64_t)nb * 64);
+  const int b = (int)((idx / 64) % nb), rr = (int)(idx % 64);
+  const int64_t row = tile * 64 + rr;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src + row * cols + (size_t)b * 32);
+  const uint4 v0 = s4[0], v1 = s4[1];
+  const uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t wv[8];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t lo = in[2 * g], hi = in[2 * g + 1];  // elements 8g..8g+3, 8g+4..8g+7
+    const uint32_t e0 = lo & 0xFFu, e1 = (lo >> 8) & 0xFFu, e2 = (lo >> 16) & 0xFFu, e3 = lo >> 24;
+    const uint32_t e4 = hi & 0xFFu, e5 = (hi >> 8) & 0xFFu, e6 = (hi >> 16) & 0xFFu, e7 = hi >> 24;
+    wv[2 * g] = e0 | (e2 << 8) | (e4 << 16) | (e6 << 24);
+    wv[2 * g + 1] = e1 | (e3 << 8) | (e5 << 16) | (e7 << 24);
+  }
+  uint4* d4 = reinterpret_cast<uint4*>(dst + tbw_off<8>((int)tile, b, nb) + (size_t)rr * 32);
+  d4[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  d4[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+}
+
+// Group scales [rows][ng] -> [rows/64][ng][64].
+__global__ __launch_bounds__(256) void k_tile_group_scales(const float* __restrict__ src, int64_t n, int ng,
+                                                           float* __restrict__ dst) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int64_t tile = idx / ((int64_t)ng * 64);
+  const int g = (int)((idx / 64) % ng), rr = (int)(idx % 64);
+  dst[idx] = src[(tile * 64 + rr) * ng + g];
+}
+
+hipError_t launch_tile_codes(const uint8_t* src, int rows, int cols, int bits, uint8_t* dst, hipStream_t st) {
+  const int64_t n = (int64_t)rows * (cols / 32);
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (bits == 8)
+    k_tile_int8<<<grid, 256, 0, st>>>(src, n, cols, dst);
+  else
+    k_tile_int4<<<grid, 256, 0, st>>>(src, n, cols, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_group_scales(const float* src, int rows, int ng, float* dst, hipStream_t st) {
+  const int64_t n = (int64_t)rows * ng;
+  if (n == 0) return hipSuccess;
+  k_tile_group_scales<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(src, n, ng, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float* d, int8_t* q_nat,
                          hipStream_t st) {
   int64_t nb = T * (H / 32);

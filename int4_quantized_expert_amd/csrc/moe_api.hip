@@ -342,6 +342,30 @@ int32_t moe_quantize_int8(const float* w, int32_t rows, int32_t cols, uint8_t* c
   return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
+int32_t moe_tile_int4(const uint8_t* rowmajor, int32_t rows, int32_t cols, uint8_t* tiled, hipStream_t stream) {
+  if (!rowmajor || !tiled) return MOE_E_NULL;
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 32 != 0) return MOE_E_SHAPE;
+  if (!aligned16(rowmajor) || !aligned16(tiled)) return MOE_E_ARG;
+  hipError_t e = launch_tile_codes(rowmajor, rows, cols, 4, tiled, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_tile_int8(const int8_t* rowmajor, int32_t rows, int32_t cols, uint8_t* tiled, hipStream_t stream) {
+  if (!rowmajor || !tiled) return MOE_E_NULL;
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 32 != 0) return MOE_E_SHAPE;
+  if (!aligned16(rowmajor) || !aligned16(tiled)) return MOE_E_ARG;
+  hipError_t e = launch_tile_codes(reinterpret_cast<const uint8_t*>(rowmajor), rows, cols, 8, tiled, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int32_t moe_tile_group_scales(const float* rowmajor, int32_t rows, int32_t n_groups, float* tiled,
+                              hipStream_t stream) {
+  if (!rowmajor || !tiled) return MOE_E_NULL;
+  if (rows <= 0 || n_groups <= 0 || rows % 64 != 0) return MOE_E_SHAPE;
+  hipError_t e = launch_tile_group_scales(rowmajor, rows, n_groups, tiled, stream);
+  return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 int32_t moe_quantize_q8_0(const float* x, int64_t n, int8_t* q, float* d, hipStream_t stream) {
   if (!x || !q || !d) return MOE_E_NULL;
   if (n <= 0 || n % 32 != 0) return MOE_E_SHAPE;

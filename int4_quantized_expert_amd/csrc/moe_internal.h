@@ -261,6 +261,8 @@ __device__ __forceinline__ const float* expert_s2(const WeightView& v, int ex, i
 hipError_t launch_q8_0_x(const float* x, int64_t T, int H, int8_t* q_perm, float* d, int8_t* q_nat,
                          hipStream_t st);
 hipError_t launch_q8_0_plain(const float* x, int64_t n, int8_t* q, float* d, hipStream_t st);
+hipError_t launch_tile_codes(const uint8_t* src, int rows, int cols, int bits, uint8_t* dst, hipStream_t st);
+hipError_t launch_tile_group_scales(const float* src, int rows, int ng, float* dst, hipStream_t st);
 hipError_t launch_quant_int8(const float* w, int rows, int cols, uint8_t* codes, float* scales, hipStream_t st);
 hipError_t launch_quant_int4_grouped(const float* w, int rows, int cols, int group, uint8_t* packed, float* scales,
                                      hipStream_t st);

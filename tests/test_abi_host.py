@@ -145,3 +145,21 @@ def test_binding_checks_tensors_before_the_library():
         L._need(x, "x", "f32")  # host tensor
     with pytest.raises(moe.ArgError):
         moe.taps(no_such_tap=x)
+
+
+def test_tile_converters_validate_before_any_device_work():
+    dummy = ctypes.c_void_p(4096)
+    for fn in (L._lib.moe_tile_int4, L._lib.moe_tile_int8):
+        assert fn(None, 64, 32, dummy, None) == L.MOE_E_NULL
+        assert fn(dummy, 64, 32, None, None) == L.MOE_E_NULL
+        assert fn(dummy, 63, 32, dummy, None) == L.MOE_E_SHAPE   # rows not whole 64-row tiles
+        assert fn(dummy, 64, 48, dummy, None) == L.MOE_E_SHAPE   # cols not whole 32-element blocks
+        assert fn(dummy, 0, 32, dummy, None) == L.MOE_E_SHAPE
+        assert fn(ctypes.c_void_p(4100), 64, 32, dummy, None) == L.MOE_E_ARG  # 16-byte loads need alignment
+        assert fn(dummy, 64, 32, ctypes.c_void_p(4104), None) == L.MOE_E_ARG
+    assert L._lib.moe_tile_group_scales(None, 64, 2, dummy, None) == L.MOE_E_NULL
+    assert L._lib.moe_tile_group_scales(dummy, 96, 2, dummy, None) == L.MOE_E_SHAPE
+    assert L._lib.moe_tile_group_scales(dummy, 64, 0, dummy, None) == L.MOE_E_SHAPE
+    import torch
+    with pytest.raises(moe.ArgError):
+        moe.moe_tile_int4(torch.zeros(64 * 16, dtype=torch.uint8), 64, 32, torch.zeros(64 * 16, dtype=torch.uint8))
