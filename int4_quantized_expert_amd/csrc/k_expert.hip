@@ -168,6 +168,17 @@ __device__ __forceinline__ void prep_wblk(const WBlk<8>& b, WPrep<8>& p) {
   p.a = b.v[0];
   p.b = b.v[1];
 }
+// Pins a prepared block in registers at this point: the unpack cannot sink
+// below the ring refill that follows it, so the refill can load into the
+// registers the block came from.
+__device__ __forceinline__ void pin_prep(WPrep<4>& p) {
+  asm volatile("" : "+v"(p.lo[0]), "+v"(p.lo[1]), "+v"(p.lo[2]), "+v"(p.lo[3]), "+v"(p.hi[0]), "+v"(p.hi[1]),
+               "+v"(p.hi[2]), "+v"(p.hi[3]));
+}
+__device__ __forceinline__ void pin_prep(WPrep<8>& p) {
+  asm volatile("" : "+v"(p.a.x), "+v"(p.a.y), "+v"(p.a.z), "+v"(p.a.w), "+v"(p.b.x), "+v"(p.b.y), "+v"(p.b.z),
+               "+v"(p.b.w));
+}
 __device__ __forceinline__ int wdot(const WPrep<4>& p, v4i xa, v4i xb) { return dot_block16(p.lo, p.hi, xa, xb) >> 4; }
 __device__ __forceinline__ int wdot(const WPrep<8>& p, v4i xa, v4i xb) {
   int s = 0;
@@ -397,50 +408,58 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
       if (slot_of(a, k, k.p0 + c0 + i) == a.sum_slot) tap_i = i;
   }
   float acc = 0.0f;  // this lane's chain (lane < 16 N)
-  for (int j0 = 0; j0 < nsteps; j0 += PF) {
-#pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const int j = j0 + kk;
-      if (j < nsteps) {
-        const int blk = 8 * j + bs;
-        const int bq = min(blk, nb - 1);
-        WPrep<W> pg, pu;
-        prep_wblk(bg[kk], pg);
-        prep_wblk(bu[kk], pu);
-        const float cg = GS ? sgq[kk] : 0.0f, cu = GS ? suq[kk] : 0.0f;
-        if (j + PF < nsteps) {  // refill with step j + PF; the last PF steps load nothing more
-          const int bn = min(8 * (j + PF) + bs, nb - 1);
-          load_wblk<W>(bg[kk], gb + (size_t)bn * kTileBlock<W>);
-          load_wblk<W>(bu[kk], ub + (size_t)bn * kTileBlock<W>);
-          if constexpr (GS) {
-            sgq[kk] = gsc[(size_t)(bn >> gsh) * 64];
-            suq[kk] = usc[(size_t)(bn >> gsh) * 64];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-          const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)bq * 32);
-          const v4i xa = xb4[0], xb = xb4[1];
-          const int Sg = wdot(pg, xa, xb);
-          const int Su = wdot(pu, xa, xb);
-          tb[((i << 3) | rl) * 8 + bs] = (float)Sg;
-          tb[(((N + i) << 3) | rl) * 8 + bs] = (float)Su;
-          if (TAP && i == tap_i && blk < nb) {
-            a.t_gu_sums[(size_t)(tile * 64 + row) * nb + blk] = Sg;
-            a.t_gu_sums[(size_t)(I + tile * 64 + row) * nb + blk] = Su;
-          }
-        }
-        if constexpr (GS) {
-          sgw[rl * 8 + bs] = cg;
-          sgw[(8 + rl) * 8 + bs] = cu;
-        }
-        wave_sync();
-        chain_step<N, 2, GS>(acc, tb, xd, sgw, lane, nbp, j, min(8, nb - 8 * j));
-        wave_sync();
+  // Step j consumes ring slot kk and, with `refill`, loads step j + PF into it. The refill goes into the
+  // registers just consumed (pinned unpack, scheduling barrier) and is unconditional inside the main loop, so
+  // every wait in the loop is for the slot it consumes only; the last PF steps (the drain) load nothing.
+  auto step = [&](const int j, const int kk, const bool refill) __attribute__((always_inline)) {
+    const int blk = 8 * j + bs;
+    const int bq = min(blk, nb - 1);
+    WPrep<W> pg, pu;
+    prep_wblk(bg[kk], pg);
+    prep_wblk(bu[kk], pu);
+    pin_prep(pg);
+    pin_prep(pu);
+    const float cg = GS ? sgq[kk] : 0.0f, cu = GS ? suq[kk] : 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) {
+      const int bn = min(8 * (j + PF) + bs, nb - 1);
+      load_wblk<W>(bg[kk], gb + (size_t)bn * kTileBlock<W>);
+      load_wblk<W>(bu[kk], ub + (size_t)bn * kTileBlock<W>);
+      if constexpr (GS) {
+        sgq[kk] = gsc[(size_t)(bn >> gsh) * 64];
+        suq[kk] = usc[(size_t)(bn >> gsh) * 64];
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)bq * 32);
+      const v4i xa = xb4[0], xb = xb4[1];
+      const int Sg = wdot(pg, xa, xb);
+      const int Su = wdot(pu, xa, xb);
+      tb[((i << 3) | rl) * 8 + bs] = (float)Sg;
+      tb[(((N + i) << 3) | rl) * 8 + bs] = (float)Su;
+      if (TAP && i == tap_i && blk < nb) {
+        a.t_gu_sums[(size_t)(tile * 64 + row) * nb + blk] = Sg;
+        a.t_gu_sums[(size_t)(I + tile * 64 + row) * nb + blk] = Su;
+      }
+    }
+    if constexpr (GS) {
+      sgw[rl * 8 + bs] = cg;
+      sgw[(8 + rl) * 8 + bs] = cu;
+    }
+    wave_sync();
+    chain_step<N, 2, GS>(acc, tb, xd, sgw, lane, nbp, j, min(8, nb - 8 * j));
+    wave_sync();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // PF divides nsteps (the host picks it so)
+  int j0 = 0;
+  for (; j0 + PF < nsteps; j0 += PF) {
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) step(j0 + kk, kk, true);
   }
+#pragma unroll
+  for (int kk = 0; kk < PF; ++kk) step(j0 + kk, kk, false);
   // chain results meet in LDS: hx[token][gate|up][row]; the row scale multiplies once
   if (lane < 16 * N) {
     constexpr int LN = N == 1 ? 0 : (N == 2 ? 1 : 2);
@@ -505,51 +524,55 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
       if (slot_of(a, k, k.p0 + c0 + i) == a.sum_slot) tap_i = i;
   }
   float acc = 0.0f;
-  for (int j0 = 0; j0 < nsteps; j0 += PF) {
+  // as in the gate/up GEMV: unconditional refills in the main loop, none in the drain
+  auto step = [&](const int j, const int kk, const bool refill) __attribute__((always_inline)) {
+    const int blk = 8 * j + bs;
+    const int bq = min(blk, nbi - 1);
+    WPrep<W> pw[TP];
+    float co[TP];
 #pragma unroll
-    for (int kk = 0; kk < PF; ++kk) {
-      const int j = j0 + kk;
-      if (j < nsteps) {
-        const int blk = 8 * j + bs;
-        const int bq = min(blk, nbi - 1);
-        WPrep<W> pw[TP];
-        float co[TP];
-#pragma unroll
-        for (int q = 0; q < TP; ++q) {
-          prep_wblk(bw[q][kk], pw[q]);
-          co[q] = GS ? soq[q][kk] : 0.0f;
-        }
-        if (j + PF < nsteps) {  // as in the gate/up GEMV
-          const int bn = min(8 * (j + PF) + bs, nbi - 1);
-#pragma unroll
-          for (int q = 0; q < TP; ++q) {
-            load_wblk<W>(bw[q][kk], wb[q] + (size_t)bn * kTileBlock<W>);
-            if constexpr (GS) soq[q][kk] = osc[q][(size_t)(bn >> gsh) * 64];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-          const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)bq * 32);
-          const v4i ha = hb4[0], hb = hb4[1];
-#pragma unroll
-          for (int q = 0; q < TP; ++q) {
-            const int S = wdot(pw[q], ha, hb);
-            tb[(((q * N + i) << 3) | rl) * 8 + bs] = (float)S;
-            if (TAP && i == tap_i && blk < nbi)
-              a.t_dn_sums[(size_t)((TP * tile2 + q) * 64 + row) * nbi + blk] = S;
-          }
-        }
-        if constexpr (GS) {
-#pragma unroll
-          for (int q = 0; q < TP; ++q) sgw[(q * 8 + rl) * 8 + bs] = co[q];
-        }
-        wave_sync();
-        chain_step<N, TP, GS>(acc, tb, hd, sgw, lane, nbp, j, min(8, nbi - 8 * j));
-        wave_sync();
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < TP; ++q) {
+      prep_wblk(bw[q][kk], pw[q]);
+      pin_prep(pw[q]);
+      co[q] = GS ? soq[q][kk] : 0.0f;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) {
+      const int bn = min(8 * (j + PF) + bs, nbi - 1);
+#pragma unroll
+      for (int q = 0; q < TP; ++q) {
+        load_wblk<W>(bw[q][kk], wb[q] + (size_t)bn * kTileBlock<W>);
+        if constexpr (GS) soq[q][kk] = osc[q][(size_t)(bn >> gsh) * 64];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)bq * 32);
+      const v4i ha = hb4[0], hb = hb4[1];
+#pragma unroll
+      for (int q = 0; q < TP; ++q) {
+        const int S = wdot(pw[q], ha, hb);
+        tb[(((q * N + i) << 3) | rl) * 8 + bs] = (float)S;
+        if (TAP && i == tap_i && blk < nbi)
+          a.t_dn_sums[(size_t)((TP * tile2 + q) * 64 + row) * nbi + blk] = S;
+      }
+    }
+    if constexpr (GS) {
+#pragma unroll
+      for (int q = 0; q < TP; ++q) sgw[(q * 8 + rl) * 8 + bs] = co[q];
+    }
+    wave_sync();
+    chain_step<N, TP, GS>(acc, tb, hd, sgw, lane, nbp, j, min(8, nbi - 8 * j));
+    wave_sync();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int j0 = 0;
+  for (; j0 + PF < nsteps; j0 += PF) {
+#pragma unroll
+    for (int kk = 0; kk < PF; ++kk) step(j0 + kk, kk, true);
   }
+#pragma unroll
+  for (int kk = 0; kk < PF; ++kk) step(j0 + kk, kk, false);
   if (lane < 8 * TP * N) {
     constexpr int LN = N == 1 ? 0 : (N == 2 ? 1 : 2);
     const int t = (lane >> 3) & (N - 1), q = lane >> (3 + LN);
