@@ -419,7 +419,12 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
     prep_wblk(bu[kk], pu);
     pin_prep(pg);
     pin_prep(pu);
-    const float cg = GS ? sgq[kk] : 0.0f, cu = GS ? suq[kk] : 0.0f;
+    float cg = 0.0f, cu = 0.0f;
+    if constexpr (GS) {
+      cg = sgq[kk];
+      cu = suq[kk];
+      asm volatile("" : "+v"(cg), "+v"(cu));
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (refill) {
       const int bn = min(8 * (j + PF) + bs, nb - 1);
@@ -534,7 +539,11 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
     for (int q = 0; q < TP; ++q) {
       prep_wblk(bw[q][kk], pw[q]);
       pin_prep(pw[q]);
-      co[q] = GS ? soq[q][kk] : 0.0f;
+      co[q] = 0.0f;
+      if constexpr (GS) {
+        co[q] = soq[q][kk];
+        asm volatile("" : "+v"(co[q]));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (refill) {
