@@ -61,7 +61,20 @@ __device__ __forceinline__ Bucket load_bucket(const ExpertArgs& a, int b) {
   return k;
 }
 
+// GEMV work item li: false past the device-side count. The count and the entry are read together (every
+// launched li lies inside the list's storage), so the weights wait for two dependent loads, not three.
+__device__ __forceinline__ bool list_entry(const ExpertArgs& a, int li, Bucket& k, int& c0) {
+  const int cnt = *cptr(a.list_count);
+  const int b = cptr(a.list)[2 * li], c = cptr(a.list)[2 * li + 1];
+  asm volatile("" ::"s"(cnt), "s"(b), "s"(c));
+  if (li >= cnt) return false;
+  k = load_bucket(a, b);
+  c0 = c;
+  return true;
+}
+
 __device__ __forceinline__ int token_of(const ExpertArgs& a, const Bucket& k, int p) {
+  if (a.T == 1) return 0;  // one token: no lookup on the way to its activations
   if (k.shared) return (p - a.TK) % a.T;
   return k.sl ? k.sl[p - k.p0] / a.K : cptr(a.pos_token)[p];
 }
@@ -1069,9 +1082,7 @@ __global__ __launch_bounds__(kGemvThreads) void k_gateup_gemv(ExpertArgs a) {
   if (a.self_min > 0) {
     if (!self_bucket(a, li, k, s_self, s_self + kGemvMaxN)) return;
   } else {
-    if (li >= *cptr(a.list_count)) return;
-    k = load_bucket(a, cptr(a.list)[2 * li]);
-    c0 = cptr(a.list)[2 * li + 1];
+    if (!list_entry(a, li, k, c0)) return;
   }
   const uint8_t* w13 = expert_w13(a.wv, k.ex, a.E, w13_bytes(a.H, a.I, W));
   const float* s13 = expert_s13(a.wv, k.ex, a.E, s13_count(a.H, a.I, GS ? a.gshift : -1));
@@ -1085,9 +1096,9 @@ template <int PF, bool TAP, int W, bool GS, int TP>
 __global__ __launch_bounds__(kGemvThreads) void k_down_gemv(ExpertArgs a) {
   extern __shared__ char gemv_lds[];
   const int li = blockIdx.y, tile = blockIdx.x;
-  if (li >= *cptr(a.list_count)) return;
-  const Bucket k = load_bucket(a, cptr(a.list)[2 * li]);
-  const int c0 = cptr(a.list)[2 * li + 1];
+  Bucket k;
+  int c0;
+  if (!list_entry(a, li, k, c0)) return;
   const uint8_t* w2 = expert_w2(a.wv, k.ex, a.E, w2_bytes(a.H, a.I, W));
   const float* s2 = expert_s2(a.wv, k.ex, a.E, s2_count(a.H, a.I, GS ? a.gshift : -1));
   const int nn = min(kGemvMaxN, k.n - c0);
