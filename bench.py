@@ -281,7 +281,9 @@ def traffic_of(kernel, workload):
 
 
 def run_stack(args):
-    """Stacked decode: every step runs all layers in order at T=32; streamed layers go through their caches."""
+    """Stacked decode: every step runs all layers in order at T=32 on one residual stream (h = fresh tokens; layer
+    input = weightless RMSNorm(h), eps 1e-6; h += the layer's output; the glue runs in torch on the compute stream);
+    streamed layers go through their caches."""
     import torch
 
     import int4_quantized_expert_amd as moe
@@ -311,20 +313,26 @@ def run_stack(args):
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
     n_steps = args.warmup + args.steps
-    xs = [[torch.from_numpy(synth.hidden_states(sh, T, seed=args.seed, step=s * 64 + l)).to(dev) for l in range(NL)]
-          for s in range(n_steps)]
+    xs = [torch.from_numpy(synth.hidden_states(sh, T, seed=args.seed, step=s * 64)).to(dev) for s in range(n_steps)]
     ws = torch.empty(moe.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device=dev)
     y = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
     compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
     wts = [g.weights() for g in layers]
 
+    h = torch.empty((T, sh.hidden), dtype=torch.float32, device=dev)
+    inp = torch.empty_like(h)
+
     def step(s):
-        for l in range(NL):
-            if l >= NL - NSTR:
-                c = caches[l - (NL - NSTR)]
-                c.forward(wts[l], hosts[l - (NL - NSTR)][0], xs[s][l], y, ws, compute, copy)
-            else:
-                moe.moe_layer_forward(cfg, wts[l], xs[s][l], y, ws, stream=compute)
+        with torch.cuda.stream(compute):
+            h.copy_(xs[s])
+            for l in range(NL):
+                torch.mul(h, torch.rsqrt(torch.mean(h * h, dim=1, keepdim=True) + 1e-6), out=inp)
+                if l >= NL - NSTR:
+                    c = caches[l - (NL - NSTR)]
+                    c.forward(wts[l], hosts[l - (NL - NSTR)][0], inp, y, ws, compute, copy)
+                else:
+                    moe.moe_layer_forward(cfg, wts[l], inp, y, ws, stream=compute)
+                h.add_(y)
 
     for s in range(args.warmup):
         step(s)
@@ -362,7 +370,7 @@ def run_stack(args):
            "config": {"workload": f"glm5.2-moe stack{NL}: {NL - NSTR} resident + {NSTR} streamed layers, "
                                   f"{args.slots} HBM slots per streamed layer, {n_pin} pinned by usage", "tokens": T,
                       "host_copies": min(NSTR, args.host_copies), "pinned_per_layer": n_pin,
-                      "learning_steps": args.warmup},
+                      "learning_steps": args.warmup, "residual": "h += layer(rmsnorm(h)) between layers"},
            "hit_rate": round(hits / max(1, hits + misses), 4), "hits": hits, "misses": misses,
            "h2d_bytes_per_step": round(h2d / args.steps), "h2d_gbs_over_step": round(h2d / dt / 1e9, 2),
            "pinned_h2d_peak_gbs": round(peak, 2),
