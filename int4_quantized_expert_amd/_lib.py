@@ -251,11 +251,14 @@ def _tile_args(src, dst, nbytes, src_dtype, names):
             raise ArgError(f"{n}: {t.numel() * t.element_size()} bytes, the call touches {nbytes}")
 
 
-def moe_tile_int4(rowmajor, rows: int, cols: int, tiled, stream=None):
+def moe_tile_int4(rowmajor, tiled, stream=None):
     """Canonical row-major packed int4 [rows][cols/2] bytes -> the row-tiled layout (byte permutation)."""
-    _tile_args(rowmajor, tiled, int(rows) * int(cols) // 2, "u8", ("rowmajor", "tiled"))
-    return _check("moe_tile_int4", _lib.moe_tile_int4(_ptr(rowmajor), int(rows), int(cols), _ptr(tiled),
-                                                      _stream(stream)))
+    _need(rowmajor, "rowmajor", "u8")
+    if rowmajor.dim() != 2:
+        raise ArgError(f"rowmajor: 2-D [rows][cols/2] expected, got {tuple(rowmajor.shape)}")
+    rows, cols = rowmajor.shape[0], 2 * rowmajor.shape[1]
+    _tile_args(rowmajor, tiled, rows * cols // 2, "u8", ("rowmajor", "tiled"))
+    return _check("moe_tile_int4", _lib.moe_tile_int4(_ptr(rowmajor), rows, cols, _ptr(tiled), _stream(stream)))
 
 
 def moe_tile_int8(rowmajor, tiled, stream=None):

@@ -162,4 +162,4 @@ def test_tile_converters_validate_before_any_device_work():
     assert L._lib.moe_tile_group_scales(dummy, 64, 0, dummy, None) == L.MOE_E_SHAPE
     import torch
     with pytest.raises(moe.ArgError):
-        moe.moe_tile_int4(torch.zeros(64 * 16, dtype=torch.uint8), 64, 32, torch.zeros(64 * 16, dtype=torch.uint8))
+        moe.moe_tile_int4(torch.zeros((64, 16), dtype=torch.uint8), torch.zeros(64 * 16, dtype=torch.uint8))

@@ -44,7 +44,7 @@ def test_tile_int4_reads_back(rows, cols):
     q = rng.integers(-8, 8, size=(rows, cols), dtype=np.int8)  # every nibble value, -8 included
     canon = O.pack_int4(q)
     tiled = torch.full((rows * cols // 2,), 0xAB, dtype=torch.uint8, device=DEV)
-    moe.moe_tile_int4(_t(canon), rows, cols, tiled)
+    moe.moe_tile_int4(_t(canon.reshape(rows, cols // 2)), tiled)
     assert np.array_equal(O.unpack_int4_tiled64(_np(tiled), rows, cols), q)
 
 
@@ -54,7 +54,7 @@ def test_tile_int4_equals_encoder(rows, cols):
     w[1] = 0.0
     q, s = O.quant_int4_rows(w)
     tiled = torch.empty(rows * cols // 2, dtype=torch.uint8, device=DEV)
-    moe.moe_tile_int4(_t(O.pack_int4(q)), rows, cols, tiled)
+    moe.moe_tile_int4(_t(O.pack_int4(q).reshape(rows, cols // 2)), tiled)
     enc = torch.empty(rows * cols // 2, dtype=torch.uint8, device=DEV)
     enc_s = torch.empty(rows, dtype=torch.float32, device=DEV)
     moe.moe_quantize_int4(_t(w), enc, enc_s)
@@ -84,7 +84,7 @@ def test_tile_grouped_equals_encoder(rows, cols, group):
     q, s = O.quant_int4_grouped(w, group)
     ng = cols // group
     codes = torch.empty(rows * cols // 2, dtype=torch.uint8, device=DEV)
-    moe.moe_tile_int4(_t(O.pack_int4(q)), rows, cols, codes)
+    moe.moe_tile_int4(_t(O.pack_int4(q).reshape(rows, cols // 2)), codes)
     sc = torch.empty(rows * ng, dtype=torch.float32, device=DEV)
     moe.moe_tile_group_scales(_t(s), sc)
     assert np.array_equal(O.unpack_scales_tiled64(_np(sc), rows, ng).view(np.uint32), s.view(np.uint32))
@@ -96,13 +96,14 @@ def test_tile_grouped_equals_encoder(rows, cols, group):
 
 
 def test_tile_rejects_bad_arguments():
-    src = torch.zeros(64 * 48, dtype=torch.uint8, device=DEV)
+    src = torch.zeros((64, 24), dtype=torch.uint8, device=DEV)  # 48 columns: not whole 32-element blocks
     dst = torch.zeros(64 * 48, dtype=torch.uint8, device=DEV)
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_tile_int4(src, 64, 40, dst)  # 40 columns: not whole 32-element blocks
+        moe.moe_tile_int4(src, dst)
     assert ei.value.rc == moe.MOE_E_SHAPE
+    flat = torch.zeros(64 * 16 + 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_tile_int4(src[1:], 64, 32, dst)  # a source that is not 16-byte aligned
+        moe.moe_tile_int4(flat[1:1 + 64 * 16].view(64, 16), dst)  # a source that is not 16-byte aligned
     assert ei.value.rc == moe.MOE_E_ARG
     with pytest.raises(moe.ArgError):
-        moe.moe_tile_int4(src, 256, 32, dst)  # the call would read 4 KB of a 3 KB buffer
+        moe.moe_tile_int4(torch.zeros((128, 16), dtype=torch.uint8, device=DEV), dst[:1024])  # 2 KB into 1 KB
