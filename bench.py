@@ -422,6 +422,38 @@ def measured_hbm_peak(moe, torch):
     return round(best, 1)
 
 
+def measured_compute_peaks(moe, torch):
+    """Best rates of plain compute kernels of known operation count: int8 MFMA (TOP/s; 4 chains of
+    v_mfma_i32_32x32x32_i8 per wavefront, 65,536 ops each) and fp32 VALU fused multiply-adds (lane-ops/s; 8 chains
+    per lane), each over a few launch shapes. The kernels' outputs are checked against their closed forms."""
+    best_mfma, best_valu = 0.0, 0.0
+    for blocks in (512, 1024, 2048):
+        it = 4000
+        out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+        moe.moe_peakbench_mfma_i8(blocks, it, 1, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_peakbench_mfma_i8(blocks, it, 1, out)
+        e1.record()
+        torch.cuda.synchronize()
+        if not bool((out == 2048 * it).all()):
+            raise RuntimeError("int8 MFMA rate kernel: wrong result")
+        best_mfma = max(best_mfma, blocks * 4 * 4 * it * 65536.0 / (e0.elapsed_time(e1) / 1e3) / 1e12)
+        it = 20000
+        outf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        moe.moe_peakbench_valu_fma(blocks, it, 1.0, 0.0, outf)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_peakbench_valu_fma(blocks, it, 1.0, 0.0, outf)
+        e1.record()
+        torch.cuda.synchronize()
+        lane = torch.arange(blocks * 256, device="cuda") % 64
+        if not bool((outf == (8 * lane + 28).float()).all()):
+            raise RuntimeError("fp32 VALU rate kernel: wrong result")
+        best_valu = max(best_valu, blocks * 256 * 8.0 * it / (e0.elapsed_time(e1) / 1e3))
+    return round(best_mfma, 1), best_valu
+
+
 def host_cpu():
     model = "unknown"
     try:
@@ -439,7 +471,7 @@ def host_cpu():
     return dict(cpu_model=model, nproc=os.cpu_count(), nproc_available=avail)
 
 
-def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_measured):
+def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_measured, peaks=(None, None)):
     """One workload's timed pass and its roofline figures (the JSON fields of a bench line, without the CPU
     baseline)."""
     T = tokens_of(workload)
@@ -550,12 +582,16 @@ def measure(args, workload, steps, moe, torch, shape, cfg, layers, wts, hbm_meas
         # the exact block epilogue: one int->fp32 conversion and one fused multiply-add per (row, token, block)
         valu = np.array([2.0 * s["mfma_tokens"] * 2 * I * (H // 32) for s in stats])
         valu_frac = float(np.mean(valu / kt) / VALU_PEAK_OPS)
+        mfma_meas, valu_meas = peaks
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
                     frac=round(achieved / INT8_PEAK_TOPS, 4), traffic=traffic_of("k_" + kname, pmc_workload),
                     kernel="k_" + kname,
                     kernel_ms=round(float(kt.mean() * 1e3), 4),
+                    frac_of_measured_peak=round(achieved / mfma_meas, 4) if mfma_meas else None,
                     per_unit="2*2I*H int8 ops per (token, expert) in the MFMA gate/up launch",
                     valu_epilogue=dict(ops_per_launch=float(valu.mean()), peak=VALU_PEAK_OPS, frac=round(valu_frac, 4),
+                                       frac_of_measured_peak=round(float(np.mean(valu / kt)) / valu_meas, 4)
+                                       if valu_meas else None,
                                        per_unit="2 VALU lane-ops (convert + FMA) per (row, token, 32-block)"))
     else:
         # HBM-bound (decode on the GEMV path, MTP verify on the MFMA path): the path's experts' gate/up weights
@@ -652,9 +688,10 @@ def main():
     WB, GSZ = args.weight_bits, args.group_size
     cfg = config_of(shape, args.gemm_min, WB, GSZ, args.topp)
     hbm_measured = measured_hbm_peak(moe, torch)
+    peaks = measured_compute_peaks(moe, torch)
     layers = [GpuLayer(shape, seed=args.seed + c, weight_bits=WB, group_size=GSZ) for c in range(args.copies)]
     wts = [l.weights() for l in layers]
-    head, xs_host = measure(args, args.workload, args.steps, moe, torch, shape, cfg, layers, wts, hbm_measured)
+    head, xs_host = measure(args, args.workload, args.steps, moe, torch, shape, cfg, layers, wts, hbm_measured, peaks)
     out = {"metric": METRIC, "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
            "steps": head.pop("steps"), "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic"}
@@ -662,12 +699,17 @@ def main():
     out["hbm_measured_peak_gbs"] = hbm_measured
     out["hbm_measured_peak_how"] = "best of plain grid-stride read kernels over 4 GiB (2048-8192 workgroups x 256 " \
                                    "lanes, 2-8 16-byte loads in flight per lane)"
+    out["mfma_i8_measured_peak_tops"] = peaks[0]
+    out["valu_measured_peak_lane_ops"] = peaks[1]
+    out["compute_measured_peaks_how"] = "best of plain kernels over 512-2048 workgroups of 4 wavefronts: 4 " \
+                                        "independent v_mfma_i32_32x32x32_i8 chains per wavefront; 8 independent " \
+                                        "fp32 FMA chains per lane"
     configs = {}
     for w in args.configs:
         if w == "stack40":
             continue
         print(f"bench: measuring {w}", file=sys.stderr, flush=True)
-        configs[w], _ = measure(args, w, args.config_steps, moe, torch, shape, cfg, layers, wts, hbm_measured)
+        configs[w], _ = measure(args, w, args.config_steps, moe, torch, shape, cfg, layers, wts, hbm_measured, peaks)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(shape, xs_host[0], args.cpu_baseline_seconds, args.seed, WB, GSZ, args.topp)
         cb.update(host_cpu())

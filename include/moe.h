@@ -380,6 +380,18 @@ int32_t moe_membench_read(const void* buf, size_t bytes, int32_t blocks, int32_t
                           hipStream_t stream);
 int32_t moe_membench_copy(const void* src, void* dst, size_t bytes, int32_t blocks, hipStream_t stream);
 
+/* Measurement only: compute rates of known operation count. moe_peakbench_mfma_i8
+ * runs `blocks` workgroups of 4 wavefronts, each wavefront 4 independent chains of
+ * `iters` v_mfma_i32_32x32x32_i8 (65,536 int8 ops each) on operands whose bytes all
+ * equal `value`; out [blocks*256] int32 receives 2048 * value^2 * iters per lane
+ * (the caller keeps that below 2^31). moe_peakbench_valu_fma runs `blocks` x 256
+ * lanes, each 8 independent chains of `iters` fp32 fused multiply-adds
+ * acc = fma(acc, m, c) from acc = lane%64 + j; out [blocks*256] fp32 receives the
+ * sum of the 8 chains (with m = 1, c = 0: 8 * (lane%64) + 28). Errors:
+ * MOE_E_NULL, MOE_E_SHAPE (blocks or iters <= 0), MOE_E_HIP. */
+int32_t moe_peakbench_mfma_i8(int32_t blocks, int32_t iters, int32_t value, int32_t* out, hipStream_t stream);
+int32_t moe_peakbench_valu_fma(int32_t blocks, int32_t iters, float m, float c, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -94,6 +94,8 @@ _sig("moe_prof_read", I32, [P, I32, P])
 _sig("moe_prof_disable", None, [])
 _sig("moe_membench_read", I32, [P, SZ, I32, I32, P, P])
 _sig("moe_membench_copy", I32, [P, P, SZ, I32, P])
+_sig("moe_peakbench_mfma_i8", I32, [I32, I32, I32, P, P])
+_sig("moe_peakbench_valu_fma", I32, [I32, I32, ctypes.c_float, ctypes.c_float, P, P])
 
 EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_workspace_bytes", "moe_quantize_int4",
             "moe_quantize_int8", "moe_quantize_int4_grouped", "moe_quantize_q8_0",
@@ -101,7 +103,8 @@ EXPORTED = ("moe_version", "moe_strerror", "moe_last_hip_error", "moe_workspace_
             "moe_layer_forward_noalloc", "moe_expert_cache_create",
             "moe_expert_cache_forward", "moe_expert_cache_stats", "moe_expert_cache_usage", "moe_expert_cache_set_usage",
             "moe_expert_cache_pin_hottest", "moe_expert_cache_destroy", "moe_prof_enable",
-            "moe_prof_read", "moe_prof_disable", "moe_membench_read", "moe_membench_copy")
+            "moe_prof_read", "moe_prof_disable", "moe_membench_read", "moe_membench_copy",
+            "moe_peakbench_mfma_i8", "moe_peakbench_valu_fma")
 
 
 class MoeError(RuntimeError):
@@ -445,6 +448,18 @@ def moe_membench_copy(src, dst, blocks: int, stream=None):
         raise ArgError("dst: smaller than src")
     return _check("moe_membench_copy", _lib.moe_membench_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
                                                               blocks, _stream(stream)))
+
+
+def moe_peakbench_mfma_i8(blocks: int, iters: int, value: int, out, stream=None):
+    _need(out, "out", "i32", int(blocks) * 256)
+    return _check("moe_peakbench_mfma_i8", _lib.moe_peakbench_mfma_i8(int(blocks), int(iters), int(value), _ptr(out),
+                                                                      _stream(stream)))
+
+
+def moe_peakbench_valu_fma(blocks: int, iters: int, m: float, c: float, out, stream=None):
+    _need(out, "out", "f32", int(blocks) * 256)
+    return _check("moe_peakbench_valu_fma", _lib.moe_peakbench_valu_fma(int(blocks), int(iters), float(m), float(c),
+                                                                        _ptr(out), _stream(stream)))
 
 
 class HostExperts:

@@ -1,8 +1,10 @@
 """GPU tests of the measurement-only entry points: stage timing events
 (moe_prof_*) and the memory microbenchmarks that calibrate the byte counters
-(moe_membench_*). Timing must not change a forward's result; the stage mask
-selects the stages that are timed; the read kernel folds every word it is
-given; the copy kernel copies every byte.
+(moe_membench_*), and the compute-rate kernels (moe_peakbench_*). Timing must
+not change a forward's result; the stage mask selects the stages that are timed;
+the read kernel folds every word it is given; the copy kernel copies every byte;
+the compute-rate kernels run every step they count (their outputs equal the
+closed forms of the work done).
 """
 import numpy as np
 import pytest
@@ -110,3 +112,33 @@ def test_membench_rejects_bad_arguments():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_membench_copy(buf, torch.zeros(32, dtype=torch.uint8, device=DEV), 0)
     assert ei.value.rc == moe.MOE_E_SHAPE
+
+
+@pytest.mark.parametrize("blocks,iters,value", [(1, 1, 1), (3, 7, 3), (512, 100, -2), (64, 1000, 1)])
+def test_peakbench_mfma_runs_every_step(blocks, iters, value):
+    out = torch.full((blocks * 256,), -1, dtype=torch.int32, device=DEV)
+    moe.moe_peakbench_mfma_i8(blocks, iters, value, out)
+    torch.cuda.synchronize()
+    # four chains of iters MFMAs, each adding 32 * value^2 to all 16 elements a lane holds
+    assert bool((out == 2048 * value * value * iters).all())
+
+
+@pytest.mark.parametrize("blocks,iters", [(1, 1), (5, 33), (512, 1000)])
+def test_peakbench_valu_runs_every_step(blocks, iters):
+    out = torch.full((blocks * 256,), -1.0, dtype=torch.float32, device=DEV)
+    moe.moe_peakbench_valu_fma(blocks, iters, 1.0, 0.0, out)
+    torch.cuda.synchronize()
+    lane = torch.arange(blocks * 256, device=DEV) % 64
+    assert bool((out == (8 * lane + 28).float()).all())
+    if iters <= 100:  # a multiplier of one half: the result shows the run length (exact, no underflow)
+        moe.moe_peakbench_valu_fma(blocks, iters, 0.5, 0.0, out)
+        torch.cuda.synchronize()
+        assert bool((out.double() == (8 * lane + 28).double() * (0.5 ** iters)).all())
+
+
+def test_peakbench_rejects_bad_arguments():
+    out = torch.empty(256, dtype=torch.int32, device=DEV)
+    for blocks, iters in ((0, 1), (1, 0), (-1, 5)):
+        assert _lib._lib.moe_peakbench_mfma_i8(blocks, iters, 1, _lib._ptr(out), None) == moe.MOE_E_SHAPE
+        assert _lib._lib.moe_peakbench_valu_fma(blocks, iters, 1.0, 0.0, _lib._ptr(out), None) == moe.MOE_E_SHAPE
+    assert _lib._lib.moe_peakbench_mfma_i8(1, 1, 1, None, None) == moe.MOE_E_NULL
