@@ -450,15 +450,19 @@ __device__ __forceinline__ void gemv_gateup_run(const ExpertArgs& a, const Bucke
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)bq * 32);
-      const v4i xa = xb4[0], xb = xb4[1];
-      const int Sg = wdot(pg, xa, xb);
-      const int Su = wdot(pu, xa, xb);
-      tb[((i << 3) | rl) * 8 + bs] = (float)Sg;
-      tb[(((N + i) << 3) | rl) * 8 + bs] = (float)Su;
-      if (TAP && i == tap_i && blk < nb) {
-        a.t_gu_sums[(size_t)(tile * 64 + row) * nb + blk] = Sg;
-        a.t_gu_sums[(size_t)(I + tile * 64 + row) * nb + blk] = Su;
+      // a 3-token chunk runs the 4-token code: its padding token's sums are never used (its chain lanes' results
+      // are not stored), so they are not computed (with grouped scales the skip costs the ring a full wait)
+      if (GS || i < nn) {
+        const v4i* xb4 = reinterpret_cast<const v4i*>(xs + (size_t)i * H + (size_t)bq * 32);
+        const v4i xa = xb4[0], xb = xb4[1];
+        const int Sg = wdot(pg, xa, xb);
+        const int Su = wdot(pu, xa, xb);
+        tb[((i << 3) | rl) * 8 + bs] = (float)Sg;
+        tb[(((N + i) << 3) | rl) * 8 + bs] = (float)Su;
+        if (TAP && i == tap_i && blk < nb) {
+          a.t_gu_sums[(size_t)(tile * 64 + row) * nb + blk] = Sg;
+          a.t_gu_sums[(size_t)(I + tile * 64 + row) * nb + blk] = Su;
+        }
       }
     }
     if constexpr (GS) {
@@ -569,14 +573,16 @@ __device__ __forceinline__ void gemv_down_run(const ExpertArgs& a, const Bucket&
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)bq * 32);
-      const v4i ha = hb4[0], hb = hb4[1];
+      if (GS || i < nn) {  // as in the gate/up GEMV
+        const v4i* hb4 = reinterpret_cast<const v4i*>(hs + (size_t)i * I + (size_t)bq * 32);
+        const v4i ha = hb4[0], hb = hb4[1];
 #pragma unroll
-      for (int q = 0; q < TP; ++q) {
-        const int S = wdot(pw[q], ha, hb);
-        tb[(((q * N + i) << 3) | rl) * 8 + bs] = (float)S;
-        if (TAP && i == tap_i && blk < nbi)
-          a.t_dn_sums[(size_t)((TP * tile2 + q) * 64 + row) * nbi + blk] = S;
+        for (int q = 0; q < TP; ++q) {
+          const int S = wdot(pw[q], ha, hb);
+          tb[(((q * N + i) << 3) | rl) * 8 + bs] = (float)S;
+          if (TAP && i == tap_i && blk < nbi)
+            a.t_dn_sums[(size_t)((TP * tile2 + q) * 64 + row) * nbi + blk] = S;
+        }
       }
     }
     if constexpr (GS) {
