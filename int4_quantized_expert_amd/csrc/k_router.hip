@@ -281,6 +281,28 @@ __device__ void dispatch_one_token(const DispatchArgs& a, const int* sel, const 
   }
 }
 
+// Cross-lane moves within a row of 16 lanes (DPP, no LDS round trip). The
+// control is an immediate of the instruction, hence one function per pattern.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over aligned groups of n lanes (n a power of two up to 64); every
+// lane of a group receives it. Lanes 1 and 2 apart are paired by quad
+// permutes, the two quads of 8 lanes by the half-row mirror and the two halves
+// of a 16-lane row by the row mirror (for a maximum any pairing of the two
+// halves serves), 16 and 32 apart by shuffles.
+__device__ __forceinline__ float group_max(float v, int n) {
+  if (n >= 2) v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  if (n >= 4) v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  if (n >= 8) v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  if (n >= 16) v = fmaxf(v, dpp_f<0x140>(v)); // row_mirror
+  if (n >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (n >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
 // Candidate key of the top-K ranking: the order-preserving bits of score c
 // (larger c, larger key; -0 taken as +0 so that equal scores tie) above the
 // complement of the candidate's position, which breaks ties toward the lower
@@ -350,12 +372,10 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
     for (int base = 0; base < E; base += 256) {
       const int e = base + tid;
       const float v = e < E ? s_c[e] : -INFINITY;
-      float m1 = v;
-      for (int o = n >> 1; o >= 1; o >>= 1) m1 = fmaxf(m1, __shfl_xor(m1, o));
+      const float m1 = group_max(v, n);
       const uint64_t eq = __ballot(v == m1) & gmask;
       const int first = __ffsll((unsigned long long)eq) - 1;
-      float m2 = lane == first ? -INFINITY : v;
-      for (int o = n >> 1; o >= 1; o >>= 1) m2 = fmaxf(m2, __shfl_xor(m2, o));
+      const float m2 = group_max(lane == first ? -INFINITY : v, n);
       if (e < E && (lane & (n - 1)) == 0) s_gs[e / n] = __fadd_rn(m1, m2);
     }
   } else if (tid < G) {
@@ -388,40 +408,49 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
   // position in the compacted candidate array (kept groups ascending, experts
   // ascending within a group), so a larger key is a higher c or an equal c at a
   // lower expert index. Each candidate counts the keys above its own with one
-  // 64-bit compare per entry. Rank k is slot k; rank K is the best expert left
-  // out.
+  // 64-bit compare per entry, on two adjacent lanes that take one half of the
+  // array each and add their counts with a quad permute. Rank k is slot k; rank
+  // K is the best expert left out.
   __shared__ int s_kpos[kMaxGroups];  // position of a kept group among the kept groups
-  __shared__ __align__(16) uint64_t s_key[kMaxExperts];
+  __shared__ __align__(16) uint64_t s_key[kMaxExperts + 4];
+  __shared__ int s_cand[kMaxExperts];  // expert of each compacted candidate
   if (wave == 0) {
     const bool kg = lane < G && s_kept[lane];
     const uint64_t km = __ballot(kg);
     if (lane < G) s_kpos[lane] = __popcll(km & ((1ull << lane) - 1));
   }
   __syncthreads();
-  const int nc = KG * n, ncp = (nc + 1) & ~1;  // candidates, padded to whole pairs
+  // candidates padded to a multiple of 4, so that each half of the key array holds whole pairs
+  const int nc = KG * n, nh = ((nc + 3) & ~3) / 2;
   for (int e = tid; e < E; e += 256) {
     const int g = e / n;
     if (s_kept[g]) {
       const int pos = s_kpos[g] * n + (e - g * n);
       s_key[pos] = cand_key(s_c[e], pos);
+      s_cand[pos] = e;
     }
   }
-  for (int j = nc + tid; j < ncp; j += 256) s_key[j] = 0;  // below every real key
+  for (int j = nc + tid; j < 2 * nh; j += 256) s_key[j] = 0;  // below every real key
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    const int g = e / n;
-    if (!s_kept[g]) continue;
-    const float v = s_c[e];
-    const uint64_t mine = cand_key(v, s_kpos[g] * n + (e - g * n));
+  // lanes 2p and 2p + 1 rank candidate p (2 * nc is even, so a pair is active or idle together)
+  for (int q = tid; q < 2 * nc; q += 256) {
+    const int p = q >> 1;
+    const uint64_t mine = s_key[p];
+    const uint64_t* kh = s_key + (q & 1) * nh;
     int rk = 0;
 #pragma unroll 8
-    for (int j = 0; j < ncp; j += 2) rk += (int)(s_key[j] > mine) + (int)(s_key[j + 1] > mine);
-    if (rk < K) {
-      s_sel[rk] = e;
-      s_selc[rk] = v;
-      s_sels[rk] = s_s[e];
-    } else if (rk == K) {
-      s_selc[K] = v;  // best expert left out
+    for (int j = 0; j < nh; j += 2) rk += (int)(kh[j] > mine) + (int)(kh[j + 1] > mine);
+    rk += __builtin_amdgcn_update_dpp(0, rk, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]: the partner's count
+    if ((q & 1) == 0) {
+      const int e = s_cand[p];
+      const float v = s_c[e];
+      if (rk < K) {
+        s_sel[rk] = e;
+        s_selc[rk] = v;
+        s_sels[rk] = s_s[e];
+      } else if (rk == K) {
+        s_selc[K] = v;  // best expert left out
+      }
     }
   }
   __syncthreads();
@@ -433,7 +462,8 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ part, c
       double sum = 0.0;  // in slot order
       for (int k = 0; k < K; ++k)
         sum += (double)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), k));
-      const float cn = __shfl_down(cv, 1);  // the next slot's score
+      // the next slot's score (within the first 16-lane row: row_shl 1)
+      const float cn = K <= 16 ? dpp_f<0x101>(cv) : __shfl_down(cv, 1);
       const uint64_t ord = __ballot(lane + 1 < K && (double)cv - (double)cn < 1e-6);
       if (lane == 0) {
         uint8_t fl = ord ? MOE_TIE_ORDER : 0;
