@@ -144,31 +144,30 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(const float* 
 #pragma unroll
     for (int be = 0; be < EB; ++be) acc[bt][be] = v4d{0.0, 0.0, 0.0, 0.0};
   if (FULL) {
-    // this lane's four h of group q: 16q + 4g + 0..3; PD groups in flight
+    // this lane's four h of group q: 16q + 4g + 0..3; PD groups in flight. The main loop refills every slot it
+    // consumes (past the last group it reloads the last one, which the drain never uses), so each wait in it is
+    // for the slot consumed; the drain runs the groups left without loading.
     float4 rx[PD][TB], rw[PD][EB];
-#pragma unroll
-    for (int kk = 0; kk < PD; ++kk) {
-      const int q = min(kk, NG - 1);
+    auto load = [&](int kk, int q) __attribute__((always_inline)) {
 #pragma unroll
       for (int bt = 0; bt < TB; ++bt) rx[kk][bt] = *reinterpret_cast<const float4*>(xrow[bt] + 16 * q);
 #pragma unroll
       for (int be = 0; be < EB; ++be) rw[kk][be] = *reinterpret_cast<const float4*>(wrow[be] + 16 * q);
-    }
-    for (int q0 = 0; q0 < NG; q0 += PD) {
+    };
+#pragma unroll
+    for (int kk = 0; kk < PD; ++kk) load(kk, min(kk, NG - 1));
+    int q0 = 0;
+    for (; q0 + PD < NG; q0 += PD) {
 #pragma unroll
       for (int kk = 0; kk < PD; ++kk) {
-        if (q0 + kk < NG) {
-          router_group_mfma<TB, EB>(acc, rx[kk], rw[kk]);
-          const int q = q0 + kk + PD;
-          if (q < NG) {
-#pragma unroll
-            for (int bt = 0; bt < TB; ++bt) rx[kk][bt] = *reinterpret_cast<const float4*>(xrow[bt] + 16 * q);
-#pragma unroll
-            for (int be = 0; be < EB; ++be) rw[kk][be] = *reinterpret_cast<const float4*>(wrow[be] + 16 * q);
-          }
-        }
+        router_group_mfma<TB, EB>(acc, rx[kk], rw[kk]);
+        __builtin_amdgcn_sched_barrier(0);
+        load(kk, min(q0 + kk + PD, NG - 1));
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < PD; ++kk)
+      if (q0 + kk < NG) router_group_mfma<TB, EB>(acc, rx[kk], rw[kk]);
   } else {
     for (int q = 0; q < NG; ++q) {
       float4 xa[TB], wb[EB];
