@@ -1011,11 +1011,21 @@ __global__ __launch_bounds__(256) void k_tile_gather(ExpertArgs a, const int32_t
   const int H = a.H, nb = H / 32;
   const int b_lo = nb * blockIdx.y / gridDim.y, b_hi = nb * (blockIdx.y + 1) / gridDim.y;
   const int items = (b_hi - b_lo) * nv * 2;  // 16-byte halves of (block, position)
-  for (int it = tid; it < items; it += 256) {
-    const int half = it & 1, jb = it >> 1;
-    const int j = jb % nv, b = b_lo + jb / nv;
-    const v4i v = *reinterpret_cast<const v4i*>(a.qx + (size_t)s_tok[j] * H + b * 32 + 16 * half);
-    *reinterpret_cast<v4i*>(a.xt + pb_off(k.p0 + t0 + j, b, nb) + 16 * half) = v;
+  // four items per lane at a time, all loads issued before the first store waits for one
+  constexpr int U = 4;
+  for (int it0 = tid; it0 < items; it0 += U * 256) {
+    v4i v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = min(it0 + u * 256, items - 1), half = it & 1, jb = it >> 1;
+      const int j = jb % nv, b = b_lo + jb / nv;
+      v[u] = *reinterpret_cast<const v4i*>(a.qx + (size_t)s_tok[j] * H + b * 32 + 16 * half);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = it0 + u * 256, half = it & 1, jb = it >> 1;
+      if (it < items) *reinterpret_cast<v4i*>(a.xt + pb_off(k.p0 + t0 + jb % nv, b_lo + jb / nv, nb) + 16 * half) = v[u];
+    }
   }
   const int sitems = (b_hi - b_lo) * nv;
   for (int it = tid; it < sitems; it += 256) {
